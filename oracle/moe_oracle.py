@@ -1,0 +1,380 @@
+"""Plain, slow, float64 CPU oracle for the top-k token-choice MoE-layer forward.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg, never by the product path.  It shares
+no code with the HIP library; both sides only consume the same seeded inputs.
+
+Sources (the pages this follows; section names as printed on each page):
+  [LAB]  "Lab: build a tiny MoE in PyTorch" (open-llm-engineering), sections
+         "The contract", "Full implementation", "Smoke test and backward pass",
+         "Trace one token by hand", "Read the loss values correctly",
+         "Ablation 2: top-1 versus top-2", "Add a capacity limit",
+         "Add a shared expert", "Required correctness tests", "Lab extensions".
+  [BOOK] "2.9 Mixture-of-Experts (MoE) Architectures" (llm-stack-book), sections
+         "From One FFN to a Bank of Experts", "The Router: Gating, Top-k, and the
+         Softmax-Then-Select Question", "A Toy MoE Layer From Scratch",
+         "The auxiliary load-balancing loss", "Capacity Factor, Token Dropping,
+         and the Worked Numbers", "DeepSeek-MoE and the fine-grained +
+         shared-expert idea", "Sparse upcycling", "Exercises".
+  [NEMO] "nemo_automodel.components.moe.layers" (NeMo AutoModel v0.4 API):
+         class ``Gate`` attributes ``score_func``, ``n_groups``, ``topk_groups``,
+         ``norm_topk_prob``, ``route_scale``; class ``MLP`` (SwiGLU, no bias).
+
+Precision: every floating-point step runs in float64 on the exact stored input
+values (bf16 or fp32 upcast without rounding).
+
+Readings taken where the pages are silent or garbled (all listed in the design doc):
+  * top-k ties go to the lower expert index; slot j holds the j-th largest
+    selection score (the tie rule is what makes a zero router pick experts
+    0..k-1, as [BOOK] "Sparse upcycling" states);
+  * capacity drops are first-come in token order, slot order inside a token
+    ([LAB] "Add a capacity limit"); counts and the balance loss use the
+    pre-drop assignments; surviving weights are not renormalised;
+  * sigmoid scoring adds the per-expert correction bias to the scores for
+    selection only; gate weights use the unbiased scores ([BOOK] "The Router",
+    noisy/top-k gating paragraph; [NEMO] ``score_func`` 'sigmoid');
+  * group-limited routing ranks each contiguous group by the sum of its two
+    largest biased scores (``group_rule='top2sum'``) or by its maximum
+    (``'max'``).  PARITY UNPINNED: the pages name ``n_groups``/``topk_groups``
+    but define no group score;
+  * for sigmoid scoring the balance loss uses P_e = mean_t s_te / sum_e' s_te'.
+    PARITY UNPINNED: the pages give no formula for this case.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "NEAR_TIE", "router_logits", "softmax", "sigmoid", "logsumexp",
+    "route", "capacity", "first_within_capacity", "permutation",
+    "swiglu_ffn", "expert_outputs", "combine", "forward",
+    "brute_force_forward", "all_experts_then_mask",
+]
+
+# Tokens whose top-(k+1) selection scores (or top group scores) sit closer than
+# this are "near ties": a last-bit difference may flip the choice.
+NEAR_TIE = 1e-5
+
+
+# ---------------------------------------------------------------- router ---
+
+def router_logits(x, w_router, logit_bias=None):
+    """h[t, e] = sum_d x[t, d] * W_r[e, d]  (+ logit_bias[e]).
+
+    The router is a bias-free Linear(d_model, E) ([LAB] "Full implementation",
+    ``self.router``); its math is done in high precision ([LAB] comment on
+    router math in float32; here float64).  ``logit_bias`` is an additive
+    per-expert logit offset ([NEMO] score function 'softmax_with_bias')."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_router, dtype=np.float64)
+    h = x @ w.T
+    if logit_bias is not None:
+        h = h + np.asarray(logit_bias, dtype=np.float64)[None, :]
+    return h
+
+
+def softmax(h):
+    """Softmax over experts with the maximum subtracted ([LAB] ``F.softmax``)."""
+    m = h.max(axis=-1, keepdims=True)
+    e = np.exp(h - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def sigmoid(h):
+    """Logistic score 1/(1+exp(-h)) ([NEMO] ``score_func`` 'sigmoid')."""
+    return 1.0 / (1.0 + np.exp(-h))
+
+
+def logsumexp(h):
+    m = h.max(axis=-1)
+    return m + np.log(np.exp(h - m[:, None]).sum(axis=-1))
+
+
+def _order_desc(v):
+    """Indices sorting each row of ``v`` by descending value, equal values
+    in ascending index order (a stable sort of the negated values)."""
+    return np.argsort(-v, axis=-1, kind="stable")
+
+
+def _group_limit(sel, n_groups, topk_groups, group_rule):
+    """Mask experts outside each token's ``topk_groups`` best groups.
+
+    Experts form ``n_groups`` contiguous groups of E/n_groups ([NEMO]
+    ``n_groups``/``topk_groups``; [LAB] "Lab extensions": no token may touch
+    more groups than allowed).  Returns (masked selection scores, group scores,
+    kept-group indices)."""
+    T, E = sel.shape
+    gs = E // n_groups
+    grouped = sel.reshape(T, n_groups, gs)
+    if group_rule == "top2sum":
+        srt = -np.sort(-grouped, axis=-1)
+        gscore = srt[..., 0] + srt[..., 1]
+    elif group_rule == "max":
+        gscore = grouped.max(axis=-1)
+    else:
+        raise ValueError(f"unknown group rule {group_rule!r}")
+    keep_groups = _order_desc(gscore)[:, :topk_groups]
+    allowed = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(allowed, keep_groups, True, axis=1)
+    allowed_e = np.repeat(allowed, gs, axis=1)
+    masked = np.where(allowed_e, sel, -np.inf)
+    return masked, gscore, keep_groups
+
+
+def _min_adjacent_gap(sorted_desc, n):
+    """Smallest gap between neighbours among the first ``n`` sorted values
+    (inf where there are fewer than two finite values)."""
+    v = sorted_desc[:, :n]
+    if v.shape[1] < 2:
+        return np.full(v.shape[0], np.inf)
+    with np.errstate(invalid="ignore"):
+        g = v[:, :-1] - v[:, 1:]
+    g = np.where(np.isfinite(g), g, np.inf)
+    return g.min(axis=1)
+
+
+def route(x, w_router, top_k, *, score="softmax", renormalize=True, route_scale=1.0,
+          logit_bias=None, select_bias=None, n_groups=1, topk_groups=1,
+          group_rule="top2sum"):
+    """Routing step of the layer, in the pages' order.
+
+    1. logits h = x W_r^T (+ logit bias)                  [LAB] "Full implementation"
+    2. scores: softmax over all E ([LAB]) or sigmoid ([NEMO] ``score_func``)
+    3. selection score = score (+ selection-only bias)   [BOOK] "The Router"
+    4. optional group limit (contiguous groups)          [NEMO] ``n_groups``
+    5. top-k IDs, descending                             [LAB] ``topk``
+    6. weights: renormalised over the k selected scores  [LAB]; ``norm_topk_prob``
+       or the raw top score (Switch top-1)               [LAB] "Ablation 2"
+       times ``route_scale``                              [NEMO] ``route_scale``
+    7. counts, f, P, balance = E sum f P, z = mean lse^2  [LAB]; [BOOK] aux loss
+
+    Returns a dict with ``ids`` [T,k] int64, ``weights`` [T,k], ``counts`` [E],
+    ``mean_prob`` [E], ``balance``, ``z``, ``margin`` [T] and ``near_tie`` [T]."""
+    h = router_logits(x, w_router, logit_bias)
+    T, E = h.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("top_k must be in [1, n_experts]")
+    if score == "softmax":
+        sc = softmax(h)
+        prob_for_P = sc
+    elif score == "sigmoid":
+        sc = sigmoid(h)
+        prob_for_P = sc / sc.sum(axis=-1, keepdims=True)
+    else:
+        raise ValueError(f"unknown score {score!r}")
+    sel = sc.copy()
+    if select_bias is not None:
+        sel = sel + np.asarray(select_bias, dtype=np.float64)[None, :]
+    group_margin = np.full(T, np.inf)
+    if n_groups > 1:
+        if E % n_groups or topk_groups < 1 or topk_groups > n_groups:
+            raise ValueError("bad group configuration")
+        if top_k > topk_groups * (E // n_groups):
+            raise ValueError("top_k exceeds the experts of the allowed groups")
+        sel, gscore, _ = _group_limit(sel, n_groups, topk_groups, group_rule)
+        gsorted = -np.sort(-gscore, axis=1)
+        group_margin = _min_adjacent_gap(gsorted, min(topk_groups + 1, n_groups))
+    order = _order_desc(sel)
+    ids = order[:, :top_k]
+    chosen = np.take_along_axis(sc, ids, axis=1)
+    if renormalize:
+        weights = chosen / chosen.sum(axis=1, keepdims=True)
+    else:
+        weights = chosen.copy()
+    weights = weights * route_scale
+    sel_sorted = np.take_along_axis(sel, order[:, :min(top_k + 1, E)], axis=1)
+    margin = np.minimum(_min_adjacent_gap(sel_sorted, min(top_k + 1, E)), group_margin)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    f = counts / float(ids.size)
+    P = prob_for_P.mean(axis=0)
+    balance = E * float(np.sum(f * P))
+    z = float(np.mean(logsumexp(h) ** 2))
+    return {
+        "logits": h, "scores": sc, "ids": ids.astype(np.int64), "weights": weights,
+        "counts": counts.astype(np.int64), "mean_prob": P, "balance": balance,
+        "z": z, "margin": margin, "near_tie": margin < NEAR_TIE,
+    }
+
+
+# -------------------------------------------------------------- capacity ---
+
+def capacity(capacity_factor, T, top_k, E):
+    """C = max(1, ceil(cf * T*k / E)); None (no limit) when dropless.
+
+    [LAB] "Add a capacity limit" (ceil of factor * assignments / experts);
+    [BOOK] "A Toy MoE Layer From Scratch" (at least 1).  Evaluated in that
+    operand order in double precision."""
+    if capacity_factor is None or capacity_factor <= 0:
+        return None
+    return max(1, math.ceil(capacity_factor * (T * top_k) / E))
+
+
+def first_within_capacity(ids, E, cap):
+    """Keep mask [T,k]: walk tokens in order, slots in order, and keep an
+    assignment while its expert has taken fewer than ``cap`` assignments
+    ([LAB] "Add a capacity limit", first-come policy).  ``cap=None`` keeps all."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    keep = np.zeros((T, k), dtype=bool)
+    if cap is None:
+        keep[:] = True
+        return keep
+    used = [0] * E
+    for t in range(T):
+        for s in range(k):
+            e = int(ids[t, s])
+            if used[e] < cap:
+                keep[t, s] = True
+                used[e] += 1
+    return keep
+
+
+def permutation(ids, keep, E):
+    """Canonical expert-major order of the kept assignments.
+
+    Kept assignments a = t*k + s are listed by (expert ascending, token
+    ascending), the sorted expert-major token list a grouped GEMM consumes
+    ([BOOK] "MoE in Practice", serving paragraph).  It is unique because a
+    token picks an expert at most once.  Returns ``expert_offsets`` [E+1],
+    ``row_to_assign`` [n_kept] and ``assign_to_row`` [T*k] (-1 = dropped)."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    flat_e = ids.reshape(-1)
+    flat_keep = np.asarray(keep).reshape(-1)
+    a = np.nonzero(flat_keep)[0]
+    tok = a // k
+    order = np.lexsort((tok, flat_e[a]))
+    row_to_assign = a[order]
+    kept_counts = np.bincount(flat_e[a], minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept_counts)
+    assign_to_row = np.full(T * k, -1, dtype=np.int64)
+    assign_to_row[row_to_assign] = np.arange(row_to_assign.size)
+    return offsets, row_to_assign.astype(np.int64), assign_to_row
+
+
+# --------------------------------------------------------------- experts ---
+
+def swiglu_ffn(z, w_gate, w_up, w_down):
+    """FFN(z) = W_down (silu(W_gate z) * (W_up z)), silu(u) = u sigmoid(u).
+
+    [LAB] ``SwiGLUExpert`` (three bias-free Linears); weights in Linear layout:
+    w_gate, w_up [H, D]; w_down [D, H].  ``z`` is [n, D]."""
+    z = np.asarray(z, dtype=np.float64)
+    g = z @ np.asarray(w_gate, dtype=np.float64).T
+    u = z @ np.asarray(w_up, dtype=np.float64).T
+    act = g * sigmoid(g) * u
+    return act @ np.asarray(w_down, dtype=np.float64).T
+
+
+def expert_outputs(x, ids, weights, keep, w_gate, w_up, w_down, tokens=None):
+    """Weighted expert output per (token, slot): Y[t, s] = w_ts FFN_{e_ts}(x_t)
+    for kept slots, 0 for dropped ones ([LAB] "Full implementation", the
+    per-expert gather / run / scale step).  Only tokens in ``tokens`` (default:
+    all) are evaluated; returns [len(tokens), k, D]."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    D = np.asarray(x).shape[1]
+    Y = np.zeros((tokens.size, k, D))
+    sub_ids = ids[tokens]
+    sub_keep = np.asarray(keep)[tokens]
+    for e in np.unique(sub_ids):
+        r, s = np.nonzero((sub_ids == e) & sub_keep)
+        if r.size == 0:
+            continue
+        out = swiglu_ffn(np.asarray(x, dtype=np.float64)[tokens[r]], w_gate[e], w_up[e],
+                         w_down[e])
+        Y[r, s] = np.asarray(weights)[tokens[r], s][:, None] * out
+    return Y
+
+
+def combine(Y, shared=None):
+    """out_t = sum over slots (in slot order) of the weighted expert outputs,
+    plus the always-on shared expert ([LAB] ``index_add_`` combine and
+    "Add a shared expert")."""
+    out = np.zeros(Y.shape[::2])
+    for s in range(Y.shape[1]):
+        out = out + Y[:, s]
+    if shared is not None:
+        out = out + shared
+    return out
+
+
+def forward(inputs, *, top_k, score="softmax", renormalize=True, route_scale=1.0,
+            n_groups=1, topk_groups=1, group_rule="top2sum", capacity_factor=None,
+            tokens=None, routing=None):
+    """The whole layer forward on float64 arrays.
+
+    ``inputs`` holds x [T,D], w_router [E,D], w_gate/w_up [E,H,D], w_down
+    [E,D,H], optional ws_gate/ws_up [Hs,D], ws_down [D,Hs], logit_bias [E],
+    select_bias [E].  ``tokens`` limits the expert/combine work to a subset of
+    tokens (routing and capacity are always computed for all tokens, because
+    drops depend on every earlier token).  ``routing`` may supply precomputed
+    ``ids``/``weights`` (e.g. those of the device, to compare the downstream
+    steps on identical routes)."""
+    x = inputs["x"]
+    T, D = x.shape
+    E = inputs["w_router"].shape[0]
+    r = route(x, inputs["w_router"], top_k, score=score, renormalize=renormalize,
+              route_scale=route_scale, logit_bias=inputs.get("logit_bias"),
+              select_bias=inputs.get("select_bias"), n_groups=n_groups,
+              topk_groups=topk_groups, group_rule=group_rule)
+    if routing is not None:
+        r = dict(r)
+        r["ids"] = np.asarray(routing["ids"], dtype=np.int64)
+        r["weights"] = np.asarray(routing["weights"], dtype=np.float64)
+        r["counts"] = np.bincount(r["ids"].reshape(-1), minlength=E)
+    cap = capacity(capacity_factor, T, top_k, E)
+    keep = first_within_capacity(r["ids"], E, cap)
+    offsets, row_to_assign, assign_to_row = permutation(r["ids"], keep, E)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    Y = expert_outputs(x, r["ids"], r["weights"], keep, inputs["w_gate"],
+                       inputs["w_up"], inputs["w_down"], tokens=tok)
+    shared = None
+    if inputs.get("ws_gate") is not None:
+        shared = swiglu_ffn(np.asarray(x, dtype=np.float64)[tok], inputs["ws_gate"],
+                            inputs["ws_up"], inputs["ws_down"])
+    out = combine(Y, shared)
+    return {
+        "out": out, "tokens": tok, "route": r, "capacity": cap, "keep": keep,
+        "expert_offsets": offsets, "row_to_assign": row_to_assign,
+        "assign_to_row": assign_to_row, "n_kept": int(keep.sum()),
+    }
+
+
+# ------------------------------------------- second implementations (tiny) ---
+
+def brute_force_forward(inputs, ids, weights, keep=None):
+    """Token-by-token, slot-by-slot loop in pure Python ([LAB] "Trace one token
+    by hand"): out_t = sum_s w_ts FFN_{e_ts}(x_t) (+ shared).  For tiny shapes."""
+    x = np.asarray(inputs["x"], dtype=np.float64)
+    T, D = x.shape
+    k = ids.shape[1]
+    out = np.zeros((T, D))
+    for t in range(T):
+        for s in range(k):
+            if keep is not None and not keep[t, s]:
+                continue
+            e = int(ids[t, s])
+            out[t] += weights[t, s] * swiglu_ffn(x[t:t + 1], inputs["w_gate"][e],
+                                                 inputs["w_up"][e], inputs["w_down"][e])[0]
+        if inputs.get("ws_gate") is not None:
+            out[t] += swiglu_ffn(x[t:t + 1], inputs["ws_gate"], inputs["ws_up"],
+                                 inputs["ws_down"])[0]
+    return out
+
+
+def all_experts_then_mask(inputs, ids, weights):
+    """Run every expert on every token and keep only the selected ones
+    ([BOOK] "A Toy MoE Layer From Scratch", second approach; unit tests only)."""
+    x = np.asarray(inputs["x"], dtype=np.float64)
+    T, D = x.shape
+    E = inputs["w_gate"].shape[0]
+    dense = np.stack([swiglu_ffn(x, inputs["w_gate"][e], inputs["w_up"][e],
+                                 inputs["w_down"][e]) for e in range(E)], axis=1)
+    gate = np.zeros((T, E))
+    np.put_along_axis(gate, np.asarray(ids), np.asarray(weights), axis=1)
+    return np.einsum("te,ted->td", gate, dense)

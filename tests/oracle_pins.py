@@ -1,0 +1,431 @@
+"""Pins for the CPU oracle: facts fixed by the pages or by mathematics.
+
+Each ``pin_*`` function takes the oracle module ``o`` and raises
+AssertionError when ``o`` disagrees with a value the pages print, a closed
+form, an identity, a special case or a brute-force loop.  The same functions
+run against the real oracle (``test_oracle_pins.py``) and against copies of it
+with a planted mistake (``test_oracle_mutants.py``), which must each fail at
+least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _sig(v):
+    return 1.0 / (1.0 + math.exp(-v))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _tiny_inputs(seed, T=9, D=6, H=5, E=4, shared=False, std=0.5):
+    r = _rng(seed)
+    inp = {
+        "x": r.normal(size=(T, D)),
+        "w_router": r.normal(size=(E, D)) * std,
+        "w_gate": r.normal(size=(E, H, D)) * std,
+        "w_up": r.normal(size=(E, H, D)) * std,
+        "w_down": r.normal(size=(E, D, H)) * std,
+    }
+    if shared:
+        inp["ws_gate"] = r.normal(size=(H + 1, D)) * std
+        inp["ws_up"] = r.normal(size=(H + 1, D)) * std
+        inp["ws_down"] = r.normal(size=(D, H + 1)) * std
+    return inp
+
+
+def _route_logits(o, logits, k, **kw):
+    """Route tokens whose logits are given directly (x = h, W_r = I)."""
+    h = np.atleast_2d(np.asarray(logits, dtype=np.float64))
+    return o.route(h, np.eye(h.shape[1]), k, **kw)
+
+
+# ------------------------------------------------------------- routing -----
+
+def pin_worked_example_ids(o):
+    """Both conventions pick experts [5, 0] for the printed 8-expert logits."""
+    g = _golden("worked_routing_example.json")
+    for renorm in (True, False):
+        r = _route_logits(o, g["logits"], g["k"], renormalize=renorm)
+        assert r["ids"][0].tolist() == g["expected_ids"], r["ids"]
+
+
+def pin_worked_example_renorm_closed_form(o):
+    """Renormalised weights are exp(3)/(exp(3)+exp(2)) = sigmoid(1) and sigmoid(-1)."""
+    g = _golden("worked_routing_example.json")
+    r = _route_logits(o, g["logits"], g["k"], renormalize=True)
+    assert np.allclose(r["weights"][0], [_sig(1.0), _sig(-1.0)], rtol=0, atol=1e-15)
+
+
+def pin_worked_example_switch_ratio(o):
+    """Without renormalisation the two kept probabilities keep the ratio
+    exp(h5 - h0) = e, and all E probabilities add to 1."""
+    g = _golden("worked_routing_example.json")
+    r = _route_logits(o, g["logits"], g["k"], renormalize=False)
+    w = r["weights"][0]
+    assert abs(w[0] / w[1] - math.e) < 1e-13
+    assert w.sum() < 1.0
+    rall = _route_logits(o, g["logits"], 8, renormalize=False)
+    assert abs(rall["weights"][0].sum() - 1.0) < 1e-15
+
+
+def pin_renorm_is_topk_then_softmax(o):
+    """Softmax-then-top-k with renormalisation equals top-k-then-softmax over the
+    k selected logits (the book's Mixtral-style route) for any logits."""
+    h = _rng(1).normal(size=(40, 12)) * 2.0
+    k = 3
+    r = _route_logits(o, h, k, renormalize=True)
+    top = np.sort(h, axis=1)[:, ::-1][:, :k]
+    alt = np.exp(top - top[:, :1])
+    alt = alt / alt.sum(axis=1, keepdims=True)
+    assert np.allclose(r["weights"], alt, rtol=0, atol=1e-14)
+    assert (np.take_along_axis(h, r["ids"], 1) == top).all()
+
+
+def pin_zero_router_picks_first_k(o):
+    """A zero router gives equal scores, so top-k picks experts 0..k-1 with
+    equal weights (book, 'Sparse upcycling')."""
+    inp = _tiny_inputs(2, E=6)
+    for k in (1, 2, 4):
+        r = o.route(inp["x"], np.zeros((6, inp["x"].shape[1])), k)
+        assert (r["ids"] == np.arange(k)[None, :]).all()
+        assert np.allclose(r["weights"], 1.0 / k, rtol=0, atol=1e-15)
+        assert r["near_tie"].all()
+
+
+def pin_weight_sums(o):
+    """Renormalised weights sum to 1 (lab smoke test); with route_scale they sum
+    to route_scale; the un-renormalised top-1 weight lies in (1/E, 1]."""
+    inp = _tiny_inputs(3, T=30, E=8)
+    r = o.route(inp["x"], inp["w_router"], 3)
+    assert np.allclose(r["weights"].sum(1), 1.0, rtol=0, atol=1e-14)
+    r = o.route(inp["x"], inp["w_router"], 3, score="sigmoid", route_scale=2.5)
+    assert np.allclose(r["weights"].sum(1), 2.5, rtol=0, atol=1e-13)
+    r = o.route(inp["x"], inp["w_router"], 1, renormalize=False)
+    assert ((r["weights"] > 1.0 / 8) & (r["weights"] <= 1.0)).all()
+
+
+def pin_slots_descending(o):
+    """Slot j holds the j-th largest selection score."""
+    inp = _tiny_inputs(4, T=25, E=10)
+    for score in ("softmax", "sigmoid"):
+        r = o.route(inp["x"], inp["w_router"], 4, score=score)
+        v = np.take_along_axis(r["scores"], r["ids"], 1)
+        assert (np.diff(v, axis=1) <= 0).all()
+        rest = r["scores"].copy()
+        np.put_along_axis(rest, r["ids"], -np.inf, 1)
+        assert (v[:, -1] >= rest.max(1)).all()
+
+
+def pin_sigmoid_closed_form(o):
+    """Sigmoid weights with renormalisation for a token with logits 0 and ln 3:
+    scores 1/2 and 3/4, weights 2.5*(2/5) and 2.5*(3/5)."""
+    h = np.array([[0.0, math.log(3.0), -5.0, -6.0]])
+    r = _route_logits(o, h, 2, score="sigmoid", route_scale=2.5)
+    assert r["ids"][0].tolist() == [1, 0]
+    assert np.allclose(r["weights"][0], [1.5, 1.0], rtol=0, atol=1e-14)
+
+
+def pin_selection_only_bias(o):
+    """A selection bias changes which experts win but the weights still come
+    from the unbiased scores (book exercise 6; DeepSeek-V3 paragraph)."""
+    inp = _tiny_inputs(5, T=20, E=8)
+    x, w = inp["x"], inp["w_router"]
+    r0 = o.route(x, w, 2, score="sigmoid")
+    rz = o.route(x, w, 2, score="sigmoid", select_bias=np.zeros(8))
+    assert (r0["ids"] == rz["ids"]).all() and np.allclose(r0["weights"], rz["weights"])
+    b = np.zeros(8)
+    b[6] = 10.0
+    rb = o.route(x, w, 2, score="sigmoid", select_bias=b)
+    assert (rb["ids"][:, 0] == 6).all()
+    s = 1.0 / (1.0 + np.exp(-(x @ w.T)))
+    chosen = np.take_along_axis(s, rb["ids"], 1)
+    assert np.allclose(rb["weights"], chosen / chosen.sum(1, keepdims=True), atol=1e-15)
+
+
+def pin_group_limit_hand_built(o):
+    """Hand-worked group-limited selection for both group rules."""
+    g = _golden("group_limit_hand_built.json")
+    sel = np.array([g["sel"]])
+    # sigmoid^-1 of the wanted scores gives logits whose sigmoid is `sel`
+    # exactly enough; feed the scores through the bias with zero logits
+    # instead: s = 1/2 everywhere, bias = sel - 1/2.
+    E = sel.shape[1]
+    for rule, key in (("top2sum", "expected_ids_top2sum"), ("max", "expected_ids_max")):
+        r = o.route(np.zeros((1, E)), np.eye(E), g["k"], score="sigmoid",
+                    select_bias=sel[0] - 0.5, n_groups=g["n_groups"],
+                    topk_groups=g["topk_groups"], group_rule=rule)
+        assert r["ids"][0].tolist() == g[key], (rule, r["ids"])
+
+
+def pin_group_limit_invariants(o):
+    """No token uses more than topk_groups groups; one group, or keeping every
+    group, is plain top-k."""
+    inp = _tiny_inputs(6, T=40, E=16)
+    x, w = inp["x"], inp["w_router"]
+    r = o.route(x, w, 4, score="sigmoid", n_groups=4, topk_groups=2)
+    assert max(len(set((r["ids"][t] // 4).tolist())) for t in range(40)) <= 2
+    plain = o.route(x, w, 4, score="sigmoid")
+    for ng, tg in ((1, 1), (4, 4)):
+        rr = o.route(x, w, 4, score="sigmoid", n_groups=ng, topk_groups=tg)
+        assert (rr["ids"] == plain["ids"]).all()
+
+
+def pin_logit_bias_is_an_extra_feature(o):
+    """An additive per-expert logit bias b routes exactly like a router with
+    one more input feature fixed at 1 whose weight column is b (a Linear with
+    bias written as a bias-free Linear); z-loss and weights included."""
+    inp = _tiny_inputs(19, T=15, E=6)
+    b = _rng(20).normal(size=6) * 2.0
+    xa = np.concatenate([inp["x"], np.ones((15, 1))], axis=1)
+    wa = np.concatenate([inp["w_router"], b[:, None]], axis=1)
+    for score, renorm in (("softmax", False), ("softmax", True), ("sigmoid", True)):
+        r1 = o.route(inp["x"], inp["w_router"], 2, score=score, renormalize=renorm,
+                     logit_bias=b)
+        r2 = o.route(xa, wa, 2, score=score, renormalize=renorm)
+        assert (r1["ids"] == r2["ids"]).all()
+        assert np.allclose(r1["weights"], r2["weights"], rtol=0, atol=1e-14)
+        assert abs(r1["z"] - r2["z"]) < 1e-12
+    r0 = o.route(inp["x"], inp["w_router"], 2)
+    r1 = o.route(inp["x"], inp["w_router"], 2, logit_bias=b)
+    assert not (r0["ids"] == r1["ids"]).all()
+
+
+def pin_near_tie_flag(o):
+    """Exact ties are flagged; well separated scores are not."""
+    h = np.array([[1.0, 1.0, 0.0, -1.0], [3.0, 0.0, -3.0, -6.0]])
+    r = _route_logits(o, h, 1)
+    assert r["near_tie"].tolist() == [True, False]
+
+
+# ------------------------------------------------------------- aux ---------
+
+def pin_balance_uniform_is_one(o):
+    """Balance loss is exactly 1 at uniform assignment and uniform mean
+    probability (lab, 'Read the loss values correctly')."""
+    E = 6
+    base = np.array([1.3, -0.2, 0.7, 0.1, -1.1, 0.4])
+    h = np.stack([np.roll(base, t) for t in range(E)])   # each expert wins once
+    r = _route_logits(o, h, 1)
+    assert (np.bincount(r["ids"][:, 0], minlength=E) == 1).all()
+    assert abs(r["balance"] - 1.0) < 1e-14
+
+
+def pin_balance_collapsed_is_E(o):
+    """A fully collapsed router gives balance = E (book, aux-loss section)."""
+    E = 5
+    h = np.tile(np.array([200.0, 0.0, 0.0, 0.0, 0.0]), (7, 1))
+    r = _route_logits(o, h, 1)
+    assert abs(r["balance"] - E) < 1e-12
+
+
+def pin_z_constant_logits(o):
+    """For constant logits c over E experts, logsumexp = c + ln E, so the
+    z-loss is (c + ln E)^2."""
+    for c, E in ((0.0, 4), (1.5, 8), (-2.0, 3)):
+        r = _route_logits(o, np.full((3, E), c), 1)
+        assert abs(r["z"] - (c + math.log(E)) ** 2) < 1e-13
+
+
+def pin_counts_sum(o):
+    """Counts sum to T*k, also when a capacity later drops assignments."""
+    inp = _tiny_inputs(7, T=33, E=5)
+    for k in (1, 2, 5):
+        r = o.route(inp["x"], inp["w_router"], k)
+        assert int(r["counts"].sum()) == 33 * k
+        f = o.forward(inp, top_k=k, capacity_factor=0.5)
+        assert int(f["route"]["counts"].sum()) == 33 * k
+        assert f["n_kept"] == int(np.minimum(f["route"]["counts"], f["capacity"]).sum())
+
+
+# ------------------------------------------------------------- capacity ----
+
+def pin_capacity_exercise(o):
+    """Book exercise 2: capacity 768, 132 dropped when 900 tokens pick one expert."""
+    g = _golden("capacity_exercise.json")
+    ex = g["expected"]
+    E, k, N, cf = g["E"], g["k"], g["N"], g["capacity_factor"]
+    assert N * k // E == ex["avg_tokens_per_expert"]
+    C = o.capacity(cf, N, k, E)
+    assert C == ex["capacity"]
+    ids = np.zeros((g["hot_expert_tokens"], 1), dtype=np.int64)
+    keep = o.first_within_capacity(ids, E, C)
+    assert int((~keep).sum()) == ex["dropped_at_hot_expert"]
+    assert E * 2 * g["d_model"] * g["d_ff"] == ex["total_expert_params_two_matrix"]
+    assert k * 2 * g["d_model"] * g["d_ff"] == ex["active_expert_params_per_token"]
+
+
+def pin_capacity_small_cases(o):
+    """ceil and the floor of 1: 1.25*8192/64 = 160 exactly; tiny batches get 1."""
+    assert o.capacity(1.25, 8192, 1, 64) == 160
+    assert o.capacity(1.0, 10, 1, 4) == 3
+    assert o.capacity(0.01, 3, 1, 64) == 1
+    assert o.capacity(None, 10, 2, 4) is None
+
+
+def pin_capacity_hand_built(o):
+    """The hand-built keep mask, offsets and row order."""
+    g = _golden("capacity_hand_built.json")
+    ids = np.array(g["ids"])
+    keep = o.first_within_capacity(ids, g["E"], g["capacity"])
+    assert keep.tolist() == g["expected_keep"]
+    assert int((~keep).sum()) == g["expected_dropped"]
+    off, r2a, a2r = o.permutation(ids, keep, g["E"])
+    assert off.tolist() == g["expected_expert_offsets"]
+    assert r2a.tolist() == g["expected_row_to_assign"]
+    assert a2r.tolist() == g["expected_assign_to_row"]
+
+
+def pin_drop_is_rank_in_token_order(o):
+    """An assignment is dropped exactly when at least C earlier tokens chose
+    the same expert (a counting restatement of the first-come walk)."""
+    r = _rng(8)
+    E, T, k, C = 5, 60, 2, 9
+    ids = np.stack([r.choice(E, size=k, replace=False, p=[.4, .3, .1, .1, .1])
+                    for _ in range(T)])
+    keep = o.first_within_capacity(ids, E, C)
+    for t in range(T):
+        for s in range(k):
+            earlier = int((ids[:t] == ids[t, s]).sum())
+            assert keep[t, s] == (earlier < C)
+
+
+def pin_permutation_inverse(o):
+    """Permute then inverse-permute restores token order; rows are sorted by
+    (expert, token) and cover every kept assignment once."""
+    r = _rng(9)
+    E, T, k = 7, 50, 3
+    ids = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)])
+    keep = o.first_within_capacity(ids, E, 12)
+    off, r2a, a2r = o.permutation(ids, keep, E)
+    payload = np.arange(T * k) * 10 + 3
+    rows = payload[r2a]
+    back = np.full(T * k, -1)
+    back[r2a] = rows
+    assert (back[keep.reshape(-1)] == payload[keep.reshape(-1)]).all()
+    assert sorted(r2a.tolist()) == np.nonzero(keep.reshape(-1))[0].tolist()
+    e_of_row = ids.reshape(-1)[r2a]
+    t_of_row = r2a // k
+    assert all((e_of_row[i], t_of_row[i]) < (e_of_row[i + 1], t_of_row[i + 1])
+               for i in range(len(r2a) - 1))
+    for e in range(E):
+        assert (e_of_row[off[e]:off[e + 1]] == e).all()
+    assert ((a2r >= 0) == keep.reshape(-1)).all()
+
+
+def pin_empty_experts(o):
+    """Forced routes that leave experts empty run and give empty groups."""
+    inp = _tiny_inputs(10, T=6, E=5)
+    ids = np.array([[3, 1]] * 6)
+    w = np.full((6, 2), 0.5)
+    f = o.forward(inp, top_k=2, routing={"ids": ids, "weights": w})
+    off = f["expert_offsets"]
+    assert off.tolist() == [0, 0, 6, 6, 12, 12]
+    ref = o.brute_force_forward(inp, ids, w)
+    assert np.allclose(f["out"], ref, rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------- experts -----
+
+def pin_swiglu_scalar_closed_form(o):
+    """D = H = 1: FFN(z) = wd * (wg z) sigmoid(wg z) * (wu z)."""
+    for z, wg, wu, wd in ((2.0, 1.0, 1.0, 1.0), (-0.7, 1.9, -0.4, 2.2)):
+        y = o.swiglu_ffn(np.array([[z]]), np.array([[wg]]), np.array([[wu]]),
+                         np.array([[wd]]))
+        want = wd * (wg * z) / (1.0 + math.exp(-wg * z)) * (wu * z)
+        assert abs(y[0, 0] - want) < 1e-15
+
+
+def pin_swiglu_loops(o):
+    """Matrix form equals explicit sums over the Linear layout W[out, in]."""
+    r = _rng(11)
+    D, H = 4, 3
+    z = r.normal(size=(2, D))
+    wg, wu, wd = r.normal(size=(H, D)), r.normal(size=(H, D)), r.normal(size=(D, H))
+    y = o.swiglu_ffn(z, wg, wu, wd)
+    for n in range(2):
+        for d in range(D):
+            acc = 0.0
+            for j in range(H):
+                g = sum(wg[j, i] * z[n, i] for i in range(D))
+                u = sum(wu[j, i] * z[n, i] for i in range(D))
+                acc += wd[d, j] * (g / (1.0 + math.exp(-g))) * u
+            assert abs(y[n, d] - acc) < 1e-13
+
+
+def pin_identical_experts_are_dense(o):
+    """Identical experts with weights summing to 1 reproduce one dense FFN
+    (lab required test; book 'Sparse upcycling' at zero jitter), with or
+    without a shared expert added on top."""
+    inp = _tiny_inputs(12, T=11, E=4, shared=True)
+    for key in ("w_gate", "w_up", "w_down"):
+        inp[key] = np.repeat(inp[key][:1], 4, axis=0)
+    inp["w_router"] = _rng(13).normal(size=inp["w_router"].shape) * 1e-3
+    dense = o.swiglu_ffn(inp["x"], inp["w_gate"][0], inp["w_up"][0], inp["w_down"][0])
+    shared = o.swiglu_ffn(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"])
+    f = o.forward(inp, top_k=2)
+    assert np.allclose(f["out"], dense + shared, rtol=0, atol=1e-13)
+    no_shared = {k: v for k, v in inp.items() if not k.startswith("ws_")}
+    f = o.forward(no_shared, top_k=3)
+    assert np.allclose(f["out"], dense, rtol=0, atol=1e-13)
+
+
+def pin_dense_limit_mean(o):
+    """top_k = E with a zero router weights every expert 1/E: the output is the
+    mean of the E experts (the dense mixture of the book's first section)."""
+    inp = _tiny_inputs(14, T=5, E=4)
+    inp["w_router"] = np.zeros_like(inp["w_router"])
+    f = o.forward(inp, top_k=4)
+    each = [o.swiglu_ffn(inp["x"], inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
+            for e in range(4)]
+    assert np.allclose(f["out"], sum(each) / 4.0, rtol=0, atol=1e-14)
+
+
+def pin_forward_matches_brute_force(o):
+    """Dispatch/combine equals the token-by-token loop and the all-experts-then-
+    mask form on tiny shapes (lab 'Trace one token by hand')."""
+    for seed, k, shared in ((15, 2, False), (16, 3, True)):
+        inp = _tiny_inputs(seed, T=13, E=5, shared=shared)
+        f = o.forward(inp, top_k=k)
+        r = f["route"]
+        bf = o.brute_force_forward(inp, r["ids"], r["weights"])
+        assert np.allclose(f["out"], bf, rtol=0, atol=1e-12)
+        if not shared:
+            am = o.all_experts_then_mask(inp, r["ids"], r["weights"])
+            assert np.allclose(f["out"], am, rtol=0, atol=1e-12)
+
+
+def pin_dropped_tokens_get_zero(o):
+    """With a capacity, a token whose every slot is dropped gets exactly zero
+    from the routed branch; kept slots match the brute-force loop."""
+    inp = _tiny_inputs(17, T=20, E=3)
+    f = o.forward(inp, top_k=1, capacity_factor=0.3)
+    keep = f["keep"]
+    assert (~keep).any()
+    bf = o.brute_force_forward(inp, f["route"]["ids"], f["route"]["weights"], keep)
+    assert np.allclose(f["out"], bf, rtol=0, atol=1e-13)
+    assert (f["out"][~keep[:, 0]] == 0).all()
+
+
+def pin_subset_tokens(o):
+    """Evaluating a subset of tokens gives the same rows as the full forward."""
+    inp = _tiny_inputs(18, T=17, E=4, shared=True)
+    full = o.forward(inp, top_k=2, capacity_factor=0.8)
+    sub = o.forward(inp, top_k=2, capacity_factor=0.8, tokens=[16, 3, 0])
+    assert np.allclose(sub["out"], full["out"][[16, 3, 0]], rtol=0, atol=1e-15)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

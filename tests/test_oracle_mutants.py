@@ -1,0 +1,112 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+every one of them breaks at least one pin.  This shows that the pins constrain
+each step: a dropped term, a wrong sign or index, a swapped operand or a wrong
+order would not go unnoticed."""
+import importlib.util
+import os
+
+import pytest
+
+from tests.oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "moe_oracle.py")
+
+# (name, text in the oracle, replacement)
+MUTANTS = [
+    ("tie_to_higher_index",
+     'return np.argsort(-v, axis=-1, kind="stable")',
+     'return (v.shape[-1] - 1) - np.argsort(-v[..., ::-1], axis=-1, kind="stable")'),
+    ("no_renormalisation",
+     "weights = chosen / chosen.sum(axis=1, keepdims=True)",
+     "weights = chosen.copy()"),
+    ("route_scale_ignored",
+     "weights = weights * route_scale",
+     "weights = weights * 1.0"),
+    ("softmax_without_max_shift_sign",
+     "e = np.exp(h - m)",
+     "e = np.exp(m - h)"),
+    ("selection_bias_in_weights",
+     "chosen = np.take_along_axis(sc, ids, axis=1)",
+     "chosen = np.take_along_axis(sel, ids, axis=1)"),
+    ("group_rule_max_for_top2sum",
+     "gscore = srt[..., 0] + srt[..., 1]",
+     "gscore = srt[..., 0]"),
+    ("group_ascending",
+     "keep_groups = _order_desc(gscore)[:, :topk_groups]",
+     "keep_groups = _order_desc(-gscore)[:, :topk_groups]"),
+    ("balance_without_E",
+     "balance = E * float(np.sum(f * P))",
+     "balance = float(np.sum(f * P))"),
+    ("z_without_square",
+     "z = float(np.mean(logsumexp(h) ** 2))",
+     "z = float(np.mean(logsumexp(h)))"),
+    ("lse_missing_max",
+     "return m + np.log(np.exp(h - m[:, None]).sum(axis=-1))",
+     "return np.log(np.exp(h - m[:, None]).sum(axis=-1))"),
+    ("capacity_floor",
+     "return max(1, math.ceil(capacity_factor * (T * top_k) / E))",
+     "return max(1, math.floor(capacity_factor * (T * top_k) / E))"),
+    ("capacity_off_by_one",
+     "if used[e] < cap:",
+     "if used[e] <= cap:"),
+    ("slot_major_priority",
+     "    for t in range(T):\n        for s in range(k):\n            e = int(ids[t, s])\n            if used[e]",
+     "    for s in range(k):\n        for t in range(T):\n            e = int(ids[t, s])\n            if used[e]"),
+    ("permutation_token_major",
+     "order = np.lexsort((tok, flat_e[a]))",
+     "order = np.lexsort((flat_e[a], tok))"),
+    ("silu_missing_gate_factor",
+     "act = g * sigmoid(g) * u",
+     "act = sigmoid(g) * u"),
+    ("gate_and_up_swapped_roles",
+     "act = g * sigmoid(g) * u",
+     "act = u * sigmoid(u) * g"),
+    ("down_transposed",
+     "return act @ np.asarray(w_down, dtype=np.float64).T",
+     "return act @ np.asarray(w_down, dtype=np.float64).reshape(-1, np.asarray(w_down).shape[0])"),
+    ("weight_not_applied",
+     "Y[r, s] = np.asarray(weights)[tokens[r], s][:, None] * out",
+     "Y[r, s] = out"),
+    ("shared_expert_dropped",
+     "    if shared is not None:\n        out = out + shared",
+     "    if shared is not None:\n        out = out + 0.0 * shared"),
+    ("router_bias_ignored",
+     "h = h + np.asarray(logit_bias, dtype=np.float64)[None, :]",
+     "h = h + 0.0"),
+]
+
+
+def _load_mutant(old, new):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site not unique/present: {old!r}"
+    spec = importlib.util.spec_from_loader("oracle_mutant", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _failing_pins(mod):
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception:  # AssertionError or a crash both count as caught
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    mod = _load_mutant(old, new)
+    assert _failing_pins(mod), f"planted mistake {name!r} passed every pin"
+
+
+def test_unmutated_copy_passes():
+    with open(SRC) as f:
+        src = f.read()
+    spec = importlib.util.spec_from_loader("oracle_copy", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(src, "oracle_copy", "exec"), mod.__dict__)
+    assert _failing_pins(mod) == []
