@@ -1,0 +1,194 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) top-k token-choice MoE-layer forward.
+ *
+ * The layer (as defined on "Lab: build a tiny MoE in PyTorch", sections
+ * "The contract" and "Full implementation", and "2.9 Mixture-of-Experts (MoE)
+ * Architectures", section "A Toy MoE Layer From Scratch"):
+ *
+ *   h      = x W_r^T (+ logit_bias)                               router
+ *   score  = softmax(h) over experts, or sigmoid(h)               fp32
+ *   sel    = score (+ select_bias), optionally group-limited      selection
+ *   ids    = top-k(sel), descending, ties to the lower index
+ *   w      = route_scale * score[ids] / sum(score[ids])  (renormalize)
+ *          | route_scale * score[ids]                    (otherwise)
+ *   keep   = first-come per expert in token order, at most C (capacity)
+ *   out[t] = sum_{kept s} w[t,s] * FFN_{ids[t,s]}(x[t])  (+ FFN_shared(x[t]))
+ *   FFN(z) = W_down (silu(W_gate z) * (W_up z))
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major
+ *    and contiguous.  The library never allocates or frees memory; scratch
+ *    comes from the caller's workspace of moe_workspace_bytes(cfg) bytes
+ *    (256-byte aligned).
+ *  - Tokens are flattened: t = b*S + s for an input of shape (B, S, D).
+ *    Assignment index a = t*top_k + slot.
+ *  - Weights use the nn.Linear layout per expert: w_gate, w_up [E, H, D];
+ *    w_down [E, D, H]; router [E, D]; shared expert [Hs, D], [Hs, D], [D, Hs].
+ *  - Calls are asynchronous on `stream`: the host validates arguments,
+ *    enqueues kernels and returns; it never waits for or reads device data.
+ *    Outputs are undefined if a call returns an error.  Arguments are checked
+ *    before anything is enqueued, so an error status means nothing ran.
+ *  - Calls on different streams with different workspaces may run
+ *    concurrently; two calls sharing one workspace must be stream-ordered.
+ *  - gfx950 only.  bf16 paths need D and H to be multiples of 64.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a size or switch outside its documented range   */
+  MOE_ERR_NULL_PTR = 2,    /* a required pointer is NULL                      */
+  MOE_ERR_UNSUPPORTED = 3, /* valid in principle, not implemented (dtype/size) */
+  MOE_ERR_WORKSPACE = 4,   /* workspace NULL, misaligned or too small         */
+  MOE_ERR_DEVICE = 5,      /* a pointer is not device memory of this device   */
+  MOE_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed      */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+/* Group score for group-limited routing: sum of the two largest selection
+ * scores of the group, or the largest one. */
+typedef enum { MOE_GROUP_TOP2SUM = 0, MOE_GROUP_MAX = 1 } moe_group_rule;
+
+typedef struct moe_config {
+  int32_t T;            /* tokens (B*S), >= 1                                  */
+  int32_t D;            /* d_model                                             */
+  int32_t H;            /* d_hidden of each routed expert                      */
+  int32_t E;            /* routed experts, 1..256                              */
+  int32_t top_k;        /* 1 <= top_k <= E, and <= 32                          */
+  int32_t H_shared;     /* d_hidden of the always-on shared expert; 0 = none   */
+  int32_t act_dtype;    /* moe_dtype of x, expert weights and the output       */
+  int32_t router_dtype; /* moe_dtype of W_r (fp32 allowed with bf16 x)         */
+  int32_t score_func;   /* moe_score                                           */
+  int32_t renormalize;  /* 1: divide by the sum of the k selected scores       */
+  float route_scale;    /* multiplies the final weights (1.0 if unused)        */
+  int32_t n_groups;     /* contiguous expert groups (1 = no group limit)       */
+  int32_t topk_groups;  /* groups each token may use, 1..n_groups              */
+  int32_t group_rule;   /* moe_group_rule                                      */
+  double capacity_factor; /* <= 0: dropless; else C = max(1, ceil(cf*T*k/E))   */
+} moe_config;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(moe_status s);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Validate the configuration alone (no pointers).  Mirrors the layer's
+ * constructor checks: top_k must lie in [1, E] ("Lab: build a tiny MoE in
+ * PyTorch", "Full implementation"); group settings must divide E. */
+moe_status moe_check_config(const moe_config* cfg);
+
+/* Capacity per expert for this configuration: max(1, ceil(cf*T*k/E)) in
+ * double precision ("Add a capacity limit" on the lab page; "A Toy MoE Layer
+ * From Scratch" on the book page), or T*k when dropless.  Returns -1 if the
+ * configuration is invalid. */
+int32_t moe_capacity(const moe_config* cfg);
+
+/* Upper bound on expert-major rows: min(T*k, E*C) (T*k when dropless). */
+int32_t moe_max_rows(const moe_config* cfg);
+
+/* Workspace bytes that suffice for every entry point below with this
+ * configuration (0 if the configuration is invalid). */
+size_t moe_workspace_bytes(const moe_config* cfg);
+
+/* Routing ("Full implementation" on the lab page: router, fp32 softmax,
+ * top-k, renormalised weights, bincount, balance and z losses; "The Router"
+ * on the book page for the selection-only bias; NeMo Gate attributes
+ * score_func / n_groups / topk_groups / route_scale).
+ *   x            [T, D]   act_dtype
+ *   w_router     [E, D]   router_dtype
+ *   logit_bias   [E] f32 or NULL: added to the logits (softmax input, z-loss)
+ *   select_bias  [E] f32 or NULL: added to the scores for selection only
+ *   expert_ids   [T, k] int32 out: slot j = j-th largest selection score
+ *   gate_w       [T, k] f32 out
+ *   counts       [E] int32 out: assignments per expert before any drop
+ *   aux          [2] f32 out or NULL: {balance = E*sum f_e P_e, z = mean lse^2}
+ *   mean_prob    [E] f32 out or NULL: P_e = mean_t p_te (sigmoid: s_te/sum s)
+ * Deterministic: repeated calls give identical bits. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* logit_bias, const float* select_bias,
+                     int32_t* expert_ids, float* gate_w, int32_t* counts,
+                     float* aux, float* mean_prob, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* Dispatch bookkeeping ("Add a capacity limit" on the lab page: keep the
+ * first C assignments of each expert in token order; the sorted expert-major
+ * token list of "MoE in Practice" on the book page).
+ *   expert_ids     [T, k] int32 in, values in [0, E); a token's k IDs distinct
+ *   capacity       > 0: per-expert limit; <= 0: dropless
+ *   expert_offsets [E+1] int32 out: kept rows of expert e are
+ *                  [offsets[e], offsets[e+1])
+ *   row_to_assign  [max_rows] int32 out: assignment a of each row, rows sorted
+ *                  by (expert, token); entries past n_kept are unspecified
+ *   assign_to_row  [T*k] int32 out: row of assignment a, -1 if dropped
+ *   n_kept         [1] int32 out (device)
+ * Integer-only and bit-exact. */
+moe_status moe_permute(const moe_config* cfg, const int32_t* expert_ids,
+                       int32_t capacity, int32_t* expert_offsets,
+                       int32_t* row_to_assign, int32_t* assign_to_row,
+                       int32_t* n_kept, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Grouped SwiGLU experts ("Full implementation" on the lab page,
+ * SwiGLUExpert, and its per-expert gather / run / scale loop):
+ *   y_rows[r] = g(r) * W_down,e (silu(W_gate,e x_t) * (W_up,e x_t))
+ * for every row r of group e, t = row_to_assign[r] / top_k and
+ * g(r) = gate_w[row_to_assign[r]] (1 if gate_w is NULL).
+ *   n_experts, hidden  groups in this call and their d_hidden
+ *   row_to_assign      [max_rows] int32, or NULL for the identity map
+ *                      (row r = token r, one group of T rows: shared expert)
+ *   expert_offsets     [n_experts+1] int32 (device), NULL with identity
+ *   max_rows           host bound on the rows (grid size); rows beyond
+ *                      offsets[n_experts] are neither read nor written
+ *   w_gate, w_up       [n_experts, hidden, D]; w_down [n_experts, D, hidden]
+ *   y_rows             [max_rows, D] act_dtype out
+ * fp32 accumulation; silu(g)*u is rounded once to act_dtype between the two
+ * GEMMs; the gate weight is applied in fp32 before the final rounding. */
+moe_status moe_grouped_swiglu(const moe_config* cfg, int32_t n_experts, int32_t hidden,
+                              const void* x, const int32_t* row_to_assign,
+                              const int32_t* expert_offsets, int32_t max_rows,
+                              const float* gate_w, const void* w_gate,
+                              const void* w_up, const void* w_down, void* y_rows,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Combine ("Full implementation" on the lab page, index_add_ back to token
+ * order; "Add a shared expert"):
+ *   out[t] = sum_{s=0..k-1, assign_to_row[t*k+s] >= 0} y_rows[assign_to_row[t*k+s]]
+ *            (+ shared_rows[t])
+ * accumulated in fp32 in slot order, one rounding to act_dtype.  No atomics:
+ * the result is deterministic.  A token with every slot dropped gets 0
+ * (plus its shared-expert row). */
+moe_status moe_combine(const moe_config* cfg, const void* y_rows,
+                       const int32_t* assign_to_row, const void* shared_rows,
+                       void* out, hipStream_t stream);
+
+/* The whole forward: moe_route, moe_permute, moe_grouped_swiglu (routed and
+ * shared expert) and moe_combine, stream-ordered, with no host
+ * synchronisation.  w_shared_* may be NULL when cfg->H_shared == 0.  The
+ * optional outputs expert_ids [T,k], gate_w [T,k], counts [E] and aux [2]
+ * receive the routing results when non-NULL. */
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* logit_bias, const float* select_bias,
+                       const void* w_gate, const void* w_up, const void* w_down,
+                       const void* w_shared_gate, const void* w_shared_up,
+                       const void* w_shared_down, void* out, int32_t* expert_ids,
+                       float* gate_w, int32_t* counts, float* aux, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

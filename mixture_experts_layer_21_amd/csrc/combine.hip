@@ -1,0 +1,118 @@
+// Combine: out[t] = sum over kept slots (slot order) of the weighted expert
+// rows, plus the shared-expert row; fp32 accumulation, one rounding.
+//
+// This is the index_add_ step of "Lab: build a tiny MoE in PyTorch" ("Full
+// implementation") written as a gather: each output row is owned by one
+// thread group, so there are no atomics and the sum order is fixed.  The
+// shared expert joins as in "Add a shared expert" on the same page.
+// HBM-bound: each thread moves 16-byte chunks along d_model.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int NTHREADS = 256;
+
+template <typename T>
+struct Vec16;  // 16 bytes of T
+template <>
+struct Vec16<uint16_t> {
+  static constexpr int N = 8;
+};
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+};
+
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, float (&v)[Vec16<T>::N]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  if constexpr (Vec16<T>::N == 8) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(q.x);
+    v[1] = __uint_as_float(q.y);
+    v[2] = __uint_as_float(q.z);
+    v[3] = __uint_as_float(q.w);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store16(T* p, const float (&v)[Vec16<T>::N]) {
+  uint4 q;
+  if constexpr (Vec16<T>::N == 8) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
+    q = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    q = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                   __float_as_uint(v[3]));
+  }
+  *reinterpret_cast<uint4*>(p) = q;
+}
+
+// Block = TPB tokens x (NTHREADS / TPB) threads per token.
+template <typename T>
+__global__ __launch_bounds__(NTHREADS) void combine_kernel(CombineParams p, int tpb) {
+  constexpr int N = Vec16<T>::N;
+  const T* y = static_cast<const T*>(p.y_rows);
+  const T* sh = static_cast<const T*>(p.shared_rows);
+  T* out = static_cast<T*>(p.out);
+  __shared__ int rows_lds[64 * kMaxTopK];
+  const int per_tok = NTHREADS / tpb;
+  const int tl = threadIdx.x / per_tok;
+  const int t = blockIdx.x * tpb + tl;
+  const int sub = threadIdx.x % per_tok;
+  for (int i = threadIdx.x; i < tpb * p.k; i += NTHREADS) {
+    const int tt = blockIdx.x * tpb + i / p.k;
+    rows_lds[i] = tt < p.T ? p.assign_to_row[(size_t)blockIdx.x * tpb * p.k + i] : -1;
+  }
+  __syncthreads();
+  if (t >= p.T) return;
+  const int* rows = rows_lds + tl * p.k;
+  const int nchunk = p.D / N;
+  for (int c = sub; c < nchunk; c += per_tok) {
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.f;
+    for (int s = 0; s < p.k; ++s) {
+      if (rows[s] < 0) continue;
+      float v[N];
+      load16<T>(y + (size_t)rows[s] * p.D + (size_t)c * N, v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += v[i];
+    }
+    if (sh) {
+      float v[N];
+      load16<T>(sh + (size_t)t * p.D + (size_t)c * N, v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += v[i];
+    }
+    store16<T>(out + (size_t)t * p.D + (size_t)c * N, acc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s) {
+  const int n = bf16 ? 8 : 4;
+  const int nchunk = p.D / n;
+  int tpb = 1;  // tokens per block: keep at least ~nchunk threads per token
+  while (tpb < 64 && NTHREADS / (tpb * 2) >= nchunk) tpb *= 2;
+  const dim3 grid((p.T + tpb - 1) / tpb), block(NTHREADS);
+  if (bf16)
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, block, 0, s, p, tpb);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, p, tpb);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,89 @@
+// Internal launchers of the gfx950 kernels.  Host code in moe_api.hip checks
+// every argument before calling these; the launchers only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens per routing block; also the granularity of the per-block expert
+// histograms that the permutation scans.
+constexpr int kRouteTile = 32;
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxGroups = 64;
+
+struct RouteParams {
+  int T, D, E, k;
+  int score_func, renormalize, n_groups, topk_groups, group_rule;
+  float route_scale;
+  int act_bf16, router_bf16;
+  const void* x;
+  const void* w_router;
+  const float* logit_bias;
+  const float* select_bias;
+  int32_t* ids;       // [T*k]
+  float* gate_w;      // [T*k]
+  int32_t* hist;      // [nblk*E]  per-block expert histogram
+  float* pe_part;     // [nblk*E]  per-block sums of P_e terms
+  float* z_part;      // [nblk]    per-block sums of lse^2
+};
+
+struct FinalizeParams {
+  int T, E, k, nblk;
+  int capacity;              // <= 0: dropless
+  const int32_t* hist;       // [nblk*E]
+  const float* pe_part;      // [nblk*E] or null (no aux)
+  const float* z_part;       // [nblk] or null
+  int32_t* counts;           // [E] or null
+  float* aux;                // [2] or null
+  float* mean_prob;          // [E] or null
+  int32_t* block_base;       // [nblk*E] or null (no permutation scan)
+  int32_t* expert_offsets;   // [E+1] or null
+  int32_t* n_kept;           // [1] or null
+};
+
+struct ScatterParams {
+  int T, E, k, capacity;
+  const int32_t* ids;
+  const int32_t* block_base;
+  const int32_t* expert_offsets;
+  int32_t* row_to_assign;
+  int32_t* assign_to_row;
+};
+
+struct GemmParams {
+  int T, D, k;               // tokens, d_model, top_k of the assignment index
+  int n_groups;              // experts in this call
+  int hidden;                // H of this call
+  int max_rows;
+  const void* x;             // [T, D]
+  const int32_t* row_to_assign;   // null: identity rows
+  const int32_t* expert_offsets;  // null: one group of T rows
+  const float* gate_w;       // null: weight 1
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  void* hbuf;                // [max_rows, hidden]
+  void* y;                   // [max_rows, D]
+};
+
+struct CombineParams {
+  int T, D, k;
+  const void* y_rows;
+  const int32_t* assign_to_row;
+  const void* shared_rows;
+  void* out;
+};
+
+hipError_t launch_route(const RouteParams& p, hipStream_t s);
+hipError_t launch_hist(int T, int E, int k, const int32_t* ids, int32_t* hist, hipStream_t s);
+hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s);
+hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
+hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
+
+inline int route_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
+
+}  // namespace moe

@@ -1,0 +1,499 @@
+// C ABI of the MoE-layer forward: argument checks, workspace layout and the
+// stream-ordered launch sequence.  Declarations and semantics: include/moe.h.
+#include <math.h>
+#include <stdarg.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t esize(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool is_dtype(int d) { return d == MOE_F32 || d == MOE_BF16; }
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_NULL_PTR, "config is NULL");
+  if (c->T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1 (got %d)", c->T);
+  if (c->D < 1 || c->H < 1) return fail(MOE_ERR_INVALID_ARG, "D and H must be >= 1");
+  if (c->E < 1 || c->E > moe::kMaxExperts)
+    return fail(MOE_ERR_INVALID_ARG, "E must be in [1, %d] (got %d)", moe::kMaxExperts, c->E);
+  if (c->top_k < 1 || c->top_k > c->E)
+    return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, n_experts] (got %d, E=%d)", c->top_k,
+                c->E);
+  if (c->top_k > moe::kMaxTopK)
+    return fail(MOE_ERR_UNSUPPORTED, "top_k > %d is not supported", moe::kMaxTopK);
+  if (c->H_shared < 0) return fail(MOE_ERR_INVALID_ARG, "H_shared must be >= 0");
+  if (!is_dtype(c->act_dtype) || !is_dtype(c->router_dtype))
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (c->score_func != MOE_SCORE_SOFTMAX && c->score_func != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "unknown score function %d", c->score_func);
+  if (c->renormalize != 0 && c->renormalize != 1)
+    return fail(MOE_ERR_INVALID_ARG, "renormalize must be 0 or 1");
+  if (!(isfinite(c->route_scale) && c->route_scale > 0.f))
+    return fail(MOE_ERR_INVALID_ARG, "route_scale must be finite and > 0");
+  if (c->n_groups < 1) return fail(MOE_ERR_INVALID_ARG, "n_groups must be >= 1");
+  if (c->n_groups > 1) {
+    if (c->n_groups > moe::kMaxGroups)
+      return fail(MOE_ERR_UNSUPPORTED, "n_groups > %d is not supported", moe::kMaxGroups);
+    if (c->E % c->n_groups)
+      return fail(MOE_ERR_INVALID_ARG, "n_groups (%d) must divide E (%d)", c->n_groups, c->E);
+    if (c->topk_groups < 1 || c->topk_groups > c->n_groups)
+      return fail(MOE_ERR_INVALID_ARG, "topk_groups must be in [1, n_groups]");
+    if (c->group_rule != MOE_GROUP_TOP2SUM && c->group_rule != MOE_GROUP_MAX)
+      return fail(MOE_ERR_INVALID_ARG, "unknown group rule %d", c->group_rule);
+    const int gsz = c->E / c->n_groups;
+    if (c->group_rule == MOE_GROUP_TOP2SUM && gsz < 2)
+      return fail(MOE_ERR_INVALID_ARG, "the top-2-sum group rule needs >= 2 experts per group");
+    if (c->top_k > c->topk_groups * gsz)
+      return fail(MOE_ERR_INVALID_ARG, "top_k exceeds the experts of the allowed groups");
+  }
+  if (!isfinite(c->capacity_factor))
+    return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
+  if ((long long)c->T * c->top_k > 0x7fffffffLL)
+    return fail(MOE_ERR_UNSUPPORTED, "T*top_k exceeds int32");
+  if (c->act_dtype == MOE_BF16) {
+    if (c->D % 64 || c->H % 64 || c->H_shared % 64)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 path needs D, H, H_shared multiples of 64");
+  } else if (c->D % 4) {
+    return fail(MOE_ERR_UNSUPPORTED, "fp32 path needs D a multiple of 4");
+  }
+  return MOE_OK;
+}
+
+long long capacity_of(const moe_config* c) {
+  const long long tk = (long long)c->T * c->top_k;
+  if (!(c->capacity_factor > 0.0)) return tk;
+  const double v = ceil(c->capacity_factor * (double)tk / (double)c->E);
+  long long cap = v < 1.0 ? 1 : (v > (double)tk ? tk : (long long)v);
+  return cap;
+}
+
+long long max_rows_of(const moe_config* c) {
+  const long long tk = (long long)c->T * c->top_k;
+  if (!(c->capacity_factor > 0.0)) return tk;
+  return std::min(tk, (long long)c->E * capacity_of(c));
+}
+
+struct Layout {
+  size_t ids, gate_w, counts, aux, hist, pe_part, z_part, block_base, offsets, n_kept, r2a,
+      a2r, hbuf, y, shared_y, total;
+};
+
+Layout layout_of(const moe_config* c) {
+  Layout L{};
+  const size_t T = c->T, k = c->top_k, E = c->E, D = c->D;
+  const size_t nblk = moe::route_blocks(c->T);
+  const size_t rows = (size_t)max_rows_of(c);
+  const size_t es = esize(c->act_dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.ids = take(T * k * 4);
+  L.gate_w = take(T * k * 4);
+  L.counts = take(E * 4);
+  L.aux = take(2 * 4);
+  L.hist = take(nblk * E * 4);
+  L.pe_part = take(nblk * E * 4);
+  L.z_part = take(nblk * 4);
+  L.block_base = take(nblk * E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.n_kept = take(4);
+  L.r2a = take(std::max<size_t>(rows, 1) * 4);
+  L.a2r = take(T * k * 4);
+  L.hbuf = take(std::max(rows * (size_t)c->H, T * (size_t)c->H_shared) * es);
+  L.y = take(rows * D * es);
+  L.shared_y = take(c->H_shared ? T * D * es : 0);
+  L.total = off;
+  return L;
+}
+
+moe_status check_ws(const moe_config* c, void* ws, size_t bytes) {
+  const size_t need = layout_of(c).total;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", bytes, need);
+  return MOE_OK;
+}
+
+// The pointer must be device (or managed) memory of the current device.
+moe_status check_dev(const void* p, const char* name, bool required) {
+  if (!p) {
+    if (required) return fail(MOE_ERR_NULL_PTR, "%s is NULL", name);
+    return MOE_OK;
+  }
+  hipPointerAttribute_t a;
+  memset(&a, 0, sizeof a);
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_DEVICE, "%s is not a HIP allocation", name);
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed");
+  if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged)
+    return fail(MOE_ERR_DEVICE, "%s is not device memory", name);
+  if (a.device != dev)
+    return fail(MOE_ERR_DEVICE, "%s lives on device %d, current device is %d", name, a.device,
+                dev);
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                   \
+  do {                                  \
+    const moe_status _s = (expr);       \
+    if (_s != MOE_OK) return _s;        \
+  } while (0)
+
+moe_status hip_ok(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe::RouteParams route_params(const moe_config* c, const void* x, const void* w_router,
+                              const float* lb, const float* sb, int32_t* ids, float* gw,
+                              void* ws, const Layout& L) {
+  moe::RouteParams p{};
+  p.T = c->T;
+  p.D = c->D;
+  p.E = c->E;
+  p.k = c->top_k;
+  p.score_func = c->score_func;
+  p.renormalize = c->renormalize;
+  p.n_groups = c->n_groups;
+  p.topk_groups = c->topk_groups;
+  p.group_rule = c->group_rule;
+  p.route_scale = c->route_scale;
+  p.act_bf16 = c->act_dtype == MOE_BF16;
+  p.router_bf16 = c->router_dtype == MOE_BF16;
+  p.x = x;
+  p.w_router = w_router;
+  p.logit_bias = lb;
+  p.select_bias = sb;
+  p.ids = ids;
+  p.gate_w = gw;
+  p.hist = at<int32_t>(ws, L.hist);
+  p.pe_part = at<float>(ws, L.pe_part);
+  p.z_part = at<float>(ws, L.z_part);
+  return p;
+}
+
+moe::GemmParams gemm_params(const moe_config* c, int n_groups, int hidden, const void* x,
+                            const int32_t* r2a, const int32_t* offsets, int max_rows,
+                            const float* gw, const void* wg, const void* wu, const void* wd,
+                            void* hbuf, void* y) {
+  moe::GemmParams p{};
+  p.T = c->T;
+  p.D = c->D;
+  p.k = c->top_k;
+  p.n_groups = n_groups;
+  p.hidden = hidden;
+  p.max_rows = max_rows;
+  p.x = x;
+  p.row_to_assign = r2a;
+  p.expert_offsets = offsets;
+  p.gate_w = gw;
+  p.w_gate = wg;
+  p.w_up = wu;
+  p.w_down = wd;
+  p.hbuf = hbuf;
+  p.y = y;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_NULL_PTR: return "MOE_ERR_NULL_PTR";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_check_config(const moe_config* cfg) {
+  MOE_TRY(check_config(cfg));
+  return ok();
+}
+
+int32_t moe_capacity(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return -1;
+  return (int32_t)capacity_of(cfg);
+}
+
+int32_t moe_max_rows(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return -1;
+  return (int32_t)max_rows_of(cfg);
+}
+
+size_t moe_workspace_bytes(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return layout_of(cfg).total;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* logit_bias, const float* select_bias, int32_t* expert_ids,
+                     float* gate_w, int32_t* counts, float* aux, float* mean_prob,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  if (!x || !w_router || !expert_ids || !gate_w || !counts)
+    return fail(MOE_ERR_NULL_PTR, "moe_route: x, w_router, expert_ids, gate_w, counts required");
+  MOE_TRY(check_ws(cfg, workspace, workspace_bytes));
+  MOE_TRY(check_dev(x, "x", true));
+  MOE_TRY(check_dev(w_router, "w_router", true));
+  MOE_TRY(check_dev(logit_bias, "logit_bias", false));
+  MOE_TRY(check_dev(select_bias, "select_bias", false));
+  MOE_TRY(check_dev(expert_ids, "expert_ids", true));
+  MOE_TRY(check_dev(gate_w, "gate_w", true));
+  MOE_TRY(check_dev(counts, "counts", true));
+  MOE_TRY(check_dev(aux, "aux", false));
+  MOE_TRY(check_dev(mean_prob, "mean_prob", false));
+  MOE_TRY(check_dev(workspace, "workspace", true));
+  const Layout L = layout_of(cfg);
+  const moe::RouteParams rp =
+      route_params(cfg, x, w_router, logit_bias, select_bias, expert_ids, gate_w, workspace, L);
+  MOE_TRY(hip_ok(moe::launch_route(rp, stream), "route kernel"));
+  moe::FinalizeParams fp{};
+  fp.T = cfg->T;
+  fp.E = cfg->E;
+  fp.k = cfg->top_k;
+  fp.nblk = moe::route_blocks(cfg->T);
+  fp.capacity = 0;
+  fp.hist = rp.hist;
+  fp.pe_part = rp.pe_part;
+  fp.z_part = rp.z_part;
+  fp.counts = counts;
+  fp.aux = aux;
+  fp.mean_prob = mean_prob;
+  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
+  return ok();
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* expert_ids, int32_t capacity,
+                       int32_t* expert_offsets, int32_t* row_to_assign, int32_t* assign_to_row,
+                       int32_t* n_kept, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  if (!expert_ids || !expert_offsets || !row_to_assign || !assign_to_row || !n_kept)
+    return fail(MOE_ERR_NULL_PTR, "moe_permute: every array argument is required");
+  MOE_TRY(check_ws(cfg, workspace, workspace_bytes));
+  MOE_TRY(check_dev(expert_ids, "expert_ids", true));
+  MOE_TRY(check_dev(expert_offsets, "expert_offsets", true));
+  MOE_TRY(check_dev(row_to_assign, "row_to_assign", true));
+  MOE_TRY(check_dev(assign_to_row, "assign_to_row", true));
+  MOE_TRY(check_dev(n_kept, "n_kept", true));
+  MOE_TRY(check_dev(workspace, "workspace", true));
+  const Layout L = layout_of(cfg);
+  int32_t* hist = at<int32_t>(workspace, L.hist);
+  int32_t* base = at<int32_t>(workspace, L.block_base);
+  MOE_TRY(hip_ok(moe::launch_hist(cfg->T, cfg->E, cfg->top_k, expert_ids, hist, stream),
+                 "hist kernel"));
+  moe::FinalizeParams fp{};
+  fp.T = cfg->T;
+  fp.E = cfg->E;
+  fp.k = cfg->top_k;
+  fp.nblk = moe::route_blocks(cfg->T);
+  fp.capacity = capacity > 0 ? capacity : 0;
+  fp.hist = hist;
+  fp.block_base = base;
+  fp.expert_offsets = expert_offsets;
+  fp.n_kept = n_kept;
+  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
+  moe::ScatterParams sp{cfg->T, cfg->E, cfg->top_k, fp.capacity, expert_ids, base,
+                        expert_offsets, row_to_assign, assign_to_row};
+  MOE_TRY(hip_ok(moe::launch_scatter(sp, stream), "scatter kernel"));
+  return ok();
+}
+
+moe_status moe_grouped_swiglu(const moe_config* cfg, int32_t n_experts, int32_t hidden,
+                              const void* x, const int32_t* row_to_assign,
+                              const int32_t* expert_offsets, int32_t max_rows,
+                              const float* gate_w, const void* w_gate, const void* w_up,
+                              const void* w_down, void* y_rows, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  if (!x || !w_gate || !w_up || !w_down || !y_rows)
+    return fail(MOE_ERR_NULL_PTR, "moe_grouped_swiglu: x, weights and y_rows are required");
+  const bool identity = row_to_assign == nullptr;
+  if (identity) {
+    if (expert_offsets || n_experts != 1 || max_rows != cfg->T)
+      return fail(MOE_ERR_INVALID_ARG,
+                  "identity rows need expert_offsets=NULL, n_experts=1, max_rows=T");
+  } else {
+    if (!expert_offsets) return fail(MOE_ERR_NULL_PTR, "expert_offsets is NULL");
+    if (n_experts < 1 || n_experts > moe::kMaxExperts)
+      return fail(MOE_ERR_INVALID_ARG, "n_experts must be in [1, %d]", moe::kMaxExperts);
+    if (max_rows < 0 || (long long)max_rows > (long long)cfg->T * cfg->top_k)
+      return fail(MOE_ERR_INVALID_ARG, "max_rows must be in [0, T*top_k]");
+  }
+  if (hidden < 1) return fail(MOE_ERR_INVALID_ARG, "hidden must be >= 1");
+  if (cfg->act_dtype == MOE_BF16 && hidden % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 path needs hidden a multiple of 64");
+  const size_t hb_need = (size_t)std::max(max_rows, 0) * hidden * esize(cfg->act_dtype);
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (workspace_bytes < hb_need)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                hb_need);
+  MOE_TRY(check_dev(x, "x", true));
+  MOE_TRY(check_dev(row_to_assign, "row_to_assign", false));
+  MOE_TRY(check_dev(expert_offsets, "expert_offsets", false));
+  MOE_TRY(check_dev(gate_w, "gate_w", false));
+  MOE_TRY(check_dev(w_gate, "w_gate", true));
+  MOE_TRY(check_dev(w_up, "w_up", true));
+  MOE_TRY(check_dev(w_down, "w_down", true));
+  MOE_TRY(check_dev(y_rows, "y_rows", true));
+  MOE_TRY(check_dev(workspace, "workspace", true));
+  if (max_rows == 0) return ok();
+  const moe::GemmParams gp =
+      gemm_params(cfg, n_experts, hidden, x, row_to_assign, expert_offsets, max_rows, gate_w,
+                  w_gate, w_up, w_down, workspace, y_rows);
+  MOE_TRY(hip_ok(moe::launch_grouped_swiglu(gp, cfg->act_dtype == MOE_BF16, stream),
+                 "grouped swiglu kernels"));
+  return ok();
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_rows, const int32_t* assign_to_row,
+                       const void* shared_rows, void* out, hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  if (!y_rows || !assign_to_row || !out)
+    return fail(MOE_ERR_NULL_PTR, "moe_combine: y_rows, assign_to_row and out are required");
+  MOE_TRY(check_dev(y_rows, "y_rows", true));
+  MOE_TRY(check_dev(assign_to_row, "assign_to_row", true));
+  MOE_TRY(check_dev(shared_rows, "shared_rows", false));
+  MOE_TRY(check_dev(out, "out", true));
+  moe::CombineParams p{cfg->T, cfg->D, cfg->top_k, y_rows, assign_to_row, shared_rows, out};
+  MOE_TRY(hip_ok(moe::launch_combine(p, cfg->act_dtype == MOE_BF16, stream), "combine kernel"));
+  return ok();
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* logit_bias, const float* select_bias, const void* w_gate,
+                       const void* w_up, const void* w_down, const void* w_shared_gate,
+                       const void* w_shared_up, const void* w_shared_down, void* out,
+                       int32_t* expert_ids, float* gate_w, int32_t* counts, float* aux,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !out)
+    return fail(MOE_ERR_NULL_PTR, "moe_forward: x, w_router, expert weights and out required");
+  if (cfg->H_shared > 0 && (!w_shared_gate || !w_shared_up || !w_shared_down))
+    return fail(MOE_ERR_NULL_PTR, "moe_forward: H_shared > 0 needs the shared-expert weights");
+  MOE_TRY(check_ws(cfg, workspace, workspace_bytes));
+  MOE_TRY(check_dev(x, "x", true));
+  MOE_TRY(check_dev(w_router, "w_router", true));
+  MOE_TRY(check_dev(logit_bias, "logit_bias", false));
+  MOE_TRY(check_dev(select_bias, "select_bias", false));
+  MOE_TRY(check_dev(w_gate, "w_gate", true));
+  MOE_TRY(check_dev(w_up, "w_up", true));
+  MOE_TRY(check_dev(w_down, "w_down", true));
+  if (cfg->H_shared > 0) {
+    MOE_TRY(check_dev(w_shared_gate, "w_shared_gate", true));
+    MOE_TRY(check_dev(w_shared_up, "w_shared_up", true));
+    MOE_TRY(check_dev(w_shared_down, "w_shared_down", true));
+  }
+  MOE_TRY(check_dev(out, "out", true));
+  MOE_TRY(check_dev(expert_ids, "expert_ids", false));
+  MOE_TRY(check_dev(gate_w, "gate_w", false));
+  MOE_TRY(check_dev(counts, "counts", false));
+  MOE_TRY(check_dev(aux, "aux", false));
+  MOE_TRY(check_dev(workspace, "workspace", true));
+
+  const Layout L = layout_of(cfg);
+  int32_t* ids = expert_ids ? expert_ids : at<int32_t>(workspace, L.ids);
+  float* gw = gate_w ? gate_w : at<float>(workspace, L.gate_w);
+  int32_t* cnt = counts ? counts : at<int32_t>(workspace, L.counts);
+  float* ax = aux ? aux : at<float>(workspace, L.aux);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* r2a = at<int32_t>(workspace, L.r2a);
+  int32_t* a2r = at<int32_t>(workspace, L.a2r);
+  const int cap = (int)capacity_of(cfg);
+  const bool dropless = !(cfg->capacity_factor > 0.0);
+  const int rows = (int)max_rows_of(cfg);
+
+  const moe::RouteParams rp =
+      route_params(cfg, x, w_router, logit_bias, select_bias, ids, gw, workspace, L);
+  MOE_TRY(hip_ok(moe::launch_route(rp, stream), "route kernel"));
+  moe::FinalizeParams fp{};
+  fp.T = cfg->T;
+  fp.E = cfg->E;
+  fp.k = cfg->top_k;
+  fp.nblk = moe::route_blocks(cfg->T);
+  fp.capacity = dropless ? 0 : cap;
+  fp.hist = rp.hist;
+  fp.pe_part = rp.pe_part;
+  fp.z_part = rp.z_part;
+  fp.counts = cnt;
+  fp.aux = ax;
+  fp.block_base = at<int32_t>(workspace, L.block_base);
+  fp.expert_offsets = offsets;
+  fp.n_kept = at<int32_t>(workspace, L.n_kept);
+  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
+  moe::ScatterParams sp{cfg->T, cfg->E, cfg->top_k, fp.capacity, ids, fp.block_base, offsets,
+                        r2a, a2r};
+  MOE_TRY(hip_ok(moe::launch_scatter(sp, stream), "scatter kernel"));
+
+  void* hbuf = at<void>(workspace, L.hbuf);
+  void* y = at<void>(workspace, L.y);
+  const bool bf16 = cfg->act_dtype == MOE_BF16;
+  const moe::GemmParams gp = gemm_params(cfg, cfg->E, cfg->H, x, r2a, offsets, rows, gw, w_gate,
+                                         w_up, w_down, hbuf, y);
+  MOE_TRY(hip_ok(moe::launch_grouped_swiglu(gp, bf16, stream), "grouped swiglu kernels"));
+  void* sy = nullptr;
+  if (cfg->H_shared > 0) {
+    sy = at<void>(workspace, L.shared_y);
+    const moe::GemmParams sp2 =
+        gemm_params(cfg, 1, cfg->H_shared, x, nullptr, nullptr, cfg->T, nullptr, w_shared_gate,
+                    w_shared_up, w_shared_down, hbuf, sy);
+    MOE_TRY(hip_ok(moe::launch_grouped_swiglu(sp2, bf16, stream), "shared expert kernels"));
+  }
+  moe::CombineParams cp{cfg->T, cfg->D, cfg->top_k, y, a2r, sy, out};
+  MOE_TRY(hip_ok(moe::launch_combine(cp, bf16, stream), "combine kernel"));
+  return ok();
+}
+
+}  // extern "C"

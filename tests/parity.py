@@ -1,0 +1,96 @@
+"""Shared helpers of the GPU parity tests: config marshalling, input staging and
+the comparison rules (bit-exact integers; the floating-point tolerances of the
+layer's accuracy target)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+
+# max|err| <= TOL * max|ref| (bf16 storage; fp32 end to end)
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+GATE_TOL = 1e-5          # absolute, on the fp32 gate weights
+AUX_RTOL = 1e-4
+
+
+def config_of(w: W.Workload):
+    import mixture_experts_layer_21_amd as moe
+    return moe.make_config(w.T, w.D, w.H, w.E, w.top_k, H_shared=w.H_shared,
+                           act_dtype=w.act_dtype, router_dtype=w.router_dtype, score=w.score,
+                           renormalize=w.renormalize, route_scale=w.route_scale,
+                           n_groups=w.n_groups, topk_groups=w.topk_groups,
+                           group_rule=w.group_rule, capacity_factor=w.capacity_factor)
+
+
+class LazyF64:
+    """Per-expert float64 view of a stacked weight tensor kept on the host."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t.detach()
+        self.shape = tuple(self.t.shape)
+
+    def __getitem__(self, e):
+        return self.t[e].to("cpu").to(torch.float64).numpy()
+
+
+def oracle_inputs(inp: dict) -> dict:
+    """Host float64 copies of the inputs the oracle needs (weights lazily)."""
+    out = {}
+    for k, v in inp.items():
+        if k in ("w_gate", "w_up", "w_down"):
+            out[k] = LazyF64(v)
+        else:
+            out[k] = W.to_f64(v)
+    return out
+
+
+def oracle_route(w: W.Workload, oi: dict):
+    return oracle.route(oi["x"], oi["w_router"], w.top_k, score=w.score,
+                        renormalize=w.renormalize, route_scale=w.route_scale,
+                        logit_bias=oi.get("logit_bias"), select_bias=oi.get("select_bias"),
+                        n_groups=w.n_groups, topk_groups=w.topk_groups,
+                        group_rule=w.group_rule)
+
+
+def oracle_forward(w: W.Workload, oi: dict, routing=None, tokens=None):
+    return oracle.forward(oi, top_k=w.top_k, score=w.score, renormalize=w.renormalize,
+                          route_scale=w.route_scale, n_groups=w.n_groups,
+                          topk_groups=w.topk_groups, group_rule=w.group_rule,
+                          capacity_factor=w.capacity_factor, routing=routing, tokens=tokens)
+
+
+def compare_route(w, r_ref, gpu):
+    """IDs bit-exact and weights within GATE_TOL on every token the oracle does
+    not flag as a near tie.  Returns (n_flagged, n_flagged_that_differ)."""
+    ids = gpu["expert_ids"].cpu().numpy().astype(np.int64)
+    gw = gpu["gate_w"].cpu().numpy().astype(np.float64)
+    flag = r_ref["near_tie"]
+    ok = ~flag
+    bad = np.nonzero(ok & (ids != r_ref["ids"]).any(1))[0]
+    assert bad.size == 0, (f"{bad.size} unflagged tokens differ, e.g. token {bad[:5]}: "
+                           f"gpu {ids[bad[:3]]} oracle {r_ref['ids'][bad[:3]]}")
+    err = np.abs(gw[ok] - r_ref["weights"][ok]).max(initial=0.0)
+    assert err <= GATE_TOL, f"gate weight error {err:.3g} > {GATE_TOL}"
+    counts = gpu["counts"].cpu().numpy()
+    assert (counts == np.bincount(ids.reshape(-1), minlength=w.E)).all(), "counts != bincount(ids)"
+    assert counts.sum() == w.T * w.top_k
+    differ = int((ids[flag] != r_ref["ids"][flag]).any(1).sum())
+    if differ == 0:
+        assert (counts == r_ref["counts"]).all()
+        aux = gpu["aux"].cpu().numpy().astype(np.float64)
+        assert abs(aux[0] - r_ref["balance"]) <= AUX_RTOL * abs(r_ref["balance"]) + 1e-6
+        assert abs(aux[1] - r_ref["z"]) <= AUX_RTOL * abs(r_ref["z"]) + 1e-6
+        mp = gpu["mean_prob"].cpu().numpy().astype(np.float64)
+        assert np.abs(mp - r_ref["mean_prob"]).max() <= 1e-5
+    return int(flag.sum()), differ
+
+
+def compare_rows(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str):
+    g = got.detach().to("cpu").to(torch.float64).numpy()
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    err = float(np.abs(g - ref).max()) if ref.size else 0.0
+    tol = TOL[dtype] * max(scale, 1e-30)
+    assert err <= tol, f"{what}: max|err| {err:.4g} > {TOL[dtype]} * max|ref| ({scale:.4g})"
+    return err, scale
