@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_21_amd.build` "
+        f"{LIB_PATH} is not built; run `python mixture_experts_layer_21_amd/build.py` "
         "(gfx950 HIP library, no CPU fallback exists)")
 _lib = ctypes.CDLL(LIB_PATH)
 

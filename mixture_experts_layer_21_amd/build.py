@@ -2,7 +2,8 @@
 
 Each source is compiled to an object in ``_build/`` in parallel, then linked
 in-tree next to this file, where the Python binding loads it.  Usage:
-``python -m mixture_experts_layer_21_amd.build``.
+``python mixture_experts_layer_21_amd/build.py`` (run it by path: importing
+the package loads the library it is about to replace).
 """
 from __future__ import annotations
 

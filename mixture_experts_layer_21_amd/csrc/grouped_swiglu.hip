@@ -21,6 +21,8 @@
 // device-side offsets, exiting when it has none.  Block indices are remapped
 // so that blocks sharing a weight tile run on the same XCD (one L2).
 // fp32: the same tiling with plain FMA (small layers only).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -246,6 +248,346 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile bf16 kernel: 512 threads (8 waves, two per SIMD), operands moved
+// global -> LDS by buffer_load ... lds (no register staging), an S-stage LDS
+// ring (loads for k-step kt+S-1 are in flight while kt is multiplied), and
+// MFMA fragments double-buffered in registers.
+//
+// Each 1 KB wave load fills 64 consecutive 16-byte LDS slots (slot = base +
+// lane*16); the lane fetches the global chunk that the swizzled layout puts in
+// that slot, so the fragment reads stay bank-conflict free.  Every stage lives
+// in its own LDS array and stage indices are compile-time constants, so the
+// wait for stage kt is an exact vmcnt and later stages stay in flight.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Swizzle of 16-byte chunk c in row r for KCH chunks per row.  The LDS serves
+// a 16-byte read for 16 lanes per cycle (64 four-byte banks); these XOR
+// patterns keep the 32-row fragment reads conflict-free, as measured with
+// SQ_LDS_BANK_CONFLICT on gfx950 (plain layouts conflict 5-12x per read).
+template <int KCH>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (KCH == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return (r >> 2) & 3;
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
+// vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the release fence of __syncthreads(): the fence
+// would wait for every load in flight, including later stages.  The wave's
+// own stage is already complete (wait_vmcnt), LDS reads of the previous stage
+// have returned (their MFMAs consumed them), and the empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BNB, int BK_, int S_, int WGM, int NWV, bool GATEUP>
+struct DmaCfg {
+  static constexpr int NT = 64 * NWV, NW = NWV, WGN = NW / WGM;
+  static constexpr int BK = BK_, KCH = BK / 8, S = S_;
+  static constexpr int A_LD = BM * KCH / 64 / NW;   // 1 KB wave loads per stage
+  static constexpr int B_LD = BNB * KCH / 64 / NW;
+  static constexpr int LPS = A_LD + B_LD;            // loads per thread per stage
+  static constexpr int WM = BM / WGM;
+  static constexpr int NB = GATEUP ? 2 : 1;
+  static constexpr int BN = BNB / NB;                // output columns of the tile
+  static constexpr int WN = BN / WGN;                // output columns per wave
+  static constexpr int MI = WM / 32, NI = WN / 32;
+  static_assert(A_LD >= 1 && B_LD >= 1 && MI >= 1 && NI >= 1, "tile shape");
+  static_assert(BM * KCH % (64 * NW) == 0 && BNB * KCH % (64 * NW) == 0, "tile shape");
+  static_assert(S_ >= 2 && S_ <= 4 && (S_ - 2) * LPS < 64, "stages");
+};
+
+template <class C, bool GATEUP>
+struct DmaLoads {
+  __amdgpu_buffer_rsrc_t rA, rG, rU;
+  const uint32_t* a_off;
+  const uint32_t* b_off;
+  int wave;
+};
+
+// Issue the global -> LDS loads of k-step kt into one stage's buffers.
+template <class C, bool GATEUP>
+__device__ __forceinline__ void dma_issue(const DmaLoads<C, GATEUP>& ld, uint16_t* sa,
+                                          uint16_t* sb, int kt) {
+  const int soff = kt * C::BK * 2;
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ld.rA, (lds_void_t*)(sa + (ld.wave + C::NW * i) * 512), 16, ld.a_off[i], soff, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::B_LD; ++i) {
+    const int blk = ld.wave + C::NW * i;
+    const bool up = GATEUP && blk * 64 >= C::BN * C::KCH;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? ld.rU : ld.rG, (lds_void_t*)(sb + blk * 512),
+                                             16, ld.b_off[i], soff, 0, 0);
+  }
+}
+
+// Multiply one stage: BK/16 k-steps of MI x NB*NI 32x32x16 MFMAs per wave.
+template <class C>
+__device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* sb, int wm,
+                                            int wn, int lr, int lk,
+                                            f32x16 (&acc)[C::NB][C::MI][C::NI]) {
+  constexpr int BK = C::BK, KCH = C::KCH, KS = BK / 16;
+  constexpr int NRD = C::MI + C::NB * C::NI;          // fragment reads per k16 step
+  constexpr int NMF = C::MI * C::NB * C::NI;          // MFMAs per k16 step
+  bf16x8 af[2][C::MI], bfr[2][C::NB][C::NI];
+  auto frags = [&](int kk, int buf) {
+    const int ch = kk * 2 + lk;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int r = wm * C::WM + mi * 32 + lr;
+      af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + r * BK + (ch ^ swz_k<KCH>(r)) * 8);
+    }
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int ni = 0; ni < C::NI; ++ni) {
+        const int r = nb * C::BN + wn * C::WN + ni * 32 + lr;
+        bfr[buf][nb][ni] =
+            *reinterpret_cast<const bf16x8*>(sb + r * BK + (ch ^ swz_k<KCH>(r)) * 8);
+      }
+  };
+  frags(0, 0);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    // Fragments of the next k16 step are read while this step's MFMAs run.
+    if (kk + 1 < KS) frags(kk + 1, (kk + 1) & 1);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+          acc[nb][mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              af[kk & 1][mi], bfr[kk & 1][nb][ni], acc[nb][mi][ni], 0, 0, 0);
+    if (kk + 1 < KS) {
+      // Scheduling hint: alternate one MFMA and one fragment read.
+#pragma unroll
+      for (int i = 0; i < NRD && i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+    }
+  }
+}
+
+// The pipelined k-loop.  The stage buffers come in as __restrict__ pointers:
+// once this is inlined, every LDS access and every LDS-bound load carries
+// scoped no-alias information, so the compiler's own wait before a fragment
+// read covers only the load into that same buffer (issued S-1 stages earlier)
+// instead of every load in flight.
+template <class C, bool GATEUP>
+__device__ __forceinline__ void dma_mainloop(
+    const DmaLoads<C, GATEUP>& ld, int nk, int wm, int wn, int lr, int lk,
+    f32x16 (&acc)[C::NB][C::MI][C::NI], uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
+    uint16_t* __restrict__ a2, uint16_t* __restrict__ a3, uint16_t* __restrict__ b0,
+    uint16_t* __restrict__ b1, uint16_t* __restrict__ b2, uint16_t* __restrict__ b3) {
+  constexpr int S = C::S;
+  // Prologue: stages 0 .. S-2 in flight (nk is a multiple of S, checked on the
+  // host).
+  dma_issue<C, GATEUP>(ld, a0, b0, 0);
+  if (S > 2) dma_issue<C, GATEUP>(ld, a1, b1, 1);
+  if (S > 3) dma_issue<C, GATEUP>(ld, a2, b2, 2);
+
+  // Every step issues one stage of loads, so exactly S-2 stages are in flight
+  // behind the one being waited for.  Past the end the loads repeat the last
+  // k-step into a buffer nobody reads again; keeping the issue unconditional
+  // keeps the compiler's view of the in-flight LDS writes precise.
+#define MOE_SA(i) ((i) == 0 ? a0 : (i) == 1 ? a1 : (i) == 2 ? a2 : a3)
+#define MOE_SB(i) ((i) == 0 ? b0 : (i) == 1 ? b1 : (i) == 2 ? b2 : b3)
+#define MOE_STEP(SI)                                                                        \
+  if constexpr (SI < S) {                                                                   \
+    const int kt = kb + SI;                                                                 \
+    wait_vmcnt<(S - 2) * C::LPS>();                                                         \
+    stage_barrier();                                                                        \
+    dma_issue<C, GATEUP>(ld, MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),            \
+                         min(kt + S - 1, nk - 1));                                          \
+    dma_compute<C>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc);                            \
+  }
+  for (int kb = 0; kb < nk; kb += S) {
+    MOE_STEP(0)
+    MOE_STEP(1)
+    MOE_STEP(2)
+    MOE_STEP(3)
+  }
+#undef MOE_STEP
+#undef MOE_SA
+#undef MOE_SB
+  // No LDS write may still be in flight when the block ends.
+  wait_vmcnt<0>();
+}
+
+template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
+__global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int max_mtiles) {
+  using C = DmaCfg<BM, BNB, BK, S, WGM, NWV, GATEUP>;
+  constexpr int KCH = C::KCH, MI = C::MI, NI = C::NI, NB = C::NB;
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA2[S > 2 ? BM * BK : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA3[S > 3 ? BM * BK : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BNB * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BNB * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[S > 2 ? BNB * BK : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB3[S > 3 ? BNB * BK : 8];
+  __shared__ int s_scan[NTHREADS + 4];
+
+  // find_tile uses the first 256 threads for its scan; all 512 take part in
+  // its barriers.
+  Tile tile;
+  {
+    const int G = gridDim.x, b = blockIdx.x;
+    const int xcd = b & 7, q = G >> 3, rem = G & 7;
+    const int L = xcd * q + min(xcd, rem) + (b >> 3);
+    const int ml = L % max_mtiles;
+    tile.nt = L / max_mtiles;
+    if (p.expert_offsets == nullptr) {
+      tile.e = 0;
+      tile.m0 = ml * BM;
+      tile.m_end = p.T;
+      if (tile.m0 >= p.T) return;
+    } else {
+      const int tid = threadIdx.x;
+      int cnt = 0;
+      if (tid < p.n_groups) {
+        const int rows = p.expert_offsets[tid + 1] - p.expert_offsets[tid];
+        cnt = (rows + BM - 1) / BM;
+      }
+      if (tid < NTHREADS) s_scan[tid] = cnt;
+      __syncthreads();
+      for (int d = 1; d < NTHREADS; d <<= 1) {
+        const int v = (tid < NTHREADS && tid >= d) ? s_scan[tid - d] : 0;
+        __syncthreads();
+        if (tid < NTHREADS) s_scan[tid] += v;
+        __syncthreads();
+      }
+      const int total = s_scan[NTHREADS - 1];
+      if (ml >= total) return;
+      if (tid < p.n_groups) {
+        const int hi = s_scan[tid], lo = hi - cnt;
+        if (ml >= lo && ml < hi) {
+          s_scan[NTHREADS] = tid;
+          s_scan[NTHREADS + 1] = p.expert_offsets[tid] + (ml - lo) * BM;
+          s_scan[NTHREADS + 2] = p.expert_offsets[tid + 1];
+        }
+      }
+      __syncthreads();
+      tile.e = s_scan[NTHREADS];
+      tile.m0 = s_scan[NTHREADS + 1];
+      tile.m_end = s_scan[NTHREADS + 2];
+    }
+  }
+
+  const int K = GATEUP ? p.D : p.hidden;
+  const int N = GATEUP ? p.hidden : p.D;
+  const int n0 = tile.nt * C::BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+
+  // Buffer resources: A is x (gathered rows) or this tile's rows of Hb; B is
+  // this expert's weight slice.  Offsets stay below 4 GB (checked on the host).
+  const uint16_t* a_base = GATEUP ? static_cast<const uint16_t*>(p.x)
+                                  : static_cast<const uint16_t*>(p.hbuf) + (size_t)tile.m0 * K;
+  const uint32_t a_bytes = GATEUP ? (uint32_t)((size_t)p.T * K * 2)
+                                  : (uint32_t)((size_t)(tile.m_end - tile.m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a_base, 0, (int)a_bytes, 0x00020000);
+  const uint16_t* wg = static_cast<const uint16_t*>(GATEUP ? p.w_gate : p.w_down) +
+                       (size_t)tile.e * N * K;
+  const uint16_t* wu = GATEUP ? static_cast<const uint16_t*>(p.w_up) + (size_t)tile.e * N * K
+                              : wg;
+  const uint32_t w_bytes = (uint32_t)((size_t)N * K * 2);
+  const __amdgpu_buffer_rsrc_t rG =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wg, 0, (int)w_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rU =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wu, 0, (int)w_bytes, 0x00020000);
+
+  // Per-lane byte offsets of each 1 KB wave load (k-step 0).
+  uint32_t a_off[C::A_LD];
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i) {
+    const int slot = (wave + C::NW * i) * 64 + lane;
+    const int r = slot / KCH, pc = slot % KCH, lc = pc ^ swz_k<KCH>(r);
+    int grow = tile.m0 + r;
+    if (grow >= tile.m_end) grow = tile.m0;
+    uint32_t rowoff;
+    if constexpr (GATEUP) {
+      const int tok = p.row_to_assign ? p.row_to_assign[grow] / p.k : grow;
+      rowoff = (uint32_t)tok * (uint32_t)K * 2u;
+    } else {
+      rowoff = (uint32_t)(grow - tile.m0) * (uint32_t)K * 2u;
+    }
+    a_off[i] = rowoff + (uint32_t)lc * 16u;
+  }
+  uint32_t b_off[C::B_LD];
+#pragma unroll
+  for (int i = 0; i < C::B_LD; ++i) {
+    const int slot = (wave + C::NW * i) * 64 + lane;
+    const int r = slot / KCH, pc = slot % KCH, lc = pc ^ swz_k<KCH>(r);
+    int n = n0 + (GATEUP ? (r % C::BN) : r);
+    if (n >= N) n = n0;
+    b_off[i] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)lc * 16u;
+  }
+  // B rows [0, BN) come from rG, [BN, 2BN) from rU (GATEUP); wave loads never
+  // straddle the two halves because BN*KCH is a multiple of 64.
+
+  const DmaLoads<C, GATEUP> ld{rA, rG, rU, a_off, b_off, wave};
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int lr = lane & 31, lk = lane >> 5;
+  f32x16 acc[NB][MI][NI];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nb][mi][ni][i] = 0.f;
+
+  dma_mainloop<C, GATEUP>(ld, K / BK, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3, sB0, sB1, sB2,
+                          sB3);
+
+  // Epilogue (32x32 accumulator layout: element i of lane l is row
+  // 8*(i/4) + 4*(l/32) + (i%4), column l%32).
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int grow = tile.m0 + wm * C::WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
+      if (grow >= tile.m_end) continue;
+      if constexpr (GATEUP) {
+        uint16_t* out = static_cast<uint16_t*>(p.hbuf) + (size_t)grow * N;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = n0 + wn * C::WN + ni * 32 + lr;
+          if (col < N) out[col] = f32_to_bf16_bits(silu_f32(acc[0][mi][ni][i]) * acc[1][mi][ni][i]);
+        }
+      } else {
+        float gw = 1.f;
+        if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[grow]];
+        uint16_t* out = static_cast<uint16_t*>(p.y) + (size_t)grow * N;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = n0 + wn * C::WN + ni * 32 + lr;
+          if (col < N) out[col] = f32_to_bf16_bits(gw * acc[0][mi][ni][i]);
+        }
+      }
+    }
+  }
+}
+
 // fp32 path: 64x64 tiles, 16x16 threads with 4x4 outputs each (rows ty+16i,
 // columns tx+16j), K staged 16 at a time, any K.
 template <bool GATEUP>
@@ -355,6 +697,18 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
+hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
+  using C = DmaCfg<BM, BNB, BK, S, WGM, NWV, GATEUP>;
+  const int N = GATEUP ? p.hidden : p.D;
+  const int mt = mtiles_bound(p, BM);
+  const long long nblocks = (long long)mt * ((N + C::BN - 1) / C::BN);
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BNB, BK, S, WGM, NWV, GATEUP>),
+                     dim3((unsigned)nblocks), dim3(64 * NWV), 0, s, p, mt);
+  return hipGetLastError();
+}
+
 template <bool GATEUP>
 hipError_t launch_f32(const GemmParams& p, hipStream_t s) {
   const int N = GATEUP ? p.hidden : p.D;
@@ -368,6 +722,29 @@ hipError_t launch_f32(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
+// Large-tile configuration (rows, B-tile rows, k-step, stages, wave rows,
+// waves);
+// overridable at build time for tuning sweeps.
+#ifndef MOE_GU_CFG
+#define MOE_GU_CFG 256, 256, 64, 2, 2, 8
+#endif
+#ifndef MOE_DN_CFG
+#define MOE_DN_CFG 256, 256, 64, 2, 2, 8
+#endif
+
+// Offsets inside the buffer resources of the large-tile kernel are 32-bit, and
+// its k-loop needs both K (D for gate/up, hidden for down) to be whole
+// multiples of BK * S.
+template <class C1, class C2>
+bool dma_fits(const GemmParams& p) {
+  if (p.D % (C1::BK * C1::S) || p.hidden % (C2::BK * C2::S)) return false;
+  const size_t lim = (size_t)1 << 31;
+  const size_t x_bytes = (size_t)p.T * p.D * 2;
+  const size_t w_bytes = (size_t)p.hidden * p.D * 2;
+  const size_t hb_tile = (size_t)256 * p.hidden * 2;
+  return x_bytes < lim && w_bytes < lim && hb_tile < lim;
+}
+
 hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s) {
   hipError_t err;
   if (!bf16) {
@@ -377,13 +754,19 @@ hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s) 
   // Rows per group decide the row-tile height: decode-sized groups use 32-row
   // tiles so that MFMA work is not spent on padding.
   const int rows = p.expert_offsets ? p.max_rows : p.T;
-  const bool small_m = (long long)rows < 64LL * (p.expert_offsets ? p.n_groups : 1);
-  if (small_m) {
+  const int groups = p.expert_offsets ? p.n_groups : 1;
+  if ((long long)rows < 64LL * groups) {
     if ((err = launch_bf16<32, 128, 1, true>(p, s)) != hipSuccess) return err;
     return launch_bf16<32, 256, 1, false>(p, s);
   }
-  if ((err = launch_bf16<128, 128, 2, true>(p, s)) != hipSuccess) return err;
-  return launch_bf16<128, 256, 2, false>(p, s);
+  using GU = DmaCfg<MOE_GU_CFG, true>;
+  using DN = DmaCfg<MOE_DN_CFG, false>;
+  if ((long long)rows < 512LL * groups || !dma_fits<GU, DN>(p)) {
+    if ((err = launch_bf16<128, 128, 2, true>(p, s)) != hipSuccess) return err;
+    return launch_bf16<128, 256, 2, false>(p, s);
+  }
+  if ((err = launch_dma<MOE_GU_CFG, true>(p, s)) != hipSuccess) return err;
+  return launch_dma<MOE_DN_CFG, false>(p, s);
 }
 
 }  // namespace moe

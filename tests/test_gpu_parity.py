@@ -316,6 +316,21 @@ def test_capacity_drops_everything_but_one(moe, dtype):
     assert (out.cpu()[torch.from_numpy(dropped)] == 0).all()
 
 
+@pytest.mark.parametrize("T,E,k", [(2000, 4, 2), (1111, 2, 1), (3001, 8, 3)])
+def test_large_tile_path(moe, T, E, k):
+    """Enough rows per expert for the 256-row direct-to-LDS kernels, with
+    ragged last tiles: every output row against the oracle."""
+    w = W.Workload("large_tiles", 1, T, D=512, H=384, E=E, top_k=k, w_std=0.05)
+    _say(f"[large tiles] T={T} E={E} k={k}")
+    inp = W.make_inputs(w, "cpu", seed=9)
+    out, ids, gw = _fwd(moe, w, inp)
+    oi = P.oracle_inputs(inp)
+    f = P.oracle_forward(w, oi, routing={"ids": ids.cpu().numpy(),
+                                         "weights": gw.cpu().numpy().astype(np.float64)})
+    err, scale = P.compare_rows(out, f["out"], "bf16", "large-tile forward")
+    _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
+
+
 def test_errors_are_reported(moe):
     w = W.SMALL["mixtral_small"]
     d = _to_dev(W.make_inputs(w, "cpu", seed=0))
