@@ -262,6 +262,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Column tiles per rasterisation band of the large-tile kernel.
+#ifndef MOE_BAND
+#define MOE_BAND 4
+#endif
+
 // Swizzle of 16-byte chunk c in row r for KCH chunks per row.  The LDS serves
 // a 16-byte read for 16 lanes per cycle (64 four-byte banks); these XOR
 // patterns keep the 32-row fragment reads conflict-free, as measured with
@@ -316,17 +321,20 @@ struct DmaLoads {
   int wave;
 };
 
-// Issue the global -> LDS loads of k-step kt into one stage's buffers.
+// Issue loads [i0, i1) of the LPS global -> LDS loads (A loads first, then B)
+// of k-step kt into one stage's buffers.
 template <class C, bool GATEUP>
 __device__ __forceinline__ void dma_issue(const DmaLoads<C, GATEUP>& ld, uint16_t* sa,
-                                          uint16_t* sb, int kt) {
+                                          uint16_t* sb, int kt, int i0, int i1) {
   const int soff = kt * C::BK * 2;
 #pragma unroll
   for (int i = 0; i < C::A_LD; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ld.rA, (lds_void_t*)(sa + (ld.wave + C::NW * i) * 512), 16, ld.a_off[i], soff, 0, 0);
+    if (i >= i0 && i < i1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ld.rA, (lds_void_t*)(sa + (ld.wave + C::NW * i) * 512), 16, ld.a_off[i], soff, 0, 0);
 #pragma unroll
   for (int i = 0; i < C::B_LD; ++i) {
+    if (C::A_LD + i < i0 || C::A_LD + i >= i1) continue;
     const int blk = ld.wave + C::NW * i;
     const bool up = GATEUP && blk * 64 >= C::BN * C::KCH;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? ld.rU : ld.rG, (lds_void_t*)(sb + blk * 512),
@@ -334,14 +342,23 @@ __device__ __forceinline__ void dma_issue(const DmaLoads<C, GATEUP>& ld, uint16_
   }
 }
 
-// Multiply one stage: BK/16 k-steps of MI x NB*NI 32x32x16 MFMAs per wave.
-template <class C>
+// Multiply one stage (BK/16 k-steps of MI x NB*NI 32x32x16 MFMAs per wave)
+// after issuing the loads of a later k-step into another stage's buffers
+// (spreading them over the k-steps measured slower on gfx950).
+template <class C, bool GATEUP>
 __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* sb, int wm,
                                             int wn, int lr, int lk,
-                                            f32x16 (&acc)[C::NB][C::MI][C::NI]) {
+                                            f32x16 (&acc)[C::NB][C::MI][C::NI],
+                                            const DmaLoads<C, GATEUP>& ld, uint16_t* na,
+                                            uint16_t* nb_, int kt_next) {
   constexpr int BK = C::BK, KCH = C::KCH, KS = BK / 16;
   constexpr int NRD = C::MI + C::NB * C::NI;          // fragment reads per k16 step
   constexpr int NMF = C::MI * C::NB * C::NI;          // MFMAs per k16 step
+#ifndef MOE_SPREAD_LOADS
+  constexpr int NLD = C::LPS;                         // all loads before the first k16 step
+#else
+  constexpr int NLD = (C::LPS + KS - 1) / KS;         // loads spread over the k16 steps
+#endif
   bf16x8 af[2][C::MI], bfr[2][C::NB][C::NI];
   auto frags = [&](int kk, int buf) {
     const int ch = kk * 2 + lk;
@@ -362,6 +379,26 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
   frags(0, 0);
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
+    constexpr int LPS = C::LPS;
+    const int i1 = (kk + 1) * NLD < LPS ? (kk + 1) * NLD : LPS;
+    {  // loads [kk*NLD, i1) of k-step kt_next (A loads first, then B)
+      const int i0 = kk * NLD, soff = kt_next * BK * 2;
+#pragma unroll
+      for (int i = 0; i < C::A_LD; ++i)
+        if (i >= i0 && i < i1)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              ld.rA, (lds_void_t*)(na + (ld.wave + C::NW * i) * 512), 16, ld.a_off[i], soff, 0,
+              0);
+#pragma unroll
+      for (int i = 0; i < C::B_LD; ++i) {
+        if (C::A_LD + i < i0 || C::A_LD + i >= i1) continue;
+        const int blk = ld.wave + C::NW * i;
+        const bool up = GATEUP && blk * 64 >= C::BN * C::KCH;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? ld.rU : ld.rG,
+                                                 (lds_void_t*)(nb_ + blk * 512), 16,
+                                                 ld.b_off[i], soff, 0, 0);
+      }
+    }
     // Fragments of the next k16 step are read while this step's MFMAs run.
     if (kk + 1 < KS) frags(kk + 1, (kk + 1) & 1);
 #pragma unroll
@@ -372,14 +409,16 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
         for (int mi = 0; mi < C::MI; ++mi)
           acc[nb][mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               af[kk & 1][mi], bfr[kk & 1][nb][ni], acc[nb][mi][ni], 0, 0, 0);
-    if (kk + 1 < KS) {
-      // Scheduling hint: alternate one MFMA and one fragment read.
+    // Scheduling hint: MFMAs interleaved with the fragment reads and loads.
+    const int nrd = kk + 1 < KS ? NRD : 0;
+    const int nld = i1 - kk * NLD;
 #pragma unroll
-      for (int i = 0; i < NRD && i < NMF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#ifdef MOE_SPREAD_LOADS
+      if (i < nld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+#endif
     }
   }
 }
@@ -396,16 +435,17 @@ __device__ __forceinline__ void dma_mainloop(
     uint16_t* __restrict__ a2, uint16_t* __restrict__ a3, uint16_t* __restrict__ b0,
     uint16_t* __restrict__ b1, uint16_t* __restrict__ b2, uint16_t* __restrict__ b3) {
   constexpr int S = C::S;
-  // Prologue: stages 0 .. S-2 in flight (nk is a multiple of S, checked on the
-  // host).
-  dma_issue<C, GATEUP>(ld, a0, b0, 0);
-  if (S > 2) dma_issue<C, GATEUP>(ld, a1, b1, 1);
-  if (S > 3) dma_issue<C, GATEUP>(ld, a2, b2, 2);
+  // Prologue: stages 0 .. S-2 in flight.
+  constexpr int LPS = C::LPS;
+  dma_issue<C, GATEUP>(ld, a0, b0, 0, 0, LPS);
+  if (S > 2) dma_issue<C, GATEUP>(ld, a1, b1, min(1, nk - 1), 0, LPS);
+  if (S > 3) dma_issue<C, GATEUP>(ld, a2, b2, min(2, nk - 1), 0, LPS);
 
   // Every step issues one stage of loads, so exactly S-2 stages are in flight
   // behind the one being waited for.  Past the end the loads repeat the last
-  // k-step into a buffer nobody reads again; keeping the issue unconditional
-  // keeps the compiler's view of the in-flight LDS writes precise.
+  // k-step into a buffer nobody reads again, and steps past the end skip the
+  // multiply; keeping the issue unconditional keeps the compiler's view of
+  // the in-flight LDS writes precise.
 #define MOE_SA(i) ((i) == 0 ? a0 : (i) == 1 ? a1 : (i) == 2 ? a2 : a3)
 #define MOE_SB(i) ((i) == 0 ? b0 : (i) == 1 ? b1 : (i) == 2 ? b2 : b3)
 #define MOE_STEP(SI)                                                                        \
@@ -413,9 +453,13 @@ __device__ __forceinline__ void dma_mainloop(
     const int kt = kb + SI;                                                                 \
     wait_vmcnt<(S - 2) * C::LPS>();                                                         \
     stage_barrier();                                                                        \
-    dma_issue<C, GATEUP>(ld, MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),            \
-                         min(kt + S - 1, nk - 1));                                          \
-    dma_compute<C>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc);                            \
+    if (kt < nk)                                                                            \
+      dma_compute<C, GATEUP>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc, ld,               \
+                             MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),            \
+                             min(kt + S - 1, nk - 1));                                      \
+    else                                                                                    \
+      dma_issue<C, GATEUP>(ld, MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S), nk - 1,  \
+                           0, C::LPS);                                                      \
   }
   for (int kb = 0; kb < nk; kb += S) {
     MOE_STEP(0)
@@ -451,8 +495,25 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ma
     const int G = gridDim.x, b = blockIdx.x;
     const int xcd = b & 7, q = G >> 3, rem = G & 7;
     const int L = xcd * q + min(xcd, rem) + (b >> 3);
-    const int ml = L % max_mtiles;
-    tile.nt = L / max_mtiles;
+    // Logical tiles run in bands of GN column tiles; inside a band the GN
+    // column tiles of one row tile are consecutive.  The blocks an XCD holds
+    // at once then cover about (32/GN) row tiles x GN column tiles, so each
+    // A slice is fetched into that XCD's L2 once for GN blocks and each B
+    // slice once for the row tiles of its expert.
+    constexpr int GN = MOE_BAND;
+    const int ntiles = G / max_mtiles;
+    const int full = ntiles / GN;
+    int ml;
+    if (L < full * max_mtiles * GN) {
+      const int r = L % (max_mtiles * GN);
+      ml = r / GN;
+      tile.nt = (L / (max_mtiles * GN)) * GN + r % GN;
+    } else {
+      const int w = ntiles - full * GN;
+      const int r = L - full * max_mtiles * GN;
+      ml = r / w;
+      tile.nt = full * GN + r % w;
+    }
     if (p.expert_offsets == nullptr) {
       tile.e = 0;
       tile.m0 = ml * BM;
@@ -731,13 +792,19 @@ hipError_t launch_f32(const GemmParams& p, hipStream_t s) {
 #ifndef MOE_DN_CFG
 #define MOE_DN_CFG 256, 256, 64, 2, 2, 8
 #endif
+// Groups of 64..511 rows on average: 128-row tiles.
+#ifndef MOE_GU_CFG_M
+#define MOE_GU_CFG_M 128, 512, 32, 2, 2, 8
+#endif
+#ifndef MOE_DN_CFG_M
+#define MOE_DN_CFG_M 128, 512, 32, 2, 2, 8
+#endif
 
 // Offsets inside the buffer resources of the large-tile kernel are 32-bit, and
-// its k-loop needs both K (D for gate/up, hidden for down) to be whole
-// multiples of BK * S.
+// its k-loop needs K (D for gate/up, hidden for down) to be a multiple of BK.
 template <class C1, class C2>
 bool dma_fits(const GemmParams& p) {
-  if (p.D % (C1::BK * C1::S) || p.hidden % (C2::BK * C2::S)) return false;
+  if (p.D % C1::BK || p.hidden % C2::BK) return false;
   const size_t lim = (size_t)1 << 31;
   const size_t x_bytes = (size_t)p.T * p.D * 2;
   const size_t w_bytes = (size_t)p.hidden * p.D * 2;
@@ -761,12 +828,18 @@ hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s) 
   }
   using GU = DmaCfg<MOE_GU_CFG, true>;
   using DN = DmaCfg<MOE_DN_CFG, false>;
-  if ((long long)rows < 512LL * groups || !dma_fits<GU, DN>(p)) {
-    if ((err = launch_bf16<128, 128, 2, true>(p, s)) != hipSuccess) return err;
-    return launch_bf16<128, 256, 2, false>(p, s);
+  using GUM = DmaCfg<MOE_GU_CFG_M, true>;
+  using DNM = DmaCfg<MOE_DN_CFG_M, false>;
+  if ((long long)rows >= 512LL * groups && dma_fits<GU, DN>(p)) {
+    if ((err = launch_dma<MOE_GU_CFG, true>(p, s)) != hipSuccess) return err;
+    return launch_dma<MOE_DN_CFG, false>(p, s);
   }
-  if ((err = launch_dma<MOE_GU_CFG, true>(p, s)) != hipSuccess) return err;
-  return launch_dma<MOE_DN_CFG, false>(p, s);
+  if (dma_fits<GUM, DNM>(p)) {
+    if ((err = launch_dma<MOE_GU_CFG_M, true>(p, s)) != hipSuccess) return err;
+    return launch_dma<MOE_DN_CFG_M, false>(p, s);
+  }
+  if ((err = launch_bf16<128, 128, 2, true>(p, s)) != hipSuccess) return err;
+  return launch_bf16<128, 256, 2, false>(p, s);
 }
 
 }  // namespace moe

@@ -25,21 +25,25 @@ struct RouteParams {
   const float* select_bias;
   int32_t* ids;       // [T*k]
   float* gate_w;      // [T*k]
-  int32_t* hist;      // [nblk*E]  per-block expert histogram
-  float* pe_part;     // [nblk*E]  per-block sums of P_e terms
+  float* logits_part; // [ksplit*T*E] split-K partial logits
+  int ksplit;
+  int32_t* hist;      // [E*nblk]  per-tile expert histogram (expert-major)
+  float* pe_part;     // [E*nblk]  per-tile sums of P_e terms
   float* z_part;      // [nblk]    per-block sums of lse^2
 };
 
 struct FinalizeParams {
   int T, E, k, nblk;
   int capacity;              // <= 0: dropless
-  const int32_t* hist;       // [nblk*E]
-  const float* pe_part;      // [nblk*E] or null (no aux)
+  const int32_t* hist;       // [E*nblk] (expert-major)
+  const float* pe_part;      // [E*nblk] or null (no aux)
   const float* z_part;       // [nblk] or null
+  int32_t* counts_ws;        // [E] scratch: counts before the capacity clip
+  float* pe_ws;              // [E] scratch: P_e
   int32_t* counts;           // [E] or null
   float* aux;                // [2] or null
   float* mean_prob;          // [E] or null
-  int32_t* block_base;       // [nblk*E] or null (no permutation scan)
+  int32_t* block_base;       // [E*nblk] or null (no permutation scan)
   int32_t* expert_offsets;   // [E+1] or null
   int32_t* n_kept;           // [1] or null
 };
@@ -85,5 +89,17 @@ hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
 
 inline int route_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
+
+// K-split of the router GEMM: enough blocks to fill the GPU while every split
+// keeps at least four k-steps (32 elements each for bf16, 16 for fp32).
+inline int route_ksplit(int T, int D, int E, bool bf16_mfma) {
+  const int nsteps = D / (bf16_mfma ? 32 : 16);
+  const int NT = (E + 15) / 16;
+  const int NTB = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
+  const long long blocks = (long long)route_blocks(T) * ((NT + NTB - 1) / NTB);
+  int ks = 1;
+  while (blocks * ks < 1024 && ks * 2 * 4 <= nsteps && ks < 16) ks *= 2;
+  return ks;
+}
 
 }  // namespace moe

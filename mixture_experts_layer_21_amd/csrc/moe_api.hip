@@ -81,9 +81,11 @@ moe_status check_config(const moe_config* c) {
   if (c->act_dtype == MOE_BF16) {
     if (c->D % 64 || c->H % 64 || c->H_shared % 64)
       return fail(MOE_ERR_UNSUPPORTED, "bf16 path needs D, H, H_shared multiples of 64");
-  } else if (c->D % 4) {
-    return fail(MOE_ERR_UNSUPPORTED, "fp32 path needs D a multiple of 4");
+  } else if (c->D % 16) {
+    return fail(MOE_ERR_UNSUPPORTED, "fp32 path needs D a multiple of 16");
   }
+  if (c->router_dtype == MOE_F32 && c->D % 16)
+    return fail(MOE_ERR_UNSUPPORTED, "an fp32 router needs D a multiple of 16");
   return MOE_OK;
 }
 
@@ -102,8 +104,8 @@ long long max_rows_of(const moe_config* c) {
 }
 
 struct Layout {
-  size_t ids, gate_w, counts, aux, hist, pe_part, z_part, block_base, offsets, n_kept, r2a,
-      a2r, hbuf, y, shared_y, total;
+  size_t ids, gate_w, counts, aux, logits, hist, pe_part, z_part, block_base, counts_ws, pe_ws,
+      offsets, n_kept, r2a, a2r, hbuf, y, shared_y, total;
 };
 
 Layout layout_of(const moe_config* c) {
@@ -122,10 +124,14 @@ Layout layout_of(const moe_config* c) {
   L.gate_w = take(T * k * 4);
   L.counts = take(E * 4);
   L.aux = take(2 * 4);
+  const bool mfma16 = c->act_dtype == MOE_BF16 && c->router_dtype == MOE_BF16;
+  L.logits = take((size_t)moe::route_ksplit(c->T, c->D, c->E, mfma16) * T * E * 4);
   L.hist = take(nblk * E * 4);
   L.pe_part = take(nblk * E * 4);
   L.z_part = take(nblk * 4);
   L.block_base = take(nblk * E * 4);
+  L.counts_ws = take(E * 4);
+  L.pe_ws = take(E * 4);
   L.offsets = take((E + 1) * 4);
   L.n_kept = take(4);
   L.r2a = take(std::max<size_t>(rows, 1) * 4);
@@ -207,6 +213,8 @@ moe::RouteParams route_params(const moe_config* c, const void* x, const void* w_
   p.select_bias = sb;
   p.ids = ids;
   p.gate_w = gw;
+  p.logits_part = at<float>(ws, L.logits);
+  p.ksplit = moe::route_ksplit(c->T, c->D, c->E, p.act_bf16 && p.router_bf16);
   p.hist = at<int32_t>(ws, L.hist);
   p.pe_part = at<float>(ws, L.pe_part);
   p.z_part = at<float>(ws, L.z_part);
@@ -304,6 +312,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   fp.nblk = moe::route_blocks(cfg->T);
   fp.capacity = 0;
   fp.hist = rp.hist;
+  fp.counts_ws = at<int32_t>(workspace, L.counts_ws);
+  fp.pe_ws = at<float>(workspace, L.pe_ws);
   fp.pe_part = rp.pe_part;
   fp.z_part = rp.z_part;
   fp.counts = counts;
@@ -339,6 +349,8 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* expert_ids, int32_t
   fp.nblk = moe::route_blocks(cfg->T);
   fp.capacity = capacity > 0 ? capacity : 0;
   fp.hist = hist;
+  fp.counts_ws = at<int32_t>(workspace, L.counts_ws);
+  fp.pe_ws = at<float>(workspace, L.pe_ws);
   fp.block_base = base;
   fp.expert_offsets = expert_offsets;
   fp.n_kept = n_kept;
@@ -465,6 +477,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   fp.nblk = moe::route_blocks(cfg->T);
   fp.capacity = dropless ? 0 : cap;
   fp.hist = rp.hist;
+  fp.counts_ws = at<int32_t>(workspace, L.counts_ws);
+  fp.pe_ws = at<float>(workspace, L.pe_ws);
   fp.pe_part = rp.pe_part;
   fp.z_part = rp.z_part;
   fp.counts = cnt;

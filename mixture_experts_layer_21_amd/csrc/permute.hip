@@ -7,12 +7,14 @@
 // token list of "2.9 Mixture-of-Experts (MoE) Architectures", "MoE in
 // Practice".  Rows are ordered by (expert, assignment index a = t*k + s).
 //
-// Tokens are cut into tiles of kRouteTile.  hist[b][e] counts tile b's
+// Tokens are cut into tiles of kRouteTile.  hist[e][b] counts tile b's
 // assignments to expert e (written by the routing kernel, or by hist_kernel
-// when the caller supplies the IDs).  finalize_kernel turns the histograms
-// into per-tile running bases, capacity-clipped expert offsets and the aux
-// losses.  scatter_kernel ranks each tile's assignments in order with wave
-// ballots and writes both directions of the permutation.
+// when the caller supplies the IDs).  column_scan_kernel (one block per
+// expert) turns each column into per-tile running bases, the expert's count
+// and its P_e sum; expert_scan_kernel clips the counts to the capacity, scans
+// them into expert offsets and finishes the aux losses.  scatter_kernel ranks
+// each tile's assignments in order with wave ballots and writes both
+// directions of the permutation.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,47 +34,97 @@ __global__ __launch_bounds__(256) void hist_kernel(int T, int E, int k, const in
     if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);  // out-of-range IDs are ignored
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)b * E + e] = h[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)e * gridDim.x + b] = h[e];
 }
 
-// One block.  Thread e walks the tiles in order for expert e; thread 0 then
-// scans the experts.  Every sum has a fixed order.
-__global__ __launch_bounds__(256) void finalize_kernel(FinalizeParams p) {
-  __shared__ int cnt[kMaxExperts];
-  __shared__ int kept[kMaxExperts];
-  __shared__ float pe[kMaxExperts];
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
-    int run = 0;
-    float ps = 0.f;
-    for (int b = 0; b < p.nblk; ++b) {
-      const size_t i = (size_t)b * p.E + e;
-      if (p.block_base) p.block_base[i] = run;
-      run += p.hist[i];
-      if (p.pe_part) ps += p.pe_part[i];
-    }
-    cnt[e] = run;
-    kept[e] = p.capacity > 0 ? min(run, p.capacity) : run;
-    pe[e] = ps / (float)p.T;
-    if (p.counts) p.counts[e] = run;
-    if (p.mean_prob) p.mean_prob[e] = pe[e];
+// Block-wide inclusive scan of one int per thread (256 threads); also
+// returns the block total.  Fixed shape, so the result is deterministic.
+__device__ __forceinline__ int block_scan_incl(int v, int* s_w, int& total) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) s_w[w] = v;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) before += s_w[i];
+    total += s_w[i];
   }
   __syncthreads();
+  return v + before;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* s_w) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  if (lane_id() == 0) s_w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float t = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+  __syncthreads();
+  return t;
+}
+
+// One block (256 threads) per expert: scan its column of tile counts.
+__global__ __launch_bounds__(256) void column_scan_kernel(FinalizeParams p) {
+  __shared__ int s_i[4];
+  __shared__ float s_f[4];
+  const int e = blockIdx.x;
+  const int32_t* h = p.hist + (size_t)e * p.nblk;
+  int run = 0;
+  float ps = 0.f;
+  for (int b0 = 0; b0 < p.nblk; b0 += 256) {
+    const int b = b0 + threadIdx.x;
+    const int v = b < p.nblk ? h[b] : 0;
+    int tot;
+    const int incl = block_scan_incl(v, s_i, tot);
+    if (p.block_base && b < p.nblk) p.block_base[(size_t)e * p.nblk + b] = run + incl - v;
+    run += tot;
+    if (p.pe_part) ps += block_sum(b < p.nblk ? p.pe_part[(size_t)e * p.nblk + b] : 0.f, s_f);
+  }
   if (threadIdx.x == 0) {
-    if (p.expert_offsets) {
-      int off = 0;
-      for (int e = 0; e < p.E; ++e) {
-        p.expert_offsets[e] = off;
-        off += kept[e];
-      }
-      p.expert_offsets[p.E] = off;
-      if (p.n_kept) *p.n_kept = off;
+    p.counts_ws[e] = run;
+    if (p.counts) p.counts[e] = run;
+    if (p.pe_part) {
+      const float pe = ps / (float)p.T;
+      p.pe_ws[e] = pe;
+      if (p.mean_prob) p.mean_prob[e] = pe;
     }
+  }
+}
+
+// One block: capacity clip, expert offsets, n_kept and the aux losses.
+__global__ __launch_bounds__(256) void expert_scan_kernel(FinalizeParams p) {
+  __shared__ int s_i[4];
+  __shared__ float s_f[4];
+  int base = 0;
+  float bal = 0.f;
+  const float inv = 1.0f / ((float)p.T * (float)p.k);
+  for (int e0 = 0; e0 < p.E; e0 += 256) {
+    const int e = e0 + threadIdx.x;
+    const int c = e < p.E ? p.counts_ws[e] : 0;
+    const int kept = p.capacity > 0 ? min(c, p.capacity) : c;
+    int tot;
+    const int incl = block_scan_incl(kept, s_i, tot);
+    if (p.expert_offsets && e < p.E) p.expert_offsets[e] = base + incl - kept;
+    base += tot;
+    if (p.aux) bal += block_sum(e < p.E ? ((float)c * inv) * p.pe_ws[e] : 0.f, s_f);
+  }
+  float z = 0.f;
+  if (p.aux) {
+    for (int b0 = 0; b0 < p.nblk; b0 += 256) {
+      const int b = b0 + threadIdx.x;
+      z += block_sum(b < p.nblk ? p.z_part[b] : 0.f, s_f);
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (p.expert_offsets) p.expert_offsets[p.E] = base;
+    if (p.n_kept) *p.n_kept = base;
     if (p.aux) {
-      const float inv = 1.0f / ((float)p.T * (float)p.k);
-      float bal = 0.f;
-      for (int e = 0; e < p.E; ++e) bal += ((float)cnt[e] * inv) * pe[e];
-      float z = 0.f;
-      for (int b = 0; b < p.nblk; ++b) z += p.z_part[b];
       p.aux[0] = (float)p.E * bal;
       p.aux[1] = z / (float)p.T;
     }
@@ -86,7 +138,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeParams p) {
 __global__ __launch_bounds__(64) void scatter_kernel(ScatterParams p) {
   __shared__ int run[kMaxExperts];
   const int b = blockIdx.x;
-  for (int e = threadIdx.x; e < p.E; e += 64) run[e] = p.block_base[(size_t)b * p.E + e];
+  for (int e = threadIdx.x; e < p.E; e += 64) run[e] = p.block_base[(size_t)e * gridDim.x + b];
   __syncthreads();
   int nbits = 1;
   while ((1 << nbits) < p.E) ++nbits;
@@ -131,7 +183,10 @@ hipError_t launch_hist(int T, int E, int k, const int32_t* ids, int32_t* hist, h
 }
 
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(column_scan_kernel, dim3(p.E), dim3(256), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Routing kernel: router GEMM, fp32 scores, optional group limit, top-k,
-// gate weights, and per-block partial sums for the balance and z losses.
+// Routing: router GEMM, fp32 scores, optional group limit, top-k, gate
+// weights, and per-block partial sums for the balance and z losses.
 //
 // Follows "Lab: build a tiny MoE in PyTorch" ("Full implementation": Linear
 // router, float32 softmax, topk, renormalised weights, bincount, balance and
@@ -7,13 +7,17 @@
 // selection-only per-expert bias), with the NeMo Gate switches score_func,
 // n_groups / topk_groups and route_scale.
 //
-// One 256-thread block routes kRouteTile tokens.  Phase 1 computes the
-// [tile x E] logits into LDS: bf16 x and bf16 W_r use 16x16x32 bf16 MFMA
-// (exact products, fp32 accumulation); any fp32 operand uses fp32 FMA.
-// Phase 2 gives each wave one token at a time: lane l holds experts
-// l, l+64, l+128, l+192; max, sums and the k arg-max rounds are butterfly
-// shuffles, so every reduction has a fixed order and results are
-// bit-reproducible.  Ties go to the lower expert index.
+// Two kernels:
+//  * route_logits_kernel: the [T x E] logits as split-K partial sums.  A
+//    256-thread block covers 32 tokens x up to 64 experts x one K range; each
+//    wave runs 16x16 MFMA tiles (bf16 x bf16: 16x16x32 bf16, products exact;
+//    any fp32 operand: 16x16x4 fp32).  Waves sharing an expert tile split the
+//    k-steps and are summed through LDS in a fixed order.
+//  * route_select_kernel: one wave per token adds the K-split partials in a
+//    fixed order and does the scores, group limit, k arg-max rounds (butterfly
+//    shuffles; ties to the lower expert index) and weights.  Lane l holds
+//    experts l, l+64, l+128, l+192.  Every reduction has a fixed order, so
+//    results are bit-reproducible.
 #include <math.h>
 
 #include "common.hpp"
@@ -25,117 +29,110 @@ namespace {
 constexpr int RT = kRouteTile;
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / MOE_WAVE;
-constexpr int LSTR = kMaxExperts + 4;  // LDS row stride of the logit tile
-constexpr int KC = 32;                 // k chunk of the fp32 path
 
-struct RouteSmem {
-  float logits[RT][LSTR];
-  union {
-    struct {
-      float xs[RT][KC + 1];
-      float ws[KC][kMaxExperts];
-    } simt;
-    float pe[NWAVES][kMaxExperts];
-  } u;
-  float zw[NWAVES];
-  int hist[kMaxExperts];
-};
-
-// bf16 x bf16 logits with v_mfma_f32_16x16x32_bf16.  Lane l supplies row
-// (l % 16) and k-slice 8*(l / 16) .. +7 of both operands; it receives output
-// rows 4*(l / 16) .. +3 of column (l % 16).
-__device__ void logits_mfma(const RouteParams& p, int t0, RouteSmem& sm) {
-  const uint16_t* x = static_cast<const uint16_t*>(p.x);
-  const uint16_t* w = static_cast<const uint16_t*>(p.w_router);
-  const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
-  const int NT = (p.E + 15) / 16;
-  const int r = lane & 15, kq = (lane >> 4) * 8;
-  const int ta = min(t0 + r, p.T - 1), tb = min(t0 + 16 + r, p.T - 1);
-  const uint16_t* pa = x + (size_t)ta * p.D + kq;
-  const uint16_t* pb = x + (size_t)tb * p.D + kq;
-  const uint16_t* pw[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = min((wave + NWAVES * j) * 16 + r, p.E - 1);
-    pw[j] = w + (size_t)e * p.D + kq;
-  }
-  f32x4 acc[2][4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    acc[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int k0 = 0; k0 < p.D; k0 += 32) {
-    const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(pa + k0);
-    const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(pb + k0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (wave + NWAVES * j < NT) {  // wave-uniform
-        const bf16x8 B = *reinterpret_cast<const bf16x8*>(pw[j] + k0);
-        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[0][j], 0, 0, 0);
-        acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[1][j], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int nt = wave + NWAVES * j;
-    if (nt < NT) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sm.logits[mt * 16 + (lane >> 4) * 4 + i][nt * 16 + (lane & 15)] = acc[mt][j][i];
-    }
-  }
+// Four consecutive elements starting at p (16-byte or 8-byte aligned) as fp32.
+__device__ __forceinline__ f32x4 load4(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ f32x4 load4(const uint16_t* p) {
+  const uint2 q = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u),
+               __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xffff0000u)};
 }
 
-// fp32 logits (any fp32 operand): thread (tg, eg) accumulates tokens
-// 8*tg .. 8*tg+7 against experts eg + 64*j, in k order.
-template <typename XT, typename WT>
-__device__ void logits_simt(const RouteParams& p, int t0, RouteSmem& sm) {
+// Partial logits part[ks][t][e] = sum over this block's K range of x[t,k] W[e,k].
+// MFMA operand mapping (both operands alike, so any fixed k permutation inside
+// a step gives the same products): 16x16x32 bf16: lane l holds row l%16 and
+// k = 8*(l/16) .. +7; 16x16x4 fp32 (four per 16-wide step): lane l holds row
+// l%16 and k = 4*(l/16) + j in the j-th MFMA.  Output element i of lane l is
+// row 4*(l/16) + i, column l%16.
+template <typename XT, typename WT, bool BF16>
+__global__ __launch_bounds__(NTHREADS) void route_logits_kernel(RouteParams p) {
+  constexpr int KSTEP = BF16 ? 32 : 16;
   const XT* x = static_cast<const XT*>(p.x);
   const WT* w = static_cast<const WT*>(p.w_router);
-  const int tid = threadIdx.x, eg = tid & 63, tg = tid >> 6;
-  float acc[8][4];
+  const int NT = (p.E + 15) / 16;
+  const int NTB = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
+  const int WPN = NWAVES / NTB;  // waves per expert tile (they split the k-steps)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+  const int nt = blockIdx.y * NTB + wave / WPN;
+  const int phase = wave % WPN;
+  const int t0 = blockIdx.x * RT;
+  const int nsteps = p.D / KSTEP;
+  const int per = (nsteps + p.ksplit - 1) / p.ksplit;
+  const int s0 = blockIdx.z * per, s1 = min(nsteps, s0 + per);
+  const bool active = nt < NT;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    const int r = lane & 15, kq = lane >> 4;
+    const int ta = min(t0 + r, p.T - 1), tb = min(t0 + 16 + r, p.T - 1);
+    const int e = min(nt * 16 + r, p.E - 1);
+    if constexpr (BF16) {
+      const uint16_t* pa = reinterpret_cast<const uint16_t*>(x) + (size_t)ta * p.D + kq * 8;
+      const uint16_t* pb = reinterpret_cast<const uint16_t*>(x) + (size_t)tb * p.D + kq * 8;
+      const uint16_t* pw = reinterpret_cast<const uint16_t*>(w) + (size_t)e * p.D + kq * 8;
+      int s = s0 + phase;
+      // Four k-steps in flight per iteration.
+      for (; s + 3 * WPN < s1; s += 4 * WPN) {
+        bf16x8 A0[4], A1[4], B[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+        for (int u = 0; u < 4; ++u) {
+          const int k0 = (s + u * WPN) * 32;
+          A0[u] = *reinterpret_cast<const bf16x8*>(pa + k0);
+          A1[u] = *reinterpret_cast<const bf16x8*>(pb + k0);
+          B[u] = *reinterpret_cast<const bf16x8*>(pw + k0);
+        }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < p.D; k0 += KC) {
-    for (int idx = tid; idx < RT * KC; idx += NTHREADS) {
-      const int rr = idx / KC, c = idx % KC;
-      const int t = t0 + rr, kk = k0 + c;
-      sm.u.simt.xs[rr][c] = (t < p.T && kk < p.D) ? Elem<XT>::load(x, (size_t)t * p.D + kk) : 0.f;
-    }
-    for (int idx = tid; idx < p.E * KC; idx += NTHREADS) {
-      const int e = idx / KC, c = idx % KC, kk = k0 + c;
-      sm.u.simt.ws[c][e] = kk < p.D ? Elem<WT>::load(w, (size_t)e * p.D + kk) : 0.f;
-    }
-    __syncthreads();
-    for (int c = 0; c < KC; ++c) {
-      float wv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = eg + 64 * j;
-        wv[j] = e < p.E ? sm.u.simt.ws[c][e] : 0.f;
+        for (int u = 0; u < 4; ++u) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[u], B[u], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[u], B[u], acc1, 0, 0, 0);
+        }
       }
+      for (; s < s1; s += WPN) {
+        const int k0 = s * 32;
+        const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(pa + k0);
+        const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(pb + k0);
+        const bf16x8 B = *reinterpret_cast<const bf16x8*>(pw + k0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc1, 0, 0, 0);
+      }
+    } else {
+      const XT* pa = x + (size_t)ta * p.D + kq * 4;
+      const XT* pb = x + (size_t)tb * p.D + kq * 4;
+      const WT* pw = w + (size_t)e * p.D + kq * 4;
+      for (int s = s0 + phase; s < s1; s += WPN) {
+        const int k0 = s * 16;
+        const f32x4 a0 = load4(pa + k0), a1 = load4(pb + k0), b = load4(pw + k0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float xv = sm.u.simt.xs[tg * 8 + i][c];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xv, wv[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j], b[j], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[j], b[j], acc1, 0, 0, 0);
+        }
       }
     }
-    __syncthreads();
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = eg + 64 * j;
-      if (e < p.E) sm.logits[tg * 8 + i][e] = acc[i][j];
+  __shared__ f32x4 red[NWAVES][2][MOE_WAVE];
+  if (WPN > 1) {  // block-uniform
+    red[wave][0][lane] = acc0;
+    red[wave][1][lane] = acc1;
+    __syncthreads();
+    if (phase == 0) {
+      for (int ph = 1; ph < WPN; ++ph) {
+        acc0 += red[wave + ph][0][lane];
+        acc1 += red[wave + ph][1][lane];
+      }
     }
+  }
+  if (active && phase == 0) {
+    const int e = nt * 16 + (lane & 15);
+    float* out = p.logits_part + (size_t)blockIdx.z * p.T * p.E;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ta = t0 + 4 * (lane >> 4) + i, tb = ta + 16;
+      if (e < p.E && ta < p.T) out[(size_t)ta * p.E + e] = acc0[i];
+      if (e < p.E && tb < p.T) out[(size_t)tb * p.E + e] = acc1[i];
+    }
+  }
 }
 
 // Arg-max over the wave of (value, index): larger value wins, equal values go
@@ -154,18 +151,17 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx, float& extra) {
   }
 }
 
-template <typename XT, typename WT, bool MFMA>
-__global__ __launch_bounds__(NTHREADS) void route_kernel(RouteParams p) {
-  __shared__ RouteSmem sm;
+struct SelectSmem {
+  float pe[NWAVES][kMaxExperts];
+  float zw[NWAVES];
+  int hist[kMaxExperts];
+};
+
+__global__ __launch_bounds__(NTHREADS) void route_select_kernel(RouteParams p) {
+  __shared__ SelectSmem sm;
   const int blk = blockIdx.x, t0 = blk * RT;
   const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
   for (int e = threadIdx.x; e < p.E; e += NTHREADS) sm.hist[e] = 0;
-
-  if constexpr (MFMA) {
-    logits_mfma(p, t0, sm);
-  } else {
-    logits_simt<XT, WT>(p, t0, sm);
-  }
   __syncthreads();
 
   const int E = p.E, k = p.k;
@@ -191,7 +187,23 @@ __global__ __launch_bounds__(NTHREADS) void route_kernel(RouteParams p) {
     float mloc = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      h[j] = ok[j] ? sm.logits[tl][lane + 64 * j] + lb[j] : -INFINITY;
+      float v = -INFINITY;
+      if (ok[j]) {
+        // K-split partials added in split order; loads issued 8 at a time.
+        const float* q = p.logits_part + (size_t)t * E + lane + 64 * j;
+        const size_t stride = (size_t)p.T * E;
+        v = 0.f;
+        for (int k0 = 0; k0 < p.ksplit; k0 += 8) {
+          float part[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) part[u] = k0 + u < p.ksplit ? q[(k0 + u) * stride] : 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (k0 + u < p.ksplit) v = (k0 + u == 0) ? part[u] : v + part[u];
+        }
+        v += lb[j];
+      }
+      h[j] = v;
       mloc = fmaxf(mloc, h[j]);
     }
     const float m = wave_max(mloc);
@@ -309,20 +321,20 @@ __global__ __launch_bounds__(NTHREADS) void route_kernel(RouteParams p) {
   }
 
   // Per-block partials, reduced across waves in a fixed order.
-  __syncthreads();  // the SIMT staging area is reused for the P_e partials
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    if (e < E) sm.u.pe[wave][e] = pacc[j];
+    if (e < E) sm.pe[wave][e] = pacc[j];
   }
   if (lane == 0) sm.zw[wave] = zacc;
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += NTHREADS) {
-    float s = sm.u.pe[0][e];
+    float s = sm.pe[0][e];
 #pragma unroll
-    for (int w = 1; w < NWAVES; ++w) s += sm.u.pe[w][e];
-    p.pe_part[(size_t)blk * E + e] = s;
-    p.hist[(size_t)blk * E + e] = sm.hist[e];
+    for (int w = 1; w < NWAVES; ++w) s += sm.pe[w][e];
+    const int nblk = gridDim.x;  // expert-major: column e holds the tiles in order
+    p.pe_part[(size_t)e * nblk + blk] = s;
+    p.hist[(size_t)e * nblk + blk] = sm.hist[e];
   }
   if (threadIdx.x == 0) {
     float s = sm.zw[0];
@@ -335,16 +347,21 @@ __global__ __launch_bounds__(NTHREADS) void route_kernel(RouteParams p) {
 }  // namespace
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s) {
-  const dim3 grid(route_blocks(p.T)), block(NTHREADS);
+  const int NT = (p.E + 15) / 16;
+  const int NTB = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
+  const dim3 grid(route_blocks(p.T), (NT + NTB - 1) / NTB, p.ksplit), block(NTHREADS);
   if (p.act_bf16 && p.router_bf16) {
-    hipLaunchKernelGGL((route_kernel<uint16_t, uint16_t, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((route_logits_kernel<uint16_t, uint16_t, true>), grid, block, 0, s, p);
   } else if (p.act_bf16) {
-    hipLaunchKernelGGL((route_kernel<uint16_t, float, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((route_logits_kernel<uint16_t, float, false>), grid, block, 0, s, p);
   } else if (p.router_bf16) {
-    hipLaunchKernelGGL((route_kernel<float, uint16_t, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((route_logits_kernel<float, uint16_t, false>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((route_kernel<float, float, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((route_logits_kernel<float, float, false>), grid, block, 0, s, p);
   }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_select_kernel, dim3(route_blocks(p.T)), block, 0, s, p);
   return hipGetLastError();
 }
 
