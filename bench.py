@@ -6,14 +6,21 @@ Mixtral-shaped workload (T=4096, d_model=4096, 8 SwiGLU experts of
 d_hidden=14336, top-2 softmax, dropless, bf16), with inputs resident in HBM,
 plus
   * ``roofline``: the grouped SwiGLU step (gate/up GEMM + down GEMM, the
-    dominant work) timed with HIP events on its stream inside the timed
-    region, against the bf16 dense MFMA peak; ``traffic`` comes from the
-    committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken on the
-    current kernel source, else null;
+    dominant work) timed with HIP events on its stream.  Its bound is the
+    one its algorithmic intensity selects: FLOP (6*D*H per kept row) per
+    algorithmic byte (the weights of every expert that keeps a row, the
+    gathered input rows and the output rows) against the ridge of the bf16
+    MFMA peak over the HBM peak.  ``traffic`` comes from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken on the current
+    kernel source, else null;
   * ``cpu_baseline``: the float64 CPU oracle on a bounded sample of tokens of
     the same workload, on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --pmc-summary FETCH_DB WRITE_DB --workload NAME
+The second form turns two rocprofv3 counter databases (one FETCH_SIZE pass,
+one WRITE_SIZE pass, each of a run with --copy-calibration) into the traffic
+summary that the first form reads.
 """
 from __future__ import annotations
 
@@ -46,6 +53,11 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB read + 1 GiB write kernel (torch.neg on "
+                         "fp32), the reference that scales the HBM byte counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="summarise two rocprofv3 counter databases and exit")
     return ap.parse_args()
 
 
@@ -70,6 +82,84 @@ def _traffic(workload, n_launch_units):
     if not m_hash or not m_bytes or m_hash.group(1) != _source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+CALIB_BYTES = 1 << 30           # bytes read (and written) by the calibration kernel
+
+
+def _copy_calibration(dev):
+    """A plain streaming kernel of known size: torch.neg over 2^28 fp32 values
+    reads 1 GiB and writes 1 GiB.  Its FETCH_SIZE / WRITE_SIZE readings give
+    the factor that turns counter units into bytes."""
+    import torch
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _pmc_means(db):
+    """Mean counter value per dispatch for each kernel of one rocprofv3 DB."""
+    import collections
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, dispatch_id, counter_name, counter_value, duration "
+                       "from pmc_events").fetchall()
+    per = collections.defaultdict(float)
+    dur = {}
+    for name, did, cn, v, d in rows:
+        per[(name, did, cn)] += v     # summed over hardware instances
+        dur[(name, did)] = d
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (name, did, cn), v in per.items():
+        out[name][cn].append(v)
+        out[name].setdefault("_dur", []).append(dur[(name, did)])
+    res = {n: {c: sum(v) / len(v) for c, v in d.items()} for n, d in out.items()}
+    for n, d in out.items():
+        res[n]["_n"] = len(d["_dur"])
+    return res
+
+
+def _short(name):
+    name = re.sub(r"\(anonymous namespace\)::", "", name).replace("void ", "")
+    return re.sub(r"\(moe::\w+Params(, int)?\)", "", name)
+
+
+def _pmc_summary(fetch_db, write_db, workload):
+    fetch, write = _pmc_means(fetch_db), _pmc_means(write_db)
+    calib = [n for n in fetch if "neg_kernel" in n]
+    assert calib, "no calibration kernel in the FETCH_SIZE run (use --copy-calibration)"
+    calib_w = [n for n in write if "neg_kernel" in n]
+    f_cal = fetch[calib[0]]["FETCH_SIZE"]
+    w_cal = write[calib_w[0]]["WRITE_SIZE"]
+    f_scale = CALIB_BYTES / f_cal
+    w_scale = CALIB_BYTES / w_cal
+    lines = [f"# HBM traffic of the MoE kernels: {workload}", "",
+             f"source_sha256_16: {_source_hash()}", "",
+             "FETCH_SIZE and WRITE_SIZE (rocprofv3, one pass each) per dispatch, scaled by",
+             "the readings of a plain torch.neg over 2^28 fp32 values (1 GiB read, 1 GiB",
+             f"written): FETCH_SIZE {f_cal:.6g} -> {f_scale:.4f} B per unit, "
+             f"WRITE_SIZE {w_cal:.6g} -> {w_scale:.4f} B per unit.  The calibration kernel "
+             f"itself moves 2 GiB in {fetch[calib[0]]['_dur'] / 1e3:.1f} us "
+             f"({2 * CALIB_BYTES / fetch[calib[0]]['_dur']:.0f} GB/s).", "",
+             "| kernel | dispatches | avg duration (us) | read (MB) | written (MB) | GB/s |",
+             "|---|---:|---:|---:|---:|---:|"]
+    step = 0.0
+    for name in sorted(n for n in fetch if "moe::" in n):
+        f = fetch[name]
+        wr = write.get(name, {})
+        rd = f["FETCH_SIZE"] * f_scale
+        wb = wr.get("WRITE_SIZE", 0.0) * w_scale
+        us = f["_dur"] / 1e3
+        lines.append(f"| `{_short(name)}` | {f['_n']} | {us:.1f} | {rd / 1e6:.1f} | "
+                     f"{wb / 1e6:.1f} | {(rd + wb) / us / 1e3:.0f} |")
+        if "gemm" in name:
+            step += rd + wb
+    lines += ["", "Grouped SwiGLU step (every gemm kernel above once per forward):", "",
+              f"hbm_bytes_per_step: {step:.6g}", ""]
+    return "\n".join(lines)
 
 
 def _cpu_baseline(w, inp, target_s):
@@ -122,6 +212,9 @@ def _cpu_baseline(w, inp, target_s):
 
 def main():
     args = _parse()
+    if args.pmc_summary:
+        print(_pmc_summary(*args.pmc_summary, args.workload))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer runs on a single MI355X; sharding is described in DESIGN.md).",
@@ -160,22 +253,13 @@ def main():
                         ws_up=inp.get("ws_up"), ws_down=inp.get("ws_down"), out=out,
                         expert_ids=ids, gate_w=gw, counts=counts, aux=aux, workspace=ws)
 
-    _log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        forward()
-    torch.cuda.synchronize()
-    _log(f"[bench] timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        forward()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = w.T / (elapsed / args.steps)
-    _log(f"[bench] {ms_per_step:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
-
-    # Stage-wise timing with HIP events on the launch stream: the same routing
-    # and permutation as the forward, each stage through its own entry point.
+    if args.copy_calibration:
+        _copy_calibration(dev)
+    # One step = one pass of the whole hot path through the C-ABI entry points
+    # (route, permute, grouped SwiGLU (+ shared expert), combine), with HIP
+    # events recorded between the stages on the launch stream.  The kernels and
+    # their order are those of moe_forward; the fused entry is timed after it
+    # as a cross-check.
     stream = torch.cuda.current_stream()
     cap = moe.capacity(cfg) if w.capacity_factor is not None else 0
     r = moe.moe_route(cfg, inp["x"], inp["w_router"], inp.get("logit_bias"),
@@ -184,16 +268,15 @@ def main():
     n_kept = int(perm["n_kept"].item())
     rows_bound = moe.max_rows(cfg)
     y = torch.empty(max(rows_bound, 1), w.D, dtype=out.dtype, device=dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    stage_ms = np.zeros(4)
     shared_y = torch.empty_like(out) if w.H_shared else None
-    for it in range(args.warmup + args.steps):
+
+    def step(ev):
         ev[0].record(stream)
         moe.moe_route(cfg, inp["x"], inp["w_router"], inp.get("logit_bias"),
                       inp.get("select_bias"), expert_ids=r["expert_ids"], gate_w=r["gate_w"],
                       counts=r["counts"], aux=r["aux"], mean_prob=r["mean_prob"], workspace=ws)
         ev[1].record(stream)
-        moe.moe_permute(cfg, r["expert_ids"], cap, workspace=ws)
+        moe.moe_permute(cfg, r["expert_ids"], cap, workspace=ws, **perm)
         ev[2].record(stream)
         moe.moe_grouped_swiglu(cfg, inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"],
                                row_to_assign=perm["row_to_assign"],
@@ -203,26 +286,64 @@ def main():
             moe.moe_grouped_swiglu(cfg, inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"],
                                    y_rows=shared_y, workspace=ws, validate=False)
         ev[3].record(stream)
-        moe.moe_combine(cfg, y, perm["assign_to_row"], shared_y, validate=False)
+        moe.moe_combine(cfg, y, perm["assign_to_row"], shared_y, out=out, validate=False)
         ev[4].record(stream)
-        ev[4].synchronize()
-        if it >= args.warmup:
-            stage_ms += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
-    stage_ms /= args.steps
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+              for _ in range(args.steps)]
+    _log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(events[i % args.steps])
+        forward()
+    torch.cuda.synchronize()
+    _log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = w.T / (elapsed / args.steps)
+    stage_ms = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+                         for ev in events]).mean(axis=0)
+    _log(f"[bench] {ms_per_step:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
     _log("[bench] stages ms: route %.4f permute %.4f grouped_swiglu %.4f combine %.4f"
          % tuple(stage_ms))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        forward()
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    _log(f"[bench] moe_forward: {fwd_ms:.3f} ms/step")
 
     # Algorithmic work of the grouped SwiGLU step: 2*D*H FLOP for each of the
-    # gate, up and down products per kept row (plus the shared expert on T rows).
+    # gate, up and down products per kept row (plus the shared expert on T
+    # rows); algorithmic bytes: the three weight matrices of every expert that
+    # keeps at least one row, the gathered input rows and the output rows.
     bf16 = w.act_dtype == "bf16"
+    esz = 2 if bf16 else 4
+    kept = np.diff(perm["expert_offsets"].cpu().numpy())
+    touched = int((kept > 0).sum())
     flops = 6.0 * w.D * w.H * n_kept + 6.0 * w.D * w.H_shared * w.T
-    achieved = flops / (stage_ms[2] * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    nbytes = (3.0 * w.D * w.H * touched * esz + 2.0 * n_kept * w.D * esz
+              + (3.0 * w.D * w.H_shared + 2.0 * w.T * w.D) * esz * (w.H_shared > 0))
+    sec = stage_ms[2] * 1e-3
+    peak_f = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     traffic = _traffic(w.name, 1)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+    mfma_bound = flops / nbytes >= peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        achieved, peak, unit = flops / sec / 1e12, peak_f, "TFLOP/s"
+    else:
+        achieved, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 2),
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": traffic,
                 "kernel": "grouped_swiglu step (gate/up GEMM + down GEMM)",
                 "algorithmic_flop_per_launch": flops,
+                "algorithmic_bytes_per_launch": nbytes,
+                "experts_with_rows": touched,
+                "tflops": round(flops / sec / 1e12, 2),
+                "hbm_gbs": round(nbytes / sec / 1e9, 1),
                 "launch_ms": round(float(stage_ms[2]), 4)}
 
     result = {
@@ -234,6 +355,7 @@ def main():
                    "experts": w.E, "top_k": w.top_k, "shared_d_hidden": w.H_shared,
                    "capacity_factor": w.capacity_factor, "kept_rows": n_kept,
                    "parallelism": "none (1 GPU)"},
+        "moe_forward_ms_per_step": round(fwd_ms, 4),
         "stages_ms": {k: round(float(v), 4) for k, v in
                       zip(("route", "permute", "grouped_swiglu", "combine"), stage_ms)},
         "roofline": roofline,

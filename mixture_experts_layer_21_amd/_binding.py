@@ -190,18 +190,27 @@ def moe_route(cfg, x, w_router, logit_bias=None, select_bias=None, *, expert_ids
             "mean_prob": mean_prob}
 
 
-def moe_permute(cfg, expert_ids, capacity_limit: int = 0, *, workspace=None):
+def moe_permute(cfg, expert_ids, capacity_limit: int = 0, *, expert_offsets=None,
+                row_to_assign=None, assign_to_row=None, n_kept=None, workspace=None):
     """Dispatch bookkeeping (see ``moe_permute``).  ``capacity_limit`` <= 0 is
-    dropless.  Returns expert_offsets, row_to_assign, assign_to_row, n_kept."""
+    dropless.  Returns expert_offsets, row_to_assign, assign_to_row, n_kept
+    (allocated here when not given; a row_to_assign allocated here starts as
+    -1, so rows past n_kept read -1)."""
     check_config(cfg)
     T, E, k = cfg.T, cfg.E, cfg.top_k
     dev = expert_ids.device
     _expect(expert_ids, "expert_ids", (T, k), torch.int32)
     rows = T * k
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    r2a = torch.full((rows,), -1, dtype=torch.int32, device=dev)
-    a2r = torch.empty(T * k, dtype=torch.int32, device=dev)
-    n_kept = torch.empty(1, dtype=torch.int32, device=dev)
+    _expect(expert_offsets, "expert_offsets", (E + 1,), torch.int32, required=False)
+    _expect(row_to_assign, "row_to_assign", (rows,), torch.int32, required=False)
+    _expect(assign_to_row, "assign_to_row", (rows,), torch.int32, required=False)
+    _expect(n_kept, "n_kept", (1,), torch.int32, required=False)
+    offsets = (torch.empty(E + 1, dtype=torch.int32, device=dev)
+               if expert_offsets is None else expert_offsets)
+    r2a = (torch.full((rows,), -1, dtype=torch.int32, device=dev)
+           if row_to_assign is None else row_to_assign)
+    a2r = torch.empty(rows, dtype=torch.int32, device=dev) if assign_to_row is None else assign_to_row
+    n_kept = torch.empty(1, dtype=torch.int32, device=dev) if n_kept is None else n_kept
     ws = new_workspace(cfg, dev) if workspace is None else workspace
     _check(_lib.moe_permute(ctypes.byref(cfg), _ptr(expert_ids), int(capacity_limit),
                             _ptr(offsets), _ptr(r2a), _ptr(a2r), _ptr(n_kept), _ptr(ws),

@@ -13,11 +13,11 @@
 //    wave runs 16x16 MFMA tiles (bf16 x bf16: 16x16x32 bf16, products exact;
 //    any fp32 operand: 16x16x4 fp32).  Waves sharing an expert tile split the
 //    k-steps and are summed through LDS in a fixed order.
-//  * route_select_kernel: one wave per token adds the K-split partials in a
-//    fixed order and does the scores, group limit, k arg-max rounds (butterfly
-//    shuffles; ties to the lower expert index) and weights.  Lane l holds
-//    experts l, l+64, l+128, l+192.  Every reduction has a fixed order, so
-//    results are bit-reproducible.
+//  * route_select_kernel: the block first adds the K-split partials of its
+//    32 tokens in split order into LDS; then one wave per token does the
+//    scores, group limit, k arg-max rounds (ties to the lower expert index)
+//    and weights.  Lane l holds experts l, l+64, l+128, l+192.  Every
+//    reduction has a fixed order, so results are bit-reproducible.
 #include <math.h>
 
 #include "common.hpp"
@@ -135,39 +135,187 @@ __global__ __launch_bounds__(NTHREADS) void route_logits_kernel(RouteParams p) {
   }
 }
 
-// Arg-max over the wave of (value, index): larger value wins, equal values go
-// to the lower index.  `extra` travels with the winner.
-__device__ __forceinline__ void wave_argmax(float& v, int& idx, float& extra) {
+// ---------------------------------------------------------------------------
+// Selection.  Cross-lane steps use DPP inside 16-lane rows (quad permutes,
+// half-row and row mirrors) and v_readlane across the four rows, instead of
+// LDS permutes: each all-reduce below is four DPP steps plus four readlanes.
+
+constexpr int SEL_THREADS = 512;
+constexpr int SEL_WAVES = SEL_THREADS / MOE_WAVE;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i inside each 8 lanes
+constexpr int DPP_ROW_MIRROR = 0x140;   // lane i <-> 15-i inside each 16 lanes
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Sum over the wave; every lane of a row holds the same row sum (partners
+// always hold disjoint lane sets, and IEEE addition is commutative), and the
+// four row sums are added in the fixed order (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<DPP_XOR1>(v);
+  v += dpp_f<DPP_XOR2>(v);
+  v += dpp_f<DPP_HALF_MIRROR>(v);
+  v += dpp_f<DPP_ROW_MIRROR>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+               fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
+  v = max(v, dpp_u<DPP_XOR1>(v));
+  v = max(v, dpp_u<DPP_XOR2>(v));
+  v = max(v, dpp_u<DPP_HALF_MIRROR>(v));
+  v = max(v, dpp_u<DPP_ROW_MIRROR>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Order-preserving unsigned key of a non-NaN float (-0 and +0 equal, as in a
+// float comparison).  Key 0 is below every float, including -inf: it marks
+// "not selectable".
+__device__ __forceinline__ uint32_t okey(float v) {
+  const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top-2 of two disjoint sets, each given as (first, second).
+__device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float b2) {
+  if (a1 >= b1) {
+    a2 = fmaxf(a2, b1);
+  } else {
+    a2 = fmaxf(a1, b2);
+    a1 = b1;
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ void top2_step(float& a1, float& a2) {
+  top2_merge(a1, a2, dpp_f<CTRL>(a1), dpp_f<CTRL>(a2));
+}
+
+// One arg-max round over the wave: among the keys of this lane's four slots
+// (slot j is expert lane + 64 j), the largest key wins; equal keys go to the
+// lower expert index.  Returns the winner's lane and slot (wave-uniform).
+__device__ __forceinline__ void wave_argmax_key(const uint32_t (&key)[4], int& wl, int& wj) {
+  uint32_t lk = key[0];
+  int lj = 0;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(v, m, MOE_WAVE);
-    const int oi = __shfl_xor(idx, m, MOE_WAVE);
-    const float ox = __shfl_xor(extra, m, MOE_WAVE);
-    if (ov > v || (ov == v && oi < idx)) {
-      v = ov;
-      idx = oi;
-      extra = ox;
+  for (int j = 1; j < 4; ++j)
+    if (key[j] > lk) {
+      lk = key[j];
+      lj = j;
+    }
+  const uint32_t M = wave_max_key(lk);
+  wl = 0;
+  wj = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t m = __ballot(lk == M && lj == j);
+    if (m) {
+      wl = __ffsll((unsigned long long)m) - 1;
+      wj = j;
+      break;
     }
   }
 }
 
+template <typename V>
+__device__ __forceinline__ V pick4(const V (&a)[4], int j) {
+  return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
+}
+
 struct SelectSmem {
-  float pe[NWAVES][kMaxExperts];
-  float zw[NWAVES];
+  float lg[RT * kMaxExperts];      // summed logits of the block's tokens, row stride E
+  float pe[SEL_WAVES][kMaxExperts];
+  float zw[SEL_WAVES];
   int hist[kMaxExperts];
 };
 
-__global__ __launch_bounds__(NTHREADS) void route_select_kernel(RouteParams p) {
+// Phase 1: the block's [RT x E] logits, the K-split partials added in split
+// order, into LDS (all threads, 16-byte loads, up to 16 loads in flight).
+// Phase 2: one wave per token: scores, group limit, k arg-max rounds,
+// weights; per-block P_e and z partials and the expert histogram.
+__global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p) {
   __shared__ SelectSmem sm;
   const int blk = blockIdx.x, t0 = blk * RT;
   const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
-  for (int e = threadIdx.x; e < p.E; e += NTHREADS) sm.hist[e] = 0;
+  const int E = p.E, k = p.k;
+  const int nt = min(RT, p.T - t0);
+  for (int e = threadIdx.x; e < E; e += SEL_THREADS) sm.hist[e] = 0;
+  {
+    const int ks = p.ksplit;
+    const int L = nt * E;
+    const size_t stride = (size_t)p.T * E;
+    const float* base = p.logits_part + (size_t)t0 * E;
+    if ((E & 3) == 0) {
+      const int L4 = L >> 2;
+      const f32x4* b4 = reinterpret_cast<const f32x4*>(base);
+      const size_t s4 = stride >> 2;
+      for (int i0 = threadIdx.x; i0 < L4; i0 += 2 * SEL_THREADS) {
+        const int i1 = i0 + SEL_THREADS;
+        const bool has1 = i1 < L4;
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+        for (int k0 = 0; k0 < ks; k0 += 8) {
+          f32x4 a[8], b[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if (k0 + u < ks) {
+              a[u] = b4[(k0 + u) * s4 + i0];
+              if (has1) b[u] = b4[(k0 + u) * s4 + i1];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if (k0 + u < ks) {
+              s0 = (k0 + u == 0) ? a[u] : s0 + a[u];
+              if (has1) s1 = (k0 + u == 0) ? b[u] : s1 + b[u];
+            }
+          }
+        }
+        *reinterpret_cast<f32x4*>(&sm.lg[4 * i0]) = s0;
+        if (has1) *reinterpret_cast<f32x4*>(&sm.lg[4 * i1]) = s1;
+      }
+    } else {
+      for (int i = threadIdx.x; i < L; i += SEL_THREADS) {
+        float s = 0.f;
+        for (int k0 = 0; k0 < ks; k0 += 8) {
+          float a[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (k0 + u < ks) a[u] = base[(k0 + u) * stride + i];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (k0 + u < ks) s = (k0 + u == 0) ? a[u] : s + a[u];
+        }
+        sm.lg[i] = s;
+      }
+    }
+  }
   __syncthreads();
 
-  const int E = p.E, k = p.k;
   const bool sigm = p.score_func == 1;
   const bool by_score = sigm || p.select_bias != nullptr;
   const int gsz = p.n_groups > 1 ? E / p.n_groups : E;
+  // Group limit with a segmented reduction: groups are aligned runs of gsz
+  // lanes in one slot when gsz is a power of two below 64.
+  const bool seg_groups = p.n_groups > 1 && gsz < 64 && (gsz & (gsz - 1)) == 0;
   float lb[4], sb[4];
   bool ok[4];
 #pragma unroll
@@ -180,40 +328,23 @@ __global__ __launch_bounds__(NTHREADS) void route_select_kernel(RouteParams p) {
   float pacc[4] = {0.f, 0.f, 0.f, 0.f};
   float zacc = 0.f;
 
-  for (int tl = wave; tl < RT; tl += NWAVES) {
+  for (int tl = wave; tl < nt; tl += SEL_WAVES) {
     const int t = t0 + tl;
-    if (t >= p.T) break;  // wave-uniform
     float h[4], sc[4], sel[4];
     float mloc = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float v = -INFINITY;
-      if (ok[j]) {
-        // K-split partials added in split order; loads issued 8 at a time.
-        const float* q = p.logits_part + (size_t)t * E + lane + 64 * j;
-        const size_t stride = (size_t)p.T * E;
-        v = 0.f;
-        for (int k0 = 0; k0 < p.ksplit; k0 += 8) {
-          float part[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) part[u] = k0 + u < p.ksplit ? q[(k0 + u) * stride] : 0.f;
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (k0 + u < p.ksplit) v = (k0 + u == 0) ? part[u] : v + part[u];
-        }
-        v += lb[j];
-      }
-      h[j] = v;
+      h[j] = ok[j] ? sm.lg[tl * E + lane + 64 * j] + lb[j] : -INFINITY;
       mloc = fmaxf(mloc, h[j]);
     }
-    const float m = wave_max(mloc);
+    const float m = wave_max_dpp(mloc);
     float ex[4], sloc = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       ex[j] = ok[j] ? expf(h[j] - m) : 0.f;
       sloc += ex[j];
     }
-    const float S = wave_sum(sloc);
+    const float S = wave_sum_dpp(sloc);
     const float lse = m + logf(S);
     zacc += lse * lse;
     if (!sigm) {
@@ -229,7 +360,7 @@ __global__ __launch_bounds__(NTHREADS) void route_select_kernel(RouteParams p) {
         sc[j] = ok[j] ? 1.0f / (1.0f + expf(-h[j])) : 0.f;
         ssl += sc[j];
       }
-      const float ss = wave_sum(ssl);
+      const float ss = wave_sum_dpp(ssl);
 #pragma unroll
       for (int j = 0; j < 4; ++j) pacc[j] += sc[j] / ss;
     }
@@ -242,76 +373,81 @@ __global__ __launch_bounds__(NTHREADS) void route_select_kernel(RouteParams p) {
 
     bool allowed[4] = {ok[0], ok[1], ok[2], ok[3]};
     if (p.n_groups > 1) {
-      float gmine = -INFINITY;
-      for (int g = 0; g < p.n_groups; ++g) {
-        float a1 = -INFINITY, a2 = -INFINITY;
+      // Group score of every group, then group g's key in lane g.
+      uint32_t gkey = 0;
+      if (seg_groups) {
+        float a1[4], a2[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (ok[j] && (lane + 64 * j) / gsz == g) {
-            const float v = sel[j];
-            if (v > a1) {
-              a2 = a1;
-              a1 = v;
-            } else if (v > a2) {
-              a2 = v;
-            }
-          }
+          a1[j] = sel[j];
+          a2[j] = -INFINITY;
+          if (gsz >= 2) top2_step<DPP_XOR1>(a1[j], a2[j]);
+          if (gsz >= 4) top2_step<DPP_XOR2>(a1[j], a2[j]);
+          if (gsz >= 8) top2_step<DPP_HALF_MIRROR>(a1[j], a2[j]);
+          if (gsz >= 16) top2_step<DPP_ROW_MIRROR>(a1[j], a2[j]);
+          if (gsz >= 32)
+            top2_merge(a1[j], a2[j], __shfl_xor(a1[j], 16, MOE_WAVE),
+                       __shfl_xor(a2[j], 16, MOE_WAVE));
         }
+        // Group g lives in slot g / (64/gsz), lanes of segment g % (64/gsz).
+        const int per_slot = MOE_WAVE / gsz;
+        const int g = lane;
+        const int gj = min(g / per_slot, 3), src = (g % per_slot) * gsz;
+        float gs = -INFINITY;
 #pragma unroll
-        for (int msk = 32; msk >= 1; msk >>= 1) {
-          const float b1 = __shfl_xor(a1, msk, MOE_WAVE);
-          const float b2 = __shfl_xor(a2, msk, MOE_WAVE);
-          if (a1 >= b1) {
-            a2 = fmaxf(a2, b1);
-          } else {
-            a2 = fmaxf(a1, b2);
-            a1 = b1;
-          }
+        for (int j = 0; j < 4; ++j) {
+          const float s1 = __shfl(a1[j], src, MOE_WAVE), s2 = __shfl(a2[j], src, MOE_WAVE);
+          if (gj == j) gs = p.group_rule == 0 ? s1 + s2 : s1;
         }
-        const float gs = p.group_rule == 0 ? a1 + a2 : a1;
-        if (lane == g) gmine = gs != gs ? -INFINITY : gs;
+        if (g < p.n_groups) gkey = okey(gs != gs ? -INFINITY : gs);
+      } else {
+        for (int g = 0; g < p.n_groups; ++g) {
+          float a1 = -INFINITY, a2 = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (ok[j] && (lane + 64 * j) / gsz == g) top2_merge(a1, a2, sel[j], -INFINITY);
+          }
+#pragma unroll
+          for (int msk = 32; msk >= 1; msk >>= 1)
+            top2_merge(a1, a2, __shfl_xor(a1, msk, MOE_WAVE), __shfl_xor(a2, msk, MOE_WAVE));
+          const float gs = p.group_rule == 0 ? a1 + a2 : a1;
+          if (lane == g) gkey = okey(gs != gs ? -INFINITY : gs);
+        }
       }
       uint64_t gmask = 0;
-      bool gtaken = false;
+      uint32_t gk[4] = {gkey, 0u, 0u, 0u};
       for (int r = 0; r < p.topk_groups; ++r) {
-        float v = (lane < p.n_groups && !gtaken) ? gmine : -INFINITY;
-        int gi = (lane < p.n_groups && !gtaken) ? lane : 0x7fffffff;
-        float dummy = 0.f;
-        wave_argmax(v, gi, dummy);
-        gmask |= 1ull << gi;
-        if (lane == gi) gtaken = true;
+        int wl, wj;
+        wave_argmax_key(gk, wl, wj);
+        gmask |= 1ull << wl;
+        if (lane == wl) gk[0] = 0u;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         allowed[j] = ok[j] && ((gmask >> ((lane + 64 * j) / gsz)) & 1ull);
     }
 
-    uint32_t taken = 0;
+    uint32_t key[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) key[j] = allowed[j] ? okey(sel[j]) : 0u;
     int my_id = 0;
     float my_sc = 0.f;
     for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY, bsc = 0.f;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (allowed[j] && !((taken >> j) & 1u)) {
-          const int e = lane + 64 * j;
-          if (sel[j] > bv || (sel[j] == bv && e < be)) {
-            bv = sel[j];
-            be = e;
-            bsc = sc[j];
-          }
-        }
-      }
-      wave_argmax(bv, be, bsc);
+      int wl, wj;
+      wave_argmax_key(key, wl, wj);
+      const float wsc = readlane_f(pick4(sc, wj), wl);
       if (lane == r) {
-        my_id = be;
-        my_sc = bsc;
+        my_id = wl + 64 * wj;
+        my_sc = wsc;
       }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
+      if (lane == wl) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j == wj) key[j] = 0u;
+      }
     }
     my_id = min(max(my_id, 0), E - 1);  // always a valid expert (see NaN note)
-    const float ssel = wave_sum(lane < k ? my_sc : 0.f);
+    const float ssel = wave_sum_dpp(lane < k ? my_sc : 0.f);
     if (lane < k) {
       const float wgt = p.renormalize ? p.route_scale * (my_sc / ssel) : p.route_scale * my_sc;
       p.ids[(size_t)t * k + lane] = my_id;
@@ -328,10 +464,10 @@ __global__ __launch_bounds__(NTHREADS) void route_select_kernel(RouteParams p) {
   }
   if (lane == 0) sm.zw[wave] = zacc;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += NTHREADS) {
+  for (int e = threadIdx.x; e < E; e += SEL_THREADS) {
     float s = sm.pe[0][e];
 #pragma unroll
-    for (int w = 1; w < NWAVES; ++w) s += sm.pe[w][e];
+    for (int w = 1; w < SEL_WAVES; ++w) s += sm.pe[w][e];
     const int nblk = gridDim.x;  // expert-major: column e holds the tiles in order
     p.pe_part[(size_t)e * nblk + blk] = s;
     p.hist[(size_t)e * nblk + blk] = sm.hist[e];
@@ -339,7 +475,7 @@ __global__ __launch_bounds__(NTHREADS) void route_select_kernel(RouteParams p) {
   if (threadIdx.x == 0) {
     float s = sm.zw[0];
 #pragma unroll
-    for (int w = 1; w < NWAVES; ++w) s += sm.zw[w];
+    for (int w = 1; w < SEL_WAVES; ++w) s += sm.zw[w];
     p.z_part[blk] = s;
   }
 }
@@ -361,7 +497,7 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_select_kernel, dim3(route_blocks(p.T)), block, 0, s, p);
+  hipLaunchKernelGGL(route_select_kernel, dim3(route_blocks(p.T)), dim3(SEL_THREADS), 0, s, p);
   return hipGetLastError();
 }
 

@@ -90,6 +90,35 @@ def test_route_small(moe, name):
     _say(f"  near ties flagged {nflag}, differing {ndiff}")
 
 
+# Group-limit shapes: group sizes 2..32 (segmented in-wave reduction), 64 and
+# 12 (the general path), both group rules, and softmax as well as sigmoid.
+GROUP_CASES = [
+    # E, n_groups, topk_groups, k, rule, score
+    (64, 32, 8, 6, "top2sum", "sigmoid"),
+    (64, 16, 4, 8, "top2sum", "sigmoid"),
+    (128, 8, 3, 8, "top2sum", "softmax"),
+    (256, 8, 4, 8, "max", "sigmoid"),
+    (256, 4, 2, 8, "top2sum", "sigmoid"),
+    (48, 4, 2, 6, "top2sum", "sigmoid"),
+    (96, 3, 1, 4, "max", "softmax"),
+]
+
+
+@pytest.mark.parametrize("E,ng,tg,k,rule,score", GROUP_CASES)
+def test_route_group_limits(moe, E, ng, tg, k, rule, score):
+    w = W.SMALL["deepseek_small"].with_(
+        seq=173, E=E, top_k=k, n_groups=ng, topk_groups=tg, group_rule=rule, score=score,
+        route_scale=2.5 if score == "sigmoid" else 1.0, H_shared=0)
+    _say(f"[route-groups] E={E} groups={ng} keep={tg} k={k} {rule} {score}")
+    inp = W.make_inputs(w, "cpu", seed=3)
+    cfg = P.config_of(w)
+    g = _route(moe, w, cfg, _to_dev(inp))
+    torch.cuda.synchronize()
+    r = P.oracle_route(w, P.oracle_inputs(inp))
+    nflag, ndiff = P.compare_route(w, r, g)
+    _say(f"  near ties flagged {nflag}, differing {ndiff}")
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_route_deterministic(moe, name):
     w = W.SMALL[name]
