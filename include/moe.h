@@ -153,8 +153,15 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* expert_ids,
  *                      offsets[n_experts] are neither read nor written
  *   w_gate, w_up       [n_experts, hidden, D]; w_down [n_experts, D, hidden]
  *   y_rows             [max_rows, D] act_dtype out
+ *   workspace          at least max_rows*hidden act_dtype elements (the
+ *                      silu(g)*u rows); a workspace of moe_workspace_bytes(cfg)
+ *                      also holds the fp32 partial tiles with which the bf16
+ *                      large-tile kernels split their last round along K
+ *                      (without that room they run the last round unsplit;
+ *                      results agree to rounding either way)
  * fp32 accumulation; silu(g)*u is rounded once to act_dtype between the two
- * GEMMs; the gate weight is applied in fp32 before the final rounding. */
+ * GEMMs; the gate weight is applied in fp32 before the final rounding.
+ * Results are deterministic for a given configuration and routing. */
 moe_status moe_grouped_swiglu(const moe_config* cfg, int32_t n_experts, int32_t hidden,
                               const void* x, const int32_t* row_to_assign,
                               const int32_t* expert_offsets, int32_t max_rows,

@@ -23,6 +23,8 @@
 // fp32: the same tiling with plain FMA (small layers only).
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -311,6 +313,7 @@ struct DmaCfg {
   static_assert(A_LD >= 1 && B_LD >= 1 && MI >= 1 && NI >= 1, "tile shape");
   static_assert(BM * KCH % (64 * NW) == 0 && BNB * KCH % (64 * NW) == 0, "tile shape");
   static_assert(S_ >= 2 && S_ <= 4 && (S_ - 2) * LPS < 64, "stages");
+  static_assert(NT >= NTHREADS, "the tile decode scans the expert offsets with 256 threads");
 };
 
 template <class C, bool GATEUP>
@@ -474,8 +477,101 @@ __device__ __forceinline__ void dma_mainloop(
   wait_vmcnt<0>();
 }
 
+// Epilogue of a finished tile (32x32 accumulator layout: element i of lane l
+// is row 8*(i/4) + 4*(l/32) + (i%4), column l%32): SiLU(gate)*up into Hb, or
+// the gate weight times the down product into Y, rounded once to bf16.
+template <class C, bool GATEUP>
+__device__ __forceinline__ void dma_epilogue(const GemmParams& p, int m0, int m_end, int n0,
+                                             int wm, int wn, int lr, int lk,
+                                             const f32x16 (&acc)[C::NB][C::MI][C::NI]) {
+  const int N = GATEUP ? p.hidden : p.D;
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int grow = m0 + wm * C::WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
+      if (grow >= m_end) continue;
+      if constexpr (GATEUP) {
+        uint16_t* out = static_cast<uint16_t*>(p.hbuf) + (size_t)grow * N;
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni) {
+          const int col = n0 + wn * C::WN + ni * 32 + lr;
+          if (col < N) out[col] = f32_to_bf16_bits(silu_f32(acc[0][mi][ni][i]) * acc[1][mi][ni][i]);
+        }
+      } else {
+        float gw = 1.f;
+        if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[grow]];
+        uint16_t* out = static_cast<uint16_t*>(p.y) + (size_t)grow * N;
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni) {
+          const int col = n0 + wn * C::WN + ni * 32 + lr;
+          if (col < N) out[col] = f32_to_bf16_bits(gw * acc[0][mi][ni][i]);
+        }
+      }
+    }
+  }
+}
+
+// Partial tiles are stored in accumulator order, vector v of thread t at
+// [v][t], so every store and load of a wave covers 1 KB contiguously.
+template <class C>
+constexpr int partial_vectors() { return C::NB * C::MI * C::NI * 4; }
+
+template <class C, bool GATEUP>
+__device__ __forceinline__ void dma_store_partial(float* slot, int tid,
+                                                  const f32x16 (&acc)[C::NB][C::MI][C::NI]) {
+  static_assert((size_t)partial_vectors<C>() * C::NT * 16 <= kTailSlotBytes, "tail slot size");
+  f32x4* dst = reinterpret_cast<f32x4*>(slot);
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int v = ((nb * C::MI + mi) * C::NI + ni) * 4 + q;
+          dst[v * C::NT + tid] = f32x4{acc[nb][mi][ni][4 * q], acc[nb][mi][ni][4 * q + 1],
+                                       acc[nb][mi][ni][4 * q + 2], acc[nb][mi][ni][4 * q + 3]};
+        }
+}
+
+// One block per (XCD, tail tile): adds the tile's partials in piece order and
+// runs the tile's epilogue.  Runs after the GEMM kernel on the same stream.
 template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
-__global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int max_mtiles) {
+__global__ __launch_bounds__(64 * NWV) void gemm_tail_reduce_kernel(GemmParams p) {
+  using C = DmaCfg<BM, BNB, BK, S, WGM, NWV, GATEUP>;
+  const int xcd = blockIdx.x / kTailSlots, j = blockIdx.x % kTailSlots;
+  const int r = p.tail_meta[2 * xcd], ns = p.tail_meta[2 * xcd + 1];
+  if (j >= r) return;
+  const int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + j) * 4;
+  const int m0 = d[1], m_end = d[2], nt = d[3];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  f32x16 acc[C::NB][C::MI][C::NI];
+  for (int pc = 0; pc < ns; ++pc) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(
+        p.tail_part + (size_t)(xcd * kTailSlots + j * ns + pc) * (kTailSlotBytes / 4));
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int v = ((nb * C::MI + mi) * C::NI + ni) * 4 + q;
+            const f32x4 x = src[v * C::NT + tid];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              acc[nb][mi][ni][4 * q + u] = pc == 0 ? x[u] : acc[nb][mi][ni][4 * q + u] + x[u];
+          }
+  }
+  dma_epilogue<C, GATEUP>(p, m0, m_end, nt * C::BN, wave / C::WGN, wave % C::WGN, lane & 31,
+                          lane >> 5, acc);
+}
+
+template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
+__global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int tail_slots) {
   using C = DmaCfg<BM, BNB, BK, S, WGM, NWV, GATEUP>;
   constexpr int KCH = C::KCH, MI = C::MI, NI = C::NI, NB = C::NB;
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[BM * BK];
@@ -488,40 +584,24 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ma
   __shared__ __attribute__((aligned(1024))) uint16_t sB3[S > 3 ? BNB * BK : 8];
   __shared__ int s_scan[NTHREADS + 4];
 
-  // find_tile uses the first 256 threads for its scan; all 512 take part in
-  // its barriers.
+  // Tile decode.  The active tiles (row tiles of every expert x column
+  // tiles) are dealt to the XCDs in contiguous runs; block b runs on XCD b%8
+  // as that XCD's (b/8)-th block.  Each XCD runs its whole rounds of
+  // tail_slots tiles at full depth; the r tiles left over are each cut along
+  // K into nsplit pieces, so the last round is short.  Pieces write fp32
+  // partial tiles that gemm_tail_reduce_kernel adds in piece order.
   Tile tile;
+  int piece = -1, nsplit = 1, tail_slot = 0, tail_tile = 0;
   {
-    const int G = gridDim.x, b = blockIdx.x;
-    const int xcd = b & 7, q = G >> 3, rem = G & 7;
-    const int L = xcd * q + min(xcd, rem) + (b >> 3);
-    // Logical tiles run in bands of GN column tiles; inside a band the GN
-    // column tiles of one row tile are consecutive.  The blocks an XCD holds
-    // at once then cover about (32/GN) row tiles x GN column tiles, so each
-    // A slice is fetched into that XCD's L2 once for GN blocks and each B
-    // slice once for the row tiles of its expert.
-    constexpr int GN = MOE_BAND;
-    const int ntiles = G / max_mtiles;
-    const int full = ntiles / GN;
-    int ml;
-    if (L < full * max_mtiles * GN) {
-      const int r = L % (max_mtiles * GN);
-      ml = r / GN;
-      tile.nt = (L / (max_mtiles * GN)) * GN + r % GN;
-    } else {
-      const int w = ntiles - full * GN;
-      const int r = L - full * max_mtiles * GN;
-      ml = r / w;
-      tile.nt = full * GN + r % w;
-    }
+    const int tid = threadIdx.x;
+    const int ntiles = ((GATEUP ? p.hidden : p.D) + C::BN - 1) / C::BN;
+    const int nk = (GATEUP ? p.D : p.hidden) / BK;
+    int total, cnt = 0;
     if (p.expert_offsets == nullptr) {
-      tile.e = 0;
-      tile.m0 = ml * BM;
-      tile.m_end = p.T;
-      if (tile.m0 >= p.T) return;
+      total = (p.T + BM - 1) / BM;
     } else {
-      const int tid = threadIdx.x;
-      int cnt = 0;
+      // Inclusive scan of the per-expert row-tile counts; the first 256
+      // threads scan, all threads take part in the barriers.
       if (tid < p.n_groups) {
         const int rows = p.expert_offsets[tid + 1] - p.expert_offsets[tid];
         cnt = (rows + BM - 1) / BM;
@@ -534,8 +614,61 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ma
         if (tid < NTHREADS) s_scan[tid] += v;
         __syncthreads();
       }
-      const int total = s_scan[NTHREADS - 1];
-      if (ml >= total) return;
+      total = s_scan[NTHREADS - 1];
+    }
+    const int A = total * ntiles;
+    const int b = blockIdx.x, xcd = b % kXcds, i = b / kXcds;
+    const int ax = A / kXcds + (xcd < A % kXcds ? 1 : 0);
+    const int start = xcd * (A / kXcds) + min(xcd, A % kXcds);
+    int nfull = ax, r = 0;
+    if (tail_slots > 0) {
+      nfull = ax / tail_slots * tail_slots;
+      r = ax - nfull;
+      nsplit = r > 0 ? min(min(tail_slots / r, 16), nk) : 1;
+      if (nsplit < 2) {
+        nfull = ax;
+        r = 0;
+        nsplit = 1;
+      }
+      if (i == 0 && tid == 0) {
+        p.tail_meta[2 * xcd] = r;
+        p.tail_meta[2 * xcd + 1] = nsplit;
+      }
+    }
+    int L;
+    if (i < nfull) {
+      L = start + i;
+    } else if (i < nfull + r * nsplit) {
+      tail_tile = (i - nfull) / nsplit;
+      piece = (i - nfull) % nsplit;
+      tail_slot = xcd * kTailSlots + (i - nfull);
+      L = start + nfull + tail_tile;
+    } else {
+      return;  // uniform across the block
+    }
+    // Logical tiles run in bands of GN column tiles; inside a band the GN
+    // column tiles of one row tile are consecutive.  The blocks an XCD holds
+    // at once then cover about (32/GN) row tiles x GN column tiles, so each
+    // A slice is fetched into that XCD's L2 once for GN blocks and each B
+    // slice once for the row tiles of its expert.
+    constexpr int GN = MOE_BAND;
+    const int full = ntiles / GN;
+    int ml;
+    if (L < full * total * GN) {
+      const int rr = L % (total * GN);
+      ml = rr / GN;
+      tile.nt = (L / (total * GN)) * GN + rr % GN;
+    } else {
+      const int w = ntiles - full * GN;
+      const int rr = L - full * total * GN;
+      ml = rr / w;
+      tile.nt = full * GN + rr % w;
+    }
+    if (p.expert_offsets == nullptr) {
+      tile.e = 0;
+      tile.m0 = ml * BM;
+      tile.m_end = p.T;
+    } else {
       if (tid < p.n_groups) {
         const int hi = s_scan[tid], lo = hi - cnt;
         if (ml >= lo && ml < hi) {
@@ -548,6 +681,13 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ma
       tile.e = s_scan[NTHREADS];
       tile.m0 = s_scan[NTHREADS + 1];
       tile.m_end = s_scan[NTHREADS + 2];
+    }
+    if (piece == 0 && tid == 0) {
+      int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + tail_tile) * 4;
+      d[0] = tile.e;
+      d[1] = tile.m0;
+      d[2] = tile.m_end;
+      d[3] = tile.nt;
     }
   }
 
@@ -604,6 +744,15 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ma
   // B rows [0, BN) come from rG, [BN, 2BN) from rU (GATEUP); wave loads never
   // straddle the two halves because BN*KCH is a multiple of 64.
 
+  // K range: all k-steps, or this piece's share of a split tail tile.
+  const int nk = K / BK;
+  const int kb = piece < 0 ? 0 : piece * nk / nsplit;
+  const int ke = piece < 0 ? nk : (piece + 1) * nk / nsplit;
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i) a_off[i] += (uint32_t)kb * BK * 2u;
+#pragma unroll
+  for (int i = 0; i < C::B_LD; ++i) b_off[i] += (uint32_t)kb * BK * 2u;
+
   const DmaLoads<C, GATEUP> ld{rA, rG, rU, a_off, b_off, wave};
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int lr = lane & 31, lk = lane >> 5;
@@ -617,36 +766,14 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ma
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[nb][mi][ni][i] = 0.f;
 
-  dma_mainloop<C, GATEUP>(ld, K / BK, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3, sB0, sB1, sB2,
+  dma_mainloop<C, GATEUP>(ld, ke - kb, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3, sB0, sB1, sB2,
                           sB3);
-
-  // Epilogue (32x32 accumulator layout: element i of lane l is row
-  // 8*(i/4) + 4*(l/32) + (i%4), column l%32).
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int grow = tile.m0 + wm * C::WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
-      if (grow >= tile.m_end) continue;
-      if constexpr (GATEUP) {
-        uint16_t* out = static_cast<uint16_t*>(p.hbuf) + (size_t)grow * N;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int col = n0 + wn * C::WN + ni * 32 + lr;
-          if (col < N) out[col] = f32_to_bf16_bits(silu_f32(acc[0][mi][ni][i]) * acc[1][mi][ni][i]);
-        }
-      } else {
-        float gw = 1.f;
-        if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[grow]];
-        uint16_t* out = static_cast<uint16_t*>(p.y) + (size_t)grow * N;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int col = n0 + wn * C::WN + ni * 32 + lr;
-          if (col < N) out[col] = f32_to_bf16_bits(gw * acc[0][mi][ni][i]);
-        }
-      }
-    }
+  if (piece >= 0) {
+    dma_store_partial<C, GATEUP>(p.tail_part + (size_t)tail_slot * (kTailSlotBytes / 4), tid,
+                                 acc);
+    return;
   }
+  dma_epilogue<C, GATEUP>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc);
 }
 
 // fp32 path: 64x64 tiles, 16x16 threads with 4x4 outputs each (rows ty+16i,
@@ -758,15 +885,42 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Resident blocks per XCD of one kernel on the current device (0 when the
+// CUs do not split evenly over the XCDs); cached per device.
+template <class Kern>
+int slots_per_xcd(Kern kern, int threads) {
+  static int cache[64];
+  static bool have[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!have[dev]) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess)
+      return 0;
+    cache[dev] = (cus % kXcds == 0) ? std::min(kTailSlots, occ * cus / kXcds) : 0;
+    have[dev] = true;
+  }
+  return cache[dev];
+}
+
 template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
 hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
   using C = DmaCfg<BM, BNB, BK, S, WGM, NWV, GATEUP>;
+  const auto kern = gemm_dma_kernel<BM, BNB, BK, S, WGM, NWV, GATEUP>;
   const int N = GATEUP ? p.hidden : p.D;
   const int mt = mtiles_bound(p, BM);
-  const long long nblocks = (long long)mt * ((N + C::BN - 1) / C::BN);
-  if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_dma_kernel<BM, BNB, BK, S, WGM, NWV, GATEUP>),
-                     dim3((unsigned)nblocks), dim3(64 * NWV), 0, s, p, mt);
+  const long long tiles = (long long)mt * ((N + C::BN - 1) / C::BN);
+  if (tiles <= 0) return hipSuccess;
+  const int slots = p.tail_part ? slots_per_xcd(kern, C::NT) : 0;
+  // Every XCD gets at most ceil(tiles/8) tiles plus at most `slots` extra
+  // blocks for the pieces of its split tail.
+  const long long nblocks = kXcds * ((tiles + kXcds - 1) / kXcds + slots);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(C::NT), 0, s, p, slots);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || slots == 0) return err;
+  hipLaunchKernelGGL((gemm_tail_reduce_kernel<BM, BNB, BK, S, WGM, NWV, GATEUP>),
+                     dim3(kXcds * kTailSlots), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -71,7 +71,21 @@ struct GemmParams {
   const void* w_down;
   void* hbuf;                // [max_rows, hidden]
   void* y;                   // [max_rows, D]
+  // Split-K tail of the large-tile kernel (null: no split).  Per XCD: the
+  // fp32 partial tiles [kTailSlots], the (tail tiles, pieces) pair and the
+  // tile descriptors (expert, first row, row end, column tile).
+  float* tail_part;
+  int32_t* tail_meta;        // [kXcds * 2]
+  int32_t* tail_desc;        // [kXcds * kTailSlots * 4]
 };
+
+// Split-K tail bookkeeping of the large-tile grouped GEMM.
+constexpr int kXcds = 8;
+constexpr int kTailSlots = 32;                       // partial tiles per XCD
+constexpr size_t kTailSlotBytes = (size_t)256 * 256 * 4;  // one fp32 256x256 tile
+inline size_t tail_workspace_bytes() {
+  return (size_t)kXcds * kTailSlots * kTailSlotBytes + 256 + (size_t)kXcds * kTailSlots * 16;
+}
 
 struct CombineParams {
   int T, D, k;

@@ -105,7 +105,7 @@ long long max_rows_of(const moe_config* c) {
 
 struct Layout {
   size_t ids, gate_w, counts, aux, logits, hist, pe_part, z_part, block_base, counts_ws, pe_ws,
-      offsets, n_kept, r2a, a2r, hbuf, y, shared_y, total;
+      offsets, n_kept, r2a, a2r, hbuf, y, shared_y, tail, total;
 };
 
 Layout layout_of(const moe_config* c) {
@@ -139,6 +139,7 @@ Layout layout_of(const moe_config* c) {
   L.hbuf = take(std::max(rows * (size_t)c->H, T * (size_t)c->H_shared) * es);
   L.y = take(rows * D * es);
   L.shared_y = take(c->H_shared ? T * D * es : 0);
+  L.tail = take(c->act_dtype == MOE_BF16 ? moe::tail_workspace_bytes() : 0);
   L.total = off;
   return L;
 }
@@ -224,8 +225,15 @@ moe::RouteParams route_params(const moe_config* c, const void* x, const void* w_
 moe::GemmParams gemm_params(const moe_config* c, int n_groups, int hidden, const void* x,
                             const int32_t* r2a, const int32_t* offsets, int max_rows,
                             const float* gw, const void* wg, const void* wu, const void* wd,
-                            void* hbuf, void* y) {
+                            void* hbuf, void* y, void* tail) {
   moe::GemmParams p{};
+  if (tail) {
+    char* t = static_cast<char*>(tail);
+    const size_t parts = (size_t)moe::kXcds * moe::kTailSlots * moe::kTailSlotBytes;
+    p.tail_part = reinterpret_cast<float*>(t);
+    p.tail_meta = reinterpret_cast<int32_t*>(t + parts);
+    p.tail_desc = reinterpret_cast<int32_t*>(t + parts + 256);
+  }
   p.T = c->T;
   p.D = c->D;
   p.k = c->top_k;
@@ -402,9 +410,14 @@ moe_status moe_grouped_swiglu(const moe_config* cfg, int32_t n_experts, int32_t 
   MOE_TRY(check_dev(y_rows, "y_rows", true));
   MOE_TRY(check_dev(workspace, "workspace", true));
   if (max_rows == 0) return ok();
+  // Room after the Hb rows holds the split-K tail of the large-tile kernel
+  // (a workspace of moe_workspace_bytes(cfg) always has it).
+  void* tail = nullptr;
+  if (cfg->act_dtype == MOE_BF16 && workspace_bytes >= align_up(hb_need) + moe::tail_workspace_bytes())
+    tail = static_cast<char*>(workspace) + align_up(hb_need);
   const moe::GemmParams gp =
       gemm_params(cfg, n_experts, hidden, x, row_to_assign, expert_offsets, max_rows, gate_w,
-                  w_gate, w_up, w_down, workspace, y_rows);
+                  w_gate, w_up, w_down, workspace, y_rows, tail);
   MOE_TRY(hip_ok(moe::launch_grouped_swiglu(gp, cfg->act_dtype == MOE_BF16, stream),
                  "grouped swiglu kernels"));
   return ok();
@@ -494,15 +507,16 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   void* hbuf = at<void>(workspace, L.hbuf);
   void* y = at<void>(workspace, L.y);
   const bool bf16 = cfg->act_dtype == MOE_BF16;
+  void* tail = bf16 ? at<void>(workspace, L.tail) : nullptr;
   const moe::GemmParams gp = gemm_params(cfg, cfg->E, cfg->H, x, r2a, offsets, rows, gw, w_gate,
-                                         w_up, w_down, hbuf, y);
+                                         w_up, w_down, hbuf, y, tail);
   MOE_TRY(hip_ok(moe::launch_grouped_swiglu(gp, bf16, stream), "grouped swiglu kernels"));
   void* sy = nullptr;
   if (cfg->H_shared > 0) {
     sy = at<void>(workspace, L.shared_y);
     const moe::GemmParams sp2 =
         gemm_params(cfg, 1, cfg->H_shared, x, nullptr, nullptr, cfg->T, nullptr, w_shared_gate,
-                    w_shared_up, w_shared_down, hbuf, sy);
+                    w_shared_up, w_shared_down, hbuf, sy, tail);
     MOE_TRY(hip_ok(moe::launch_grouped_swiglu(sp2, bf16, stream), "shared expert kernels"));
   }
   moe::CombineParams cp{cfg->T, cfg->D, cfg->top_k, y, a2r, sy, out};
