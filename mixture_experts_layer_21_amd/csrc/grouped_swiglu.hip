@@ -324,36 +324,34 @@ struct DmaLoads {
   int wave;
 };
 
-// Issue loads [i0, i1) of the LPS global -> LDS loads (A loads first, then B)
-// of k-step kt into one stage's buffers.
-template <class C, bool GATEUP>
-__device__ __forceinline__ void dma_issue(const DmaLoads<C, GATEUP>& ld, uint16_t* sa,
-                                          uint16_t* sb, int kt, int i0, int i1) {
-  const int soff = kt * C::BK * 2;
-#pragma unroll
-  for (int i = 0; i < C::A_LD; ++i)
-    if (i >= i0 && i < i1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ld.rA, (lds_void_t*)(sa + (ld.wave + C::NW * i) * 512), 16, ld.a_off[i], soff, 0, 0);
-#pragma unroll
-  for (int i = 0; i < C::B_LD; ++i) {
-    if (C::A_LD + i < i0 || C::A_LD + i >= i1) continue;
-    const int blk = ld.wave + C::NW * i;
-    const bool up = GATEUP && blk * 64 >= C::BN * C::KCH;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? ld.rU : ld.rG, (lds_void_t*)(sb + blk * 512),
-                                             16, ld.b_off[i], soff, 0, 0);
-  }
-}
+// Issue all LPS global -> LDS loads (A loads first, then B) of k-step kt into
+// one stage's buffers.  (A macro: the host pass of hipcc rejects this body as
+// a device function template called from the k-loop.)
+#define MOE_DMA_ISSUE(C, GATEUP, ld, sa, sb, kt)                                             \
+  do {                                                                                      \
+    const int soff_ = (kt) * C::BK * 2;                                                     \
+    _Pragma("unroll") for (int i_ = 0; i_ < C::A_LD; ++i_)                                  \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                           \
+            (ld).rA, (lds_void_t*)((sa) + ((ld).wave + C::NW * i_) * 512), 16,              \
+            (ld).a_off[i_], soff_, 0, 0);                                                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < C::B_LD; ++i_) {                                \
+      const int blk_ = (ld).wave + C::NW * i_;                                              \
+      const bool up_ = (GATEUP) && blk_ * 64 >= C::BN * C::KCH;                             \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(up_ ? (ld).rU : (ld).rG,                     \
+                                               (lds_void_t*)((sb) + blk_ * 512), 16,        \
+                                               (ld).b_off[i_], soff_, 0, 0);                \
+    }                                                                                       \
+  } while (0)
 
 // Multiply one stage (BK/16 k-steps of MI x NB*NI 32x32x16 MFMAs per wave)
 // after issuing the loads of a later k-step into another stage's buffers
 // (spreading them over the k-steps measured slower on gfx950).
-template <class C, bool GATEUP>
+template <class C, bool GATEUP, bool PARTIAL>
 __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* sb, int wm,
                                             int wn, int lr, int lk,
                                             f32x16 (&acc)[C::NB][C::MI][C::NI],
                                             const DmaLoads<C, GATEUP>& ld, uint16_t* na,
-                                            uint16_t* nb_, int kt_next) {
+                                            uint16_t* nb_, int kt_next, int mi_n) {
   constexpr int BK = C::BK, KCH = C::KCH, KS = BK / 16;
   constexpr int NRD = C::MI + C::NB * C::NI;          // fragment reads per k16 step
   constexpr int NMF = C::MI * C::NB * C::NI;          // MFMAs per k16 step
@@ -367,9 +365,11 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
     const int ch = kk * 2 + lk;
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
+      if (PARTIAL && mi >= mi_n) continue;
       const int r = wm * C::WM + mi * 32 + lr;
       af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + r * BK + (ch ^ swz_k<KCH>(r)) * 8);
     }
+    if (PARTIAL && mi_n == 0) return;
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -409,9 +409,12 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
 #pragma unroll
       for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi)
+        for (int mi = 0; mi < C::MI; ++mi) {
+          if (PARTIAL && mi >= mi_n) continue;
           acc[nb][mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               af[kk & 1][mi], bfr[kk & 1][nb][ni], acc[nb][mi][ni], 0, 0, 0);
+        }
+    if (PARTIAL) continue;  // no fixed instruction pattern to schedule
     // Scheduling hint: MFMAs interleaved with the fragment reads and loads.
     const int nrd = kk + 1 < KS ? NRD : 0;
     const int nld = i1 - kk * NLD;
@@ -431,18 +434,18 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
 // scoped no-alias information, so the compiler's own wait before a fragment
 // read covers only the load into that same buffer (issued S-1 stages earlier)
 // instead of every load in flight.
-template <class C, bool GATEUP>
+template <class C, bool GATEUP, bool PARTIAL>
 __device__ __forceinline__ void dma_mainloop(
-    const DmaLoads<C, GATEUP>& ld, int nk, int wm, int wn, int lr, int lk,
+    const DmaLoads<C, GATEUP>& ld, int nk, int mi_n, int wm, int wn, int lr, int lk,
     f32x16 (&acc)[C::NB][C::MI][C::NI], uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
     uint16_t* __restrict__ a2, uint16_t* __restrict__ a3, uint16_t* __restrict__ b0,
     uint16_t* __restrict__ b1, uint16_t* __restrict__ b2, uint16_t* __restrict__ b3) {
   constexpr int S = C::S;
   // Prologue: stages 0 .. S-2 in flight.
   constexpr int LPS = C::LPS;
-  dma_issue<C, GATEUP>(ld, a0, b0, 0, 0, LPS);
-  if (S > 2) dma_issue<C, GATEUP>(ld, a1, b1, min(1, nk - 1), 0, LPS);
-  if (S > 3) dma_issue<C, GATEUP>(ld, a2, b2, min(2, nk - 1), 0, LPS);
+  MOE_DMA_ISSUE(C, GATEUP, ld, a0, b0, 0);
+  if (S > 2) MOE_DMA_ISSUE(C, GATEUP, ld, a1, b1, min(1, nk - 1));
+  if (S > 3) MOE_DMA_ISSUE(C, GATEUP, ld, a2, b2, min(2, nk - 1));
 
   // Every step issues one stage of loads, so exactly S-2 stages are in flight
   // behind the one being waited for.  Past the end the loads repeat the last
@@ -457,12 +460,12 @@ __device__ __forceinline__ void dma_mainloop(
     wait_vmcnt<(S - 2) * C::LPS>();                                                         \
     stage_barrier();                                                                        \
     if (kt < nk)                                                                            \
-      dma_compute<C, GATEUP>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc, ld,               \
-                             MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),            \
-                             min(kt + S - 1, nk - 1));                                      \
+      dma_compute<C, GATEUP, PARTIAL>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc, ld,      \
+                                      MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),   \
+                                      min(kt + S - 1, nk - 1), mi_n);                       \
     else                                                                                    \
-      dma_issue<C, GATEUP>(ld, MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S), nk - 1,  \
-                           0, C::LPS);                                                      \
+      MOE_DMA_ISSUE(C, GATEUP, ld, MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),     \
+                    nk - 1);                                                                \
   }
   for (int kb = 0; kb < nk; kb += S) {
     MOE_STEP(0)
@@ -483,10 +486,12 @@ __device__ __forceinline__ void dma_mainloop(
 template <class C, bool GATEUP>
 __device__ __forceinline__ void dma_epilogue(const GemmParams& p, int m0, int m_end, int n0,
                                              int wm, int wn, int lr, int lk,
-                                             const f32x16 (&acc)[C::NB][C::MI][C::NI]) {
+                                             const f32x16 (&acc)[C::NB][C::MI][C::NI],
+                                             int mi_sel = -1) {
   const int N = GATEUP ? p.hidden : p.D;
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {
+    if (mi_sel >= 0 && mi != mi_sel) continue;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int grow = m0 + wm * C::WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
@@ -536,17 +541,24 @@ __device__ __forceinline__ void dma_store_partial(float* slot, int tid,
         }
 }
 
-// One block per (XCD, tail tile): adds the tile's partials in piece order and
-// runs the tile's epilogue.  Runs after the GEMM kernel on the same stream.
+// One block per (XCD, tail tile, wave row, 32-row block): the block stands in
+// for the WGN waves of one wave row of the GEMM block, adds their partials of
+// that row block in piece order and runs the epilogue on those rows.  Runs
+// after the GEMM kernel on the same stream.
 template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
-__global__ __launch_bounds__(64 * NWV) void gemm_tail_reduce_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * (NWV / WGM)) void gemm_tail_reduce_kernel(GemmParams p) {
   using C = DmaCfg<BM, BNB, BK, S, WGM, NWV, GATEUP>;
-  const int xcd = blockIdx.x / kTailSlots, j = blockIdx.x % kTailSlots;
+  constexpr int PER_TILE = WGM * C::MI;
+  const int tile_id = blockIdx.x / PER_TILE, sub = blockIdx.x % PER_TILE;
+  const int wm = sub / C::MI, mi = sub % C::MI;
+  const int xcd = tile_id / kTailSlots, j = tile_id % kTailSlots;
   const int r = p.tail_meta[2 * xcd], ns = p.tail_meta[2 * xcd + 1];
   if (j >= r) return;
   const int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + j) * 4;
   const int m0 = d[1], m_end = d[2], nt = d[3];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (m0 + wm * C::WM + mi * 32 >= m_end) return;  // no valid row in this block
+  const int t = threadIdx.x, lane = t & 63, wn = t >> 6;
+  const int tid = wm * C::WGN * 64 + t;             // thread of the GEMM block
   f32x16 acc[C::NB][C::MI][C::NI];
   for (int pc = 0; pc < ns; ++pc) {
     const f32x4* src = reinterpret_cast<const f32x4*>(
@@ -554,20 +566,22 @@ __global__ __launch_bounds__(64 * NWV) void gemm_tail_reduce_kernel(GemmParams p
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi)
+      for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni)
+        for (int q = 0; q < 4; ++q) {
+          const int v = ((nb * C::MI + mi) * C::NI + ni) * 4 + q;
+          const f32x4 x = src[v * C::NT + tid];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int v = ((nb * C::MI + mi) * C::NI + ni) * 4 + q;
-            const f32x4 x = src[v * C::NT + tid];
+          for (int u = 0; u < 4; ++u) {
+            // mi is uniform but not constant: select the accumulator by value
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-              acc[nb][mi][ni][4 * q + u] = pc == 0 ? x[u] : acc[nb][mi][ni][4 * q + u] + x[u];
+            for (int m = 0; m < C::MI; ++m)
+              if (m == mi)
+                acc[nb][m][ni][4 * q + u] = pc == 0 ? x[u] : acc[nb][m][ni][4 * q + u] + x[u];
           }
+        }
   }
-  dma_epilogue<C, GATEUP>(p, m0, m_end, nt * C::BN, wave / C::WGN, wave % C::WGN, lane & 31,
-                          lane >> 5, acc);
+  dma_epilogue<C, GATEUP>(p, m0, m_end, nt * C::BN, wm, wn, lane & 31, lane >> 5, acc, mi);
 }
 
 template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
@@ -766,8 +780,17 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[nb][mi][ni][i] = 0.f;
 
-  dma_mainloop<C, GATEUP>(ld, ke - kb, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3, sB0, sB1, sB2,
-                          sB3);
+  // Row blocks of this wave that hold valid rows (the last row tile of an
+  // expert is usually partial); the others skip their reads and MFMAs.  Only
+  // tiles with four row blocks per wave take the second path: with fewer the
+  // saving is small and the extra code makes the kernel spill.
+  const int mi_n = min(C::MI, max(0, (tile.m_end - tile.m0 - wm * C::WM + 31) / 32));
+  if (C::MI < 4 || mi_n == C::MI)
+    dma_mainloop<C, GATEUP, false>(ld, ke - kb, C::MI, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3,
+                                   sB0, sB1, sB2, sB3);
+  else if constexpr (C::MI >= 4)
+    dma_mainloop<C, GATEUP, true>(ld, ke - kb, mi_n, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3,
+                                  sB0, sB1, sB2, sB3);
   if (piece >= 0) {
     dma_store_partial<C, GATEUP>(p.tail_part + (size_t)tail_slot * (kTailSlotBytes / 4), tid,
                                  acc);
@@ -920,7 +943,7 @@ hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || slots == 0) return err;
   hipLaunchKernelGGL((gemm_tail_reduce_kernel<BM, BNB, BK, S, WGM, NWV, GATEUP>),
-                     dim3(kXcds * kTailSlots), dim3(C::NT), 0, s, p);
+                     dim3(kXcds * kTailSlots * WGM * C::MI), dim3(64 * C::WGN), 0, s, p);
   return hipGetLastError();
 }
 
