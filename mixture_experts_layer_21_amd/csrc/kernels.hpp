@@ -104,10 +104,23 @@ hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
 
 inline int route_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
 
+// The LDS-tiled router GEMM (64 tokens x 256 experts per block) serves bf16
+// routers with many experts and tokens; the others use the per-wave kernel.
+inline bool route_tiled(int T, int E, bool bf16_mfma) { return bf16_mfma && E >= 128 && T >= 1024; }
+constexpr int kRouteTiledM = 64, kRouteTiledN = 256;
+
 // K-split of the router GEMM: enough blocks to fill the GPU while every split
-// keeps at least four k-steps (32 elements each for bf16, 16 for fp32).
+// keeps at least four k-steps (32 elements each for bf16, 16 for fp32); the
+// tiled kernel keeps at least eight.
 inline int route_ksplit(int T, int D, int E, bool bf16_mfma) {
   const int nsteps = D / (bf16_mfma ? 32 : 16);
+  if (route_tiled(T, E, bf16_mfma)) {
+    const long long blocks =
+        (long long)((T + kRouteTiledM - 1) / kRouteTiledM) * ((E + kRouteTiledN - 1) / kRouteTiledN);
+    int ks = 1;
+    while (blocks * ks < 512 && ks * 2 * 8 <= nsteps && ks < 16) ks *= 2;
+    return ks;
+  }
   const int NT = (E + 15) / 16;
   const int NTB = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
   const long long blocks = (long long)route_blocks(T) * ((NT + NTB - 1) / NTB);

@@ -135,6 +135,101 @@ __global__ __launch_bounds__(NTHREADS) void route_logits_kernel(RouteParams p) {
   }
 }
 
+// LDS-tiled router GEMM for bf16 x and W: a block computes 64 tokens x 256
+// experts over its K range (32-deep k-steps staged through LDS in two
+// buffers); four waves in a 2 x 2 grid each hold 32 tokens x 128 experts as
+// four 32x32x16 MFMA tiles.  x is read once per K range instead of once per
+// expert tile.  Rows are 64 bytes in LDS; the 16-byte chunk c of row r sits
+// at c ^ ((r >> 2) & 3), which keeps the fragment reads conflict-free.
+__device__ __forceinline__ int rswz(int r) { return (r >> 2) & 3; }
+
+__global__ __launch_bounds__(NTHREADS) void route_logits_tiled_kernel(RouteParams p) {
+  constexpr int BM = kRouteTiledM, BN = kRouteTiledN, BK = 32;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+  const uint16_t* x = static_cast<const uint16_t*>(p.x);
+  const uint16_t* w = static_cast<const uint16_t*>(p.w_router);
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int t0 = blockIdx.x * BM, e0 = blockIdx.y * BN;
+  const int nsteps = p.D / BK;
+  const int per = (nsteps + p.ksplit - 1) / p.ksplit;
+  const int s0 = blockIdx.z * per, s1 = min(nsteps, s0 + per);
+
+  // This thread's 16-byte chunks: one of A (row tid/4), four of B.
+  const int ar = tid >> 2, ac = tid & 3;
+  const uint16_t* asrc = x + (size_t)min(t0 + ar, p.T - 1) * p.D + ac * 8;
+  const int adst = ar * BK + (ac ^ rswz(ar)) * 8;
+  const uint16_t* bsrc[4];
+  int bdst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + NTHREADS * i, r = c >> 2, cc = c & 3;
+    bsrc[i] = w + (size_t)min(e0 + r, p.E - 1) * p.D + cc * 8;
+    bdst[i] = r * BK + (cc ^ rswz(r)) * 8;
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[ni][i] = 0.f;
+
+  if (s0 < s1) {
+    u32x4 ra, rb[4];
+#define MOE_RLOAD(s)                                                                        \
+  do {                                                                                      \
+    const int k0_ = (s) * BK;                                                               \
+    ra = *reinterpret_cast<const u32x4*>(asrc + k0_);                                       \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) rb[i] =                                   \
+        *reinterpret_cast<const u32x4*>(bsrc[i] + k0_);                                     \
+  } while (0)
+#define MOE_RSTORE(buf)                                                                     \
+  do {                                                                                      \
+    *reinterpret_cast<u32x4*>(&As[buf][adst]) = ra;                                         \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+        *reinterpret_cast<u32x4*>(&Bs[buf][bdst[i]]) = rb[i];                               \
+  } while (0)
+    MOE_RLOAD(s0);
+    MOE_RSTORE(0);
+    __syncthreads();
+    for (int s = s0; s < s1; ++s) {
+      const int cur = (s - s0) & 1;
+      if (s + 1 < s1) MOE_RLOAD(s + 1);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int ch = kk * 2 + lk;
+        const int r = wm * 32 + lr;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[cur][r * BK + (ch ^ rswz(r)) * 8]);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int rb_ = wn * 128 + ni * 32 + lr;
+          const bf16x8 bfr =
+              *reinterpret_cast<const bf16x8*>(&Bs[cur][rb_ * BK + (ch ^ rswz(rb_)) * 8]);
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[ni], 0, 0, 0);
+        }
+      }
+      if (s + 1 < s1) MOE_RSTORE(cur ^ 1);
+      __syncthreads();
+    }
+#undef MOE_RLOAD
+#undef MOE_RSTORE
+  }
+  // Partial logits (an empty K range writes zeros).  32x32 accumulator
+  // layout: element i of lane l is row 8*(i/4) + 4*(l/32) + (i%4), column l%32.
+  float* out = p.logits_part + (size_t)blockIdx.z * p.T * p.E;
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int e = e0 + wn * 128 + ni * 32 + lr;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + wm * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
+      if (t < p.T && e < p.E) out[(size_t)t * p.E + e] = acc[ni][i];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Selection.  Cross-lane steps use DPP inside 16-lane rows (quad permutes,
 // half-row and row mirrors) and v_readlane across the four rows, instead of
@@ -486,7 +581,11 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s) {
   const int NT = (p.E + 15) / 16;
   const int NTB = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
   const dim3 grid(route_blocks(p.T), (NT + NTB - 1) / NTB, p.ksplit), block(NTHREADS);
-  if (p.act_bf16 && p.router_bf16) {
+  if (route_tiled(p.T, p.E, p.act_bf16 && p.router_bf16)) {
+    const dim3 tgrid((p.T + kRouteTiledM - 1) / kRouteTiledM,
+                     (p.E + kRouteTiledN - 1) / kRouteTiledN, p.ksplit);
+    hipLaunchKernelGGL(route_logits_tiled_kernel, tgrid, block, 0, s, p);
+  } else if (p.act_bf16 && p.router_bf16) {
     hipLaunchKernelGGL((route_logits_kernel<uint16_t, uint16_t, true>), grid, block, 0, s, p);
   } else if (p.act_bf16) {
     hipLaunchKernelGGL((route_logits_kernel<uint16_t, float, false>), grid, block, 0, s, p);

@@ -119,6 +119,25 @@ def test_route_group_limits(moe, E, ng, tg, k, rule, score):
     _say(f"  near ties flagged {nflag}, differing {ndiff}")
 
 
+# Shapes that take the LDS-tiled router GEMM (bf16, E >= 128, T >= 1024):
+# ragged token and expert tiles, E below and at one 256-wide tile.
+TILED_ROUTER_CASES = [(1100, 160, 6, "softmax"), (2048, 256, 8, "sigmoid"), (1031, 128, 4, "softmax")]
+
+
+@pytest.mark.parametrize("T,E,k,score", TILED_ROUTER_CASES)
+def test_route_tiled_router_gemm(moe, T, E, k, score):
+    w = W.SMALL["decode_small"].with_(batch=1, seq=T, D=768, E=E, top_k=k, score=score,
+                                      H=128, route_scale=2.5 if score == "sigmoid" else 1.0)
+    _say(f"[route-tiled] T={T} E={E} k={k} {score}")
+    inp = W.make_inputs(w, "cpu", seed=5)
+    cfg = P.config_of(w)
+    g = _route(moe, w, cfg, _to_dev(inp))
+    torch.cuda.synchronize()
+    r = P.oracle_route(w, P.oracle_inputs(inp))
+    nflag, ndiff = P.compare_route(w, r, g)
+    _say(f"  near ties flagged {nflag}, differing {ndiff}")
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_route_deterministic(moe, name):
     w = W.SMALL[name]
