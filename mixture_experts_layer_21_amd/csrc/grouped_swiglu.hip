@@ -969,7 +969,11 @@ hipError_t launch_f32(const GemmParams& p, hipStream_t s) {
 #ifndef MOE_DN_CFG
 #define MOE_DN_CFG 256, 256, 64, 2, 2, 8
 #endif
-// Groups of 64..511 rows on average: 128-row tiles.
+// Average rows per group from which the 256-row tiles are used.
+#ifndef MOE_LARGE_MIN_ROWS
+#define MOE_LARGE_MIN_ROWS 192
+#endif
+// Smaller groups of 64 or more rows on average: 128-row tiles.
 #ifndef MOE_GU_CFG_M
 #define MOE_GU_CFG_M 128, 512, 32, 2, 2, 8
 #endif
@@ -1007,7 +1011,7 @@ hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s) 
   using DN = DmaCfg<MOE_DN_CFG, false>;
   using GUM = DmaCfg<MOE_GU_CFG_M, true>;
   using DNM = DmaCfg<MOE_DN_CFG_M, false>;
-  if ((long long)rows >= 512LL * groups && dma_fits<GU, DN>(p)) {
+  if ((long long)rows >= (long long)MOE_LARGE_MIN_ROWS * groups && dma_fits<GU, DN>(p)) {
     if ((err = launch_dma<MOE_GU_CFG, true>(p, s)) != hipSuccess) return err;
     return launch_dma<MOE_DN_CFG, false>(p, s);
   }
