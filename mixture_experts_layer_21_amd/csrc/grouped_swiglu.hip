@@ -355,11 +355,7 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
   constexpr int BK = C::BK, KCH = C::KCH, KS = BK / 16;
   constexpr int NRD = C::MI + C::NB * C::NI;          // fragment reads per k16 step
   constexpr int NMF = C::MI * C::NB * C::NI;          // MFMAs per k16 step
-#ifndef MOE_SPREAD_LOADS
   constexpr int NLD = C::LPS;                         // all loads before the first k16 step
-#else
-  constexpr int NLD = (C::LPS + KS - 1) / KS;         // loads spread over the k16 steps
-#endif
   bf16x8 af[2][C::MI], bfr[2][C::NB][C::NI];
   auto frags = [&](int kk, int buf) {
     const int ch = kk * 2 + lk;
@@ -415,17 +411,12 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
               af[kk & 1][mi], bfr[kk & 1][nb][ni], acc[nb][mi][ni], 0, 0, 0);
         }
     if (PARTIAL) continue;  // no fixed instruction pattern to schedule
-    // Scheduling hint: MFMAs interleaved with the fragment reads and loads.
-    const int nrd = kk + 1 < KS ? NRD : 0;
-    const int nld = i1 - kk * NLD;
-#pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#ifdef MOE_SPREAD_LOADS
-      if (i < nld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-#endif
-    }
+    // Scheduling hint: two MFMAs, then all fragment reads of the next k16
+    // step, then the remaining MFMAs (measured 2-3% ahead of a 1:1
+    // interleave and 10% ahead of no hint on the 256x256 tile).
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (kk + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF - 2, 0);
   }
 }
 
