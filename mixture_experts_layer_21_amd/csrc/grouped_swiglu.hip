@@ -346,17 +346,46 @@ struct DmaLoads {
 // Multiply one stage (BK/16 k-steps of MI x NB*NI 32x32x16 MFMAs per wave)
 // after issuing the loads of a later k-step into another stage's buffers
 // (spreading them over the k-steps measured slower on gfx950).
+template <class C, bool PARTIAL>
+__device__ __forceinline__ void dma_mfmas(const bf16x8 (&af)[C::MI], const bf16x8 (&bfr)[C::NB][C::NI],
+                                          f32x16 (&acc)[C::NB][C::MI][C::NI], int mi_n) {
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi) {
+        if (PARTIAL && mi >= mi_n) continue;
+        acc[nb][mi][ni] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[nb][ni], acc[nb][mi][ni], 0, 0, 0);
+      }
+}
+
+// s_waitcnt lgkmcnt(0) with the other counters left open.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// With MOE_DEFER the MFMAs of a stage's last k16 step run after the next
+// stage's barrier (their fragments are already in registers), so they cover
+// the latency of the next stage's first fragment reads.
+#ifndef MOE_DEFER
+#define MOE_DEFER 1
+#endif
+
 template <class C, bool GATEUP, bool PARTIAL>
 __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* sb, int wm,
                                             int wn, int lr, int lk,
                                             f32x16 (&acc)[C::NB][C::MI][C::NI],
                                             const DmaLoads<C, GATEUP>& ld, uint16_t* na,
-                                            uint16_t* nb_, int kt_next, int mi_n) {
+                                            uint16_t* nb_, int kt_next, int mi_n,
+                                            bf16x8 (&af)[2][C::MI],
+                                            bf16x8 (&bfr)[2][C::NB][C::NI]) {
   constexpr int BK = C::BK, KCH = C::KCH, KS = BK / 16;
+  static_assert(KS % 2 == 0, "the deferred k16 step uses fragment buffer 1");
   constexpr int NRD = C::MI + C::NB * C::NI;          // fragment reads per k16 step
   constexpr int NMF = C::MI * C::NB * C::NI;          // MFMAs per k16 step
   constexpr int NLD = C::LPS;                         // all loads before the first k16 step
-  bf16x8 af[2][C::MI], bfr[2][C::NB][C::NI];
   auto frags = [&](int kk, int buf) {
     const int ch = kk * 2 + lk;
 #pragma unroll
@@ -376,6 +405,7 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
       }
   };
   frags(0, 0);
+  if (MOE_DEFER) dma_mfmas<C, PARTIAL>(af[1], bfr[1], acc, mi_n);
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
     constexpr int LPS = C::LPS;
@@ -400,16 +430,11 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
     }
     // Fragments of the next k16 step are read while this step's MFMAs run.
     if (kk + 1 < KS) frags(kk + 1, (kk + 1) & 1);
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi) {
-          if (PARTIAL && mi >= mi_n) continue;
-          acc[nb][mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              af[kk & 1][mi], bfr[kk & 1][nb][ni], acc[nb][mi][ni], 0, 0, 0);
-        }
+    if (MOE_DEFER && kk + 1 == KS) {
+      wait_lgkmcnt0();  // the deferred fragments are in registers before the barrier
+      continue;
+    }
+    dma_mfmas<C, PARTIAL>(af[kk & 1], bfr[kk & 1], acc, mi_n);
     if (PARTIAL) continue;  // no fixed instruction pattern to schedule
     // Scheduling hint: two MFMAs, then all fragment reads of the next k16
     // step, then the remaining MFMAs (measured 2-3% ahead of a 1:1
@@ -432,8 +457,16 @@ __device__ __forceinline__ void dma_mainloop(
     uint16_t* __restrict__ a2, uint16_t* __restrict__ a3, uint16_t* __restrict__ b0,
     uint16_t* __restrict__ b1, uint16_t* __restrict__ b2, uint16_t* __restrict__ b3) {
   constexpr int S = C::S;
+  // Fragment buffers; buffer 1 starts at zero so that the first stage's
+  // deferred MFMAs add nothing.
+  bf16x8 af[2][C::MI], bfr[2][C::NB][C::NI];
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) af[1][mi] = bf16x8{};
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni) bfr[1][nb][ni] = bf16x8{};
   // Prologue: stages 0 .. S-2 in flight.
-  constexpr int LPS = C::LPS;
   MOE_DMA_ISSUE(C, GATEUP, ld, a0, b0, 0);
   if (S > 2) MOE_DMA_ISSUE(C, GATEUP, ld, a1, b1, min(1, nk - 1));
   if (S > 3) MOE_DMA_ISSUE(C, GATEUP, ld, a2, b2, min(2, nk - 1));
@@ -453,7 +486,7 @@ __device__ __forceinline__ void dma_mainloop(
     if (kt < nk)                                                                            \
       dma_compute<C, GATEUP, PARTIAL>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc, ld,      \
                                       MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),   \
-                                      min(kt + S - 1, nk - 1), mi_n);                       \
+                                      min(kt + S - 1, nk - 1), mi_n, af, bfr);              \
     else                                                                                    \
       MOE_DMA_ISSUE(C, GATEUP, ld, MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),     \
                     nk - 1);                                                                \
@@ -467,6 +500,7 @@ __device__ __forceinline__ void dma_mainloop(
 #undef MOE_STEP
 #undef MOE_SA
 #undef MOE_SB
+  if (MOE_DEFER && nk > 0) dma_mfmas<C, PARTIAL>(af[1], bfr[1], acc, mi_n);
   // No LDS write may still be in flight when the block ends.
   wait_vmcnt<0>();
 }
