@@ -39,6 +39,20 @@ Readings taken where the pages are silent or garbled (all listed in the design doc):
     but define no group score;
   * for sigmoid scoring the balance loss uses P_e = mean_t s_te / sum_e' s_te'.
     PARITY UNPINNED: the pages give no formula for this case.
+  * ``score='sqrtsoftplus'`` ([NEMO] ``score_func``): s = sqrt(softplus(h)),
+    normalised like sigmoid.  The pages only name it; the score is read from
+    the name (pinned by its closed form and by selecting exactly what the
+    logits select);
+  * a token mask ([NEMO] ``Gate.forward(x, token_mask)``, ``MoE.forward``'s
+    ``padding_mask``): masked tokens are not routed (IDs -1, weights 0), take
+    no capacity, contribute no routed output, and are left out of counts and
+    of the means in P_e and z; the shared expert still applies to them;
+  * ``swiglu_limit`` ([NEMO] ``MLP``, ``_clamped_swiglu_act``): the gate and
+    up projections are each clamped to [-limit, limit] before silu(g) * u;
+    0 means no clamp.  PARITY UNPINNED: the pages name the clamp, not its form;
+  * a shared-expert gate ([NEMO] ``MoE.shared_expert_gate``): the shared
+    output is scaled per token by sigmoid(x . w_sg).  PARITY UNPINNED: the
+    pages name the gate, not its form.
 """
 from __future__ import annotations
 
@@ -47,9 +61,9 @@ import math
 import numpy as np
 
 __all__ = [
-    "NEAR_TIE", "router_logits", "softmax", "sigmoid", "logsumexp",
+    "NEAR_TIE", "router_logits", "softmax", "sigmoid", "softplus", "logsumexp",
     "route", "capacity", "first_within_capacity", "permutation",
-    "swiglu_ffn", "expert_outputs", "combine", "forward",
+    "swiglu_ffn", "expert_outputs", "shared_expert", "combine", "forward",
     "brute_force_forward", "all_experts_then_mask",
 ]
 
@@ -85,6 +99,12 @@ def softmax(h):
 def sigmoid(h):
     """Logistic score 1/(1+exp(-h)) ([NEMO] ``score_func`` 'sigmoid')."""
     return 1.0 / (1.0 + np.exp(-h))
+
+
+def softplus(h):
+    """log(1 + e^h), evaluated without overflow."""
+    h = np.asarray(h, dtype=np.float64)
+    return np.maximum(h, 0.0) + np.log1p(np.exp(-np.abs(h)))
 
 
 def logsumexp(h):
@@ -137,7 +157,7 @@ def _min_adjacent_gap(sorted_desc, n):
 
 def route(x, w_router, top_k, *, score="softmax", renormalize=True, route_scale=1.0,
           logit_bias=None, select_bias=None, n_groups=1, topk_groups=1,
-          group_rule="top2sum"):
+          group_rule="top2sum", token_mask=None):
     """Routing step of the layer, in the pages' order.
 
     1. logits h = x W_r^T (+ logit bias)                  [LAB] "Full implementation"
@@ -149,9 +169,11 @@ def route(x, w_router, top_k, *, score="softmax", renormalize=True, route_scale=
        or the raw top score (Switch top-1)               [LAB] "Ablation 2"
        times ``route_scale``                              [NEMO] ``route_scale``
     7. counts, f, P, balance = E sum f P, z = mean lse^2  [LAB]; [BOOK] aux loss
+       over the unmasked tokens                           [NEMO] ``token_mask``
 
-    Returns a dict with ``ids`` [T,k] int64, ``weights`` [T,k], ``counts`` [E],
-    ``mean_prob`` [E], ``balance``, ``z``, ``margin`` [T] and ``near_tie`` [T]."""
+    Returns a dict with ``ids`` [T,k] int64 (-1 for masked tokens),
+    ``weights`` [T,k], ``counts`` [E], ``mean_prob`` [E], ``balance``, ``z``,
+    ``margin`` [T] and ``near_tie`` [T]."""
     h = router_logits(x, w_router, logit_bias)
     T, E = h.shape
     if not 1 <= top_k <= E:
@@ -161,6 +183,9 @@ def route(x, w_router, top_k, *, score="softmax", renormalize=True, route_scale=
         prob_for_P = sc
     elif score == "sigmoid":
         sc = sigmoid(h)
+        prob_for_P = sc / sc.sum(axis=-1, keepdims=True)
+    elif score == "sqrtsoftplus":
+        sc = np.sqrt(softplus(h))
         prob_for_P = sc / sc.sum(axis=-1, keepdims=True)
     else:
         raise ValueError(f"unknown score {score!r}")
@@ -186,11 +211,19 @@ def route(x, w_router, top_k, *, score="softmax", renormalize=True, route_scale=
     weights = weights * route_scale
     sel_sorted = np.take_along_axis(sel, order[:, :min(top_k + 1, E)], axis=1)
     margin = np.minimum(_min_adjacent_gap(sel_sorted, min(top_k + 1, E)), group_margin)
-    counts = np.bincount(ids.reshape(-1), minlength=E)
-    f = counts / float(ids.size)
-    P = prob_for_P.mean(axis=0)
+    valid = np.ones(T, dtype=bool) if token_mask is None else np.asarray(token_mask, dtype=bool)
+    ids = np.where(valid[:, None], ids, -1)
+    weights = np.where(valid[:, None], weights, 0.0)
+    margin = np.where(valid, margin, np.inf)
+    n_valid = int(valid.sum())
+    counts = np.bincount(ids[valid].reshape(-1), minlength=E)
+    if n_valid:
+        f = counts / float(n_valid * top_k)
+        P = prob_for_P[valid].mean(axis=0)
+        z = float(np.mean(logsumexp(h[valid]) ** 2))
+    else:
+        f, P, z = np.zeros(E), np.zeros(E), 0.0
     balance = E * float(np.sum(f * P))
-    z = float(np.mean(logsumexp(h) ** 2))
     return {
         "logits": h, "scores": sc, "ids": ids.astype(np.int64), "weights": weights,
         "counts": counts.astype(np.int64), "mean_prob": P, "balance": balance,
@@ -219,12 +252,14 @@ def first_within_capacity(ids, E, cap):
     T, k = ids.shape
     keep = np.zeros((T, k), dtype=bool)
     if cap is None:
-        keep[:] = True
+        keep[:] = ids >= 0
         return keep
     used = [0] * E
     for t in range(T):
         for s in range(k):
             e = int(ids[t, s])
+            if e < 0:  # masked token: not routed
+                continue
             if used[e] < cap:
                 keep[t, s] = True
                 used[e] += 1
@@ -257,19 +292,23 @@ def permutation(ids, keep, E):
 
 # --------------------------------------------------------------- experts ---
 
-def swiglu_ffn(z, w_gate, w_up, w_down):
+def swiglu_ffn(z, w_gate, w_up, w_down, limit=0.0):
     """FFN(z) = W_down (silu(W_gate z) * (W_up z)), silu(u) = u sigmoid(u).
 
     [LAB] ``SwiGLUExpert`` (three bias-free Linears); weights in Linear layout:
-    w_gate, w_up [H, D]; w_down [D, H].  ``z`` is [n, D]."""
+    w_gate, w_up [H, D]; w_down [D, H].  ``z`` is [n, D].  ``limit`` > 0
+    clamps both projections to [-limit, limit] first ([NEMO] ``swiglu_limit``)."""
     z = np.asarray(z, dtype=np.float64)
     g = z @ np.asarray(w_gate, dtype=np.float64).T
     u = z @ np.asarray(w_up, dtype=np.float64).T
+    if limit > 0:
+        g = np.clip(g, -limit, limit)
+        u = np.clip(u, -limit, limit)
     act = g * sigmoid(g) * u
     return act @ np.asarray(w_down, dtype=np.float64).T
 
 
-def expert_outputs(x, ids, weights, keep, w_gate, w_up, w_down, tokens=None):
+def expert_outputs(x, ids, weights, keep, w_gate, w_up, w_down, tokens=None, limit=0.0):
     """Weighted expert output per (token, slot): Y[t, s] = w_ts FFN_{e_ts}(x_t)
     for kept slots, 0 for dropped ones ([LAB] "Full implementation", the
     per-expert gather / run / scale step).  Only tokens in ``tokens`` (default:
@@ -283,10 +322,10 @@ def expert_outputs(x, ids, weights, keep, w_gate, w_up, w_down, tokens=None):
     sub_keep = np.asarray(keep)[tokens]
     for e in np.unique(sub_ids):
         r, s = np.nonzero((sub_ids == e) & sub_keep)
-        if r.size == 0:
+        if e < 0 or r.size == 0:
             continue
         out = swiglu_ffn(np.asarray(x, dtype=np.float64)[tokens[r]], w_gate[e], w_up[e],
-                         w_down[e])
+                         w_down[e], limit)
         Y[r, s] = np.asarray(weights)[tokens[r], s][:, None] * out
     return Y
 
@@ -303,14 +342,28 @@ def combine(Y, shared=None):
     return out
 
 
+def shared_expert(x, inputs, limit=0.0):
+    """Always-on shared expert ([LAB] "Add a shared expert"; [BOOK]
+    DeepSeek-MoE), scaled per token by sigmoid(x . w_sg) when ``ws_sgate``
+    [D] is given ([NEMO] ``shared_expert_gate``); None without one."""
+    if inputs.get("ws_gate") is None:
+        return None
+    x = np.asarray(x, dtype=np.float64)
+    s = swiglu_ffn(x, inputs["ws_gate"], inputs["ws_up"], inputs["ws_down"], limit)
+    if inputs.get("ws_sgate") is not None:
+        s = sigmoid(x @ np.asarray(inputs["ws_sgate"], dtype=np.float64))[:, None] * s
+    return s
+
+
 def forward(inputs, *, top_k, score="softmax", renormalize=True, route_scale=1.0,
             n_groups=1, topk_groups=1, group_rule="top2sum", capacity_factor=None,
-            tokens=None, routing=None):
+            tokens=None, routing=None, token_mask=None, swiglu_limit=0.0):
     """The whole layer forward on float64 arrays.
 
     ``inputs`` holds x [T,D], w_router [E,D], w_gate/w_up [E,H,D], w_down
-    [E,D,H], optional ws_gate/ws_up [Hs,D], ws_down [D,Hs], logit_bias [E],
-    select_bias [E].  ``tokens`` limits the expert/combine work to a subset of
+    [E,D,H], optional ws_gate/ws_up [Hs,D], ws_down [D,Hs], ws_sgate [D],
+    logit_bias [E], select_bias [E].  ``token_mask`` [T] (True = valid) and
+    ``swiglu_limit`` are the [NEMO] switches read in the module docstring.  ``tokens`` limits the expert/combine work to a subset of
     tokens (routing and capacity are always computed for all tokens, because
     drops depend on every earlier token).  ``routing`` may supply precomputed
     ``ids``/``weights`` (e.g. those of the device, to compare the downstream
@@ -321,22 +374,19 @@ def forward(inputs, *, top_k, score="softmax", renormalize=True, route_scale=1.0
     r = route(x, inputs["w_router"], top_k, score=score, renormalize=renormalize,
               route_scale=route_scale, logit_bias=inputs.get("logit_bias"),
               select_bias=inputs.get("select_bias"), n_groups=n_groups,
-              topk_groups=topk_groups, group_rule=group_rule)
+              topk_groups=topk_groups, group_rule=group_rule, token_mask=token_mask)
     if routing is not None:
         r = dict(r)
         r["ids"] = np.asarray(routing["ids"], dtype=np.int64)
         r["weights"] = np.asarray(routing["weights"], dtype=np.float64)
-        r["counts"] = np.bincount(r["ids"].reshape(-1), minlength=E)
+        r["counts"] = np.bincount(r["ids"][r["ids"] >= 0].reshape(-1), minlength=E)
     cap = capacity(capacity_factor, T, top_k, E)
     keep = first_within_capacity(r["ids"], E, cap)
     offsets, row_to_assign, assign_to_row = permutation(r["ids"], keep, E)
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     Y = expert_outputs(x, r["ids"], r["weights"], keep, inputs["w_gate"],
-                       inputs["w_up"], inputs["w_down"], tokens=tok)
-    shared = None
-    if inputs.get("ws_gate") is not None:
-        shared = swiglu_ffn(np.asarray(x, dtype=np.float64)[tok], inputs["ws_gate"],
-                            inputs["ws_up"], inputs["ws_down"])
+                       inputs["w_up"], inputs["w_down"], tokens=tok, limit=swiglu_limit)
+    shared = shared_expert(np.asarray(x, dtype=np.float64)[tok], inputs, swiglu_limit)
     out = combine(Y, shared)
     return {
         "out": out, "tokens": tok, "route": r, "capacity": cap, "keep": keep,
@@ -347,9 +397,10 @@ def forward(inputs, *, top_k, score="softmax", renormalize=True, route_scale=1.0
 
 # ------------------------------------------- second implementations (tiny) ---
 
-def brute_force_forward(inputs, ids, weights, keep=None):
+def brute_force_forward(inputs, ids, weights, keep=None, limit=0.0):
     """Token-by-token, slot-by-slot loop in pure Python ([LAB] "Trace one token
-    by hand"): out_t = sum_s w_ts FFN_{e_ts}(x_t) (+ shared).  For tiny shapes."""
+    by hand"): out_t = sum_s w_ts FFN_{e_ts}(x_t) (+ shared, times its gate).
+    For tiny shapes; IDs < 0 (masked tokens) are skipped."""
     x = np.asarray(inputs["x"], dtype=np.float64)
     T, D = x.shape
     k = ids.shape[1]
@@ -359,11 +410,18 @@ def brute_force_forward(inputs, ids, weights, keep=None):
             if keep is not None and not keep[t, s]:
                 continue
             e = int(ids[t, s])
+            if e < 0:
+                continue
             out[t] += weights[t, s] * swiglu_ffn(x[t:t + 1], inputs["w_gate"][e],
-                                                 inputs["w_up"][e], inputs["w_down"][e])[0]
+                                                 inputs["w_up"][e], inputs["w_down"][e],
+                                                 limit)[0]
         if inputs.get("ws_gate") is not None:
-            out[t] += swiglu_ffn(x[t:t + 1], inputs["ws_gate"], inputs["ws_up"],
-                                 inputs["ws_down"])[0]
+            sh = swiglu_ffn(x[t:t + 1], inputs["ws_gate"], inputs["ws_up"],
+                            inputs["ws_down"], limit)[0]
+            if inputs.get("ws_sgate") is not None:
+                dot = sum(float(a) * float(b) for a, b in zip(x[t], inputs["ws_sgate"]))
+                sh = sh / (1.0 + math.exp(-dot))
+            out[t] += sh
     return out
 
 
@@ -376,5 +434,9 @@ def all_experts_then_mask(inputs, ids, weights):
     dense = np.stack([swiglu_ffn(x, inputs["w_gate"][e], inputs["w_up"][e],
                                  inputs["w_down"][e]) for e in range(E)], axis=1)
     gate = np.zeros((T, E))
-    np.put_along_axis(gate, np.asarray(ids), np.asarray(weights), axis=1)
+    ids = np.asarray(ids)
+    for t in range(T):
+        for s in range(ids.shape[1]):
+            if ids[t, s] >= 0:
+                gate[t, ids[t, s]] += weights[t, s]
     return np.einsum("te,ted->td", gate, dense)

@@ -428,4 +428,117 @@ def pin_subset_tokens(o):
     assert np.allclose(sub["out"], full["out"][[16, 3, 0]], rtol=0, atol=1e-15)
 
 
+# ------------------------------------------- forward variants (NeMo flags) --
+
+
+def pin_sqrtsoftplus_closed_form(o):
+    """score_func 'sqrtsoftplus': s = sqrt(ln(1 + e^h)) per expert, written out
+    with math on scalars; renormalised weights s_i / sum s times route_scale."""
+    h = [1.5, -0.25, 3.0, -4.0, 0.0]
+    r = _route_logits(o, [h], 2, score="sqrtsoftplus", route_scale=2.0)
+    s = [math.sqrt(math.log(1.0 + math.exp(v))) for v in h]
+    assert np.allclose(r["scores"][0], s, rtol=0, atol=1e-14)
+    assert r["ids"][0].tolist() == [2, 0]
+    assert np.allclose(r["weights"][0], [2.0 * s[2] / (s[2] + s[0]), 2.0 * s[0] / (s[2] + s[0])],
+                       rtol=0, atol=1e-14)
+    # large logits do not overflow: softplus(h) -> h
+    r2 = _route_logits(o, [[800.0, 0.0]], 1, score="sqrtsoftplus", renormalize=False)
+    assert abs(r2["weights"][0, 0] - math.sqrt(800.0)) < 1e-12
+
+
+def pin_sqrtsoftplus_selects_like_logits(o):
+    """sqrt(softplus(.)) is strictly increasing, so without a bias it selects
+    exactly the experts softmax selects, in the same slot order."""
+    inp = _tiny_inputs(31, T=40, E=7)
+    a = o.route(inp["x"], inp["w_router"], 3, score="sqrtsoftplus")
+    b = o.route(inp["x"], inp["w_router"], 3, score="softmax")
+    assert (a["ids"] == b["ids"]).all()
+
+
+def pin_softmax_then_topk_without_renorm(o):
+    """GShard/Switch convention for k > 1 (book 'The Router'): the kept weights
+    are the slice of the full softmax and do not sum to 1."""
+    h = [2.0, 1.0, 0.0, -1.0]
+    r = _route_logits(o, [h], 2, renormalize=False)
+    e = [math.exp(v) for v in h]
+    assert np.allclose(r["weights"][0], [e[0] / sum(e), e[1] / sum(e)], rtol=0, atol=1e-15)
+    assert r["weights"][0].sum() < 1.0
+
+
+def pin_token_mask_routing(o):
+    """Masked tokens are not routed: IDs -1, weights 0, no load, and the aux
+    means run over the unmasked tokens only (a masked copy of a routed batch
+    gives the balance and z of the unmasked part)."""
+    inp = _tiny_inputs(32, T=12, E=5)
+    x, w = inp["x"], inp["w_router"]
+    mask = np.array([1, 0, 1, 1, 0, 0, 1, 1, 1, 0, 1, 1], dtype=bool)
+    r = o.route(x, w, 2, token_mask=mask)
+    sub = o.route(x[mask], w, 2)
+    assert (r["ids"][~mask] == -1).all() and (r["weights"][~mask] == 0).all()
+    assert (r["ids"][mask] == sub["ids"]).all()
+    assert (r["counts"] == sub["counts"]).all() and r["counts"].sum() == 2 * mask.sum()
+    assert abs(r["balance"] - sub["balance"]) < 1e-14 and abs(r["z"] - sub["z"]) < 1e-14
+    assert np.allclose(r["mean_prob"], sub["mean_prob"], rtol=0, atol=1e-15)
+    none = o.route(x, w, 2, token_mask=np.zeros(12, dtype=bool))
+    assert none["counts"].sum() == 0 and none["balance"] == 0 and none["z"] == 0
+
+
+def pin_token_mask_forward(o):
+    """Masked tokens get no routed output (only the shared expert), take no
+    capacity, and the unmasked tokens match the layer run on them alone."""
+    inp = _tiny_inputs(33, T=14, E=3, shared=True)
+    mask = np.ones(14, dtype=bool)
+    mask[[0, 5, 6, 13]] = False
+    f = o.forward(inp, top_k=2, capacity_factor=0.7, token_mask=mask)
+    sub_inp = dict(inp, x=inp["x"][mask])
+    T_sub = int(mask.sum())
+    # same C as the masked run (C counts the configured T, not the unmasked)
+    cap = o.capacity(0.7, 14, 2, 3)
+    r_sub = o.route(sub_inp["x"], inp["w_router"], 2)
+    keep_sub = o.first_within_capacity(r_sub["ids"], 3, cap)
+    assert (f["keep"][mask] == keep_sub).all() and not f["keep"][~mask].any()
+    Y = o.expert_outputs(sub_inp["x"], r_sub["ids"], r_sub["weights"], keep_sub,
+                         inp["w_gate"], inp["w_up"], inp["w_down"])
+    shared = o.swiglu_ffn(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"])
+    assert np.allclose(f["out"][mask], Y.sum(1) + shared[mask], rtol=0, atol=1e-13)
+    assert np.allclose(f["out"][~mask], shared[~mask], rtol=0, atol=1e-14)
+    assert T_sub == 10
+
+
+def pin_swiglu_limit_closed_form(o):
+    """Clamped SwiGLU: both projections clamped to [-L, L] (scalars worked by
+    hand), a limit above every projection changes nothing, 0 means off."""
+    L = 0.5
+    z = np.array([[1.0]])
+    for g, u in ((2.0, 3.0), (-2.0, 0.25), (0.3, -4.0)):
+        out = o.swiglu_ffn(z, [[g]], [[u]], [[1.0]], limit=L)[0, 0]
+        gc, uc = max(-L, min(L, g)), max(-L, min(L, u))
+        assert abs(out - gc * _sig(gc) * uc) < 1e-15
+    inp = _tiny_inputs(34, T=6, E=3)
+    a = o.forward(inp, top_k=2)["out"]
+    b = o.forward(inp, top_k=2, swiglu_limit=1e9)["out"]
+    c = o.forward(inp, top_k=2, swiglu_limit=0.0)["out"]
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    d = o.forward(inp, top_k=2, swiglu_limit=0.05)["out"]
+    assert not np.allclose(a, d)
+
+
+def pin_shared_expert_gate(o):
+    """A zero gate vector halves the shared output (sigmoid(0) = 1/2); a gate
+    vector along x with a large norm passes it through; the token loop agrees."""
+    inp = _tiny_inputs(35, T=7, E=3, shared=True)
+    base = o.forward(inp, top_k=1)
+    plain = o.shared_expert(inp["x"], inp)
+    half = o.forward(dict(inp, ws_sgate=np.zeros(inp["x"].shape[1])), top_k=1)
+    assert np.allclose(half["out"], base["out"] - 0.5 * plain, rtol=0, atol=1e-13)
+    big = o.forward(dict(inp, ws_sgate=50.0 * np.ones(inp["x"].shape[1])), top_k=1)
+    s = inp["x"].sum(1)
+    g = 1.0 / (1.0 + np.exp(-50.0 * s))
+    assert np.allclose(big["out"], base["out"] - plain + g[:, None] * plain, rtol=0, atol=1e-12)
+    r = big["route"]
+    bf = o.brute_force_forward(dict(inp, ws_sgate=50.0 * np.ones(inp["x"].shape[1])),
+                               r["ids"], r["weights"])
+    assert np.allclose(big["out"], bf, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

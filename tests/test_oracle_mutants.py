@@ -39,8 +39,8 @@ MUTANTS = [
      "balance = E * float(np.sum(f * P))",
      "balance = float(np.sum(f * P))"),
     ("z_without_square",
-     "z = float(np.mean(logsumexp(h) ** 2))",
-     "z = float(np.mean(logsumexp(h)))"),
+     "z = float(np.mean(logsumexp(h[valid]) ** 2))",
+     "z = float(np.mean(logsumexp(h[valid])))"),
     ("lse_missing_max",
      "return m + np.log(np.exp(h - m[:, None]).sum(axis=-1))",
      "return np.log(np.exp(h - m[:, None]).sum(axis=-1))"),
@@ -51,8 +51,8 @@ MUTANTS = [
      "if used[e] < cap:",
      "if used[e] <= cap:"),
     ("slot_major_priority",
-     "    for t in range(T):\n        for s in range(k):\n            e = int(ids[t, s])\n            if used[e]",
-     "    for s in range(k):\n        for t in range(T):\n            e = int(ids[t, s])\n            if used[e]"),
+     "    for t in range(T):\n        for s in range(k):\n            e = int(ids[t, s])\n            if e < 0",
+     "    for s in range(k):\n        for t in range(T):\n            e = int(ids[t, s])\n            if e < 0"),
     ("permutation_token_major",
      "order = np.lexsort((tok, flat_e[a]))",
      "order = np.lexsort((flat_e[a], tok))"),
@@ -71,6 +71,30 @@ MUTANTS = [
     ("shared_expert_dropped",
      "    if shared is not None:\n        out = out + shared",
      "    if shared is not None:\n        out = out + 0.0 * shared"),
+    ("sqrtsoftplus_without_sqrt",
+     "sc = np.sqrt(softplus(h))",
+     "sc = softplus(h)"),
+    ("softplus_sign",
+     "return np.maximum(h, 0.0) + np.log1p(np.exp(-np.abs(h)))",
+     "return np.maximum(h, 0.0) + np.log1p(np.exp(np.abs(h)))"),
+    ("mask_still_counted",
+     "counts = np.bincount(ids[valid].reshape(-1), minlength=E)",
+     "counts = np.bincount(np.where(ids < 0, 0, ids).reshape(-1), minlength=E)"),
+    ("mask_mean_over_all_tokens",
+     "P = prob_for_P[valid].mean(axis=0)",
+     "P = prob_for_P[valid].sum(axis=0) / T"),
+    ("mask_takes_capacity",
+     "            if e < 0:  # masked token: not routed\n                continue\n",
+     "            if e < 0:  # masked token: not routed\n                used[0] += 1\n                continue\n"),
+    ("clamp_gate_only",
+     "        u = np.clip(u, -limit, limit)",
+     "        u = u"),
+    ("clamp_one_sided",
+     "        g = np.clip(g, -limit, limit)",
+     "        g = np.minimum(g, limit)"),
+    ("shared_gate_not_applied",
+     "        s = sigmoid(x @ np.asarray(inputs[\"ws_sgate\"], dtype=np.float64))[:, None] * s",
+     "        s = s"),
     ("router_bias_ignored",
      "h = h + np.asarray(logit_bias, dtype=np.float64)[None, :]",
      "h = h + 0.0"),
