@@ -55,7 +55,15 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
-typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+/* Router scores (NeMo Gate score_func): softmax over the experts, sigmoid,
+ * or sqrt(softplus(h)); the last two are normalised over the selected
+ * experts when renormalize is set.  A select_bias turns softmax and sigmoid
+ * into the "_with_bias" forms (bias used for selection only). */
+typedef enum {
+  MOE_SCORE_SOFTMAX = 0,
+  MOE_SCORE_SIGMOID = 1,
+  MOE_SCORE_SQRTSOFTPLUS = 2
+} moe_score;
 /* Group score for group-limited routing: sum of the two largest selection
  * scores of the group, or the largest one. */
 typedef enum { MOE_GROUP_TOP2SUM = 0, MOE_GROUP_MAX = 1 } moe_group_rule;
@@ -76,6 +84,8 @@ typedef struct moe_config {
   int32_t topk_groups;  /* groups each token may use, 1..n_groups              */
   int32_t group_rule;   /* moe_group_rule                                      */
   double capacity_factor; /* <= 0: dropless; else C = max(1, ceil(cf*T*k/E))   */
+  float swiglu_limit;   /* > 0: gate and up projections clamped to [-L, L]
+                           before silu(g)*u (NeMo MLP swiglu_limit); 0 = off   */
 } moe_config;
 
 /* Human-readable name of a status code (static storage). */
@@ -110,6 +120,10 @@ size_t moe_workspace_bytes(const moe_config* cfg);
  *   w_router     [E, D]   router_dtype
  *   logit_bias   [E] f32 or NULL: added to the logits (softmax input, z-loss)
  *   select_bias  [E] f32 or NULL: added to the scores for selection only
+ *   token_mask   [T] uint8 or NULL (all valid): 0 marks a padding token
+ *                (NeMo Gate.forward token_mask); such a token is not routed:
+ *                its IDs are -1 and weights 0, it adds nothing to counts, and
+ *                the means in P_e and z run over the unmasked tokens only
  *   expert_ids   [T, k] int32 out: slot j = j-th largest selection score
  *   gate_w       [T, k] f32 out
  *   counts       [E] int32 out: assignments per expert before any drop
@@ -118,14 +132,16 @@ size_t moe_workspace_bytes(const moe_config* cfg);
  * Deterministic: repeated calls give identical bits. */
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
                      const float* logit_bias, const float* select_bias,
-                     int32_t* expert_ids, float* gate_w, int32_t* counts,
-                     float* aux, float* mean_prob, void* workspace,
+                     const uint8_t* token_mask, int32_t* expert_ids, float* gate_w,
+                     int32_t* counts, float* aux, float* mean_prob, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
 /* Dispatch bookkeeping ("Add a capacity limit" on the lab page: keep the
  * first C assignments of each expert in token order; the sorted expert-major
  * token list of "MoE in Practice" on the book page).
- *   expert_ids     [T, k] int32 in, values in [0, E); a token's k IDs distinct
+ *   expert_ids     [T, k] int32 in, values in [0, E) and a token's k IDs
+ *                  distinct; other values (-1 for a masked token) mean
+ *                  "not routed": the slot is neither counted nor kept
  *   capacity       > 0: per-expert limit; <= 0: dropless
  *   expert_offsets [E+1] int32 out: kept rows of expert e are
  *                  [offsets[e], offsets[e+1])
@@ -171,26 +187,32 @@ moe_status moe_grouped_swiglu(const moe_config* cfg, int32_t n_experts, int32_t 
                               hipStream_t stream);
 
 /* Combine ("Full implementation" on the lab page, index_add_ back to token
- * order; "Add a shared expert"):
+ * order; "Add a shared expert"; NeMo MoE shared_expert_gate):
  *   out[t] = sum_{s=0..k-1, assign_to_row[t*k+s] >= 0} y_rows[assign_to_row[t*k+s]]
- *            (+ shared_rows[t])
+ *            (+ g_t * shared_rows[t]),
+ *   g_t = sigmoid(x[t] . shared_expert_gate) when shared_expert_gate [D]
+ *   (act_dtype) is given, else 1; x [T, D] is read only in that case.
  * accumulated in fp32 in slot order, one rounding to act_dtype.  No atomics:
  * the result is deterministic.  A token with every slot dropped gets 0
  * (plus its shared-expert row). */
 moe_status moe_combine(const moe_config* cfg, const void* y_rows,
                        const int32_t* assign_to_row, const void* shared_rows,
-                       void* out, hipStream_t stream);
+                       const void* x, const void* shared_expert_gate, void* out,
+                       hipStream_t stream);
 
 /* The whole forward: moe_route, moe_permute, moe_grouped_swiglu (routed and
  * shared expert) and moe_combine, stream-ordered, with no host
- * synchronisation.  w_shared_* may be NULL when cfg->H_shared == 0.  The
- * optional outputs expert_ids [T,k], gate_w [T,k], counts [E] and aux [2]
- * receive the routing results when non-NULL. */
+ * synchronisation.  w_shared_* may be NULL when cfg->H_shared == 0;
+ * shared_expert_gate [D] (optional, needs a shared expert) scales its output
+ * per token as in moe_combine; token_mask as in moe_route.  The optional
+ * outputs expert_ids [T,k], gate_w [T,k], counts [E] and aux [2] receive the
+ * routing results when non-NULL. */
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* logit_bias, const float* select_bias,
-                       const void* w_gate, const void* w_up, const void* w_down,
-                       const void* w_shared_gate, const void* w_shared_up,
-                       const void* w_shared_down, void* out, int32_t* expert_ids,
+                       const uint8_t* token_mask, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* w_shared_gate,
+                       const void* w_shared_up, const void* w_shared_down,
+                       const void* shared_expert_gate, void* out, int32_t* expert_ids,
                        float* gate_w, int32_t* counts, float* aux, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 

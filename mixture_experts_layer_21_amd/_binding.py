@@ -30,7 +30,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_NULL_PTR",
           3: "MOE_ERR_UNSUPPORTED", 4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_DEVICE",
           6: "MOE_ERR_HIP"}
 DTYPES = {"f32": 0, "bf16": 1}
-SCORES = {"softmax": 0, "sigmoid": 1}
+SCORES = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
 GROUP_RULES = {"top2sum": 0, "max": 1}
 _TORCH = {0: torch.float32, 1: torch.bfloat16}
 
@@ -51,7 +51,7 @@ class MoeConfig(ctypes.Structure):
         ("score_func", ctypes.c_int32), ("renormalize", ctypes.c_int32),
         ("route_scale", ctypes.c_float), ("n_groups", ctypes.c_int32),
         ("topk_groups", ctypes.c_int32), ("group_rule", ctypes.c_int32),
-        ("capacity_factor", ctypes.c_double),
+        ("capacity_factor", ctypes.c_double), ("swiglu_limit", ctypes.c_float),
     ]
 
     @property
@@ -65,13 +65,15 @@ class MoeConfig(ctypes.Structure):
 
 def make_config(T, D, H, E, top_k, *, H_shared=0, act_dtype="bf16", router_dtype="bf16",
                 score="softmax", renormalize=True, route_scale=1.0, n_groups=1,
-                topk_groups=1, group_rule="top2sum", capacity_factor=None) -> MoeConfig:
+                topk_groups=1, group_rule="top2sum", capacity_factor=None,
+                swiglu_limit=0.0) -> MoeConfig:
     return MoeConfig(T=T, D=D, H=H, E=E, top_k=top_k, H_shared=H_shared,
                      act_dtype=DTYPES[act_dtype], router_dtype=DTYPES[router_dtype],
                      score_func=SCORES[score], renormalize=int(bool(renormalize)),
                      route_scale=route_scale, n_groups=n_groups, topk_groups=topk_groups,
                      group_rule=GROUP_RULES[group_rule],
-                     capacity_factor=0.0 if capacity_factor is None else capacity_factor)
+                     capacity_factor=0.0 if capacity_factor is None else capacity_factor,
+                     swiglu_limit=float(swiglu_limit))
 
 
 _P = ctypes.c_void_p
@@ -85,13 +87,13 @@ _sigs = {
     "moe_capacity": (_I32, [_CFG]),
     "moe_max_rows": (_I32, [_CFG]),
     "moe_workspace_bytes": (_SZ, [_CFG]),
-    "moe_route": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute": (ctypes.c_int, [_CFG, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_swiglu": (ctypes.c_int, [_CFG, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P,
                                           _P, _P, _P, _SZ, _P]),
-    "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P]),
+    "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                   _P, _P, _P, _SZ, _P]),
+                                   _P, _P, _P, _P, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -114,6 +116,17 @@ def _stream():
 def _check(status: int, where: str):
     if status != MOE_OK:
         raise MoeError(status, where)
+
+
+def _mask(token_mask, T):
+    """A [T] token mask as contiguous uint8 (nonzero = valid), or None."""
+    if token_mask is None:
+        return None
+    if not token_mask.is_cuda or tuple(token_mask.shape) != (T,):
+        raise ValueError(f"token_mask must be a device tensor of shape ({T},)")
+    if token_mask.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("token_mask must be bool or uint8")
+    return token_mask.to(torch.uint8).contiguous()
 
 
 def _expect(t: Optional[torch.Tensor], name: str, shape, dtype, required=True):
@@ -160,10 +173,12 @@ def new_workspace(cfg: MoeConfig, device="cuda") -> torch.Tensor:
 
 # ---------------------------------------------------------- entry points ---
 
-def moe_route(cfg, x, w_router, logit_bias=None, select_bias=None, *, expert_ids=None,
-              gate_w=None, counts=None, aux=None, mean_prob=None, workspace=None):
-    """Routing (see ``moe_route`` in include/moe.h).  Returns a dict of the
-    output tensors (allocated here when not given)."""
+def moe_route(cfg, x, w_router, logit_bias=None, select_bias=None, *, token_mask=None,
+              expert_ids=None, gate_w=None, counts=None, aux=None, mean_prob=None,
+              workspace=None):
+    """Routing (see ``moe_route`` in include/moe.h).  ``token_mask`` [T]
+    (bool or uint8, nonzero = valid) leaves padding tokens unrouted.  Returns
+    a dict of the output tensors (allocated here when not given)."""
     check_config(cfg)
     T, D, E, k = cfg.T, cfg.D, cfg.E, cfg.top_k
     dev = x.device
@@ -171,6 +186,7 @@ def moe_route(cfg, x, w_router, logit_bias=None, select_bias=None, *, expert_ids
     _expect(w_router, "w_router", (E, D), cfg.router_torch_dtype)
     _expect(logit_bias, "logit_bias", (E,), torch.float32, required=False)
     _expect(select_bias, "select_bias", (E,), torch.float32, required=False)
+    token_mask = _mask(token_mask, T)
     expert_ids = torch.empty(T, k, dtype=torch.int32, device=dev) if expert_ids is None else expert_ids
     gate_w = torch.empty(T, k, dtype=torch.float32, device=dev) if gate_w is None else gate_w
     counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
@@ -183,7 +199,8 @@ def moe_route(cfg, x, w_router, logit_bias=None, select_bias=None, *, expert_ids
     _expect(mean_prob, "mean_prob", (E,), torch.float32)
     ws = new_workspace(cfg, dev) if workspace is None else workspace
     _check(_lib.moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logit_bias),
-                          _ptr(select_bias), _ptr(expert_ids), _ptr(gate_w), _ptr(counts),
+                          _ptr(select_bias), _ptr(token_mask), _ptr(expert_ids), _ptr(gate_w),
+                          _ptr(counts),
                           _ptr(aux), _ptr(mean_prob), _ptr(ws), ws.numel(), _stream()),
            "moe_route")
     return {"expert_ids": expert_ids, "gate_w": gate_w, "counts": counts, "aux": aux,
@@ -269,7 +286,8 @@ def moe_grouped_swiglu(cfg, x, w_gate, w_up, w_down, *, row_to_assign=None,
     return y_rows
 
 
-def moe_combine(cfg, y_rows, assign_to_row, shared_rows=None, out=None, validate=True):
+def moe_combine(cfg, y_rows, assign_to_row, shared_rows=None, out=None, validate=True, *,
+                x=None, shared_expert_gate=None):
     """Combine (see ``moe_combine``).  Every non-negative entry of
     ``assign_to_row`` must index a row of ``y_rows``; ``validate`` checks that
     on the host (a synchronisation)."""
@@ -282,16 +300,20 @@ def moe_combine(cfg, y_rows, assign_to_row, shared_rows=None, out=None, validate
     if validate and int(assign_to_row.max()) >= y_rows.shape[0]:
         raise ValueError("assign_to_row indexes past the end of y_rows")
     _expect(shared_rows, "shared_rows", (T, D), dt, required=False)
+    _expect(x, "x", (T, D), dt, required=False)
+    _expect(shared_expert_gate, "shared_expert_gate", (D,), dt, required=False)
     out = torch.empty(T, D, dtype=dt, device=y_rows.device) if out is None else out
     _expect(out, "out", (T, D), dt)
     _check(_lib.moe_combine(ctypes.byref(cfg), _ptr(y_rows), _ptr(assign_to_row),
-                            _ptr(shared_rows), _ptr(out), _stream()), "moe_combine")
+                            _ptr(shared_rows), _ptr(x), _ptr(shared_expert_gate), _ptr(out),
+                            _stream()), "moe_combine")
     return out
 
 
 def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, select_bias=None,
                 ws_gate=None, ws_up=None, ws_down=None, out=None, expert_ids=None, gate_w=None,
-                counts=None, aux=None, workspace=None):
+                counts=None, aux=None, workspace=None, token_mask=None,
+                shared_expert_gate=None):
     """The whole layer forward (see ``moe_forward``)."""
     check_config(cfg)
     T, D, H, E, k, Hs = cfg.T, cfg.D, cfg.H, cfg.E, cfg.top_k, cfg.H_shared
@@ -307,6 +329,8 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, sele
         _expect(ws_gate, "ws_gate", (Hs, D), dt)
         _expect(ws_up, "ws_up", (Hs, D), dt)
         _expect(ws_down, "ws_down", (D, Hs), dt)
+    _expect(shared_expert_gate, "shared_expert_gate", (D,), dt, required=False)
+    token_mask = _mask(token_mask, T)
     out = torch.empty(T, D, dtype=dt, device=x.device) if out is None else out
     _expect(out, "out", (T, D), dt)
     _expect(expert_ids, "expert_ids", (T, k), torch.int32, required=False)
@@ -315,8 +339,9 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, sele
     _expect(aux, "aux", (2,), torch.float32, required=False)
     ws = new_workspace(cfg, x.device) if workspace is None else workspace
     _check(_lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logit_bias),
-                            _ptr(select_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-                            _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(out),
+                            _ptr(select_bias), _ptr(token_mask), _ptr(w_gate), _ptr(w_up),
+                            _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
+                            _ptr(shared_expert_gate), _ptr(out),
                             _ptr(expert_ids), _ptr(gate_w), _ptr(counts), _ptr(aux), _ptr(ws),
                             ws.numel(), _stream()), "moe_forward")
     return out

@@ -1,5 +1,6 @@
 // Combine: out[t] = sum over kept slots (slot order) of the weighted expert
-// rows, plus the shared-expert row; fp32 accumulation, one rounding.
+// rows, plus the shared-expert row (optionally scaled by its per-token gate);
+// fp32 accumulation, one rounding.
 //
 // This is the index_add_ step of "Lab: build a tiny MoE in PyTorch" ("Full
 // implementation") written as a gather: each output row is owned by one
@@ -59,7 +60,10 @@ __device__ __forceinline__ void store16(T* p, const float (&v)[Vec16<T>::N]) {
   *reinterpret_cast<uint4*>(p) = q;
 }
 
-// Block = TPB tokens x (NTHREADS / TPB) threads per token.
+// Block = TPB tokens x (NTHREADS / TPB) threads per token.  With a shared
+// expert gate, the token's threads first form x[t] . g in fp32 (each thread
+// over its chunks, then the token's partials added in thread order), and
+// the shared row is scaled by sigmoid of it.
 template <typename T>
 __global__ __launch_bounds__(NTHREADS) void combine_kernel(CombineParams p, int tpb) {
   constexpr int N = Vec16<T>::N;
@@ -67,18 +71,41 @@ __global__ __launch_bounds__(NTHREADS) void combine_kernel(CombineParams p, int 
   const T* sh = static_cast<const T*>(p.shared_rows);
   T* out = static_cast<T*>(p.out);
   __shared__ int rows_lds[64 * kMaxTopK];
+  __shared__ float red[NTHREADS];
+  __shared__ float gate_lds[64];
   const int per_tok = NTHREADS / tpb;
   const int tl = threadIdx.x / per_tok;
   const int t = blockIdx.x * tpb + tl;
   const int sub = threadIdx.x % per_tok;
+  const int nchunk = p.D / N;
   for (int i = threadIdx.x; i < tpb * p.k; i += NTHREADS) {
     const int tt = blockIdx.x * tpb + i / p.k;
     rows_lds[i] = tt < p.T ? p.assign_to_row[(size_t)blockIdx.x * tpb * p.k + i] : -1;
   }
+  const bool gated = sh && p.shared_gate;  // uniform
+  if (gated) {
+    const T* xr = static_cast<const T*>(p.x) + (size_t)min(t, p.T - 1) * p.D;
+    const T* g = static_cast<const T*>(p.shared_gate);
+    float dot = 0.f;
+    for (int c = sub; c < nchunk; c += per_tok) {
+      float a[N], b[N];
+      load16<T>(xr + (size_t)c * N, a);
+      load16<T>(g + (size_t)c * N, b);
+#pragma unroll
+      for (int i = 0; i < N; ++i) dot += a[i] * b[i];
+    }
+    red[threadIdx.x] = dot;
+    __syncthreads();
+    if (sub == 0) {
+      float s = red[tl * per_tok];
+      for (int i = 1; i < per_tok; ++i) s += red[tl * per_tok + i];
+      gate_lds[tl] = 1.0f / (1.0f + expf(-s));
+    }
+  }
   __syncthreads();
   if (t >= p.T) return;
+  const float gs = gated ? gate_lds[tl] : 1.f;
   const int* rows = rows_lds + tl * p.k;
-  const int nchunk = p.D / N;
   for (int c = sub; c < nchunk; c += per_tok) {
     float acc[N];
 #pragma unroll
@@ -93,8 +120,13 @@ __global__ __launch_bounds__(NTHREADS) void combine_kernel(CombineParams p, int 
     if (sh) {
       float v[N];
       load16<T>(sh + (size_t)t * p.D + (size_t)c * N, v);
+      if (gated) {
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += v[i];
+        for (int i = 0; i < N; ++i) acc[i] += gs * v[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] += v[i];
+      }
     }
     store16<T>(out + (size_t)t * p.D + (size_t)c * N, acc);
   }

@@ -33,6 +33,16 @@ namespace {
 
 constexpr int NTHREADS = 256;
 
+// silu(g) * u, with both projections first clamped to [-limit, limit] when
+// limit > 0 (the clamped SwiGLU of the NeMo MLP, swiglu_limit).
+__device__ __forceinline__ float swiglu_act(float g, float u, float limit) {
+  if (limit > 0.f) {
+    g = fminf(fmaxf(g, -limit), limit);
+    u = fminf(fmaxf(u, -limit), limit);
+  }
+  return silu_f32(g) * u;
+}
+
 struct Tile {
   int e, m0, m_end, nt;
 };
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
           const int col = n0 + wn * WN + ni * 32 + lr;
           if (col < N) {
             const float g = acc[0][mi][ni][i], u = acc[1][mi][ni][i];
-            out[col] = f32_to_bf16_bits(silu_f32(g) * u);
+            out[col] = f32_to_bf16_bits(swiglu_act(g, u, p.swiglu_limit));
           }
         }
       } else {
@@ -526,7 +536,9 @@ __device__ __forceinline__ void dma_epilogue(const GemmParams& p, int m0, int m_
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni) {
           const int col = n0 + wn * C::WN + ni * 32 + lr;
-          if (col < N) out[col] = f32_to_bf16_bits(silu_f32(acc[0][mi][ni][i]) * acc[1][mi][ni][i]);
+          if (col < N)
+            out[col] = f32_to_bf16_bits(
+                swiglu_act(acc[0][mi][ni][i], acc[1][mi][ni][i], p.swiglu_limit));
         }
       } else {
         float gw = 1.f;
@@ -909,7 +921,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f32_kernel(GemmParams p, int ma
       if (col >= N) continue;
       if constexpr (GATEUP) {
         static_cast<float*>(p.hbuf)[(size_t)grow * N + col] =
-            silu_f32(acc[0][i][j]) * acc[NB - 1][i][j];
+            swiglu_act(acc[0][i][j], acc[NB - 1][i][j], p.swiglu_limit);
       } else {
         static_cast<float*>(p.y)[(size_t)grow * N + col] = gw * acc[0][i][j];
       }

@@ -23,6 +23,7 @@ struct RouteParams {
   const void* w_router;
   const float* logit_bias;
   const float* select_bias;
+  const uint8_t* token_mask;  // [T] or null: 0 = padding token (not routed)
   int32_t* ids;       // [T*k]
   float* gate_w;      // [T*k]
   float* logits_part; // [ksplit*T*E] split-K partial logits
@@ -30,6 +31,7 @@ struct RouteParams {
   int32_t* hist;      // [E*nblk]  per-tile expert histogram (expert-major)
   float* pe_part;     // [E*nblk]  per-tile sums of P_e terms
   float* z_part;      // [nblk]    per-block sums of lse^2
+  int32_t* valid_part;  // [nblk]  unmasked tokens per block
 };
 
 struct FinalizeParams {
@@ -38,6 +40,7 @@ struct FinalizeParams {
   const int32_t* hist;       // [E*nblk] (expert-major)
   const float* pe_part;      // [E*nblk] or null (no aux)
   const float* z_part;       // [nblk] or null
+  const int32_t* valid_part; // [nblk] unmasked tokens per block, or null (all T)
   int32_t* counts_ws;        // [E] scratch: counts before the capacity clip
   float* pe_ws;              // [E] scratch: P_e
   int32_t* counts;           // [E] or null
@@ -71,6 +74,7 @@ struct GemmParams {
   const void* w_down;
   void* hbuf;                // [max_rows, hidden]
   void* y;                   // [max_rows, D]
+  float swiglu_limit;        // > 0: clamp gate and up to [-limit, limit]
   // Split-K tail of the large-tile kernel (null: no split).  Per XCD: the
   // fp32 partial tiles [kTailSlots], the (tail tiles, pieces) pair and the
   // tile descriptors (expert, first row, row end, column tile).
@@ -92,6 +96,8 @@ struct CombineParams {
   const void* y_rows;
   const int32_t* assign_to_row;
   const void* shared_rows;
+  const void* x;             // [T, D], read only with shared_gate
+  const void* shared_gate;   // [D] or null: shared rows scaled by sigmoid(x . g)
   void* out;
 };
 

@@ -52,8 +52,11 @@ moe_status check_config(const moe_config* c) {
   if (c->H_shared < 0) return fail(MOE_ERR_INVALID_ARG, "H_shared must be >= 0");
   if (!is_dtype(c->act_dtype) || !is_dtype(c->router_dtype))
     return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
-  if (c->score_func != MOE_SCORE_SOFTMAX && c->score_func != MOE_SCORE_SIGMOID)
+  if (c->score_func != MOE_SCORE_SOFTMAX && c->score_func != MOE_SCORE_SIGMOID &&
+      c->score_func != MOE_SCORE_SQRTSOFTPLUS)
     return fail(MOE_ERR_INVALID_ARG, "unknown score function %d", c->score_func);
+  if (!(isfinite(c->swiglu_limit) && c->swiglu_limit >= 0.f))
+    return fail(MOE_ERR_INVALID_ARG, "swiglu_limit must be finite and >= 0 (0 = off)");
   if (c->renormalize != 0 && c->renormalize != 1)
     return fail(MOE_ERR_INVALID_ARG, "renormalize must be 0 or 1");
   if (!(isfinite(c->route_scale) && c->route_scale > 0.f))
@@ -104,7 +107,8 @@ long long max_rows_of(const moe_config* c) {
 }
 
 struct Layout {
-  size_t ids, gate_w, counts, aux, logits, hist, pe_part, z_part, block_base, counts_ws, pe_ws,
+  size_t ids, gate_w, counts, aux, logits, hist, pe_part, z_part, valid_part, block_base,
+      counts_ws, pe_ws,
       offsets, n_kept, r2a, a2r, hbuf, y, shared_y, tail, total;
 };
 
@@ -129,6 +133,7 @@ Layout layout_of(const moe_config* c) {
   L.hist = take(nblk * E * 4);
   L.pe_part = take(nblk * E * 4);
   L.z_part = take(nblk * 4);
+  L.valid_part = take(nblk * 4);
   L.block_base = take(nblk * E * 4);
   L.counts_ws = take(E * 4);
   L.pe_ws = take(E * 4);
@@ -193,8 +198,8 @@ T* at(void* ws, size_t off) {
 }
 
 moe::RouteParams route_params(const moe_config* c, const void* x, const void* w_router,
-                              const float* lb, const float* sb, int32_t* ids, float* gw,
-                              void* ws, const Layout& L) {
+                              const float* lb, const float* sb, const uint8_t* mask,
+                              int32_t* ids, float* gw, void* ws, const Layout& L) {
   moe::RouteParams p{};
   p.T = c->T;
   p.D = c->D;
@@ -212,6 +217,7 @@ moe::RouteParams route_params(const moe_config* c, const void* x, const void* w_
   p.w_router = w_router;
   p.logit_bias = lb;
   p.select_bias = sb;
+  p.token_mask = mask;
   p.ids = ids;
   p.gate_w = gw;
   p.logits_part = at<float>(ws, L.logits);
@@ -219,6 +225,7 @@ moe::RouteParams route_params(const moe_config* c, const void* x, const void* w_
   p.hist = at<int32_t>(ws, L.hist);
   p.pe_part = at<float>(ws, L.pe_part);
   p.z_part = at<float>(ws, L.z_part);
+  p.valid_part = at<int32_t>(ws, L.valid_part);
   return p;
 }
 
@@ -249,6 +256,7 @@ moe::GemmParams gemm_params(const moe_config* c, int n_groups, int hidden, const
   p.w_down = wd;
   p.hbuf = hbuf;
   p.y = y;
+  p.swiglu_limit = c->swiglu_limit;
   return p;
 }
 
@@ -292,9 +300,10 @@ size_t moe_workspace_bytes(const moe_config* cfg) {
 }
 
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
-                     const float* logit_bias, const float* select_bias, int32_t* expert_ids,
-                     float* gate_w, int32_t* counts, float* aux, float* mean_prob,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                     const float* logit_bias, const float* select_bias,
+                     const uint8_t* token_mask, int32_t* expert_ids, float* gate_w,
+                     int32_t* counts, float* aux, float* mean_prob, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_config(cfg));
   if (!x || !w_router || !expert_ids || !gate_w || !counts)
     return fail(MOE_ERR_NULL_PTR, "moe_route: x, w_router, expert_ids, gate_w, counts required");
@@ -303,6 +312,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   MOE_TRY(check_dev(w_router, "w_router", true));
   MOE_TRY(check_dev(logit_bias, "logit_bias", false));
   MOE_TRY(check_dev(select_bias, "select_bias", false));
+  MOE_TRY(check_dev(token_mask, "token_mask", false));
   MOE_TRY(check_dev(expert_ids, "expert_ids", true));
   MOE_TRY(check_dev(gate_w, "gate_w", true));
   MOE_TRY(check_dev(counts, "counts", true));
@@ -310,8 +320,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   MOE_TRY(check_dev(mean_prob, "mean_prob", false));
   MOE_TRY(check_dev(workspace, "workspace", true));
   const Layout L = layout_of(cfg);
-  const moe::RouteParams rp =
-      route_params(cfg, x, w_router, logit_bias, select_bias, expert_ids, gate_w, workspace, L);
+  const moe::RouteParams rp = route_params(cfg, x, w_router, logit_bias, select_bias, token_mask,
+                                          expert_ids, gate_w, workspace, L);
   MOE_TRY(hip_ok(moe::launch_route(rp, stream), "route kernel"));
   moe::FinalizeParams fp{};
   fp.T = cfg->T;
@@ -324,6 +334,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   fp.pe_ws = at<float>(workspace, L.pe_ws);
   fp.pe_part = rp.pe_part;
   fp.z_part = rp.z_part;
+  fp.valid_part = rp.valid_part;
   fp.counts = counts;
   fp.aux = aux;
   fp.mean_prob = mean_prob;
@@ -424,23 +435,31 @@ moe_status moe_grouped_swiglu(const moe_config* cfg, int32_t n_experts, int32_t 
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* y_rows, const int32_t* assign_to_row,
-                       const void* shared_rows, void* out, hipStream_t stream) {
+                       const void* shared_rows, const void* x, const void* shared_expert_gate,
+                       void* out, hipStream_t stream) {
   MOE_TRY(check_config(cfg));
   if (!y_rows || !assign_to_row || !out)
     return fail(MOE_ERR_NULL_PTR, "moe_combine: y_rows, assign_to_row and out are required");
+  if (shared_expert_gate && (!shared_rows || !x))
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_combine: shared_expert_gate needs shared_rows and x");
   MOE_TRY(check_dev(y_rows, "y_rows", true));
   MOE_TRY(check_dev(assign_to_row, "assign_to_row", true));
   MOE_TRY(check_dev(shared_rows, "shared_rows", false));
+  MOE_TRY(check_dev(x, "x", false));
+  MOE_TRY(check_dev(shared_expert_gate, "shared_expert_gate", false));
   MOE_TRY(check_dev(out, "out", true));
-  moe::CombineParams p{cfg->T, cfg->D, cfg->top_k, y_rows, assign_to_row, shared_rows, out};
+  moe::CombineParams p{cfg->T,      cfg->D, cfg->top_k, y_rows, assign_to_row, shared_rows,
+                       x,           shared_expert_gate,  out};
   MOE_TRY(hip_ok(moe::launch_combine(p, cfg->act_dtype == MOE_BF16, stream), "combine kernel"));
   return ok();
 }
 
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
-                       const float* logit_bias, const float* select_bias, const void* w_gate,
-                       const void* w_up, const void* w_down, const void* w_shared_gate,
-                       const void* w_shared_up, const void* w_shared_down, void* out,
+                       const float* logit_bias, const float* select_bias,
+                       const uint8_t* token_mask, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* w_shared_gate, const void* w_shared_up,
+                       const void* w_shared_down, const void* shared_expert_gate, void* out,
                        int32_t* expert_ids, float* gate_w, int32_t* counts, float* aux,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_config(cfg));
@@ -448,11 +467,15 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     return fail(MOE_ERR_NULL_PTR, "moe_forward: x, w_router, expert weights and out required");
   if (cfg->H_shared > 0 && (!w_shared_gate || !w_shared_up || !w_shared_down))
     return fail(MOE_ERR_NULL_PTR, "moe_forward: H_shared > 0 needs the shared-expert weights");
+  if (shared_expert_gate && cfg->H_shared == 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward: shared_expert_gate needs a shared expert");
   MOE_TRY(check_ws(cfg, workspace, workspace_bytes));
   MOE_TRY(check_dev(x, "x", true));
   MOE_TRY(check_dev(w_router, "w_router", true));
   MOE_TRY(check_dev(logit_bias, "logit_bias", false));
   MOE_TRY(check_dev(select_bias, "select_bias", false));
+  MOE_TRY(check_dev(token_mask, "token_mask", false));
+  MOE_TRY(check_dev(shared_expert_gate, "shared_expert_gate", false));
   MOE_TRY(check_dev(w_gate, "w_gate", true));
   MOE_TRY(check_dev(w_up, "w_up", true));
   MOE_TRY(check_dev(w_down, "w_down", true));
@@ -481,7 +504,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   const int rows = (int)max_rows_of(cfg);
 
   const moe::RouteParams rp =
-      route_params(cfg, x, w_router, logit_bias, select_bias, ids, gw, workspace, L);
+      route_params(cfg, x, w_router, logit_bias, select_bias, token_mask, ids, gw, workspace, L);
   MOE_TRY(hip_ok(moe::launch_route(rp, stream), "route kernel"));
   moe::FinalizeParams fp{};
   fp.T = cfg->T;
@@ -494,6 +517,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   fp.pe_ws = at<float>(workspace, L.pe_ws);
   fp.pe_part = rp.pe_part;
   fp.z_part = rp.z_part;
+  fp.valid_part = rp.valid_part;
   fp.counts = cnt;
   fp.aux = ax;
   fp.block_base = at<int32_t>(workspace, L.block_base);
@@ -519,7 +543,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                     w_shared_up, w_shared_down, hbuf, sy, tail);
     MOE_TRY(hip_ok(moe::launch_grouped_swiglu(sp2, bf16, stream), "shared expert kernels"));
   }
-  moe::CombineParams cp{cfg->T, cfg->D, cfg->top_k, y, a2r, sy, out};
+  moe::CombineParams cp{cfg->T, cfg->D, cfg->top_k, y, a2r, sy, x, shared_expert_gate, out};
   MOE_TRY(hip_ok(moe::launch_combine(cp, bf16, stream), "combine kernel"));
   return ok();
 }

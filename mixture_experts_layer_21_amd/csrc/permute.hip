@@ -69,6 +69,19 @@ __device__ __forceinline__ float block_sum(float v, float* s_w) {
   return t;
 }
 
+// Unmasked tokens: the sum of the per-block counts (fixed order), or T.
+__device__ __forceinline__ int valid_tokens(const FinalizeParams& p, int* s_i) {
+  if (!p.valid_part) return p.T;
+  int n = 0;
+  for (int b0 = 0; b0 < p.nblk; b0 += 256) {
+    const int b = b0 + threadIdx.x;
+    int tot;
+    block_scan_incl(b < p.nblk ? p.valid_part[b] : 0, s_i, tot);
+    n += tot;
+  }
+  return n;
+}
+
 // One block (256 threads) per expert: scan its column of tile counts.
 __global__ __launch_bounds__(256) void column_scan_kernel(FinalizeParams p) {
   __shared__ int s_i[4];
@@ -86,11 +99,12 @@ __global__ __launch_bounds__(256) void column_scan_kernel(FinalizeParams p) {
     run += tot;
     if (p.pe_part) ps += block_sum(b < p.nblk ? p.pe_part[(size_t)e * p.nblk + b] : 0.f, s_f);
   }
+  const int nv = p.pe_part ? valid_tokens(p, s_i) : p.T;
   if (threadIdx.x == 0) {
     p.counts_ws[e] = run;
     if (p.counts) p.counts[e] = run;
     if (p.pe_part) {
-      const float pe = ps / (float)p.T;
+      const float pe = nv > 0 ? ps / (float)nv : 0.f;
       p.pe_ws[e] = pe;
       if (p.mean_prob) p.mean_prob[e] = pe;
     }
@@ -103,7 +117,8 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(FinalizeParams p) {
   __shared__ float s_f[4];
   int base = 0;
   float bal = 0.f;
-  const float inv = 1.0f / ((float)p.T * (float)p.k);
+  const int nv = p.aux ? valid_tokens(p, s_i) : p.T;
+  const float inv = nv > 0 ? 1.0f / ((float)nv * (float)p.k) : 0.f;
   for (int e0 = 0; e0 < p.E; e0 += 256) {
     const int e = e0 + threadIdx.x;
     const int c = e < p.E ? p.counts_ws[e] : 0;
@@ -126,7 +141,7 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(FinalizeParams p) {
     if (p.n_kept) *p.n_kept = base;
     if (p.aux) {
       p.aux[0] = (float)p.E * bal;
-      p.aux[1] = z / (float)p.T;
+      p.aux[1] = nv > 0 ? z / (float)nv : 0.f;
     }
   }
 }

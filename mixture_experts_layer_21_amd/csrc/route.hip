@@ -340,8 +340,14 @@ struct SelectSmem {
   float lg[RT * kMaxExperts];      // summed logits of the block's tokens, row stride E
   float pe[SEL_WAVES][kMaxExperts];
   float zw[SEL_WAVES];
+  int nv[SEL_WAVES];
   int hist[kMaxExperts];
 };
+
+// sqrt(softplus(h)), softplus(h) = log(1 + e^h) written without overflow.
+__device__ __forceinline__ float sqrt_softplus(float h) {
+  return sqrtf(fmaxf(h, 0.f) + log1pf(expf(-fabsf(h))));
+}
 
 // Phase 1: the block's [RT x E] logits, the K-split partials added in split
 // order, into LDS (all threads, 16-byte loads, up to 16 loads in flight).
@@ -405,8 +411,10 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
   }
   __syncthreads();
 
-  const bool sigm = p.score_func == 1;
-  const bool by_score = sigm || p.select_bias != nullptr;
+  // softmax scores are a distribution over the experts; sigmoid and
+  // sqrt-softplus scores are per expert and normalised where a sum is needed.
+  const bool per_expert = p.score_func != 0;
+  const bool by_score = per_expert || p.select_bias != nullptr;
   const int gsz = p.n_groups > 1 ? E / p.n_groups : E;
   // Group limit with a segmented reduction: groups are aligned runs of gsz
   // lanes in one slot when gsz is a power of two below 64.
@@ -422,9 +430,18 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
   }
   float pacc[4] = {0.f, 0.f, 0.f, 0.f};
   float zacc = 0.f;
+  int nvalid = 0;
 
   for (int tl = wave; tl < nt; tl += SEL_WAVES) {
     const int t = t0 + tl;
+    if (p.token_mask && !p.token_mask[t]) {  // padding token: not routed
+      if (lane < k) {
+        p.ids[(size_t)t * k + lane] = -1;
+        p.gate_w[(size_t)t * k + lane] = 0.f;
+      }
+      continue;
+    }
+    ++nvalid;
     float h[4], sc[4], sel[4];
     float mloc = -INFINITY;
 #pragma unroll
@@ -442,7 +459,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
     const float S = wave_sum_dpp(sloc);
     const float lse = m + logf(S);
     zacc += lse * lse;
-    if (!sigm) {
+    if (!per_expert) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         sc[j] = ex[j] / S;
@@ -452,7 +469,10 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
       float ssl = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sc[j] = ok[j] ? 1.0f / (1.0f + expf(-h[j])) : 0.f;
+        if (!ok[j])
+          sc[j] = 0.f;
+        else
+          sc[j] = p.score_func == 1 ? 1.0f / (1.0f + expf(-h[j])) : sqrt_softplus(h[j]);
         ssl += sc[j];
       }
       const float ss = wave_sum_dpp(ssl);
@@ -557,7 +577,10 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
     const int e = lane + 64 * j;
     if (e < E) sm.pe[wave][e] = pacc[j];
   }
-  if (lane == 0) sm.zw[wave] = zacc;
+  if (lane == 0) {
+    sm.zw[wave] = zacc;
+    sm.nv[wave] = nvalid;
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += SEL_THREADS) {
     float s = sm.pe[0][e];
@@ -569,9 +592,14 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
   }
   if (threadIdx.x == 0) {
     float s = sm.zw[0];
+    int nv = sm.nv[0];
 #pragma unroll
-    for (int w = 1; w < SEL_WAVES; ++w) s += sm.zw[w];
+    for (int w = 1; w < SEL_WAVES; ++w) {
+      s += sm.zw[w];
+      nv += sm.nv[w];
+    }
     p.z_part[blk] = s;
+    p.valid_part[blk] = nv;
   }
 }
 

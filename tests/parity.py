@@ -15,13 +15,14 @@ GATE_TOL = 1e-5          # absolute, on the fp32 gate weights
 AUX_RTOL = 1e-4
 
 
-def config_of(w: W.Workload):
+def config_of(w: W.Workload, swiglu_limit=0.0):
     import mixture_experts_layer_21_amd as moe
     return moe.make_config(w.T, w.D, w.H, w.E, w.top_k, H_shared=w.H_shared,
                            act_dtype=w.act_dtype, router_dtype=w.router_dtype, score=w.score,
                            renormalize=w.renormalize, route_scale=w.route_scale,
                            n_groups=w.n_groups, topk_groups=w.topk_groups,
-                           group_rule=w.group_rule, capacity_factor=w.capacity_factor)
+                           group_rule=w.group_rule, capacity_factor=w.capacity_factor,
+                           swiglu_limit=swiglu_limit)
 
 
 class LazyF64:
@@ -46,19 +47,21 @@ def oracle_inputs(inp: dict) -> dict:
     return out
 
 
-def oracle_route(w: W.Workload, oi: dict):
+def oracle_route(w: W.Workload, oi: dict, token_mask=None):
     return oracle.route(oi["x"], oi["w_router"], w.top_k, score=w.score,
                         renormalize=w.renormalize, route_scale=w.route_scale,
                         logit_bias=oi.get("logit_bias"), select_bias=oi.get("select_bias"),
                         n_groups=w.n_groups, topk_groups=w.topk_groups,
-                        group_rule=w.group_rule)
+                        group_rule=w.group_rule, token_mask=token_mask)
 
 
-def oracle_forward(w: W.Workload, oi: dict, routing=None, tokens=None):
+def oracle_forward(w: W.Workload, oi: dict, routing=None, tokens=None, token_mask=None,
+                   swiglu_limit=0.0):
     return oracle.forward(oi, top_k=w.top_k, score=w.score, renormalize=w.renormalize,
                           route_scale=w.route_scale, n_groups=w.n_groups,
                           topk_groups=w.topk_groups, group_rule=w.group_rule,
-                          capacity_factor=w.capacity_factor, routing=routing, tokens=tokens)
+                          capacity_factor=w.capacity_factor, routing=routing, tokens=tokens,
+                          token_mask=token_mask, swiglu_limit=swiglu_limit)
 
 
 def compare_route(w, r_ref, gpu):
@@ -74,8 +77,11 @@ def compare_route(w, r_ref, gpu):
     err = np.abs(gw[ok] - r_ref["weights"][ok]).max(initial=0.0)
     assert err <= GATE_TOL, f"gate weight error {err:.3g} > {GATE_TOL}"
     counts = gpu["counts"].cpu().numpy()
-    assert (counts == np.bincount(ids.reshape(-1), minlength=w.E)).all(), "counts != bincount(ids)"
-    assert counts.sum() == w.T * w.top_k
+    routed = ids >= 0
+    assert (counts == np.bincount(ids[routed].reshape(-1), minlength=w.E)).all(), \
+        "counts != bincount(ids)"
+    n_valid = int((r_ref["ids"][:, 0] >= 0).sum())
+    assert counts.sum() == n_valid * w.top_k
     differ = int((ids[flag] != r_ref["ids"][flag]).any(1).sum())
     if differ == 0:
         assert (counts == r_ref["counts"]).all()

@@ -56,6 +56,7 @@ def test_status_strings(moe):
     (dict(n_groups=4, topk_groups=1, top_k=3), "exceeds the experts"),
     (dict(D=100), "multiples of 64"),
     (dict(route_scale=0.0), "route_scale"),
+    (dict(swiglu_limit=-1.0), "swiglu_limit"),
 ])
 def test_config_errors(moe, kw, match):
     base = dict(T=16, D=128, H=64, E=8, top_k=2)
@@ -86,7 +87,23 @@ def test_workspace_grows_with_problem(moe):
     assert b >= 4096 * 2 * (14336 + 4096) * 2
 
 
-def test_struct_layout_matches_header(moe):
-    assert ctypes.sizeof(moe.MoeConfig) == 64
-    assert moe.MoeConfig.capacity_factor.offset == 56
-    assert moe.MoeConfig.route_scale.offset == 40
+def test_struct_layout_matches_header(moe, tmp_path):
+    """Every field of the ctypes mirror sits where the C compiler puts it in
+    include/moe.h (a host C program prints sizeof and each offsetof)."""
+    import subprocess
+    fields = [f[0] for f in moe.MoeConfig._fields_]
+    prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "moe.h"',
+            "int main(void) {", '  printf("%zu\\n", sizeof(moe_config));']
+    prog += [f'  printf("%zu\\n", offsetof(moe_config, {n}));' for n in fields]
+    prog += ["  return 0;", "}"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(prog) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(ROOT, "include")
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", inc, "-I", "/opt/rocm/include",
+                    str(c), "-o", str(exe)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                           text=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(moe.MoeConfig)
+    for name, off in zip(fields, vals[1:]):
+        assert getattr(moe.MoeConfig, name).offset == off, name

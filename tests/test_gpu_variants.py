@@ -1,0 +1,169 @@
+"""GPU parity of the forward variants named on the NeMo AutoModel MoE page:
+score functions (sqrt-softplus; softmax with a selection bias; softmax-then-
+top-k without renormalisation for k > 1), the token (padding) mask, the
+clamped SwiGLU (swiglu_limit) and the gated shared expert, each against the
+CPU oracle on the reduced workloads (every output element compared)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import mixture_experts_layer_21_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return m
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _to_dev(inp):
+    return {k: v.to("cuda") for k, v in inp.items()}
+
+
+def _mask(T, seed, frac=0.3):
+    g = np.random.default_rng(seed)
+    m = g.random(T) >= frac
+    m[0] = False           # the first token of the first tile is padding
+    return m
+
+
+def _forward(moe, w, cfg, d, **kw):
+    ids = torch.empty(w.T, w.top_k, dtype=torch.int32, device="cuda")
+    gw = torch.empty(w.T, w.top_k, dtype=torch.float32, device="cuda")
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    aux = torch.empty(2, dtype=torch.float32, device="cuda")
+    out = moe.moe_forward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                          logit_bias=d.get("logit_bias"), select_bias=d.get("select_bias"),
+                          ws_gate=d.get("ws_gate"), ws_up=d.get("ws_up"),
+                          ws_down=d.get("ws_down"), expert_ids=ids, gate_w=gw, counts=counts,
+                          aux=aux, **kw)
+    torch.cuda.synchronize()
+    return out, ids, gw, counts, aux
+
+
+SCORE_CASES = [
+    # workload, score, renormalize, selection bias sigma, k override
+    ("mixtral_small", "sqrtsoftplus", True, 0.0, None),
+    ("deepseek_small", "sqrtsoftplus", True, 0.01, None),
+    ("decode_small", "softmax", False, 0.0, 4),
+    ("mixtral_small", "softmax", True, 0.01, None),
+    ("switch_small", "sqrtsoftplus", False, 0.0, None),
+]
+
+
+@pytest.mark.parametrize("name,score,renorm,sb,k", SCORE_CASES)
+def test_route_score_variants(moe, name, score, renorm, sb, k):
+    w = W.SMALL[name].with_(score=score, renormalize=renorm, select_bias_sigma=sb,
+                            top_k=k or W.SMALL[name].top_k)
+    _say(f"[score] {name} {score} renorm={renorm} sb={sb} k={w.top_k}")
+    inp = W.make_inputs(w, "cpu", seed=11)
+    d = _to_dev(inp)
+    cfg = P.config_of(w)
+    g = moe.moe_route(cfg, d["x"], d["w_router"], d.get("logit_bias"), d.get("select_bias"))
+    torch.cuda.synchronize()
+    r = P.oracle_route(w, P.oracle_inputs(inp))
+    nflag, ndiff = P.compare_route(w, r, g)
+    _say(f"  near ties flagged {nflag}, differing {ndiff}")
+    if not renorm and score == "softmax":
+        assert (g["gate_w"].sum(1) < 1.0).all()
+
+
+@pytest.mark.parametrize("name", sorted(W.SMALL))
+def test_forward_token_mask(moe, name):
+    w = W.SMALL[name]
+    _say(f"[mask] {name}")
+    inp = W.make_inputs(w, "cpu", seed=12)
+    d = _to_dev(inp)
+    cfg = P.config_of(w)
+    mask = _mask(w.T, 12)
+    out, ids, gw, counts, aux = _forward(moe, w, cfg, d,
+                                         token_mask=torch.from_numpy(mask).cuda())
+    oi = P.oracle_inputs(inp)
+    r = P.oracle_route(w, oi, token_mask=mask)
+    ids_h = ids.cpu().numpy()
+    assert (ids_h[~mask] == -1).all() and (gw.cpu().numpy()[~mask] == 0).all()
+    P.compare_route(w, r, {"expert_ids": ids, "gate_w": gw, "counts": counts, "aux": aux,
+                           "mean_prob": moe.moe_route(cfg, d["x"], d["w_router"],
+                                                      d.get("logit_bias"), d.get("select_bias"),
+                                                      token_mask=torch.from_numpy(mask).cuda())
+                           ["mean_prob"]})
+    f = P.oracle_forward(w, oi, routing={"ids": ids_h.astype(np.int64),
+                                         "weights": gw.cpu().numpy().astype(np.float64)},
+                         token_mask=mask)
+    err, scale = P.compare_rows(out, f["out"], w.act_dtype, f"{name} masked forward")
+    _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
+
+
+def test_all_tokens_masked(moe):
+    w = W.SMALL["deepseek_small"]
+    inp = W.make_inputs(w, "cpu", seed=13)
+    d = _to_dev(inp)
+    cfg = P.config_of(w)
+    mask = torch.zeros(w.T, dtype=torch.bool, device="cuda")
+    out, ids, gw, counts, aux = _forward(moe, w, cfg, d, token_mask=mask)
+    assert (ids == -1).all() and (counts == 0).all() and (aux == 0).all()
+    oi = P.oracle_inputs(inp)
+    shared = P.oracle.shared_expert(oi["x"], oi)
+    P.compare_rows(out, shared, w.act_dtype, "all masked: shared expert only")
+
+
+LIMIT_CASES = [("mixtral_small", 0.2), ("decode_small", 0.2), ("tiny", 0.1),
+               ("deepseek_small", 0.05), ("switch_small", 0.2)]
+
+
+@pytest.mark.parametrize("name,limit", LIMIT_CASES)
+def test_forward_swiglu_limit(moe, name, limit):
+    w = W.SMALL[name]
+    _say(f"[swiglu_limit] {name} L={limit}")
+    inp = W.make_inputs(w, "cpu", seed=14)
+    d = _to_dev(inp)
+    cfg = P.config_of(w, swiglu_limit=limit)
+    out, ids, gw, _, _ = _forward(moe, w, cfg, d)
+    oi = P.oracle_inputs(inp)
+    routing = {"ids": ids.cpu().numpy().astype(np.int64),
+               "weights": gw.cpu().numpy().astype(np.float64)}
+    f = P.oracle_forward(w, oi, routing=routing, swiglu_limit=limit)
+    err, scale = P.compare_rows(out, f["out"], w.act_dtype, f"{name} clamped forward")
+    plain = P.oracle_forward(w, oi, routing=routing)["out"]
+    assert np.abs(plain - f["out"]).max() > 10 * (err + 1e-12), "the clamp changed nothing"
+    _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
+
+
+@pytest.mark.parametrize("name", ["deepseek_small", "decode_small"])
+def test_forward_shared_expert_gate(moe, name):
+    w = W.SMALL[name].with_(H_shared=W.SMALL[name].H_shared or 256)
+    _say(f"[shared gate] {name}")
+    inp = W.make_inputs(w, "cpu", seed=15)
+    gen = torch.Generator().manual_seed(15)
+    inp["ws_sgate"] = (torch.randn(w.D, generator=gen) / w.D ** 0.5).to(
+        W.torch_dtype(w.act_dtype))
+    d = _to_dev(inp)
+    cfg = P.config_of(w)
+    out, ids, gw, _, _ = _forward(moe, w, cfg, d, shared_expert_gate=d["ws_sgate"])
+    oi = P.oracle_inputs(inp)
+    f = P.oracle_forward(w, oi, routing={"ids": ids.cpu().numpy().astype(np.int64),
+                                         "weights": gw.cpu().numpy().astype(np.float64)})
+    err, scale = P.compare_rows(out, f["out"], w.act_dtype, f"{name} gated shared expert")
+    _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
+
+
+def test_shared_gate_needs_shared_expert(moe):
+    w = W.SMALL["mixtral_small"]
+    d = _to_dev(W.make_inputs(w, "cpu", seed=16))
+    cfg = P.config_of(w)
+    with pytest.raises(moe.MoeError, match="shared_expert_gate"):
+        moe.moe_forward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                        shared_expert_gate=torch.zeros(w.D, dtype=torch.bfloat16,
+                                                       device="cuda"))
