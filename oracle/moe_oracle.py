@@ -63,7 +63,7 @@ import numpy as np
 __all__ = [
     "NEAR_TIE", "router_logits", "softmax", "sigmoid", "softplus", "logsumexp",
     "route", "capacity", "first_within_capacity", "permutation",
-    "swiglu_ffn", "expert_outputs", "shared_expert", "combine", "forward",
+    "swiglu_ffn", "expert_outputs", "shared_expert", "combine", "forward", "update_bias",
     "brute_force_forward", "all_experts_then_mask",
 ]
 
@@ -330,15 +330,19 @@ def expert_outputs(x, ids, weights, keep, w_gate, w_up, w_down, tokens=None, lim
     return Y
 
 
-def combine(Y, shared=None):
+def combine(Y, shared=None, residual=None):
     """out_t = sum over slots (in slot order) of the weighted expert outputs,
     plus the always-on shared expert ([LAB] ``index_add_`` combine and
-    "Add a shared expert")."""
+    "Add a shared expert"), plus the residual stream when given (the block's
+    skip connection around the layer, [BOOK] "From One FFN to a Bank of
+    Experts": the MoE layer replaces the FFN of a transformer block)."""
     out = np.zeros(Y.shape[::2])
     for s in range(Y.shape[1]):
         out = out + Y[:, s]
     if shared is not None:
         out = out + shared
+    if residual is not None:
+        out = out + np.asarray(residual, dtype=np.float64)
     return out
 
 
@@ -357,7 +361,7 @@ def shared_expert(x, inputs, limit=0.0):
 
 def forward(inputs, *, top_k, score="softmax", renormalize=True, route_scale=1.0,
             n_groups=1, topk_groups=1, group_rule="top2sum", capacity_factor=None,
-            tokens=None, routing=None, token_mask=None, swiglu_limit=0.0):
+            tokens=None, routing=None, token_mask=None, swiglu_limit=0.0, residual=None):
     """The whole layer forward on float64 arrays.
 
     ``inputs`` holds x [T,D], w_router [E,D], w_gate/w_up [E,H,D], w_down
@@ -387,12 +391,28 @@ def forward(inputs, *, top_k, score="softmax", renormalize=True, route_scale=1.0
     Y = expert_outputs(x, r["ids"], r["weights"], keep, inputs["w_gate"],
                        inputs["w_up"], inputs["w_down"], tokens=tok, limit=swiglu_limit)
     shared = shared_expert(np.asarray(x, dtype=np.float64)[tok], inputs, swiglu_limit)
-    out = combine(Y, shared)
+    out = combine(Y, shared, None if residual is None else np.asarray(residual)[tok])
     return {
         "out": out, "tokens": tok, "route": r, "capacity": cap, "keep": keep,
         "expert_offsets": offsets, "row_to_assign": row_to_assign,
         "assign_to_row": assign_to_row, "n_kept": int(keep.sum()),
     }
+
+
+# ------------------------------------------------ bias-adjustment balancer ---
+
+def update_bias(bias, counts, gamma):
+    """One step of the auxiliary-loss-free balancer ([BOOK] "DeepSeek-MoE and
+    the fine-grained + shared-expert idea" and "Exercises" 6; [NEMO]
+    ``Gate.update_bias``): every expert above the mean load has its selection
+    bias lowered by ``gamma``, every expert below it raised, an expert exactly
+    at the mean left alone.  The comparison count_e <> mean(counts) is taken
+    exactly, as E * count_e <> sum(counts) on integers."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.size
+    total = int(counts.sum())
+    step = np.sign(total - E * counts).astype(np.float64)
+    return np.asarray(bias, dtype=np.float64) + gamma * step
 
 
 # ------------------------------------------- second implementations (tiny) ---

@@ -541,4 +541,40 @@ def pin_shared_expert_gate(o):
     assert np.allclose(big["out"], bf, rtol=0, atol=1e-12)
 
 
+def pin_update_bias_rule(o):
+    """Hand-worked step: counts (5, 1, 2, 0) have mean 2, so expert 0 goes
+    down, experts 1 and 3 go up and expert 2 (at the mean) stays."""
+    b = o.update_bias([0.5, -0.25, 0.0, 1.0], [5, 1, 2, 0], 0.125)
+    assert b.tolist() == [0.375, -0.125, 0.0, 1.125]
+    assert o.update_bias([0.1, 0.2], [7, 7], 1.0).tolist() == [0.1, 0.2]
+
+
+def pin_update_bias_balances(o):
+    """The book's demonstration: a router that favours one expert, corrected by
+    repeated select-with-bias steps, ends far more uniform, with a negative
+    bias on the favourite (selection on logits + bias, renormalised softmax of
+    the unbiased logits, as in the exercise)."""
+    r = np.random.default_rng(36)
+    h = r.normal(size=(1024, 8))
+    h[:, 0] += 3.0
+    bias = np.zeros(8)
+    first = None
+    for _ in range(200):
+        rr = _route_logits(o, h + bias[None, :], 2)
+        counts = rr["counts"]
+        first = counts if first is None else first
+        bias = o.update_bias(bias, counts, 1e-2)
+    assert counts.max() / max(counts.min(), 1) < first.max() / max(first.min(), 1) / 4
+    assert bias[0] < 0 and bias[0] == bias.min()
+
+
+def pin_residual_is_added(o):
+    """The residual stream adds to the layer output exactly."""
+    inp = _tiny_inputs(37, T=8, E=3, shared=True)
+    res = _rng(38).normal(size=inp["x"].shape)
+    a = o.forward(inp, top_k=2)["out"]
+    b = o.forward(inp, top_k=2, residual=res)["out"]
+    assert np.allclose(b, a + res, rtol=0, atol=1e-15)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -95,6 +95,15 @@ MUTANTS = [
     ("shared_gate_not_applied",
      "        s = sigmoid(x @ np.asarray(inputs[\"ws_sgate\"], dtype=np.float64))[:, None] * s",
      "        s = s"),
+    ("bias_update_sign_flipped",
+     "step = np.sign(total - E * counts).astype(np.float64)",
+     "step = np.sign(E * counts - total).astype(np.float64)"),
+    ("bias_update_against_max",
+     "step = np.sign(total - E * counts).astype(np.float64)",
+     "step = np.sign(counts.max() - counts).astype(np.float64)"),
+    ("residual_dropped",
+     "        out = out + np.asarray(residual, dtype=np.float64)",
+     "        out = out + 0.0"),
     ("router_bias_ignored",
      "h = h + np.asarray(logit_bias, dtype=np.float64)[None, :]",
      "h = h + 0.0"),
