@@ -189,22 +189,25 @@ moe_status moe_grouped_swiglu(const moe_config* cfg, int32_t n_experts, int32_t 
 /* Combine ("Full implementation" on the lab page, index_add_ back to token
  * order; "Add a shared expert"; NeMo MoE shared_expert_gate):
  *   out[t] = sum_{s=0..k-1, assign_to_row[t*k+s] >= 0} y_rows[assign_to_row[t*k+s]]
- *            (+ g_t * shared_rows[t]),
+ *            (+ g_t * shared_rows[t]) (+ residual[t]),
  *   g_t = sigmoid(x[t] . shared_expert_gate) when shared_expert_gate [D]
- *   (act_dtype) is given, else 1; x [T, D] is read only in that case.
+ *   (act_dtype) is given, else 1; x [T, D] is read only in that case;
+ *   residual [T, D] act_dtype or NULL: the block's skip connection (may be
+ *   x itself; it must not alias out unless it is out).
  * accumulated in fp32 in slot order, one rounding to act_dtype.  No atomics:
  * the result is deterministic.  A token with every slot dropped gets 0
  * (plus its shared-expert row). */
 moe_status moe_combine(const moe_config* cfg, const void* y_rows,
                        const int32_t* assign_to_row, const void* shared_rows,
-                       const void* x, const void* shared_expert_gate, void* out,
-                       hipStream_t stream);
+                       const void* x, const void* shared_expert_gate,
+                       const void* residual, void* out, hipStream_t stream);
 
 /* The whole forward: moe_route, moe_permute, moe_grouped_swiglu (routed and
  * shared expert) and moe_combine, stream-ordered, with no host
  * synchronisation.  w_shared_* may be NULL when cfg->H_shared == 0;
  * shared_expert_gate [D] (optional, needs a shared expert) scales its output
- * per token as in moe_combine; token_mask as in moe_route.  The optional
+ * per token as in moe_combine; token_mask as in moe_route; residual [T, D]
+ * (optional) is added to the output as in moe_combine.  The optional
  * outputs expert_ids [T,k], gate_w [T,k], counts [E] and aux [2] receive the
  * routing results when non-NULL. */
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
@@ -212,9 +215,21 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        const uint8_t* token_mask, const void* w_gate, const void* w_up,
                        const void* w_down, const void* w_shared_gate,
                        const void* w_shared_up, const void* w_shared_down,
-                       const void* shared_expert_gate, void* out, int32_t* expert_ids,
+                       const void* shared_expert_gate, const void* residual, void* out,
+                       int32_t* expert_ids,
                        float* gate_w, int32_t* counts, float* aux, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/* Auxiliary-loss-free balancer step ("DeepSeek-MoE and the fine-grained +
+ * shared-expert idea" and "Exercises" 6 on the book page; NeMo
+ * Gate.update_bias), in place on the selection bias that moe_route adds for
+ * selection only:
+ *   select_bias[e] += gamma * sign(mean_e' counts[e'] - counts[e])
+ * with the comparison taken exactly on integers.  counts [E] int32 (e.g. the
+ * counts output of moe_route), select_bias [E] f32, both device memory;
+ * gamma finite. */
+moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma,
+                           float* select_bias, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,6 @@ Importing it fails loudly when the library has not been built.
 """
 from ._binding import (  # noqa: F401
     EXPORTED, LIB_PATH, MoeConfig, MoeError, capacity, check_config, make_config, max_rows,
-    moe_combine, moe_forward, moe_grouped_swiglu, moe_permute, moe_route, new_workspace,
-    status_string, workspace_bytes,
+    moe_combine, moe_forward, moe_grouped_swiglu, moe_permute, moe_route, moe_update_bias,
+    new_workspace, status_string, workspace_bytes,
 )

@@ -91,9 +91,10 @@ _sigs = {
     "moe_permute": (ctypes.c_int, [_CFG, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_swiglu": (ctypes.c_int, [_CFG, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P,
                                           _P, _P, _P, _SZ, _P]),
-    "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                   _P, _P, _P, _P, _P, _SZ, _P]),
+                                   _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_update_bias": (ctypes.c_int, [_CFG, _P, ctypes.c_float, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -287,7 +288,7 @@ def moe_grouped_swiglu(cfg, x, w_gate, w_up, w_down, *, row_to_assign=None,
 
 
 def moe_combine(cfg, y_rows, assign_to_row, shared_rows=None, out=None, validate=True, *,
-                x=None, shared_expert_gate=None):
+                x=None, shared_expert_gate=None, residual=None):
     """Combine (see ``moe_combine``).  Every non-negative entry of
     ``assign_to_row`` must index a row of ``y_rows``; ``validate`` checks that
     on the host (a synchronisation)."""
@@ -302,18 +303,19 @@ def moe_combine(cfg, y_rows, assign_to_row, shared_rows=None, out=None, validate
     _expect(shared_rows, "shared_rows", (T, D), dt, required=False)
     _expect(x, "x", (T, D), dt, required=False)
     _expect(shared_expert_gate, "shared_expert_gate", (D,), dt, required=False)
+    _expect(residual, "residual", (T, D), dt, required=False)
     out = torch.empty(T, D, dtype=dt, device=y_rows.device) if out is None else out
     _expect(out, "out", (T, D), dt)
     _check(_lib.moe_combine(ctypes.byref(cfg), _ptr(y_rows), _ptr(assign_to_row),
-                            _ptr(shared_rows), _ptr(x), _ptr(shared_expert_gate), _ptr(out),
-                            _stream()), "moe_combine")
+                            _ptr(shared_rows), _ptr(x), _ptr(shared_expert_gate),
+                            _ptr(residual), _ptr(out), _stream()), "moe_combine")
     return out
 
 
 def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, select_bias=None,
                 ws_gate=None, ws_up=None, ws_down=None, out=None, expert_ids=None, gate_w=None,
                 counts=None, aux=None, workspace=None, token_mask=None,
-                shared_expert_gate=None):
+                shared_expert_gate=None, residual=None):
     """The whole layer forward (see ``moe_forward``)."""
     check_config(cfg)
     T, D, H, E, k, Hs = cfg.T, cfg.D, cfg.H, cfg.E, cfg.top_k, cfg.H_shared
@@ -330,6 +332,7 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, sele
         _expect(ws_up, "ws_up", (Hs, D), dt)
         _expect(ws_down, "ws_down", (D, Hs), dt)
     _expect(shared_expert_gate, "shared_expert_gate", (D,), dt, required=False)
+    _expect(residual, "residual", (T, D), dt, required=False)
     token_mask = _mask(token_mask, T)
     out = torch.empty(T, D, dtype=dt, device=x.device) if out is None else out
     _expect(out, "out", (T, D), dt)
@@ -341,7 +344,18 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, sele
     _check(_lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logit_bias),
                             _ptr(select_bias), _ptr(token_mask), _ptr(w_gate), _ptr(w_up),
                             _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
-                            _ptr(shared_expert_gate), _ptr(out),
+                            _ptr(shared_expert_gate), _ptr(residual), _ptr(out),
                             _ptr(expert_ids), _ptr(gate_w), _ptr(counts), _ptr(aux), _ptr(ws),
                             ws.numel(), _stream()), "moe_forward")
     return out
+
+
+def moe_update_bias(cfg, counts, gamma, select_bias):
+    """Auxiliary-loss-free balancer step on ``select_bias`` [E] f32, in place
+    (see ``moe_update_bias``); ``counts`` [E] int32 as returned by routing."""
+    check_config(cfg)
+    _expect(counts, "counts", (cfg.E,), torch.int32)
+    _expect(select_bias, "select_bias", (cfg.E,), torch.float32)
+    _check(_lib.moe_update_bias(ctypes.byref(cfg), _ptr(counts), float(gamma),
+                                _ptr(select_bias), _stream()), "moe_update_bias")
+    return select_bias

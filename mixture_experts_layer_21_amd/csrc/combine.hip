@@ -1,6 +1,6 @@
 // Combine: out[t] = sum over kept slots (slot order) of the weighted expert
-// rows, plus the shared-expert row (optionally scaled by its per-token gate);
-// fp32 accumulation, one rounding.
+// rows, plus the shared-expert row (optionally scaled by its per-token gate),
+// plus the residual stream when given; fp32 accumulation, one rounding.
 //
 // This is the index_add_ step of "Lab: build a tiny MoE in PyTorch" ("Full
 // implementation") written as a gather: each output row is owned by one
@@ -69,6 +69,7 @@ __global__ __launch_bounds__(NTHREADS) void combine_kernel(CombineParams p, int 
   constexpr int N = Vec16<T>::N;
   const T* y = static_cast<const T*>(p.y_rows);
   const T* sh = static_cast<const T*>(p.shared_rows);
+  const T* res = static_cast<const T*>(p.residual);
   T* out = static_cast<T*>(p.out);
   __shared__ int rows_lds[64 * kMaxTopK];
   __shared__ float red[NTHREADS];
@@ -127,6 +128,12 @@ __global__ __launch_bounds__(NTHREADS) void combine_kernel(CombineParams p, int 
 #pragma unroll
         for (int i = 0; i < N; ++i) acc[i] += v[i];
       }
+    }
+    if (res) {  // the residual stream joins last, before the one rounding
+      float v[N];
+      load16<T>(res + (size_t)t * p.D + (size_t)c * N, v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += v[i];
     }
     store16<T>(out + (size_t)t * p.D + (size_t)c * N, acc);
   }

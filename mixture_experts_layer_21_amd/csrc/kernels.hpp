@@ -98,6 +98,7 @@ struct CombineParams {
   const void* shared_rows;
   const void* x;             // [T, D], read only with shared_gate
   const void* shared_gate;   // [D] or null: shared rows scaled by sigmoid(x . g)
+  const void* residual;      // [T, D] or null: added to the output
   void* out;
 };
 
@@ -107,6 +108,8 @@ hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
 hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
+hipError_t launch_update_bias(int E, const int32_t* counts, float gamma, float* bias,
+                              hipStream_t s);
 
 inline int route_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
 

@@ -436,7 +436,7 @@ moe_status moe_grouped_swiglu(const moe_config* cfg, int32_t n_experts, int32_t 
 
 moe_status moe_combine(const moe_config* cfg, const void* y_rows, const int32_t* assign_to_row,
                        const void* shared_rows, const void* x, const void* shared_expert_gate,
-                       void* out, hipStream_t stream) {
+                       const void* residual, void* out, hipStream_t stream) {
   MOE_TRY(check_config(cfg));
   if (!y_rows || !assign_to_row || !out)
     return fail(MOE_ERR_NULL_PTR, "moe_combine: y_rows, assign_to_row and out are required");
@@ -448,9 +448,10 @@ moe_status moe_combine(const moe_config* cfg, const void* y_rows, const int32_t*
   MOE_TRY(check_dev(shared_rows, "shared_rows", false));
   MOE_TRY(check_dev(x, "x", false));
   MOE_TRY(check_dev(shared_expert_gate, "shared_expert_gate", false));
+  MOE_TRY(check_dev(residual, "residual", false));
   MOE_TRY(check_dev(out, "out", true));
-  moe::CombineParams p{cfg->T,      cfg->D, cfg->top_k, y_rows, assign_to_row, shared_rows,
-                       x,           shared_expert_gate,  out};
+  moe::CombineParams p{cfg->T, cfg->D, cfg->top_k,        y_rows,   assign_to_row,
+                       shared_rows, x, shared_expert_gate, residual, out};
   MOE_TRY(hip_ok(moe::launch_combine(p, cfg->act_dtype == MOE_BF16, stream), "combine kernel"));
   return ok();
 }
@@ -459,8 +460,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        const float* logit_bias, const float* select_bias,
                        const uint8_t* token_mask, const void* w_gate, const void* w_up,
                        const void* w_down, const void* w_shared_gate, const void* w_shared_up,
-                       const void* w_shared_down, const void* shared_expert_gate, void* out,
-                       int32_t* expert_ids, float* gate_w, int32_t* counts, float* aux,
+                       const void* w_shared_down, const void* shared_expert_gate,
+                       const void* residual, void* out, int32_t* expert_ids, float* gate_w,
+                       int32_t* counts, float* aux,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_config(cfg));
   if (!x || !w_router || !w_gate || !w_up || !w_down || !out)
@@ -476,6 +478,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   MOE_TRY(check_dev(select_bias, "select_bias", false));
   MOE_TRY(check_dev(token_mask, "token_mask", false));
   MOE_TRY(check_dev(shared_expert_gate, "shared_expert_gate", false));
+  MOE_TRY(check_dev(residual, "residual", false));
   MOE_TRY(check_dev(w_gate, "w_gate", true));
   MOE_TRY(check_dev(w_up, "w_up", true));
   MOE_TRY(check_dev(w_down, "w_down", true));
@@ -543,8 +546,22 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                     w_shared_up, w_shared_down, hbuf, sy, tail);
     MOE_TRY(hip_ok(moe::launch_grouped_swiglu(sp2, bf16, stream), "shared expert kernels"));
   }
-  moe::CombineParams cp{cfg->T, cfg->D, cfg->top_k, y, a2r, sy, x, shared_expert_gate, out};
+  moe::CombineParams cp{cfg->T, cfg->D, cfg->top_k, y,        a2r,
+                        sy,     x,      shared_expert_gate,      residual, out};
   MOE_TRY(hip_ok(moe::launch_combine(cp, bf16, stream), "combine kernel"));
+  return ok();
+}
+
+moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma,
+                           float* select_bias, hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  if (!counts || !select_bias)
+    return fail(MOE_ERR_NULL_PTR, "moe_update_bias: counts and select_bias are required");
+  if (!isfinite(gamma)) return fail(MOE_ERR_INVALID_ARG, "gamma must be finite");
+  MOE_TRY(check_dev(counts, "counts", true));
+  MOE_TRY(check_dev(select_bias, "select_bias", true));
+  MOE_TRY(hip_ok(moe::launch_update_bias(cfg->E, counts, gamma, select_bias, stream),
+                 "update bias kernel"));
   return ok();
 }
 

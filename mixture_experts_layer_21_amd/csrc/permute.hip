@@ -190,7 +190,35 @@ __global__ __launch_bounds__(64) void scatter_kernel(ScatterParams p) {
   }
 }
 
+// Auxiliary-loss-free balancer step ("DeepSeek-MoE and the fine-grained +
+// shared-expert idea" and "Exercises" 6 on the book page; NeMo
+// Gate.update_bias): bias[e] moves by +gamma when expert e is below the mean
+// load and by -gamma when above; the comparison is exact on integers
+// (E * counts[e] against the total).
+__global__ __launch_bounds__(256) void update_bias_kernel(int E, const int32_t* counts,
+                                                          float gamma, float* bias) {
+  __shared__ int s_i[4];
+  long long total = 0;
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int e = e0 + threadIdx.x;
+    int tot;
+    block_scan_incl(e < E ? counts[e] : 0, s_i, tot);
+    total += tot;
+  }
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const long long d = total - (long long)E * counts[e];
+    const float step = d > 0 ? 1.f : (d < 0 ? -1.f : 0.f);
+    bias[e] = bias[e] + gamma * step;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_update_bias(int E, const int32_t* counts, float gamma, float* bias,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(update_bias_kernel, dim3(1), dim3(256), 0, s, E, counts, gamma, bias);
+  return hipGetLastError();
+}
 
 hipError_t launch_hist(int T, int E, int k, const int32_t* ids, int32_t* hist, hipStream_t s) {
   hipLaunchKernelGGL(hist_kernel, dim3(route_blocks(T)), dim3(256), 0, s, T, E, k, ids, hist);

@@ -167,3 +167,48 @@ def test_shared_gate_needs_shared_expert(moe):
         moe.moe_forward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
                         shared_expert_gate=torch.zeros(w.D, dtype=torch.bfloat16,
                                                        device="cuda"))
+
+
+def test_residual_add(moe):
+    """out = x + MoE(x) when the residual is x itself, and in place into x."""
+    w = W.SMALL["deepseek_small"]
+    inp = W.make_inputs(w, "cpu", seed=17)
+    d = _to_dev(inp)
+    cfg = P.config_of(w)
+    out, ids, gw, _, _ = _forward(moe, w, cfg, d, residual=d["x"])
+    oi = P.oracle_inputs(inp)
+    routing = {"ids": ids.cpu().numpy().astype(np.int64),
+               "weights": gw.cpu().numpy().astype(np.float64)}
+    f = P.oracle_forward(w, oi, routing=routing, residual=oi["x"])
+    P.compare_rows(out, f["out"], w.act_dtype, "residual forward")
+    # combine in place: residual and out the same buffer
+    base = P.oracle_forward(w, oi, routing=routing)
+    y = torch.zeros(moe.max_rows(cfg), w.D, dtype=torch.bfloat16, device="cuda")
+    r = moe.moe_permute(cfg, ids, 0)
+    moe.moe_grouped_swiglu(cfg, d["x"], d["w_gate"], d["w_up"], d["w_down"],
+                           row_to_assign=r["row_to_assign"], expert_offsets=r["expert_offsets"],
+                           gate_w=gw, y_rows=y)
+    sy = moe.moe_grouped_swiglu(cfg, d["x"], d["ws_gate"], d["ws_up"], d["ws_down"])
+    acc = d["x"].clone()
+    moe.moe_combine(cfg, y, r["assign_to_row"], sy, out=acc, residual=acc)
+    P.compare_rows(acc, base["out"] + oi["x"], w.act_dtype, "in-place residual combine")
+
+
+@pytest.mark.parametrize("E,gamma", [(8, 0.01), (64, 0.125), (256, 1e-3)])
+def test_update_bias(moe, E, gamma):
+    """One balancer step on the device equals the oracle's (one fp32 rounding
+    of bias + gamma * sign), including experts exactly at the mean."""
+    w = W.SMALL["deepseek_small"].with_(E=E, n_groups=1, topk_groups=1)
+    cfg = P.config_of(w)
+    g = np.random.default_rng(E)
+    counts = g.integers(0, 50, size=E).astype(np.int32)
+    counts[: E // 4] = int(round(counts.mean()))  # some at (or near) the mean
+    bias = (g.normal(size=E) * 0.1).astype(np.float32)
+    dev_bias = torch.from_numpy(bias).cuda()
+    moe.moe_update_bias(cfg, torch.from_numpy(counts).cuda(), gamma, dev_bias)
+    torch.cuda.synchronize()
+    ref = P.oracle.update_bias(bias.astype(np.float64), counts, np.float32(gamma))
+    got = dev_bias.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -23 * np.maximum(np.abs(ref), 1e-30) + 1e-12)
+    step = np.sign(counts.sum() - E * counts.astype(np.int64))
+    assert (np.sign(got - bias.astype(np.float64)) == step).all()
