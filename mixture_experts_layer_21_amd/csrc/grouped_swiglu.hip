@@ -95,13 +95,135 @@ __device__ bool find_tile(const GemmParams& p, int max_mtiles, Tile& t, int* s_s
   return true;
 }
 
+// Column tiles per rasterisation band of the large-tile kernel.
+#ifndef MOE_BAND
+#define MOE_BAND 4
+#endif
+
+// Tile decode shared by the grouped GEMM kernels (blockDim >= 256; every
+// thread must call it, it contains barriers).  The active tiles (row tiles of
+// every expert x column tiles) are dealt to the XCDs in contiguous runs;
+// block b runs on XCD b%8 as that XCD's (b/8)-th block.  Each XCD runs its
+// whole rounds of tail_slots tiles at full depth; the r tiles left over are
+// each cut along K (64-deep k-steps) into nsplit pieces, so the last round is
+// short.  Pieces write fp32 partial tiles that a reduce kernel adds in piece
+// order.  Returns false when the block has no work.
+template <int BM, int BN, bool GATEUP>
+__device__ bool decode_job(const GemmParams& p, int tail_slots, int* s_scan, Tile& tile,
+                           int& piece, int& nsplit, int& tail_slot) {
+  piece = -1;
+  nsplit = 1;
+  tail_slot = 0;
+  int tail_tile = 0;
+  {
+    const int tid = threadIdx.x;
+    const int ntiles = ((GATEUP ? p.hidden : p.D) + BN - 1) / BN;
+    const int nk = (GATEUP ? p.D : p.hidden) / 64;
+    int total, cnt = 0;
+    if (p.expert_offsets == nullptr) {
+      total = (p.T + BM - 1) / BM;
+    } else {
+      // Inclusive scan of the per-expert row-tile counts; the first 256
+      // threads scan, all threads take part in the barriers.
+      if (tid < p.n_groups) {
+        const int rows = p.expert_offsets[tid + 1] - p.expert_offsets[tid];
+        cnt = (rows + BM - 1) / BM;
+      }
+      if (tid < NTHREADS) s_scan[tid] = cnt;
+      __syncthreads();
+      for (int d = 1; d < NTHREADS; d <<= 1) {
+        const int v = (tid < NTHREADS && tid >= d) ? s_scan[tid - d] : 0;
+        __syncthreads();
+        if (tid < NTHREADS) s_scan[tid] += v;
+        __syncthreads();
+      }
+      total = s_scan[NTHREADS - 1];
+    }
+    const int A = total * ntiles;
+    const int b = blockIdx.x, xcd = b % kXcds, i = b / kXcds;
+    const int ax = A / kXcds + (xcd < A % kXcds ? 1 : 0);
+    const int start = xcd * (A / kXcds) + min(xcd, A % kXcds);
+    int nfull = ax, r = 0;
+    if (tail_slots > 0) {
+      nfull = ax / tail_slots * tail_slots;
+      r = ax - nfull;
+      nsplit = r > 0 ? min(min(tail_slots / r, 16), nk) : 1;
+      if (nsplit < 2) {
+        nfull = ax;
+        r = 0;
+        nsplit = 1;
+      }
+      if (i == 0 && tid == 0) {
+        p.tail_meta[2 * xcd] = r;
+        p.tail_meta[2 * xcd + 1] = nsplit;
+      }
+    }
+    int L;
+    if (i < nfull) {
+      L = start + i;
+    } else if (i < nfull + r * nsplit) {
+      tail_tile = (i - nfull) / nsplit;
+      piece = (i - nfull) % nsplit;
+      tail_slot = xcd * kTailSlots + (i - nfull);
+      L = start + nfull + tail_tile;
+    } else {
+      return false;  // uniform across the block
+    }
+    // Logical tiles run in bands of GN column tiles; inside a band the GN
+    // column tiles of one row tile are consecutive.  The blocks an XCD holds
+    // at once then cover about (32/GN) row tiles x GN column tiles, so each
+    // A slice is fetched into that XCD's L2 once for GN blocks and each B
+    // slice once for the row tiles of its expert.
+    constexpr int GN = MOE_BAND;
+    const int full = ntiles / GN;
+    int ml;
+    if (L < full * total * GN) {
+      const int rr = L % (total * GN);
+      ml = rr / GN;
+      tile.nt = (L / (total * GN)) * GN + rr % GN;
+    } else {
+      const int w = ntiles - full * GN;
+      const int rr = L - full * total * GN;
+      ml = rr / w;
+      tile.nt = full * GN + rr % w;
+    }
+    if (p.expert_offsets == nullptr) {
+      tile.e = 0;
+      tile.m0 = ml * BM;
+      tile.m_end = p.T;
+    } else {
+      if (tid < p.n_groups) {
+        const int hi = s_scan[tid], lo = hi - cnt;
+        if (ml >= lo && ml < hi) {
+          s_scan[NTHREADS] = tid;
+          s_scan[NTHREADS + 1] = p.expert_offsets[tid] + (ml - lo) * BM;
+          s_scan[NTHREADS + 2] = p.expert_offsets[tid + 1];
+        }
+      }
+      __syncthreads();
+      tile.e = s_scan[NTHREADS];
+      tile.m0 = s_scan[NTHREADS + 1];
+      tile.m_end = s_scan[NTHREADS + 2];
+    }
+    if (piece == 0 && tid == 0) {
+      int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + tail_tile) * 4;
+      d[0] = tile.e;
+      d[1] = tile.m0;
+      d[2] = tile.m_end;
+      d[3] = tile.nt;
+    }
+  }
+
+  return true;
+}
+
 // XOR swizzle of the 16-byte chunk index inside a 64-element (128-byte) row:
 // any 8 consecutive rows, and the even or odd rows of any 16 consecutive
 // rows, land on distinct chunk positions.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <int BM, int BN, int WGM, bool GATEUP>
-__global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int max_mtiles) {
+__global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int tail_slots) {
   constexpr int BK = 64;
   constexpr int WGN = 4 / WGM;
   constexpr int NB = GATEUP ? 2 : 1;
@@ -118,12 +240,18 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
   __shared__ int s_scan[NTHREADS + 4];
 
   Tile tile;
-  if (!find_tile<BM>(p, max_mtiles, tile, s_scan)) return;
+  int piece, nsplit, tail_slot;
+  if (!decode_job<BM, BN, GATEUP>(p, tail_slots, s_scan, tile, piece, nsplit, tail_slot))
+    return;
 
   const int K = GATEUP ? p.D : p.hidden;
   const int N = GATEUP ? p.hidden : p.D;
   const int n0 = tile.nt * BN;
   const int tid = threadIdx.x;
+  // K range: all k-steps, or this piece's share of a split tail tile.
+  const int nk_all = K / BK;
+  const int kb = piece < 0 ? 0 : piece * nk_all / nsplit;
+  const int ke = piece < 0 ? nk_all : (piece + 1) * nk_all / nsplit;
   const uint16_t* x = static_cast<const uint16_t*>(p.x);
   const uint16_t* hb = static_cast<const uint16_t*>(p.hbuf);
 
@@ -142,7 +270,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
     } else {
       base = hb + (size_t)grow * K;
     }
-    a_src[i] = base + kc * 8;
+    a_src[i] = base + kc * 8 + (size_t)kb * BK;
     a_dst[i] = r * BK + (kc ^ swz(r)) * 8;
   }
   const uint16_t* b_src[BC];
@@ -160,7 +288,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
       n = n0 + r;
     }
     if (n >= N) n = n0;
-    b_src[i] = w + ((size_t)tile.e * N + n) * K + kc * 8;
+    b_src[i] = w + ((size_t)tile.e * N + n) * K + kc * 8 + (size_t)kb * BK;
     b_dst[i] = r * BK + (kc ^ swz(r)) * 8;
   }
 
@@ -197,7 +325,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
   MOE_GLOAD(0);
   MOE_SSTORE(0);
   __syncthreads();
-  const int nk = K / BK;
+  const int nk = ke - kb;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) MOE_GLOAD((kt + 1) * BK);
@@ -230,6 +358,23 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
 
   // Epilogue.  32x32 accumulator layout: element i of lane l is row
   // 8*(i/4) + 4*(l/32) + (i%4), column l%32.
+  if (piece >= 0) {
+    // A piece of a split tail tile: the raw fp32 sums, row-major over the
+    // tile's BM rows and NB*BN columns (gate columns, then up columns).
+    float* part = p.tail_part + (size_t)tail_slot * (kTailSlotBytes / 4);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int rl = wm * WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
+            part[rl * BROWS + nb * BN + wn * WN + ni * 32 + lr] = acc[nb][mi][ni][i];
+          }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -260,6 +405,45 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
   }
 }
 
+// Reduce of the split tail tiles of gemm_bf16_kernel: one block per (XCD,
+// tail tile) adds the row-major partials in piece order and runs the epilogue.
+template <int BM, int BN, bool GATEUP>
+__global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmParams p) {
+  constexpr int NB = GATEUP ? 2 : 1, W = NB * BN;
+  static_assert((size_t)BM * W * 4 <= kTailSlotBytes, "tail slot size");
+  const int xcd = blockIdx.x / kTailSlots, j = blockIdx.x % kTailSlots;
+  const int r = p.tail_meta[2 * xcd], ns = p.tail_meta[2 * xcd + 1];
+  if (j >= r) return;
+  const int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + j) * 4;
+  const int m0 = d[1], m_end = d[2], n0 = d[3] * BN;
+  const int N = GATEUP ? p.hidden : p.D;
+  const int rows = min(BM, m_end - m0);
+  for (int idx = threadIdx.x; idx < rows * BN; idx += NTHREADS) {
+    const int rl = idx / BN, cl = idx % BN, col = n0 + cl;
+    if (col >= N) continue;
+    float a0 = 0.f, a1 = 0.f;
+    for (int pc = 0; pc < ns; ++pc) {
+      const float* part =
+          p.tail_part + (size_t)(xcd * kTailSlots + j * ns + pc) * (kTailSlotBytes / 4);
+      const float v0 = part[rl * W + cl];
+      a0 = pc == 0 ? v0 : a0 + v0;
+      if constexpr (GATEUP) {
+        const float v1 = part[rl * W + BN + cl];
+        a1 = pc == 0 ? v1 : a1 + v1;
+      }
+    }
+    const int grow = m0 + rl;
+    if constexpr (GATEUP) {
+      static_cast<uint16_t*>(p.hbuf)[(size_t)grow * N + col] =
+          f32_to_bf16_bits(swiglu_act(a0, a1, p.swiglu_limit));
+    } else {
+      float gw = 1.f;
+      if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[grow]];
+      static_cast<uint16_t*>(p.y)[(size_t)grow * N + col] = f32_to_bf16_bits(gw * a0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Large-tile bf16 kernel: 512 threads (8 waves, two per SIMD), operands moved
 // global -> LDS by buffer_load ... lds (no register staging), an S-stage LDS
@@ -274,10 +458,6 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int m
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Column tiles per rasterisation band of the large-tile kernel.
-#ifndef MOE_BAND
-#define MOE_BAND 4
-#endif
 
 // Swizzle of 16-byte chunk c in row r for KCH chunks per row.  The LDS serves
 // a 16-byte read for 16 lanes per cycle (64 four-byte banks); these XOR
@@ -635,112 +815,10 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
   __shared__ __attribute__((aligned(1024))) uint16_t sB3[S > 3 ? BNB * BK : 8];
   __shared__ int s_scan[NTHREADS + 4];
 
-  // Tile decode.  The active tiles (row tiles of every expert x column
-  // tiles) are dealt to the XCDs in contiguous runs; block b runs on XCD b%8
-  // as that XCD's (b/8)-th block.  Each XCD runs its whole rounds of
-  // tail_slots tiles at full depth; the r tiles left over are each cut along
-  // K into nsplit pieces, so the last round is short.  Pieces write fp32
-  // partial tiles that gemm_tail_reduce_kernel adds in piece order.
   Tile tile;
-  int piece = -1, nsplit = 1, tail_slot = 0, tail_tile = 0;
-  {
-    const int tid = threadIdx.x;
-    const int ntiles = ((GATEUP ? p.hidden : p.D) + C::BN - 1) / C::BN;
-    const int nk = (GATEUP ? p.D : p.hidden) / BK;
-    int total, cnt = 0;
-    if (p.expert_offsets == nullptr) {
-      total = (p.T + BM - 1) / BM;
-    } else {
-      // Inclusive scan of the per-expert row-tile counts; the first 256
-      // threads scan, all threads take part in the barriers.
-      if (tid < p.n_groups) {
-        const int rows = p.expert_offsets[tid + 1] - p.expert_offsets[tid];
-        cnt = (rows + BM - 1) / BM;
-      }
-      if (tid < NTHREADS) s_scan[tid] = cnt;
-      __syncthreads();
-      for (int d = 1; d < NTHREADS; d <<= 1) {
-        const int v = (tid < NTHREADS && tid >= d) ? s_scan[tid - d] : 0;
-        __syncthreads();
-        if (tid < NTHREADS) s_scan[tid] += v;
-        __syncthreads();
-      }
-      total = s_scan[NTHREADS - 1];
-    }
-    const int A = total * ntiles;
-    const int b = blockIdx.x, xcd = b % kXcds, i = b / kXcds;
-    const int ax = A / kXcds + (xcd < A % kXcds ? 1 : 0);
-    const int start = xcd * (A / kXcds) + min(xcd, A % kXcds);
-    int nfull = ax, r = 0;
-    if (tail_slots > 0) {
-      nfull = ax / tail_slots * tail_slots;
-      r = ax - nfull;
-      nsplit = r > 0 ? min(min(tail_slots / r, 16), nk) : 1;
-      if (nsplit < 2) {
-        nfull = ax;
-        r = 0;
-        nsplit = 1;
-      }
-      if (i == 0 && tid == 0) {
-        p.tail_meta[2 * xcd] = r;
-        p.tail_meta[2 * xcd + 1] = nsplit;
-      }
-    }
-    int L;
-    if (i < nfull) {
-      L = start + i;
-    } else if (i < nfull + r * nsplit) {
-      tail_tile = (i - nfull) / nsplit;
-      piece = (i - nfull) % nsplit;
-      tail_slot = xcd * kTailSlots + (i - nfull);
-      L = start + nfull + tail_tile;
-    } else {
-      return;  // uniform across the block
-    }
-    // Logical tiles run in bands of GN column tiles; inside a band the GN
-    // column tiles of one row tile are consecutive.  The blocks an XCD holds
-    // at once then cover about (32/GN) row tiles x GN column tiles, so each
-    // A slice is fetched into that XCD's L2 once for GN blocks and each B
-    // slice once for the row tiles of its expert.
-    constexpr int GN = MOE_BAND;
-    const int full = ntiles / GN;
-    int ml;
-    if (L < full * total * GN) {
-      const int rr = L % (total * GN);
-      ml = rr / GN;
-      tile.nt = (L / (total * GN)) * GN + rr % GN;
-    } else {
-      const int w = ntiles - full * GN;
-      const int rr = L - full * total * GN;
-      ml = rr / w;
-      tile.nt = full * GN + rr % w;
-    }
-    if (p.expert_offsets == nullptr) {
-      tile.e = 0;
-      tile.m0 = ml * BM;
-      tile.m_end = p.T;
-    } else {
-      if (tid < p.n_groups) {
-        const int hi = s_scan[tid], lo = hi - cnt;
-        if (ml >= lo && ml < hi) {
-          s_scan[NTHREADS] = tid;
-          s_scan[NTHREADS + 1] = p.expert_offsets[tid] + (ml - lo) * BM;
-          s_scan[NTHREADS + 2] = p.expert_offsets[tid + 1];
-        }
-      }
-      __syncthreads();
-      tile.e = s_scan[NTHREADS];
-      tile.m0 = s_scan[NTHREADS + 1];
-      tile.m_end = s_scan[NTHREADS + 2];
-    }
-    if (piece == 0 && tid == 0) {
-      int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + tail_tile) * 4;
-      d[0] = tile.e;
-      d[1] = tile.m0;
-      d[2] = tile.m_end;
-      d[3] = tile.nt;
-    }
-  }
+  int piece, nsplit, tail_slot;
+  if (!decode_job<BM, C::BN, GATEUP>(p, tail_slots, s_scan, tile, piece, nsplit, tail_slot))
+    return;
 
   const int K = GATEUP ? p.D : p.hidden;
   const int N = GATEUP ? p.hidden : p.D;
@@ -934,17 +1012,6 @@ int mtiles_bound(const GemmParams& p, int bm) {
   return (p.max_rows + bm - 1) / bm + p.n_groups;
 }
 
-template <int BM, int BN, int WGM, bool GATEUP>
-hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
-  const int N = GATEUP ? p.hidden : p.D;
-  const int mt = mtiles_bound(p, BM);
-  const long long nblocks = (long long)mt * ((N + BN - 1) / BN);
-  if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, GATEUP>), dim3((unsigned)nblocks),
-                     dim3(NTHREADS), 0, s, p, mt);
-  return hipGetLastError();
-}
-
 // Resident blocks per XCD of one kernel on the current device (0 when the
 // CUs do not split evenly over the XCDs); cached per device.
 template <class Kern>
@@ -962,6 +1029,25 @@ int slots_per_xcd(Kern kern, int threads) {
     have[dev] = true;
   }
   return cache[dev];
+}
+
+template <int BM, int BN, int WGM, bool GATEUP>
+hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
+  const auto kern = gemm_bf16_kernel<BM, BN, WGM, GATEUP>;
+  const int N = GATEUP ? p.hidden : p.D;
+  const int mt = mtiles_bound(p, BM);
+  const long long tiles = (long long)mt * ((N + BN - 1) / BN);
+  if (tiles <= 0) return hipSuccess;
+  const int slots = p.tail_part ? slots_per_xcd(kern, NTHREADS) : 0;
+  // Every XCD gets at most ceil(tiles/8) tiles plus at most `slots` extra
+  // blocks for the pieces of its split tail.
+  const long long nblocks = kXcds * ((tiles + kXcds - 1) / kXcds + slots);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(NTHREADS), 0, s, p, slots);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || slots == 0) return err;
+  hipLaunchKernelGGL((gemm_tail_reduce_flat_kernel<BM, BN, GATEUP>), dim3(kXcds * kTailSlots),
+                     dim3(NTHREADS), 0, s, p);
+  return hipGetLastError();
 }
 
 template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>

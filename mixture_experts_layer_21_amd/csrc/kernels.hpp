@@ -85,7 +85,7 @@ struct GemmParams {
 
 // Split-K tail bookkeeping of the large-tile grouped GEMM.
 constexpr int kXcds = 8;
-constexpr int kTailSlots = 32;                       // partial tiles per XCD
+constexpr int kTailSlots = 64;                       // partial tiles per XCD
 constexpr size_t kTailSlotBytes = (size_t)256 * 256 * 4;  // one fp32 256x256 tile
 inline size_t tail_workspace_bytes() {
   return (size_t)kXcds * kTailSlots * kTailSlotBytes + 256 + (size_t)kXcds * kTailSlots * 16;
