@@ -411,25 +411,34 @@ template <int BM, int BN, bool GATEUP>
 __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmParams p) {
   constexpr int NB = GATEUP ? 2 : 1, W = NB * BN;
   static_assert((size_t)BM * W * 4 <= kTailSlotBytes, "tail slot size");
-  const int xcd = blockIdx.x / kTailSlots, j = blockIdx.x % kTailSlots;
+  // Block b runs on XCD b % 8, the XCD whose L2 holds the partials.
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
   const int r = p.tail_meta[2 * xcd], ns = p.tail_meta[2 * xcd + 1];
   if (j >= r) return;
   const int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + j) * 4;
   const int m0 = d[1], m_end = d[2], n0 = d[3] * BN;
   const int N = GATEUP ? p.hidden : p.D;
   const int rows = min(BM, m_end - m0);
+  const float* part0 = p.tail_part + (size_t)(xcd * kTailSlots + j * ns) * (kTailSlotBytes / 4);
   for (int idx = threadIdx.x; idx < rows * BN; idx += NTHREADS) {
     const int rl = idx / BN, cl = idx % BN, col = n0 + cl;
     if (col >= N) continue;
-    float a0 = 0.f, a1 = 0.f;
-    for (int pc = 0; pc < ns; ++pc) {
-      const float* part =
-          p.tail_part + (size_t)(xcd * kTailSlots + j * ns + pc) * (kTailSlotBytes / 4);
-      const float v0 = part[rl * W + cl];
-      a0 = pc == 0 ? v0 : a0 + v0;
-      if constexpr (GATEUP) {
-        const float v1 = part[rl * W + BN + cl];
-        a1 = pc == 0 ? v1 : a1 + v1;
+    // All pieces' values are loaded before the fixed-order sum (ns <= 16).
+    float v0[16], v1[16];
+#pragma unroll
+    for (int pc = 0; pc < 16; ++pc) {
+      if (pc < ns) {
+        const float* part = part0 + (size_t)pc * (kTailSlotBytes / 4);
+        v0[pc] = part[rl * W + cl];
+        if constexpr (GATEUP) v1[pc] = part[rl * W + BN + cl];
+      }
+    }
+    float a0 = v0[0], a1 = GATEUP ? v1[0] : 0.f;
+#pragma unroll
+    for (int pc = 1; pc < 16; ++pc) {
+      if (pc < ns) {
+        a0 += v0[pc];
+        if constexpr (GATEUP) a1 += v1[pc];
       }
     }
     const int grow = m0 + rl;
@@ -766,9 +775,10 @@ template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
 __global__ __launch_bounds__(64 * (NWV / WGM)) void gemm_tail_reduce_kernel(GemmParams p) {
   using C = DmaCfg<BM, BNB, BK, S, WGM, NWV, GATEUP>;
   constexpr int PER_TILE = WGM * C::MI;
-  const int tile_id = blockIdx.x / PER_TILE, sub = blockIdx.x % PER_TILE;
+  // Block b runs on XCD b % 8, the XCD whose L2 holds the partials.
+  const int xcd = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
+  const int j = rest / PER_TILE, sub = rest % PER_TILE;
   const int wm = sub / C::MI, mi = sub % C::MI;
-  const int xcd = tile_id / kTailSlots, j = tile_id % kTailSlots;
   const int r = p.tail_meta[2 * xcd], ns = p.tail_meta[2 * xcd + 1];
   if (j >= r) return;
   const int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + j) * 4;
