@@ -144,6 +144,15 @@ def _pmc_summary(fetch_db, write_db, workload):
              f"WRITE_SIZE {w_cal:.6g} -> {w_scale:.4f} B per unit.  The calibration kernel "
              f"itself moves 2 GiB in {fetch[calib[0]]['_dur'] / 1e3:.1f} us "
              f"({2 * CALIB_BYTES / fetch[calib[0]]['_dur']:.0f} GB/s).", "",
+             "Commands (one MI355X; the counter passes, then this summary):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp",
+             *(f"rocprofv3 --kernel-include-regex 'moe::|neg_kernel' --pmc {c} -d /tmp/t_{c} "
+               f"-o {workload} -- python3 /root/repo/bench.py --workload {workload} --steps 2 "
+               f"--warmup 1 --no-cpu-baseline --copy-calibration"
+               for c in ("FETCH_SIZE", "WRITE_SIZE")),
+             f"python3 /root/repo/bench.py --pmc-summary /tmp/t_FETCH_SIZE/{workload}_results.db "
+             f"/tmp/t_WRITE_SIZE/{workload}_results.db --workload {workload}",
+             "```", "",
              "| kernel | dispatches | avg duration (us) | read (MB) | written (MB) | GB/s |",
              "|---|---:|---:|---:|---:|---:|"]
     step = 0.0
