@@ -16,6 +16,8 @@ Sources (the pages this follows; section names as printed on each page):
          "The auxiliary load-balancing loss", "Capacity Factor, Token Dropping,
          and the Worked Numbers", "DeepSeek-MoE and the fine-grained +
          shared-expert idea", "Sparse upcycling", "Exercises".
+  [ST]   "st-moe-pytorch" API reference, "rms-norm" (RMSNorm before the MoE
+         inside ``SparseMoEBlock``; the prenormalisation pattern).
   [NEMO] "nemo_automodel.components.moe.layers" (NeMo AutoModel v0.4 API):
          class ``Gate`` attributes ``score_func``, ``n_groups``, ``topk_groups``,
          ``norm_topk_prob``, ``route_scale``; class ``MLP`` (SwiGLU, no bias).
@@ -52,7 +54,12 @@ Readings taken where the pages are silent or garbled (all listed in the design doc):
     0 means no clamp.  PARITY UNPINNED: the pages name the clamp, not its form;
   * a shared-expert gate ([NEMO] ``MoE.shared_expert_gate``): the shared
     output is scaled per token by sigmoid(x . w_sg).  PARITY UNPINNED: the
-    pages name the gate, not its form.
+    pages name the gate, not its form;
+  * the pre-norm ([LAB] "Put the MoE into a decoder block", where the MoE
+    branch takes the RMS-normalised residual stream; [ST] the RMSNorm of
+    ``SparseMoEBlock``): y = x * w / sqrt(mean(x^2) + eps) per token, computed
+    in float64 and rounded once to the activation dtype (bfloat16: nearest,
+    ties to even), because the layer receives a tensor of that dtype.
 """
 from __future__ import annotations
 
@@ -64,6 +71,7 @@ __all__ = [
     "NEAR_TIE", "router_logits", "softmax", "sigmoid", "softplus", "logsumexp",
     "route", "capacity", "first_within_capacity", "permutation",
     "swiglu_ffn", "expert_outputs", "shared_expert", "combine", "forward", "update_bias",
+    "round_to_bf16", "rms_norm",
     "brute_force_forward", "all_experts_then_mask",
 ]
 
@@ -361,18 +369,24 @@ def shared_expert(x, inputs, limit=0.0):
 
 def forward(inputs, *, top_k, score="softmax", renormalize=True, route_scale=1.0,
             n_groups=1, topk_groups=1, group_rule="top2sum", capacity_factor=None,
-            tokens=None, routing=None, token_mask=None, swiglu_limit=0.0, residual=None):
+            tokens=None, routing=None, token_mask=None, swiglu_limit=0.0, residual=None,
+            pre_norm=None):
     """The whole layer forward on float64 arrays.
 
     ``inputs`` holds x [T,D], w_router [E,D], w_gate/w_up [E,H,D], w_down
     [E,D,H], optional ws_gate/ws_up [Hs,D], ws_down [D,Hs], ws_sgate [D],
     logit_bias [E], select_bias [E].  ``token_mask`` [T] (True = valid) and
-    ``swiglu_limit`` are the [NEMO] switches read in the module docstring.  ``tokens`` limits the expert/combine work to a subset of
+    ``swiglu_limit`` are the [NEMO] switches read in the module docstring.
+    ``pre_norm`` = (weight or None, eps, act) runs ``rms_norm`` on x first;
+    router, experts and shared expert then all take the normalised rows, and
+    the residual (if any) is added as given.  ``tokens`` limits the expert/combine work to a subset of
     tokens (routing and capacity are always computed for all tokens, because
     drops depend on every earlier token).  ``routing`` may supply precomputed
     ``ids``/``weights`` (e.g. those of the device, to compare the downstream
     steps on identical routes)."""
     x = inputs["x"]
+    if pre_norm is not None:
+        x = rms_norm(x, pre_norm[0], pre_norm[1], pre_norm[2])
     T, D = x.shape
     E = inputs["w_router"].shape[0]
     r = route(x, inputs["w_router"], top_k, score=score, renormalize=renormalize,
@@ -395,8 +409,42 @@ def forward(inputs, *, top_k, score="softmax", renormalize=True, route_scale=1.0
     return {
         "out": out, "tokens": tok, "route": r, "capacity": cap, "keep": keep,
         "expert_offsets": offsets, "row_to_assign": row_to_assign,
-        "assign_to_row": assign_to_row, "n_kept": int(keep.sum()),
+        "assign_to_row": assign_to_row, "n_kept": int(keep.sum()), "x_in": x,
     }
+
+
+# -------------------------------------------------------------- pre-norm ---
+
+def round_to_bf16(v):
+    """Nearest bfloat16 value of each float64 in ``v`` (ties to even), as
+    float64.  bfloat16 is the upper 16 bits of an IEEE single: 8 significant
+    bits and the single's exponent range.  The rounding is taken once, on the
+    float64 bit pattern (52 fraction bits, of which the lowest 45 go), so no
+    intermediate float32 rounding can shift a tie.  Finite, normal inputs."""
+    v = np.asarray(v, dtype=np.float64)
+    bits = v.view(np.uint64).copy()
+    drop = np.uint64(45)
+    keep_lsb = (bits >> drop) & np.uint64(1)
+    bits = bits + (np.uint64((1 << 44) - 1) + keep_lsb)
+    bits = bits & ~np.uint64((1 << 45) - 1)
+    return bits.view(np.float64)
+
+
+def rms_norm(x, weight=None, eps=1e-6, act="bf16"):
+    """RMSNorm of every token row: y = x * w / sqrt(mean_d x_d^2 + eps)
+    ([LAB] "Put the MoE into a decoder block"; [ST] "rms-norm"), w = 1 when
+    ``weight`` is None.  float64, then one rounding to the activation dtype
+    ``act`` ('bf16', 'f32', or None for no rounding)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    y = x / np.sqrt(ms + eps)
+    if weight is not None:
+        y = y * np.asarray(weight, dtype=np.float64)[None, :]
+    if act == "bf16":
+        return round_to_bf16(y)
+    if act == "f32":
+        return y.astype(np.float32).astype(np.float64)
+    return y
 
 
 # ------------------------------------------------ bias-adjustment balancer ---

@@ -577,4 +577,72 @@ def pin_residual_is_added(o):
     assert np.allclose(b, a + res, rtol=0, atol=1e-15)
 
 
+def pin_bf16_rounding_ties_and_library(o):
+    """Rounding to bfloat16 (8 significant bits): exact ties go to the even
+    neighbour, anything past a tie goes up, and float32 inputs (exact in
+    float64) round as torch's own float32 -> bfloat16 conversion does."""
+    u = 2.0 ** -7                                 # bf16 spacing in [1, 2)
+    cases = {1.0: 1.0, 1.0 + u: 1.0 + u, 1.0 + u / 2: 1.0, 1.0 + 3 * u / 2: 1.0 + 2 * u,
+             1.0 + u / 2 + 2.0 ** -40: 1.0 + u, 1.0 + u / 2 - 2.0 ** -40: 1.0,
+             -(1.0 + 3 * u / 2): -(1.0 + 2 * u), 2.0 - 3 * u / 4: 2.0 - u, 2.0 - u / 4: 2.0,
+             2.0 - u / 2: 2.0,
+             3.0 * 2.0 ** -20: 3.0 * 2.0 ** -20}
+    got = o.round_to_bf16(np.array(list(cases)))
+    assert np.array_equal(got, np.array(list(cases.values()))), got
+    import torch
+    v32 = (_rng(41).normal(size=4000) * np.exp(_rng(42).uniform(-8, 8, 4000))).astype(np.float32)
+    lib = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(o.round_to_bf16(v32.astype(np.float64)), lib)
+
+
+def pin_rms_norm_loops_and_library(o):
+    """RMSNorm against a pure-Python loop on a tiny matrix and against
+    torch.nn.functional.rms_norm in float64; unit mean square with w = 1 and
+    eps = 0; a constant row c gives w * c / sqrt(c^2 + eps)."""
+    r = _rng(43)
+    x = r.normal(size=(4, 7)) * 3.0
+    w = r.uniform(0.5, 2.0, size=7)
+    eps = 0.25
+    got = o.rms_norm(x, w, eps, act=None)
+    for t in range(4):
+        ms = sum(v * v for v in x[t]) / 7
+        for d in range(7):
+            assert abs(got[t, d] - x[t, d] / math.sqrt(ms + eps) * w[d]) < 1e-14
+    import torch
+    lib = torch.nn.functional.rms_norm(torch.from_numpy(x), (7,), torch.from_numpy(w), eps)
+    assert np.allclose(got, lib.numpy(), rtol=1e-14, atol=0)
+    y = o.rms_norm(x, None, 0.0, act=None)
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-14)
+    c = np.full((1, 5), -0.5)
+    assert np.allclose(o.rms_norm(c, w[:5], 0.75, act=None), w[:5] * -0.5 / 1.0, rtol=1e-15)
+
+
+def pin_rms_norm_rounds_once(o):
+    """The normalised rows are the float64 values rounded once to the
+    activation dtype."""
+    x = _rng(44).normal(size=(6, 33))
+    exact = o.rms_norm(x, None, 1e-6, act=None)
+    assert np.array_equal(o.rms_norm(x, None, 1e-6, act="bf16"), o.round_to_bf16(exact))
+    assert np.array_equal(o.rms_norm(x, None, 1e-6, act="f32"),
+                          exact.astype(np.float32).astype(np.float64))
+
+
+def pin_pre_norm_layer_is_scale_free(o):
+    """With eps = 0 the pre-normed layer cannot see the scale of its input:
+    x and 4x (a power of two, so every rounding is the same) give the same
+    routes and outputs; the router and experts take the normalised rows."""
+    inp = _tiny_inputs(45, T=10, E=4, shared=True)
+    w = _rng(46).uniform(0.5, 1.5, size=inp["x"].shape[1])
+    a = o.forward(inp, top_k=2, pre_norm=(w, 0.0, "bf16"))
+    big = dict(inp, x=inp["x"] * 4.0)
+    b = o.forward(big, top_k=2, pre_norm=(w, 0.0, "bf16"))
+    assert np.array_equal(a["route"]["ids"], b["route"]["ids"])
+    assert np.allclose(a["out"], b["out"], rtol=0, atol=1e-14)
+    normed = dict(inp, x=o.rms_norm(inp["x"], w, 0.0, "bf16"))
+    c = o.forward(normed, top_k=2)
+    assert np.allclose(a["out"], c["out"], rtol=0, atol=1e-14)
+    raw = o.forward(inp, top_k=2)
+    assert not np.allclose(a["out"], raw["out"], rtol=0, atol=1e-6)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

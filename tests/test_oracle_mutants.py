@@ -104,6 +104,30 @@ MUTANTS = [
     ("residual_dropped",
      "        out = out + np.asarray(residual, dtype=np.float64)",
      "        out = out + 0.0"),
+    ("rms_eps_dropped",
+     "y = x / np.sqrt(ms + eps)",
+     "y = x / np.sqrt(ms)"),
+    ("rms_sum_not_mean",
+     "ms = np.mean(x * x, axis=1, keepdims=True)",
+     "ms = np.sum(x * x, axis=1, keepdims=True)"),
+    ("rms_over_tokens",
+     "ms = np.mean(x * x, axis=1, keepdims=True)",
+     "ms = np.mean(x * x, axis=0, keepdims=True)"),
+    ("rms_weight_not_applied",
+     "y = y * np.asarray(weight, dtype=np.float64)[None, :]",
+     "y = y * 1.0"),
+    ("bf16_ties_away",
+     "bits = bits + (np.uint64((1 << 44) - 1) + keep_lsb)",
+     "bits = bits + np.uint64(1 << 44)"),
+    ("bf16_truncates",
+     "bits = bits + (np.uint64((1 << 44) - 1) + keep_lsb)",
+     "bits = bits + np.uint64(0)"),
+    ("bf16_keeps_a_bit_too_many",
+     "drop = np.uint64(45)",
+     "drop = np.uint64(44)"),
+    ("pre_norm_ignored",
+     "        x = rms_norm(x, pre_norm[0], pre_norm[1], pre_norm[2])",
+     "        x = x"),
     ("router_bias_ignored",
      "h = h + np.asarray(logit_bias, dtype=np.float64)[None, :]",
      "h = h + 0.0"),
