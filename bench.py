@@ -325,6 +325,22 @@ def main():
     fwd_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     _log(f"[bench] moe_forward: {fwd_ms:.3f} ms/step")
 
+    # A step beside the layer, timed on its own (not part of the step above):
+    # the RMSNorm pre-norm of the residual stream.  Algorithmic bytes: x read
+    # once, the normalised rows written once, the weight vector.
+    xn = torch.empty_like(inp["x"])
+    nw = torch.ones(w.D, dtype=torch.float32, device=dev)
+    moe.moe_rmsnorm(cfg, inp["x"], nw, out=xn)
+    rev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    rev[0].record(stream)
+    for _ in range(args.steps):
+        moe.moe_rmsnorm(cfg, inp["x"], nw, out=xn)
+    rev[1].record(stream)
+    torch.cuda.synchronize()
+    rms_ms = rev[0].elapsed_time(rev[1]) / args.steps
+    esz_x = 2 if w.act_dtype == "bf16" else 4
+    rms_bytes = 2.0 * w.T * w.D * esz_x + 4.0 * w.D
+
     # Algorithmic work of the grouped SwiGLU step: 2*D*H FLOP for each of the
     # gate, up and down products per kept row (plus the shared expert on T
     # rows); algorithmic bytes: the three weight matrices of every expert that
@@ -368,6 +384,8 @@ def main():
         "stages_ms": {k: round(float(v), 4) for k, v in
                       zip(("route", "permute", "grouped_swiglu", "combine"), stage_ms)},
         "roofline": roofline,
+        "beside_the_step": {"rmsnorm_ms": round(rms_ms, 4),
+                            "rmsnorm_gbs": round(rms_bytes / (rms_ms * 1e-3) / 1e9, 1)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(w, inp, args.cpu_seconds)

@@ -86,6 +86,10 @@ typedef struct moe_config {
   double capacity_factor; /* <= 0: dropless; else C = max(1, ceil(cf*T*k/E))   */
   float swiglu_limit;   /* > 0: gate and up projections clamped to [-L, L]
                            before silu(g)*u (NeMo MLP swiglu_limit); 0 = off   */
+  int32_t pre_norm;     /* 1: moe_forward RMS-normalises x first (moe_rmsnorm)
+                           and the whole layer takes the normalised rows; the
+                           workspace then also holds them.  0 = off           */
+  float norm_eps;       /* eps of moe_rmsnorm, finite and >= 0                */
 } moe_config;
 
 /* Human-readable name of a status code (static storage). */
@@ -202,15 +206,35 @@ moe_status moe_combine(const moe_config* cfg, const void* y_rows,
                        const void* x, const void* shared_expert_gate,
                        const void* residual, void* out, hipStream_t stream);
 
+/* RMSNorm of the residual stream ahead of the layer ("Lab: build a tiny MoE
+ * in PyTorch", "Put the MoE into a decoder block": the MoE branch of the
+ * block takes the RMS-normalised stream; st-moe-pytorch "rms-norm": RMSNorm
+ * ahead of the MoE inside SparseMoEBlock):
+ *   x_norm[t, d] = x[t, d] / sqrt(mean_d' x[t, d']^2 + cfg->norm_eps) * w[d]
+ *   x            [T, D] act_dtype
+ *   norm_weight  [D] f32, or NULL for w = 1
+ *   x_norm       [T, D] act_dtype out; may be x itself (in place)
+ * The mean square and the formula are evaluated in fp64 and each output is
+ * rounded once to act_dtype (bf16: nearest, ties to even), so the result is
+ * the correctly rounded value of the formula up to fp64 summation order.
+ * Deterministic.  A row of zeros with eps = 0 gives NaN (0/0). */
+moe_status moe_rmsnorm(const moe_config* cfg, const void* x, const float* norm_weight,
+                       void* x_norm, hipStream_t stream);
+
 /* The whole forward: moe_route, moe_permute, moe_grouped_swiglu (routed and
  * shared expert) and moe_combine, stream-ordered, with no host
- * synchronisation.  w_shared_* may be NULL when cfg->H_shared == 0;
+ * synchronisation.  With cfg->pre_norm the forward first runs moe_rmsnorm on
+ * x with norm_weight (NULL: w = 1) into the workspace, and router, experts
+ * and shared-expert gate take those rows; x itself is not changed (pass it
+ * as residual for the block's out = x + MoE(RMSNorm(x))); norm_weight must
+ * be NULL without pre_norm.  w_shared_* may be NULL when cfg->H_shared == 0;
  * shared_expert_gate [D] (optional, needs a shared expert) scales its output
  * per token as in moe_combine; token_mask as in moe_route; residual [T, D]
  * (optional) is added to the output as in moe_combine.  The optional
  * outputs expert_ids [T,k], gate_w [T,k], counts [E] and aux [2] receive the
  * routing results when non-NULL. */
-moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_weight,
+                       const void* w_router,
                        const float* logit_bias, const float* select_bias,
                        const uint8_t* token_mask, const void* w_gate, const void* w_up,
                        const void* w_down, const void* w_shared_gate,

@@ -52,6 +52,7 @@ class MoeConfig(ctypes.Structure):
         ("route_scale", ctypes.c_float), ("n_groups", ctypes.c_int32),
         ("topk_groups", ctypes.c_int32), ("group_rule", ctypes.c_int32),
         ("capacity_factor", ctypes.c_double), ("swiglu_limit", ctypes.c_float),
+        ("pre_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float),
     ]
 
     @property
@@ -66,14 +67,15 @@ class MoeConfig(ctypes.Structure):
 def make_config(T, D, H, E, top_k, *, H_shared=0, act_dtype="bf16", router_dtype="bf16",
                 score="softmax", renormalize=True, route_scale=1.0, n_groups=1,
                 topk_groups=1, group_rule="top2sum", capacity_factor=None,
-                swiglu_limit=0.0) -> MoeConfig:
+                swiglu_limit=0.0, pre_norm=False, norm_eps=1e-6) -> MoeConfig:
     return MoeConfig(T=T, D=D, H=H, E=E, top_k=top_k, H_shared=H_shared,
                      act_dtype=DTYPES[act_dtype], router_dtype=DTYPES[router_dtype],
                      score_func=SCORES[score], renormalize=int(bool(renormalize)),
                      route_scale=route_scale, n_groups=n_groups, topk_groups=topk_groups,
                      group_rule=GROUP_RULES[group_rule],
                      capacity_factor=0.0 if capacity_factor is None else capacity_factor,
-                     swiglu_limit=float(swiglu_limit))
+                     swiglu_limit=float(swiglu_limit), pre_norm=int(bool(pre_norm)),
+                     norm_eps=float(norm_eps))
 
 
 _P = ctypes.c_void_p
@@ -93,7 +95,8 @@ _sigs = {
                                           _P, _P, _P, _SZ, _P]),
     "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                   _P, _P, _P, _P, _P, _P, _SZ, _P]),
+                                   _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_rmsnorm": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
     "moe_update_bias": (ctypes.c_int, [_CFG, _P, ctypes.c_float, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
@@ -315,8 +318,9 @@ def moe_combine(cfg, y_rows, assign_to_row, shared_rows=None, out=None, validate
 def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, select_bias=None,
                 ws_gate=None, ws_up=None, ws_down=None, out=None, expert_ids=None, gate_w=None,
                 counts=None, aux=None, workspace=None, token_mask=None,
-                shared_expert_gate=None, residual=None):
-    """The whole layer forward (see ``moe_forward``)."""
+                shared_expert_gate=None, residual=None, norm_weight=None):
+    """The whole layer forward (see ``moe_forward``); with ``cfg.pre_norm``
+    the layer takes RMSNorm(x) (``norm_weight`` [D] f32 or None)."""
     check_config(cfg)
     T, D, H, E, k, Hs = cfg.T, cfg.D, cfg.H, cfg.E, cfg.top_k, cfg.H_shared
     dt = cfg.act_torch_dtype
@@ -333,6 +337,7 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, sele
         _expect(ws_down, "ws_down", (D, Hs), dt)
     _expect(shared_expert_gate, "shared_expert_gate", (D,), dt, required=False)
     _expect(residual, "residual", (T, D), dt, required=False)
+    _expect(norm_weight, "norm_weight", (D,), torch.float32, required=False)
     token_mask = _mask(token_mask, T)
     out = torch.empty(T, D, dtype=dt, device=x.device) if out is None else out
     _expect(out, "out", (T, D), dt)
@@ -341,12 +346,27 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, sele
     _expect(counts, "counts", (E,), torch.int32, required=False)
     _expect(aux, "aux", (2,), torch.float32, required=False)
     ws = new_workspace(cfg, x.device) if workspace is None else workspace
-    _check(_lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logit_bias),
+    _check(_lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(norm_weight), _ptr(w_router),
+                            _ptr(logit_bias),
                             _ptr(select_bias), _ptr(token_mask), _ptr(w_gate), _ptr(w_up),
                             _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
                             _ptr(shared_expert_gate), _ptr(residual), _ptr(out),
                             _ptr(expert_ids), _ptr(gate_w), _ptr(counts), _ptr(aux), _ptr(ws),
                             ws.numel(), _stream()), "moe_forward")
+    return out
+
+
+def moe_rmsnorm(cfg, x, norm_weight=None, out=None):
+    """RMSNorm of x [T, D] (see ``moe_rmsnorm``): x / sqrt(mean(x^2) +
+    cfg.norm_eps) * norm_weight, in act dtype; ``out`` may be ``x``."""
+    check_config(cfg)
+    dt = cfg.act_torch_dtype
+    _expect(x, "x", (cfg.T, cfg.D), dt)
+    _expect(norm_weight, "norm_weight", (cfg.D,), torch.float32, required=False)
+    out = torch.empty_like(x) if out is None else out
+    _expect(out, "out", (cfg.T, cfg.D), dt)
+    _check(_lib.moe_rmsnorm(ctypes.byref(cfg), _ptr(x), _ptr(norm_weight), _ptr(out),
+                            _stream()), "moe_rmsnorm")
     return out
 
 

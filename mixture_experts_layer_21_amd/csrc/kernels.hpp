@@ -110,6 +110,8 @@ hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
 hipError_t launch_update_bias(int E, const int32_t* counts, float gamma, float* bias,
                               hipStream_t s);
+hipError_t launch_rmsnorm(int T, int D, bool bf16, const void* x, const float* w, float eps,
+                          void* y, hipStream_t s);
 
 inline int route_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
 

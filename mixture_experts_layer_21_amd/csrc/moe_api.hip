@@ -57,6 +57,10 @@ moe_status check_config(const moe_config* c) {
     return fail(MOE_ERR_INVALID_ARG, "unknown score function %d", c->score_func);
   if (!(isfinite(c->swiglu_limit) && c->swiglu_limit >= 0.f))
     return fail(MOE_ERR_INVALID_ARG, "swiglu_limit must be finite and >= 0 (0 = off)");
+  if (c->pre_norm != 0 && c->pre_norm != 1)
+    return fail(MOE_ERR_INVALID_ARG, "pre_norm must be 0 or 1");
+  if (!(isfinite(c->norm_eps) && c->norm_eps >= 0.f))
+    return fail(MOE_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
   if (c->renormalize != 0 && c->renormalize != 1)
     return fail(MOE_ERR_INVALID_ARG, "renormalize must be 0 or 1");
   if (!(isfinite(c->route_scale) && c->route_scale > 0.f))
@@ -109,7 +113,7 @@ long long max_rows_of(const moe_config* c) {
 struct Layout {
   size_t ids, gate_w, counts, aux, logits, hist, pe_part, z_part, valid_part, block_base,
       counts_ws, pe_ws,
-      offsets, n_kept, r2a, a2r, hbuf, y, shared_y, tail, total;
+      offsets, n_kept, r2a, a2r, hbuf, y, shared_y, tail, x_norm, total;
 };
 
 Layout layout_of(const moe_config* c) {
@@ -145,6 +149,7 @@ Layout layout_of(const moe_config* c) {
   L.y = take(rows * D * es);
   L.shared_y = take(c->H_shared ? T * D * es : 0);
   L.tail = take(c->act_dtype == MOE_BF16 ? moe::tail_workspace_bytes() : 0);
+  L.x_norm = take(c->pre_norm ? T * D * es : 0);
   L.total = off;
   return L;
 }
@@ -456,7 +461,21 @@ moe_status moe_combine(const moe_config* cfg, const void* y_rows, const int32_t*
   return ok();
 }
 
-moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+moe_status moe_rmsnorm(const moe_config* cfg, const void* x, const float* norm_weight,
+                       void* x_norm, hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  if (!x || !x_norm) return fail(MOE_ERR_NULL_PTR, "moe_rmsnorm: x and x_norm are required");
+  MOE_TRY(check_dev(x, "x", true));
+  MOE_TRY(check_dev(norm_weight, "norm_weight", false));
+  MOE_TRY(check_dev(x_norm, "x_norm", true));
+  MOE_TRY(hip_ok(moe::launch_rmsnorm(cfg->T, cfg->D, cfg->act_dtype == MOE_BF16, x, norm_weight,
+                                     cfg->norm_eps, x_norm, stream),
+                 "rmsnorm kernel"));
+  return ok();
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_weight,
+                       const void* w_router,
                        const float* logit_bias, const float* select_bias,
                        const uint8_t* token_mask, const void* w_gate, const void* w_up,
                        const void* w_down, const void* w_shared_gate, const void* w_shared_up,
@@ -471,8 +490,11 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     return fail(MOE_ERR_NULL_PTR, "moe_forward: H_shared > 0 needs the shared-expert weights");
   if (shared_expert_gate && cfg->H_shared == 0)
     return fail(MOE_ERR_INVALID_ARG, "moe_forward: shared_expert_gate needs a shared expert");
+  if (norm_weight && !cfg->pre_norm)
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward: norm_weight needs cfg->pre_norm = 1");
   MOE_TRY(check_ws(cfg, workspace, workspace_bytes));
   MOE_TRY(check_dev(x, "x", true));
+  MOE_TRY(check_dev(norm_weight, "norm_weight", false));
   MOE_TRY(check_dev(w_router, "w_router", true));
   MOE_TRY(check_dev(logit_bias, "logit_bias", false));
   MOE_TRY(check_dev(select_bias, "select_bias", false));
@@ -506,6 +528,13 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   const bool dropless = !(cfg->capacity_factor > 0.0);
   const int rows = (int)max_rows_of(cfg);
 
+  if (cfg->pre_norm) {  // the layer takes the normalised rows from here on
+    void* xn = at<void>(workspace, L.x_norm);
+    MOE_TRY(hip_ok(moe::launch_rmsnorm(cfg->T, cfg->D, cfg->act_dtype == MOE_BF16, x,
+                                       norm_weight, cfg->norm_eps, xn, stream),
+                   "rmsnorm kernel"));
+    x = xn;
+  }
   const moe::RouteParams rp =
       route_params(cfg, x, w_router, logit_bias, select_bias, token_mask, ids, gw, workspace, L);
   MOE_TRY(hip_ok(moe::launch_route(rp, stream), "route kernel"));

@@ -1,0 +1,118 @@
+// RMSNorm of the residual stream ahead of the MoE branch:
+//   y[t, d] = x[t, d] / sqrt(mean_d' x[t, d']^2 + eps) * w[d]
+// The decoder block of "Lab: build a tiny MoE in PyTorch" ("Put the MoE into
+// a decoder block") normalises the stream before the layer and adds the
+// layer's output back to it; st-moe-pytorch ("rms-norm") puts the same norm
+// ahead of the MoE inside SparseMoEBlock.
+//
+// One wave per token row, 16-byte chunks along d_model; HBM-bound (one read
+// of x from memory, a second from cache, one write).  The mean square and
+// the formula run in fp64 and each output is rounded once from fp64 to the
+// activation dtype, so the rows are the correctly rounded values of the
+// formula up to fp64 summation order.  The wave sum is a fixed butterfly, so
+// every lane holds the same bits and repeated calls agree bit for bit.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int NTHREADS = 256;
+constexpr int ROWS_PER_BLOCK = NTHREADS / 64;
+
+// Nearest bf16 of a finite fp64 value (ties to even), taken on the fp64 bit
+// pattern: the low 45 of its 52 fraction bits go, leaving bf16's 8
+// significant bits; the rounded value then converts to fp32 exactly (bf16
+// has fp32's exponent range), and its upper half is the bf16.  Values below
+// fp32's normal range are outside this kernel's use.
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double v) {
+  uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+  b += ((1ull << 44) - 1) + ((b >> 45) & 1ull);
+  b &= ~((1ull << 45) - 1);
+  const float f = static_cast<float>(__longlong_as_double(static_cast<long long>(b)));
+  return static_cast<uint16_t>(__float_as_uint(f) >> 16);
+}
+
+template <bool BF16>
+struct Chunk {
+  static constexpr int N = BF16 ? 8 : 4;  // elements per 16 bytes
+  static __device__ __forceinline__ void unpack(const uint4& q, double (&v)[N]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = static_cast<double>(__uint_as_float(w[i] << 16));
+        v[2 * i + 1] = static_cast<double>(__uint_as_float(w[i] & 0xffff0000u));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = static_cast<double>(__uint_as_float(w[i]));
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const double (&v)[N]) {
+    uint32_t w[4];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = static_cast<uint32_t>(f64_to_bf16_bits(v[2 * i])) |
+               (static_cast<uint32_t>(f64_to_bf16_bits(v[2 * i + 1])) << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(static_cast<float>(v[i]));
+    }
+    return uint4{w[0], w[1], w[2], w[3]};
+  }
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(NTHREADS) void rmsnorm_kernel(int T, int D, const void* x,
+                                                           const float* w, double eps,
+                                                           void* y) {
+  using C = Chunk<BF16>;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave
+  const int nch = D / C::N;
+  const size_t row_bytes = (size_t)D * (BF16 ? 2 : 4);
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + t * row_bytes);
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(y) + t * row_bytes);
+
+  double ss = 0.0;
+  for (int c = lane; c < nch; c += 64) {
+    double v[C::N];
+    C::unpack(src[c], v);
+#pragma unroll
+    for (int i = 0; i < C::N; ++i) ss = fma(v[i], v[i], ss);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  const double s = sqrt(ss / (double)D + eps);
+
+  // Each lane rewrites only the chunks it reads here, so y may alias x.
+  for (int c = lane; c < nch; c += 64) {
+    double v[C::N];
+    C::unpack(src[c], v);
+#pragma unroll
+    for (int i = 0; i < C::N; ++i) {
+      v[i] = v[i] / s;
+      if (w) v[i] *= static_cast<double>(w[c * C::N + i]);
+    }
+    dst[c] = C::pack(v);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(int T, int D, bool bf16, const void* x, const float* w, float eps,
+                          void* y, hipStream_t s) {
+  const int blocks = (T + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  if (bf16)
+    hipLaunchKernelGGL(rmsnorm_kernel<true>, dim3(blocks), dim3(NTHREADS), 0, s, T, D, x, w,
+                       (double)eps, y);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<false>, dim3(blocks), dim3(NTHREADS), 0, s, T, D, x, w,
+                       (double)eps, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

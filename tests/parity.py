@@ -56,12 +56,13 @@ def oracle_route(w: W.Workload, oi: dict, token_mask=None):
 
 
 def oracle_forward(w: W.Workload, oi: dict, routing=None, tokens=None, token_mask=None,
-                   swiglu_limit=0.0, residual=None):
+                   swiglu_limit=0.0, residual=None, pre_norm=None):
     return oracle.forward(oi, top_k=w.top_k, score=w.score, renormalize=w.renormalize,
                           route_scale=w.route_scale, n_groups=w.n_groups,
                           topk_groups=w.topk_groups, group_rule=w.group_rule,
                           capacity_factor=w.capacity_factor, routing=routing, tokens=tokens,
-                          token_mask=token_mask, swiglu_limit=swiglu_limit, residual=residual)
+                          token_mask=token_mask, swiglu_limit=swiglu_limit, residual=residual,
+                          pre_norm=pre_norm)
 
 
 def compare_route(w, r_ref, gpu):

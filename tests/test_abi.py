@@ -57,6 +57,8 @@ def test_status_strings(moe):
     (dict(D=100), "multiples of 64"),
     (dict(route_scale=0.0), "route_scale"),
     (dict(swiglu_limit=-1.0), "swiglu_limit"),
+    (dict(norm_eps=-1e-6), "norm_eps"),
+    (dict(norm_eps=float("inf")), "norm_eps"),
 ])
 def test_config_errors(moe, kw, match):
     base = dict(T=16, D=128, H=64, E=8, top_k=2)
@@ -78,6 +80,12 @@ def test_capacity_and_rows(moe):
         assert moe.max_rows(cfg) == min(T * k, E * oracle.capacity(cf, T, k, E))
     cfg = moe.make_config(100, 64, 64, 8, 2)
     assert moe.max_rows(cfg) == 200 and moe.capacity(cfg) == 200
+
+
+def test_pre_norm_workspace_holds_the_rows(moe):
+    a = moe.workspace_bytes(moe.make_config(4096, 4096, 14336, 8, 2))
+    b = moe.workspace_bytes(moe.make_config(4096, 4096, 14336, 8, 2, pre_norm=True))
+    assert b - a >= 4096 * 4096 * 2
 
 
 def test_workspace_grows_with_problem(moe):

@@ -1,8 +1,10 @@
 """GPU parity of the forward variants named on the NeMo AutoModel MoE page:
 score functions (sqrt-softplus; softmax with a selection bias; softmax-then-
 top-k without renormalisation for k > 1), the token (padding) mask, the
-clamped SwiGLU (swiglu_limit) and the gated shared expert, each against the
-CPU oracle on the reduced workloads (every output element compared)."""
+clamped SwiGLU (swiglu_limit) and the gated shared expert, and the steps on
+either side of the layer (RMSNorm pre-norm, residual add, bias update), each
+against the CPU oracle on the reduced workloads (every output element
+compared)."""
 from __future__ import annotations
 
 import sys
@@ -212,3 +214,92 @@ def test_update_bias(moe, E, gamma):
     assert np.all(np.abs(got - ref) <= 2.0 ** -23 * np.maximum(np.abs(ref), 1e-30) + 1e-12)
     step = np.sign(counts.sum() - E * counts.astype(np.int64))
     assert (np.sign(got - bias.astype(np.float64)) == step).all()
+
+
+def _near_rounding_tie(exact, act, rel=1e-12):
+    """Elements whose exact value lies within ``rel`` of a rounding tie of the
+    activation dtype: there the last fp64 bits of a differently ordered sum
+    may pick either neighbour, so both are correct."""
+    lo, hi = exact * (1 - rel), exact * (1 + rel)
+    if act == "bf16":
+        return P.oracle.round_to_bf16(lo) != P.oracle.round_to_bf16(hi)
+    return lo.astype(np.float32) != hi.astype(np.float32)
+
+
+RMS_CASES = [
+    # act, T, D, weight, scale of x
+    ("bf16", 301, 4096, True, 1.0),
+    ("bf16", 67, 64, False, 1e3),
+    ("bf16", 5, 7168, True, 1e-3),
+    ("f32", 129, 48, True, 1.0),
+    ("f32", 33, 4096, False, 10.0),
+]
+
+
+@pytest.mark.parametrize("act,T,D,wt,scale", RMS_CASES)
+def test_rmsnorm_correctly_rounded(moe, act, T, D, wt, scale):
+    """moe_rmsnorm returns the oracle's float64 RMSNorm rounded once to the
+    activation dtype, bit for bit (ties within 1e-12 excepted), also in place;
+    a zero row stays zero."""
+    _say(f"[rmsnorm] {act} T={T} D={D} weight={wt} scale={scale}")
+    dt = W.torch_dtype(act)
+    g = torch.Generator().manual_seed(T * D)
+    x = (torch.randn(T, D, generator=g) * scale).to(dt)
+    x[min(3, T - 1)] = 0
+    nw = (torch.rand(D, generator=g) * 1.5 + 0.25) if wt else None
+    eps = 1e-6
+    cfg = moe.make_config(T, D, 64, 4, 2, act_dtype=act, router_dtype=act, norm_eps=eps)
+    xd = x.cuda()
+    got = moe.moe_rmsnorm(cfg, xd, None if nw is None else nw.cuda())
+    torch.cuda.synchronize()
+    x64 = x.to(torch.float64).numpy()
+    w64 = None if nw is None else nw.to(torch.float64).numpy()
+    eps64 = float(np.float32(eps))
+    ref = P.oracle.rms_norm(x64, w64, eps64, act=act)
+    near = _near_rounding_tie(P.oracle.rms_norm(x64, w64, eps64, act=None), act)
+    g64 = got.cpu().to(torch.float64).numpy()
+    bad = (g64 != ref) & ~near
+    assert not bad.any(), f"{int(bad.sum())} elements differ, e.g. {np.argwhere(bad)[:3]}"
+    _say(f"  {int(near.sum())} elements within 1e-12 of a tie")
+    assert (g64[min(3, T - 1)] == 0).all()
+    moe.moe_rmsnorm(cfg, xd, None if nw is None else nw.cuda(), out=xd)
+    torch.cuda.synchronize()
+    assert torch.equal(xd, got), "in-place result differs"
+
+
+@pytest.mark.parametrize("name", ["mixtral_small", "deepseek_small", "decode_small", "tiny"])
+def test_forward_pre_norm(moe, name):
+    """out = x + MoE(RMSNorm(x)) in one moe_forward call: routing of the
+    normalised rows bit-exact, the output within the layer tolerance."""
+    w = W.SMALL[name]
+    _say(f"[pre-norm] {name}")
+    inp = W.make_inputs(w, "cpu", seed=18)
+    d = _to_dev(inp)
+    cfg = P.config_of(w)
+    cfg.pre_norm, cfg.norm_eps = 1, 1e-5
+    nw = torch.rand(w.D, generator=torch.Generator().manual_seed(18)) + 0.5
+    out, ids, gw, counts, aux = _forward(moe, w, cfg, d, residual=d["x"], norm_weight=nw.cuda())
+    oi = P.oracle_inputs(inp)
+    pre = (nw.to(torch.float64).numpy(), float(np.float32(1e-5)), w.act_dtype)
+    xn = P.oracle.rms_norm(oi["x"], *pre)
+    r = P.oracle_route(w, dict(oi, x=xn))
+    xn_dev = moe.moe_rmsnorm(cfg, d["x"], nw.cuda())
+    g = moe.moe_route(cfg, xn_dev, d["w_router"], d.get("logit_bias"), d.get("select_bias"))
+    torch.cuda.synchronize()
+    assert torch.equal(g["expert_ids"], ids) and torch.equal(g["gate_w"], gw)
+    nflag, ndiff = P.compare_route(w, r, {"expert_ids": ids, "gate_w": gw, "counts": counts,
+                                          "aux": aux, "mean_prob": g["mean_prob"]})
+    f = P.oracle_forward(w, oi, routing={"ids": ids.cpu().numpy().astype(np.int64),
+                                         "weights": gw.cpu().numpy().astype(np.float64)},
+                         residual=oi["x"], pre_norm=pre)
+    err, scale = P.compare_rows(out, f["out"], w.act_dtype, f"{name} pre-norm forward")
+    _say(f"  near ties {nflag} (differing {ndiff}); max|err| {err:.3g} max|ref| {scale:.3g}")
+
+
+def test_norm_weight_needs_pre_norm(moe):
+    w = W.SMALL["mixtral_small"]
+    d = _to_dev(W.make_inputs(w, "cpu", seed=19))
+    cfg = P.config_of(w)
+    with pytest.raises(moe.MoeError, match="pre_norm"):
+        moe.moe_forward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                        norm_weight=torch.ones(w.D, device="cuda"))
