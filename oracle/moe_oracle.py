@@ -55,6 +55,11 @@ Readings taken where the pages are silent or garbled (all listed in the design doc):
   * a shared-expert gate ([NEMO] ``MoE.shared_expert_gate``): the shared
     output is scaled per token by sigmoid(x . w_sg).  PARITY UNPINNED: the
     pages name the gate, not its form;
+  * the backward pass: gradients of <dout, out> + alpha * balance + beta * z
+    ([LAB] "Smoke test and backward pass") with the selected IDs, the drops
+    and the counts f held constant ([BOOK] "The Router": top-k is a stop-
+    gradient on the index decision; "The auxiliary load-balancing loss": f is
+    detached); the SwiGLU clamp passes gradient strictly inside the limits;
   * the pre-norm ([LAB] "Put the MoE into a decoder block", where the MoE
     branch takes the RMS-normalised residual stream; [ST] the RMSNorm of
     ``SparseMoEBlock``): y = x * w / sqrt(mean(x^2) + eps) per token, computed
@@ -71,7 +76,7 @@ __all__ = [
     "NEAR_TIE", "router_logits", "softmax", "sigmoid", "softplus", "logsumexp",
     "route", "capacity", "first_within_capacity", "permutation",
     "swiglu_ffn", "expert_outputs", "shared_expert", "combine", "forward", "update_bias",
-    "round_to_bf16", "rms_norm",
+    "round_to_bf16", "rms_norm", "loss", "backward", "swiglu_ffn_backward",
     "brute_force_forward", "all_experts_then_mask",
 ]
 
@@ -461,6 +466,135 @@ def update_bias(bias, counts, gamma):
     total = int(counts.sum())
     step = np.sign(total - E * counts).astype(np.float64)
     return np.asarray(bias, dtype=np.float64) + gamma * step
+
+
+# -------------------------------------------------------------- backward ---
+#
+# The training objective of [LAB] "Smoke test and backward pass": a task loss
+# plus alpha * balance + beta * z.  Here the task term is <dout, out> (dout is
+# the gradient the rest of the network sends back).  As in [BOOK] "The
+# Router" (top-k is a stop-gradient on the index decision) and "The auxiliary
+# load-balancing loss" (f is detached), the selected IDs, the capacity drops
+# and the counts f are constants; gradients reach the router through the gate
+# weights of the kept slots, through P_e and through z.
+
+def loss(inputs, dout, aux_coef=(0.0, 0.0), **fw):
+    """L = <dout, out> + alpha * balance + beta * z for the forward ``fw``."""
+    f = forward(inputs, **fw)
+    a, b = aux_coef
+    return (float(np.sum(np.asarray(dout, dtype=np.float64) * f["out"]))
+            + a * f["route"]["balance"] + b * f["route"]["z"]), f
+
+
+def _dsilu(v):
+    s = sigmoid(v)
+    return s + v * s * (1.0 - s)
+
+
+def swiglu_ffn_backward(z, w_gate, w_up, w_down, dF, limit=0.0):
+    """Gradients of sum(dF * FFN(z)) for FFN of ``swiglu_ffn``: returns
+    (dz [n,D], dW_gate [H,D], dW_up [H,D], dW_down [D,H], F [n,D]).  The clamp
+    passes gradient where |g| < limit (resp. |u|) and none outside."""
+    z = np.asarray(z, dtype=np.float64)
+    wg, wu, wd = (np.asarray(w, dtype=np.float64) for w in (w_gate, w_up, w_down))
+    g, u = z @ wg.T, z @ wu.T
+    gc, uc = (np.clip(g, -limit, limit), np.clip(u, -limit, limit)) if limit > 0 else (g, u)
+    act = gc * sigmoid(gc) * uc
+    F = act @ wd.T
+    da = dF @ wd
+    dWd = dF.T @ act
+    dgc = da * uc * _dsilu(gc)
+    duc = da * gc * sigmoid(gc)
+    if limit > 0:
+        dgc = dgc * (np.abs(g) < limit)
+        duc = duc * (np.abs(u) < limit)
+    dz = dgc @ wg + duc @ wu
+    return dz, dgc.T @ z, duc.T @ z, dWd, F
+
+
+def backward(inputs, dout, *, top_k, score="softmax", renormalize=True, route_scale=1.0,
+             n_groups=1, topk_groups=1, group_rule="top2sum", capacity_factor=None,
+             token_mask=None, swiglu_limit=0.0, aux_coef=(0.0, 0.0)):
+    """Gradients of ``loss`` with respect to x, W_r and every expert weight
+    (float64).  Returns dx, dw_router, dw_gate, dw_up, dw_down (+ dws_gate,
+    dws_up, dws_down with a shared expert), and the intermediates
+    d_gate_w [T,k] (dL/dw per slot) and d_logits [T,E]."""
+    fw = dict(top_k=top_k, score=score, renormalize=renormalize, route_scale=route_scale,
+              n_groups=n_groups, topk_groups=topk_groups, group_rule=group_rule,
+              capacity_factor=capacity_factor, token_mask=token_mask,
+              swiglu_limit=swiglu_limit)
+    if inputs.get("ws_sgate") is not None:
+        raise ValueError("backward: the shared-expert gate is not covered")
+    f = forward(inputs, **fw)
+    r = f["route"]
+    x = np.asarray(inputs["x"], dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    T, D = x.shape
+    E = inputs["w_router"].shape[0]
+    ids, keep, wts = r["ids"], f["keep"], r["weights"]
+    k = ids.shape[1]
+    dx = np.zeros((T, D))
+    grads = {n: np.zeros(np.shape(inputs[n])) for n in ("w_gate", "w_up", "w_down")}
+    d_gate_w = np.zeros((T, k))
+    # experts: each kept slot sends w_ts * dout_t into FFN_e; dL/dw_ts = <dout_t, FFN_e(x_t)>
+    for e in range(E):
+        t, s = np.nonzero((ids == e) & keep)
+        if t.size == 0:
+            continue
+        dF = wts[t, s][:, None] * dout[t]
+        dz, dwg, dwu, dwd, F = swiglu_ffn_backward(x[t], inputs["w_gate"][e], inputs["w_up"][e],
+                                                   inputs["w_down"][e], dF, swiglu_limit)
+        np.add.at(dx, t, dz)
+        grads["w_gate"][e] += dwg
+        grads["w_up"][e] += dwu
+        grads["w_down"][e] += dwd
+        d_gate_w[t, s] = np.sum(dout[t] * F, axis=1)
+    out = {"dw_gate": grads["w_gate"], "dw_up": grads["w_up"], "dw_down": grads["w_down"]}
+    if inputs.get("ws_gate") is not None:
+        dz, dwg, dwu, dwd, _ = swiglu_ffn_backward(x, inputs["ws_gate"], inputs["ws_up"],
+                                                   inputs["ws_down"], dout, swiglu_limit)
+        dx += dz
+        out.update(dws_gate=dwg, dws_up=dwu, dws_down=dwd)
+    # router: gate weights -> chosen scores
+    sc, h = r["scores"], r["logits"]
+    valid = ids[:, 0] >= 0
+    dsc = np.zeros((T, E))
+    for t in np.nonzero(valid)[0]:
+        c = sc[t, ids[t]]
+        if renormalize:
+            S = c.sum()
+            dc = route_scale / S * (d_gate_w[t] - np.sum(d_gate_w[t] * c) / S)
+        else:
+            dc = route_scale * d_gate_w[t]
+        np.add.at(dsc[t], ids[t], dc)
+    # balance = E * sum_e f_e P_e, P_e = mean over valid tokens of q_te
+    alpha, beta = aux_coef
+    n_valid = int(valid.sum())
+    if n_valid and alpha:
+        f_e = r["counts"] / float(n_valid * top_k)
+        dq = np.where(valid[:, None], alpha * E * f_e[None, :] / n_valid, 0.0)
+        if score == "softmax":
+            dsc += dq
+        else:  # q = s / sum_e s
+            ssum = sc.sum(axis=1, keepdims=True)
+            q = sc / ssum
+            dsc += (dq - np.sum(dq * q, axis=1, keepdims=True)) / ssum
+    # scores -> logits
+    if score == "softmax":
+        dh = sc * (dsc - np.sum(dsc * sc, axis=1, keepdims=True))
+    elif score == "sigmoid":
+        dh = dsc * sc * (1.0 - sc)
+    else:  # s = sqrt(softplus(h)): ds/dh = sigmoid(h) / (2 s)
+        dh = dsc * sigmoid(h) / (2.0 * sc)
+    # z = mean over valid tokens of lse(h_t)^2
+    if n_valid and beta:
+        lse = logsumexp(h)
+        dh += np.where(valid[:, None], beta * 2.0 * lse[:, None] * softmax(h) / n_valid, 0.0)
+    dh = np.where(valid[:, None], dh, 0.0)
+    wr = np.asarray(inputs["w_router"], dtype=np.float64)
+    dx += dh @ wr
+    out.update(dx=dx, dw_router=dh.T @ x, d_gate_w=d_gate_w, d_logits=dh)
+    return out
 
 
 # ------------------------------------------- second implementations (tiny) ---

@@ -645,4 +645,73 @@ def pin_pre_norm_layer_is_scale_free(o):
     assert not np.allclose(a["out"], raw["out"], rtol=0, atol=1e-6)
 
 
+GRAD_OF = {"x": "dx", "w_router": "dw_router", "w_gate": "dw_gate", "w_up": "dw_up",
+           "w_down": "dw_down", "ws_gate": "dws_gate", "ws_up": "dws_up", "ws_down": "dws_down"}
+
+
+def _fd_agrees(o, inp, seed, aux, **fw):
+    """Central finite differences of the loss along random directions, one per
+    parameter, against the analytic gradient.  The step is small enough that
+    no route or drop changes (checked)."""
+    r = _rng(seed)
+    dout = r.normal(size=inp["x"].shape)
+    g = o.backward(inp, dout, aux_coef=aux, **fw)
+    base = o.forward(inp, **fw)
+    eps = 1e-6
+    for name, gname in GRAD_OF.items():
+        if inp.get(name) is None:
+            continue
+        V = r.normal(size=np.shape(inp[name]))
+        lp, fp = o.loss(dict(inp, **{name: inp[name] + eps * V}), dout, aux, **fw)
+        lm, fm = o.loss(dict(inp, **{name: inp[name] - eps * V}), dout, aux, **fw)
+        for ff in (fp, fm):
+            assert np.array_equal(ff["route"]["ids"], base["route"]["ids"]), "route moved"
+            assert np.array_equal(ff["keep"], base["keep"]), "drops moved"
+        fd = (lp - lm) / (2 * eps)
+        an = float(np.sum(g[gname] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+        assert abs(an) > 1e-3, (name, an)  # the direction exercises the gradient
+
+
+def pin_backward_fd_softmax_capacity_shared(o):
+    """Softmax, renormalised top-2, capacity drops, shared expert, both aux terms."""
+    inp = _tiny_inputs(51, T=12, E=4, shared=True)
+    _fd_agrees(o, inp, 52, (0.3, 0.2), top_k=2, capacity_factor=0.75)
+
+
+def pin_backward_fd_sigmoid_groups_scale(o):
+    """Sigmoid scores with a selection bias, group limit, route_scale 2.5."""
+    inp = _tiny_inputs(53, T=10, E=8)
+    inp["select_bias"] = _rng(54).normal(size=8) * 0.1
+    _fd_agrees(o, inp, 55, (0.5, 0.1), top_k=3, score="sigmoid", route_scale=2.5,
+               n_groups=4, topk_groups=2)
+
+
+def pin_backward_fd_switch_top1(o):
+    """Switch top-1: raw softmax weight (no renorm) times a route scale, logit
+    bias, capacity."""
+    inp = _tiny_inputs(56, T=14, E=4)
+    inp["logit_bias"] = -1.1 * np.log(np.arange(1, 5))
+    _fd_agrees(o, inp, 57, (0.2, 0.05), top_k=1, renormalize=False, capacity_factor=1.0,
+               route_scale=1.7)
+
+
+def pin_backward_fd_sqrtsoftplus_mask_limit(o):
+    """sqrt-softplus scores, a token mask and the SwiGLU clamp."""
+    inp = _tiny_inputs(58, T=11, E=5, std=0.8)
+    mask = np.ones(11, dtype=bool)
+    mask[[0, 4, 5]] = False
+    _fd_agrees(o, inp, 59, (0.4, 0.3), top_k=2, score="sqrtsoftplus", token_mask=mask,
+               swiglu_limit=0.6)
+
+
+def pin_backward_zero_router_grad_top1_renorm(o):
+    """Renormalised top-1 weights are exactly 1, so without aux terms the
+    router gets no gradient ([LAB] "Ablation 2: top-1 versus top-2")."""
+    inp = _tiny_inputs(60, T=9, E=4)
+    g = o.backward(inp, _rng(61).normal(size=inp["x"].shape), top_k=1)
+    assert np.abs(g["dw_gate"]).max() > 0.1
+    assert np.abs(g["dw_router"]).max() < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -128,6 +128,48 @@ MUTANTS = [
     ("pre_norm_ignored",
      "        x = rms_norm(x, pre_norm[0], pre_norm[1], pre_norm[2])",
      "        x = x"),
+    ("bwd_dsilu_missing_term",
+     "return s + v * s * (1.0 - s)",
+     "return s"),
+    ("bwd_up_grad_without_gate",
+     "duc = da * gc * sigmoid(gc)",
+     "duc = da * sigmoid(gc)"),
+    ("bwd_gate_weight_not_in_dF",
+     "dF = wts[t, s][:, None] * dout[t]",
+     "dF = dout[t]"),
+    ("bwd_renorm_jacobian_no_subtract",
+     "dc = route_scale / S * (d_gate_w[t] - np.sum(d_gate_w[t] * c) / S)",
+     "dc = route_scale / S * d_gate_w[t]"),
+    ("bwd_route_scale_dropped",
+     "dc = route_scale * d_gate_w[t]",
+     "dc = d_gate_w[t]"),
+    ("bwd_balance_without_f",
+     "dq = np.where(valid[:, None], alpha * E * f_e[None, :] / n_valid, 0.0)",
+     "dq = np.where(valid[:, None], alpha * E / E + 0 * f_e[None, :] / n_valid, 0.0)"),
+    ("bwd_normalised_q_jacobian",
+     "dsc += (dq - np.sum(dq * q, axis=1, keepdims=True)) / ssum",
+     "dsc += dq / ssum"),
+    ("bwd_softmax_jacobian_sign",
+     "dh = sc * (dsc - np.sum(dsc * sc, axis=1, keepdims=True))",
+     "dh = sc * (dsc + np.sum(dsc * sc, axis=1, keepdims=True))"),
+    ("bwd_sigmoid_derivative",
+     "dh = dsc * sc * (1.0 - sc)",
+     "dh = dsc * sc"),
+    ("bwd_sqrtsoftplus_half",
+     "dh = dsc * sigmoid(h) / (2.0 * sc)",
+     "dh = dsc * sigmoid(h) / sc"),
+    ("bwd_z_without_2",
+     "beta * 2.0 * lse[:, None]",
+     "beta * lse[:, None]"),
+    ("bwd_router_dx_missing",
+     "dx += dh @ wr",
+     "dx += 0.0 * (dh @ wr)"),
+    ("bwd_clamp_passes_gradient",
+     "dgc = dgc * (np.abs(g) < limit)",
+     "dgc = dgc * 1.0"),
+    ("bwd_shared_expert_dx_missing",
+     "        dx += dz\n        out.update(dws_gate=dwg",
+     "        dx += 0 * dz\n        out.update(dws_gate=dwg"),
     ("router_bias_ignored",
      "h = h + np.asarray(logit_bias, dtype=np.float64)[None, :]",
      "h = h + 0.0"),
