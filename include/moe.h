@@ -244,6 +244,43 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
                        float* gate_w, int32_t* counts, float* aux, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes of moe_backward (0 if the configuration is invalid or not
+ * covered by the backward: bf16 activations without pre_norm). */
+size_t moe_backward_workspace_bytes(const moe_config* cfg);
+
+/* Backward pass of the layer ("Lab: build a tiny MoE in PyTorch", "Smoke test
+ * and backward pass": the loss is a task term plus alpha*balance + beta*z).
+ * Gradients of  L = <dout, out> + balance_coef*balance + z_coef*z  with the
+ * routes, the capacity drops and the counts f of the forward held constant
+ * ("2.9 Mixture-of-Experts (MoE) Architectures": top-k is a stop-gradient on
+ * the index decision ("The Router"), f is detached ("The auxiliary
+ * load-balancing loss")); gradients reach the router through the gate weights
+ * of the kept slots, through P_e and through z.
+ *   x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_*: as moe_forward
+ *   expert_ids, gate_w  [T, k]: the routes and gate weights of the forward
+ *                       (moe_route / moe_forward outputs; -1 marks a masked
+ *                       token)
+ *   dout                [T, D] act_dtype: gradient of the layer output
+ *   dx                  [T, D] act_dtype out
+ *   dw_router           [E, D] f32 out; dw_gate, dw_up [E, H, D] f32 out;
+ *   dw_down             [E, D, H] f32 out; dws_* (shared expert) f32 out in
+ *                       the shapes of w_shared_* (required when H_shared > 0)
+ *   d_gate_w            [T, k] f32 out or NULL: dL/d gate weight per slot
+ *                       (0 for dropped and masked slots)
+ * bf16 activations only; pre_norm and the shared-expert gate are not
+ * covered.  fp32 accumulation; intermediates (the SwiGLU factors, dL/dg and
+ * dL/du, dL/dh) are rounded to bf16 between GEMMs.  Deterministic: no float
+ * atomics, every sum runs in a fixed order. */
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
+                        const float* logit_bias, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* w_shared_gate, const void* w_shared_up,
+                        const void* w_shared_down, const int32_t* expert_ids,
+                        const float* gate_w, const void* dout, float balance_coef,
+                        float z_coef, void* dx, float* dw_router, float* dw_gate, float* dw_up,
+                        float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
+                        float* d_gate_w, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
 /* Auxiliary-loss-free balancer step ("DeepSeek-MoE and the fine-grained +
  * shared-expert idea" and "Exercises" 6 on the book page; NeMo
  * Gate.update_bias), in place on the selection bias that moe_route adds for

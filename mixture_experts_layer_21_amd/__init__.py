@@ -5,8 +5,8 @@ declared in include/moe.h); this package is its thin Python binding.
 Importing it fails loudly when the library has not been built.
 """
 from ._binding import (  # noqa: F401
-    EXPORTED, LIB_PATH, MoeConfig, MoeError, capacity, check_config, make_config, max_rows,
-    moe_combine, moe_forward, moe_grouped_swiglu, moe_permute, moe_rmsnorm, moe_route,
-    moe_update_bias,
-    new_workspace, status_string, workspace_bytes,
+    EXPORTED, LIB_PATH, MoeConfig, MoeError, backward_workspace_bytes, capacity, check_config,
+    make_config, max_rows, moe_backward, moe_combine, moe_forward, moe_grouped_swiglu,
+    moe_permute, moe_rmsnorm, moe_route, moe_update_bias, new_workspace, status_string,
+    workspace_bytes,
 )

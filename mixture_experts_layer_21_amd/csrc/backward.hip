@@ -1,0 +1,529 @@
+// Backward pass of the MoE layer on gfx950.
+//
+// The objective is the training loss of "Lab: build a tiny MoE in PyTorch"
+// ("Smoke test and backward pass"): a task term whose gradient dout reaches
+// the layer output, plus alpha * balance + beta * z.  As in "2.9
+// Mixture-of-Experts (MoE) Architectures" ("The Router": top-k is a
+// stop-gradient on the index decision; "The auxiliary load-balancing loss":
+// the dispatch fractions f are detached), the routes, drops and counts of the
+// forward are constants; gradients reach the router through the kept gate
+// weights, through P_e and through z.
+//
+// Every GEMM of the backward runs on one grouped bf16 MFMA kernel whose two
+// operands are K-contiguous (the forward's layout): weights are transposed
+// once ([D,H] -> [H,D] etc.), and the operands of the weight gradients, whose
+// contraction runs over the rows of an expert, are written transposed with
+// each expert's rows padded to a multiple of 64 columns, so every k-step lies
+// inside one expert.
+//
+//   recompute  g, u = x_t W_g^T, x_t W_u^T  ->  act, p1 = d act/d g, p2 = d act/d u
+//   down dgrad dact = dout_t W_d;  dg = w dact p1, du = w dact p2;  dL/dw = act . dact
+//   router     dh from dL/dw, the balance and z terms        (router_bwd_kernel)
+//   up dgrad   dz = [dg du] [W_g; W_u];  dx_router = dh W_r;  dx = gather-sum (dx_kernel)
+//   wgrad      dW_d = (w dout)^T act,  [dW_g; dW_u] = [dg du]^T x,  dW_r = dh^T x
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int BT = 256;                  // threads of the GEMM block: 4 waves
+constexpr int BBM = 128, BBN = 128, BBK = 64;
+constexpr int BKCH = BBK / 8;            // 16-byte chunks per LDS row
+constexpr int BCH = BBM * BKCH / BT;     // chunks per thread and operand (4)
+
+// XOR swizzle of the 16-byte chunk inside a 128-byte LDS row (as the forward:
+// conflict-free 32-row fragment reads).
+__device__ __forceinline__ int bswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ float sigm(float v) { return 1.0f / (1.0f + __expf(-v)); }
+
+// Tile of the block: group, first row (MROWS: global row), row end, column
+// tile, and the k range.  Returns false when the block has no tile.
+struct BTile {
+  int g, m0, m_end, nt, k0, k1;
+};
+
+// bn: output columns per tile (64 h for the paired gate/up tile, else 128).
+__device__ bool bwd_tile(const BwdGemmParams& p, int bn, BTile& t, int* s_scan) {
+  const int b = blockIdx.x;
+  if (p.grouping == BWD_DENSE) {
+    const int ntn = (p.N + bn - 1) / bn, ntm = (p.M + BBM - 1) / BBM;
+    if (b >= ntn * ntm) return false;
+    t.g = 0;
+    t.m0 = (b % ntm) * BBM;
+    t.nt = b / ntm;
+    t.m_end = p.M;
+    t.k0 = 0;
+    t.k1 = p.K;
+    return true;
+  }
+  if (p.grouping == BWD_KRAGGED) {
+    const int ntn = (p.N + bn - 1) / bn, ntm = (p.M + BBM - 1) / BBM;
+    const int per = ntn * ntm;
+    if (b >= per * p.G) return false;
+    t.g = b / per;
+    const int q = b % per;
+    t.m0 = (q % ntm) * BBM;
+    t.nt = q / ntm;
+    t.m_end = p.M;
+    t.k0 = p.offsets[t.g];
+    t.k1 = p.offsets[t.g + 1];
+    return true;
+  }
+  // MROWS: the row tiles of all groups, column tile major; one scan of the
+  // per-group row-tile counts (G <= 256) finds the block's group.
+  const int tid = threadIdx.x;
+  int cnt = 0;
+  if (tid < p.G) cnt = (p.offsets[tid + 1] - p.offsets[tid] + BBM - 1) / BBM;
+  s_scan[tid] = cnt;
+  __syncthreads();
+  for (int d = 1; d < BT; d <<= 1) {
+    const int v = tid >= d ? s_scan[tid - d] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  const int total = s_scan[BT - 1];
+  const int mt_bound = (p.max_rows + BBM - 1) / BBM + p.G;
+  const int ml = b % mt_bound;
+  t.nt = b / mt_bound;
+  if (ml >= total || t.nt * bn >= p.N) return false;  // uniform across the block
+  if (tid < p.G) {
+    const int hi = s_scan[tid], lo = hi - cnt;
+    if (ml >= lo && ml < hi) {
+      s_scan[BT] = tid;
+      s_scan[BT + 1] = p.offsets[tid] + (ml - lo) * BBM;
+      s_scan[BT + 2] = p.offsets[tid + 1];
+    }
+  }
+  __syncthreads();
+  t.g = s_scan[BT];
+  t.m0 = s_scan[BT + 1];
+  t.m_end = s_scan[BT + 2];
+  t.k0 = 0;
+  t.k1 = p.K;
+  return true;
+}
+
+// 128x128 output tile, 4 waves stacked along M (each 32 rows x 128 columns:
+// four 32x32 accumulators), BK = 64, LDS double-buffered through registers.
+template <int EPI>
+__global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BBM * BBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BBN * BBK];
+  __shared__ int s_scan[BT + 4];
+  BTile t;
+  if (!bwd_tile(p, EPI == BWD_EPI_GATEUP_SAVE ? BBN / 2 : BBN, t, s_scan)) return;
+  const int tid = threadIdx.x;
+  const bool kr = p.grouping == BWD_KRAGGED;
+
+  // Row pointers of this thread's chunks (rows past the end load a valid row).
+  const uint16_t* a_src[BCH];
+  const uint16_t* b_src[BCH];
+  int dst[BCH];
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int c = tid + BT * i, r = c / BKCH, kc = c % BKCH;
+    dst[i] = r * BBK + (kc ^ bswz(r)) * 8;
+    int m = t.m0 + r;
+    if (m >= t.m_end) m = t.m0;
+    long long arow;
+    if (kr) {
+      arow = (long long)m * p.lda + t.k0;
+    } else {
+      const int src = p.gather ? p.gather[m] / p.gdiv : m;
+      arow = (long long)src * p.lda;
+    }
+    a_src[i] = p.A + arow + kc * 8;
+    const uint16_t* bb;
+    if (EPI == BWD_EPI_GATEUP_SAVE) {
+      // 64 gate rows then the same 64 up rows of column tile nt
+      int n = t.nt * (BBN / 2) + (r % (BBN / 2));
+      if (n >= p.N) n = 0;
+      bb = (r < BBN / 2 ? p.B : p.B2) + (long long)t.g * p.b_gstride + (long long)n * p.ldb;
+    } else {
+      int n = t.nt * BBN + r;
+      if (n >= p.N) n = 0;
+      bb = kr ? p.B + (long long)n * p.ldb + t.k0
+              : p.B + (long long)t.g * p.b_gstride + (long long)n * p.ldb;
+    }
+    b_src[i] = bb + kc * 8;
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[ni][i] = 0.f;
+
+  const int nk = (t.k1 - t.k0) / BBK;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, lk = lane >> 5;
+  u32x4 ra[BCH], rb[BCH];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kt * BBK);
+      rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + (size_t)kt * BBK);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      *reinterpret_cast<u32x4*>(&As[buf][dst[i]]) = ra[i];
+      *reinterpret_cast<u32x4*>(&Bs[buf][dst[i]]) = rb[i];
+    }
+  };
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < BBK / 16; ++kk) {
+      const int ch = kk * 2 + lk;
+      const int ra_ = wave * 32 + lr;
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[cur][ra_ * BBK + (ch ^ bswz(ra_)) * 8]);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int rb_ = ni * 32 + lr;
+        const bf16x8 bfr =
+            *reinterpret_cast<const bf16x8*>(&Bs[cur][rb_ * BBK + (ch ^ bswz(rb_)) * 8]);
+        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[ni], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue.  Accumulator element i of lane l: row 8*(i/4) + 4*(l/32) + (i%4)
+  // of the wave's 32 rows, column l%32 of the 32-column block ni.
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = t.m0 + wave * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
+    const bool row_ok = m < t.m_end;
+    if (EPI == BWD_EPI_F32) {
+      if (!row_ok) continue;
+      float* base;
+      long long row = m;
+      if (m >= p.c_split) {
+        base = p.C2;
+        row = m - p.c_split;
+      } else {
+        base = p.C;
+      }
+      base += (long long)t.g * p.c_gstride + row * p.ldc;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int n = t.nt * BBN + ni * 32 + lr;
+        if (n < p.N) base[n] = acc[ni][i];
+      }
+    } else if (EPI == BWD_EPI_GATEUP_SAVE) {
+      if (!row_ok) continue;
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int h = t.nt * (BBN / 2) + ni * 32 + lr;
+        if (h >= p.N) continue;
+        const float g = acc[ni][i], u = acc[ni + 2][i];
+        float gc = g, uc = u, mg = 1.f, mu = 1.f;
+        if (p.limit > 0.f) {
+          gc = fminf(fmaxf(g, -p.limit), p.limit);
+          uc = fminf(fmaxf(u, -p.limit), p.limit);
+          mg = fabsf(g) < p.limit ? 1.f : 0.f;
+          mu = fabsf(u) < p.limit ? 1.f : 0.f;
+        }
+        const float s = sigm(gc);
+        const long long o = (long long)m * p.ldh + h;
+        p.act[o] = f32_to_bf16_bits(gc * s * uc);
+        p.p1[o] = f32_to_bf16_bits(mg * uc * (s + gc * s * (1.f - s)));
+        p.p2[o] = f32_to_bf16_bits(mu * gc * s);
+      }
+    } else {  // BWD_EPI_DOWN_DGRAD
+      float w = 1.f;
+      if (row_ok && p.gate_w) w = p.gate_w[p.r2a[m]];
+      float rs = 0.f;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int h = t.nt * BBN + ni * 32 + lr;
+        if (!row_ok || h >= p.N) continue;
+        const long long o = (long long)m * p.ldh + h;
+        const float da = acc[ni][i];
+        const float a = bf16_bits_to_f32(p.act[o]);
+        rs += a * da;
+        const long long od = (long long)m * p.lddgu + h;
+        p.dgu[od] = f32_to_bf16_bits(w * da * bf16_bits_to_f32(p.p1[o]));
+        p.dgu[od + p.H] = f32_to_bf16_bits(w * da * bf16_bits_to_f32(p.p2[o]));
+      }
+      if (p.dw_part) {
+        // the 32 lanes of a half-wave hold the row's 128 columns: fixed butterfly
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) rs += __shfl_xor(rs, off);
+        if (row_ok && lr == 0) p.dw_part[(long long)m * p.npart + t.nt] = rs;
+      }
+    }
+  }
+}
+
+// 64x64 tiled transpose through LDS (see TransposeParams).
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeParams p) {
+  __shared__ float tile[64][65];
+  const int b = blockIdx.z;
+  const int jc0 = blockIdx.x * 64;           // first destination column (padded space)
+  const int c0 = blockIdx.y * 64;            // first source column
+  if (jc0 >= p.out_cols) return;
+  // Source rows j of this tile: with ragged groups a 64-column tile lies in
+  // one group (padded offsets are multiples of 64).
+  int j0 = jc0, j_end = p.rows;
+  if (p.offsets) {
+    int g = 0;
+    while (g + 1 < p.G && p.padoff[g + 1] <= jc0) ++g;
+    if (jc0 >= p.padoff[p.G]) {
+      j0 = 0;
+      j_end = 0;  // past the last group: zeros
+    } else {
+      j0 = p.offsets[g] + (jc0 - p.padoff[g]);
+      j_end = p.offsets[g + 1];
+    }
+  }
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int jj = ty; jj < 64; jj += 4) {
+    const int j = j0 + jj, c = c0 + tx;
+    float v = 0.f;
+    if (j < j_end && c < p.cols) {
+      const int src_row = p.gather ? p.gather[j] / p.gdiv : j;
+      const long long o = (long long)b * p.src_bstride + (long long)src_row * p.ld_src + c;
+      v = p.src_f32 ? static_cast<const float*>(p.src)[o]
+                    : bf16_bits_to_f32(static_cast<const uint16_t*>(p.src)[o]);
+      if (p.scale) v *= p.scale[p.scale_idx ? p.scale_idx[j] : j];
+    }
+    tile[jj][tx] = v;
+  }
+  __syncthreads();
+  for (int cc = ty; cc < 64; cc += 4) {
+    const int c = c0 + cc, jc = jc0 + tx;
+    if (c < p.cols && jc < p.out_cols)
+      p.dst[(long long)b * p.dst_bstride + (long long)c * p.ld_dst + p.dst_col0 + jc] =
+          f32_to_bf16_bits(tile[tx][cc]);
+  }
+}
+
+// padoff[g] = sum over g' < g of the rows of g' rounded up to 64.
+__global__ __launch_bounds__(256) void pad_offsets_kernel(int G, const int32_t* offsets,
+                                                          int32_t* padoff) {
+  __shared__ int s[257];
+  const int tid = threadIdx.x;
+  s[tid + 1] = tid < G ? (offsets[tid + 1] - offsets[tid] + 63) / 64 * 64 : 0;
+  if (tid == 0) s[0] = 0;
+  __syncthreads();
+  if (tid == 0)
+    for (int g = 1; g <= G; ++g) s[g] += s[g - 1];
+  __syncthreads();
+  if (tid <= G) padoff[tid] = s[tid];
+}
+
+// dL/dh for one token per wave (experts lane + 64j, j < 4).
+__global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
+  const int E = p.E, k = p.k;
+  uint16_t* dh_row = p.dh + (long long)t * p.Epad;
+  if (p.ids[(long long)t * k] < 0) {  // masked token: no gradient
+    for (int e = lane; e < p.Epad; e += 64) dh_row[e] = 0;
+    if (p.dgw && lane < k) p.dgw[(long long)t * k + lane] = 0.f;
+    return;
+  }
+  float h[4], sc[4], smx[4];
+  bool ok[4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    ok[j] = e < E;
+    h[j] = ok[j] ? p.logits[(long long)t * E + e] : -INFINITY;
+    m = fmaxf(m, h[j]);
+  }
+  m = wave_max(m);
+  float S = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    smx[j] = ok[j] ? __expf(h[j] - m) : 0.f;
+    S += smx[j];
+  }
+  S = wave_sum(S);
+  const float lse = m + __logf(S);
+  float ssum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    smx[j] /= S;
+    if (!ok[j]) {
+      sc[j] = 0.f;
+    } else if (p.score_func == 0) {
+      sc[j] = smx[j];
+    } else if (p.score_func == 1) {
+      sc[j] = sigm(h[j]);
+    } else {
+      const float sp = h[j] > 20.f ? h[j] : log1pf(__expf(h[j]));
+      sc[j] = sqrtf(sp);
+    }
+    ssum += sc[j];
+  }
+  ssum = wave_sum(ssum);
+
+  // dL/dw of each slot: the fixed-order sum of the row's column-tile partials.
+  float dw[kMaxTopK];
+  float csum = 0.f, dwc = 0.f;
+  for (int s = 0; s < k; ++s) {
+    const int r = p.a2r[(long long)t * k + s];
+    float v = 0.f;
+    if (r >= 0)
+      for (int q = 0; q < p.npart; ++q) v += p.dw_part[(long long)r * p.npart + q];
+    dw[s] = v;
+    const int e = p.ids[(long long)t * k + s];
+    float cj = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e >> 6 == j) cj = __shfl(sc[j], e & 63);
+    csum += cj;
+    dwc += v * cj;
+  }
+  if (p.dgw && lane < k) {
+    float mine = 0.f;
+    for (int s = 0; s < k; ++s)
+      if (s == lane) mine = dw[s];
+    p.dgw[(long long)t * k + lane] = mine;
+  }
+  // dL/d score
+  float dsc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < k; ++s) {
+    const int e = p.ids[(long long)t * k + s];
+    const float dc = p.renormalize ? p.route_scale / csum * (dw[s] - dwc / csum)
+                                   : p.route_scale * dw[s];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j == e) dsc[j] += dc;
+  }
+  // balance: E * sum f_e P_e with f = counts / (n_valid k) held constant
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) tot += ok[j] ? p.counts[lane + 64 * j] : 0;
+  tot = wave_sum_int(tot);
+  const float n_valid = (float)(tot / k);
+  if (p.alpha != 0.f && tot > 0) {
+    float dq[4], dqq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dq[j] = ok[j] ? p.alpha * (float)E * ((float)p.counts[lane + 64 * j] / (float)tot) / n_valid
+                    : 0.f;
+      dqq += dq[j] * sc[j];
+    }
+    dqq = wave_sum(dqq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (p.score_func == 0)
+        dsc[j] += dq[j];
+      else
+        dsc[j] += (dq[j] - dqq / ssum) / ssum;
+    }
+  }
+  // scores -> logits, then z = mean lse^2
+  float dss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dss += dsc[j] * sc[j];
+  dss = wave_sum(dss);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float d;
+    if (!ok[j]) {
+      d = 0.f;
+    } else if (p.score_func == 0) {
+      d = sc[j] * (dsc[j] - dss);
+    } else if (p.score_func == 1) {
+      d = dsc[j] * sc[j] * (1.f - sc[j]);
+    } else {
+      d = dsc[j] * sigm(h[j]) / (2.f * sc[j]);
+    }
+    if (ok[j] && p.beta != 0.f && tot > 0) d += p.beta * 2.f * lse * smx[j] / n_valid;
+    const int e = lane + 64 * j;
+    if (e < p.Epad) dh_row[e] = f32_to_bf16_bits(ok[j] ? d : 0.f);
+  }
+}
+
+// dx[t] = sum over kept slots (slot order) of dz[row] + dzs[t] + dxr[t]
+template <typename T>
+__global__ __launch_bounds__(256) void dx_kernel(DxParams p) {
+  const long long n4 = (long long)p.T * p.D / 4;
+  for (long long q = blockIdx.x * 256ll + threadIdx.x; q < n4; q += (long long)gridDim.x * 256) {
+    const long long o = q * 4;
+    const int t = (int)(o / p.D), d = (int)(o % p.D);
+    f32x4 s = *reinterpret_cast<const f32x4*>(p.dxr + o);
+    for (int j = 0; j < p.k; ++j) {
+      const int r = p.a2r[(long long)t * p.k + j];
+      if (r >= 0) s += *reinterpret_cast<const f32x4*>(p.dz + (long long)r * p.D + d);
+    }
+    if (p.dzs) s += *reinterpret_cast<const f32x4*>(p.dzs + o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Elem<T>::store(static_cast<T*>(p.dx), o + i, s[i]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s) {
+  long long blocks;
+  const int nN = p.epilogue == BWD_EPI_GATEUP_SAVE ? (p.N + BBN / 2 - 1) / (BBN / 2)
+                                                  : (p.N + BBN - 1) / BBN;
+  if (p.grouping == BWD_DENSE)
+    blocks = (long long)nN * ((p.M + BBM - 1) / BBM);
+  else if (p.grouping == BWD_KRAGGED)
+    blocks = (long long)nN * ((p.M + BBM - 1) / BBM) * p.G;
+  else
+    blocks = (long long)nN * ((p.max_rows + BBM - 1) / BBM + p.G);
+  if (blocks <= 0) return hipSuccess;
+  const BwdGemmParams& q = p;
+  switch (p.epilogue) {
+    case BWD_EPI_F32:
+      hipLaunchKernelGGL(bwd_gemm_kernel<BWD_EPI_F32>, dim3((unsigned)blocks), dim3(BT), 0, s, q);
+      break;
+    case BWD_EPI_GATEUP_SAVE:
+      hipLaunchKernelGGL(bwd_gemm_kernel<BWD_EPI_GATEUP_SAVE>, dim3((unsigned)blocks), dim3(BT),
+                         0, s, q);
+      break;
+    default:
+      hipLaunchKernelGGL(bwd_gemm_kernel<BWD_EPI_DOWN_DGRAD>, dim3((unsigned)blocks), dim3(BT),
+                         0, s, q);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const TransposeParams& p, hipStream_t s) {
+  if (p.out_cols <= 0 || p.cols <= 0 || p.batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_kernel, dim3((p.out_cols + 63) / 64, (p.cols + 63) / 64, p.batch),
+                     dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_offsets(int G, const int32_t* offsets, int32_t* padoff, hipStream_t s) {
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, s, G, offsets, padoff);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const RouterBwdParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx(const DxParams& p, bool bf16, hipStream_t s) {
+  const long long n4 = (long long)p.T * p.D / 4;
+  const unsigned blocks = (unsigned)std::min<long long>((n4 + 255) / 256, 8192);
+  if (bf16)
+    hipLaunchKernelGGL(dx_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(dx_kernel<float>, dim3(blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

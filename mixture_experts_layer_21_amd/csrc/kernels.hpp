@@ -32,6 +32,7 @@ struct RouteParams {
   float* pe_part;     // [E*nblk]  per-tile sums of P_e terms
   float* z_part;      // [nblk]    per-block sums of lse^2
   int32_t* valid_part;  // [nblk]  unmasked tokens per block
+  float* logits_out;    // [T*E] or null: the logits (bias included) of unmasked tokens
 };
 
 struct FinalizeParams {
@@ -101,6 +102,106 @@ struct CombineParams {
   const void* residual;      // [T, D] or null: added to the output
   void* out;
 };
+
+// ------------------------------------------------------------ backward --
+
+// Grouped bf16 GEMM of the backward pass, both operands K-contiguous:
+//   C[g](m, n) = sum_k A[g](m, k) * B[g](n, k), fp32 accumulation.
+enum BwdGrouping { BWD_DENSE = 0, BWD_MROWS = 1, BWD_KRAGGED = 2 };
+enum BwdEpilogue { BWD_EPI_F32 = 0, BWD_EPI_GATEUP_SAVE = 1, BWD_EPI_DOWN_DGRAD = 2 };
+
+struct BwdGemmParams {
+  int grouping, epilogue;
+  int M, N, K;               // DENSE: all three; MROWS: N and K; KRAGGED: M and N
+  int G;                     // groups (experts)
+  const int32_t* offsets;    // MROWS: [G+1] row offsets; KRAGGED: [G+1] k offsets (multiples of 64)
+  int max_rows;              // MROWS: host bound on offsets[G] (grid size)
+  // A: MROWS/DENSE row r at A + src(r)*lda, src(r) = gather ? gather[r] / gdiv : r;
+  //    KRAGGED row m at A + m*lda + offsets[g]
+  const uint16_t* A;
+  long long lda;
+  const int32_t* gather;
+  int gdiv;
+  // B: MROWS/DENSE row n at B + g*b_gstride + n*ldb; KRAGGED row n at B + n*ldb + offsets[g].
+  // GATEUP_SAVE: a column tile is 64 rows of B (gate) and the same 64 rows of B2 (up).
+  const uint16_t* B;
+  const uint16_t* B2;
+  long long ldb, b_gstride;
+  // EPI_F32: C row m of group g (KRAGGED) / row r (MROWS, DENSE) at
+  // C + g*c_gstride + m*ldc; rows m >= c_split go to C2 + g*c_gstride + (m-c_split)*ldc.
+  float* C;
+  float* C2;
+  long long ldc, c_gstride;
+  int c_split;
+  // GATEUP_SAVE: act = silu(g)*u and the two factors p1 = d act/d g, p2 = d act/d u
+  // (clamp included) at [r][h], row stride ldh; limit = swiglu_limit.
+  uint16_t* act;
+  uint16_t* p1;
+  uint16_t* p2;
+  long long ldh;
+  float limit;
+  // DOWN_DGRAD: the accumulator is d(act) for unit gate weight; with the saved
+  // act/p1/p2 (ldh) it writes dg = w*dact*p1 and du = w*dact*p2 to dgu [r][h]
+  // and [r][H+h] (stride lddgu), w = gate_w[r2a[r]] (1 without gate_w), and
+  // the row sums of act*dact over each 128-column tile to dw_part [r][npart].
+  const float* gate_w;
+  const int32_t* r2a;
+  uint16_t* dgu;
+  long long lddgu;
+  int H;
+  float* dw_part;
+  int npart;
+};
+
+// dst[c][col(j)] = scale(j) * src[row(j)][c]: a tiled transpose.  col(j) = j,
+// or, with offsets/padoff (ragged groups), group g's rows offsets[g].. go to
+// columns padoff[g].. and the columns up to padoff[g+1] are zero.
+struct TransposeParams {
+  int rows, cols;            // source rows j (before padding) and columns c
+  const void* src;
+  int src_f32;               // source element type: fp32 (1) or bf16 (0)
+  long long ld_src, src_bstride;
+  const int32_t* gather;     // source row of j: gather[j] / gdiv (null: j)
+  int gdiv;
+  const float* scale;        // per-j factor scale[scale_idx[j]] (null: 1)
+  const int32_t* scale_idx;
+  const int32_t* offsets;    // [G+1] or null (col = j)
+  const int32_t* padoff;     // [G+1] padded column offsets (multiples of 64)
+  int G;
+  int out_cols;              // columns of dst to fill (padded total bound)
+  uint16_t* dst;
+  long long ld_dst, dst_bstride;
+  int dst_col0;              // first destination column
+  int batch;
+};
+
+struct RouterBwdParams {
+  int T, E, Epad, k, score_func, renormalize;
+  float route_scale, alpha, beta;
+  const float* logits;       // [T, E] (logit bias included)
+  const int32_t* ids;        // [T, k]
+  const int32_t* a2r;        // [T*k]
+  const float* dw_part;      // [rows, npart]
+  int npart;
+  const int32_t* counts;     // [E] pre-drop
+  uint16_t* dh;              // [T, Epad] bf16 out
+  float* dgw;                // [T, k] or null
+};
+
+struct DxParams {
+  int T, D, k;
+  const float* dz;           // [rows, D] per kept row
+  const int32_t* a2r;
+  const float* dzs;          // [T, D] or null (shared expert)
+  const float* dxr;          // [T, D] (router)
+  void* dx;                  // [T, D] act dtype
+};
+
+hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s);
+hipError_t launch_transpose(const TransposeParams& p, hipStream_t s);
+hipError_t launch_pad_offsets(int G, const int32_t* offsets, int32_t* padoff, hipStream_t s);
+hipError_t launch_router_bwd(const RouterBwdParams& p, hipStream_t s);
+hipError_t launch_dx(const DxParams& p, bool bf16, hipStream_t s);
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
 hipError_t launch_hist(int T, int E, int k, const int32_t* ids, int32_t* hist, hipStream_t s);

@@ -154,6 +154,65 @@ Layout layout_of(const moe_config* c) {
   return L;
 }
 
+// Backward workspace: the forward layout (route and permutation scratch),
+// then the backward's own buffers.
+struct BwdLayout {
+  size_t logits, padoff, wdT, wguT, wrT, act, p1, p2, dgu, part, dh, dz, dxr, dFT, XT, AT, DGUT,
+      dhT, xT, swdT, swguT, sact, sp1, sp2, sdgu, sdz, doutT, sAT, sDGUT, total;
+  int Epad, Tpad, Kpad, npart;
+};
+
+BwdLayout bwd_layout_of(const moe_config* c) {
+  BwdLayout B{};
+  const Layout L = layout_of(c);
+  size_t off = L.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t T = c->T, D = c->D, H = c->H, E = c->E, Hs = c->H_shared;
+  const size_t R = (size_t)std::max<long long>(max_rows_of(c), 1);
+  B.Epad = (int)((E + 63) / 64 * 64);
+  B.Tpad = (int)((T + 63) / 64 * 64);
+  B.Kpad = (int)((R + 64 * E + 63) / 64 * 64);
+  B.npart = (int)((H + 127) / 128);
+  const size_t Kp = B.Kpad, Tp = B.Tpad, Ep = B.Epad;
+  B.logits = take(T * E * 4);
+  B.padoff = take((E + 1) * 4);
+  B.wdT = take(E * H * D * 2);
+  B.wguT = take(E * D * 2 * H * 2);
+  B.wrT = take(D * Ep * 2);
+  B.act = take(R * H * 2);
+  B.p1 = take(R * H * 2);
+  B.p2 = take(R * H * 2);
+  B.dgu = take(R * 2 * H * 2);
+  B.part = take(R * B.npart * 4);
+  B.dh = take(T * Ep * 2);
+  B.dz = take(R * D * 4);
+  B.dxr = take(T * D * 4);
+  B.dFT = take(D * Kp * 2);
+  B.XT = take(D * Kp * 2);
+  B.AT = take(H * Kp * 2);
+  B.DGUT = take(2 * H * Kp * 2);
+  B.dhT = take(Ep * Tp * 2);
+  B.xT = take(D * Tp * 2);
+  if (Hs) {
+    B.swdT = take(Hs * D * 2);
+    B.swguT = take(D * 2 * Hs * 2);
+    B.sact = take(T * Hs * 2);
+    B.sp1 = take(T * Hs * 2);
+    B.sp2 = take(T * Hs * 2);
+    B.sdgu = take(T * 2 * Hs * 2);
+    B.sdz = take(T * D * 4);
+    B.doutT = take(D * Tp * 2);
+    B.sAT = take(Hs * Tp * 2);
+    B.sDGUT = take(2 * Hs * Tp * 2);
+  }
+  B.total = off;
+  return B;
+}
+
 moe_status check_ws(const moe_config* c, void* ws, size_t bytes) {
   const size_t need = layout_of(c).total;
   if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
@@ -578,6 +637,419 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
   moe::CombineParams cp{cfg->T, cfg->D, cfg->top_k, y,        a2r,
                         sy,     x,      shared_expert_gate,      residual, out};
   MOE_TRY(hip_ok(moe::launch_combine(cp, bf16, stream), "combine kernel"));
+  return ok();
+}
+
+size_t moe_backward_workspace_bytes(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK || cfg->act_dtype != MOE_BF16 || cfg->pre_norm) return 0;
+  return bwd_layout_of(cfg).total;
+}
+
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
+                        const float* logit_bias, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* w_shared_gate, const void* w_shared_up,
+                        const void* w_shared_down, const int32_t* expert_ids,
+                        const float* gate_w, const void* dout, float balance_coef,
+                        float z_coef, void* dx, float* dw_router, float* dw_gate, float* dw_up,
+                        float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
+                        float* d_gate_w, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  if (cfg->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward: bf16 activations only");
+  if (cfg->pre_norm) return fail(MOE_ERR_UNSUPPORTED, "moe_backward: pre_norm is not covered");
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !expert_ids || !gate_w || !dout ||
+      !dx || !dw_router || !dw_gate || !dw_up || !dw_down)
+    return fail(MOE_ERR_NULL_PTR, "moe_backward: inputs, routing and gradient outputs required");
+  const bool sh = cfg->H_shared > 0;
+  if (sh && (!w_shared_gate || !w_shared_up || !w_shared_down || !dws_gate || !dws_up ||
+             !dws_down))
+    return fail(MOE_ERR_NULL_PTR, "moe_backward: H_shared > 0 needs the shared weights and grads");
+  if (!isfinite(balance_coef) || !isfinite(z_coef))
+    return fail(MOE_ERR_INVALID_ARG, "moe_backward: loss coefficients must be finite");
+  const BwdLayout B = bwd_layout_of(cfg);
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (workspace_bytes < B.total)
+    return fail(MOE_ERR_WORKSPACE, "backward workspace too small: %zu < %zu bytes",
+                workspace_bytes, B.total);
+  const void* dev_in[] = {x, w_router, w_gate, w_up, w_down, expert_ids, gate_w, dout, dx,
+                          dw_router, dw_gate, dw_up, dw_down, workspace};
+  const char* names[] = {"x", "w_router", "w_gate", "w_up", "w_down", "expert_ids", "gate_w",
+                         "dout", "dx", "dw_router", "dw_gate", "dw_up", "dw_down", "workspace"};
+  for (int i = 0; i < 14; ++i) MOE_TRY(check_dev(dev_in[i], names[i], true));
+  MOE_TRY(check_dev(logit_bias, "logit_bias", false));
+  MOE_TRY(check_dev(d_gate_w, "d_gate_w", false));
+  if (sh) {
+    MOE_TRY(check_dev(w_shared_gate, "w_shared_gate", true));
+    MOE_TRY(check_dev(w_shared_up, "w_shared_up", true));
+    MOE_TRY(check_dev(w_shared_down, "w_shared_down", true));
+    MOE_TRY(check_dev(dws_gate, "dws_gate", true));
+    MOE_TRY(check_dev(dws_up, "dws_up", true));
+    MOE_TRY(check_dev(dws_down, "dws_down", true));
+  }
+
+  const Layout L = layout_of(cfg);
+  const int T = cfg->T, D = cfg->D, H = cfg->H, E = cfg->E, k = cfg->top_k, Hs = cfg->H_shared;
+  const int R = (int)max_rows_of(cfg);
+  const int cap = (int)capacity_of(cfg);
+  const bool dropless = !(cfg->capacity_factor > 0.0);
+  auto ws = [&](size_t off) { return static_cast<char*>(workspace) + off; };
+  auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws(off)); };
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws(off)); };
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* r2a = at<int32_t>(workspace, L.r2a);
+  int32_t* a2r = at<int32_t>(workspace, L.a2r);
+  int32_t* counts = at<int32_t>(workspace, L.counts_ws);
+  int32_t* padoff = at<int32_t>(workspace, B.padoff);
+
+  // 1. the forward's permutation, from the given routes
+  MOE_TRY(hip_ok(moe::launch_hist(T, E, k, expert_ids, at<int32_t>(workspace, L.hist), stream),
+                 "hist kernel"));
+  moe::FinalizeParams fp{};
+  fp.T = T;
+  fp.E = E;
+  fp.k = k;
+  fp.nblk = moe::route_blocks(T);
+  fp.capacity = dropless ? 0 : cap;
+  fp.hist = at<int32_t>(workspace, L.hist);
+  fp.counts_ws = counts;
+  fp.pe_ws = at<float>(workspace, L.pe_ws);
+  fp.block_base = at<int32_t>(workspace, L.block_base);
+  fp.expert_offsets = offsets;
+  fp.n_kept = at<int32_t>(workspace, L.n_kept);
+  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
+  moe::ScatterParams sp{T, E, k, fp.capacity, expert_ids, fp.block_base, offsets, r2a, a2r};
+  MOE_TRY(hip_ok(moe::launch_scatter(sp, stream), "scatter kernel"));
+  MOE_TRY(hip_ok(moe::launch_pad_offsets(E, offsets, padoff, stream), "pad offsets kernel"));
+
+  // 2. the logits (the routing kernels rerun; their own routes are not used)
+  moe::RouteParams rp = route_params(cfg, x, w_router, logit_bias, nullptr, nullptr,
+                                     at<int32_t>(workspace, L.ids),
+                                     at<float>(workspace, L.gate_w), workspace, L);
+  rp.logits_out = f32(B.logits);
+  MOE_TRY(hip_ok(moe::launch_route(rp, stream), "route kernel"));
+
+  // 3. K-contiguous copies of the weights
+  auto transpose = [&](int rows, int cols, const void* src, bool src_f32, long long ld_src,
+                       long long src_b, int out_cols, uint16_t* dst, long long ld_dst,
+                       long long dst_b, int col0, int batch, const int32_t* gather,
+                       const float* scale, const int32_t* scale_idx, bool ragged) {
+    moe::TransposeParams t{};
+    t.rows = rows;
+    t.cols = cols;
+    t.src = src;
+    t.src_f32 = src_f32;
+    t.ld_src = ld_src;
+    t.src_bstride = src_b;
+    t.gather = gather;
+    t.gdiv = k;
+    t.scale = scale;
+    t.scale_idx = scale_idx;
+    t.offsets = ragged ? offsets : nullptr;
+    t.padoff = ragged ? padoff : nullptr;
+    t.G = E;
+    t.out_cols = out_cols;
+    t.dst = dst;
+    t.ld_dst = ld_dst;
+    t.dst_bstride = dst_b;
+    t.dst_col0 = col0;
+    t.batch = batch;
+    return hip_ok(moe::launch_transpose(t, stream), "transpose kernel");
+  };
+  MOE_TRY(transpose(D, H, w_down, false, H, (long long)D * H, D, u16(B.wdT), D,
+                    (long long)H * D, 0, E, nullptr, nullptr, nullptr, false));
+  MOE_TRY(transpose(H, D, w_gate, false, D, (long long)H * D, H, u16(B.wguT), 2 * H,
+                    (long long)D * 2 * H, 0, E, nullptr, nullptr, nullptr, false));
+  MOE_TRY(transpose(H, D, w_up, false, D, (long long)H * D, H, u16(B.wguT), 2 * H,
+                    (long long)D * 2 * H, H, E, nullptr, nullptr, nullptr, false));
+  MOE_TRY(transpose(E, D, w_router, cfg->router_dtype == MOE_F32, D, 0, B.Epad, u16(B.wrT),
+                    B.Epad, 0, 0, 1, nullptr, nullptr, nullptr, false));
+  if (sh) {
+    MOE_TRY(transpose(D, Hs, w_shared_down, false, Hs, 0, D, u16(B.swdT), D, 0, 0, 1, nullptr,
+                      nullptr, nullptr, false));
+    MOE_TRY(transpose(Hs, D, w_shared_gate, false, D, 0, Hs, u16(B.swguT), 2 * Hs, 0, 0, 1,
+                      nullptr, nullptr, nullptr, false));
+    MOE_TRY(transpose(Hs, D, w_shared_up, false, D, 0, Hs, u16(B.swguT), 2 * Hs, 0, Hs, 1,
+                      nullptr, nullptr, nullptr, false));
+  }
+
+  auto gemm = [&](moe::BwdGemmParams g, const char* what) {
+    return hip_ok(moe::launch_bwd_gemm(g, stream), what);
+  };
+  const int kNoSplit = 0x7fffffff;
+  // 4. recompute gate/up: act, p1, p2 of every kept row
+  {
+    moe::BwdGemmParams g{};
+    g.grouping = moe::BWD_MROWS;
+    g.epilogue = moe::BWD_EPI_GATEUP_SAVE;
+    g.N = H;
+    g.K = D;
+    g.G = E;
+    g.offsets = offsets;
+    g.max_rows = R;
+    g.A = static_cast<const uint16_t*>(x);
+    g.lda = D;
+    g.gather = r2a;
+    g.gdiv = k;
+    g.B = static_cast<const uint16_t*>(w_gate);
+    g.B2 = static_cast<const uint16_t*>(w_up);
+    g.ldb = D;
+    g.b_gstride = (long long)H * D;
+    g.act = u16(B.act);
+    g.p1 = u16(B.p1);
+    g.p2 = u16(B.p2);
+    g.ldh = H;
+    g.limit = cfg->swiglu_limit;
+    MOE_TRY(gemm(g, "recompute gate/up"));
+    // 5. down dgrad with the gate weights: dg, du and dL/dw partials
+    moe::BwdGemmParams d{};
+    d.grouping = moe::BWD_MROWS;
+    d.epilogue = moe::BWD_EPI_DOWN_DGRAD;
+    d.N = H;
+    d.K = D;
+    d.G = E;
+    d.offsets = offsets;
+    d.max_rows = R;
+    d.A = static_cast<const uint16_t*>(dout);
+    d.lda = D;
+    d.gather = r2a;
+    d.gdiv = k;
+    d.B = u16(B.wdT);
+    d.ldb = D;
+    d.b_gstride = (long long)H * D;
+    d.act = u16(B.act);
+    d.p1 = u16(B.p1);
+    d.p2 = u16(B.p2);
+    d.ldh = H;
+    d.gate_w = gate_w;
+    d.r2a = r2a;
+    d.dgu = u16(B.dgu);
+    d.lddgu = 2 * H;
+    d.H = H;
+    d.dw_part = f32(B.part);
+    d.npart = B.npart;
+    MOE_TRY(gemm(d, "down dgrad"));
+  }
+  // 6. router: dL/dh
+  {
+    moe::RouterBwdParams r{};
+    r.T = T;
+    r.E = E;
+    r.Epad = B.Epad;
+    r.k = k;
+    r.score_func = cfg->score_func;
+    r.renormalize = cfg->renormalize;
+    r.route_scale = cfg->route_scale;
+    r.alpha = balance_coef;
+    r.beta = z_coef;
+    r.logits = f32(B.logits);
+    r.ids = expert_ids;
+    r.a2r = a2r;
+    r.dw_part = f32(B.part);
+    r.npart = B.npart;
+    r.counts = counts;
+    r.dh = u16(B.dh);
+    r.dgw = d_gate_w;
+    MOE_TRY(hip_ok(moe::launch_router_bwd(r, stream), "router backward kernel"));
+  }
+  // 7. input gradients: dz of every kept row, dx of the router, shared expert
+  {
+    moe::BwdGemmParams g{};
+    g.grouping = moe::BWD_MROWS;
+    g.epilogue = moe::BWD_EPI_F32;
+    g.N = D;
+    g.K = 2 * H;
+    g.G = E;
+    g.offsets = offsets;
+    g.max_rows = R;
+    g.A = u16(B.dgu);
+    g.lda = 2 * H;
+    g.B = u16(B.wguT);
+    g.ldb = 2 * H;
+    g.b_gstride = (long long)D * 2 * H;
+    g.C = f32(B.dz);
+    g.ldc = D;
+    g.c_split = kNoSplit;
+    MOE_TRY(gemm(g, "gate/up dgrad"));
+    moe::BwdGemmParams r{};
+    r.grouping = moe::BWD_DENSE;
+    r.epilogue = moe::BWD_EPI_F32;
+    r.M = T;
+    r.N = D;
+    r.K = B.Epad;
+    r.G = 1;
+    r.A = u16(B.dh);
+    r.lda = B.Epad;
+    r.B = u16(B.wrT);
+    r.ldb = B.Epad;
+    r.C = f32(B.dxr);
+    r.ldc = D;
+    r.c_split = kNoSplit;
+    MOE_TRY(gemm(r, "router dgrad"));
+  }
+  if (sh) {
+    moe::BwdGemmParams g{};
+    g.grouping = moe::BWD_DENSE;
+    g.epilogue = moe::BWD_EPI_GATEUP_SAVE;
+    g.M = T;
+    g.N = Hs;
+    g.K = D;
+    g.G = 1;
+    g.A = static_cast<const uint16_t*>(x);
+    g.lda = D;
+    g.B = static_cast<const uint16_t*>(w_shared_gate);
+    g.B2 = static_cast<const uint16_t*>(w_shared_up);
+    g.ldb = D;
+    g.act = u16(B.sact);
+    g.p1 = u16(B.sp1);
+    g.p2 = u16(B.sp2);
+    g.ldh = Hs;
+    g.limit = cfg->swiglu_limit;
+    MOE_TRY(gemm(g, "shared recompute"));
+    moe::BwdGemmParams d{};
+    d.grouping = moe::BWD_DENSE;
+    d.epilogue = moe::BWD_EPI_DOWN_DGRAD;
+    d.M = T;
+    d.N = Hs;
+    d.K = D;
+    d.G = 1;
+    d.A = static_cast<const uint16_t*>(dout);
+    d.lda = D;
+    d.B = u16(B.swdT);
+    d.ldb = D;
+    d.act = u16(B.sact);
+    d.p1 = u16(B.sp1);
+    d.p2 = u16(B.sp2);
+    d.ldh = Hs;
+    d.dgu = u16(B.sdgu);
+    d.lddgu = 2 * Hs;
+    d.H = Hs;
+    MOE_TRY(gemm(d, "shared down dgrad"));
+    moe::BwdGemmParams z{};
+    z.grouping = moe::BWD_DENSE;
+    z.epilogue = moe::BWD_EPI_F32;
+    z.M = T;
+    z.N = D;
+    z.K = 2 * Hs;
+    z.G = 1;
+    z.A = u16(B.sdgu);
+    z.lda = 2 * Hs;
+    z.B = u16(B.swguT);
+    z.ldb = 2 * Hs;
+    z.C = f32(B.sdz);
+    z.ldc = D;
+    z.c_split = kNoSplit;
+    MOE_TRY(gemm(z, "shared gate/up dgrad"));
+  }
+  {
+    moe::DxParams p{T, D, k, f32(B.dz), a2r, sh ? f32(B.sdz) : nullptr, f32(B.dxr), dx};
+    MOE_TRY(hip_ok(moe::launch_dx(p, true, stream), "dx kernel"));
+  }
+
+  // 8. weight gradients: operands transposed, each expert's rows padded to 64
+  MOE_TRY(transpose(R, D, dout, false, D, 0, B.Kpad, u16(B.dFT), B.Kpad, 0, 0, 1, r2a, gate_w,
+                    r2a, true));
+  MOE_TRY(transpose(R, D, x, false, D, 0, B.Kpad, u16(B.XT), B.Kpad, 0, 0, 1, r2a, nullptr,
+                    nullptr, true));
+  MOE_TRY(transpose(R, H, u16(B.act), false, H, 0, B.Kpad, u16(B.AT), B.Kpad, 0, 0, 1, nullptr,
+                    nullptr, nullptr, true));
+  MOE_TRY(transpose(R, 2 * H, u16(B.dgu), false, 2 * H, 0, B.Kpad, u16(B.DGUT), B.Kpad, 0, 0, 1,
+                    nullptr, nullptr, nullptr, true));
+  MOE_TRY(transpose(T, B.Epad, u16(B.dh), false, B.Epad, 0, B.Tpad, u16(B.dhT), B.Tpad, 0, 0, 1,
+                    nullptr, nullptr, nullptr, false));
+  MOE_TRY(transpose(T, D, x, false, D, 0, B.Tpad, u16(B.xT), B.Tpad, 0, 0, 1, nullptr, nullptr,
+                    nullptr, false));
+  {
+    moe::BwdGemmParams g{};
+    g.grouping = moe::BWD_KRAGGED;
+    g.epilogue = moe::BWD_EPI_F32;
+    g.M = D;
+    g.N = H;
+    g.G = E;
+    g.offsets = padoff;
+    g.A = u16(B.dFT);
+    g.lda = B.Kpad;
+    g.B = u16(B.AT);
+    g.ldb = B.Kpad;
+    g.C = dw_down;
+    g.ldc = H;
+    g.c_gstride = (long long)D * H;
+    g.c_split = kNoSplit;
+    MOE_TRY(gemm(g, "down wgrad"));
+    moe::BwdGemmParams u{};
+    u.grouping = moe::BWD_KRAGGED;
+    u.epilogue = moe::BWD_EPI_F32;
+    u.M = 2 * H;
+    u.N = D;
+    u.G = E;
+    u.offsets = padoff;
+    u.A = u16(B.DGUT);
+    u.lda = B.Kpad;
+    u.B = u16(B.XT);
+    u.ldb = B.Kpad;
+    u.C = dw_gate;
+    u.C2 = dw_up;
+    u.ldc = D;
+    u.c_gstride = (long long)H * D;
+    u.c_split = H;
+    MOE_TRY(gemm(u, "gate/up wgrad"));
+    moe::BwdGemmParams r{};
+    r.grouping = moe::BWD_DENSE;
+    r.epilogue = moe::BWD_EPI_F32;
+    r.M = E;
+    r.N = D;
+    r.K = B.Tpad;
+    r.G = 1;
+    r.A = u16(B.dhT);
+    r.lda = B.Tpad;
+    r.B = u16(B.xT);
+    r.ldb = B.Tpad;
+    r.C = dw_router;
+    r.ldc = D;
+    r.c_split = kNoSplit;
+    MOE_TRY(gemm(r, "router wgrad"));
+  }
+  if (sh) {
+    MOE_TRY(transpose(T, D, dout, false, D, 0, B.Tpad, u16(B.doutT), B.Tpad, 0, 0, 1, nullptr,
+                      nullptr, nullptr, false));
+    MOE_TRY(transpose(T, Hs, u16(B.sact), false, Hs, 0, B.Tpad, u16(B.sAT), B.Tpad, 0, 0, 1,
+                      nullptr, nullptr, nullptr, false));
+    MOE_TRY(transpose(T, 2 * Hs, u16(B.sdgu), false, 2 * Hs, 0, B.Tpad, u16(B.sDGUT), B.Tpad, 0,
+                      0, 1, nullptr, nullptr, nullptr, false));
+    moe::BwdGemmParams g{};
+    g.grouping = moe::BWD_DENSE;
+    g.epilogue = moe::BWD_EPI_F32;
+    g.M = D;
+    g.N = Hs;
+    g.K = B.Tpad;
+    g.G = 1;
+    g.A = u16(B.doutT);
+    g.lda = B.Tpad;
+    g.B = u16(B.sAT);
+    g.ldb = B.Tpad;
+    g.C = dws_down;
+    g.ldc = Hs;
+    g.c_split = kNoSplit;
+    MOE_TRY(gemm(g, "shared down wgrad"));
+    moe::BwdGemmParams u{};
+    u.grouping = moe::BWD_DENSE;
+    u.epilogue = moe::BWD_EPI_F32;
+    u.M = 2 * Hs;
+    u.N = D;
+    u.K = B.Tpad;
+    u.G = 1;
+    u.A = u16(B.sDGUT);
+    u.lda = B.Tpad;
+    u.B = u16(B.xT);
+    u.ldb = B.Tpad;
+    u.C = dws_gate;
+    u.C2 = dws_up;
+    u.ldc = D;
+    u.c_split = Hs;
+    MOE_TRY(gemm(u, "shared gate/up wgrad"));
+  }
   return ok();
 }
 

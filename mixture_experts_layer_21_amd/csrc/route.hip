@@ -448,6 +448,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
     for (int j = 0; j < 4; ++j) {
       h[j] = ok[j] ? sm.lg[tl * E + lane + 64 * j] + lb[j] : -INFINITY;
       mloc = fmaxf(mloc, h[j]);
+      if (p.logits_out && ok[j]) p.logits_out[(size_t)t * E + lane + 64 * j] = h[j];
     }
     const float m = wave_max_dpp(mloc);
     float ex[4], sloc = 0.f;
