@@ -56,6 +56,8 @@ def _parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB read + 1 GiB write kernel (torch.neg on "
                          "fp32), the reference that scales the HBM byte counters")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time moe_backward (beside the forward step) and report it")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="summarise two rocprofv3 counter databases and exit")
     return ap.parse_args()
@@ -169,6 +171,43 @@ def _pmc_summary(fetch_db, write_db, workload):
     lines += ["", "Grouped SwiGLU step (every gemm kernel above once per forward):", "",
               f"hbm_bytes_per_step: {step:.6g}", ""]
     return "\n".join(lines)
+
+
+def _time_backward(moe, w, cfg, inp, r, n_kept, steps, stream):
+    """moe_backward on the forward's routes with a seeded dout, timed with HIP
+    events on the launch stream.  Algorithmic FLOP: the input-gradient and
+    weight-gradient products of every kept row (2 x the forward's 6*D*H per
+    row, plus the shared expert on T rows) and of the router (2 x 2*T*D*E)."""
+    import torch
+    if w.act_dtype != "bf16":
+        return {"skipped": "the backward covers bf16 activations"}
+    gen = torch.Generator(device=inp["x"].device)
+    gen.manual_seed(1)
+    dout = torch.randn(w.T, w.D, generator=gen, device=inp["x"].device).to(inp["x"].dtype)
+    ws = torch.empty(moe.backward_workspace_bytes(cfg), dtype=torch.uint8,
+                     device=inp["x"].device)
+
+    def bwd():
+        return moe.moe_backward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
+                                inp["w_down"], r["expert_ids"], r["gate_w"], dout,
+                                logit_bias=inp.get("logit_bias"), ws_gate=inp.get("ws_gate"),
+                                ws_up=inp.get("ws_up"), ws_down=inp.get("ws_down"),
+                                balance_coef=0.01, z_coef=0.001, workspace=ws)
+    bwd()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        bwd()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    flops = (12.0 * w.D * w.H * n_kept + 12.0 * w.D * w.H_shared * w.T
+             + 4.0 * w.T * w.D * w.E)
+    _log(f"[bench] moe_backward: {ms:.3f} ms/step, {flops / ms / 1e9:.1f} TFLOP/s")
+    return {"ms_per_step": round(ms, 4), "algorithmic_flop": flops,
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def _cpu_baseline(w, inp, target_s):
@@ -387,6 +426,8 @@ def main():
         "beside_the_step": {"rmsnorm_ms": round(rms_ms, 4),
                             "rmsnorm_gbs": round(rms_bytes / (rms_ms * 1e-3) / 1e9, 1)},
     }
+    if args.backward:
+        result["backward"] = _time_backward(moe, w, cfg, inp, r, n_kept, args.steps, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)

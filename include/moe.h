@@ -214,6 +214,7 @@ moe_status moe_combine(const moe_config* cfg, const void* y_rows,
  *   x            [T, D] act_dtype
  *   norm_weight  [D] f32, or NULL for w = 1
  *   x_norm       [T, D] act_dtype out; may be x itself (in place)
+ * x, norm_weight and x_norm must be 16-byte aligned (else MOE_ERR_INVALID_ARG).
  * The mean square and the formula are evaluated in fp64 and each output is
  * rounded once to act_dtype (bf16: nearest, ties to even), so the result is
  * the correctly rounded value of the formula up to fp64 summation order.
@@ -227,7 +228,7 @@ moe_status moe_rmsnorm(const moe_config* cfg, const void* x, const float* norm_w
  * x with norm_weight (NULL: w = 1) into the workspace, and router, experts
  * and shared-expert gate take those rows; x itself is not changed (pass it
  * as residual for the block's out = x + MoE(RMSNorm(x))); norm_weight must
- * be NULL without pre_norm.  w_shared_* may be NULL when cfg->H_shared == 0;
+ * be NULL without pre_norm, and 16-byte aligned.  w_shared_* may be NULL when cfg->H_shared == 0;
  * shared_expert_gate [D] (optional, needs a shared expert) scales its output
  * per token as in moe_combine; token_mask as in moe_route; residual [T, D]
  * (optional) is added to the output as in moe_combine.  The optional

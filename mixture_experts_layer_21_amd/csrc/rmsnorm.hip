@@ -6,10 +6,9 @@
 // ahead of the MoE inside SparseMoEBlock.
 //
 // One wave per token row, 16-byte chunks along d_model; HBM-bound (one read
-// of x from memory, a second from cache, one write).  The mean square and
-// the formula run in fp64 and each output is rounded once from fp64 to the
-// activation dtype, so the rows are the correctly rounded values of the
-// formula up to fp64 summation order.  The wave sum is a fixed butterfly, so
+// of x, one write).  The mean square and the formula run in fp64 and each
+// output is rounded once from fp64 to the activation dtype, so the rows are
+// the correctly rounded values of the formula up to fp64 rounding.  The wave sum is a fixed butterfly, so
 // every lane holds the same bits and repeated calls agree bit for bit.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -64,6 +63,10 @@ struct Chunk {
   }
 };
 
+// Rows of up to 64 * CPL chunks stay in registers between the two passes
+// (one read from memory); longer rows are read again from cache.
+constexpr int CPL = 16;
+
 template <bool BF16>
 __global__ __launch_bounds__(NTHREADS) void rmsnorm_kernel(int T, int D, const void* x,
                                                            const float* w, double eps,
@@ -76,28 +79,60 @@ __global__ __launch_bounds__(NTHREADS) void rmsnorm_kernel(int T, int D, const v
   const size_t row_bytes = (size_t)D * (BF16 ? 2 : 4);
   const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + t * row_bytes);
   uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(y) + t * row_bytes);
+  const bool cached = nch <= 64 * CPL;
 
+  uint4 q[CPL];
   double ss = 0.0;
-  for (int c = lane; c < nch; c += 64) {
-    double v[C::N];
-    C::unpack(src[c], v);
+  if (cached) {
 #pragma unroll
-    for (int i = 0; i < C::N; ++i) ss = fma(v[i], v[i], ss);
+    for (int i = 0; i < CPL; ++i)
+      if (lane + 64 * i < nch) q[i] = src[lane + 64 * i];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      if (lane + 64 * i < nch) {
+        double v[C::N];
+        C::unpack(q[i], v);
+#pragma unroll
+        for (int e = 0; e < C::N; ++e) ss = fma(v[e], v[e], ss);
+      }
+    }
+  } else {
+    for (int c = lane; c < nch; c += 64) {
+      double v[C::N];
+      C::unpack(src[c], v);
+#pragma unroll
+      for (int e = 0; e < C::N; ++e) ss = fma(v[e], v[e], ss);
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  const double s = sqrt(ss / (double)D + eps);
+  // One reciprocal per row: x * (1/s) differs from x / s by at most an fp64
+  // rounding, far below the output's rounding.
+  const double inv = 1.0 / sqrt(ss / (double)D + eps);
 
-  // Each lane rewrites only the chunks it reads here, so y may alias x.
-  for (int c = lane; c < nch; c += 64) {
+  // Each lane rewrites only the chunks it has read, so y may alias x.
+  auto emit = [&](int c, const uint4& qq) {
     double v[C::N];
-    C::unpack(src[c], v);
+    C::unpack(qq, v);
 #pragma unroll
-    for (int i = 0; i < C::N; ++i) {
-      v[i] = v[i] / s;
-      if (w) v[i] *= static_cast<double>(w[c * C::N + i]);
+    for (int e = 0; e < C::N; ++e) v[e] = v[e] * inv;
+    if (w) {  // the chunk's weights in 16-byte loads (w is 16-byte aligned)
+      const f32x4* w4 = reinterpret_cast<const f32x4*>(w) + c * (C::N / 4);
+#pragma unroll
+      for (int q4 = 0; q4 < C::N / 4; ++q4) {
+        const f32x4 wv = w4[q4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * q4 + e] *= static_cast<double>(wv[e]);
+      }
     }
     dst[c] = C::pack(v);
+  };
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      if (lane + 64 * i < nch) emit(lane + 64 * i, q[i]);
+  } else {
+    for (int c = lane; c < nch; c += 64) emit(c, src[c]);
   }
 }
 
