@@ -60,6 +60,9 @@ def _parse():
                     help="also time moe_backward (beside the forward step) and report it")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="summarise two rocprofv3 counter databases and exit")
+    ap.add_argument("--mfma-summary", metavar="DB",
+                    help="summarise a rocprofv3 database of SQ_VALU_MFMA_BUSY_CYCLES, "
+                         "SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE and exit")
     return ap.parse_args()
 
 
@@ -210,6 +213,60 @@ def _time_backward(moe, w, cfg, inp, r, n_kept, steps, stream):
             "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+SIMDS = 256 * 4  # MI355X: 256 compute units of four SIMDs
+
+
+def _mfma_summary(db, workload):
+    """Clock and MFMA utilisation per kernel from one rocprofv3 counter pass:
+    clock = GRBM_GUI_ACTIVE / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES
+    (summed over the SIMDs) / (SIMDS * GRBM_GUI_ACTIVE)."""
+    import collections
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, dispatch_id, counter_name, counter_value, duration "
+                       "from pmc_events").fetchall()
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = {}
+    for name, did, cn, v, d in rows:
+        per[(name, did)][cn].append(v)
+        dur[(name, did)] = d
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (name, did), cs in per.items():
+        if "moe::" not in name:
+            continue
+        for cn, vals in cs.items():  # GRBM: one clock for the chip; SQ: summed
+            agg[name][cn].append(max(vals) if cn.startswith("GRBM") else sum(vals))
+        agg[name]["_dur"].append(dur[(name, did)])
+    cmd = (f"rocprofv3 --kernel-include-regex 'moe::' --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+           f"SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -d /tmp/t_mfma -o {workload} -- python3 "
+           f"/root/repo/bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline")
+    lines = [f"# Clock and MFMA utilisation of the MoE kernels: {workload}", "",
+             f"source_sha256_16: {_source_hash()}", "",
+             "One rocprofv3 counter pass.  clock = GRBM_GUI_ACTIVE / duration;",
+             f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS} SIMDs x GRBM_GUI_ACTIVE),",
+             "the fraction of SIMD cycles in which the matrix core is busy.  At the",
+             "nominal 2.4 GHz a fully busy matrix core gives the 2.5 PFLOP/s bf16 peak.",
+             "Kernels under 100 us are listed without either figure: GRBM_GUI_ACTIVE",
+             "then counts more cycles than the kernel runs.", "",
+             "Commands (one MI355X):", "", "```", "cd /tmp && export TMPDIR=/tmp", cmd,
+             f"python3 /root/repo/bench.py --mfma-summary /tmp/t_mfma/{workload}_results.db "
+             f"--workload {workload}", "```", "",
+             "| kernel | dispatches | avg duration (us) | clock (GHz) | MFMA busy |",
+             "|---|---:|---:|---:|---:|"]
+    for name in sorted(agg):
+        d = agg[name]
+        us = sum(d["_dur"]) / len(d["_dur"]) / 1e3
+        g = sum(d.get("GRBM_GUI_ACTIVE", [0])) / max(len(d.get("GRBM_GUI_ACTIVE", [])), 1)
+        m = sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])) / max(
+            len(d.get("SQ_VALU_MFMA_BUSY_CYCLES", [])), 1)
+        if us < 100.0 or not g:  # the counter window outlasts short kernels
+            lines.append(f"| `{_short(name)}` | {len(d['_dur'])} | {us:.1f} | - | - |")
+            continue
+        lines.append(f"| `{_short(name)}` | {len(d['_dur'])} | {us:.1f} | "
+                     f"{g / (us * 1e3):.2f} | {100 * m / (SIMDS * g):.1f}% |")
+    return "\n".join(lines) + "\n"
+
+
 def _cpu_baseline(w, inp, target_s):
     """The float64 oracle on a sample of tokens: routing of every token (the
     capacity rule needs all of them) and the expert work of the sample."""
@@ -262,6 +319,9 @@ def main():
     args = _parse()
     if args.pmc_summary:
         print(_pmc_summary(*args.pmc_summary, args.workload))
+        return
+    if args.mfma_summary:
+        print(_mfma_summary(args.mfma_summary, args.workload))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
