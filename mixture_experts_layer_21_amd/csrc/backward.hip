@@ -21,7 +21,10 @@
 //   router     dh from dL/dw, the balance and z terms        (router_bwd_kernel)
 //   up dgrad   dz = [dg du] [W_g; W_u];  dx_router = dh W_r;  dx = gather-sum (dx_kernel)
 //   wgrad      dW_d = (w dout)^T act,  [dW_g; dW_u] = [dg du]^T x,  dW_r = dh^T x
+#include <algorithm>
+
 #include "common.hpp"
+#include "dma_gemm.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -44,14 +47,16 @@ struct BTile {
   int g, m0, m_end, nt, k0, k1;
 };
 
-// bn: output columns per tile (64 h for the paired gate/up tile, else 128).
+// BM rows and bn output columns per tile.  Every thread of the block calls
+// it (MROWS has barriers); the first 256 threads scan.
+template <int BM>
 __device__ bool bwd_tile(const BwdGemmParams& p, int bn, BTile& t, int* s_scan) {
   const int b = blockIdx.x;
   if (p.grouping == BWD_DENSE) {
-    const int ntn = (p.N + bn - 1) / bn, ntm = (p.M + BBM - 1) / BBM;
+    const int ntn = (p.N + bn - 1) / bn, ntm = (p.M + BM - 1) / BM;
     if (b >= ntn * ntm) return false;
     t.g = 0;
-    t.m0 = (b % ntm) * BBM;
+    t.m0 = (b % ntm) * BM;
     t.nt = b / ntm;
     t.m_end = p.M;
     t.k0 = 0;
@@ -59,12 +64,12 @@ __device__ bool bwd_tile(const BwdGemmParams& p, int bn, BTile& t, int* s_scan) 
     return true;
   }
   if (p.grouping == BWD_KRAGGED) {
-    const int ntn = (p.N + bn - 1) / bn, ntm = (p.M + BBM - 1) / BBM;
+    const int ntn = (p.N + bn - 1) / bn, ntm = (p.M + BM - 1) / BM;
     const int per = ntn * ntm;
     if (b >= per * p.G) return false;
     t.g = b / per;
     const int q = b % per;
-    t.m0 = (q % ntm) * BBM;
+    t.m0 = (q % ntm) * BM;
     t.nt = q / ntm;
     t.m_end = p.M;
     t.k0 = p.offsets[t.g];
@@ -75,17 +80,17 @@ __device__ bool bwd_tile(const BwdGemmParams& p, int bn, BTile& t, int* s_scan) 
   // per-group row-tile counts (G <= 256) finds the block's group.
   const int tid = threadIdx.x;
   int cnt = 0;
-  if (tid < p.G) cnt = (p.offsets[tid + 1] - p.offsets[tid] + BBM - 1) / BBM;
-  s_scan[tid] = cnt;
+  if (tid < p.G) cnt = (p.offsets[tid + 1] - p.offsets[tid] + BM - 1) / BM;
+  if (tid < BT) s_scan[tid] = cnt;
   __syncthreads();
   for (int d = 1; d < BT; d <<= 1) {
-    const int v = tid >= d ? s_scan[tid - d] : 0;
+    const int v = (tid < BT && tid >= d) ? s_scan[tid - d] : 0;
     __syncthreads();
-    s_scan[tid] += v;
+    if (tid < BT) s_scan[tid] += v;
     __syncthreads();
   }
   const int total = s_scan[BT - 1];
-  const int mt_bound = (p.max_rows + BBM - 1) / BBM + p.G;
+  const int mt_bound = (p.max_rows + BM - 1) / BM + p.G;
   const int ml = b % mt_bound;
   t.nt = b / mt_bound;
   if (ml >= total || t.nt * bn >= p.N) return false;  // uniform across the block
@@ -93,7 +98,7 @@ __device__ bool bwd_tile(const BwdGemmParams& p, int bn, BTile& t, int* s_scan) 
     const int hi = s_scan[tid], lo = hi - cnt;
     if (ml >= lo && ml < hi) {
       s_scan[BT] = tid;
-      s_scan[BT + 1] = p.offsets[tid] + (ml - lo) * BBM;
+      s_scan[BT + 1] = p.offsets[tid] + (ml - lo) * BM;
       s_scan[BT + 2] = p.offsets[tid + 1];
     }
   }
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BBN * BBK];
   __shared__ int s_scan[BT + 4];
   BTile t;
-  if (!bwd_tile(p, EPI == BWD_EPI_GATEUP_SAVE ? BBN / 2 : BBN, t, s_scan)) return;
+  if (!bwd_tile<BBM>(p, EPI == BWD_EPI_GATEUP_SAVE ? BBN / 2 : BBN, t, s_scan)) return;
   const int tid = threadIdx.x;
   const bool kr = p.grouping == BWD_KRAGGED;
 
@@ -267,10 +272,169 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
   }
 }
 
-// 64x64 tiled transpose through LDS (see TransposeParams).
+// The same GEMM on the forward's 256x256 direct-to-LDS main loop: 512
+// threads, BK = 64, two LDS stages, operands fetched straight into the
+// swizzled LDS tiles by buffer loads with 32-bit offsets.  With the paired
+// gate/up tile the B tile is 128 gate rows then the same 128 up rows.
+template <int EPI>
+__global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
+  constexpr bool PAIRED = EPI == BWD_EPI_GATEUP_SAVE;
+  using C = dma::DmaCfg<256, 256, 64, 2, 2, 8, PAIRED>;
+  constexpr int BM = 256, BK = 64, KCH = C::KCH, MI = C::MI, NI = C::NI, NB = C::NB;
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[256 * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[256 * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX[8];  // unused stages
+  __shared__ int s_scan[BT + 4];
+  __shared__ float s_red[2 * 4 * 128];
+  BTile t;
+  if (!bwd_tile<BM>(p, C::BN, t, s_scan)) return;
+  const bool kr = p.grouping == BWD_KRAGGED;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, (int)p.a_bytes, 0x00020000);
+  const long long bg = kr ? 0 : (long long)t.g * p.b_gstride;
+  const __amdgpu_buffer_rsrc_t rG =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + bg), 0, (int)p.b_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rU =
+      PAIRED ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.B2 + bg), 0, (int)p.b_bytes, 0x00020000)
+             : rG;
+  uint32_t a_off[C::A_LD];
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i) {
+    const int slot = (wave + C::NW * i) * 64 + lane;
+    const int r = slot / KCH, lc = (slot % KCH) ^ dma::swz_k<KCH>(r);
+    int m = t.m0 + r;
+    if (m >= t.m_end) m = t.m0;
+    const long long row = kr ? (long long)m * p.lda + t.k0
+                             : (long long)(p.gather ? p.gather[m] / p.gdiv : m) * p.lda;
+    a_off[i] = (uint32_t)(row * 2) + (uint32_t)lc * 16u;
+  }
+  uint32_t b_off[C::B_LD];
+#pragma unroll
+  for (int i = 0; i < C::B_LD; ++i) {
+    const int slot = (wave + C::NW * i) * 64 + lane;
+    const int r = slot / KCH, lc = (slot % KCH) ^ dma::swz_k<KCH>(r);
+    int n = t.nt * C::BN + (PAIRED ? r % C::BN : r);
+    if (n >= p.N) n = 0;
+    const long long row = (long long)n * p.ldb + (kr ? t.k0 : 0);
+    b_off[i] = (uint32_t)(row * 2) + (uint32_t)lc * 16u;
+  }
+  const dma::DmaLoads<C, PAIRED> ld{rA, rG, rU, a_off, b_off, wave};
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int lr = lane & 31, lk = lane >> 5;
+  f32x16 acc[NB][MI][NI];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nb][mi][ni][i] = 0.f;
+  const int nk = (t.k1 - t.k0) / BK;
+  // (Device pass only: the host pass of hipcc rejects this call's template
+  // deduction; kernel bodies are never run on the host.)
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (nk > 0)
+    dma::dma_mainloop<C, PAIRED, false>(ld, nk, MI, wm, wn, lr, lk, acc, sA0, sA1, sX, sX, sB0,
+                                        sB1, sX, sX);
+#endif
+
+  // Epilogue: element i of accumulator (nb, mi, ni) of lane l is row
+  // wm*WM + mi*32 + 8*(i/4) + 4*(l/32) + (i%4), column wn*WN + ni*32 + l%32.
+  const int n_base = t.nt * C::BN + wn * C::WN;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rloc = wm * C::WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
+      const int m = t.m0 + rloc;
+      const bool row_ok = m < t.m_end;
+      if (EPI == BWD_EPI_F32) {
+        if (!row_ok) continue;
+        float* base = m >= p.c_split ? p.C2 : p.C;
+        const long long row = m >= p.c_split ? m - p.c_split : m;
+        base += (long long)t.g * p.c_gstride + row * p.ldc;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int n = n_base + ni * 32 + lr;
+          if (n < p.N) base[n] = acc[0][mi][ni][i];
+        }
+      } else if (EPI == BWD_EPI_GATEUP_SAVE) {
+        if (!row_ok) continue;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int h = n_base + ni * 32 + lr;
+          if (h >= p.N) continue;
+          const float g = acc[0][mi][ni][i], u = acc[NB - 1][mi][ni][i];
+          float gc = g, uc = u, mg = 1.f, mu = 1.f;
+          if (p.limit > 0.f) {
+            gc = fminf(fmaxf(g, -p.limit), p.limit);
+            uc = fminf(fmaxf(u, -p.limit), p.limit);
+            mg = fabsf(g) < p.limit ? 1.f : 0.f;
+            mu = fabsf(u) < p.limit ? 1.f : 0.f;
+          }
+          const float s = sigm(gc);
+          const long long o = (long long)m * p.ldh + h;
+          p.act[o] = f32_to_bf16_bits(gc * s * uc);
+          p.p1[o] = f32_to_bf16_bits(mg * uc * (s + gc * s * (1.f - s)));
+          p.p2[o] = f32_to_bf16_bits(mu * gc * s);
+        }
+      } else {  // BWD_EPI_DOWN_DGRAD
+        float w = 1.f;
+        if (row_ok && p.gate_w) w = p.gate_w[p.r2a[m]];
+        float rs = 0.f;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int h = n_base + ni * 32 + lr;
+          if (!row_ok || h >= p.N) continue;
+          const long long o = (long long)m * p.ldh + h;
+          const float da = acc[0][mi][ni][i];
+          rs += bf16_bits_to_f32(p.act[o]) * da;
+          const long long od = (long long)m * p.lddgu + h;
+          p.dgu[od] = f32_to_bf16_bits(w * da * bf16_bits_to_f32(p.p1[o]));
+          p.dgu[od + p.H] = f32_to_bf16_bits(w * da * bf16_bits_to_f32(p.p2[o]));
+        }
+        if (p.dw_part) {
+#pragma unroll
+          for (int off = 16; off >= 1; off >>= 1) rs += __shfl_xor(rs, off);
+          if (lr == 0) s_red[(wm * C::WGN + wn) * 128 + (rloc - wm * C::WM)] = rs;
+        }
+      }
+    }
+  }
+  if (EPI == BWD_EPI_DOWN_DGRAD && p.dw_part) {
+    // the row's sums over this tile's columns: the WGN waves in order
+    __syncthreads();
+    if (tid < BM) {
+      const int wmr = tid / C::WM, rr = tid % C::WM, m = t.m0 + tid;
+      if (m < t.m_end) {
+        float v = s_red[(wmr * C::WGN) * 128 + rr];
+#pragma unroll
+        for (int q = 1; q < C::WGN; ++q) v += s_red[(wmr * C::WGN + q) * 128 + rr];
+        p.dw_part[(long long)m * p.npart + t.nt] = v;
+      }
+    }
+  }
+}
+
+bool bwd_dma_fits(const BwdGemmParams& p) {
+  const long long lim = 1ll << 31;
+  return p.a_bytes > 0 && p.b_bytes > 0 && p.a_bytes < lim && p.b_bytes < lim;
+}
+
+// 64x64 tiled transpose through LDS (see TransposeParams), 16-byte global
+// accesses on both sides (every row stride and column offset is a multiple
+// of 8 elements).  With skip_rows, a batch b whose group has no rows
+// (skip_rows[b+1] == skip_rows[b]) is left untouched: its weights feed no
+// gradient.
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeParams p) {
-  __shared__ float tile[64][65];
+  __shared__ uint16_t tile[64][66];
   const int b = blockIdx.z;
+  if (p.skip_rows && p.skip_rows[b + 1] == p.skip_rows[b]) return;
   const int jc0 = blockIdx.x * 64;           // first destination column (padded space)
   const int c0 = blockIdx.y * 64;            // first source column
   if (jc0 >= p.out_cols) return;
@@ -288,25 +452,49 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeParams p) {
       j_end = p.offsets[g + 1];
     }
   }
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int jj = ty; jj < 64; jj += 4) {
-    const int j = j0 + jj, c = c0 + tx;
-    float v = 0.f;
+  const int tid = threadIdx.x;
+  // load: 64 source rows x 64 columns; a thread takes 16-byte chunks
+  const int per = p.src_f32 ? 4 : 8;           // elements per chunk
+  const int cpr = 64 / per;                    // chunks per row
+  for (int q = tid; q < 64 * cpr; q += 256) {
+    const int jj = q / cpr, cc = (q % cpr) * per;
+    const int j = j0 + jj, c = c0 + cc;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (j < j_end && c < p.cols) {
       const int src_row = p.gather ? p.gather[j] / p.gdiv : j;
       const long long o = (long long)b * p.src_bstride + (long long)src_row * p.ld_src + c;
-      v = p.src_f32 ? static_cast<const float*>(p.src)[o]
-                    : bf16_bits_to_f32(static_cast<const uint16_t*>(p.src)[o]);
-      if (p.scale) v *= p.scale[p.scale_idx ? p.scale_idx[j] : j];
+      if (p.src_f32) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.src) + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = x[e];
+      } else {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.src) + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = __uint_as_float(x[e] << 16);
+          v[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
+        }
+      }
+      if (p.scale) {
+        const float sc = p.scale[p.scale_idx ? p.scale_idx[j] : j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= sc;
+      }
     }
-    tile[jj][tx] = v;
+    for (int e = 0; e < per; ++e) tile[jj][cc + e] = f32_to_bf16_bits(v[e]);
   }
   __syncthreads();
-  for (int cc = ty; cc < 64; cc += 4) {
-    const int c = c0 + cc, jc = jc0 + tx;
-    if (c < p.cols && jc < p.out_cols)
-      p.dst[(long long)b * p.dst_bstride + (long long)c * p.ld_dst + p.dst_col0 + jc] =
-          f32_to_bf16_bits(tile[tx][cc]);
+  // store: 64 destination rows (source columns) x 64 columns, 8 per chunk
+  for (int q = tid; q < 64 * 8; q += 256) {
+    const int cc = q / 8, jj = (q % 8) * 8;
+    const int c = c0 + cc, jc = jc0 + jj;
+    if (c >= p.cols || jc >= p.out_cols) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[jj + 2 * e][cc] | ((uint32_t)tile[jj + 2 * e + 1][cc] << 16);
+    *reinterpret_cast<u32x4*>(p.dst + (long long)b * p.dst_bstride + (long long)c * p.ld_dst +
+                              p.dst_col0 + jc) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -472,7 +660,36 @@ __global__ __launch_bounds__(256) void dx_kernel(DxParams p) {
 
 }  // namespace
 
+int bwd_gemm_col_tile(const BwdGemmParams& p) {
+  const int full = bwd_dma_fits(p) ? 256 : BBN;
+  return p.epilogue == BWD_EPI_GATEUP_SAVE ? full / 2 : full;
+}
+
 hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s) {
+  if (bwd_dma_fits(p)) {
+    const int bn = bwd_gemm_col_tile(p), nN = (p.N + bn - 1) / bn;
+    long long blocks;
+    if (p.grouping == BWD_DENSE)
+      blocks = (long long)nN * ((p.M + 255) / 256);
+    else if (p.grouping == BWD_KRAGGED)
+      blocks = (long long)nN * ((p.M + 255) / 256) * p.G;
+    else
+      blocks = (long long)nN * ((p.max_rows + 255) / 256 + p.G);
+    if (blocks <= 0) return hipSuccess;
+    switch (p.epilogue) {
+      case BWD_EPI_F32:
+        hipLaunchKernelGGL(bwd_dma_kernel<BWD_EPI_F32>, dim3((unsigned)blocks), dim3(512), 0, s, p);
+        break;
+      case BWD_EPI_GATEUP_SAVE:
+        hipLaunchKernelGGL(bwd_dma_kernel<BWD_EPI_GATEUP_SAVE>, dim3((unsigned)blocks), dim3(512),
+                           0, s, p);
+        break;
+      default:
+        hipLaunchKernelGGL(bwd_dma_kernel<BWD_EPI_DOWN_DGRAD>, dim3((unsigned)blocks), dim3(512),
+                           0, s, p);
+    }
+    return hipGetLastError();
+  }
   long long blocks;
   const int nN = p.epilogue == BWD_EPI_GATEUP_SAVE ? (p.N + BBN / 2 - 1) / (BBN / 2)
                                                   : (p.N + BBN - 1) / BBN;

@@ -26,10 +26,13 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "dma_gemm.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
+
+using namespace dma;
 
 constexpr int NTHREADS = 256;
 
@@ -451,257 +454,6 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmPar
       static_cast<uint16_t*>(p.y)[(size_t)grow * N + col] = f32_to_bf16_bits(gw * a0);
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Large-tile bf16 kernel: 512 threads (8 waves, two per SIMD), operands moved
-// global -> LDS by buffer_load ... lds (no register staging), an S-stage LDS
-// ring (loads for k-step kt+S-1 are in flight while kt is multiplied), and
-// MFMA fragments double-buffered in registers.
-//
-// Each 1 KB wave load fills 64 consecutive 16-byte LDS slots (slot = base +
-// lane*16); the lane fetches the global chunk that the swizzled layout puts in
-// that slot, so the fragment reads stay bank-conflict free.  Every stage lives
-// in its own LDS array and stage indices are compile-time constants, so the
-// wait for stage kt is an exact vmcnt and later stages stay in flight.
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-
-// Swizzle of 16-byte chunk c in row r for KCH chunks per row.  The LDS serves
-// a 16-byte read for 16 lanes per cycle (64 four-byte banks); these XOR
-// patterns keep the 32-row fragment reads conflict-free, as measured with
-// SQ_LDS_BANK_CONFLICT on gfx950 (plain layouts conflict 5-12x per read).
-template <int KCH>
-__device__ __forceinline__ int swz_k(int r) {
-  if constexpr (KCH == 8) return (r & 7) ^ ((r >> 3) & 1);
-  else return (r >> 2) & 3;
-}
-
-// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
-// vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier without the release fence of __syncthreads(): the fence
-// would wait for every load in flight, including later stages.  The wave's
-// own stage is already complete (wait_vmcnt), LDS reads of the previous stage
-// have returned (their MFMAs consumed them), and the empty asm statements keep
-// the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int BM, int BNB, int BK_, int S_, int WGM, int NWV, bool GATEUP>
-struct DmaCfg {
-  static constexpr int NT = 64 * NWV, NW = NWV, WGN = NW / WGM;
-  static constexpr int BK = BK_, KCH = BK / 8, S = S_;
-  static constexpr int A_LD = BM * KCH / 64 / NW;   // 1 KB wave loads per stage
-  static constexpr int B_LD = BNB * KCH / 64 / NW;
-  static constexpr int LPS = A_LD + B_LD;            // loads per thread per stage
-  static constexpr int WM = BM / WGM;
-  static constexpr int NB = GATEUP ? 2 : 1;
-  static constexpr int BN = BNB / NB;                // output columns of the tile
-  static constexpr int WN = BN / WGN;                // output columns per wave
-  static constexpr int MI = WM / 32, NI = WN / 32;
-  static_assert(A_LD >= 1 && B_LD >= 1 && MI >= 1 && NI >= 1, "tile shape");
-  static_assert(BM * KCH % (64 * NW) == 0 && BNB * KCH % (64 * NW) == 0, "tile shape");
-  static_assert(S_ >= 2 && S_ <= 4 && (S_ - 2) * LPS < 64, "stages");
-  static_assert(NT >= NTHREADS, "the tile decode scans the expert offsets with 256 threads");
-};
-
-template <class C, bool GATEUP>
-struct DmaLoads {
-  __amdgpu_buffer_rsrc_t rA, rG, rU;
-  const uint32_t* a_off;
-  const uint32_t* b_off;
-  int wave;
-};
-
-// Issue all LPS global -> LDS loads (A loads first, then B) of k-step kt into
-// one stage's buffers.  (A macro: the host pass of hipcc rejects this body as
-// a device function template called from the k-loop.)
-#define MOE_DMA_ISSUE(C, GATEUP, ld, sa, sb, kt)                                             \
-  do {                                                                                      \
-    const int soff_ = (kt) * C::BK * 2;                                                     \
-    _Pragma("unroll") for (int i_ = 0; i_ < C::A_LD; ++i_)                                  \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                           \
-            (ld).rA, (lds_void_t*)((sa) + ((ld).wave + C::NW * i_) * 512), 16,              \
-            (ld).a_off[i_], soff_, 0, 0);                                                   \
-    _Pragma("unroll") for (int i_ = 0; i_ < C::B_LD; ++i_) {                                \
-      const int blk_ = (ld).wave + C::NW * i_;                                              \
-      const bool up_ = (GATEUP) && blk_ * 64 >= C::BN * C::KCH;                             \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(up_ ? (ld).rU : (ld).rG,                     \
-                                               (lds_void_t*)((sb) + blk_ * 512), 16,        \
-                                               (ld).b_off[i_], soff_, 0, 0);                \
-    }                                                                                       \
-  } while (0)
-
-// Multiply one stage (BK/16 k-steps of MI x NB*NI 32x32x16 MFMAs per wave)
-// after issuing the loads of a later k-step into another stage's buffers
-// (spreading them over the k-steps measured slower on gfx950).
-template <class C, bool PARTIAL>
-__device__ __forceinline__ void dma_mfmas(const bf16x8 (&af)[C::MI], const bf16x8 (&bfr)[C::NB][C::NI],
-                                          f32x16 (&acc)[C::NB][C::MI][C::NI], int mi_n) {
-#pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-    for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi) {
-        if (PARTIAL && mi >= mi_n) continue;
-        acc[nb][mi][ni] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[nb][ni], acc[nb][mi][ni], 0, 0, 0);
-      }
-}
-
-// s_waitcnt lgkmcnt(0) with the other counters left open.
-__device__ __forceinline__ void wait_lgkmcnt0() {
-  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
-}
-
-// With MOE_DEFER the MFMAs of a stage's last k16 step run after the next
-// stage's barrier (their fragments are already in registers), so they cover
-// the latency of the next stage's first fragment reads.
-#ifndef MOE_DEFER
-#define MOE_DEFER 1
-#endif
-
-template <class C, bool GATEUP, bool PARTIAL>
-__device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* sb, int wm,
-                                            int wn, int lr, int lk,
-                                            f32x16 (&acc)[C::NB][C::MI][C::NI],
-                                            const DmaLoads<C, GATEUP>& ld, uint16_t* na,
-                                            uint16_t* nb_, int kt_next, int mi_n,
-                                            bf16x8 (&af)[2][C::MI],
-                                            bf16x8 (&bfr)[2][C::NB][C::NI]) {
-  constexpr int BK = C::BK, KCH = C::KCH, KS = BK / 16;
-  static_assert(KS % 2 == 0, "the deferred k16 step uses fragment buffer 1");
-  constexpr int NRD = C::MI + C::NB * C::NI;          // fragment reads per k16 step
-  constexpr int NMF = C::MI * C::NB * C::NI;          // MFMAs per k16 step
-  constexpr int NLD = C::LPS;                         // all loads before the first k16 step
-  auto frags = [&](int kk, int buf) {
-    const int ch = kk * 2 + lk;
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
-      if (PARTIAL && mi >= mi_n) continue;
-      const int r = wm * C::WM + mi * 32 + lr;
-      af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + r * BK + (ch ^ swz_k<KCH>(r)) * 8);
-    }
-    if (PARTIAL && mi_n == 0) return;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int ni = 0; ni < C::NI; ++ni) {
-        const int r = nb * C::BN + wn * C::WN + ni * 32 + lr;
-        bfr[buf][nb][ni] =
-            *reinterpret_cast<const bf16x8*>(sb + r * BK + (ch ^ swz_k<KCH>(r)) * 8);
-      }
-  };
-  frags(0, 0);
-  if (MOE_DEFER) dma_mfmas<C, PARTIAL>(af[1], bfr[1], acc, mi_n);
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    constexpr int LPS = C::LPS;
-    const int i1 = (kk + 1) * NLD < LPS ? (kk + 1) * NLD : LPS;
-    {  // loads [kk*NLD, i1) of k-step kt_next (A loads first, then B)
-      const int i0 = kk * NLD, soff = kt_next * BK * 2;
-#pragma unroll
-      for (int i = 0; i < C::A_LD; ++i)
-        if (i >= i0 && i < i1)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              ld.rA, (lds_void_t*)(na + (ld.wave + C::NW * i) * 512), 16, ld.a_off[i], soff, 0,
-              0);
-#pragma unroll
-      for (int i = 0; i < C::B_LD; ++i) {
-        if (C::A_LD + i < i0 || C::A_LD + i >= i1) continue;
-        const int blk = ld.wave + C::NW * i;
-        const bool up = GATEUP && blk * 64 >= C::BN * C::KCH;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? ld.rU : ld.rG,
-                                                 (lds_void_t*)(nb_ + blk * 512), 16,
-                                                 ld.b_off[i], soff, 0, 0);
-      }
-    }
-    // Fragments of the next k16 step are read while this step's MFMAs run.
-    if (kk + 1 < KS) frags(kk + 1, (kk + 1) & 1);
-    if (MOE_DEFER && kk + 1 == KS) {
-      wait_lgkmcnt0();  // the deferred fragments are in registers before the barrier
-      continue;
-    }
-    dma_mfmas<C, PARTIAL>(af[kk & 1], bfr[kk & 1], acc, mi_n);
-    if (PARTIAL) continue;  // no fixed instruction pattern to schedule
-    // Scheduling hint: two MFMAs, then all fragment reads of the next k16
-    // step, then the remaining MFMAs (measured 2-3% ahead of a 1:1
-    // interleave and 10% ahead of no hint on the 256x256 tile).
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    if (kk + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF - 2, 0);
-  }
-}
-
-// The pipelined k-loop.  The stage buffers come in as __restrict__ pointers:
-// once this is inlined, every LDS access and every LDS-bound load carries
-// scoped no-alias information, so the compiler's own wait before a fragment
-// read covers only the load into that same buffer (issued S-1 stages earlier)
-// instead of every load in flight.
-template <class C, bool GATEUP, bool PARTIAL>
-__device__ __forceinline__ void dma_mainloop(
-    const DmaLoads<C, GATEUP>& ld, int nk, int mi_n, int wm, int wn, int lr, int lk,
-    f32x16 (&acc)[C::NB][C::MI][C::NI], uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
-    uint16_t* __restrict__ a2, uint16_t* __restrict__ a3, uint16_t* __restrict__ b0,
-    uint16_t* __restrict__ b1, uint16_t* __restrict__ b2, uint16_t* __restrict__ b3) {
-  constexpr int S = C::S;
-  // Fragment buffers; buffer 1 starts at zero so that the first stage's
-  // deferred MFMAs add nothing.
-  bf16x8 af[2][C::MI], bfr[2][C::NB][C::NI];
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi) af[1][mi] = bf16x8{};
-#pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-    for (int ni = 0; ni < C::NI; ++ni) bfr[1][nb][ni] = bf16x8{};
-  // Prologue: stages 0 .. S-2 in flight.
-  MOE_DMA_ISSUE(C, GATEUP, ld, a0, b0, 0);
-  if (S > 2) MOE_DMA_ISSUE(C, GATEUP, ld, a1, b1, min(1, nk - 1));
-  if (S > 3) MOE_DMA_ISSUE(C, GATEUP, ld, a2, b2, min(2, nk - 1));
-
-  // Every step issues one stage of loads, so exactly S-2 stages are in flight
-  // behind the one being waited for.  Past the end the loads repeat the last
-  // k-step into a buffer nobody reads again, and steps past the end skip the
-  // multiply; keeping the issue unconditional keeps the compiler's view of
-  // the in-flight LDS writes precise.
-#define MOE_SA(i) ((i) == 0 ? a0 : (i) == 1 ? a1 : (i) == 2 ? a2 : a3)
-#define MOE_SB(i) ((i) == 0 ? b0 : (i) == 1 ? b1 : (i) == 2 ? b2 : b3)
-#define MOE_STEP(SI)                                                                        \
-  if constexpr (SI < S) {                                                                   \
-    const int kt = kb + SI;                                                                 \
-    wait_vmcnt<(S - 2) * C::LPS>();                                                         \
-    stage_barrier();                                                                        \
-    if (kt < nk)                                                                            \
-      dma_compute<C, GATEUP, PARTIAL>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc, ld,      \
-                                      MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),   \
-                                      min(kt + S - 1, nk - 1), mi_n, af, bfr);              \
-    else                                                                                    \
-      MOE_DMA_ISSUE(C, GATEUP, ld, MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),     \
-                    nk - 1);                                                                \
-  }
-  for (int kb = 0; kb < nk; kb += S) {
-    MOE_STEP(0)
-    MOE_STEP(1)
-    MOE_STEP(2)
-    MOE_STEP(3)
-  }
-#undef MOE_STEP
-#undef MOE_SA
-#undef MOE_SB
-  if (MOE_DEFER && nk > 0) dma_mfmas<C, PARTIAL>(af[1], bfr[1], acc, mi_n);
-  // No LDS write may still be in flight when the block ends.
-  wait_vmcnt<0>();
 }
 
 // Epilogue of a finished tile (32x32 accumulator layout: element i of lane l

@@ -151,9 +151,18 @@ struct BwdGemmParams {
   int H;
   float* dw_part;
   int npart;
+  // Byte extents of A and of one group's B (the whole B when KRAGGED): the
+  // 256x256 direct-to-LDS path addresses them with 32-bit buffer offsets.
+  long long a_bytes, b_bytes;
 };
 
-// dst[c][col(j)] = scale(j) * src[row(j)][c]: a tiled transpose.  col(j) = j,
+// Output columns per tile of the backward GEMM that launch_bwd_gemm picks for
+// p (256 on the direct-to-LDS path, 128 otherwise; half that for the paired
+// gate/up recompute): the DOWN_DGRAD partials have ceil(N / this) columns.
+int bwd_gemm_col_tile(const BwdGemmParams& p);
+
+// dst[c][col(j)] = scale(j) * src[row(j)][c]: a tiled transpose.  Row
+// strides, column offsets and the column counts are multiples of 8 elements.  col(j) = j,
 // or, with offsets/padoff (ragged groups), group g's rows offsets[g].. go to
 // columns padoff[g].. and the columns up to padoff[g+1] are zero.
 struct TransposeParams {
@@ -173,6 +182,7 @@ struct TransposeParams {
   long long ld_dst, dst_bstride;
   int dst_col0;              // first destination column
   int batch;
+  const int32_t* skip_rows;  // [batch+1] offsets or null: batches with no rows are skipped
 };
 
 struct RouterBwdParams {

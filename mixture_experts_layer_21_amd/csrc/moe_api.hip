@@ -735,7 +735,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   auto transpose = [&](int rows, int cols, const void* src, bool src_f32, long long ld_src,
                        long long src_b, int out_cols, uint16_t* dst, long long ld_dst,
                        long long dst_b, int col0, int batch, const int32_t* gather,
-                       const float* scale, const int32_t* scale_idx, bool ragged) {
+                       const float* scale, const int32_t* scale_idx, bool ragged,
+                       const int32_t* skip_rows = nullptr) {
     moe::TransposeParams t{};
     t.rows = rows;
     t.cols = cols;
@@ -756,14 +757,16 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     t.dst_bstride = dst_b;
     t.dst_col0 = col0;
     t.batch = batch;
+    t.skip_rows = skip_rows;
     return hip_ok(moe::launch_transpose(t, stream), "transpose kernel");
   };
+  // (experts without rows are skipped: their weights feed no gradient)
   MOE_TRY(transpose(D, H, w_down, false, H, (long long)D * H, D, u16(B.wdT), D,
-                    (long long)H * D, 0, E, nullptr, nullptr, nullptr, false));
+                    (long long)H * D, 0, E, nullptr, nullptr, nullptr, false, offsets));
   MOE_TRY(transpose(H, D, w_gate, false, D, (long long)H * D, H, u16(B.wguT), 2 * H,
-                    (long long)D * 2 * H, 0, E, nullptr, nullptr, nullptr, false));
+                    (long long)D * 2 * H, 0, E, nullptr, nullptr, nullptr, false, offsets));
   MOE_TRY(transpose(H, D, w_up, false, D, (long long)H * D, H, u16(B.wguT), 2 * H,
-                    (long long)D * 2 * H, H, E, nullptr, nullptr, nullptr, false));
+                    (long long)D * 2 * H, H, E, nullptr, nullptr, nullptr, false, offsets));
   MOE_TRY(transpose(E, D, w_router, cfg->router_dtype == MOE_F32, D, 0, B.Epad, u16(B.wrT),
                     B.Epad, 0, 0, 1, nullptr, nullptr, nullptr, false));
   if (sh) {
@@ -779,6 +782,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     return hip_ok(moe::launch_bwd_gemm(g, stream), what);
   };
   const int kNoSplit = 0x7fffffff;
+  int npart = B.npart;  // column tiles of the down dgrad (its partials' row stride)
   // 4. recompute gate/up: act, p1, p2 of every kept row
   {
     moe::BwdGemmParams g{};
@@ -802,6 +806,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     g.p2 = u16(B.p2);
     g.ldh = H;
     g.limit = cfg->swiglu_limit;
+    g.a_bytes = 2ll * T * D;
+    g.b_bytes = 2ll * H * D;
     MOE_TRY(gemm(g, "recompute gate/up"));
     // 5. down dgrad with the gate weights: dg, du and dL/dw partials
     moe::BwdGemmParams d{};
@@ -829,7 +835,10 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     d.lddgu = 2 * H;
     d.H = H;
     d.dw_part = f32(B.part);
-    d.npart = B.npart;
+    d.a_bytes = 2ll * T * D;
+    d.b_bytes = 2ll * H * D;
+    npart = (H + moe::bwd_gemm_col_tile(d) - 1) / moe::bwd_gemm_col_tile(d);
+    d.npart = npart;
     MOE_TRY(gemm(d, "down dgrad"));
   }
   // 6. router: dL/dh
@@ -848,7 +857,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     r.ids = expert_ids;
     r.a2r = a2r;
     r.dw_part = f32(B.part);
-    r.npart = B.npart;
+    r.npart = npart;
     r.counts = counts;
     r.dh = u16(B.dh);
     r.dgw = d_gate_w;
@@ -872,6 +881,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     g.C = f32(B.dz);
     g.ldc = D;
     g.c_split = kNoSplit;
+    g.a_bytes = 2ll * R * 2 * H;
+    g.b_bytes = 2ll * D * 2 * H;
     MOE_TRY(gemm(g, "gate/up dgrad"));
     moe::BwdGemmParams r{};
     r.grouping = moe::BWD_DENSE;
@@ -887,6 +898,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     r.C = f32(B.dxr);
     r.ldc = D;
     r.c_split = kNoSplit;
+    r.a_bytes = 2ll * T * B.Epad;
+    r.b_bytes = 2ll * D * B.Epad;
     MOE_TRY(gemm(r, "router dgrad"));
   }
   if (sh) {
@@ -907,6 +920,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     g.p2 = u16(B.sp2);
     g.ldh = Hs;
     g.limit = cfg->swiglu_limit;
+    g.a_bytes = 2ll * T * D;
+    g.b_bytes = 2ll * Hs * D;
     MOE_TRY(gemm(g, "shared recompute"));
     moe::BwdGemmParams d{};
     d.grouping = moe::BWD_DENSE;
@@ -926,6 +941,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     d.dgu = u16(B.sdgu);
     d.lddgu = 2 * Hs;
     d.H = Hs;
+    d.a_bytes = 2ll * T * D;
+    d.b_bytes = 2ll * Hs * D;
     MOE_TRY(gemm(d, "shared down dgrad"));
     moe::BwdGemmParams z{};
     z.grouping = moe::BWD_DENSE;
@@ -941,6 +958,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     z.C = f32(B.sdz);
     z.ldc = D;
     z.c_split = kNoSplit;
+    z.a_bytes = 2ll * T * 2 * Hs;
+    z.b_bytes = 2ll * D * 2 * Hs;
     MOE_TRY(gemm(z, "shared gate/up dgrad"));
   }
   {
@@ -977,6 +996,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     g.ldc = H;
     g.c_gstride = (long long)D * H;
     g.c_split = kNoSplit;
+    g.a_bytes = 2ll * D * B.Kpad;
+    g.b_bytes = 2ll * H * B.Kpad;
     MOE_TRY(gemm(g, "down wgrad"));
     moe::BwdGemmParams u{};
     u.grouping = moe::BWD_KRAGGED;
@@ -994,6 +1015,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     u.ldc = D;
     u.c_gstride = (long long)H * D;
     u.c_split = H;
+    u.a_bytes = 2ll * 2 * H * B.Kpad;
+    u.b_bytes = 2ll * D * B.Kpad;
     MOE_TRY(gemm(u, "gate/up wgrad"));
     moe::BwdGemmParams r{};
     r.grouping = moe::BWD_DENSE;
@@ -1009,6 +1032,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     r.C = dw_router;
     r.ldc = D;
     r.c_split = kNoSplit;
+    r.a_bytes = 2ll * B.Epad * B.Tpad;
+    r.b_bytes = 2ll * D * B.Tpad;
     MOE_TRY(gemm(r, "router wgrad"));
   }
   if (sh) {
@@ -1032,6 +1057,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     g.C = dws_down;
     g.ldc = Hs;
     g.c_split = kNoSplit;
+    g.a_bytes = 2ll * D * B.Tpad;
+    g.b_bytes = 2ll * Hs * B.Tpad;
     MOE_TRY(gemm(g, "shared down wgrad"));
     moe::BwdGemmParams u{};
     u.grouping = moe::BWD_DENSE;
@@ -1048,6 +1075,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     u.C2 = dws_up;
     u.ldc = D;
     u.c_split = Hs;
+    u.a_bytes = 2ll * 2 * Hs * B.Tpad;
+    u.b_bytes = 2ll * D * B.Tpad;
     MOE_TRY(gemm(u, "shared gate/up wgrad"));
   }
   return ok();
