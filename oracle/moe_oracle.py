@@ -76,7 +76,8 @@ __all__ = [
     "NEAR_TIE", "router_logits", "softmax", "sigmoid", "softplus", "logsumexp",
     "route", "capacity", "first_within_capacity", "permutation",
     "swiglu_ffn", "expert_outputs", "shared_expert", "combine", "forward", "update_bias",
-    "round_to_bf16", "rms_norm", "loss", "backward", "swiglu_ffn_backward",
+    "round_to_bf16", "rms_norm", "loss", "backward", "router_backward",
+    "swiglu_ffn_backward",
     "brute_force_forward", "all_experts_then_mask",
 ]
 
@@ -512,6 +513,55 @@ def swiglu_ffn_backward(z, w_gate, w_up, w_down, dF, limit=0.0):
     return dz, dgc.T @ z, duc.T @ z, dWd, F
 
 
+def router_backward(r, d_gate_w, *, top_k, score="softmax", renormalize=True,
+                    route_scale=1.0, aux_coef=(0.0, 0.0), tokens=None):
+    """dL/dh [T,E] (or the rows of ``tokens``) of ``loss`` for the routing
+    ``r`` of ``route`` and dL/dw per slot ``d_gate_w`` (zero for dropped
+    slots): through the kept gate weights (renormalised or raw, times
+    route_scale), P_e of the balance term (f held constant) and z."""
+    # router: gate weights -> chosen scores
+    ids = r["ids"]
+    T, k = ids.shape
+    E = r["logits"].shape[1]
+    sc, h = r["scores"], r["logits"]
+    valid = ids[:, 0] >= 0
+    dsc = np.zeros((T, E))
+    rows = np.nonzero(valid)[0] if tokens is None else [t for t in tokens if valid[t]]
+    for t in rows:  # (d_gate_w is read on these rows only)
+        c = sc[t, ids[t]]
+        if renormalize:
+            S = c.sum()
+            dc = route_scale / S * (d_gate_w[t] - np.sum(d_gate_w[t] * c) / S)
+        else:
+            dc = route_scale * d_gate_w[t]
+        np.add.at(dsc[t], ids[t], dc)
+    # balance = E * sum_e f_e P_e, P_e = mean over valid tokens of q_te
+    alpha, beta = aux_coef
+    n_valid = int(valid.sum())
+    if n_valid and alpha:
+        f_e = r["counts"] / float(n_valid * top_k)
+        dq = np.where(valid[:, None], alpha * E * f_e[None, :] / n_valid, 0.0)
+        if score == "softmax":
+            dsc += dq
+        else:  # q = s / sum_e s
+            ssum = sc.sum(axis=1, keepdims=True)
+            q = sc / ssum
+            dsc += (dq - np.sum(dq * q, axis=1, keepdims=True)) / ssum
+    # scores -> logits
+    if score == "softmax":
+        dh = sc * (dsc - np.sum(dsc * sc, axis=1, keepdims=True))
+    elif score == "sigmoid":
+        dh = dsc * sc * (1.0 - sc)
+    else:  # s = sqrt(softplus(h)): ds/dh = sigmoid(h) / (2 s)
+        dh = dsc * sigmoid(h) / (2.0 * sc)
+    # z = mean over valid tokens of lse(h_t)^2
+    if n_valid and beta:
+        lse = logsumexp(h)
+        dh += np.where(valid[:, None], beta * 2.0 * lse[:, None] * softmax(h) / n_valid, 0.0)
+    dh = np.where(valid[:, None], dh, 0.0)
+    return dh if tokens is None else dh[np.asarray(tokens)]
+
+
 def backward(inputs, dout, *, top_k, score="softmax", renormalize=True, route_scale=1.0,
              n_groups=1, topk_groups=1, group_rule="top2sum", capacity_factor=None,
              token_mask=None, swiglu_limit=0.0, aux_coef=(0.0, 0.0)):
@@ -555,42 +605,8 @@ def backward(inputs, dout, *, top_k, score="softmax", renormalize=True, route_sc
                                                    inputs["ws_down"], dout, swiglu_limit)
         dx += dz
         out.update(dws_gate=dwg, dws_up=dwu, dws_down=dwd)
-    # router: gate weights -> chosen scores
-    sc, h = r["scores"], r["logits"]
-    valid = ids[:, 0] >= 0
-    dsc = np.zeros((T, E))
-    for t in np.nonzero(valid)[0]:
-        c = sc[t, ids[t]]
-        if renormalize:
-            S = c.sum()
-            dc = route_scale / S * (d_gate_w[t] - np.sum(d_gate_w[t] * c) / S)
-        else:
-            dc = route_scale * d_gate_w[t]
-        np.add.at(dsc[t], ids[t], dc)
-    # balance = E * sum_e f_e P_e, P_e = mean over valid tokens of q_te
-    alpha, beta = aux_coef
-    n_valid = int(valid.sum())
-    if n_valid and alpha:
-        f_e = r["counts"] / float(n_valid * top_k)
-        dq = np.where(valid[:, None], alpha * E * f_e[None, :] / n_valid, 0.0)
-        if score == "softmax":
-            dsc += dq
-        else:  # q = s / sum_e s
-            ssum = sc.sum(axis=1, keepdims=True)
-            q = sc / ssum
-            dsc += (dq - np.sum(dq * q, axis=1, keepdims=True)) / ssum
-    # scores -> logits
-    if score == "softmax":
-        dh = sc * (dsc - np.sum(dsc * sc, axis=1, keepdims=True))
-    elif score == "sigmoid":
-        dh = dsc * sc * (1.0 - sc)
-    else:  # s = sqrt(softplus(h)): ds/dh = sigmoid(h) / (2 s)
-        dh = dsc * sigmoid(h) / (2.0 * sc)
-    # z = mean over valid tokens of lse(h_t)^2
-    if n_valid and beta:
-        lse = logsumexp(h)
-        dh += np.where(valid[:, None], beta * 2.0 * lse[:, None] * softmax(h) / n_valid, 0.0)
-    dh = np.where(valid[:, None], dh, 0.0)
+    dh = router_backward(r, d_gate_w, top_k=top_k, score=score, renormalize=renormalize,
+                         route_scale=route_scale, aux_coef=aux_coef)
     wr = np.asarray(inputs["w_router"], dtype=np.float64)
     dx += dh @ wr
     out.update(dx=dx, dw_router=dh.T @ x, d_gate_w=d_gate_w, d_logits=dh)

@@ -714,4 +714,15 @@ def pin_backward_zero_router_grad_top1_renorm(o):
     assert np.abs(g["dw_router"]).max() < 1e-12
 
 
+def pin_router_backward_rows(o):
+    """The router gradient of a subset of tokens equals those rows of the
+    full one (the balance and z terms use every token's counts)."""
+    inp = _tiny_inputs(62, T=12, E=5)
+    r = o.route(inp["x"], inp["w_router"], 2)
+    dgw = _rng(63).normal(size=(12, 2))
+    full = o.router_backward(r, dgw, top_k=2, aux_coef=(0.3, 0.2))
+    sub = o.router_backward(r, dgw, top_k=2, aux_coef=(0.3, 0.2), tokens=[1, 4, 11])
+    assert np.array_equal(sub, full[[1, 4, 11]])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

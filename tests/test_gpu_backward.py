@@ -1,8 +1,9 @@
 """GPU parity of the backward pass (moe_backward) against the oracle's float64
-gradients of <dout, out> + alpha * balance + beta * z, on the reduced
-workloads.  The device gets the oracle's own routes and gate weights, so both
-sides differentiate the same routed layer; every element of every gradient is
-compared at the layer's bf16 tolerance (max|err| <= 2e-2 * max|ref|)."""
+gradients of <dout, out> + alpha * balance + beta * z.  The device gets the
+oracle's own routes and gate weights, so both sides differentiate the same
+routed layer.  On the reduced workloads every element of every gradient is
+compared; at full size, sampled tokens and sampled weight-gradient rows.  The
+bar is the layer's bf16 tolerance (max|err| <= 2e-2 * max|ref|)."""
 from __future__ import annotations
 
 import sys
@@ -104,3 +105,83 @@ def test_backward_dropped_slots(moe):
                             capacity_factor=w.capacity_factor)["keep"]
     assert (~keep).any()
     assert (g["d_gate_w"].cpu().numpy()[~keep] == 0).all()
+
+
+# ------------------------------------------------------------- full size ---
+
+FULL = ["mixtral_8x_top2", "switch_top1_capacity", "decode_128x_top8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_backward(moe, name):
+    """Full-size workload as bench.py draws it, on the oracle's routes: dx and
+    dL/dw on sampled tokens, and whole weight-gradient rows for sampled
+    (expert, hidden unit) pairs.  A SwiGLU FFN is a sum over its hidden units,
+    so the one-unit FFN of unit h gives exactly row h of dW_gate and dW_up and
+    column h of dW_down from all of the expert's rows."""
+    w = W.WORKLOADS[name]
+    _say(f"[full backward] {name}: drawing inputs")
+    inp = {k: v.to("cuda") for k, v in W.make_inputs(w, "cuda", seed=0).items()}
+    oi = P.oracle_inputs(inp)
+    aux = (0.01, 0.001)
+    _say(f"[full backward] {name}: oracle routing")
+    r = P.oracle_route(w, oi)
+    cap = P.oracle.capacity(w.capacity_factor, w.T, w.top_k, w.E)
+    keep = P.oracle.first_within_capacity(r["ids"], w.E, cap)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    dout = torch.randn(w.T, w.D, generator=gen, device="cuda").to(torch.bfloat16)
+    cfg = P.config_of(w)
+    _say(f"[full backward] {name}: moe_backward")
+    g = moe.moe_backward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
+                         inp["w_down"], torch.from_numpy(r["ids"].astype(np.int32)).cuda(),
+                         torch.from_numpy(r["weights"].astype(np.float32)).cuda(), dout,
+                         logit_bias=inp.get("logit_bias"), balance_coef=aux[0], z_coef=aux[1],
+                         d_gate_w=True)
+    torch.cuda.synchronize()
+    x, do = oi["x"], dout.to(torch.float64).cpu().numpy()
+    # sampled tokens: experts' input gradients, dL/dw, and the router's share
+    rng = np.random.default_rng(3)
+    toks = np.unique(np.concatenate([rng.choice(w.T, 16, replace=False), [0, w.T - 1],
+                                     np.nonzero(~keep.any(1))[0][:4]]))
+    _say(f"[full backward] {name}: oracle on {toks.size} tokens")
+    dx = np.zeros((toks.size, w.D))
+    dgw = np.zeros_like(r["weights"])
+    for i, t in enumerate(toks):
+        for s_ in range(w.top_k):
+            if not keep[t, s_]:
+                continue
+            e = r["ids"][t, s_]
+            dz, _, _, _, F = P.oracle.swiglu_ffn_backward(
+                x[t:t + 1], oi["w_gate"][e], oi["w_up"][e], oi["w_down"][e],
+                r["weights"][t, s_] * do[t:t + 1])
+            dx[i] += dz[0]
+            dgw[t, s_] = float(np.sum(do[t] * F[0]))
+    dh = P.oracle.router_backward(r, dgw, top_k=w.top_k, score=w.score,
+                                  renormalize=w.renormalize, route_scale=w.route_scale,
+                                  aux_coef=aux, tokens=toks)
+    dx += dh @ oi["w_router"]
+    sel = torch.from_numpy(toks).cuda()
+    P.compare_rows(g["dx"][sel], dx, "bf16", f"{name} dx on sampled tokens")
+    P.compare_rows(g["d_gate_w"][sel], dgw[toks], "bf16", f"{name} dL/dw on sampled tokens")
+    assert (g["d_gate_w"].cpu().numpy()[~keep] == 0).all()
+    # weight-gradient rows of sampled experts and hidden units
+    kept_rows = [np.nonzero((r["ids"] == e) & keep) for e in range(w.E)]
+    with_rows = [e for e in range(w.E) if kept_rows[e][0].size]
+    pick = rng.choice(with_rows, size=min(3, len(with_rows)), replace=False)
+    for e in pick:
+        t, s_ = kept_rows[e]
+        dF = r["weights"][t, s_][:, None] * do[t]
+        for h in rng.choice(w.H, size=2, replace=False):
+            _, dwg, dwu, dwd, _ = P.oracle.swiglu_ffn_backward(
+                x[t], oi["w_gate"][e][h:h + 1], oi["w_up"][e][h:h + 1],
+                oi["w_down"][e][:, h:h + 1], dF)
+            what = f"{name} expert {e} unit {h}"
+            P.compare_rows(g["dw_gate"][e, h], dwg[0], "bf16", what + " dW_gate row")
+            P.compare_rows(g["dw_up"][e, h], dwu[0], "bf16", what + " dW_up row")
+            P.compare_rows(g["dw_down"][e, :, h], dwd[:, 0], "bf16", what + " dW_down column")
+    for e in range(w.E):
+        if not kept_rows[e][0].size:  # an expert without rows gets exactly zero
+            assert not g["dw_gate"][e].any() and not g["dw_down"][e].any()
+            break
+    _say(f"[full backward] {name}: {len(with_rows)} experts with rows; checked {list(pick)}")
