@@ -212,6 +212,15 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
     const bool row_ok = m < t.m_end;
     if (EPI == BWD_EPI_F32) {
       if (!row_ok) continue;
+      if (p.Cb) {
+        uint16_t* cb = p.Cb + (long long)t.g * p.c_gstride + (long long)m * p.ldc;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int n = t.nt * BBN + ni * 32 + lr;
+          if (n < p.N) cb[n] = f32_to_bf16_bits(acc[ni][i]);
+        }
+        continue;
+      }
       float* base;
       long long row = m;
       if (m >= p.c_split) {
@@ -246,28 +255,6 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
         p.p1[o] = f32_to_bf16_bits(mg * uc * (s + gc * s * (1.f - s)));
         p.p2[o] = f32_to_bf16_bits(mu * gc * s);
       }
-    } else {  // BWD_EPI_DOWN_DGRAD
-      float w = 1.f;
-      if (row_ok && p.gate_w) w = p.gate_w[p.r2a[m]];
-      float rs = 0.f;
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int h = t.nt * BBN + ni * 32 + lr;
-        if (!row_ok || h >= p.N) continue;
-        const long long o = (long long)m * p.ldh + h;
-        const float da = acc[ni][i];
-        const float a = bf16_bits_to_f32(p.act[o]);
-        rs += a * da;
-        const long long od = (long long)m * p.lddgu + h;
-        p.dgu[od] = f32_to_bf16_bits(w * da * bf16_bits_to_f32(p.p1[o]));
-        p.dgu[od + p.H] = f32_to_bf16_bits(w * da * bf16_bits_to_f32(p.p2[o]));
-      }
-      if (p.dw_part) {
-        // the 32 lanes of a half-wave hold the row's 128 columns: fixed butterfly
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) rs += __shfl_xor(rs, off);
-        if (row_ok && lr == 0) p.dw_part[(long long)m * p.npart + t.nt] = rs;
-      }
     }
   }
 }
@@ -287,7 +274,6 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sB1[256 * BK];
   __shared__ __attribute__((aligned(1024))) uint16_t sX[8];  // unused stages
   __shared__ int s_scan[BT + 4];
-  __shared__ float s_red[2 * 4 * 128];
   BTile t;
   if (!bwd_tile<BM>(p, C::BN, t, s_scan)) return;
   const bool kr = p.grouping == BWD_KRAGGED;
@@ -355,6 +341,15 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
       const bool row_ok = m < t.m_end;
       if (EPI == BWD_EPI_F32) {
         if (!row_ok) continue;
+        if (p.Cb) {
+          uint16_t* cb = p.Cb + (long long)t.g * p.c_gstride + (long long)m * p.ldc;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const int n = n_base + ni * 32 + lr;
+            if (n < p.N) cb[n] = f32_to_bf16_bits(acc[0][mi][ni][i]);
+          }
+          continue;
+        }
         float* base = m >= p.c_split ? p.C2 : p.C;
         const long long row = m >= p.c_split ? m - p.c_split : m;
         base += (long long)t.g * p.c_gstride + row * p.ldc;
@@ -383,39 +378,6 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
           p.p1[o] = f32_to_bf16_bits(mg * uc * (s + gc * s * (1.f - s)));
           p.p2[o] = f32_to_bf16_bits(mu * gc * s);
         }
-      } else {  // BWD_EPI_DOWN_DGRAD
-        float w = 1.f;
-        if (row_ok && p.gate_w) w = p.gate_w[p.r2a[m]];
-        float rs = 0.f;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int h = n_base + ni * 32 + lr;
-          if (!row_ok || h >= p.N) continue;
-          const long long o = (long long)m * p.ldh + h;
-          const float da = acc[0][mi][ni][i];
-          rs += bf16_bits_to_f32(p.act[o]) * da;
-          const long long od = (long long)m * p.lddgu + h;
-          p.dgu[od] = f32_to_bf16_bits(w * da * bf16_bits_to_f32(p.p1[o]));
-          p.dgu[od + p.H] = f32_to_bf16_bits(w * da * bf16_bits_to_f32(p.p2[o]));
-        }
-        if (p.dw_part) {
-#pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) rs += __shfl_xor(rs, off);
-          if (lr == 0) s_red[(wm * C::WGN + wn) * 128 + (rloc - wm * C::WM)] = rs;
-        }
-      }
-    }
-  }
-  if (EPI == BWD_EPI_DOWN_DGRAD && p.dw_part) {
-    // the row's sums over this tile's columns: the WGN waves in order
-    __syncthreads();
-    if (tid < BM) {
-      const int wmr = tid / C::WM, rr = tid % C::WM, m = t.m0 + tid;
-      if (m < t.m_end) {
-        float v = s_red[(wmr * C::WGN) * 128 + rr];
-#pragma unroll
-        for (int q = 1; q < C::WGN; ++q) v += s_red[(wmr * C::WGN + q) * 128 + rr];
-        p.dw_part[(long long)m * p.npart + t.nt] = v;
       }
     }
   }
@@ -424,6 +386,44 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
 bool bwd_dma_fits(const BwdGemmParams& p) {
   const long long lim = 1ll << 31;
   return p.a_bytes > 0 && p.b_bytes > 0 && p.a_bytes < lim && p.b_bytes < lim;
+}
+
+// SwiGLU backward, one wave per row, 16-byte chunks along H (see
+// SwigluBwdParams).  The dL/dw sum runs per lane in chunk order, then over
+// the lanes in a fixed butterfly.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rows = p.offsets ? p.offsets[p.G] : p.n;
+  if (r >= rows) return;  // whole wave
+  const float w = p.gate_w ? p.gate_w[p.r2a[r]] : 1.f;
+  const long long base = (long long)r * p.H;
+  const long long based = (long long)r * 2 * p.H;
+  float rs = 0.f;
+  for (int c = lane * 8; c < p.H; c += 64 * 8) {
+    const u32x4 d4 = *reinterpret_cast<const u32x4*>(p.dact + base + c);
+    const u32x4 a4 = *reinterpret_cast<const u32x4*>(p.act + base + c);
+    const u32x4 q4 = *reinterpret_cast<const u32x4*>(p.p1 + base + c);
+    const u32x4 v4 = *reinterpret_cast<const u32x4*>(p.p2 + base + c);
+    u32x4 g4, u4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d0 = __uint_as_float(d4[e] << 16), d1 = __uint_as_float(d4[e] & 0xffff0000u);
+      rs += __uint_as_float(a4[e] << 16) * d0;
+      rs += __uint_as_float(a4[e] & 0xffff0000u) * d1;
+      g4[e] = (uint32_t)f32_to_bf16_bits(w * d0 * __uint_as_float(q4[e] << 16)) |
+              ((uint32_t)f32_to_bf16_bits(w * d1 * __uint_as_float(q4[e] & 0xffff0000u)) << 16);
+      u4[e] = (uint32_t)f32_to_bf16_bits(w * d0 * __uint_as_float(v4[e] << 16)) |
+              ((uint32_t)f32_to_bf16_bits(w * d1 * __uint_as_float(v4[e] & 0xffff0000u)) << 16);
+    }
+    *reinterpret_cast<u32x4*>(p.dgu + based + c) = g4;
+    *reinterpret_cast<u32x4*>(p.dgu + based + p.H + c) = u4;
+  }
+  if (p.dw) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) rs += __shfl_xor(rs, off);
+    if (lane == 0) p.dw[r] = rs;
+  }
 }
 
 // 64x64 tiled transpose through LDS (see TransposeParams), 16-byte global
@@ -561,14 +561,12 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdParams p) {
   }
   ssum = wave_sum(ssum);
 
-  // dL/dw of each slot: the fixed-order sum of the row's column-tile partials.
+  // dL/dw of each slot: that of its kept row (0 when dropped).
   float dw[kMaxTopK];
   float csum = 0.f, dwc = 0.f;
   for (int s = 0; s < k; ++s) {
     const int r = p.a2r[(long long)t * k + s];
-    float v = 0.f;
-    if (r >= 0)
-      for (int q = 0; q < p.npart; ++q) v += p.dw_part[(long long)r * p.npart + q];
+    const float v = r >= 0 ? p.dw[r] : 0.f;
     dw[s] = v;
     const int e = p.ids[(long long)t * k + s];
     float cj = 0.f;
@@ -660,14 +658,9 @@ __global__ __launch_bounds__(256) void dx_kernel(DxParams p) {
 
 }  // namespace
 
-int bwd_gemm_col_tile(const BwdGemmParams& p) {
-  const int full = bwd_dma_fits(p) ? 256 : BBN;
-  return p.epilogue == BWD_EPI_GATEUP_SAVE ? full / 2 : full;
-}
-
 hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s) {
   if (bwd_dma_fits(p)) {
-    const int bn = bwd_gemm_col_tile(p), nN = (p.N + bn - 1) / bn;
+    const int bn = p.epilogue == BWD_EPI_GATEUP_SAVE ? 128 : 256, nN = (p.N + bn - 1) / bn;
     long long blocks;
     if (p.grouping == BWD_DENSE)
       blocks = (long long)nN * ((p.M + 255) / 256);
@@ -680,12 +673,8 @@ hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s) {
       case BWD_EPI_F32:
         hipLaunchKernelGGL(bwd_dma_kernel<BWD_EPI_F32>, dim3((unsigned)blocks), dim3(512), 0, s, p);
         break;
-      case BWD_EPI_GATEUP_SAVE:
-        hipLaunchKernelGGL(bwd_dma_kernel<BWD_EPI_GATEUP_SAVE>, dim3((unsigned)blocks), dim3(512),
-                           0, s, p);
-        break;
       default:
-        hipLaunchKernelGGL(bwd_dma_kernel<BWD_EPI_DOWN_DGRAD>, dim3((unsigned)blocks), dim3(512),
+        hipLaunchKernelGGL(bwd_dma_kernel<BWD_EPI_GATEUP_SAVE>, dim3((unsigned)blocks), dim3(512),
                            0, s, p);
     }
     return hipGetLastError();
@@ -700,19 +689,17 @@ hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s) {
   else
     blocks = (long long)nN * ((p.max_rows + BBM - 1) / BBM + p.G);
   if (blocks <= 0) return hipSuccess;
-  const BwdGemmParams& q = p;
-  switch (p.epilogue) {
-    case BWD_EPI_F32:
-      hipLaunchKernelGGL(bwd_gemm_kernel<BWD_EPI_F32>, dim3((unsigned)blocks), dim3(BT), 0, s, q);
-      break;
-    case BWD_EPI_GATEUP_SAVE:
-      hipLaunchKernelGGL(bwd_gemm_kernel<BWD_EPI_GATEUP_SAVE>, dim3((unsigned)blocks), dim3(BT),
-                         0, s, q);
-      break;
-    default:
-      hipLaunchKernelGGL(bwd_gemm_kernel<BWD_EPI_DOWN_DGRAD>, dim3((unsigned)blocks), dim3(BT),
-                         0, s, q);
-  }
+  if (p.epilogue == BWD_EPI_F32)
+    hipLaunchKernelGGL(bwd_gemm_kernel<BWD_EPI_F32>, dim3((unsigned)blocks), dim3(BT), 0, s, p);
+  else
+    hipLaunchKernelGGL(bwd_gemm_kernel<BWD_EPI_GATEUP_SAVE>, dim3((unsigned)blocks), dim3(BT), 0,
+                       s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const SwigluBwdParams& p, hipStream_t s) {
+  if (p.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((p.n + 3) / 4), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -108,7 +108,7 @@ struct CombineParams {
 // Grouped bf16 GEMM of the backward pass, both operands K-contiguous:
 //   C[g](m, n) = sum_k A[g](m, k) * B[g](n, k), fp32 accumulation.
 enum BwdGrouping { BWD_DENSE = 0, BWD_MROWS = 1, BWD_KRAGGED = 2 };
-enum BwdEpilogue { BWD_EPI_F32 = 0, BWD_EPI_GATEUP_SAVE = 1, BWD_EPI_DOWN_DGRAD = 2 };
+enum BwdEpilogue { BWD_EPI_F32 = 0, BWD_EPI_GATEUP_SAVE = 1 };
 
 struct BwdGemmParams {
   int grouping, epilogue;
@@ -129,8 +129,10 @@ struct BwdGemmParams {
   long long ldb, b_gstride;
   // EPI_F32: C row m of group g (KRAGGED) / row r (MROWS, DENSE) at
   // C + g*c_gstride + m*ldc; rows m >= c_split go to C2 + g*c_gstride + (m-c_split)*ldc.
+  // With Cb (bf16) instead of C the rows are rounded once into Cb (no split).
   float* C;
   float* C2;
+  uint16_t* Cb;
   long long ldc, c_gstride;
   int c_split;
   // GATEUP_SAVE: act = silu(g)*u and the two factors p1 = d act/d g, p2 = d act/d u
@@ -140,26 +142,29 @@ struct BwdGemmParams {
   uint16_t* p2;
   long long ldh;
   float limit;
-  // DOWN_DGRAD: the accumulator is d(act) for unit gate weight; with the saved
-  // act/p1/p2 (ldh) it writes dg = w*dact*p1 and du = w*dact*p2 to dgu [r][h]
-  // and [r][H+h] (stride lddgu), w = gate_w[r2a[r]] (1 without gate_w), and
-  // the row sums of act*dact over each 128-column tile to dw_part [r][npart].
-  const float* gate_w;
-  const int32_t* r2a;
-  uint16_t* dgu;
-  long long lddgu;
-  int H;
-  float* dw_part;
-  int npart;
   // Byte extents of A and of one group's B (the whole B when KRAGGED): the
   // 256x256 direct-to-LDS path addresses them with 32-bit buffer offsets.
   long long a_bytes, b_bytes;
 };
 
-// Output columns per tile of the backward GEMM that launch_bwd_gemm picks for
-// p (256 on the direct-to-LDS path, 128 otherwise; half that for the paired
-// gate/up recompute): the DOWN_DGRAD partials have ceil(N / this) columns.
-int bwd_gemm_col_tile(const BwdGemmParams& p);
+// SwiGLU backward of the rows r < rows (rows = offsets[G] when offsets is
+// given, else n): from dact = dL/d act for unit gate weight (bf16 [r][H]) and
+// the saved act, p1, p2 ([r][H]): dgu[r][h] = w*dact*p1, dgu[r][H+h] =
+// w*dact*p2 (w = gate_w[r2a[r]], 1 without gate_w) and, with dw, dw[r] = sum
+// over h of act*dact (dL/dw of the row's slot) in a fixed order.
+struct SwigluBwdParams {
+  int n, H;
+  const int32_t* offsets;
+  int G;
+  const uint16_t* dact;
+  const uint16_t* act;
+  const uint16_t* p1;
+  const uint16_t* p2;
+  const float* gate_w;
+  const int32_t* r2a;
+  uint16_t* dgu;
+  float* dw;
+};
 
 // dst[c][col(j)] = scale(j) * src[row(j)][c]: a tiled transpose.  Row
 // strides, column offsets and the column counts are multiples of 8 elements.  col(j) = j,
@@ -191,8 +196,7 @@ struct RouterBwdParams {
   const float* logits;       // [T, E] (logit bias included)
   const int32_t* ids;        // [T, k]
   const int32_t* a2r;        // [T*k]
-  const float* dw_part;      // [rows, npart]
-  int npart;
+  const float* dw;           // [rows]: dL/dw of each kept row
   const int32_t* counts;     // [E] pre-drop
   uint16_t* dh;              // [T, Epad] bf16 out
   float* dgw;                // [T, k] or null
@@ -208,6 +212,7 @@ struct DxParams {
 };
 
 hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s);
+hipError_t launch_swiglu_bwd(const SwigluBwdParams& p, hipStream_t s);
 hipError_t launch_transpose(const TransposeParams& p, hipStream_t s);
 hipError_t launch_pad_offsets(int G, const int32_t* offsets, int32_t* padoff, hipStream_t s);
 hipError_t launch_router_bwd(const RouterBwdParams& p, hipStream_t s);

@@ -157,9 +157,9 @@ Layout layout_of(const moe_config* c) {
 // Backward workspace: the forward layout (route and permutation scratch),
 // then the backward's own buffers.
 struct BwdLayout {
-  size_t logits, padoff, wdT, wguT, wrT, act, p1, p2, dgu, part, dh, dz, dxr, dFT, XT, AT, DGUT,
-      dhT, xT, swdT, swguT, sact, sp1, sp2, sdgu, sdz, doutT, sAT, sDGUT, total;
-  int Epad, Tpad, Kpad, npart;
+  size_t logits, padoff, wdT, wguT, wrT, act, p1, p2, dact, dgu, dw, dh, dz, dxr, dFT, XT, AT,
+      DGUT, dhT, xT, swdT, swguT, sact, sp1, sp2, sdact, sdgu, sdz, doutT, sAT, sDGUT, total;
+  int Epad, Tpad, Kpad;
 };
 
 BwdLayout bwd_layout_of(const moe_config* c) {
@@ -176,7 +176,6 @@ BwdLayout bwd_layout_of(const moe_config* c) {
   B.Epad = (int)((E + 63) / 64 * 64);
   B.Tpad = (int)((T + 63) / 64 * 64);
   B.Kpad = (int)((R + 64 * E + 63) / 64 * 64);
-  B.npart = (int)((H + 127) / 128);
   const size_t Kp = B.Kpad, Tp = B.Tpad, Ep = B.Epad;
   B.logits = take(T * E * 4);
   B.padoff = take((E + 1) * 4);
@@ -186,8 +185,9 @@ BwdLayout bwd_layout_of(const moe_config* c) {
   B.act = take(R * H * 2);
   B.p1 = take(R * H * 2);
   B.p2 = take(R * H * 2);
+  B.dact = take(R * H * 2);
   B.dgu = take(R * 2 * H * 2);
-  B.part = take(R * B.npart * 4);
+  B.dw = take(R * 4);
   B.dh = take(T * Ep * 2);
   B.dz = take(R * D * 4);
   B.dxr = take(T * D * 4);
@@ -203,6 +203,7 @@ BwdLayout bwd_layout_of(const moe_config* c) {
     B.sact = take(T * Hs * 2);
     B.sp1 = take(T * Hs * 2);
     B.sp2 = take(T * Hs * 2);
+    B.sdact = take(T * Hs * 2);
     B.sdgu = take(T * 2 * Hs * 2);
     B.sdz = take(T * D * 4);
     B.doutT = take(D * Tp * 2);
@@ -782,7 +783,6 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     return hip_ok(moe::launch_bwd_gemm(g, stream), what);
   };
   const int kNoSplit = 0x7fffffff;
-  int npart = B.npart;  // column tiles of the down dgrad (its partials' row stride)
   // 4. recompute gate/up: act, p1, p2 of every kept row
   {
     moe::BwdGemmParams g{};
@@ -809,10 +809,11 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     g.a_bytes = 2ll * T * D;
     g.b_bytes = 2ll * H * D;
     MOE_TRY(gemm(g, "recompute gate/up"));
-    // 5. down dgrad with the gate weights: dg, du and dL/dw partials
+    // 5. down dgrad: dL/d act for unit gate weight (bf16), then the SwiGLU
+    // backward with the gate weights: dg, du and dL/dw of every kept row
     moe::BwdGemmParams d{};
     d.grouping = moe::BWD_MROWS;
-    d.epilogue = moe::BWD_EPI_DOWN_DGRAD;
+    d.epilogue = moe::BWD_EPI_F32;
     d.N = H;
     d.K = D;
     d.G = E;
@@ -825,21 +826,15 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     d.B = u16(B.wdT);
     d.ldb = D;
     d.b_gstride = (long long)H * D;
-    d.act = u16(B.act);
-    d.p1 = u16(B.p1);
-    d.p2 = u16(B.p2);
-    d.ldh = H;
-    d.gate_w = gate_w;
-    d.r2a = r2a;
-    d.dgu = u16(B.dgu);
-    d.lddgu = 2 * H;
-    d.H = H;
-    d.dw_part = f32(B.part);
+    d.Cb = u16(B.dact);
+    d.ldc = H;
+    d.c_split = kNoSplit;
     d.a_bytes = 2ll * T * D;
     d.b_bytes = 2ll * H * D;
-    npart = (H + moe::bwd_gemm_col_tile(d) - 1) / moe::bwd_gemm_col_tile(d);
-    d.npart = npart;
     MOE_TRY(gemm(d, "down dgrad"));
+    moe::SwigluBwdParams q{R, H, offsets, E, u16(B.dact), u16(B.act), u16(B.p1), u16(B.p2),
+                           gate_w, r2a, u16(B.dgu), f32(B.dw)};
+    MOE_TRY(hip_ok(moe::launch_swiglu_bwd(q, stream), "swiglu backward kernel"));
   }
   // 6. router: dL/dh
   {
@@ -856,8 +851,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     r.logits = f32(B.logits);
     r.ids = expert_ids;
     r.a2r = a2r;
-    r.dw_part = f32(B.part);
-    r.npart = npart;
+    r.dw = f32(B.dw);
     r.counts = counts;
     r.dh = u16(B.dh);
     r.dgw = d_gate_w;
@@ -925,7 +919,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     MOE_TRY(gemm(g, "shared recompute"));
     moe::BwdGemmParams d{};
     d.grouping = moe::BWD_DENSE;
-    d.epilogue = moe::BWD_EPI_DOWN_DGRAD;
+    d.epilogue = moe::BWD_EPI_F32;
     d.M = T;
     d.N = Hs;
     d.K = D;
@@ -934,16 +928,15 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     d.lda = D;
     d.B = u16(B.swdT);
     d.ldb = D;
-    d.act = u16(B.sact);
-    d.p1 = u16(B.sp1);
-    d.p2 = u16(B.sp2);
-    d.ldh = Hs;
-    d.dgu = u16(B.sdgu);
-    d.lddgu = 2 * Hs;
-    d.H = Hs;
+    d.Cb = u16(B.sdact);
+    d.ldc = Hs;
+    d.c_split = kNoSplit;
     d.a_bytes = 2ll * T * D;
     d.b_bytes = 2ll * Hs * D;
     MOE_TRY(gemm(d, "shared down dgrad"));
+    moe::SwigluBwdParams q{T, Hs, nullptr, 1, u16(B.sdact), u16(B.sact), u16(B.sp1),
+                           u16(B.sp2), nullptr, nullptr, u16(B.sdgu), nullptr};
+    MOE_TRY(hip_ok(moe::launch_swiglu_bwd(q, stream), "shared swiglu backward kernel"));
     moe::BwdGemmParams z{};
     z.grouping = moe::BWD_DENSE;
     z.epilogue = moe::BWD_EPI_F32;
