@@ -39,7 +39,9 @@ METRIC = "MoE-layer fwd tokens/s; grouped-GEMM TFLOP/s as % bf16 MFMA peak (1 GP
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3         # MI355X fp32 (vector)
 PEAK_HBM_GBS = 8000.0
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_21_amd", "csrc", "grouped_swiglu.hip")
+# The grouped SwiGLU kernels' source: the traffic summaries record its hash.
+GEMM_SRC = [os.path.join(ROOT, "mixture_experts_layer_21_amd", "csrc", f)
+            for f in ("grouped_swiglu.hip", "dma_gemm.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_swiglu_traffic_{workload}.md")
 
 
@@ -71,8 +73,11 @@ def _log(*a):
 
 
 def _source_hash():
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(workload, n_launch_units):
