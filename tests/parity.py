@@ -94,6 +94,26 @@ def compare_route(w, r_ref, gpu):
     return int(flag.sum()), differ
 
 
+def comparable_tokens(w, ref_ids, dev_ids, min_frac=0.9):
+    """Tokens whose device routes equal the oracle's own, so that their
+    outputs can be compared with the oracle's forward on its own routes.
+    Routes differ only on flagged near ties, so this is normally every token.
+    With a capacity limit a different route can move later drops (first come
+    in token order), so only tokens before the first difference count."""
+    dev = dev_ids.cpu().numpy() if torch.is_tensor(dev_ids) else np.asarray(dev_ids)
+    same = (dev == np.asarray(ref_ids)).all(axis=1)
+    if w.capacity_factor is not None and not same.all():
+        same[int(np.argmin(same)):] = False
+    assert same.mean() >= min_frac, f"only {same.mean():.2%} of the tokens are comparable"
+    return same
+
+
+def compare_tokens(got: torch.Tensor, ref: np.ndarray, mask: np.ndarray, dtype: str, what: str):
+    """compare_rows on the tokens of ``mask`` (rows of got and ref)."""
+    sel = torch.from_numpy(np.nonzero(mask)[0]).to(got.device)
+    return compare_rows(got[sel], ref[mask], dtype, what)
+
+
 def compare_rows(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str):
     g = got.detach().to("cpu").to(torch.float64).numpy()
     scale = float(np.abs(ref).max()) if ref.size else 0.0

@@ -46,11 +46,13 @@ def _cap_int(w):
     return 0 if c is None else c
 
 
-def _check_permute(moe, w, cfg, ids_dev, cap):
-    ids = ids_dev.cpu().numpy().astype(np.int64)
+def _check_permute(moe, w, cfg, ids, cap):
+    """The device permutation of the routes ``ids`` (the oracle's, or a
+    test's own) against the oracle's, bit for bit."""
+    ids = np.asarray(ids).astype(np.int64)
     keep = oracle.first_within_capacity(ids, w.E, cap if cap > 0 else None)
     off, r2a, a2r = oracle.permutation(ids, keep, w.E)
-    g = moe.moe_permute(cfg, ids_dev, cap)
+    g = moe.moe_permute(cfg, torch.from_numpy(ids.astype(np.int32)).cuda(), cap)
     n = int(g["n_kept"].item())
     assert n == int(keep.sum())
     assert (g["expert_offsets"].cpu().numpy() == off).all()
@@ -159,13 +161,12 @@ def test_capacity_matches_oracle(moe, name):
 def test_permute_small(moe, name):
     w = W.SMALL[name]
     _say(f"[permute] {name}")
-    d = _to_dev(W.make_inputs(w, "cpu", seed=0))
     cfg = P.config_of(w)
-    g = _route(moe, w, cfg, d)
-    _check_permute(moe, w, cfg, g["expert_ids"], _cap_int(w))
+    r = P.oracle_route(w, P.oracle_inputs(W.make_inputs(w, "cpu", seed=0)))
+    _check_permute(moe, w, cfg, r["ids"], _cap_int(w))
     # also with a tight capacity, so that drops happen on every workload
     tight = max(1, (w.T * w.top_k) // (4 * w.E))
-    _check_permute(moe, w, cfg, g["expert_ids"], tight)
+    _check_permute(moe, w, cfg, r["ids"], tight)
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -175,18 +176,18 @@ def test_grouped_swiglu_small(moe, name):
     inp = W.make_inputs(w, "cpu", seed=0)
     d = _to_dev(inp)
     cfg = P.config_of(w)
-    g = _route(moe, w, cfg, d)
-    perm, keep = _check_permute(moe, w, cfg, g["expert_ids"], _cap_int(w))
+    oi = P.oracle_inputs(inp)
+    r = P.oracle_route(w, oi)  # the oracle's routes and weights go in
+    perm, keep = _check_permute(moe, w, cfg, r["ids"], _cap_int(w))
     n = int(perm["n_kept"].item())
     y = moe.moe_grouped_swiglu(cfg, d["x"], d["w_gate"], d["w_up"], d["w_down"],
                                row_to_assign=perm["row_to_assign"],
                                expert_offsets=perm["expert_offsets"],
-                               max_rows_bound=moe.max_rows(cfg), gate_w=g["gate_w"])
+                               max_rows_bound=moe.max_rows(cfg),
+                               gate_w=torch.from_numpy(r["weights"].astype(np.float32)).cuda())
     torch.cuda.synchronize()
-    oi = P.oracle_inputs(inp)
-    ids = g["expert_ids"].cpu().numpy().astype(np.int64)
-    gw = g["gate_w"].cpu().numpy().astype(np.float64)
-    ref = _reference_rows(w, oi, ids, gw, keep, perm["row_to_assign"][:n].cpu().numpy())
+    ref = _reference_rows(w, oi, r["ids"], r["weights"], keep,
+                          perm["row_to_assign"][:n].cpu().numpy())
     P.compare_rows(y[:n], ref, w.act_dtype, f"{name} expert rows")
 
 
@@ -207,8 +208,8 @@ def test_combine_small(moe, name):
     inp = W.make_inputs(w, "cpu", seed=0)
     d = _to_dev(inp)
     cfg = P.config_of(w)
-    g = _route(moe, w, cfg, d)
-    perm, keep = _check_permute(moe, w, cfg, g["expert_ids"], _cap_int(w))
+    r = P.oracle_route(w, P.oracle_inputs(inp))
+    perm, keep = _check_permute(moe, w, cfg, r["ids"], _cap_int(w))
     n = int(perm["n_kept"].item())
     dt = W.torch_dtype(w.act_dtype)
     gen = torch.Generator().manual_seed(5)
@@ -248,9 +249,9 @@ def test_forward_small(moe, name):
     oi = P.oracle_inputs(inp)
     r = P.oracle_route(w, oi)
     P.compare_route(w, r, g)
-    f = P.oracle_forward(w, oi, routing={"ids": ids.cpu().numpy(),
-                                         "weights": gw.cpu().numpy().astype(np.float64)})
-    err, scale = P.compare_rows(out, f["out"], w.act_dtype, f"{name} forward")
+    f = P.oracle_forward(w, oi)
+    err, scale = P.compare_tokens(out, f["out"], P.comparable_tokens(w, r["ids"], ids),
+                                  w.act_dtype, f"{name} forward")
     _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
 
 
@@ -286,9 +287,9 @@ def test_single_token(moe, dtype):
     inp = W.make_inputs(w, "cpu", seed=3)
     out, ids, gw = _fwd(moe, w, inp)
     oi = P.oracle_inputs(inp)
-    f = P.oracle_forward(w, oi, routing={"ids": ids.cpu().numpy(),
-                                         "weights": gw.cpu().numpy().astype(np.float64)})
-    P.compare_rows(out, f["out"], dtype, "single token")
+    f = P.oracle_forward(w, oi)
+    P.compare_tokens(out, f["out"], P.comparable_tokens(w, f["route"]["ids"], ids, 1.0), dtype,
+                     "single token")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -336,7 +337,7 @@ def test_forced_routes_with_empty_experts(moe, dtype):
     cfg = P.config_of(w)
     ids = torch.tensor([[4, 1]] * 30 + [[1, 4]] * 20, dtype=torch.int32)
     gw = torch.tensor([[0.75, 0.25]] * 50, dtype=torch.float32)
-    perm, keep = _check_permute(moe, w, cfg, ids.cuda(), 0)
+    perm, keep = _check_permute(moe, w, cfg, ids.numpy(), 0)
     assert perm["expert_offsets"].cpu().tolist() == [0, 0, 50, 50, 50, 100, 100, 100]
     y = moe.moe_grouped_swiglu(cfg, d["x"], d["w_gate"], d["w_up"], d["w_down"],
                                row_to_assign=perm["row_to_assign"],
@@ -356,11 +357,11 @@ def test_capacity_drops_everything_but_one(moe, dtype):
     inp = W.make_inputs(w, "cpu", seed=8)
     out, ids, gw = _fwd(moe, w, inp)
     oi = P.oracle_inputs(inp)
-    f = P.oracle_forward(w, oi, routing={"ids": ids.cpu().numpy(),
-                                         "weights": gw.cpu().numpy().astype(np.float64)})
+    f = P.oracle_forward(w, oi)
     assert f["capacity"] == 1 and f["n_kept"] <= 4
-    P.compare_rows(out, f["out"], dtype, "capacity 1")
-    dropped = ~f["keep"][:, 0]
+    same = P.comparable_tokens(w, f["route"]["ids"], ids)
+    P.compare_tokens(out, f["out"], same, dtype, "capacity 1")
+    dropped = ~f["keep"][:, 0] & same
     assert (out.cpu()[torch.from_numpy(dropped)] == 0).all()
 
 
@@ -373,9 +374,9 @@ def test_large_tile_path(moe, T, E, k):
     inp = W.make_inputs(w, "cpu", seed=9)
     out, ids, gw = _fwd(moe, w, inp)
     oi = P.oracle_inputs(inp)
-    f = P.oracle_forward(w, oi, routing={"ids": ids.cpu().numpy(),
-                                         "weights": gw.cpu().numpy().astype(np.float64)})
-    err, scale = P.compare_rows(out, f["out"], "bf16", "large-tile forward")
+    f = P.oracle_forward(w, oi)
+    err, scale = P.compare_tokens(out, f["out"], P.comparable_tokens(w, f["route"]["ids"], ids),
+                                  "bf16", "large-tile forward")
     _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
 
 
@@ -432,17 +433,16 @@ def test_full_size_forward(moe, name):
          "mean_prob": _route(moe, w, cfg, inp)["mean_prob"]}
     nflag, ndiff = P.compare_route(w, r, g)
     _say(f"  near ties flagged {nflag}, differing {ndiff}")
-    _check_permute(moe, w, cfg, ids, _cap_int(w))
+    _check_permute(moe, w, cfg, r["ids"], _cap_int(w))
     toks = _sample_tokens(w.T, 24 if w.T > 1024 else w.T, seed=11)
     if w.capacity_factor is not None:  # include dropped and kept tokens
-        keep = oracle.first_within_capacity(ids.cpu().numpy(), w.E,
+        keep = oracle.first_within_capacity(r["ids"], w.E,
                                             oracle.capacity(w.capacity_factor, w.T, w.top_k, w.E))
         toks = np.unique(np.concatenate([toks, np.nonzero(keep.any(1))[0][:8],
                                          np.nonzero(~keep.any(1))[0][:8]]))
     _say(f"[full] {name}: oracle outputs on {toks.size} tokens")
-    f = P.oracle_forward(w, oi, tokens=toks,
-                         routing={"ids": ids.cpu().numpy(),
-                                  "weights": gw.cpu().numpy().astype(np.float64)})
-    err, scale = P.compare_rows(out[torch.from_numpy(toks).cuda()], f["out"], w.act_dtype,
-                                f"{name} sampled outputs")
+    f = P.oracle_forward(w, oi, tokens=toks)
+    same = P.comparable_tokens(w, r["ids"], ids)[toks]
+    err, scale = P.compare_tokens(out[torch.from_numpy(toks).cuda()], f["out"], same,
+                                  w.act_dtype, f"{name} sampled outputs")
     _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")

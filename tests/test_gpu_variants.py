@@ -101,10 +101,9 @@ def test_forward_token_mask(moe, name):
                                                       d.get("logit_bias"), d.get("select_bias"),
                                                       token_mask=torch.from_numpy(mask).cuda())
                            ["mean_prob"]})
-    f = P.oracle_forward(w, oi, routing={"ids": ids_h.astype(np.int64),
-                                         "weights": gw.cpu().numpy().astype(np.float64)},
-                         token_mask=mask)
-    err, scale = P.compare_rows(out, f["out"], w.act_dtype, f"{name} masked forward")
+    f = P.oracle_forward(w, oi, token_mask=mask)
+    err, scale = P.compare_tokens(out, f["out"], P.comparable_tokens(w, r["ids"], ids_h),
+                                  w.act_dtype, f"{name} masked forward")
     _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
 
 
@@ -134,11 +133,10 @@ def test_forward_swiglu_limit(moe, name, limit):
     cfg = P.config_of(w, swiglu_limit=limit)
     out, ids, gw, _, _ = _forward(moe, w, cfg, d)
     oi = P.oracle_inputs(inp)
-    routing = {"ids": ids.cpu().numpy().astype(np.int64),
-               "weights": gw.cpu().numpy().astype(np.float64)}
-    f = P.oracle_forward(w, oi, routing=routing, swiglu_limit=limit)
-    err, scale = P.compare_rows(out, f["out"], w.act_dtype, f"{name} clamped forward")
-    plain = P.oracle_forward(w, oi, routing=routing)["out"]
+    f = P.oracle_forward(w, oi, swiglu_limit=limit)
+    same = P.comparable_tokens(w, f["route"]["ids"], ids)
+    err, scale = P.compare_tokens(out, f["out"], same, w.act_dtype, f"{name} clamped forward")
+    plain = P.oracle_forward(w, oi)["out"]
     assert np.abs(plain - f["out"]).max() > 10 * (err + 1e-12), "the clamp changed nothing"
     _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
 
@@ -155,9 +153,9 @@ def test_forward_shared_expert_gate(moe, name):
     cfg = P.config_of(w)
     out, ids, gw, _, _ = _forward(moe, w, cfg, d, shared_expert_gate=d["ws_sgate"])
     oi = P.oracle_inputs(inp)
-    f = P.oracle_forward(w, oi, routing={"ids": ids.cpu().numpy().astype(np.int64),
-                                         "weights": gw.cpu().numpy().astype(np.float64)})
-    err, scale = P.compare_rows(out, f["out"], w.act_dtype, f"{name} gated shared expert")
+    f = P.oracle_forward(w, oi)
+    err, scale = P.compare_tokens(out, f["out"], P.comparable_tokens(w, f["route"]["ids"], ids),
+                                  w.act_dtype, f"{name} gated shared expert")
     _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
 
 
@@ -179,17 +177,18 @@ def test_residual_add(moe):
     cfg = P.config_of(w)
     out, ids, gw, _, _ = _forward(moe, w, cfg, d, residual=d["x"])
     oi = P.oracle_inputs(inp)
-    routing = {"ids": ids.cpu().numpy().astype(np.int64),
-               "weights": gw.cpu().numpy().astype(np.float64)}
-    f = P.oracle_forward(w, oi, routing=routing, residual=oi["x"])
-    P.compare_rows(out, f["out"], w.act_dtype, "residual forward")
-    # combine in place: residual and out the same buffer
-    base = P.oracle_forward(w, oi, routing=routing)
+    f = P.oracle_forward(w, oi, residual=oi["x"])
+    same = P.comparable_tokens(w, f["route"]["ids"], ids)
+    P.compare_tokens(out, f["out"], same, w.act_dtype, "residual forward")
+    # combine in place (residual and out the same buffer), on the oracle's routes
+    base = P.oracle_forward(w, oi)
+    rids = torch.from_numpy(base["route"]["ids"].astype(np.int32)).cuda()
+    rgw = torch.from_numpy(base["route"]["weights"].astype(np.float32)).cuda()
     y = torch.zeros(moe.max_rows(cfg), w.D, dtype=torch.bfloat16, device="cuda")
-    r = moe.moe_permute(cfg, ids, 0)
+    r = moe.moe_permute(cfg, rids, 0)
     moe.moe_grouped_swiglu(cfg, d["x"], d["w_gate"], d["w_up"], d["w_down"],
                            row_to_assign=r["row_to_assign"], expert_offsets=r["expert_offsets"],
-                           gate_w=gw, y_rows=y)
+                           gate_w=rgw, y_rows=y)
     sy = moe.moe_grouped_swiglu(cfg, d["x"], d["ws_gate"], d["ws_up"], d["ws_down"])
     acc = d["x"].clone()
     moe.moe_combine(cfg, y, r["assign_to_row"], sy, out=acc, residual=acc)
@@ -289,10 +288,9 @@ def test_forward_pre_norm(moe, name):
     assert torch.equal(g["expert_ids"], ids) and torch.equal(g["gate_w"], gw)
     nflag, ndiff = P.compare_route(w, r, {"expert_ids": ids, "gate_w": gw, "counts": counts,
                                           "aux": aux, "mean_prob": g["mean_prob"]})
-    f = P.oracle_forward(w, oi, routing={"ids": ids.cpu().numpy().astype(np.int64),
-                                         "weights": gw.cpu().numpy().astype(np.float64)},
-                         residual=oi["x"], pre_norm=pre)
-    err, scale = P.compare_rows(out, f["out"], w.act_dtype, f"{name} pre-norm forward")
+    f = P.oracle_forward(w, oi, residual=oi["x"], pre_norm=pre)
+    err, scale = P.compare_tokens(out, f["out"], P.comparable_tokens(w, r["ids"], ids),
+                                  w.act_dtype, f"{name} pre-norm forward")
     _say(f"  near ties {nflag} (differing {ndiff}); max|err| {err:.3g} max|ref| {scale:.3g}")
 
 
