@@ -330,7 +330,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer runs on a single MI355X; sharding is described in DESIGN.md).",
+              "(the layer runs on a single MI355X; it shards by expert across GPUs).",
               file=sys.stderr)
         sys.exit(2)
 

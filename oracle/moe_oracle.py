@@ -25,7 +25,7 @@ Sources (the pages this follows; section names as printed on each page):
 Precision: every floating-point step runs in float64 on the exact stored input
 values (bf16 or fp32 upcast without rounding).
 
-Readings taken where the pages are silent or garbled (all listed in the design doc):
+Readings taken where the pages are silent or garbled:
   * top-k ties go to the lower expert index; slot j holds the j-th largest
     selection score (the tie rule is what makes a zero router pick experts
     0..k-1, as [BOOK] "Sparse upcycling" states);
