@@ -109,6 +109,66 @@ def test_backward_dropped_slots(moe):
 
 # ------------------------------------------------------------- full size ---
 
+def _sampled_weight_rows(g, r, keep, oi, do, w, rng, what, n_experts=3):
+    """Rows h of dW_gate/dW_up and columns h of dW_down of sampled experts
+    from the one-unit FFN of h over all of the expert's kept rows."""
+    kept_rows = [np.nonzero((r["ids"] == e) & keep) for e in range(w.E)]
+    with_rows = [e for e in range(w.E) if kept_rows[e][0].size]
+    pick = rng.choice(with_rows, size=min(n_experts, len(with_rows)), replace=False)
+    for e in pick:
+        t, s_ = kept_rows[e]
+        dF = r["weights"][t, s_][:, None] * do[t]
+        for h in rng.choice(w.H, size=2, replace=False):
+            _, dwg, dwu, dwd, _ = P.oracle.swiglu_ffn_backward(
+                oi["x"][t], oi["w_gate"][e][h:h + 1], oi["w_up"][e][h:h + 1],
+                oi["w_down"][e][:, h:h + 1], dF)
+            tag = f"{what} expert {e} unit {h}"
+            P.compare_rows(g["dw_gate"][e, h], dwg[0], "bf16", tag + " dW_gate row")
+            P.compare_rows(g["dw_up"][e, h], dwu[0], "bf16", tag + " dW_up row")
+            P.compare_rows(g["dw_down"][e, :, h], dwd[:, 0], "bf16", tag + " dW_down column")
+    return kept_rows, with_rows, pick
+
+
+def test_backward_beyond_32bit_offsets(moe):
+    """Backward of a layer whose input passes 2 GB (most operands beyond the
+    32-bit buffer offsets: the register-staged GEMM path): dx on sampled
+    tokens and sampled weight-gradient rows."""
+    w = W.Workload("beyond_2gb", 1, 262144, D=4096, H=64, E=8, top_k=2)
+    _say(f"[backward beyond 2 GB] T={w.T}: drawing inputs")
+    inp = {k: v.to("cuda") for k, v in W.make_inputs(w, "cuda", seed=23).items()}
+    oi = P.oracle_inputs(inp)
+    r = P.oracle_route(w, oi)
+    keep = r["ids"] >= 0
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(24)
+    dout = torch.randn(w.T, w.D, generator=gen, device="cuda").to(torch.bfloat16)
+    aux = (0.01, 0.001)
+    g = moe.moe_backward(P.config_of(w), inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
+                         inp["w_down"], torch.from_numpy(r["ids"].astype(np.int32)).cuda(),
+                         torch.from_numpy(r["weights"].astype(np.float32)).cuda(), dout,
+                         balance_coef=aux[0], z_coef=aux[1], d_gate_w=True)
+    torch.cuda.synchronize()
+    do = dout.to(torch.float64).cpu().numpy()
+    rng = np.random.default_rng(25)
+    toks = np.unique(np.concatenate([rng.choice(w.T, 12, replace=False), [0, w.T - 1]]))
+    dx = np.zeros((toks.size, w.D))
+    dgw = np.zeros_like(r["weights"])
+    for i, t in enumerate(toks):
+        for s_ in range(w.top_k):
+            e = r["ids"][t, s_]
+            dz, _, _, _, F = P.oracle.swiglu_ffn_backward(
+                oi["x"][t:t + 1], oi["w_gate"][e], oi["w_up"][e], oi["w_down"][e],
+                r["weights"][t, s_] * do[t:t + 1])
+            dx[i] += dz[0]
+            dgw[t, s_] = float(np.sum(do[t] * F[0]))
+    dx += P.oracle.router_backward(r, dgw, top_k=w.top_k, aux_coef=aux, tokens=toks) @ \
+        oi["w_router"]
+    sel = torch.from_numpy(toks).cuda()
+    P.compare_rows(g["dx"][sel], dx, "bf16", "beyond 2 GB dx on sampled tokens")
+    P.compare_rows(g["d_gate_w"][sel], dgw[toks], "bf16", "beyond 2 GB dL/dw")
+    _sampled_weight_rows(g, r, keep, oi, do, w, rng, "beyond 2 GB", n_experts=2)
+
+
 FULL = ["mixtral_8x_top2", "switch_top1_capacity", "decode_128x_top8"]
 
 

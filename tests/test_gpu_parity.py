@@ -380,6 +380,31 @@ def test_large_tile_path(moe, T, E, k):
     _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
 
 
+# x of exactly 2^31 bytes: past the 32-bit buffer offsets of the
+# direct-to-LDS kernels, so the grouped GEMMs take the register-staged path.
+BEYOND_2GB = W.Workload("beyond_2gb", 1, 262144, D=4096, H=64, E=8, top_k=2)
+
+
+def test_forward_beyond_32bit_offsets(moe):
+    """A layer whose input passes 2 GB: routing of every token bit-exact and
+    sampled outputs against the oracle on its own routes."""
+    w = BEYOND_2GB
+    _say(f"[beyond 2 GB] T={w.T} D={w.D}: drawing inputs")
+    inp = W.make_inputs(w, "cuda", seed=21)
+    assert inp["x"].numel() * 2 >= 1 << 31
+    out, ids, gw = _fwd(moe, w, inp)
+    _say("[beyond 2 GB] oracle routing")
+    oi = P.oracle_inputs(inp)
+    r = P.oracle_route(w, oi)
+    P.compare_route(w, r, dict(_route(moe, w, P.config_of(w), inp), expert_ids=ids, gate_w=gw))
+    toks = _sample_tokens(w.T, 24, seed=22)
+    f = P.oracle_forward(w, oi, tokens=toks)
+    same = P.comparable_tokens(w, r["ids"], ids)[toks]
+    err, scale = P.compare_tokens(out[torch.from_numpy(toks).cuda()], f["out"], same, "bf16",
+                                  "beyond 2 GB sampled outputs")
+    _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
+
+
 def test_errors_are_reported(moe):
     w = W.SMALL["mixtral_small"]
     d = _to_dev(W.make_inputs(w, "cpu", seed=0))
