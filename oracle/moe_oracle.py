@@ -76,7 +76,7 @@ __all__ = [
     "NEAR_TIE", "router_logits", "softmax", "sigmoid", "softplus", "logsumexp",
     "route", "capacity", "first_within_capacity", "permutation",
     "swiglu_ffn", "expert_outputs", "shared_expert", "combine", "forward", "update_bias",
-    "round_to_bf16", "rms_norm", "loss", "backward", "router_backward",
+    "round_to_bf16", "rms_norm", "rms_norm_backward", "loss", "backward", "router_backward",
     "swiglu_ffn_backward",
     "brute_force_forward", "all_experts_then_mask",
 ]
@@ -453,6 +453,21 @@ def rms_norm(x, weight=None, eps=1e-6, act="bf16"):
     return y
 
 
+def rms_norm_backward(x, weight, eps, dy):
+    """Gradients of sum(dy * rms_norm(x, weight, eps, act=None)): returns
+    (dx, dweight).  With s_t = sqrt(mean_d x_td^2 + eps):
+    dx_td = w_d dy_td / s_t - x_td sum_j(dy_tj w_j x_tj) / (D s_t^3) and
+    dweight_d = sum_t dy_td x_td / s_t (w = 1 when ``weight`` is None)."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    D = x.shape[1]
+    w = np.ones(D) if weight is None else np.asarray(weight, dtype=np.float64)
+    s = np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    g = dy * w[None, :]
+    dx = g / s - x * np.sum(g * x, axis=1, keepdims=True) / (D * s ** 3)
+    return dx, np.sum(dy * x / s, axis=0)
+
+
 # ------------------------------------------------ bias-adjustment balancer ---
 
 def update_bias(bias, counts, gamma):
@@ -564,9 +579,11 @@ def router_backward(r, d_gate_w, *, top_k, score="softmax", renormalize=True,
 
 def backward(inputs, dout, *, top_k, score="softmax", renormalize=True, route_scale=1.0,
              n_groups=1, topk_groups=1, group_rule="top2sum", capacity_factor=None,
-             token_mask=None, swiglu_limit=0.0, aux_coef=(0.0, 0.0)):
+             token_mask=None, swiglu_limit=0.0, aux_coef=(0.0, 0.0), pre_norm=None):
     """Gradients of ``loss`` with respect to x, W_r and every expert weight
-    (float64).  Returns dx, dw_router, dw_gate, dw_up, dw_down (+ dws_gate,
+    (float64).  With ``pre_norm`` = (weight, eps, act) the layer takes
+    rms_norm(x) (rounded to ``act``; the rounding passes gradients through
+    unchanged) and the result also holds d_norm_weight.  Returns dx, dw_router, dw_gate, dw_up, dw_down (+ dws_gate,
     dws_up, dws_down with a shared expert), and the intermediates
     d_gate_w [T,k] (dL/dw per slot) and d_logits [T,E]."""
     fw = dict(top_k=top_k, score=score, renormalize=renormalize, route_scale=route_scale,
@@ -575,6 +592,13 @@ def backward(inputs, dout, *, top_k, score="softmax", renormalize=True, route_sc
               swiglu_limit=swiglu_limit)
     if inputs.get("ws_sgate") is not None:
         raise ValueError("backward: the shared-expert gate is not covered")
+    if pre_norm is not None:
+        x_raw = np.asarray(inputs["x"], dtype=np.float64)
+        inner = backward(dict(inputs, x=rms_norm(x_raw, *pre_norm)), dout, aux_coef=aux_coef,
+                         **fw)
+        inner["dx"], inner["d_norm_weight"] = rms_norm_backward(
+            x_raw, pre_norm[0], pre_norm[1], inner["dx"])
+        return inner
     f = forward(inputs, **fw)
     r = f["route"]
     x = np.asarray(inputs["x"], dtype=np.float64)

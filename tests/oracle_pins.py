@@ -725,4 +725,51 @@ def pin_router_backward_rows(o):
     assert np.array_equal(sub, full[[1, 4, 11]])
 
 
+def pin_backward_fd_pre_norm(o):
+    """The pre-normed layer (without the rounding of the normalised rows):
+    central differences for x, the norm weight and the experts; dx then
+    includes the norm's own Jacobian."""
+    inp = _tiny_inputs(64, T=10, E=4, shared=True)
+    r = _rng(65)
+    nw = r.uniform(0.5, 1.5, size=inp["x"].shape[1])
+    dout = r.normal(size=inp["x"].shape)
+    aux = (0.2, 0.1)
+    fw = dict(top_k=2)
+    g = o.backward(inp, dout, aux_coef=aux, pre_norm=(nw, 0.05, None), **fw)
+    eps = 1e-6
+    base = o.forward(inp, pre_norm=(nw, 0.05, None), **fw)
+    for name in ("x", "w_gate", "w_router", "norm"):
+        V = r.normal(size=nw.shape if name == "norm" else np.shape(inp[name]))
+        vals = []
+        for sgn in (1, -1):
+            if name == "norm":
+                lv, f = o.loss(inp, dout, aux, pre_norm=(nw + sgn * eps * V, 0.05, None), **fw)
+            else:
+                lv, f = o.loss(dict(inp, **{name: inp[name] + sgn * eps * V}), dout, aux,
+                               pre_norm=(nw, 0.05, None), **fw)
+            assert np.array_equal(f["route"]["ids"], base["route"]["ids"]), "route moved"
+            vals.append(lv)
+        fd = (vals[0] - vals[1]) / (2 * eps)
+        an = float(np.sum((g["d_norm_weight"] if name == "norm" else g[GRAD_OF[name]]) * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def pin_rms_norm_backward_loops(o):
+    """The RMSNorm gradients against a pure-Python loop of the chain rule."""
+    r = _rng(66)
+    x, w, dy = r.normal(size=(3, 5)), r.uniform(0.5, 2, 5), r.normal(size=(3, 5))
+    dx, dw = o.rms_norm_backward(x, w, 0.3, dy)
+    for t in range(3):
+        s = math.sqrt(sum(v * v for v in x[t]) / 5 + 0.3)
+        for d in range(5):
+            ref = 0.0
+            for j in range(5):  # d y_tj / d x_td
+                dyj_dxd = (w[j] / s) * ((1.0 if j == d else 0.0) - x[t, j] * x[t, d] / (5 * s * s))
+                ref += dy[t, j] * dyj_dxd
+            assert abs(dx[t, d] - ref) < 1e-13
+    for d in range(5):
+        assert abs(dw[d] - sum(dy[t, d] * x[t, d] / math.sqrt(np.mean(x[t] ** 2) + 0.3)
+                               for t in range(3))) < 1e-13
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -170,6 +170,15 @@ MUTANTS = [
     ("bwd_shared_expert_dx_missing",
      "        dx += dz\n        out.update(dws_gate=dwg",
      "        dx += 0 * dz\n        out.update(dws_gate=dwg"),
+    ("rms_bwd_projection_dropped",
+     "dx = g / s - x * np.sum(g * x, axis=1, keepdims=True) / (D * s ** 3)",
+     "dx = g / s"),
+    ("rms_bwd_wrong_power",
+     "dx = g / s - x * np.sum(g * x, axis=1, keepdims=True) / (D * s ** 3)",
+     "dx = g / s - x * np.sum(g * x, axis=1, keepdims=True) / (D * s ** 2)"),
+    ("rms_bwd_weight_grad_unnormalised",
+     "return dx, np.sum(dy * x / s, axis=0)",
+     "return dx, np.sum(dy * x, axis=0)"),
     ("router_bias_ignored",
      "h = h + np.asarray(logit_bias, dtype=np.float64)[None, :]",
      "h = h + 0.0"),
