@@ -246,7 +246,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
                        size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes of moe_backward (0 if the configuration is invalid or not
- * covered by the backward: bf16 activations without pre_norm). */
+ * covered by the backward: bf16 activations only). */
 size_t moe_backward_workspace_bytes(const moe_config* cfg);
 
 /* Backward pass of the layer ("Lab: build a tiny MoE in PyTorch", "Smoke test
@@ -257,7 +257,9 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg);
  * the index decision ("The Router"), f is detached ("The auxiliary
  * load-balancing loss")); gradients reach the router through the gate weights
  * of the kept slots, through P_e and through z.
- *   x, w_router, logit_bias, w_gate, w_up, w_down, w_shared_*: as moe_forward
+ *   x, norm_weight, w_router, logit_bias, w_gate, w_up, w_down, w_shared_*:
+ *                       as moe_forward (x is the layer input before the
+ *                       pre-norm when cfg->pre_norm = 1)
  *   expert_ids, gate_w  [T, k]: the routes and gate weights of the forward
  *                       (moe_route / moe_forward outputs; -1 marks a masked
  *                       token)
@@ -268,19 +270,25 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg);
  *                       the shapes of w_shared_* (required when H_shared > 0)
  *   d_gate_w            [T, k] f32 out or NULL: dL/d gate weight per slot
  *                       (0 for dropped and masked slots)
- * bf16 activations only; pre_norm and the shared-expert gate are not
- * covered.  fp32 accumulation; intermediates (the SwiGLU factors, dL/dg and
+ *   d_norm_weight       [D] f32 out or NULL (pre_norm only): dL/d norm weight
+ * With the pre-norm ("Transformer Architecture": the block normalises its
+ * input before the sublayer, RMSNorm), the rows are renormalised with the
+ * forward's kernel and the gradient passes back through the norm:
+ * with s = sqrt(mean(x^2) + eps) and g = norm_weight * dL/dy,
+ *   dx = g / s - x * sum(g x) / (D s^3),   dL/dw_d = sum_t dL/dy_td x_td / s_t,
+ * dL/dy kept fp32, dx rounded once.
+ * bf16 activations only; the shared-expert gate is not covered.  fp32 accumulation; intermediates (the SwiGLU factors, dL/dg and
  * dL/du, dL/dh) are rounded to bf16 between GEMMs.  Deterministic: no float
  * atomics, every sum runs in a fixed order. */
-moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
-                        const float* logit_bias, const void* w_gate, const void* w_up,
-                        const void* w_down, const void* w_shared_gate, const void* w_shared_up,
-                        const void* w_shared_down, const int32_t* expert_ids,
-                        const float* gate_w, const void* dout, float balance_coef,
-                        float z_coef, void* dx, float* dw_router, float* dw_gate, float* dw_up,
-                        float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
-                        float* d_gate_w, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream);
+moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_weight,
+                        const void* w_router, const float* logit_bias, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* w_shared_gate,
+                        const void* w_shared_up, const void* w_shared_down,
+                        const int32_t* expert_ids, const float* gate_w, const void* dout,
+                        float balance_coef, float z_coef, void* dx, float* dw_router,
+                        float* dw_gate, float* dw_up, float* dw_down, float* dws_gate,
+                        float* dws_up, float* dws_down, float* d_gate_w, float* d_norm_weight,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Auxiliary-loss-free balancer step ("DeepSeek-MoE and the fine-grained +
  * shared-expert idea" and "Exercises" 6 on the book page; NeMo

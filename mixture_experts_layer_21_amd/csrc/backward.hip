@@ -651,6 +651,10 @@ __global__ __launch_bounds__(256) void dx_kernel(DxParams p) {
       if (r >= 0) s += *reinterpret_cast<const f32x4*>(p.dz + (long long)r * p.D + d);
     }
     if (p.dzs) s += *reinterpret_cast<const f32x4*>(p.dzs + o);
+    if (p.dx_f32) {
+      *reinterpret_cast<f32x4*>(p.dx_f32 + o) = s;
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) Elem<T>::store(static_cast<T*>(p.dx), o + i, s[i]);
   }

@@ -208,7 +208,8 @@ struct DxParams {
   const int32_t* a2r;
   const float* dzs;          // [T, D] or null (shared expert)
   const float* dxr;          // [T, D] (router)
-  void* dx;                  // [T, D] act dtype
+  void* dx;                  // [T, D] act dtype, or null with dx_f32
+  float* dx_f32;             // [T, D] fp32 out instead of dx (the pre-norm backward's input)
 };
 
 hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s);
@@ -228,6 +229,12 @@ hipError_t launch_update_bias(int E, const int32_t* counts, float gamma, float* 
                               hipStream_t s);
 hipError_t launch_rmsnorm(int T, int D, bool bf16, const void* x, const float* w, float eps,
                           void* y, hipStream_t s);
+// Backward of launch_rmsnorm: dx from dy (fp32 [T, D]); with dw (f32 [D]) also
+// the weight gradient through dw_part (f32 [rmsnorm_dw_chunks(T), D]).
+int rmsnorm_dw_chunks(int T);
+hipError_t launch_rmsnorm_bwd(int T, int D, bool bf16, const void* x, const float* w, float eps,
+                              const float* dy, void* dx, float* inv_s, float* dw_part,
+                              float* dw, hipStream_t s);
 
 inline int route_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
 

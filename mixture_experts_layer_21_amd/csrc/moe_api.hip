@@ -158,7 +158,8 @@ Layout layout_of(const moe_config* c) {
 // then the backward's own buffers.
 struct BwdLayout {
   size_t logits, padoff, wdT, wguT, wrT, act, p1, p2, dact, dgu, dw, dh, dz, dxr, dFT, XT, AT,
-      DGUT, dhT, xT, swdT, swguT, sact, sp1, sp2, sdact, sdgu, sdz, doutT, sAT, sDGUT, total;
+      DGUT, dhT, xT, swdT, swguT, sact, sp1, sp2, sdact, sdgu, sdz, doutT, sAT, sDGUT, ninv,
+      ndwp, total;
   int Epad, Tpad, Kpad;
 };
 
@@ -210,6 +211,10 @@ BwdLayout bwd_layout_of(const moe_config* c) {
     B.sAT = take(Hs * Tp * 2);
     B.sDGUT = take(2 * Hs * Tp * 2);
   }
+  if (c->pre_norm) {  // the norm's backward: 1/s per row, weight-gradient partials
+    B.ninv = take(T * 4);
+    B.ndwp = take((size_t)moe::rmsnorm_dw_chunks((int)T) * D * 4);
+  }
   B.total = off;
   return B;
 }
@@ -221,6 +226,13 @@ moe_status check_ws(const moe_config* c, void* ws, size_t bytes) {
     return fail(MOE_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
   if (bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", bytes, need);
+  return MOE_OK;
+}
+
+// The norm kernels move 16-byte chunks.
+moe_status check_align16(const void* p, const char* name) {
+  if (reinterpret_cast<uintptr_t>(p) % 16)
+    return fail(MOE_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
   return MOE_OK;
 }
 
@@ -528,6 +540,9 @@ moe_status moe_rmsnorm(const moe_config* cfg, const void* x, const float* norm_w
   MOE_TRY(check_dev(x, "x", true));
   MOE_TRY(check_dev(norm_weight, "norm_weight", false));
   MOE_TRY(check_dev(x_norm, "x_norm", true));
+  MOE_TRY(check_align16(x, "x"));
+  MOE_TRY(check_align16(norm_weight, "norm_weight"));
+  MOE_TRY(check_align16(x_norm, "x_norm"));
   MOE_TRY(hip_ok(moe::launch_rmsnorm(cfg->T, cfg->D, cfg->act_dtype == MOE_BF16, x, norm_weight,
                                      cfg->norm_eps, x_norm, stream),
                  "rmsnorm kernel"));
@@ -575,6 +590,10 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
   MOE_TRY(check_dev(counts, "counts", false));
   MOE_TRY(check_dev(aux, "aux", false));
   MOE_TRY(check_dev(workspace, "workspace", true));
+  if (cfg->pre_norm) {
+    MOE_TRY(check_align16(x, "x"));
+    MOE_TRY(check_align16(norm_weight, "norm_weight"));
+  }
 
   const Layout L = layout_of(cfg);
   int32_t* ids = expert_ids ? expert_ids : at<int32_t>(workspace, L.ids);
@@ -642,23 +661,25 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
 }
 
 size_t moe_backward_workspace_bytes(const moe_config* cfg) {
-  if (check_config(cfg) != MOE_OK || cfg->act_dtype != MOE_BF16 || cfg->pre_norm) return 0;
+  if (check_config(cfg) != MOE_OK || cfg->act_dtype != MOE_BF16) return 0;
   return bwd_layout_of(cfg).total;
 }
 
-moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
-                        const float* logit_bias, const void* w_gate, const void* w_up,
-                        const void* w_down, const void* w_shared_gate, const void* w_shared_up,
-                        const void* w_shared_down, const int32_t* expert_ids,
-                        const float* gate_w, const void* dout, float balance_coef,
-                        float z_coef, void* dx, float* dw_router, float* dw_gate, float* dw_up,
-                        float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
-                        float* d_gate_w, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
+moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_weight,
+                        const void* w_router, const float* logit_bias, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* w_shared_gate,
+                        const void* w_shared_up, const void* w_shared_down,
+                        const int32_t* expert_ids, const float* gate_w, const void* dout,
+                        float balance_coef, float z_coef, void* dx, float* dw_router,
+                        float* dw_gate, float* dw_up, float* dw_down, float* dws_gate,
+                        float* dws_up, float* dws_down, float* d_gate_w, float* d_norm_weight,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_config(cfg));
   if (cfg->act_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "moe_backward: bf16 activations only");
-  if (cfg->pre_norm) return fail(MOE_ERR_UNSUPPORTED, "moe_backward: pre_norm is not covered");
+  if ((norm_weight || d_norm_weight) && !cfg->pre_norm)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_backward: norm_weight and d_norm_weight need cfg->pre_norm = 1");
   if (!x || !w_router || !w_gate || !w_up || !w_down || !expert_ids || !gate_w || !dout ||
       !dx || !dw_router || !dw_gate || !dw_up || !dw_down)
     return fail(MOE_ERR_NULL_PTR, "moe_backward: inputs, routing and gradient outputs required");
@@ -682,6 +703,13 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   for (int i = 0; i < 14; ++i) MOE_TRY(check_dev(dev_in[i], names[i], true));
   MOE_TRY(check_dev(logit_bias, "logit_bias", false));
   MOE_TRY(check_dev(d_gate_w, "d_gate_w", false));
+  MOE_TRY(check_dev(norm_weight, "norm_weight", false));
+  MOE_TRY(check_dev(d_norm_weight, "d_norm_weight", false));
+  if (cfg->pre_norm) {
+    MOE_TRY(check_align16(x, "x"));
+    MOE_TRY(check_align16(norm_weight, "norm_weight"));
+    MOE_TRY(check_align16(dx, "dx"));
+  }
   if (sh) {
     MOE_TRY(check_dev(w_shared_gate, "w_shared_gate", true));
     MOE_TRY(check_dev(w_shared_up, "w_shared_up", true));
@@ -704,6 +732,16 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   int32_t* a2r = at<int32_t>(workspace, L.a2r);
   int32_t* counts = at<int32_t>(workspace, L.counts_ws);
   int32_t* padoff = at<int32_t>(workspace, B.padoff);
+
+  // 0. with the pre-norm, the layer's input is the normalised rows, recomputed
+  // by the forward's own kernel (bit-identical)
+  const void* x_raw = x;
+  if (cfg->pre_norm) {
+    void* xn = ws(L.x_norm);
+    MOE_TRY(hip_ok(moe::launch_rmsnorm(T, D, true, x, norm_weight, cfg->norm_eps, xn, stream),
+                   "rmsnorm kernel"));
+    x = xn;
+  }
 
   // 1. the forward's permutation, from the given routes
   MOE_TRY(hip_ok(moe::launch_hist(T, E, k, expert_ids, at<int32_t>(workspace, L.hist), stream),
@@ -956,8 +994,16 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     MOE_TRY(gemm(z, "shared gate/up dgrad"));
   }
   {
-    moe::DxParams p{T, D, k, f32(B.dz), a2r, sh ? f32(B.sdz) : nullptr, f32(B.dxr), dx};
+    // with the pre-norm, dL/d(normalised rows) stays fp32, in place over the
+    // router's dx (each element is read before it is written, by one thread)
+    moe::DxParams p{T, D, k, f32(B.dz), a2r, sh ? f32(B.sdz) : nullptr, f32(B.dxr),
+                    cfg->pre_norm ? nullptr : dx, cfg->pre_norm ? f32(B.dxr) : nullptr};
     MOE_TRY(hip_ok(moe::launch_dx(p, true, stream), "dx kernel"));
+    if (cfg->pre_norm)
+      MOE_TRY(hip_ok(moe::launch_rmsnorm_bwd(T, D, true, x_raw, norm_weight, cfg->norm_eps,
+                                             f32(B.dxr), dx, f32(B.ninv), f32(B.ndwp),
+                                             d_norm_weight, stream),
+                     "rmsnorm backward kernel"));
   }
 
   // 8. weight gradients: operands transposed, each expert's rows padded to 64

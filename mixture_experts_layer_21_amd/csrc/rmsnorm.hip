@@ -136,7 +136,121 @@ __global__ __launch_bounds__(NTHREADS) void rmsnorm_kernel(int T, int D, const v
   }
 }
 
+// Backward of the norm, one wave per row: with g = w * dy,
+//   dx = g / s - x * sum_d(g x) / (D s^3)
+// (s as in the forward, fp64), rounded once to the activation dtype; 1/s of
+// every row goes to inv_s for the weight gradient.
+template <bool BF16>
+__global__ __launch_bounds__(NTHREADS) void rmsnorm_bwd_kernel(int T, int D, const void* x,
+                                                               const float* w, double eps,
+                                                               const float* dy, void* dx,
+                                                               float* inv_s) {
+  using C = Chunk<BF16>;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave
+  const int nch = D / C::N;
+  const size_t row_bytes = (size_t)D * (BF16 ? 2 : 4);
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + t * row_bytes);
+  const float* dyr = dy + (size_t)t * D;
+  double ss = 0.0, gx = 0.0;
+  for (int c = lane; c < nch; c += 64) {
+    double v[C::N];
+    C::unpack(src[c], v);
+#pragma unroll
+    for (int e = 0; e < C::N; ++e) {
+      const double g = (double)dyr[c * C::N + e] * (w ? (double)w[c * C::N + e] : 1.0);
+      ss = fma(v[e], v[e], ss);
+      gx = fma(g, v[e], gx);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    ss += __shfl_xor(ss, off);
+    gx += __shfl_xor(gx, off);
+  }
+  const double s = sqrt(ss / (double)D + eps);
+  const double inv = 1.0 / s, k = gx / ((double)D * s * s * s);
+  if (lane == 0 && inv_s) inv_s[t] = (float)inv;
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(dx) + t * row_bytes);
+  for (int c = lane; c < nch; c += 64) {
+    double v[C::N];
+    C::unpack(src[c], v);
+#pragma unroll
+    for (int e = 0; e < C::N; ++e) {
+      const double g = (double)dyr[c * C::N + e] * (w ? (double)w[c * C::N + e] : 1.0);
+      v[e] = g * inv - v[e] * k;
+    }
+    dst[c] = C::pack(v);
+  }
+}
+
+// Weight gradient of the norm, sum_t dy_td x_td / s_t: each block sums a chunk
+// of rows (256, more past 2^24 rows to keep the grid's y extent within 65535)
+// for 256 columns in row order; a second pass adds the chunks in order.
+constexpr int kNormRowsPerChunk = 256;
+constexpr int kMaxChunks = 65535;
+
+int rows_per_chunk(int T) {
+  const int per = (T + kMaxChunks - 1) / kMaxChunks;
+  return per > kNormRowsPerChunk ? per : kNormRowsPerChunk;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void rmsnorm_dw_part_kernel(int T, int D, const void* x,
+                                                              const float* dy,
+                                                              const float* inv_s, int per,
+                                                              float* part) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= D) return;
+  const long long t0 = (long long)blockIdx.y * per;
+  const long long t1 = min((long long)T, t0 + per);
+  float acc = 0.f;
+  for (long long t = t0; t < t1; ++t) {
+    const float xv = BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(x)[(size_t)t * D + d])
+                          : static_cast<const float*>(x)[(size_t)t * D + d];
+    acc += dy[(size_t)t * D + d] * xv * inv_s[t];
+  }
+  part[(size_t)blockIdx.y * D + d] = acc;
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_dw_final_kernel(int D, int nchunk,
+                                                               const float* part, float* dw) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= D) return;
+  float acc = part[d];
+  for (int c = 1; c < nchunk; ++c) acc += part[(size_t)c * D + d];
+  dw[d] = acc;
+}
+
 }  // namespace
+
+int rmsnorm_dw_chunks(int T) { return (T + rows_per_chunk(T) - 1) / rows_per_chunk(T); }
+
+hipError_t launch_rmsnorm_bwd(int T, int D, bool bf16, const void* x, const float* w, float eps,
+                              const float* dy, void* dx, float* inv_s, float* dw_part,
+                              float* dw, hipStream_t s) {
+  const int blocks = (T + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  if (bf16)
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<true>, dim3(blocks), dim3(NTHREADS), 0, s, T, D, x, w,
+                       (double)eps, dy, dx, inv_s);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<false>, dim3(blocks), dim3(NTHREADS), 0, s, T, D, x, w,
+                       (double)eps, dy, dx, inv_s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !dw) return err;
+  const dim3 grid((D + 255) / 256, rmsnorm_dw_chunks(T));
+  if (bf16)
+    hipLaunchKernelGGL(rmsnorm_dw_part_kernel<true>, grid, dim3(256), 0, s, T, D, x, dy, inv_s,
+                       rows_per_chunk(T), dw_part);
+  else
+    hipLaunchKernelGGL(rmsnorm_dw_part_kernel<false>, grid, dim3(256), 0, s, T, D, x, dy, inv_s,
+                       rows_per_chunk(T), dw_part);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(rmsnorm_dw_final_kernel, dim3((D + 255) / 256), dim3(256), 0, s, D,
+                     rmsnorm_dw_chunks(T), dw_part, dw);
+  return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm(int T, int D, bool bf16, const void* x, const float* w, float eps,
                           void* y, hipStream_t s) {

@@ -88,6 +88,46 @@ def test_pre_norm_workspace_holds_the_rows(moe):
     assert b - a >= 4096 * 4096 * 2
 
 
+def test_backward_workspace_covers_pre_norm(moe):
+    """The backward covers bf16 with and without the pre-norm (its norm
+    scratch adds the rows' 1/s and the weight-gradient partials); not fp32."""
+    a = moe.backward_workspace_bytes(moe.make_config(4096, 4096, 14336, 8, 2))
+    b = moe.backward_workspace_bytes(moe.make_config(4096, 4096, 14336, 8, 2, pre_norm=True))
+    assert 0 < a and b - a >= 4096 * 4096 * 2 + 4096 * 4 + 16 * 4096 * 4
+    assert moe.backward_workspace_bytes(
+        moe.make_config(256, 64, 128, 4, 2, act_dtype="f32", router_dtype="f32")) == 0
+
+
+def test_backward_host_checks(moe):
+    """Argument errors of moe_backward found before any device access."""
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    f = lib.moe_backward
+    f.restype = ctypes.c_int
+    f.argtypes = list(moe._binding._sigs["moe_backward"][1])
+    nargs = len(f.argtypes)
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(cfg, norm_weight=None, d_norm_weight=None):
+        args = [ctypes.byref(cfg)] + [fake] * (nargs - 1)
+        args[2], args[25] = norm_weight, d_norm_weight  # norm_weight, d_norm_weight
+        args[14] = args[15] = 0.0  # loss coefficients
+        args[-2], args[-1] = 0, None  # workspace bytes, stream
+        return f(*args)
+
+    assert nargs == 29
+    cfg = moe.make_config(256, 64, 128, 4, 2)
+    assert call(cfg, norm_weight=fake) == 1  # MOE_ERR_INVALID_ARG: needs pre_norm
+    assert "pre_norm" in lib_error(moe)
+    assert call(cfg, d_norm_weight=fake) == 1
+    f32 = moe.make_config(256, 64, 128, 4, 2, act_dtype="f32", router_dtype="f32")
+    assert call(f32) == 3  # MOE_ERR_UNSUPPORTED
+    assert "bf16" in lib_error(moe)
+
+
+def lib_error(moe):
+    return moe._binding._lib.moe_last_error().decode()
+
+
 def test_workspace_grows_with_problem(moe):
     a = moe.workspace_bytes(moe.make_config(256, 64, 128, 4, 2, act_dtype="f32", router_dtype="f32"))
     b = moe.workspace_bytes(moe.make_config(4096, 4096, 14336, 8, 2))

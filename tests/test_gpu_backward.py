@@ -32,31 +32,45 @@ def _say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _run(moe, w, seed, aux=(0.3, 0.2), token_mask=None, swiglu_limit=0.0):
+def _run(moe, w, seed, aux=(0.3, 0.2), token_mask=None, swiglu_limit=0.0, pre_norm=None):
+    """``pre_norm`` = (norm weight [D] f32 CPU tensor or None, eps): the layer
+    takes RMSNorm(x) and x is the input before the norm."""
     inp = W.make_inputs(w, "cpu", seed=seed)
     oi = P.oracle_inputs(inp)
+    x_route = oi["x"]
+    if pre_norm is not None:
+        nw, eps = pre_norm
+        pre = (np.ones(w.D) if nw is None else nw.to(torch.float64).numpy(),
+               float(np.float32(eps)), w.act_dtype)
+        x_route = P.oracle.rms_norm(oi["x"], *pre)
     dout = torch.randn(w.T, w.D, generator=torch.Generator().manual_seed(seed + 1)).to(
         W.torch_dtype(w.act_dtype))
     fw = dict(top_k=w.top_k, score=w.score, renormalize=w.renormalize,
               route_scale=w.route_scale, n_groups=w.n_groups, topk_groups=w.topk_groups,
               group_rule=w.group_rule, capacity_factor=w.capacity_factor,
               token_mask=token_mask, swiglu_limit=swiglu_limit)
-    ref = P.oracle.backward(oi, dout.to(torch.float64).numpy(), aux_coef=aux, **fw)
-    r = P.oracle.route(oi["x"], oi["w_router"], w.top_k, score=w.score,
+    ref = P.oracle.backward(oi, dout.to(torch.float64).numpy(), aux_coef=aux,
+                            pre_norm=None if pre_norm is None else pre, **fw)
+    r = P.oracle.route(x_route, oi["w_router"], w.top_k, score=w.score,
                        renormalize=w.renormalize, route_scale=w.route_scale,
                        logit_bias=oi.get("logit_bias"), select_bias=oi.get("select_bias"),
                        n_groups=w.n_groups, topk_groups=w.topk_groups,
                        group_rule=w.group_rule, token_mask=token_mask)
     d = {k: v.to("cuda") for k, v in inp.items()}
     cfg = P.config_of(w, swiglu_limit=swiglu_limit)
+    nw_dev = None
+    if pre_norm is not None:
+        cfg.pre_norm, cfg.norm_eps = 1, eps
+        nw_dev = None if nw is None else nw.cuda()
     ids = torch.from_numpy(r["ids"].astype(np.int32)).cuda()
     gw = torch.from_numpy(r["weights"].astype(np.float32)).cuda()
-    _say(f"[backward] {w.name} T={w.T} E={w.E} k={w.top_k} aux={aux} limit={swiglu_limit}")
+    _say(f"[backward] {w.name} T={w.T} E={w.E} k={w.top_k} aux={aux} limit={swiglu_limit} "
+         f"pre_norm={pre_norm is not None}")
     g = moe.moe_backward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"], ids,
                          gw, dout.cuda(), logit_bias=d.get("logit_bias"),
                          ws_gate=d.get("ws_gate"), ws_up=d.get("ws_up"),
                          ws_down=d.get("ws_down"), balance_coef=aux[0], z_coef=aux[1],
-                         d_gate_w=True)
+                         d_gate_w=True, norm_weight=nw_dev)
     torch.cuda.synchronize()
     return g, ref
 
@@ -94,6 +108,34 @@ def test_backward_token_mask_and_clamp(moe):
     g, ref = _run(moe, w, seed=32, token_mask=mask, swiglu_limit=0.05)
     _compare(g, ref, GRADS + SHARED + ("d_gate_w",), "masked, clamped")
     assert (g["d_gate_w"].cpu().numpy()[~mask] == 0).all()
+
+
+@pytest.mark.parametrize("name,unit_weight", [("mixtral_small", False),
+                                              ("deepseek_small", False),
+                                              ("decode_small", True)])
+def test_backward_pre_norm(moe, name, unit_weight):
+    """Backward of MoE(RMSNorm(x)): every gradient, and dL/d norm weight,
+    through the norm against the oracle's chain rule; deterministic."""
+    w = W.SMALL[name]
+    nw = None if unit_weight else \
+        torch.rand(w.D, generator=torch.Generator().manual_seed(34)) + 0.5
+    g, ref = _run(moe, w, seed=34, pre_norm=(nw, 1e-5))
+    names = GRADS + (SHARED if w.H_shared else ()) + ("d_gate_w", "d_norm_weight")
+    _compare(g, ref, names, f"{name} pre-norm")
+    g2, _ = _run(moe, w, seed=34, pre_norm=(nw, 1e-5))
+    for n in names:
+        assert torch.equal(g[n], g2[n]), n
+
+
+def test_norm_weight_needs_pre_norm_backward(moe):
+    w = W.SMALL["mixtral_small"]
+    d = {k: v.to("cuda") for k, v in W.make_inputs(w, "cpu", seed=35).items()}
+    ids = torch.zeros(w.T, w.top_k, dtype=torch.int32, device="cuda")
+    ids[:, 1] = 1
+    gw = torch.full((w.T, w.top_k), 0.5, device="cuda")
+    with pytest.raises(moe.MoeError, match="pre_norm"):
+        moe.moe_backward(P.config_of(w), d["x"], d["w_router"], d["w_gate"], d["w_up"],
+                         d["w_down"], ids, gw, d["x"], norm_weight=torch.ones(w.D, device="cuda"))
 
 
 def test_backward_dropped_slots(moe):
