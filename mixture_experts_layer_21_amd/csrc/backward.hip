@@ -142,6 +142,10 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
     }
     a_src[i] = p.A + arow + kc * 8;
     const uint16_t* bb;
+    if (p.b_kmajor) {  // chunk c: k row c / 16, columns 8*(c % 16) .. +7
+      b_src[i] = nullptr;
+      continue;
+    }
     if (EPI == BWD_EPI_GATEUP_SAVE) {
       // 64 gate rows then the same 64 up rows of column tile nt
       int n = t.nt * (BBN / 2) + (r % (BBN / 2));
@@ -169,14 +173,35 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
       ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kt * BBK);
-      rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + (size_t)kt * BBK);
+      if (p.b_kmajor) {
+        const int c = tid + BT * i, k = kt * BBK + c / (BBN / 8);
+        int n = t.nt * BBN + (c % (BBN / 8)) * 8;
+        if (n >= p.N) n = 0;
+        const uint16_t* src = k >= p.k_split
+            ? p.B2 + (long long)t.g * p.b_gstride + (long long)(k - p.k_split) * p.ldb + n
+            : p.B + (long long)t.g * p.b_gstride + (long long)k * p.ldb + n;
+        rb[i] = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + (size_t)kt * BBK);
+      }
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
       *reinterpret_cast<u32x4*>(&As[buf][dst[i]]) = ra[i];
-      *reinterpret_cast<u32x4*>(&Bs[buf][dst[i]]) = rb[i];
+      if (p.b_kmajor) {  // 8 columns of one k row into the n-major tile
+        const int c = tid + BT * i, k = c / (BBN / 8), n0 = (c % (BBN / 8)) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int n = n0 + e;
+          const uint32_t w = rb[i][e >> 1];
+          Bs[buf][n * BBK + ((k >> 3) ^ bswz(n)) * 8 + (k & 7)] =
+              (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+        }
+      } else {
+        *reinterpret_cast<u32x4*>(&Bs[buf][dst[i]]) = rb[i];
+      }
     }
   };
   if (nk > 0) {
@@ -263,7 +288,7 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
 // threads, BK = 64, two LDS stages, operands fetched straight into the
 // swizzled LDS tiles by buffer loads with 32-bit offsets.  With the paired
 // gate/up tile the B tile is 128 gate rows then the same 128 up rows.
-template <int EPI>
+template <int EPI, bool BTR>
 __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   constexpr bool PAIRED = EPI == BWD_EPI_GATEUP_SAVE;
   using C = dma::DmaCfg<256, 256, 64, 2, 2, 8, PAIRED>;
@@ -285,8 +310,9 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   const __amdgpu_buffer_rsrc_t rG =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + bg), 0, (int)p.b_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rU =
-      PAIRED ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.B2 + bg), 0, (int)p.b_bytes, 0x00020000)
-             : rG;
+      (PAIRED || (BTR && p.B2))
+          ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.B2 + bg), 0, (int)p.b_bytes, 0x00020000)
+          : rG;
   uint32_t a_off[C::A_LD];
 #pragma unroll
   for (int i = 0; i < C::A_LD; ++i) {
@@ -301,14 +327,26 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   uint32_t b_off[C::B_LD];
 #pragma unroll
   for (int i = 0; i < C::B_LD; ++i) {
-    const int slot = (wave + C::NW * i) * 64 + lane;
-    const int r = slot / KCH, lc = (slot % KCH) ^ dma::swz_k<KCH>(r);
-    int n = t.nt * C::BN + (PAIRED ? r % C::BN : r);
-    if (n >= p.N) n = 0;
-    const long long row = (long long)n * p.ldb + (kr ? t.k0 : 0);
-    b_off[i] = (uint32_t)(row * 2) + (uint32_t)lc * 16u;
+    if constexpr (BTR) {
+      // k-major tile: a wave load is two k rows of 32 chunks (8 columns
+      // each); chunk c of row k sits at c ^ 4*(k%4) (the layout the
+      // transposed fragment reads expect)
+      const int k = 2 * (wave + C::NW * i) + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (k & 3));
+      int n = t.nt * C::BN + c * 8;
+      if (n >= p.N) n = 0;
+      b_off[i] = (uint32_t)(((long long)k * p.ldb + n) * 2);
+    } else {
+      const int slot = (wave + C::NW * i) * 64 + lane;
+      const int r = slot / KCH, lc = (slot % KCH) ^ dma::swz_k<KCH>(r);
+      int n = t.nt * C::BN + (PAIRED ? r % C::BN : r);
+      if (n >= p.N) n = 0;
+      const long long row = (long long)n * p.ldb + (kr ? t.k0 : 0);
+      b_off[i] = (uint32_t)(row * 2) + (uint32_t)lc * 16u;
+    }
   }
-  const dma::DmaLoads<C, PAIRED> ld{rA, rG, rU, a_off, b_off, wave};
+  const dma::DmaLoads<C, PAIRED> ld{rA, rG, rU, a_off, b_off, wave,
+                                    (uint32_t)(p.ldb * 2), BTR ? p.k_split : 0};
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int lr = lane & 31, lk = lane >> 5;
   f32x16 acc[NB][MI][NI];
@@ -325,8 +363,8 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   // deduction; kernel bodies are never run on the host.)
 #if defined(__HIP_DEVICE_COMPILE__)
   if (nk > 0)
-    dma::dma_mainloop<C, PAIRED, false>(ld, nk, MI, wm, wn, lr, lk, acc, sA0, sA1, sX, sX, sB0,
-                                        sB1, sX, sX);
+    dma::dma_mainloop<C, PAIRED, false, BTR>(ld, nk, MI, wm, wn, lr, lk, acc, sA0, sA1, sX, sX,
+                                             sB0, sB1, sX, sX);
 #endif
 
   // Epilogue: element i of accumulator (nb, mi, ni) of lane l is row
@@ -673,14 +711,15 @@ hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s) {
     else
       blocks = (long long)nN * ((p.max_rows + 255) / 256 + p.G);
     if (blocks <= 0) return hipSuccess;
-    switch (p.epilogue) {
-      case BWD_EPI_F32:
-        hipLaunchKernelGGL(bwd_dma_kernel<BWD_EPI_F32>, dim3((unsigned)blocks), dim3(512), 0, s, p);
-        break;
-      default:
-        hipLaunchKernelGGL(bwd_dma_kernel<BWD_EPI_GATEUP_SAVE>, dim3((unsigned)blocks), dim3(512),
-                           0, s, p);
-    }
+    if (p.epilogue != BWD_EPI_F32)
+      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_GATEUP_SAVE, false>), dim3((unsigned)blocks),
+                         dim3(512), 0, s, p);
+    else if (p.b_kmajor)
+      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_F32, true>), dim3((unsigned)blocks), dim3(512),
+                         0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_F32, false>), dim3((unsigned)blocks), dim3(512),
+                         0, s, p);
     return hipGetLastError();
   }
   long long blocks;

@@ -127,6 +127,10 @@ struct BwdGemmParams {
   const uint16_t* B;
   const uint16_t* B2;
   long long ldb, b_gstride;
+  // b_kmajor (MROWS/DENSE, EPI_F32): B is stored k-major instead, row k of
+  // group g at B + g*b_gstride + k*ldb holding the N columns; rows k >= k_split
+  // are row k - k_split of B2 (k_split a multiple of 64; INT_MAX: no B2).
+  int b_kmajor, k_split;
   // EPI_F32: C row m of group g (KRAGGED) / row r (MROWS, DENSE) at
   // C + g*c_gstride + m*ldc; rows m >= c_split go to C2 + g*c_gstride + (m-c_split)*ldc.
   // With Cb (bf16) instead of C the rows are rounded once into Cb (no split).

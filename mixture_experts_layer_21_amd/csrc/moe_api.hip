@@ -157,8 +157,8 @@ Layout layout_of(const moe_config* c) {
 // Backward workspace: the forward layout (route and permutation scratch),
 // then the backward's own buffers.
 struct BwdLayout {
-  size_t logits, padoff, wdT, wguT, wrT, act, p1, p2, dact, dgu, dw, dh, dz, dxr, dFT, XT, AT,
-      DGUT, dhT, xT, swdT, swguT, sact, sp1, sp2, sdact, sdgu, sdz, doutT, sAT, sDGUT, ninv,
+  size_t logits, padoff, wrT, act, p1, p2, dact, dgu, dw, dh, dz, dxr, dFT, XT, AT,
+      DGUT, dhT, xT, sact, sp1, sp2, sdact, sdgu, sdz, doutT, sAT, sDGUT, ninv,
       ndwp, total;
   int Epad, Tpad, Kpad;
 };
@@ -180,8 +180,6 @@ BwdLayout bwd_layout_of(const moe_config* c) {
   const size_t Kp = B.Kpad, Tp = B.Tpad, Ep = B.Epad;
   B.logits = take(T * E * 4);
   B.padoff = take((E + 1) * 4);
-  B.wdT = take(E * H * D * 2);
-  B.wguT = take(E * D * 2 * H * 2);
   B.wrT = take(D * Ep * 2);
   B.act = take(R * H * 2);
   B.p1 = take(R * H * 2);
@@ -199,8 +197,6 @@ BwdLayout bwd_layout_of(const moe_config* c) {
   B.dhT = take(Ep * Tp * 2);
   B.xT = take(D * Tp * 2);
   if (Hs) {
-    B.swdT = take(Hs * D * 2);
-    B.swguT = take(D * 2 * Hs * 2);
     B.sact = take(T * Hs * 2);
     B.sp1 = take(T * Hs * 2);
     B.sp2 = take(T * Hs * 2);
@@ -770,7 +766,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
   rp.logits_out = f32(B.logits);
   MOE_TRY(hip_ok(moe::launch_route(rp, stream), "route kernel"));
 
-  // 3. K-contiguous copies of the weights
+  // 3. K-contiguous copy of the router weights (the expert weights are read
+  // k-major by the dgrad GEMMs)
   auto transpose = [&](int rows, int cols, const void* src, bool src_f32, long long ld_src,
                        long long src_b, int out_cols, uint16_t* dst, long long ld_dst,
                        long long dst_b, int col0, int batch, const int32_t* gather,
@@ -799,23 +796,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     t.skip_rows = skip_rows;
     return hip_ok(moe::launch_transpose(t, stream), "transpose kernel");
   };
-  // (experts without rows are skipped: their weights feed no gradient)
-  MOE_TRY(transpose(D, H, w_down, false, H, (long long)D * H, D, u16(B.wdT), D,
-                    (long long)H * D, 0, E, nullptr, nullptr, nullptr, false, offsets));
-  MOE_TRY(transpose(H, D, w_gate, false, D, (long long)H * D, H, u16(B.wguT), 2 * H,
-                    (long long)D * 2 * H, 0, E, nullptr, nullptr, nullptr, false, offsets));
-  MOE_TRY(transpose(H, D, w_up, false, D, (long long)H * D, H, u16(B.wguT), 2 * H,
-                    (long long)D * 2 * H, H, E, nullptr, nullptr, nullptr, false, offsets));
   MOE_TRY(transpose(E, D, w_router, cfg->router_dtype == MOE_F32, D, 0, B.Epad, u16(B.wrT),
                     B.Epad, 0, 0, 1, nullptr, nullptr, nullptr, false));
-  if (sh) {
-    MOE_TRY(transpose(D, Hs, w_shared_down, false, Hs, 0, D, u16(B.swdT), D, 0, 0, 1, nullptr,
-                      nullptr, nullptr, false));
-    MOE_TRY(transpose(Hs, D, w_shared_gate, false, D, 0, Hs, u16(B.swguT), 2 * Hs, 0, 0, 1,
-                      nullptr, nullptr, nullptr, false));
-    MOE_TRY(transpose(Hs, D, w_shared_up, false, D, 0, Hs, u16(B.swguT), 2 * Hs, 0, Hs, 1,
-                      nullptr, nullptr, nullptr, false));
-  }
 
   auto gemm = [&](moe::BwdGemmParams g, const char* what) {
     return hip_ok(moe::launch_bwd_gemm(g, stream), what);
@@ -861,9 +843,11 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     d.lda = D;
     d.gather = r2a;
     d.gdiv = k;
-    d.B = u16(B.wdT);
-    d.ldb = D;
-    d.b_gstride = (long long)H * D;
+    d.B = static_cast<const uint16_t*>(w_down);  // [D][H]: k-major
+    d.b_kmajor = 1;
+    d.k_split = kNoSplit;
+    d.ldb = H;
+    d.b_gstride = (long long)D * H;
     d.Cb = u16(B.dact);
     d.ldc = H;
     d.c_split = kNoSplit;
@@ -907,14 +891,17 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     g.max_rows = R;
     g.A = u16(B.dgu);
     g.lda = 2 * H;
-    g.B = u16(B.wguT);
-    g.ldb = 2 * H;
-    g.b_gstride = (long long)D * 2 * H;
+    g.B = static_cast<const uint16_t*>(w_gate);  // [H][D] then [H][D] of w_up: k-major
+    g.B2 = static_cast<const uint16_t*>(w_up);
+    g.b_kmajor = 1;
+    g.k_split = H;
+    g.ldb = D;
+    g.b_gstride = (long long)H * D;
     g.C = f32(B.dz);
     g.ldc = D;
     g.c_split = kNoSplit;
     g.a_bytes = 2ll * R * 2 * H;
-    g.b_bytes = 2ll * D * 2 * H;
+    g.b_bytes = 2ll * H * D;
     MOE_TRY(gemm(g, "gate/up dgrad"));
     moe::BwdGemmParams r{};
     r.grouping = moe::BWD_DENSE;
@@ -964,8 +951,10 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     d.G = 1;
     d.A = static_cast<const uint16_t*>(dout);
     d.lda = D;
-    d.B = u16(B.swdT);
-    d.ldb = D;
+    d.B = static_cast<const uint16_t*>(w_shared_down);  // [D][Hs]: k-major
+    d.b_kmajor = 1;
+    d.k_split = kNoSplit;
+    d.ldb = Hs;
     d.Cb = u16(B.sdact);
     d.ldc = Hs;
     d.c_split = kNoSplit;
@@ -984,13 +973,16 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     z.G = 1;
     z.A = u16(B.sdgu);
     z.lda = 2 * Hs;
-    z.B = u16(B.swguT);
-    z.ldb = 2 * Hs;
+    z.B = static_cast<const uint16_t*>(w_shared_gate);  // k-major, then w_shared_up
+    z.B2 = static_cast<const uint16_t*>(w_shared_up);
+    z.b_kmajor = 1;
+    z.k_split = Hs;
+    z.ldb = D;
     z.C = f32(B.sdz);
     z.ldc = D;
     z.c_split = kNoSplit;
     z.a_bytes = 2ll * T * 2 * Hs;
-    z.b_bytes = 2ll * D * 2 * Hs;
+    z.b_bytes = 2ll * Hs * D;
     MOE_TRY(gemm(z, "shared gate/up dgrad"));
   }
   {
