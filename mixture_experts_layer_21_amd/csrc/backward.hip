@@ -471,26 +471,31 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdParams p) {
 // gradient.
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeParams p) {
   __shared__ uint16_t tile[64][66];
+  __shared__ int s_group;
   const int b = blockIdx.z;
   if (p.skip_rows && p.skip_rows[b + 1] == p.skip_rows[b]) return;
   const int jc0 = blockIdx.x * 64;           // first destination column (padded space)
   const int c0 = blockIdx.y * 64;            // first source column
   if (jc0 >= p.out_cols) return;
+  const int tid = threadIdx.x;
   // Source rows j of this tile: with ragged groups a 64-column tile lies in
-  // one group (padded offsets are multiples of 64).
+  // one group (padded offsets are multiples of 64), found by one thread per
+  // group (G <= 256); -1: past the last group, the tile is zeros.
   int j0 = jc0, j_end = p.rows;
   if (p.offsets) {
-    int g = 0;
-    while (g + 1 < p.G && p.padoff[g + 1] <= jc0) ++g;
-    if (jc0 >= p.padoff[p.G]) {
+    if (tid == 0) s_group = -1;
+    __syncthreads();
+    if (tid < p.G && p.padoff[tid] <= jc0 && jc0 < p.padoff[tid + 1]) s_group = tid;
+    __syncthreads();
+    const int g = s_group;
+    if (g < 0) {
       j0 = 0;
-      j_end = 0;  // past the last group: zeros
+      j_end = 0;
     } else {
       j0 = p.offsets[g] + (jc0 - p.padoff[g]);
       j_end = p.offsets[g + 1];
     }
   }
-  const int tid = threadIdx.x;
   // load: 64 source rows x 64 columns; a thread takes 16-byte chunks
   const int per = p.src_f32 ? 4 : 8;           // elements per chunk
   const int cpr = 64 / per;                    // chunks per row
