@@ -51,7 +51,14 @@ struct BTile {
 // it (MROWS has barriers); the first 256 threads scan.
 template <int BM>
 __device__ bool bwd_tile(const BwdGemmParams& p, int bn, BTile& t, int* s_scan) {
-  const int b = blockIdx.x;
+  // Logical tile b.  DENSE and MROWS: block i runs on XCD i % 8, and each XCD
+  // takes a contiguous run of logical tiles, so the blocks that share a B
+  // slice (the row tiles of one column tile, consecutive below) share that
+  // XCD's L2.  KRAGGED (short k ranges, fp32 tiles out) keeps the block
+  // order: measured faster spread over the XCDs.
+  const int nb = gridDim.x, xcd = blockIdx.x & 7, q = nb >> 3, rem = nb & 7;
+  const int b = p.grouping == BWD_KRAGGED ? (int)blockIdx.x
+                                          : xcd * q + min(xcd, rem) + (int)(blockIdx.x >> 3);
   if (p.grouping == BWD_DENSE) {
     const int ntn = (p.N + bn - 1) / bn, ntm = (p.M + BM - 1) / BM;
     if (b >= ntn * ntm) return false;
