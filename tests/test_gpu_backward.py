@@ -32,10 +32,14 @@ def _say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _run(moe, w, seed, aux=(0.3, 0.2), token_mask=None, swiglu_limit=0.0, pre_norm=None):
+def _run(moe, w, seed, aux=(0.3, 0.2), token_mask=None, swiglu_limit=0.0, pre_norm=None,
+         mutate=None):
     """``pre_norm`` = (norm weight [D] f32 CPU tensor or None, eps): the layer
-    takes RMSNorm(x) and x is the input before the norm."""
+    takes RMSNorm(x) and x is the input before the norm.  ``mutate`` edits the
+    drawn inputs in place before either side sees them."""
     inp = W.make_inputs(w, "cpu", seed=seed)
+    if mutate is not None:
+        mutate(inp)
     oi = P.oracle_inputs(inp)
     x_route = oi["x"]
     if pre_norm is not None:
@@ -136,6 +140,49 @@ def test_norm_weight_needs_pre_norm_backward(moe):
     with pytest.raises(moe.MoeError, match="pre_norm"):
         moe.moe_backward(P.config_of(w), d["x"], d["w_router"], d["w_gate"], d["w_up"],
                          d["w_down"], ids, gw, d["x"], norm_weight=torch.ones(w.D, device="cuda"))
+
+
+def test_backward_single_token(moe):
+    w = W.Workload("one", 1, 1, D=128, H=64, E=8, top_k=3)
+    g, ref = _run(moe, w, seed=36)
+    _compare(g, ref, GRADS + ("d_gate_w",), "single token")
+
+
+def test_backward_zero_router_leaves_experts_empty(moe):
+    """A zero router sends every token to experts 0..k-1 (ties to the lower
+    index): the other experts get exactly zero weight gradients."""
+    w = W.Workload("zero", 1, 70, D=128, H=64, E=8, top_k=3)
+    g, ref = _run(moe, w, seed=37, mutate=lambda inp: inp["w_router"].zero_())
+    _compare(g, ref, GRADS + ("d_gate_w",), "zero router")
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert not g[n][3:].any(), n
+
+
+def test_backward_dense_limit(moe):
+    """top_k = E: every expert sees every token."""
+    w = W.Workload("dense", 1, 45, D=64, H=128, E=4, top_k=4, w_std=0.1)
+    g, ref = _run(moe, w, seed=38)
+    _compare(g, ref, GRADS + ("d_gate_w",), "top_k = E")
+
+
+def test_backward_all_tokens_masked(moe):
+    """No valid token: no expert row, no auxiliary term; every gradient is
+    exactly zero on both sides."""
+    w = W.SMALL["mixtral_small"]
+    mask = np.zeros(w.T, dtype=bool)
+    g, ref = _run(moe, w, seed=39, token_mask=mask)
+    for n in GRADS + ("d_gate_w",):
+        assert not np.abs(ref[n]).any(), n
+        assert not g[n].any(), n
+
+
+@pytest.mark.parametrize("T,E,k", [(2000, 4, 2), (1111, 2, 1)])
+def test_backward_large_ragged_tiles(moe, T, E, k):
+    """Hundreds of rows per expert with ragged tails: several 256-row tiles
+    and 64-row k blocks per expert in every backward GEMM."""
+    w = W.Workload("ragged", 1, T, D=256, H=192, E=E, top_k=k, w_std=0.05)
+    g, ref = _run(moe, w, seed=40)
+    _compare(g, ref, GRADS + ("d_gate_w",), f"T={T} E={E} k={k}")
 
 
 def test_backward_dropped_slots(moe):
