@@ -584,14 +584,16 @@ def backward(inputs, dout, *, top_k, score="softmax", renormalize=True, route_sc
     (float64).  With ``pre_norm`` = (weight, eps, act) the layer takes
     rms_norm(x) (rounded to ``act``; the rounding passes gradients through
     unchanged) and the result also holds d_norm_weight.  Returns dx, dw_router, dw_gate, dw_up, dw_down (+ dws_gate,
-    dws_up, dws_down with a shared expert), and the intermediates
-    d_gate_w [T,k] (dL/dw per slot) and d_logits [T,E]."""
+    dws_up, dws_down with a shared expert, + d_shared_gate with its gate), and
+    the intermediates d_gate_w [T,k] (dL/dw per slot) and d_logits [T,E].
+
+    The gated shared expert adds g_t S(x_t) with g_t = sigmoid(x_t . w_sg):
+    S sees g_t dout_t, and the gate's logit gets g_t (1 - g_t) <dout_t, S(x_t)>,
+    which reaches w_sg (times x_t) and x_t (times w_sg)."""
     fw = dict(top_k=top_k, score=score, renormalize=renormalize, route_scale=route_scale,
               n_groups=n_groups, topk_groups=topk_groups, group_rule=group_rule,
               capacity_factor=capacity_factor, token_mask=token_mask,
               swiglu_limit=swiglu_limit)
-    if inputs.get("ws_sgate") is not None:
-        raise ValueError("backward: the shared-expert gate is not covered")
     if pre_norm is not None:
         x_raw = np.asarray(inputs["x"], dtype=np.float64)
         inner = backward(dict(inputs, x=rms_norm(x_raw, *pre_norm)), dout, aux_coef=aux_coef,
@@ -625,10 +627,17 @@ def backward(inputs, dout, *, top_k, score="softmax", renormalize=True, route_sc
         d_gate_w[t, s] = np.sum(dout[t] * F, axis=1)
     out = {"dw_gate": grads["w_gate"], "dw_up": grads["w_up"], "dw_down": grads["w_down"]}
     if inputs.get("ws_gate") is not None:
-        dz, dwg, dwu, dwd, _ = swiglu_ffn_backward(x, inputs["ws_gate"], inputs["ws_up"],
-                                                   inputs["ws_down"], dout, swiglu_limit)
+        wsg = inputs.get("ws_sgate")
+        g = np.ones(T) if wsg is None else sigmoid(x @ np.asarray(wsg, dtype=np.float64))
+        dz, dwg, dwu, dwd, S = swiglu_ffn_backward(x, inputs["ws_gate"], inputs["ws_up"],
+                                                   inputs["ws_down"], g[:, None] * dout,
+                                                   swiglu_limit)
         dx += dz
         out.update(dws_gate=dwg, dws_up=dwu, dws_down=dwd)
+        if wsg is not None:
+            dlogit = g * (1.0 - g) * np.sum(dout * S, axis=1)
+            dx += dlogit[:, None] * np.asarray(wsg, dtype=np.float64)[None, :]
+            out["d_shared_gate"] = dlogit @ x
     dh = router_backward(r, d_gate_w, top_k=top_k, score=score, renormalize=renormalize,
                          route_scale=route_scale, aux_coef=aux_coef)
     wr = np.asarray(inputs["w_router"], dtype=np.float64)

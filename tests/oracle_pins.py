@@ -646,7 +646,8 @@ def pin_pre_norm_layer_is_scale_free(o):
 
 
 GRAD_OF = {"x": "dx", "w_router": "dw_router", "w_gate": "dw_gate", "w_up": "dw_up",
-           "w_down": "dw_down", "ws_gate": "dws_gate", "ws_up": "dws_up", "ws_down": "dws_down"}
+           "w_down": "dw_down", "ws_gate": "dws_gate", "ws_up": "dws_up", "ws_down": "dws_down",
+           "ws_sgate": "d_shared_gate"}
 
 
 def _fd_agrees(o, inp, seed, aux, **fw):
@@ -677,6 +678,14 @@ def pin_backward_fd_softmax_capacity_shared(o):
     """Softmax, renormalised top-2, capacity drops, shared expert, both aux terms."""
     inp = _tiny_inputs(51, T=12, E=4, shared=True)
     _fd_agrees(o, inp, 52, (0.3, 0.2), top_k=2, capacity_factor=0.75)
+
+
+def pin_backward_fd_gated_shared_expert(o):
+    """The shared expert scaled per token by sigmoid(x . w_sg): central
+    differences for w_sg, x and the shared weights."""
+    inp = _tiny_inputs(60, T=9, E=4, shared=True)
+    inp["ws_sgate"] = _rng(61).normal(size=inp["x"].shape[1]) * 0.5
+    _fd_agrees(o, inp, 62, (0.1, 0.05), top_k=2)
 
 
 def pin_backward_fd_sigmoid_groups_scale(o):

@@ -179,6 +179,15 @@ MUTANTS = [
     ("rms_bwd_weight_grad_unnormalised",
      "return dx, np.sum(dy * x / s, axis=0)",
      "return dx, np.sum(dy * x, axis=0)"),
+    ("shared_gate_bwd_no_sigmoid_slope",
+     "dlogit = g * (1.0 - g) * np.sum(dout * S, axis=1)",
+     "dlogit = np.sum(dout * S, axis=1)"),
+    ("shared_gate_bwd_ungated_branch",
+     "inputs[\"ws_down\"], g[:, None] * dout,",
+     "inputs[\"ws_down\"], dout,"),
+    ("shared_gate_bwd_no_dx_term",
+     "dx += dlogit[:, None] * np.asarray(wsg, dtype=np.float64)[None, :]",
+     "dx += 0.0"),
     ("router_bias_ignored",
      "h = h + np.asarray(logit_bias, dtype=np.float64)[None, :]",
      "h = h + 0.0"),
