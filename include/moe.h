@@ -257,8 +257,8 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg);
  * the index decision ("The Router"), f is detached ("The auxiliary
  * load-balancing loss")); gradients reach the router through the gate weights
  * of the kept slots, through P_e and through z.
- *   x, norm_weight, w_router, logit_bias, w_gate, w_up, w_down, w_shared_*:
- *                       as moe_forward (x is the layer input before the
+ *   x, norm_weight, w_router, logit_bias, w_gate, w_up, w_down, w_shared_*,
+ *   shared_expert_gate: as moe_forward (x is the layer input before the
  *                       pre-norm when cfg->pre_norm = 1)
  *   expert_ids, gate_w  [T, k]: the routes and gate weights of the forward
  *                       (moe_route / moe_forward outputs; -1 marks a masked
@@ -271,23 +271,31 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg);
  *   d_gate_w            [T, k] f32 out or NULL: dL/d gate weight per slot
  *                       (0 for dropped and masked slots)
  *   d_norm_weight       [D] f32 out or NULL (pre_norm only): dL/d norm weight
+ *   d_shared_gate       [D] f32 out or NULL (needs shared_expert_gate):
+ *                       dL/d shared-expert gate vector
+ * With the gated shared expert (NeMo MoE.shared_expert_gate, read as
+ * g_t = sigmoid(x_t . w_sg) scaling the shared expert's output), the shared
+ * expert receives g_t dout_t and the gate's logit g_t (1 - g_t) <dout_t, S_t>,
+ * formed from the shared down dgrad and the saved SwiGLU output without
+ * recomputing S; it reaches w_sg (fixed-order column sums) and dx.
  * With the pre-norm ("Transformer Architecture": the block normalises its
  * input before the sublayer, RMSNorm), the rows are renormalised with the
  * forward's kernel and the gradient passes back through the norm:
  * with s = sqrt(mean(x^2) + eps) and g = norm_weight * dL/dy,
  *   dx = g / s - x * sum(g x) / (D s^3),   dL/dw_d = sum_t dL/dy_td x_td / s_t,
  * dL/dy kept fp32, dx rounded once.
- * bf16 activations only; the shared-expert gate is not covered.  fp32 accumulation; intermediates (the SwiGLU factors, dL/dg and
+ * bf16 activations only.  fp32 accumulation; intermediates (the SwiGLU factors, dL/dg and
  * dL/du, dL/dh) are rounded to bf16 between GEMMs.  Deterministic: no float
  * atomics, every sum runs in a fixed order. */
 moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_weight,
                         const void* w_router, const float* logit_bias, const void* w_gate,
                         const void* w_up, const void* w_down, const void* w_shared_gate,
                         const void* w_shared_up, const void* w_shared_down,
-                        const int32_t* expert_ids, const float* gate_w, const void* dout,
-                        float balance_coef, float z_coef, void* dx, float* dw_router,
-                        float* dw_gate, float* dw_up, float* dw_down, float* dws_gate,
-                        float* dws_up, float* dws_down, float* d_gate_w, float* d_norm_weight,
+                        const void* shared_expert_gate, const int32_t* expert_ids,
+                        const float* gate_w, const void* dout, float balance_coef, float z_coef,
+                        void* dx, float* dw_router, float* dw_gate, float* dw_up,
+                        float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
+                        float* d_shared_gate, float* d_gate_w, float* d_norm_weight,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Auxiliary-loss-free balancer step ("DeepSeek-MoE and the fine-grained +

@@ -99,8 +99,8 @@ _sigs = {
     "moe_rmsnorm": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
     "moe_backward_workspace_bytes": (_SZ, [_CFG]),
     "moe_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                    ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _P, _P,
-                                    _P, _P, _P, _P, _P, _SZ, _P]),
+                                    _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_update_bias": (ctypes.c_int, [_CFG, _P, ctypes.c_float, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
@@ -380,13 +380,15 @@ def backward_workspace_bytes(cfg) -> int:
 
 def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, expert_ids, gate_w, dout, *,
                  logit_bias=None, ws_gate=None, ws_up=None, ws_down=None, balance_coef=0.0,
-                 z_coef=0.0, workspace=None, d_gate_w=False, norm_weight=None):
+                 z_coef=0.0, workspace=None, d_gate_w=False, norm_weight=None,
+                 shared_expert_gate=None):
     """Gradients of <dout, out> + balance_coef*balance + z_coef*z (see
     ``moe_backward``).  Returns a dict with dx (act dtype) and the fp32
     weight gradients dw_router, dw_gate, dw_up, dw_down (+ dws_* with a shared
     expert, + d_gate_w [T,k] when asked, + d_norm_weight [D] with the
-    pre-norm).  With ``cfg.pre_norm``, ``x`` is the input before the norm and
-    ``norm_weight`` [D] f32 (None: unit weight) its weight."""
+    pre-norm, + d_shared_gate [D] with ``shared_expert_gate``).  With
+    ``cfg.pre_norm``, ``x`` is the input before the norm and ``norm_weight``
+    [D] f32 (None: unit weight) its weight."""
     check_config(cfg)
     T, D, H, E, k, Hs = cfg.T, cfg.D, cfg.H, cfg.E, cfg.top_k, cfg.H_shared
     dt = cfg.act_torch_dtype
@@ -400,6 +402,7 @@ def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, expert_ids, gate_w, dou
     _expect(gate_w, "gate_w", (T, k), torch.float32)
     _expect(dout, "dout", (T, D), dt)
     _expect(norm_weight, "norm_weight", (D,), torch.float32, required=False)
+    _expect(shared_expert_gate, "shared_expert_gate", (D,), dt, required=False)
     if Hs:
         _expect(ws_gate, "ws_gate", (Hs, D), dt)
         _expect(ws_up, "ws_up", (Hs, D), dt)
@@ -416,6 +419,8 @@ def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, expert_ids, gate_w, dou
         g["d_gate_w"] = torch.empty(T, k, **f32)
     if cfg.pre_norm:
         g["d_norm_weight"] = torch.empty(D, **f32)
+    if shared_expert_gate is not None and Hs:
+        g["d_shared_gate"] = torch.empty(D, **f32)
     nbytes = backward_workspace_bytes(cfg)  # 0: not covered, the library says why
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -423,11 +428,13 @@ def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, expert_ids, gate_w, dou
     _check(_lib.moe_backward(ctypes.byref(cfg), _ptr(x), _ptr(norm_weight), _ptr(w_router),
                              _ptr(logit_bias),
                              _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up),
-                             _ptr(ws_down), _ptr(expert_ids), _ptr(gate_w), _ptr(dout),
+                             _ptr(ws_down), _ptr(shared_expert_gate), _ptr(expert_ids),
+                             _ptr(gate_w), _ptr(dout),
                              float(balance_coef), float(z_coef), _ptr(g["dx"]),
                              _ptr(g["dw_router"]), _ptr(g["dw_gate"]), _ptr(g["dw_up"]),
                              _ptr(g["dw_down"]), _ptr(g.get("dws_gate")), _ptr(g.get("dws_up")),
-                             _ptr(g.get("dws_down")), _ptr(g.get("d_gate_w")),
+                             _ptr(g.get("dws_down")), _ptr(g.get("d_shared_gate")),
+                             _ptr(g.get("d_gate_w")),
                              _ptr(g.get("d_norm_weight")), _ptr(ws),
                              0 if ws is None else ws.numel(), _stream()), "moe_backward")
     return g

@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdParams p) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int rows = p.offsets ? p.offsets[p.G] : p.n;
   if (r >= rows) return;  // whole wave
-  const float w = p.gate_w ? p.gate_w[p.r2a[r]] : 1.f;
+  const float w = p.gate_w ? p.gate_w[p.r2a ? p.r2a[r] : r] : 1.f;
   const long long base = (long long)r * p.H;
   const long long based = (long long)r * 2 * p.H;
   float rs = 0.f;
@@ -701,6 +701,14 @@ __global__ __launch_bounds__(256) void dx_kernel(DxParams p) {
       if (r >= 0) s += *reinterpret_cast<const f32x4*>(p.dz + (long long)r * p.D + d);
     }
     if (p.dzs) s += *reinterpret_cast<const f32x4*>(p.dzs + o);
+    if (p.sg) {
+      const float g = p.sg[t], dl = g * (1.f - g) * p.sdw[t];
+      const uint2 w2 = *reinterpret_cast<const uint2*>(p.wsg + d);
+      s[0] += dl * __uint_as_float(w2.x << 16);
+      s[1] += dl * __uint_as_float(w2.x & 0xffff0000u);
+      s[2] += dl * __uint_as_float(w2.y << 16);
+      s[3] += dl * __uint_as_float(w2.y & 0xffff0000u);
+    }
     if (p.dx_f32) {
       *reinterpret_cast<f32x4*>(p.dx_f32 + o) = s;
       continue;
@@ -710,7 +718,82 @@ __global__ __launch_bounds__(256) void dx_kernel(DxParams p) {
   }
 }
 
+// Gate of the shared expert: one wave per token, the fp32 dot product of
+// 8-element chunks per lane, then a butterfly over the lanes.
+__global__ __launch_bounds__(256) void shared_gate_kernel(int T, int D, const uint16_t* x,
+                                                          const uint16_t* wsg, float* g) {
+  const int lane = threadIdx.x & 63, t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave
+  float acc = 0.f;
+  for (int c = lane * 8; c < D; c += 64 * 8) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + (long long)t * D + c);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(wsg + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc += __uint_as_float(xv[e] << 16) * __uint_as_float(wv[e] << 16);
+      acc += __uint_as_float(xv[e] & 0xffff0000u) * __uint_as_float(wv[e] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) g[t] = sigm(acc);
+}
+
+// Weight gradient of the gate: each block sums a chunk of rows for 256
+// columns in row order; a second pass adds the chunks in order.
+constexpr int kGateRowsPerChunk = 256;
+
+int gate_rows_per_chunk(int T) {
+  const int per = (T + 65534) / 65535;  // the grid's y extent stays within 65535
+  return per > kGateRowsPerChunk ? per : kGateRowsPerChunk;
+}
+
+__global__ __launch_bounds__(256) void gate_dw_part_kernel(int T, int D, const uint16_t* x,
+                                                           const float* g, const float* sdw,
+                                                           int per, float* part) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= D) return;
+  const long long t0 = (long long)blockIdx.y * per;
+  const long long t1 = min((long long)T, t0 + per);
+  float acc = 0.f;
+  for (long long t = t0; t < t1; ++t) {
+    const float dl = g[t] * (1.f - g[t]) * sdw[t];
+    acc += dl * __uint_as_float((uint32_t)x[t * D + d] << 16);
+  }
+  part[(long long)blockIdx.y * D + d] = acc;
+}
+
+__global__ __launch_bounds__(256) void colsum_final_kernel(int D, int nchunk, const float* part,
+                                                           float* out) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= D) return;
+  float acc = part[d];
+  for (int c = 1; c < nchunk; ++c) acc += part[(long long)c * D + d];
+  out[d] = acc;
+}
+
 }  // namespace
+
+int gate_dw_chunks(int T) { return (T + gate_rows_per_chunk(T) - 1) / gate_rows_per_chunk(T); }
+
+hipError_t launch_shared_gate(int T, int D, const uint16_t* x, const uint16_t* wsg, float* g,
+                              hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(shared_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, s, T, D, x, wsg, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_dw(int T, int D, const uint16_t* x, const float* g, const float* sdw,
+                          float* part, float* dwsg, hipStream_t s) {
+  const dim3 grid((D + 255) / 256, gate_dw_chunks(T));
+  hipLaunchKernelGGL(gate_dw_part_kernel, grid, dim3(256), 0, s, T, D, x, g, sdw,
+                     gate_rows_per_chunk(T), part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((D + 255) / 256), dim3(256), 0, s, D,
+                     gate_dw_chunks(T), part, dwsg);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s) {
   if (bwd_dma_fits(p)) {

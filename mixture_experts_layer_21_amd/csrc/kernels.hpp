@@ -214,6 +214,11 @@ struct DxParams {
   const float* dxr;          // [T, D] (router)
   void* dx;                  // [T, D] act dtype, or null with dx_f32
   float* dx_f32;             // [T, D] fp32 out instead of dx (the pre-norm backward's input)
+  // gated shared expert (or null): adds g_t (1 - g_t) sdw[t] * wsg[d], the
+  // gate logit's gradient times the gate vector (bf16 [D])
+  const float* sg;
+  const float* sdw;
+  const uint16_t* wsg;
 };
 
 hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s);
@@ -221,6 +226,14 @@ hipError_t launch_swiglu_bwd(const SwigluBwdParams& p, hipStream_t s);
 hipError_t launch_transpose(const TransposeParams& p, hipStream_t s);
 hipError_t launch_pad_offsets(int G, const int32_t* offsets, int32_t* padoff, hipStream_t s);
 hipError_t launch_router_bwd(const RouterBwdParams& p, hipStream_t s);
+// Gated shared expert: g[t] = sigmoid(x[t] . wsg) (bf16 x [T, D], wsg [D]);
+// and dwsg[d] = sum_t g_t (1 - g_t) sdw[t] x[t][d] in a fixed order through
+// part (f32 [gate_dw_chunks(T), D]).
+hipError_t launch_shared_gate(int T, int D, const uint16_t* x, const uint16_t* wsg, float* g,
+                              hipStream_t s);
+int gate_dw_chunks(int T);
+hipError_t launch_gate_dw(int T, int D, const uint16_t* x, const float* g, const float* sdw,
+                          float* part, float* dwsg, hipStream_t s);
 hipError_t launch_dx(const DxParams& p, bool bf16, hipStream_t s);
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s);

@@ -158,7 +158,7 @@ Layout layout_of(const moe_config* c) {
 // then the backward's own buffers.
 struct BwdLayout {
   size_t logits, padoff, wrT, act, p1, p2, dact, dgu, dw, dh, dz, dxr, dFT, XT, AT,
-      DGUT, dhT, xT, sact, sp1, sp2, sdact, sdgu, sdz, doutT, sAT, sDGUT, ninv,
+      DGUT, dhT, xT, sact, sp1, sp2, sdact, sdgu, sdz, doutT, sAT, sDGUT, sgv, sdw, sgp, ninv,
       ndwp, total;
   int Epad, Tpad, Kpad;
 };
@@ -206,6 +206,10 @@ BwdLayout bwd_layout_of(const moe_config* c) {
     B.doutT = take(D * Tp * 2);
     B.sAT = take(Hs * Tp * 2);
     B.sDGUT = take(2 * Hs * Tp * 2);
+    // the shared expert's gate: g per token, <dout, S> per token, dL/dw_sg partials
+    B.sgv = take(T * 4);
+    B.sdw = take(T * 4);
+    B.sgp = take((size_t)moe::gate_dw_chunks((int)T) * D * 4);
   }
   if (c->pre_norm) {  // the norm's backward: 1/s per row, weight-gradient partials
     B.ninv = take(T * 4);
@@ -665,10 +669,11 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
                         const void* w_router, const float* logit_bias, const void* w_gate,
                         const void* w_up, const void* w_down, const void* w_shared_gate,
                         const void* w_shared_up, const void* w_shared_down,
-                        const int32_t* expert_ids, const float* gate_w, const void* dout,
-                        float balance_coef, float z_coef, void* dx, float* dw_router,
-                        float* dw_gate, float* dw_up, float* dw_down, float* dws_gate,
-                        float* dws_up, float* dws_down, float* d_gate_w, float* d_norm_weight,
+                        const void* shared_expert_gate, const int32_t* expert_ids,
+                        const float* gate_w, const void* dout, float balance_coef, float z_coef,
+                        void* dx, float* dw_router, float* dw_gate, float* dw_up,
+                        float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
+                        float* d_shared_gate, float* d_gate_w, float* d_norm_weight,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_config(cfg));
   if (cfg->act_dtype != MOE_BF16)
@@ -676,6 +681,10 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
   if ((norm_weight || d_norm_weight) && !cfg->pre_norm)
     return fail(MOE_ERR_INVALID_ARG,
                 "moe_backward: norm_weight and d_norm_weight need cfg->pre_norm = 1");
+  if ((shared_expert_gate || d_shared_gate) && cfg->H_shared == 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_backward: shared_expert_gate needs a shared expert");
+  if (d_shared_gate && !shared_expert_gate)
+    return fail(MOE_ERR_INVALID_ARG, "moe_backward: d_shared_gate needs shared_expert_gate");
   if (!x || !w_router || !w_gate || !w_up || !w_down || !expert_ids || !gate_w || !dout ||
       !dx || !dw_router || !dw_gate || !dw_up || !dw_down)
     return fail(MOE_ERR_NULL_PTR, "moe_backward: inputs, routing and gradient outputs required");
@@ -701,6 +710,9 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
   MOE_TRY(check_dev(d_gate_w, "d_gate_w", false));
   MOE_TRY(check_dev(norm_weight, "norm_weight", false));
   MOE_TRY(check_dev(d_norm_weight, "d_norm_weight", false));
+  MOE_TRY(check_dev(shared_expert_gate, "shared_expert_gate", false));
+  MOE_TRY(check_dev(d_shared_gate, "d_shared_gate", false));
+  MOE_TRY(check_align16(shared_expert_gate, "shared_expert_gate"));
   if (cfg->pre_norm) {
     MOE_TRY(check_align16(x, "x"));
     MOE_TRY(check_align16(norm_weight, "norm_weight"));
@@ -921,7 +933,12 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     r.b_bytes = 2ll * D * B.Epad;
     MOE_TRY(gemm(r, "router dgrad"));
   }
+  const uint16_t* sgate = static_cast<const uint16_t*>(shared_expert_gate);
   if (sh) {
+    if (sgate)  // the shared expert's per-token gate on the layer's input rows
+      MOE_TRY(hip_ok(moe::launch_shared_gate(T, D, static_cast<const uint16_t*>(x), sgate,
+                                             f32(B.sgv), stream),
+                     "shared gate kernel"));
     moe::BwdGemmParams g{};
     g.grouping = moe::BWD_DENSE;
     g.epilogue = moe::BWD_EPI_GATEUP_SAVE;
@@ -961,8 +978,11 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     d.a_bytes = 2ll * T * D;
     d.b_bytes = 2ll * Hs * D;
     MOE_TRY(gemm(d, "shared down dgrad"));
+    // with the gate: the branch sees g_t dout_t, and <dout_t, S_t> (for the
+    // gate's own gradient) is sum_h act * dact, as dL/dw of a routed row
     moe::SwigluBwdParams q{T, Hs, nullptr, 1, u16(B.sdact), u16(B.sact), u16(B.sp1),
-                           u16(B.sp2), nullptr, nullptr, u16(B.sdgu), nullptr};
+                           u16(B.sp2), sgate ? f32(B.sgv) : nullptr, nullptr, u16(B.sdgu),
+                           sgate ? f32(B.sdw) : nullptr};
     MOE_TRY(hip_ok(moe::launch_swiglu_bwd(q, stream), "shared swiglu backward kernel"));
     moe::BwdGemmParams z{};
     z.grouping = moe::BWD_DENSE;
@@ -989,7 +1009,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     // with the pre-norm, dL/d(normalised rows) stays fp32, in place over the
     // router's dx (each element is read before it is written, by one thread)
     moe::DxParams p{T, D, k, f32(B.dz), a2r, sh ? f32(B.sdz) : nullptr, f32(B.dxr),
-                    cfg->pre_norm ? nullptr : dx, cfg->pre_norm ? f32(B.dxr) : nullptr};
+                    cfg->pre_norm ? nullptr : dx, cfg->pre_norm ? f32(B.dxr) : nullptr,
+                    sgate ? f32(B.sgv) : nullptr, sgate ? f32(B.sdw) : nullptr, sgate};
     MOE_TRY(hip_ok(moe::launch_dx(p, true, stream), "dx kernel"));
     if (cfg->pre_norm)
       MOE_TRY(hip_ok(moe::launch_rmsnorm_bwd(T, D, true, x_raw, norm_weight, cfg->norm_eps,
@@ -1069,7 +1090,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
   }
   if (sh) {
     MOE_TRY(transpose(T, D, dout, false, D, 0, B.Tpad, u16(B.doutT), B.Tpad, 0, 0, 1, nullptr,
-                      nullptr, nullptr, false));
+                      sgate ? f32(B.sgv) : nullptr, nullptr, false));
     MOE_TRY(transpose(T, Hs, u16(B.sact), false, Hs, 0, B.Tpad, u16(B.sAT), B.Tpad, 0, 0, 1,
                       nullptr, nullptr, nullptr, false));
     MOE_TRY(transpose(T, 2 * Hs, u16(B.sdgu), false, 2 * Hs, 0, B.Tpad, u16(B.sDGUT), B.Tpad, 0,
@@ -1109,6 +1130,10 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     u.a_bytes = 2ll * 2 * Hs * B.Tpad;
     u.b_bytes = 2ll * D * B.Tpad;
     MOE_TRY(gemm(u, "shared gate/up wgrad"));
+    if (d_shared_gate)
+      MOE_TRY(hip_ok(moe::launch_gate_dw(T, D, static_cast<const uint16_t*>(x), f32(B.sgv),
+                                         f32(B.sdw), f32(B.sgp), d_shared_gate, stream),
+                     "shared gate weight-gradient kernels"));
   }
   return ok();
 }

@@ -107,18 +107,27 @@ def test_backward_host_checks(moe):
     nargs = len(f.argtypes)
     fake = ctypes.c_void_p(0x1000)
 
-    def call(cfg, norm_weight=None, d_norm_weight=None):
+    def call(cfg, **given):
+        # positions: 2 norm_weight, 11 shared_expert_gate, 15/16 loss
+        # coefficients, 25 d_shared_gate, 27 d_norm_weight, 29 bytes, 30 stream
         args = [ctypes.byref(cfg)] + [fake] * (nargs - 1)
-        args[2], args[25] = norm_weight, d_norm_weight  # norm_weight, d_norm_weight
-        args[14] = args[15] = 0.0  # loss coefficients
-        args[-2], args[-1] = 0, None  # workspace bytes, stream
+        args[2] = args[11] = args[25] = args[27] = None
+        for pos, v in given.items():
+            args[int(pos[1:])] = v
+        args[15] = args[16] = 0.0
+        args[-2], args[-1] = 0, None
         return f(*args)
 
-    assert nargs == 29
+    assert nargs == 31
     cfg = moe.make_config(256, 64, 128, 4, 2)
-    assert call(cfg, norm_weight=fake) == 1  # MOE_ERR_INVALID_ARG: needs pre_norm
+    assert call(cfg, p2=fake) == 1  # MOE_ERR_INVALID_ARG: norm_weight needs pre_norm
     assert "pre_norm" in lib_error(moe)
-    assert call(cfg, d_norm_weight=fake) == 1
+    assert call(cfg, p27=fake) == 1
+    assert call(cfg, p11=fake) == 1  # a shared-expert gate without a shared expert
+    assert "shared expert" in lib_error(moe)
+    shared = moe.make_config(256, 64, 128, 4, 2, H_shared=64)
+    assert call(shared, p25=fake) == 1  # its gradient without the gate
+    assert "d_shared_gate" in lib_error(moe)
     f32 = moe.make_config(256, 64, 128, 4, 2, act_dtype="f32", router_dtype="f32")
     assert call(f32) == 3  # MOE_ERR_UNSUPPORTED
     assert "bf16" in lib_error(moe)

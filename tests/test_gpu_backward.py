@@ -74,7 +74,8 @@ def _run(moe, w, seed, aux=(0.3, 0.2), token_mask=None, swiglu_limit=0.0, pre_no
                          gw, dout.cuda(), logit_bias=d.get("logit_bias"),
                          ws_gate=d.get("ws_gate"), ws_up=d.get("ws_up"),
                          ws_down=d.get("ws_down"), balance_coef=aux[0], z_coef=aux[1],
-                         d_gate_w=True, norm_weight=nw_dev)
+                         d_gate_w=True, norm_weight=nw_dev,
+                         shared_expert_gate=d.get("ws_sgate"))
     torch.cuda.synchronize()
     return g, ref
 
@@ -183,6 +184,28 @@ def test_backward_large_ragged_tiles(moe, T, E, k):
     w = W.Workload("ragged", 1, T, D=256, H=192, E=E, top_k=k, w_std=0.05)
     g, ref = _run(moe, w, seed=40)
     _compare(g, ref, GRADS + ("d_gate_w",), f"T={T} E={E} k={k}")
+
+
+def _with_shared_gate(seed):
+    def mutate(inp):
+        g = torch.Generator().manual_seed(seed)
+        inp["ws_sgate"] = (torch.randn(inp["x"].shape[1], generator=g) * 0.05).to(
+            inp["x"].dtype)
+    return mutate
+
+
+@pytest.mark.parametrize("pre_norm", [False, True])
+def test_backward_gated_shared_expert(moe, pre_norm):
+    """Shared expert scaled by sigmoid(x . w_sg): every gradient, and
+    dL/dw_sg, against the oracle; with the pre-norm the gate sees the
+    normalised rows."""
+    w = W.SMALL["deepseek_small"]
+    nw = torch.rand(w.D, generator=torch.Generator().manual_seed(41)) + 0.5
+    g, ref = _run(moe, w, seed=41, mutate=_with_shared_gate(42),
+                  pre_norm=(nw, 1e-5) if pre_norm else None)
+    names = GRADS + SHARED + ("d_gate_w", "d_shared_gate") + (
+        ("d_norm_weight",) if pre_norm else ())
+    _compare(g, ref, names, "gated shared expert")
 
 
 def test_backward_dropped_slots(moe):
