@@ -213,9 +213,49 @@ def _time_backward(moe, w, cfg, inp, r, n_kept, steps, stream):
     flops = (12.0 * w.D * w.H * n_kept + 12.0 * w.D * w.H_shared * w.T
              + 4.0 * w.T * w.D * w.E)
     _log(f"[bench] moe_backward: {ms:.3f} ms/step, {flops / ms / 1e9:.1f} TFLOP/s")
+
+    # The same step with the SwiGLU state saved by the forward: the forward
+    # writes two more bf16 [rows, H] arrays, the backward skips the gate/up
+    # recompute.
+    saved = moe.new_saved(cfg, inp["x"].device)
+    fws = moe.new_workspace(cfg, inp["x"].device)
+
+    def fwd(save):
+        return moe.moe_forward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
+                               inp["w_down"], logit_bias=inp.get("logit_bias"),
+                               select_bias=inp.get("select_bias"), ws_gate=inp.get("ws_gate"),
+                               ws_up=inp.get("ws_up"), ws_down=inp.get("ws_down"),
+                               workspace=fws, saved=saved if save else None)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    f_plain = timed(lambda: fwd(False))
+    f_save = timed(lambda: fwd(True))
+
+    def bwd_saved():
+        return moe.moe_backward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
+                                inp["w_down"], r["expert_ids"], r["gate_w"], dout,
+                                logit_bias=inp.get("logit_bias"), ws_gate=inp.get("ws_gate"),
+                                ws_up=inp.get("ws_up"), ws_down=inp.get("ws_down"),
+                                balance_coef=0.01, z_coef=0.001, workspace=ws, saved=saved)
+    ms_saved = timed(bwd_saved)
+    _log(f"[bench] with saved state: forward {f_plain:.3f} -> {f_save:.3f} ms, backward "
+         f"{ms:.3f} -> {ms_saved:.3f} ms")
     return {"ms_per_step": round(ms, 4), "algorithmic_flop": flops,
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "with_saved_state": {"forward_ms": round(f_save, 4),
+                                 "forward_without_saving_ms": round(f_plain, 4),
+                                 "backward_ms": round(ms_saved, 4),
+                                 "saved_bytes": moe.saved_bytes(cfg)}}
 
 
 SIMDS = 256 * 4  # MI355X: 256 compute units of four SIMDs

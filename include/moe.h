@@ -233,7 +233,11 @@ moe_status moe_rmsnorm(const moe_config* cfg, const void* x, const float* norm_w
  * per token as in moe_combine; token_mask as in moe_route; residual [T, D]
  * (optional) is added to the output as in moe_combine.  The optional
  * outputs expert_ids [T,k], gate_w [T,k], counts [E] and aux [2] receive the
- * routing results when non-NULL. */
+ * routing results when non-NULL.  saved (optional, bf16 only; device memory
+ * of moe_saved_bytes(cfg) bytes, 256-byte aligned, caller-owned) receives the
+ * SwiGLU state of every routed row and of the shared expert for
+ * moe_backward, which then skips recomputing it: silu(g)*u (the forward's
+ * own hidden rows) and the factors d act/d g, d act/d u, bf16. */
 moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_weight,
                        const void* w_router,
                        const float* logit_bias, const float* select_bias,
@@ -242,8 +246,13 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
                        const void* w_shared_up, const void* w_shared_down,
                        const void* shared_expert_gate, const void* residual, void* out,
                        int32_t* expert_ids,
-                       float* gate_w, int32_t* counts, float* aux, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+                       float* gate_w, int32_t* counts, float* aux, void* saved,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the forward's saved SwiGLU state (0 if the configuration is
+ * invalid or not bf16): act, d act/d g and d act/d u of moe_max_rows(cfg)
+ * routed rows x H, then of T rows x H_shared. */
+size_t moe_saved_bytes(const moe_config* cfg);
 
 /* Workspace bytes of moe_backward (0 if the configuration is invalid or not
  * covered by the backward: bf16 activations only). */
@@ -273,6 +282,9 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg);
  *   d_norm_weight       [D] f32 out or NULL (pre_norm only): dL/d norm weight
  *   d_shared_gate       [D] f32 out or NULL (needs shared_expert_gate):
  *                       dL/d shared-expert gate vector
+ *   saved               NULL, or the state moe_forward saved for these same
+ *                       inputs and routes (then the gate/up GEMMs are not
+ *                       recomputed)
  * With the gated shared expert (NeMo MoE.shared_expert_gate, read as
  * g_t = sigmoid(x_t . w_sg) scaling the shared expert's output), the shared
  * expert receives g_t dout_t and the gate's logit g_t (1 - g_t) <dout_t, S_t>,
@@ -296,7 +308,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
                         void* dx, float* dw_router, float* dw_gate, float* dw_up,
                         float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
                         float* d_shared_gate, float* d_gate_w, float* d_norm_weight,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+                        const void* saved, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 /* Auxiliary-loss-free balancer step ("DeepSeek-MoE and the fine-grained +
  * shared-expert idea" and "Exercises" 6 on the book page; NeMo

@@ -7,6 +7,6 @@ Importing it fails loudly when the library has not been built.
 from ._binding import (  # noqa: F401
     EXPORTED, LIB_PATH, MoeConfig, MoeError, backward_workspace_bytes, capacity, check_config,
     make_config, max_rows, moe_backward, moe_combine, moe_forward, moe_grouped_swiglu,
-    moe_permute, moe_rmsnorm, moe_route, moe_update_bias, new_workspace, status_string,
-    workspace_bytes,
+    moe_permute, moe_rmsnorm, moe_route, moe_update_bias, new_saved, new_workspace,
+    saved_bytes, status_string, workspace_bytes,
 )

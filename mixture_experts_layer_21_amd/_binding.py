@@ -95,12 +95,13 @@ _sigs = {
                                           _P, _P, _P, _SZ, _P]),
     "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                   _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+                                   _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_saved_bytes": (ctypes.c_size_t, [_CFG]),
     "moe_rmsnorm": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
     "moe_backward_workspace_bytes": (_SZ, [_CFG]),
     "moe_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P, _P, _P,
-                                    _P, _P, _P, _P, _P, _P, _SZ, _P]),
+                                    _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_update_bias": (ctypes.c_int, [_CFG, _P, ctypes.c_float, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
@@ -322,9 +323,11 @@ def moe_combine(cfg, y_rows, assign_to_row, shared_rows=None, out=None, validate
 def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, select_bias=None,
                 ws_gate=None, ws_up=None, ws_down=None, out=None, expert_ids=None, gate_w=None,
                 counts=None, aux=None, workspace=None, token_mask=None,
-                shared_expert_gate=None, residual=None, norm_weight=None):
+                shared_expert_gate=None, residual=None, norm_weight=None, saved=None):
     """The whole layer forward (see ``moe_forward``); with ``cfg.pre_norm``
-    the layer takes RMSNorm(x) (``norm_weight`` [D] f32 or None)."""
+    the layer takes RMSNorm(x) (``norm_weight`` [D] f32 or None).  ``saved``
+    (uint8 device tensor of ``saved_bytes(cfg)``, see ``new_saved``) receives
+    the SwiGLU state that ``moe_backward(saved=...)`` then reuses."""
     check_config(cfg)
     T, D, H, E, k, Hs = cfg.T, cfg.D, cfg.H, cfg.E, cfg.top_k, cfg.H_shared
     dt = cfg.act_torch_dtype
@@ -355,8 +358,8 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, sele
                             _ptr(select_bias), _ptr(token_mask), _ptr(w_gate), _ptr(w_up),
                             _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
                             _ptr(shared_expert_gate), _ptr(residual), _ptr(out),
-                            _ptr(expert_ids), _ptr(gate_w), _ptr(counts), _ptr(aux), _ptr(ws),
-                            ws.numel(), _stream()), "moe_forward")
+                            _ptr(expert_ids), _ptr(gate_w), _ptr(counts), _ptr(aux),
+                            _ptr(saved), _ptr(ws), ws.numel(), _stream()), "moe_forward")
     return out
 
 
@@ -378,15 +381,29 @@ def backward_workspace_bytes(cfg) -> int:
     return int(_lib.moe_backward_workspace_bytes(ctypes.byref(cfg)))
 
 
+def saved_bytes(cfg):
+    """Bytes of the forward's saved SwiGLU state (0: not bf16)."""
+    return int(_lib.moe_saved_bytes(ctypes.byref(cfg)))
+
+
+def new_saved(cfg, device="cuda"):
+    n = saved_bytes(cfg)
+    if n == 0:
+        raise ValueError("saved SwiGLU state needs bf16 activations")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, expert_ids, gate_w, dout, *,
                  logit_bias=None, ws_gate=None, ws_up=None, ws_down=None, balance_coef=0.0,
                  z_coef=0.0, workspace=None, d_gate_w=False, norm_weight=None,
-                 shared_expert_gate=None):
+                 shared_expert_gate=None, saved=None):
     """Gradients of <dout, out> + balance_coef*balance + z_coef*z (see
     ``moe_backward``).  Returns a dict with dx (act dtype) and the fp32
     weight gradients dw_router, dw_gate, dw_up, dw_down (+ dws_* with a shared
     expert, + d_gate_w [T,k] when asked, + d_norm_weight [D] with the
-    pre-norm, + d_shared_gate [D] with ``shared_expert_gate``).  With
+    pre-norm, + d_shared_gate [D] with ``shared_expert_gate``).  ``saved``:
+    the state ``moe_forward(saved=...)`` kept for these inputs and routes
+    (the gate/up GEMMs are then not recomputed).  With
     ``cfg.pre_norm``, ``x`` is the input before the norm and ``norm_weight``
     [D] f32 (None: unit weight) its weight."""
     check_config(cfg)
@@ -435,7 +452,7 @@ def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, expert_ids, gate_w, dou
                              _ptr(g["dw_down"]), _ptr(g.get("dws_gate")), _ptr(g.get("dws_up")),
                              _ptr(g.get("dws_down")), _ptr(g.get("d_shared_gate")),
                              _ptr(g.get("d_gate_w")),
-                             _ptr(g.get("d_norm_weight")), _ptr(ws),
+                             _ptr(g.get("d_norm_weight")), _ptr(saved), _ptr(ws),
                              0 if ws is None else ws.numel(), _stream()), "moe_backward")
     return g
 

@@ -46,6 +46,22 @@ __device__ __forceinline__ float swiglu_act(float g, float u, float limit) {
   return silu_f32(g) * u;
 }
 
+// The two factors of d act = p1 dg + p2 du for act = silu(g) u (each input
+// clamped to [-limit, limit] first when limit > 0, with no gradient where it
+// clamps), rounded to bf16 at element o of save_p1 / save_p2.
+__device__ __forceinline__ void save_factors(const GemmParams& p, size_t o, float g, float u) {
+  float gc = g, uc = u, mg = 1.f, mu = 1.f;
+  if (p.swiglu_limit > 0.f) {
+    gc = fminf(fmaxf(g, -p.swiglu_limit), p.swiglu_limit);
+    uc = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+    mg = fabsf(g) < p.swiglu_limit ? 1.f : 0.f;
+    mu = fabsf(u) < p.swiglu_limit ? 1.f : 0.f;
+  }
+  const float s = 1.0f / (1.0f + __expf(-gc));
+  p.save_p1[o] = f32_to_bf16_bits(mg * uc * (s + gc * s * (1.f - s)));
+  p.save_p2[o] = f32_to_bf16_bits(mu * gc * s);
+}
+
 struct Tile {
   int e, m0, m_end, nt;
 };
@@ -392,6 +408,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int t
           if (col < N) {
             const float g = acc[0][mi][ni][i], u = acc[1][mi][ni][i];
             out[col] = f32_to_bf16_bits(swiglu_act(g, u, p.swiglu_limit));
+            if (p.save_p1) save_factors(p, (size_t)grow * N + col, g, u);
           }
         }
       } else {
@@ -448,6 +465,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmPar
     if constexpr (GATEUP) {
       static_cast<uint16_t*>(p.hbuf)[(size_t)grow * N + col] =
           f32_to_bf16_bits(swiglu_act(a0, a1, p.swiglu_limit));
+      if (p.save_p1) save_factors(p, (size_t)grow * N + col, a0, a1);
     } else {
       float gw = 1.f;
       if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[grow]];
@@ -477,9 +495,12 @@ __device__ __forceinline__ void dma_epilogue(const GemmParams& p, int m0, int m_
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni) {
           const int col = n0 + wn * C::WN + ni * 32 + lr;
-          if (col < N)
+          if (col < N) {
             out[col] = f32_to_bf16_bits(
                 swiglu_act(acc[0][mi][ni][i], acc[1][mi][ni][i], p.swiglu_limit));
+            if (p.save_p1)
+              save_factors(p, (size_t)grow * N + col, acc[0][mi][ni][i], acc[1][mi][ni][i]);
+          }
         }
       } else {
         float gw = 1.f;

@@ -76,6 +76,11 @@ struct GemmParams {
   void* hbuf;                // [max_rows, hidden]
   void* y;                   // [max_rows, D]
   float swiglu_limit;        // > 0: clamp gate and up to [-limit, limit]
+  // bf16 gate/up only, or null: the two SwiGLU factors d act/d g and
+  // d act/d u (clamp included) of every Hb element, [max_rows, hidden] like
+  // hbuf, kept for the backward
+  uint16_t* save_p1;
+  uint16_t* save_p2;
   // Split-K tail of the large-tile kernel (null: no split).  Per XCD: the
   // fp32 partial tiles [kTailSlots], the (tail tiles, pieces) pair and the
   // tile descriptors (expert, first row, row end, column tile).

@@ -376,6 +376,36 @@ size_t moe_workspace_bytes(const moe_config* cfg) {
   return layout_of(cfg).total;
 }
 
+// Saved SwiGLU state: act, p1, p2 of every routed row [rows, H], then the
+// same of the shared expert [T, Hs], bf16.
+struct SavedLayout {
+  size_t act, p1, p2, sact, sp1, sp2, total;
+};
+
+SavedLayout saved_layout_of(const moe_config* c) {
+  SavedLayout S{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t R = (size_t)max_rows_of(c), H = c->H, T = c->T, Hs = c->H_shared;
+  S.act = take(R * H * 2);
+  S.p1 = take(R * H * 2);
+  S.p2 = take(R * H * 2);
+  S.sact = take(T * Hs * 2);
+  S.sp1 = take(T * Hs * 2);
+  S.sp2 = take(T * Hs * 2);
+  S.total = off;
+  return S;
+}
+
+size_t moe_saved_bytes(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK || cfg->act_dtype != MOE_BF16) return 0;
+  return saved_layout_of(cfg).total;
+}
+
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
                      const float* logit_bias, const float* select_bias,
                      const uint8_t* token_mask, int32_t* expert_ids, float* gate_w,
@@ -556,9 +586,11 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
                        const void* w_down, const void* w_shared_gate, const void* w_shared_up,
                        const void* w_shared_down, const void* shared_expert_gate,
                        const void* residual, void* out, int32_t* expert_ids, float* gate_w,
-                       int32_t* counts, float* aux,
+                       int32_t* counts, float* aux, void* saved,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_config(cfg));
+  if (saved && cfg->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_forward: saved needs bf16 activations");
   if (!x || !w_router || !w_gate || !w_up || !w_down || !out)
     return fail(MOE_ERR_NULL_PTR, "moe_forward: x, w_router, expert weights and out required");
   if (cfg->H_shared > 0 && (!w_shared_gate || !w_shared_up || !w_shared_down))
@@ -590,6 +622,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
   MOE_TRY(check_dev(counts, "counts", false));
   MOE_TRY(check_dev(aux, "aux", false));
   MOE_TRY(check_dev(workspace, "workspace", true));
+  MOE_TRY(check_dev(saved, "saved", false));
+  if (reinterpret_cast<uintptr_t>(saved) % kAlign)
+    return fail(MOE_ERR_INVALID_ARG, "saved must be %zu-byte aligned", kAlign);
   if (cfg->pre_norm) {
     MOE_TRY(check_align16(x, "x"));
     MOE_TRY(check_align16(norm_weight, "norm_weight"));
@@ -643,15 +678,27 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
   void* y = at<void>(workspace, L.y);
   const bool bf16 = cfg->act_dtype == MOE_BF16;
   void* tail = bf16 ? at<void>(workspace, L.tail) : nullptr;
-  const moe::GemmParams gp = gemm_params(cfg, cfg->E, cfg->H, x, r2a, offsets, rows, gw, w_gate,
-                                         w_up, w_down, hbuf, y, tail);
+  // With `saved`, Hb of the routed rows and of the shared expert lives there
+  // (act), next to the SwiGLU factors the gate/up epilogues add.
+  const SavedLayout SV = saved_layout_of(cfg);
+  auto sv = [&](size_t off) { return reinterpret_cast<uint16_t*>(static_cast<char*>(saved) + off); };
+  moe::GemmParams gp = gemm_params(cfg, cfg->E, cfg->H, x, r2a, offsets, rows, gw, w_gate, w_up,
+                                   w_down, saved ? sv(SV.act) : hbuf, y, tail);
+  if (saved) {
+    gp.save_p1 = sv(SV.p1);
+    gp.save_p2 = sv(SV.p2);
+  }
   MOE_TRY(hip_ok(moe::launch_grouped_swiglu(gp, bf16, stream), "grouped swiglu kernels"));
   void* sy = nullptr;
   if (cfg->H_shared > 0) {
     sy = at<void>(workspace, L.shared_y);
-    const moe::GemmParams sp2 =
+    moe::GemmParams sp2 =
         gemm_params(cfg, 1, cfg->H_shared, x, nullptr, nullptr, cfg->T, nullptr, w_shared_gate,
-                    w_shared_up, w_shared_down, hbuf, sy, tail);
+                    w_shared_up, w_shared_down, saved ? sv(SV.sact) : hbuf, sy, tail);
+    if (saved) {
+      sp2.save_p1 = sv(SV.sp1);
+      sp2.save_p2 = sv(SV.sp2);
+    }
     MOE_TRY(hip_ok(moe::launch_grouped_swiglu(sp2, bf16, stream), "shared expert kernels"));
   }
   moe::CombineParams cp{cfg->T, cfg->D, cfg->top_k, y,        a2r,
@@ -674,7 +721,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
                         void* dx, float* dw_router, float* dw_gate, float* dw_up,
                         float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
                         float* d_shared_gate, float* d_gate_w, float* d_norm_weight,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        const void* saved, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   MOE_TRY(check_config(cfg));
   if (cfg->act_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "moe_backward: bf16 activations only");
@@ -712,6 +760,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
   MOE_TRY(check_dev(d_norm_weight, "d_norm_weight", false));
   MOE_TRY(check_dev(shared_expert_gate, "shared_expert_gate", false));
   MOE_TRY(check_dev(d_shared_gate, "d_shared_gate", false));
+  MOE_TRY(check_dev(saved, "saved", false));
   MOE_TRY(check_align16(shared_expert_gate, "shared_expert_gate"));
   if (cfg->pre_norm) {
     MOE_TRY(check_align16(x, "x"));
@@ -815,6 +864,20 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     return hip_ok(moe::launch_bwd_gemm(g, stream), what);
   };
   const int kNoSplit = 0x7fffffff;
+  // The SwiGLU state (act, p1, p2 per row): the forward's `saved`, else
+  // recomputed into the workspace.
+  const SavedLayout SV = saved_layout_of(cfg);
+  auto state = [&](size_t saved_off, size_t ws_off) {
+    return saved ? reinterpret_cast<uint16_t*>(const_cast<char*>(static_cast<const char*>(saved)) +
+                                               saved_off)
+                 : u16(ws_off);
+  };
+  uint16_t* const act_p = state(SV.act, B.act);
+  uint16_t* const p1_p = state(SV.p1, B.p1);
+  uint16_t* const p2_p = state(SV.p2, B.p2);
+  uint16_t* const sact_p = state(SV.sact, B.sact);
+  uint16_t* const sp1_p = state(SV.sp1, B.sp1);
+  uint16_t* const sp2_p = state(SV.sp2, B.sp2);
   // 4. recompute gate/up: act, p1, p2 of every kept row
   {
     moe::BwdGemmParams g{};
@@ -833,14 +896,14 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     g.B2 = static_cast<const uint16_t*>(w_up);
     g.ldb = D;
     g.b_gstride = (long long)H * D;
-    g.act = u16(B.act);
-    g.p1 = u16(B.p1);
-    g.p2 = u16(B.p2);
+    g.act = act_p;
+    g.p1 = p1_p;
+    g.p2 = p2_p;
     g.ldh = H;
     g.limit = cfg->swiglu_limit;
     g.a_bytes = 2ll * T * D;
     g.b_bytes = 2ll * H * D;
-    MOE_TRY(gemm(g, "recompute gate/up"));
+    if (!saved) MOE_TRY(gemm(g, "recompute gate/up"));
     // 5. down dgrad: dL/d act for unit gate weight (bf16), then the SwiGLU
     // backward with the gate weights: dg, du and dL/dw of every kept row
     moe::BwdGemmParams d{};
@@ -866,7 +929,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     d.a_bytes = 2ll * T * D;
     d.b_bytes = 2ll * H * D;
     MOE_TRY(gemm(d, "down dgrad"));
-    moe::SwigluBwdParams q{R, H, offsets, E, u16(B.dact), u16(B.act), u16(B.p1), u16(B.p2),
+    moe::SwigluBwdParams q{R, H, offsets, E, u16(B.dact), act_p, p1_p, p2_p,
                            gate_w, r2a, u16(B.dgu), f32(B.dw)};
     MOE_TRY(hip_ok(moe::launch_swiglu_bwd(q, stream), "swiglu backward kernel"));
   }
@@ -951,14 +1014,14 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     g.B = static_cast<const uint16_t*>(w_shared_gate);
     g.B2 = static_cast<const uint16_t*>(w_shared_up);
     g.ldb = D;
-    g.act = u16(B.sact);
-    g.p1 = u16(B.sp1);
-    g.p2 = u16(B.sp2);
+    g.act = sact_p;
+    g.p1 = sp1_p;
+    g.p2 = sp2_p;
     g.ldh = Hs;
     g.limit = cfg->swiglu_limit;
     g.a_bytes = 2ll * T * D;
     g.b_bytes = 2ll * Hs * D;
-    MOE_TRY(gemm(g, "shared recompute"));
+    if (!saved) MOE_TRY(gemm(g, "shared recompute"));
     moe::BwdGemmParams d{};
     d.grouping = moe::BWD_DENSE;
     d.epilogue = moe::BWD_EPI_F32;
@@ -980,8 +1043,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     MOE_TRY(gemm(d, "shared down dgrad"));
     // with the gate: the branch sees g_t dout_t, and <dout_t, S_t> (for the
     // gate's own gradient) is sum_h act * dact, as dL/dw of a routed row
-    moe::SwigluBwdParams q{T, Hs, nullptr, 1, u16(B.sdact), u16(B.sact), u16(B.sp1),
-                           u16(B.sp2), sgate ? f32(B.sgv) : nullptr, nullptr, u16(B.sdgu),
+    moe::SwigluBwdParams q{T, Hs, nullptr, 1, u16(B.sdact), sact_p, sp1_p, sp2_p,
+                           sgate ? f32(B.sgv) : nullptr, nullptr, u16(B.sdgu),
                            sgate ? f32(B.sdw) : nullptr};
     MOE_TRY(hip_ok(moe::launch_swiglu_bwd(q, stream), "shared swiglu backward kernel"));
     moe::BwdGemmParams z{};
@@ -1024,7 +1087,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
                     r2a, true));
   MOE_TRY(transpose(R, D, x, false, D, 0, B.Kpad, u16(B.XT), B.Kpad, 0, 0, 1, r2a, nullptr,
                     nullptr, true));
-  MOE_TRY(transpose(R, H, u16(B.act), false, H, 0, B.Kpad, u16(B.AT), B.Kpad, 0, 0, 1, nullptr,
+  MOE_TRY(transpose(R, H, act_p, false, H, 0, B.Kpad, u16(B.AT), B.Kpad, 0, 0, 1, nullptr,
                     nullptr, nullptr, true));
   MOE_TRY(transpose(R, 2 * H, u16(B.dgu), false, 2 * H, 0, B.Kpad, u16(B.DGUT), B.Kpad, 0, 0, 1,
                     nullptr, nullptr, nullptr, true));
@@ -1091,7 +1154,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
   if (sh) {
     MOE_TRY(transpose(T, D, dout, false, D, 0, B.Tpad, u16(B.doutT), B.Tpad, 0, 0, 1, nullptr,
                       sgate ? f32(B.sgv) : nullptr, nullptr, false));
-    MOE_TRY(transpose(T, Hs, u16(B.sact), false, Hs, 0, B.Tpad, u16(B.sAT), B.Tpad, 0, 0, 1,
+    MOE_TRY(transpose(T, Hs, sact_p, false, Hs, 0, B.Tpad, u16(B.sAT), B.Tpad, 0, 0, 1,
                       nullptr, nullptr, nullptr, false));
     MOE_TRY(transpose(T, 2 * Hs, u16(B.sdgu), false, 2 * Hs, 0, B.Tpad, u16(B.sDGUT), B.Tpad, 0,
                       0, 1, nullptr, nullptr, nullptr, false));

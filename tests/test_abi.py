@@ -109,16 +109,17 @@ def test_backward_host_checks(moe):
 
     def call(cfg, **given):
         # positions: 2 norm_weight, 11 shared_expert_gate, 15/16 loss
-        # coefficients, 25 d_shared_gate, 27 d_norm_weight, 29 bytes, 30 stream
+        # coefficients, 25 d_shared_gate, 27 d_norm_weight, 28 saved,
+        # 30 bytes, 31 stream
         args = [ctypes.byref(cfg)] + [fake] * (nargs - 1)
-        args[2] = args[11] = args[25] = args[27] = None
+        args[2] = args[11] = args[25] = args[27] = args[28] = None
         for pos, v in given.items():
             args[int(pos[1:])] = v
         args[15] = args[16] = 0.0
         args[-2], args[-1] = 0, None
         return f(*args)
 
-    assert nargs == 31
+    assert nargs == 32
     cfg = moe.make_config(256, 64, 128, 4, 2)
     assert call(cfg, p2=fake) == 1  # MOE_ERR_INVALID_ARG: norm_weight needs pre_norm
     assert "pre_norm" in lib_error(moe)
@@ -135,6 +136,17 @@ def test_backward_host_checks(moe):
 
 def lib_error(moe):
     return moe._binding._lib.moe_last_error().decode()
+
+
+def test_saved_bytes(moe):
+    """The forward's saved SwiGLU state: three bf16 [rows, H] arrays and three
+    [T, Hs] arrays; none for fp32 activations."""
+    cfg = moe.make_config(4096, 4096, 14336, 8, 2)
+    assert moe.saved_bytes(cfg) >= 3 * 8192 * 14336 * 2
+    sh = moe.make_config(512, 1024, 256, 16, 4, H_shared=512)
+    assert moe.saved_bytes(sh) >= 3 * 2 * (moe.max_rows(sh) * 256 + 512 * 512)
+    assert moe.saved_bytes(moe.make_config(256, 64, 128, 4, 2, act_dtype="f32",
+                                           router_dtype="f32")) == 0
 
 
 def test_workspace_grows_with_problem(moe):

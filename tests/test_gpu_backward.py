@@ -208,6 +208,51 @@ def test_backward_gated_shared_expert(moe, pre_norm):
     _compare(g, ref, names, "gated shared expert")
 
 
+@pytest.mark.parametrize("name", ["mixtral_small", "deepseek_small", "switch_small",
+                                  "decode_small"])
+def test_backward_with_saved_state(moe, name):
+    """moe_forward(saved=...) keeps the SwiGLU state and moe_backward(saved=...)
+    skips the gate/up recompute: the forward output is unchanged by saving,
+    and the gradients still match the oracle.  (The device's routes equal the
+    oracle's at this seed, so the saved rows are the oracle's rows.)"""
+    w = W.SMALL[name]
+    inp = W.make_inputs(w, "cpu", seed=43)
+    oi = P.oracle_inputs(inp)
+    r = P.oracle_route(w, oi)
+    d = {k: v.to("cuda") for k, v in inp.items()}
+    cfg = P.config_of(w)
+    ids = torch.empty(w.T, w.top_k, dtype=torch.int32, device="cuda")
+    gw = torch.empty(w.T, w.top_k, dtype=torch.float32, device="cuda")
+    kw = dict(logit_bias=d.get("logit_bias"), select_bias=d.get("select_bias"),
+              ws_gate=d.get("ws_gate"), ws_up=d.get("ws_up"), ws_down=d.get("ws_down"))
+    saved = moe.new_saved(cfg)
+    _say(f"[saved state] {name}: forward with and without saving")
+    out = moe.moe_forward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                          expert_ids=ids, gate_w=gw, saved=saved, **kw)
+    plain = moe.moe_forward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                            **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)
+    assert (ids.cpu().numpy() == r["ids"]).all()
+    dout = torch.randn(w.T, w.D, generator=torch.Generator().manual_seed(44)).to(
+        W.torch_dtype(w.act_dtype))
+    aux = (0.3, 0.2)
+    fw = dict(top_k=w.top_k, score=w.score, renormalize=w.renormalize,
+              route_scale=w.route_scale, n_groups=w.n_groups, topk_groups=w.topk_groups,
+              group_rule=w.group_rule, capacity_factor=w.capacity_factor)
+    ref = P.oracle.backward(oi, dout.to(torch.float64).numpy(), aux_coef=aux, **fw)
+    _say(f"[saved state] {name}: backward on the saved state")
+    g = moe.moe_backward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                         torch.from_numpy(r["ids"].astype(np.int32)).cuda(),
+                         torch.from_numpy(r["weights"].astype(np.float32)).cuda(), dout.cuda(),
+                         logit_bias=d.get("logit_bias"), ws_gate=d.get("ws_gate"),
+                         ws_up=d.get("ws_up"), ws_down=d.get("ws_down"), balance_coef=aux[0],
+                         z_coef=aux[1], d_gate_w=True, saved=saved)
+    torch.cuda.synchronize()
+    names = GRADS + (SHARED if w.H_shared else ()) + ("d_gate_w",)
+    _compare(g, ref, names, f"{name} with saved state")
+
+
 def test_backward_dropped_slots(moe):
     """Capacity drops: a dropped slot's dL/dw is exactly 0."""
     w = W.SMALL["switch_small"]
