@@ -147,7 +147,7 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
       const int src = p.gather ? p.gather[m] / p.gdiv : m;
       arow = (long long)src * p.lda;
     }
-    a_src[i] = p.A + arow + kc * 8;
+    a_src[i] = p.a_kmajor ? nullptr : p.A + arow + kc * 8;
     const uint16_t* bb;
     if (p.b_kmajor) {  // chunk c: k row c / 16, columns 8*(c % 16) .. +7
       b_src[i] = nullptr;
@@ -176,39 +176,70 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
   const int nk = (t.k1 - t.k0) / BBK;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, lk = lane >> 5;
   u32x4 ra[BCH], rb[BCH];
+  // k-major operands: chunk c of a stage is k row c / 16, columns
+  // 8*(c % 16) .. +7 of the tile; rows past the operand's rows (the group's,
+  // for KRAGGED; else past its byte extent) load as zeros.
+  const long long a_rows = kr ? 0 : p.a_bytes / (2 * p.lda);
+  const long long b_rows = kr ? 0 : p.b_bytes / (2 * p.ldb);
+  const int kg0 = kr && p.krows ? p.krows[t.g] : 0;
+  const int kg1 = kr && p.krows ? p.krows[t.g + 1] : 0;
+  auto kmajor_load = [&](const uint16_t* base, const uint16_t* base2, long long ld, long long rows,
+                         int k, int col, int ncols) -> u32x4 {
+    if (col >= ncols) col = 0;
+    long long row;
+    const uint16_t* src = base;
+    if (kr) {
+      row = kg0 + (long long)k;
+      if (row >= kg1) return u32x4{0u, 0u, 0u, 0u};
+    } else {
+      row = k;
+      if (base2 && k >= p.k_split) {
+        src = base2;
+        row = k - p.k_split;
+      }
+      if (row >= rows) return u32x4{0u, 0u, 0u, 0u};
+    }
+    return *reinterpret_cast<const u32x4*>(src + row * ld + col);
+  };
   auto gload = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kt * BBK);
+      const int c = tid + BT * i, k = kt * BBK + c / (BBN / 8), c8 = (c % (BBN / 8)) * 8;
+      if (p.a_kmajor)
+        ra[i] = kmajor_load(p.A, nullptr, p.lda, a_rows, k, t.m0 + c8, p.M);
+      else
+        ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + (size_t)kt * BBK);
       if (p.b_kmajor) {
-        const int c = tid + BT * i, k = kt * BBK + c / (BBN / 8);
-        int n = t.nt * BBN + (c % (BBN / 8)) * 8;
-        if (n >= p.N) n = 0;
-        const uint16_t* src = k >= p.k_split
-            ? p.B2 + (long long)t.g * p.b_gstride + (long long)(k - p.k_split) * p.ldb + n
-            : p.B + (long long)t.g * p.b_gstride + (long long)k * p.ldb + n;
-        rb[i] = *reinterpret_cast<const u32x4*>(src);
+        const long long gs = kr ? 0 : (long long)t.g * p.b_gstride;
+        rb[i] = kmajor_load(p.B + gs, p.B2 ? p.B2 + gs : nullptr, p.ldb, b_rows, k,
+                            t.nt * BBN + c8, p.N);
       } else {
         rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + (size_t)kt * BBK);
       }
     }
   };
+  // 8 columns of one k row into the row-major (k-contiguous) swizzled tile
+  auto scatter8 = [&](uint16_t* tile, const u32x4& v, int c) {
+    const int k = c / (BBN / 8), n0 = (c % (BBN / 8)) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int n = n0 + e;
+      const uint32_t w = v[e >> 1];
+      tile[n * BBK + ((k >> 3) ^ bswz(n)) * 8 + (k & 7)] =
+          (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+  };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-      *reinterpret_cast<u32x4*>(&As[buf][dst[i]]) = ra[i];
-      if (p.b_kmajor) {  // 8 columns of one k row into the n-major tile
-        const int c = tid + BT * i, k = c / (BBN / 8), n0 = (c % (BBN / 8)) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int n = n0 + e;
-          const uint32_t w = rb[i][e >> 1];
-          Bs[buf][n * BBK + ((k >> 3) ^ bswz(n)) * 8 + (k & 7)] =
-              (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
-        }
-      } else {
+      if (p.a_kmajor)
+        scatter8(As[buf], ra[i], tid + BT * i);
+      else
+        *reinterpret_cast<u32x4*>(&As[buf][dst[i]]) = ra[i];
+      if (p.b_kmajor)
+        scatter8(Bs[buf], rb[i], tid + BT * i);
+      else
         *reinterpret_cast<u32x4*>(&Bs[buf][dst[i]]) = rb[i];
-      }
     }
   };
   if (nk > 0) {
@@ -295,7 +326,7 @@ __global__ __launch_bounds__(BT) void bwd_gemm_kernel(BwdGemmParams p) {
 // threads, BK = 64, two LDS stages, operands fetched straight into the
 // swizzled LDS tiles by buffer loads with 32-bit offsets.  With the paired
 // gate/up tile the B tile is 128 gate rows then the same 128 up rows.
-template <int EPI, bool BTR>
+template <int EPI, bool ATR, bool BTR>
 __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   constexpr bool PAIRED = EPI == BWD_EPI_GATEUP_SAVE;
   using C = dma::DmaCfg<256, 256, 64, 2, 2, 8, PAIRED>;
@@ -311,11 +342,16 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   const bool kr = p.grouping == BWD_KRAGGED;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const __amdgpu_buffer_rsrc_t rA =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, (int)p.a_bytes, 0x00020000);
-  const long long bg = kr ? 0 : (long long)t.g * p.b_gstride;
-  const __amdgpu_buffer_rsrc_t rG =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + bg), 0, (int)p.b_bytes, 0x00020000);
+  // A k-major operand of a ragged-K group starts at the group's first row and
+  // its resource covers exactly the group's rows (past them: zeros).
+  const int kr0 = kr && (ATR || BTR) ? p.krows[t.g] : 0;
+  const long long krn = kr && (ATR || BTR) ? p.krows[t.g + 1] - kr0 : 0;
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.A + (ATR && kr ? (long long)kr0 * p.lda : 0)), 0,
+      (int)(ATR && kr ? krn * p.lda * 2 : p.a_bytes), 0x00020000);
+  const long long bg = kr ? (BTR ? (long long)kr0 * p.ldb : 0) : (long long)t.g * p.b_gstride;
+  const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.B + bg), 0, (int)(BTR && kr ? krn * p.ldb * 2 : p.b_bytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t rU =
       (PAIRED || (BTR && p.B2))
           ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.B2 + bg), 0, (int)p.b_bytes, 0x00020000)
@@ -323,6 +359,14 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   uint32_t a_off[C::A_LD];
 #pragma unroll
   for (int i = 0; i < C::A_LD; ++i) {
+    if constexpr (ATR) {  // k-major tile, as the B tile below
+      const int k = 2 * (wave + C::NW * i) + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (k & 3));
+      int m = t.m0 + c * 8;
+      if (m >= p.M) m = 0;
+      a_off[i] = (uint32_t)(((long long)k * p.lda + m) * 2);
+      continue;
+    }
     const int slot = (wave + C::NW * i) * 64 + lane;
     const int r = slot / KCH, lc = (slot % KCH) ^ dma::swz_k<KCH>(r);
     int m = t.m0 + r;
@@ -353,7 +397,8 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
     }
   }
   const dma::DmaLoads<C, PAIRED> ld{rA, rG, rU, a_off, b_off, wave,
-                                    (uint32_t)(p.ldb * 2), BTR ? p.k_split : 0};
+                                    (uint32_t)(p.ldb * 2), BTR ? p.k_split : 0,
+                                    (uint32_t)(p.lda * 2)};
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int lr = lane & 31, lk = lane >> 5;
   f32x16 acc[NB][MI][NI];
@@ -370,8 +415,8 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   // deduction; kernel bodies are never run on the host.)
 #if defined(__HIP_DEVICE_COMPILE__)
   if (nk > 0)
-    dma::dma_mainloop<C, PAIRED, false, BTR>(ld, nk, MI, wm, wn, lr, lk, acc, sA0, sA1, sX, sX,
-                                             sB0, sB1, sX, sX);
+    dma::dma_mainloop<C, PAIRED, false, BTR, ATR>(ld, nk, MI, wm, wn, lr, lk, acc, sA0, sA1, sX,
+                                                  sX, sB0, sB1, sX, sX);
 #endif
 
   // Epilogue: element i of accumulator (nb, mi, ni) of lane l is row
@@ -806,15 +851,17 @@ hipError_t launch_bwd_gemm(const BwdGemmParams& p, hipStream_t s) {
     else
       blocks = (long long)nN * ((p.max_rows + 255) / 256 + p.G);
     if (blocks <= 0) return hipSuccess;
+    const dim3 grid((unsigned)blocks), block(512);
     if (p.epilogue != BWD_EPI_F32)
-      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_GATEUP_SAVE, false>), dim3((unsigned)blocks),
-                         dim3(512), 0, s, p);
+      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_GATEUP_SAVE, false, false>), grid, block, 0, s, p);
+    else if (p.a_kmajor && p.b_kmajor)
+      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_F32, true, true>), grid, block, 0, s, p);
+    else if (p.a_kmajor)
+      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_F32, true, false>), grid, block, 0, s, p);
     else if (p.b_kmajor)
-      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_F32, true>), dim3((unsigned)blocks), dim3(512),
-                         0, s, p);
+      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_F32, false, true>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_F32, false>), dim3((unsigned)blocks), dim3(512),
-                         0, s, p);
+      hipLaunchKernelGGL((bwd_dma_kernel<BWD_EPI_F32, false, false>), grid, block, 0, s, p);
     return hipGetLastError();
   }
   long long blocks;

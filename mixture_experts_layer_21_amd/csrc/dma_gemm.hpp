@@ -82,13 +82,16 @@ struct DmaLoads {
   // k-major B only: bytes per k row, and the k from which rows come from rU
   uint32_t b_kbytes;
   int k_split;
+  // k-major A only: bytes per k row
+  uint32_t a_kbytes;
 };
 
 // One wave load (1 KB) of the B tile of k-step kt into stage buffer sb.
 // K-contiguous B (BTR false): 16-byte chunks along k of BNB rows, GATEUP
 // taking the second half of the rows from rU.  k-major B (BTR true, "B
 // transposed": row k holds the N columns): BK rows of BNB columns, the rows
-// at and past k_split from rU.
+// at and past k_split from rU; the k advance goes into the lane offset, so
+// the resource's range check sees it (rows past the range read as zeros).
 #define MOE_DMA_B(C, GATEUP, BTR, ld, sb, kt, i)                                             \
   do {                                                                                      \
     const int blk_ = (ld).wave + C::NW * (i);                                               \
@@ -96,8 +99,9 @@ struct DmaLoads {
       const int k_ = (kt) * C::BK;                                                          \
       const bool hi_ = k_ >= (ld).k_split;                                                  \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(                                             \
-          hi_ ? (ld).rU : (ld).rG, (lds_void_t*)((sb) + blk_ * 512), 16, (ld).b_off[i],     \
-          (int)((uint32_t)(hi_ ? k_ - (ld).k_split : k_) * (ld).b_kbytes), 0, 0);            \
+          hi_ ? (ld).rU : (ld).rG, (lds_void_t*)((sb) + blk_ * 512), 16,                    \
+          (ld).b_off[i] + (uint32_t)(hi_ ? k_ - (ld).k_split : k_) * (ld).b_kbytes, 0, 0,    \
+          0);                                                                               \
     } else {                                                                                \
       const bool up_ = (GATEUP) && blk_ * 64 >= C::BN * C::KCH;                             \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(up_ ? (ld).rU : (ld).rG,                     \
@@ -109,12 +113,24 @@ struct DmaLoads {
 // Issue all LPS global -> LDS loads (A loads first, then B) of k-step kt into
 // one stage's buffers.  (A macro: the host pass of hipcc rejects this body as
 // a device function template called from the k-loop.)
-#define MOE_DMA_ISSUE(C, GATEUP, BTR, ld, sa, sb, kt)                                        \
+// One wave load of the A tile: k-contiguous (ATR false) or k-major (BK rows
+// of BM columns, the k advance in the lane offset as for B).
+#define MOE_DMA_A(C, ATR, ld, sa, kt, i)                                                     \
+  do {                                                                                      \
+    if constexpr (ATR)                                                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                             \
+          (ld).rA, (lds_void_t*)((sa) + ((ld).wave + C::NW * (i)) * 512), 16,               \
+          (ld).a_off[i] + (uint32_t)((kt) * C::BK) * (ld).a_kbytes, 0, 0, 0);                \
+    else                                                                                    \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                             \
+          (ld).rA, (lds_void_t*)((sa) + ((ld).wave + C::NW * (i)) * 512), 16,               \
+          (ld).a_off[i], (kt) * C::BK * 2, 0, 0);                                           \
+  } while (0)
+
+#define MOE_DMA_ISSUE(C, GATEUP, ATR, BTR, ld, sa, sb, kt)                                   \
   do {                                                                                      \
     _Pragma("unroll") for (int i_ = 0; i_ < C::A_LD; ++i_)                                  \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                           \
-            (ld).rA, (lds_void_t*)((sa) + ((ld).wave + C::NW * i_) * 512), 16,              \
-            (ld).a_off[i_], (kt) * C::BK * 2, 0, 0);                                        \
+        MOE_DMA_A(C, ATR, ld, sa, kt, i_);                                                  \
     _Pragma("unroll") for (int i_ = 0; i_ < C::B_LD; ++i_)                                  \
         MOE_DMA_B(C, GATEUP, BTR, ld, sb, kt, i_);                                          \
   } while (0)
@@ -149,7 +165,29 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 #define MOE_DEFER 1
 #endif
 
-template <class C, bool GATEUP, bool PARTIAL, bool BTR>
+// Two ds_read_b64_tr_b16 give one MFMA operand fragment (8 consecutive k of
+// one column) from a k-major tile whose rows hold `cols` bf16 with 16-byte
+// chunk c of row k at c ^ 4*(k%4): in each group of 16 lanes, lane 4j+q
+// points at row k0+j, columns n0+4q..n0+4q+3, and lane i receives rows
+// k0..k0+3 of column n0+i, the first or second half of its 8 k values.
+template <int COLS>
+__device__ __forceinline__ bf16x8 tr_fragment(const uint16_t* tile, int kk, int col0, int lr,
+                                              int lk) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const int j = (lr >> 2) & 3, q = lr & 3;
+  const int row = kk * 16 + 8 * lk + j;  // + 4 for the second read
+  const int col = col0 + 16 * ((lr >> 4) & 1) + 4 * q;
+  const int byte = row * (COLS * 2) + (((col >> 3) ^ (4 * j)) << 4) + ((q & 1) << 3);
+  const char* base = reinterpret_cast<const char*>(tile);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + byte));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + byte + 4 * COLS * 2));
+  const v8s v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <class C, bool GATEUP, bool PARTIAL, bool BTR, bool ATR = false>
 __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* sb, int wm,
                                             int wn, int lr, int lk,
                                             f32x16 (&acc)[C::NB][C::MI][C::NI],
@@ -167,35 +205,22 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
       if (PARTIAL && mi >= mi_n) continue;
-      const int r = wm * C::WM + mi * 32 + lr;
-      af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + r * BK + (ch ^ swz_k<KCH>(r)) * 8);
+      if constexpr (ATR) {
+        af[buf][mi] = tr_fragment<C::WM * (C::NW / C::WGN)>(sa, kk, wm * C::WM + mi * 32,
+                                                                 lr, lk);
+      } else {
+        const int r = wm * C::WM + mi * 32 + lr;
+        af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + r * BK + (ch ^ swz_k<KCH>(r)) * 8);
+      }
     }
     if (PARTIAL && mi_n == 0) return;
     if constexpr (BTR) {
-      // k-major tile, rows of BNB columns with 16-byte chunk c of row k at
-      // c ^ 4*(k%4).  Two ds_read_b64_tr_b16 per fragment: in each group of
-      // 16 lanes, lane 4j+q points at row k0+j, columns n0+4q..n0+4q+3, and
-      // lane i receives rows k0..k0+3 of column n0+i, the first or second
-      // half of its 8 k values.
-      const int j = (lr >> 2) & 3, q = lr & 3;
-      const int row = kk * 16 + 8 * lk + j;  // + 4 for the second read
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) {
-          const int col = nb * C::BN + wn * C::WN + ni * 32 + 16 * ((lr >> 4) & 1) + 4 * q;
-          const int byte = row * (C::NB * C::BN * 2) + ((((col >> 3) ^ (4 * j))) << 4) +
-                           ((q & 1) << 3);
-          typedef short v4s __attribute__((ext_vector_type(4)));
-          typedef short v8s __attribute__((ext_vector_type(8)));
-          typedef __attribute__((address_space(3))) v4s lds_v4s;
-          const char* base = reinterpret_cast<const char*>(sb);
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + byte));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4s*)(base + byte + 4 * C::NB * C::BN * 2));
-          const v8s v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          bfr[buf][nb][ni] = __builtin_bit_cast(bf16x8, v);
-        }
+        for (int ni = 0; ni < C::NI; ++ni)
+          bfr[buf][nb][ni] =
+              tr_fragment<C::NB * C::BN>(sb, kk, nb * C::BN + wn * C::WN + ni * 32, lr, lk);
     } else {
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
@@ -214,13 +239,10 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
     constexpr int LPS = C::LPS;
     const int i1 = (kk + 1) * NLD < LPS ? (kk + 1) * NLD : LPS;
     {  // loads [kk*NLD, i1) of k-step kt_next (A loads first, then B)
-      const int i0 = kk * NLD, soff = kt_next * BK * 2;
+      const int i0 = kk * NLD;
 #pragma unroll
       for (int i = 0; i < C::A_LD; ++i)
-        if (i >= i0 && i < i1)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              ld.rA, (lds_void_t*)(na + (ld.wave + C::NW * i) * 512), 16, ld.a_off[i], soff, 0,
-              0);
+        if (i >= i0 && i < i1) MOE_DMA_A(C, ATR, ld, na, kt_next, i);
 #pragma unroll
       for (int i = 0; i < C::B_LD; ++i) {
         if (C::A_LD + i < i0 || C::A_LD + i >= i1) continue;
@@ -249,7 +271,7 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
 // scoped no-alias information, so the compiler's own wait before a fragment
 // read covers only the load into that same buffer (issued S-1 stages earlier)
 // instead of every load in flight.
-template <class C, bool GATEUP, bool PARTIAL, bool BTR = false>
+template <class C, bool GATEUP, bool PARTIAL, bool BTR = false, bool ATR = false>
 __device__ __forceinline__ void dma_mainloop(
     const DmaLoads<C, GATEUP>& ld, int nk, int mi_n, int wm, int wn, int lr, int lk,
     f32x16 (&acc)[C::NB][C::MI][C::NI], uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
@@ -266,9 +288,9 @@ __device__ __forceinline__ void dma_mainloop(
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni) bfr[1][nb][ni] = bf16x8{};
   // Prologue: stages 0 .. S-2 in flight.
-  MOE_DMA_ISSUE(C, GATEUP, BTR, ld, a0, b0, 0);
-  if (S > 2) MOE_DMA_ISSUE(C, GATEUP, BTR, ld, a1, b1, min(1, nk - 1));
-  if (S > 3) MOE_DMA_ISSUE(C, GATEUP, BTR, ld, a2, b2, min(2, nk - 1));
+  MOE_DMA_ISSUE(C, GATEUP, ATR, BTR, ld, a0, b0, 0);
+  if (S > 2) MOE_DMA_ISSUE(C, GATEUP, ATR, BTR, ld, a1, b1, min(1, nk - 1));
+  if (S > 3) MOE_DMA_ISSUE(C, GATEUP, ATR, BTR, ld, a2, b2, min(2, nk - 1));
 
   // Every step issues one stage of loads, so exactly S-2 stages are in flight
   // behind the one being waited for.  Past the end the loads repeat the last
@@ -283,11 +305,12 @@ __device__ __forceinline__ void dma_mainloop(
     wait_vmcnt<(S - 2) * C::LPS>();                                                         \
     stage_barrier();                                                                        \
     if (kt < nk)                                                                            \
-      dma_compute<C, GATEUP, PARTIAL, BTR>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc, ld, \
+      dma_compute<C, GATEUP, PARTIAL, BTR, ATR>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc, \
+                                                ld,                                         \
                                       MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),   \
                                       min(kt + S - 1, nk - 1), mi_n, af, bfr);              \
     else                                                                                    \
-      MOE_DMA_ISSUE(C, GATEUP, BTR, ld, MOE_SA((SI + S - 1) % S),                          \
+      MOE_DMA_ISSUE(C, GATEUP, ATR, BTR, ld, MOE_SA((SI + S - 1) % S),                     \
                     MOE_SB((SI + S - 1) % S), nk - 1);                                      \
   }
   for (int kb = 0; kb < nk; kb += S) {

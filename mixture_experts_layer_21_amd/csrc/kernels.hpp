@@ -132,10 +132,15 @@ struct BwdGemmParams {
   const uint16_t* B;
   const uint16_t* B2;
   long long ldb, b_gstride;
-  // b_kmajor (MROWS/DENSE, EPI_F32): B is stored k-major instead, row k of
-  // group g at B + g*b_gstride + k*ldb holding the N columns; rows k >= k_split
-  // are row k - k_split of B2 (k_split a multiple of 64; INT_MAX: no B2).
-  int b_kmajor, k_split;
+  // b_kmajor (EPI_F32): B is stored k-major instead, row k of group g at
+  // B + g*b_gstride + k*ldb holding the N columns (KRAGGED: row krows[g] + k
+  // of B); rows k >= k_split are row k - k_split of B2 (k_split a multiple of
+  // 64; INT_MAX: no B2).  a_kmajor (EPI_F32, DENSE or KRAGGED): A likewise,
+  // row k at A + k*lda (KRAGGED: row krows[g] + k) holding the M columns.
+  // A k-major operand reads zeros past its rows: past krows[g+1] (KRAGGED)
+  // or past a_bytes / b_bytes.
+  int b_kmajor, k_split, a_kmajor;
+  const int32_t* krows;      // KRAGGED with a k-major operand: [G+1] row offsets
   // EPI_F32: C row m of group g (KRAGGED) / row r (MROWS, DENSE) at
   // C + g*c_gstride + m*ldc; rows m >= c_split go to C2 + g*c_gstride + (m-c_split)*ldc.
   // With Cb (bf16) instead of C the rows are rounded once into Cb (no split).

@@ -157,8 +157,8 @@ Layout layout_of(const moe_config* c) {
 // Backward workspace: the forward layout (route and permutation scratch),
 // then the backward's own buffers.
 struct BwdLayout {
-  size_t logits, padoff, wrT, act, p1, p2, dact, dgu, dw, dh, dz, dxr, dFT, XT, AT,
-      DGUT, dhT, xT, sact, sp1, sp2, sdact, sdgu, sdz, doutT, sAT, sDGUT, sgv, sdw, sgp, ninv,
+  size_t logits, padoff, wrT, act, p1, p2, dact, dgu, dw, dh, dz, dxr, dFT, XT, sact, sp1,
+      sp2, sdact, sdgu, sdz, doutT, sgv, sdw, sgp, ninv,
       ndwp, total;
   int Epad, Tpad, Kpad;
 };
@@ -192,10 +192,6 @@ BwdLayout bwd_layout_of(const moe_config* c) {
   B.dxr = take(T * D * 4);
   B.dFT = take(D * Kp * 2);
   B.XT = take(D * Kp * 2);
-  B.AT = take(H * Kp * 2);
-  B.DGUT = take(2 * H * Kp * 2);
-  B.dhT = take(Ep * Tp * 2);
-  B.xT = take(D * Tp * 2);
   if (Hs) {
     B.sact = take(T * Hs * 2);
     B.sp1 = take(T * Hs * 2);
@@ -204,8 +200,6 @@ BwdLayout bwd_layout_of(const moe_config* c) {
     B.sdgu = take(T * 2 * Hs * 2);
     B.sdz = take(T * D * 4);
     B.doutT = take(D * Tp * 2);
-    B.sAT = take(Hs * Tp * 2);
-    B.sDGUT = take(2 * Hs * Tp * 2);
     // the shared expert's gate: g per token, <dout, S> per token, dL/dw_sg partials
     B.sgv = take(T * 4);
     B.sdw = take(T * 4);
@@ -1082,19 +1076,13 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
                      "rmsnorm backward kernel"));
   }
 
-  // 8. weight gradients: operands transposed, each expert's rows padded to 64
+  // 8. weight gradients.  Row-major per-row operands (act, [dg du], dh, x)
+  // are read k-major as they are; the gathered ones (w * dout rows, x rows
+  // of the kept slots) are transposed with each expert's rows padded to 64.
   MOE_TRY(transpose(R, D, dout, false, D, 0, B.Kpad, u16(B.dFT), B.Kpad, 0, 0, 1, r2a, gate_w,
                     r2a, true));
   MOE_TRY(transpose(R, D, x, false, D, 0, B.Kpad, u16(B.XT), B.Kpad, 0, 0, 1, r2a, nullptr,
                     nullptr, true));
-  MOE_TRY(transpose(R, H, act_p, false, H, 0, B.Kpad, u16(B.AT), B.Kpad, 0, 0, 1, nullptr,
-                    nullptr, nullptr, true));
-  MOE_TRY(transpose(R, 2 * H, u16(B.dgu), false, 2 * H, 0, B.Kpad, u16(B.DGUT), B.Kpad, 0, 0, 1,
-                    nullptr, nullptr, nullptr, true));
-  MOE_TRY(transpose(T, B.Epad, u16(B.dh), false, B.Epad, 0, B.Tpad, u16(B.dhT), B.Tpad, 0, 0, 1,
-                    nullptr, nullptr, nullptr, false));
-  MOE_TRY(transpose(T, D, x, false, D, 0, B.Tpad, u16(B.xT), B.Tpad, 0, 0, 1, nullptr, nullptr,
-                    nullptr, false));
   {
     moe::BwdGemmParams g{};
     g.grouping = moe::BWD_KRAGGED;
@@ -1105,14 +1093,17 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     g.offsets = padoff;
     g.A = u16(B.dFT);
     g.lda = B.Kpad;
-    g.B = u16(B.AT);
-    g.ldb = B.Kpad;
+    g.B = act_p;  // [rows, H]: k-major, the expert's rows from krows
+    g.b_kmajor = 1;
+    g.k_split = kNoSplit;
+    g.krows = offsets;
+    g.ldb = H;
     g.C = dw_down;
     g.ldc = H;
     g.c_gstride = (long long)D * H;
     g.c_split = kNoSplit;
     g.a_bytes = 2ll * D * B.Kpad;
-    g.b_bytes = 2ll * H * B.Kpad;
+    g.b_bytes = 2ll * R * H;
     MOE_TRY(gemm(g, "down wgrad"));
     moe::BwdGemmParams u{};
     u.grouping = moe::BWD_KRAGGED;
@@ -1121,8 +1112,10 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     u.N = D;
     u.G = E;
     u.offsets = padoff;
-    u.A = u16(B.DGUT);
-    u.lda = B.Kpad;
+    u.A = u16(B.dgu);  // [rows, 2H]: k-major
+    u.a_kmajor = 1;
+    u.krows = offsets;
+    u.lda = 2 * H;
     u.B = u16(B.XT);
     u.ldb = B.Kpad;
     u.C = dw_gate;
@@ -1130,7 +1123,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     u.ldc = D;
     u.c_gstride = (long long)H * D;
     u.c_split = H;
-    u.a_bytes = 2ll * 2 * H * B.Kpad;
+    u.a_bytes = 2ll * R * 2 * H;
     u.b_bytes = 2ll * D * B.Kpad;
     MOE_TRY(gemm(u, "gate/up wgrad"));
     moe::BwdGemmParams r{};
@@ -1140,24 +1133,23 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     r.N = D;
     r.K = B.Tpad;
     r.G = 1;
-    r.A = u16(B.dhT);
-    r.lda = B.Tpad;
-    r.B = u16(B.xT);
-    r.ldb = B.Tpad;
+    r.A = u16(B.dh);  // [T, Epad] and x [T, D]: both k-major, rows past T zero
+    r.a_kmajor = 1;
+    r.lda = B.Epad;
+    r.B = static_cast<const uint16_t*>(x);
+    r.b_kmajor = 1;
+    r.k_split = kNoSplit;
+    r.ldb = D;
     r.C = dw_router;
     r.ldc = D;
     r.c_split = kNoSplit;
-    r.a_bytes = 2ll * B.Epad * B.Tpad;
-    r.b_bytes = 2ll * D * B.Tpad;
+    r.a_bytes = 2ll * T * B.Epad;
+    r.b_bytes = 2ll * T * D;
     MOE_TRY(gemm(r, "router wgrad"));
   }
   if (sh) {
     MOE_TRY(transpose(T, D, dout, false, D, 0, B.Tpad, u16(B.doutT), B.Tpad, 0, 0, 1, nullptr,
                       sgate ? f32(B.sgv) : nullptr, nullptr, false));
-    MOE_TRY(transpose(T, Hs, sact_p, false, Hs, 0, B.Tpad, u16(B.sAT), B.Tpad, 0, 0, 1,
-                      nullptr, nullptr, nullptr, false));
-    MOE_TRY(transpose(T, 2 * Hs, u16(B.sdgu), false, 2 * Hs, 0, B.Tpad, u16(B.sDGUT), B.Tpad, 0,
-                      0, 1, nullptr, nullptr, nullptr, false));
     moe::BwdGemmParams g{};
     g.grouping = moe::BWD_DENSE;
     g.epilogue = moe::BWD_EPI_F32;
@@ -1167,13 +1159,15 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     g.G = 1;
     g.A = u16(B.doutT);
     g.lda = B.Tpad;
-    g.B = u16(B.sAT);
-    g.ldb = B.Tpad;
+    g.B = sact_p;  // [T, Hs]: k-major
+    g.b_kmajor = 1;
+    g.k_split = kNoSplit;
+    g.ldb = Hs;
     g.C = dws_down;
     g.ldc = Hs;
     g.c_split = kNoSplit;
     g.a_bytes = 2ll * D * B.Tpad;
-    g.b_bytes = 2ll * Hs * B.Tpad;
+    g.b_bytes = 2ll * T * Hs;
     MOE_TRY(gemm(g, "shared down wgrad"));
     moe::BwdGemmParams u{};
     u.grouping = moe::BWD_DENSE;
@@ -1182,16 +1176,19 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
     u.N = D;
     u.K = B.Tpad;
     u.G = 1;
-    u.A = u16(B.sDGUT);
-    u.lda = B.Tpad;
-    u.B = u16(B.xT);
-    u.ldb = B.Tpad;
+    u.A = u16(B.sdgu);  // [T, 2Hs] and x [T, D]: both k-major
+    u.a_kmajor = 1;
+    u.lda = 2 * Hs;
+    u.B = static_cast<const uint16_t*>(x);
+    u.b_kmajor = 1;
+    u.k_split = kNoSplit;
+    u.ldb = D;
     u.C = dws_gate;
     u.C2 = dws_up;
     u.ldc = D;
     u.c_split = Hs;
-    u.a_bytes = 2ll * 2 * Hs * B.Tpad;
-    u.b_bytes = 2ll * D * B.Tpad;
+    u.a_bytes = 2ll * T * 2 * Hs;
+    u.b_bytes = 2ll * T * D;
     MOE_TRY(gemm(u, "shared gate/up wgrad"));
     if (d_shared_gate)
       MOE_TRY(hip_ok(moe::launch_gate_dw(T, D, static_cast<const uint16_t*>(x), f32(B.sgv),
