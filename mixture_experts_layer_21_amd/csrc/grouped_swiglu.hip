@@ -480,12 +480,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmPar
 template <class C, bool GATEUP>
 __device__ __forceinline__ void dma_epilogue(const GemmParams& p, int m0, int m_end, int n0,
                                              int wm, int wn, int lr, int lk,
-                                             const f32x16 (&acc)[C::NB][C::MI][C::NI],
-                                             int mi_sel = -1) {
+                                             const f32x16 (&acc)[C::NB][C::MI][C::NI]) {
   const int N = GATEUP ? p.hidden : p.D;
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {
-    if (mi_sel >= 0 && mi != mi_sel) continue;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int grow = m0 + wm * C::WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
@@ -540,48 +538,66 @@ __device__ __forceinline__ void dma_store_partial(float* slot, int tid,
         }
 }
 
-// One block per (XCD, tail tile, wave row, 32-row block): the block stands in
-// for the WGN waves of one wave row of the GEMM block, adds their partials of
-// that row block in piece order and runs the epilogue on those rows.  Runs
-// after the GEMM kernel on the same stream.
+// Sum of a split tail tile's pieces and its epilogue.  Each XCD's blocks
+// (block b runs on XCD b % 8, whose L2 holds the partials) stride over that
+// XCD's tail tiles x the f32x4 accumulator vectors of the GEMM block: a
+// thread loads one vector of every piece (both halves for gate/up) before
+// adding them in piece order, and writes the 4 rows x 1 column they hold.
 template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
-__global__ __launch_bounds__(64 * (NWV / WGM)) void gemm_tail_reduce_kernel(GemmParams p) {
+__global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmParams p) {
   using C = DmaCfg<BM, BNB, BK, S, WGM, NWV, GATEUP>;
-  constexpr int PER_TILE = WGM * C::MI;
-  // Block b runs on XCD b % 8, the XCD whose L2 holds the partials.
-  const int xcd = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
-  const int j = rest / PER_TILE, sub = rest % PER_TILE;
-  const int wm = sub / C::MI, mi = sub % C::MI;
+  constexpr int VPT = C::MI * C::NI * 4;  // f32x4 vectors of one GEMM thread per NB part
+  constexpr int PER_TILE = VPT * C::NT;
+  constexpr size_t SLOT = kTailSlotBytes / 4;
+  const int xcd = blockIdx.x % kXcds, bx = blockIdx.x / kXcds, nbx = gridDim.x / kXcds;
   const int r = p.tail_meta[2 * xcd], ns = p.tail_meta[2 * xcd + 1];
-  if (j >= r) return;
-  const int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + j) * 4;
-  const int m0 = d[1], m_end = d[2], nt = d[3];
-  if (m0 + wm * C::WM + mi * 32 >= m_end) return;  // no valid row in this block
-  const int t = threadIdx.x, lane = t & 63, wn = t >> 6;
-  const int tid = wm * C::WGN * 64 + t;             // thread of the GEMM block
-  f32x16 acc[C::NB][C::MI][C::NI];
-  for (int pc = 0; pc < ns; ++pc) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(
-        p.tail_part + (size_t)(xcd * kTailSlots + j * ns + pc) * (kTailSlotBytes / 4));
+  const int N = GATEUP ? p.hidden : p.D;
+  for (int idx = bx * 256 + threadIdx.x; idx < r * PER_TILE; idx += nbx * 256) {
+    const int j = idx / PER_TILE, w = idx % PER_TILE;
+    const int vv = w / C::NT, tid = w % C::NT;
+    const int mi = vv / (C::NI * 4), ni = (vv / 4) % C::NI, q = vv % 4;
+    const int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + j) * 4;
+    const int m0 = d[1], m_end = d[2], nt = d[3];
+    const int lane = tid & 63, wv = tid >> 6, wm = wv / C::WGN, wn = wv % C::WGN;
+    // accumulator element 4q+u of (mi, ni): row 8q + 4*(lane/32) + u of the
+    // 32-row block, column lane % 32 (as in dma_store_partial's order)
+    const int row0 = m0 + wm * C::WM + mi * 32 + 8 * q + 4 * (lane >> 5);
+    const int col = nt * C::BN + wn * C::WN + ni * 32 + (lane & 31);
+    if (row0 >= m_end || col >= N) continue;
+    const float* base = p.tail_part + (size_t)(xcd * kTailSlots + j * ns) * SLOT;
+    f32x4 x[C::NB][16];
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+    for (int nb = 0; nb < C::NB; ++nb) {
+      const int v = ((nb * C::MI + mi) * C::NI + ni) * 4 + q;
 #pragma unroll
-      for (int ni = 0; ni < C::NI; ++ni)
+      for (int pc = 0; pc < 16; ++pc)
+        if (pc < ns)
+          x[nb][pc] = reinterpret_cast<const f32x4*>(base + pc * SLOT)[v * C::NT + tid];
+    }
+    f32x4 sum[C::NB];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int v = ((nb * C::MI + mi) * C::NI + ni) * 4 + q;
-          const f32x4 x = src[v * C::NT + tid];
+    for (int nb = 0; nb < C::NB; ++nb) {
+      sum[nb] = x[nb][0];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            // mi is uniform but not constant: select the accumulator by value
+      for (int pc = 1; pc < 16; ++pc)
+        if (pc < ns) sum[nb] += x[nb][pc];
+    }
 #pragma unroll
-            for (int m = 0; m < C::MI; ++m)
-              if (m == mi)
-                acc[nb][m][ni][4 * q + u] = pc == 0 ? x[u] : acc[nb][m][ni][4 * q + u] + x[u];
-          }
-        }
+    for (int u = 0; u < 4; ++u) {
+      const int row = row0 + u;
+      if (row >= m_end) break;
+      const size_t o = (size_t)row * N + col;
+      if constexpr (GATEUP) {
+        const float g = sum[0][u], up = sum[C::NB - 1][u];
+        static_cast<uint16_t*>(p.hbuf)[o] = f32_to_bf16_bits(swiglu_act(g, up, p.swiglu_limit));
+        if (p.save_p1) save_factors(p, o, g, up);
+      } else {
+        float gw = 1.f;
+        if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[row]];
+        static_cast<uint16_t*>(p.y)[o] = f32_to_bf16_bits(gw * sum[0][u]);
+      }
+    }
   }
-  dma_epilogue<C, GATEUP>(p, m0, m_end, nt * C::BN, wm, wn, lane & 31, lane >> 5, acc, mi);
 }
 
 template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
@@ -849,7 +865,7 @@ hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || slots == 0) return err;
   hipLaunchKernelGGL((gemm_tail_reduce_kernel<BM, BNB, BK, S, WGM, NWV, GATEUP>),
-                     dim3(kXcds * kTailSlots * WGM * C::MI), dim3(64 * C::WGN), 0, s, p);
+                     dim3(kXcds * 64), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
