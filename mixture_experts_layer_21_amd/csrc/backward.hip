@@ -413,10 +413,18 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
   const int nk = (t.k1 - t.k0) / BK;
   // (Device pass only: the host pass of hipcc rejects this call's template
   // deduction; kernel bodies are never run on the host.)
+  // Waves whose 32-row blocks lie past the tile's rows (the last row tile of
+  // an expert) skip those blocks' fragment reads and MFMAs.
+  const int mi_n = min(MI, max(0, (t.m_end - t.m0 - wm * C::WM + 31) / 32));
 #if defined(__HIP_DEVICE_COMPILE__)
-  if (nk > 0)
-    dma::dma_mainloop<C, PAIRED, false, BTR, ATR>(ld, nk, MI, wm, wn, lr, lk, acc, sA0, sA1, sX,
-                                                  sX, sB0, sB1, sX, sX);
+  if (nk > 0) {
+    if (mi_n == MI)
+      dma::dma_mainloop<C, PAIRED, false, BTR, ATR>(ld, nk, MI, wm, wn, lr, lk, acc, sA0, sA1, sX,
+                                                    sX, sB0, sB1, sX, sX);
+    else
+      dma::dma_mainloop<C, PAIRED, true, BTR, ATR>(ld, nk, mi_n, wm, wn, lr, lk, acc, sA0, sA1,
+                                                   sX, sX, sB0, sB1, sX, sX);
+  }
 #endif
 
   // Epilogue: element i of accumulator (nb, mi, ni) of lane l is row
