@@ -90,13 +90,13 @@ __device__ bool bwd_tile(const BwdGemmParams& p, int bn, BTile& t, int* s_scan) 
   if (tid < p.G) cnt = (p.offsets[tid + 1] - p.offsets[tid] + BM - 1) / BM;
   if (tid < BT) s_scan[tid] = cnt;
   __syncthreads();
-  for (int d = 1; d < BT; d <<= 1) {
+  for (int d = 1; d < p.G; d <<= 1) {  // prefixes of the groups only
     const int v = (tid < BT && tid >= d) ? s_scan[tid - d] : 0;
     __syncthreads();
     if (tid < BT) s_scan[tid] += v;
     __syncthreads();
   }
-  const int total = s_scan[BT - 1];
+  const int total = s_scan[p.G - 1];
   const int mt_bound = (p.max_rows + BM - 1) / BM + p.G;
   const int ml = b % mt_bound;
   t.nt = b / mt_bound;

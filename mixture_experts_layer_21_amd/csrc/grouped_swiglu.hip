@@ -91,13 +91,13 @@ __device__ bool find_tile(const GemmParams& p, int max_mtiles, Tile& t, int* s_s
   }
   s_scan[tid] = cnt;
   __syncthreads();
-  for (int d = 1; d < NTHREADS; d <<= 1) {
+  for (int d = 1; d < p.n_groups; d <<= 1) {  // prefixes of the groups only
     const int v = tid >= d ? s_scan[tid - d] : 0;
     __syncthreads();
     s_scan[tid] += v;
     __syncthreads();
   }
-  const int total = s_scan[NTHREADS - 1];
+  const int total = s_scan[p.n_groups - 1];
   if (ml >= total) return false;  // uniform across the block
   if (tid < p.n_groups) {
     const int hi = s_scan[tid], lo = hi - cnt;
@@ -150,13 +150,13 @@ __device__ bool decode_job(const GemmParams& p, int tail_slots, int* s_scan, Til
       }
       if (tid < NTHREADS) s_scan[tid] = cnt;
       __syncthreads();
-      for (int d = 1; d < NTHREADS; d <<= 1) {
+      for (int d = 1; d < p.n_groups; d <<= 1) {  // prefixes of the groups only
         const int v = (tid < NTHREADS && tid >= d) ? s_scan[tid - d] : 0;
         __syncthreads();
         if (tid < NTHREADS) s_scan[tid] += v;
         __syncthreads();
       }
-      total = s_scan[NTHREADS - 1];
+      total = s_scan[p.n_groups - 1];
     }
     const int A = total * ntiles;
     const int b = blockIdx.x, xcd = b % kXcds, i = b / kXcds;
