@@ -253,6 +253,46 @@ def test_backward_with_saved_state(moe, name):
     _compare(g, ref, names, f"{name} with saved state")
 
 
+def test_backward_saved_state_clamp_gate_pre_norm(moe):
+    """Saved state with the SwiGLU clamp (the forward's epilogues then store
+    the clamped factors), the gated shared expert and the pre-norm together."""
+    w = W.SMALL["deepseek_small"]
+    limit, eps = 0.05, 1e-5
+    inp = W.make_inputs(w, "cpu", seed=45)
+    _with_shared_gate(46)(inp)
+    nw = torch.rand(w.D, generator=torch.Generator().manual_seed(47)) + 0.5
+    oi = P.oracle_inputs(inp)
+    pre = (nw.to(torch.float64).numpy(), float(np.float32(eps)), w.act_dtype)
+    r = P.oracle_route(w, dict(oi, x=P.oracle.rms_norm(oi["x"], *pre)))
+    d = {k: v.to("cuda") for k, v in inp.items()}
+    cfg = P.config_of(w, swiglu_limit=limit)
+    cfg.pre_norm, cfg.norm_eps = 1, eps
+    ids = torch.empty(w.T, w.top_k, dtype=torch.int32, device="cuda")
+    kw = dict(logit_bias=d.get("logit_bias"), ws_gate=d["ws_gate"], ws_up=d["ws_up"],
+              ws_down=d["ws_down"])
+    saved = moe.new_saved(cfg)
+    moe.moe_forward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                    select_bias=d.get("select_bias"), expert_ids=ids, saved=saved,
+                    norm_weight=nw.cuda(), shared_expert_gate=d["ws_sgate"], **kw)
+    torch.cuda.synchronize()
+    assert (ids.cpu().numpy() == r["ids"]).all()
+    dout = torch.randn(w.T, w.D, generator=torch.Generator().manual_seed(48)).to(
+        W.torch_dtype(w.act_dtype))
+    aux = (0.3, 0.2)
+    fw = dict(top_k=w.top_k, score=w.score, renormalize=w.renormalize,
+              route_scale=w.route_scale, n_groups=w.n_groups, topk_groups=w.topk_groups,
+              group_rule=w.group_rule, capacity_factor=w.capacity_factor, swiglu_limit=limit)
+    ref = P.oracle.backward(oi, dout.to(torch.float64).numpy(), aux_coef=aux, pre_norm=pre, **fw)
+    g = moe.moe_backward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                         torch.from_numpy(r["ids"].astype(np.int32)).cuda(),
+                         torch.from_numpy(r["weights"].astype(np.float32)).cuda(), dout.cuda(),
+                         balance_coef=aux[0], z_coef=aux[1], d_gate_w=True, saved=saved,
+                         norm_weight=nw.cuda(), shared_expert_gate=d["ws_sgate"], **kw)
+    torch.cuda.synchronize()
+    _compare(g, ref, GRADS + SHARED + ("d_gate_w", "d_shared_gate", "d_norm_weight"),
+             "saved state, clamp, gate, pre-norm")
+
+
 def test_backward_dropped_slots(moe):
     """Capacity drops: a dropped slot's dL/dw is exactly 0."""
     w = W.SMALL["switch_small"]
