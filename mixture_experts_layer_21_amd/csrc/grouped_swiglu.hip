@@ -480,7 +480,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmPar
 template <class C, bool GATEUP>
 __device__ __forceinline__ void dma_epilogue(const GemmParams& p, int m0, int m_end, int n0,
                                              int wm, int wn, int lr, int lk,
-                                             const f32x16 (&acc)[C::NB][C::MI][C::NI]) {
+                                             const f32x16 (&acc)[C::NB][C::MI][C::NI],
+                                             const float* row_gw) {
   const int N = GATEUP ? p.hidden : p.D;
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {
@@ -501,8 +502,7 @@ __device__ __forceinline__ void dma_epilogue(const GemmParams& p, int m0, int m_
           }
         }
       } else {
-        float gw = 1.f;
-        if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[grow]];
+        const float gw = row_gw[grow - m0];
         uint16_t* out = static_cast<uint16_t*>(p.y) + (size_t)grow * N;
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni) {
@@ -613,11 +613,23 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
   __shared__ __attribute__((aligned(1024))) uint16_t sB2[S > 2 ? BNB * BK : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t sB3[S > 3 ? BNB * BK : 8];
   __shared__ int s_scan[NTHREADS + 4];
+  __shared__ float s_gw[GATEUP ? 1 : BM];
 
   Tile tile;
   int piece, nsplit, tail_slot;
   if (!decode_job<BM, C::BN, GATEUP>(p, tail_slots, s_scan, tile, piece, nsplit, tail_slot))
     return;
+  if constexpr (!GATEUP) {
+    // The gate weight of each of the tile's rows for the epilogue, fetched
+    // once ahead of the k-loop rather than per row at the end.
+    if (threadIdx.x < BM) {
+      const int row = tile.m0 + (int)threadIdx.x;
+      s_gw[threadIdx.x] = (p.gate_w && p.row_to_assign && row < tile.m_end)
+                              ? p.gate_w[p.row_to_assign[row]]
+                              : 1.f;
+    }
+    __syncthreads();
+  }
 
   const int K = GATEUP ? p.D : p.hidden;
   const int N = GATEUP ? p.hidden : p.D;
@@ -710,7 +722,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
                                  acc);
     return;
   }
-  dma_epilogue<C, GATEUP>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc);
+  dma_epilogue<C, GATEUP>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc, s_gw);
 }
 
 // fp32 path: 64x64 tiles, 16x16 threads with 4x4 outputs each (rows ty+16i,
