@@ -519,6 +519,54 @@ __device__ __forceinline__ void dma_epilogue(const GemmParams& p, int m0, int m_
 template <class C>
 constexpr int partial_vectors() { return C::NB * C::MI * C::NI * 4; }
 
+// The same epilogue through LDS, for tiles of BM rows x BN output columns
+// whose bf16 result fits the four 32 KB stage buffers: each wave writes its
+// results as [row][column] bf16 (16-byte chunk c of row r at c ^ 4*((r/4)%4),
+// so the two rows one write touches use different banks), then every thread
+// stores whole 16-byte row chunks, full 128-byte lines per row.  The caller
+// has passed the k-loop; the first barrier makes the stage buffers free.
+template <class C, bool GATEUP>
+__device__ __forceinline__ void dma_epilogue_staged(
+    const GemmParams& p, int m0, int m_end, int n0, int wm, int wn, int lr, int lk,
+    const f32x16 (&acc)[C::NB][C::MI][C::NI], const float* row_gw, uint16_t* s0, uint16_t* s1,
+    uint16_t* s2, uint16_t* s3) {
+  constexpr int BM = C::WM * (C::NW / C::WGN), BN = C::BN;
+  constexpr int ROWS_PER = 16384 / BN;   // rows of one 32 KB buffer
+  constexpr int CPR = BN / 8;            // 16-byte chunks per row
+  static_assert(BM <= 4 * ROWS_PER && CPR >= 16, "staged epilogue shape");
+  auto at = [&](int r, int c) -> uint16_t* {  // chunk c of tile row r
+    const int b = r / ROWS_PER, rl = r % ROWS_PER;
+    uint16_t* base = b == 0 ? s0 : b == 1 ? s1 : b == 2 ? s2 : s3;
+    return base + rl * BN + ((c ^ (4 * ((r >> 2) & 3))) << 3);
+  };
+  const int N = GATEUP ? p.hidden : p.D;
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = wm * C::WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
+      const float gw = GATEUP ? 1.f : row_gw[r];
+#pragma unroll
+      for (int ni = 0; ni < C::NI; ++ni) {
+        const int col = wn * C::WN + ni * 32 + lr;
+        const float v = GATEUP
+            ? swiglu_act(acc[0][mi][ni][i], acc[C::NB - 1][mi][ni][i], p.swiglu_limit)
+            : gw * acc[0][mi][ni][i];
+        at(r, col >> 3)[col & 7] = f32_to_bf16_bits(v);
+      }
+    }
+  __syncthreads();
+  uint16_t* out = static_cast<uint16_t*>(GATEUP ? p.hbuf : p.y);
+  for (int q = threadIdx.x; q < BM * CPR; q += C::NT) {
+    const int r = q / CPR, c = q % CPR;
+    const int row = m0 + r, col = n0 + c * 8;
+    if (row >= m_end || col >= N) continue;
+    *reinterpret_cast<u32x4*>(out + (size_t)row * N + col) =
+        *reinterpret_cast<const u32x4*>(at(r, c));
+  }
+}
+
 template <class C, bool GATEUP>
 __device__ __forceinline__ void dma_store_partial(float* slot, int tid,
                                                   const f32x16 (&acc)[C::NB][C::MI][C::NI]) {
@@ -721,6 +769,13 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
     dma_store_partial<C, GATEUP>(p.tail_part + (size_t)tail_slot * (kTailSlotBytes / 4), tid,
                                  acc);
     return;
+  }
+  if constexpr (BM == 256 && BNB == 256 && BK == 64 && S == 2) {
+    if (!(GATEUP && p.save_p1)) {  // (saving the SwiGLU factors stores per element)
+      dma_epilogue_staged<C, GATEUP>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc, s_gw, sA0,
+                                     sA1, sB0, sB1);
+      return;
+    }
   }
   dma_epilogue<C, GATEUP>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc, s_gw);
 }
