@@ -459,6 +459,8 @@ def main():
     tokens_per_s = w.T / (elapsed / args.steps)
     stage_ms = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
                          for ev in events]).mean(axis=0)
+    # each timed step on the device clock (HIP events around the step)
+    step_dev = np.array([ev[0].elapsed_time(ev[4]) for ev in events])
     _log(f"[bench] {ms_per_step:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
     _log("[bench] stages ms: route %.4f permute %.4f grouped_swiglu %.4f combine %.4f"
          % tuple(stage_ms))
@@ -525,6 +527,9 @@ def main():
                    "capacity_factor": w.capacity_factor, "kept_rows": n_kept,
                    "parallelism": "none (1 GPU)"},
         "moe_forward_ms_per_step": round(fwd_ms, 4),
+        "step_ms_device": {"median": round(float(np.median(step_dev)), 4),
+                           "min": round(float(step_dev.min()), 4),
+                           "p90": round(float(np.percentile(step_dev, 90)), 4)},
         "stages_ms": {k: round(float(v), 4) for k, v in
                       zip(("route", "permute", "grouped_swiglu", "combine"), stage_ms)},
         "roofline": roofline,
