@@ -18,9 +18,12 @@ plus
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --pmc-summary FETCH_DB WRITE_DB --workload NAME
+       python bench.py --trace-summary KERNEL_TRACE_CSV --workload NAME [--steps K --warmup W]
 The second form turns two rocprofv3 counter databases (one FETCH_SIZE pass,
 one WRITE_SIZE pass, each of a run with --copy-calibration) into the traffic
-summary that the first form reads.
+summary that the first form reads; the third turns the kernel trace of a
+first-form run into per-kernel durations, with the mean over the dispatches of
+the timed steps beside the mean over all of them.
 """
 from __future__ import annotations
 
@@ -62,6 +65,9 @@ def _parse():
                     help="also time moe_backward (beside the forward step) and report it")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="summarise two rocprofv3 counter databases and exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="summarise a rocprofv3 kernel trace (CSV) of a run with the same "
+                         "--workload, --steps and --warmup, and exit")
     ap.add_argument("--mfma-summary", metavar="DB",
                     help="summarise a rocprofv3 database of SQ_VALU_MFMA_BUSY_CYCLES, "
                          "SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE and exit")
@@ -178,6 +184,64 @@ def _pmc_summary(fetch_db, write_db, workload):
             step += rd + wb
     lines += ["", "Grouped SwiGLU step (every gemm kernel above once per forward):", "",
               f"hbm_bytes_per_step: {step:.6g}", ""]
+    return "\n".join(lines)
+
+
+def _trace_summary(csv_path, workload, steps, warmup):
+    """Per-kernel durations from a rocprofv3 kernel trace of
+    `bench.py --workload W --steps K --warmup W0 --no-cpu-baseline`.  Each
+    warm-up round runs one staged step and one moe_forward, then the K timed
+    staged steps run, then K moe_forward calls; a kernel with p launches per
+    step therefore has 2*(W0+K)*p dispatches, and the timed steps' ones are
+    dispatches [2*W0*p, (2*W0+K)*p) in start order."""
+    import collections
+    import csv
+    import statistics
+    rows = list(csv.DictReader(open(csv_path)))
+    key = lambda *names: next(k for k in rows[0] if k in names)
+    kn, ks, ke = (key("Kernel_Name", "Name"), key("Start_Timestamp", "Start"),
+                  key("End_Timestamp", "End"))
+    per = collections.defaultdict(list)
+    for r in rows:
+        if "moe::" in r[kn]:
+            per[r[kn]].append((int(r[ks]), int(r[ke]) - int(r[ks])))
+    cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --kernel-include-regex "
+           f"'moe::' --output-format csv -d /tmp/kt_{workload} -o run -- python3 "
+           f"/root/repo/bench.py --workload {workload} --steps {steps} --warmup {warmup} "
+           f"--no-cpu-baseline")
+    lines = [f"# Kernel trace of the MoE forward: {workload}", "",
+             "Per-dispatch durations from a rocprofv3 kernel trace (the library's kernels",
+             f"only) of bench.py on one MI355X: {warmup} warm-up rounds (a staged step and a",
+             f"`moe_forward` each), {steps} timed staged steps, then {steps} `moe_forward`",
+             "calls, plus the route/permute calls of the set-up.  \"timed steps\" is the mean",
+             "per step over the dispatches of the timed staged steps (the region bench.py",
+             "times with HIP events), for kernels whose dispatch count is a whole number",
+             "of launches per step; \"all\" is the mean over every dispatch, warm-up included.",
+             "", "Commands:", "", "```", cmd,
+             f"python3 /root/repo/bench.py --trace-summary "
+             f"$(find /tmp/kt_{workload} -name run_kernel_trace.csv) "
+             f"--workload {workload} --steps {steps} --warmup {warmup}", "```", "",
+             "| kernel | dispatches | launches per step | timed steps, per step (us) | "
+             "all: mean (us) | median (us) | min (us) | max (us) |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    rounds = 2 * (warmup + steps)
+    step_sum = 0.0
+    for name in sorted(per):
+        d = sorted(per[name])
+        us = [x[1] / 1e3 for x in d]
+        p = len(d) // rounds if len(d) % rounds == 0 else 0
+        if p:
+            timed = sum(us[2 * warmup * p:(2 * warmup + steps) * p]) / steps
+            tcol = f"{timed:.1f}"
+            if "gemm" in name:
+                step_sum += timed
+        else:
+            tcol = "-"
+        lines.append(f"| `{_short(name)}` | {len(d)} | {p or '-'} | {tcol} | "
+                     f"{sum(us) / len(us):.1f} | {statistics.median(us):.1f} | "
+                     f"{min(us):.1f} | {max(us):.1f} |")
+    lines += ["", "Grouped SwiGLU step (every gemm kernel, timed steps): "
+              f"{step_sum:.1f} us per step.", ""]
     return "\n".join(lines)
 
 
@@ -367,6 +431,9 @@ def main():
         return
     if args.mfma_summary:
         print(_mfma_summary(args.mfma_summary, args.workload))
+        return
+    if args.trace_summary:
+        print(_trace_summary(args.trace_summary, args.workload, args.steps, args.warmup))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
