@@ -1,29 +1,37 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE-layer forward on one MI355X.
 
-Prints ONE JSON line: whole-layer forward throughput (tokens/s) on the
-Mixtral-shaped workload (T=4096, d_model=4096, 8 SwiGLU experts of
-d_hidden=14336, top-2 softmax, dropless, bf16), with inputs resident in HBM,
-plus
+Prints ONE JSON line.  By default all five workloads run in one process (the
+tiny fp32 layer, the Switch-style capacity layer, the Mixtral-shaped layer,
+the DeepSeek-V3-shaped layer and the decode-shaped layer); the headline
+fields (value, roofline, cpu_baseline, ...) are those of the Mixtral-shaped
+workload (T=4096, d_model=4096, 8 SwiGLU experts of d_hidden=14336, top-2
+softmax, dropless, bf16), the configuration the metric is quoted on, and
+``configs`` carries every workload's tokens/s, stages, rooflines and CPU
+baseline.  Inputs are resident in HBM when timing starts.
   * ``roofline``: the grouped SwiGLU step (gate/up GEMM + down GEMM, the
     dominant work) timed with HIP events on its stream.  Its bound is the
     one its algorithmic intensity selects: FLOP (6*D*H per kept row) per
-    algorithmic byte (the weights of every expert that keeps a row, the
-    gathered input rows and the output rows) against the ridge of the bf16
-    MFMA peak over the HBM peak.  ``traffic`` comes from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken on the current
-    kernel source, else null;
-  * ``cpu_baseline``: the float64 CPU oracle on a bounded sample of tokens of
-    the same workload, on this host's cores.
+    algorithmic byte (the weights of every expert that keeps a row, x read
+    once, the output written once) against the ridge of the bf16 MFMA peak
+    over the HBM peak.  ``traffic`` comes from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary when it was taken on the current kernel
+    source, else null;
+  * ``layer``: the whole step (route, permute, grouped SwiGLU, combine)
+    against both peaks (the router GEMM and weights added);
+  * ``cpu_baseline``: the float64 CPU oracle on the same workload (whole
+    layer, or a bounded sample of it), on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
        python bench.py --pmc-summary FETCH_DB WRITE_DB --workload NAME
+       python bench.py --mfma-summary DB --workload NAME
+       python bench.py --stall-summary DB --workload NAME
        python bench.py --trace-summary KERNEL_TRACE_CSV --workload NAME [--steps K --warmup W]
-The second form turns two rocprofv3 counter databases (one FETCH_SIZE pass,
-one WRITE_SIZE pass, each of a run with --copy-calibration) into the traffic
-summary that the first form reads; the third turns the kernel trace of a
-first-form run into per-kernel durations, with the mean over the dispatches of
-the timed steps beside the mean over all of them.
+The summary forms turn rocprofv3 counter databases of single-workload runs
+(the FETCH_SIZE and WRITE_SIZE passes with --copy-calibration; the MFMA pass;
+the wait/LDS pass) into the summaries under profiles/; the last turns the
+kernel trace of a single-workload run into per-kernel durations, with the
+mean over the dispatches of the timed steps beside the mean over all of them.
 """
 from __future__ import annotations
 
@@ -53,10 +61,12 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_8x_top2")
+    ap.add_argument("--workload", default="all",
+                    help="one workload, or 'all' (default): the five in one run, the "
+                         "headline fields from the Mixtral-shaped layer")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB read + 1 GiB write kernel (torch.neg on "
@@ -71,6 +81,9 @@ def _parse():
     ap.add_argument("--mfma-summary", metavar="DB",
                     help="summarise a rocprofv3 database of SQ_VALU_MFMA_BUSY_CYCLES, "
                          "SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE and exit")
+    ap.add_argument("--stall-summary", metavar="DB",
+                    help="summarise a rocprofv3 database of SQ_WAIT_ANY, SQ_WAVE_CYCLES, "
+                         "SQ_LDS_BANK_CONFLICT, SQ_INSTS_LDS and GRBM_GUI_ACTIVE and exit")
     return ap.parse_args()
 
 
@@ -116,26 +129,38 @@ def _copy_calibration(dev):
     del src, dst
 
 
-def _pmc_means(db):
-    """Mean counter value per dispatch for each kernel of one rocprofv3 DB."""
+# Steps of the counter runs: each warm-up round and each timed round runs one
+# staged step and one moe_forward, so a grouped GEMM kernel with p launches
+# per step has 2 * (PMC_WARMUP + PMC_STEPS) * p dispatches.
+PMC_STEPS, PMC_WARMUP = 2, 1
+
+
+def _pmc_dispatches(db, grbm_max=False):
+    """Per kernel: the dispatches of one rocprofv3 DB in dispatch order, each
+    as (counter -> value summed over hardware instances, duration in ns);
+    with grbm_max the GRBM counters (one clock for the chip) take the largest
+    instance instead."""
     import collections
     import sqlite3
     con = sqlite3.connect(db)
     rows = con.execute("select name, dispatch_id, counter_name, counter_value, duration "
                        "from pmc_events").fetchall()
-    per = collections.defaultdict(float)
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
     dur = {}
     for name, did, cn, v, d in rows:
-        per[(name, did, cn)] += v     # summed over hardware instances
+        if grbm_max and cn.startswith("GRBM"):
+            per[(name, did)][cn] = max(per[(name, did)][cn], v)
+        else:
+            per[(name, did)][cn] += v
         dur[(name, did)] = d
-    out = collections.defaultdict(lambda: collections.defaultdict(list))
-    for (name, did, cn), v in per.items():
-        out[name][cn].append(v)
-        out[name].setdefault("_dur", []).append(dur[(name, did)])
-    res = {n: {c: sum(v) / len(v) for c, v in d.items()} for n, d in out.items()}
-    for n, d in out.items():
-        res[n]["_n"] = len(d["_dur"])
-    return res
+    out = collections.defaultdict(list)
+    for (name, did) in sorted(per, key=lambda k: k[1]):
+        out[name].append((dict(per[(name, did)]), dur[(name, did)]))
+    return out
+
+
+def _mean(vals):
+    return sum(vals) / len(vals) if vals else 0.0
 
 
 def _short(name):
@@ -144,46 +169,58 @@ def _short(name):
 
 
 def _pmc_summary(fetch_db, write_db, workload):
-    fetch, write = _pmc_means(fetch_db), _pmc_means(write_db)
+    fetch, write = _pmc_dispatches(fetch_db), _pmc_dispatches(write_db)
     calib = [n for n in fetch if "neg_kernel" in n]
     assert calib, "no calibration kernel in the FETCH_SIZE run (use --copy-calibration)"
     calib_w = [n for n in write if "neg_kernel" in n]
-    f_cal = fetch[calib[0]]["FETCH_SIZE"]
-    w_cal = write[calib_w[0]]["WRITE_SIZE"]
+    f_cal = _mean([c["FETCH_SIZE"] for c, _ in fetch[calib[0]]])
+    w_cal = _mean([c["WRITE_SIZE"] for c, _ in write[calib_w[0]]])
+    cal_us = _mean([d for _, d in fetch[calib[0]]]) / 1e3
     f_scale = CALIB_BYTES / f_cal
     w_scale = CALIB_BYTES / w_cal
+    rounds = 2 * (PMC_WARMUP + PMC_STEPS)
     lines = [f"# HBM traffic of the MoE kernels: {workload}", "",
              f"source_sha256_16: {_source_hash()}", "",
              "FETCH_SIZE and WRITE_SIZE (rocprofv3, one pass each) per dispatch, scaled by",
              "the readings of a plain torch.neg over 2^28 fp32 values (1 GiB read, 1 GiB",
              f"written): FETCH_SIZE {f_cal:.6g} -> {f_scale:.4f} B per unit, "
              f"WRITE_SIZE {w_cal:.6g} -> {w_scale:.4f} B per unit.  The calibration kernel "
-             f"itself moves 2 GiB in {fetch[calib[0]]['_dur'] / 1e3:.1f} us "
-             f"({2 * CALIB_BYTES / fetch[calib[0]]['_dur']:.0f} GB/s).", "",
+             f"itself moves 2 GiB in {cal_us:.1f} us ({2 * CALIB_BYTES / (cal_us * 1e3):.0f} GB/s).",
+             "",
+             "A grouped GEMM kernel that runs p times per step (the routed experts, then",
+             "the shared expert) has one row per launch: the i-th dispatch of every step",
+             "goes to row i.  The step's bytes add every launch of every gemm kernel.", "",
              "Commands (one MI355X; the counter passes, then this summary):", "", "```",
              "cd /tmp && export TMPDIR=/tmp",
              *(f"rocprofv3 --kernel-include-regex 'moe::|neg_kernel' --pmc {c} -d /tmp/t_{c} "
-               f"-o {workload} -- python3 /root/repo/bench.py --workload {workload} --steps 2 "
-               f"--warmup 1 --no-cpu-baseline --copy-calibration"
+               f"-o {workload} -- python3 /root/repo/bench.py --workload {workload} "
+               f"--steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline "
+               f"--copy-calibration"
                for c in ("FETCH_SIZE", "WRITE_SIZE")),
              f"python3 /root/repo/bench.py --pmc-summary /tmp/t_FETCH_SIZE/{workload}_results.db "
              f"/tmp/t_WRITE_SIZE/{workload}_results.db --workload {workload}",
              "```", "",
-             "| kernel | dispatches | avg duration (us) | read (MB) | written (MB) | GB/s |",
-             "|---|---:|---:|---:|---:|---:|"]
+             "| kernel | launch | dispatches | avg duration (us) | read (MB) | written (MB) "
+             "| GB/s |",
+             "|---|---|---:|---:|---:|---:|---:|"]
     step = 0.0
     for name in sorted(n for n in fetch if "moe::" in n):
-        f = fetch[name]
-        wr = write.get(name, {})
-        rd = f["FETCH_SIZE"] * f_scale
-        wb = wr.get("WRITE_SIZE", 0.0) * w_scale
-        us = f["_dur"] / 1e3
-        lines.append(f"| `{_short(name)}` | {f['_n']} | {us:.1f} | {rd / 1e6:.1f} | "
-                     f"{wb / 1e6:.1f} | {(rd + wb) / us / 1e3:.0f} |")
-        if "gemm" in name:
-            step += rd + wb
-    lines += ["", "Grouped SwiGLU step (every gemm kernel above once per forward):", "",
-              f"hbm_bytes_per_step: {step:.6g}", ""]
+        fd, wd = fetch[name], write.get(name, [])
+        n = len(fd)
+        p = n // rounds if ("gemm" in name and n % rounds == 0 and len(wd) == n) else 1
+        for i in range(p):
+            f_i = fd[i::p] if p > 1 else fd
+            w_i = wd[i::p] if p > 1 else wd
+            rd = _mean([c.get("FETCH_SIZE", 0.0) for c, _ in f_i]) * f_scale
+            wb = _mean([c.get("WRITE_SIZE", 0.0) for c, _ in w_i]) * w_scale
+            us = _mean([d for _, d in f_i]) / 1e3
+            launch = f"{i + 1} of {p}" if p > 1 else "all"
+            lines.append(f"| `{_short(name)}` | {launch} | {len(f_i)} | {us:.1f} | "
+                         f"{rd / 1e6:.1f} | {wb / 1e6:.1f} | {(rd + wb) / us / 1e3:.0f} |")
+            if "gemm" in name:
+                step += rd + wb
+    lines += ["", "Grouped SwiGLU step (every launch of every gemm kernel above, per step):",
+              "", f"hbm_bytes_per_step: {step:.6g}", ""]
     return "\n".join(lines)
 
 
@@ -325,132 +362,206 @@ def _time_backward(moe, w, cfg, inp, r, n_kept, steps, stream):
 SIMDS = 256 * 4  # MI355X: 256 compute units of four SIMDs
 
 
-def _mfma_summary(db, workload):
-    """Clock and MFMA utilisation per kernel from one rocprofv3 counter pass:
-    clock = GRBM_GUI_ACTIVE / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES
-    (summed over the SIMDs) / (SIMDS * GRBM_GUI_ACTIVE)."""
-    import collections
-    import sqlite3
-    con = sqlite3.connect(db)
-    rows = con.execute("select name, dispatch_id, counter_name, counter_value, duration "
-                       "from pmc_events").fetchall()
-    per = collections.defaultdict(lambda: collections.defaultdict(list))
-    dur = {}
-    for name, did, cn, v, d in rows:
-        per[(name, did)][cn].append(v)
-        dur[(name, did)] = d
-    agg = collections.defaultdict(lambda: collections.defaultdict(list))
-    for (name, did), cs in per.items():
-        if "moe::" not in name:
-            continue
-        for cn, vals in cs.items():  # GRBM: one clock for the chip; SQ: summed
-            agg[name][cn].append(max(vals) if cn.startswith("GRBM") else sum(vals))
-        agg[name]["_dur"].append(dur[(name, did)])
-    cmd = (f"rocprofv3 --kernel-include-regex 'moe::' --pmc SQ_VALU_MFMA_BUSY_CYCLES "
-           f"SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -d /tmp/t_mfma -o {workload} -- python3 "
-           f"/root/repo/bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline")
-    lines = [f"# Clock and MFMA utilisation of the MoE kernels: {workload}", "",
+def _launch_rows(disp):
+    """Dispatch lists of each kernel split per launch of a step (see
+    _pmc_summary): [(kernel, launch label, dispatches)]."""
+    rounds = 2 * (PMC_WARMUP + PMC_STEPS)
+    out = []
+    for name in sorted(n for n in disp if "moe::" in n):
+        d = disp[name]
+        p = len(d) // rounds if ("gemm" in name and len(d) % rounds == 0) else 1
+        for i in range(p):
+            out.append((name, f"{i + 1} of {p}" if p > 1 else "all", d[i::p] if p > 1 else d))
+    return out
+
+
+def _counter_table(db, workload, kind):
+    """Per kernel launch, from one rocprofv3 counter pass over
+    `bench.py --steps PMC_STEPS --warmup PMC_WARMUP`: clock = GRBM_GUI_ACTIVE
+    / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs)
+    / (SIMDS * GRBM_GUI_ACTIVE) (kind "mfma"); or the fraction of wave cycles
+    spent waiting (waitcnt and barrier), SQ_WAIT_ANY / SQ_WAVE_CYCLES, and
+    the LDS bank-conflict cycles per LDS instruction (kind "stall")."""
+    counters = {"mfma": "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+                "stall": "SQ_WAIT_ANY SQ_WAVE_CYCLES SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS "
+                         "GRBM_GUI_ACTIVE"}[kind]
+    disp = _pmc_dispatches(db, grbm_max=True)
+    cmd = (f"rocprofv3 --kernel-include-regex 'moe::' --pmc {counters} -d /tmp/t_{kind} "
+           f"-o {workload} -- python3 /root/repo/bench.py --workload {workload} "
+           f"--steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline")
+    title = {"mfma": "Clock and MFMA utilisation", "stall": "Wait and LDS-conflict cycles"}[kind]
+    lines = [f"# {title} of the MoE kernels: {workload}", "",
              f"source_sha256_16: {_source_hash()}", "",
-             "One rocprofv3 counter pass.  clock = GRBM_GUI_ACTIVE / duration;",
-             f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS} SIMDs x GRBM_GUI_ACTIVE),",
-             "the fraction of SIMD cycles in which the matrix core is busy.  At the",
-             "nominal 2.4 GHz a fully busy matrix core gives the 2.5 PFLOP/s bf16 peak.",
-             "Kernels under 100 us are listed without either figure: GRBM_GUI_ACTIVE",
-             "then counts more cycles than the kernel runs.", "",
-             "Commands (one MI355X):", "", "```", "cd /tmp && export TMPDIR=/tmp", cmd,
-             f"python3 /root/repo/bench.py --mfma-summary /tmp/t_mfma/{workload}_results.db "
-             f"--workload {workload}", "```", "",
-             "| kernel | dispatches | avg duration (us) | clock (GHz) | MFMA busy |",
-             "|---|---:|---:|---:|---:|"]
-    for name in sorted(agg):
-        d = agg[name]
-        us = sum(d["_dur"]) / len(d["_dur"]) / 1e3
-        g = sum(d.get("GRBM_GUI_ACTIVE", [0])) / max(len(d.get("GRBM_GUI_ACTIVE", [])), 1)
-        m = sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])) / max(
-            len(d.get("SQ_VALU_MFMA_BUSY_CYCLES", [])), 1)
+             "One rocprofv3 counter pass.  clock = GRBM_GUI_ACTIVE / duration."]
+    if kind == "mfma":
+        lines += [f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS} SIMDs x GRBM_GUI_ACTIVE),",
+                  "the fraction of SIMD cycles in which the matrix core is busy.  At the",
+                  "nominal 2.4 GHz a fully busy matrix core gives the 2.5 PFLOP/s bf16 peak."]
+        head = "| kernel | launch | dispatches | avg duration (us) | clock (GHz) | MFMA busy |"
+        sep = "|---|---|---:|---:|---:|---:|"
+    else:
+        lines += ["wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES: the share of the waves' cycles spent",
+                  "in s_waitcnt or at a barrier; LDS conflicts = SQ_LDS_BANK_CONFLICT cycles",
+                  "per LDS instruction (SQ_INSTS_LDS)."]
+        head = ("| kernel | launch | dispatches | avg duration (us) | clock (GHz) | wait | "
+                "LDS conflict cycles / LDS instruction |")
+        sep = "|---|---|---:|---:|---:|---:|---:|"
+    lines += ["Kernels under 100 us are listed without these figures: GRBM_GUI_ACTIVE",
+              "then counts more cycles than the kernel runs.  A grouped GEMM kernel that",
+              "runs p times per step (routed experts, then the shared expert) has one row",
+              "per launch.", "", "Commands (one MI355X):", "", "```",
+              "cd /tmp && export TMPDIR=/tmp", cmd,
+              f"python3 /root/repo/bench.py --{kind}-summary /tmp/t_{kind}/{workload}_results.db "
+              f"--workload {workload}", "```", "", head, sep]
+    for name, launch, d in _launch_rows(disp):
+        us = _mean([x[1] for x in d]) / 1e3
+        c = {k: _mean([x[0].get(k, 0.0) for x in d]) for k in counters.split()}
+        g = c["GRBM_GUI_ACTIVE"]
         if us < 100.0 or not g:  # the counter window outlasts short kernels
-            lines.append(f"| `{_short(name)}` | {len(d['_dur'])} | {us:.1f} | - | - |")
+            lines.append(f"| `{_short(name)}` | {launch} | {len(d)} | {us:.1f} | - | - |"
+                         + (" - |" if kind == "stall" else ""))
             continue
-        lines.append(f"| `{_short(name)}` | {len(d['_dur'])} | {us:.1f} | "
-                     f"{g / (us * 1e3):.2f} | {100 * m / (SIMDS * g):.1f}% |")
+        clock = g / (us * 1e3)
+        if kind == "mfma":
+            lines.append(f"| `{_short(name)}` | {launch} | {len(d)} | {us:.1f} | {clock:.2f} | "
+                         f"{100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (SIMDS * g):.1f}% |")
+        else:
+            wait = c["SQ_WAIT_ANY"] / max(c["SQ_WAVE_CYCLES"], 1.0)
+            conf = c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_INSTS_LDS"], 1.0)
+            lines.append(f"| `{_short(name)}` | {launch} | {len(d)} | {us:.1f} | {clock:.2f} | "
+                         f"{100 * wait:.1f}% | {conf:.3f} |")
     return "\n".join(lines) + "\n"
 
 
+class _F64Experts:
+    """Stacked expert weights as the oracle reads them, w[e] -> float64,
+    upcast from the stored bf16/fp32 tensor once per expert and kept."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+        self.cache = {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            import torch
+            self.cache[e] = self.t[e].to("cpu").to(torch.float64).numpy()
+        return self.cache[e]
+
+    def prefetch(self, experts):
+        for e in experts:
+            self[e]
+
+
+CPU_F64_CAP = 12e9   # host bytes of float64 expert weights the CPU baseline keeps
+
+
+def _blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"] or threadpool_info()
+        d = max(info, key=lambda d: d.get("num_threads", 1))
+        return int(d.get("num_threads", 1)), f"{d.get('internal_api')} {d.get('version')}"
+    except Exception:  # pragma: no cover
+        return os.cpu_count(), "unknown"
+
+
 def _cpu_baseline(w, inp, target_s):
-    """The float64 oracle on a sample of tokens: routing of every token (the
-    capacity rule needs all of them) and the expert work of the sample."""
+    """The float64 CPU oracle on the same workload, on this host's cores.
+
+    Inputs are upcast to float64 first (outside the timing): the oracle's
+    input format.  When the float64 weights of every expert that keeps a row
+    fit in CPU_F64_CAP bytes, the whole layer (oracle.forward) is timed,
+    repeated up to ~target_s.  Otherwise (the 256-expert layer: 90 GB in
+    float64) the oracle's steps are timed on a bounded sample: routing,
+    capacity and permutation of every token; the expert FFNs of an evenly
+    spaced sample of the experts with rows, each on all its kept rows; the
+    shared expert and the combine on a sample of tokens; each part scaled to
+    the whole layer."""
     import numpy as np
-    import torch
 
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    _log("[cpu] converting inputs to float64")
-    oi = {}
-    for k, v in inp.items():
-        if k in ("w_gate", "w_up", "w_down"):
-            oi[k] = [v[e].to("cpu").to(torch.float64).numpy() for e in range(v.shape[0])]
-        else:
-            oi[k] = W.to_f64(v)
+    threads, blas = _blas_info()
+    cores = {"cores": threads, "host_cpus": os.cpu_count(), "blas": blas}
+    oi = {k: (_F64Experts(v) if k in ("w_gate", "w_up", "w_down") else W.to_f64(v))
+          for k, v in inp.items()}
+    kw = dict(top_k=w.top_k, score=w.score, renormalize=w.renormalize,
+              route_scale=w.route_scale, n_groups=w.n_groups, topk_groups=w.topk_groups,
+              group_rule=w.group_rule)
+    t0 = time.perf_counter()
+    r = oracle.route(oi["x"], oi["w_router"], w.top_k, score=w.score,
+                     renormalize=w.renormalize, route_scale=w.route_scale,
+                     logit_bias=oi.get("logit_bias"), select_bias=oi.get("select_bias"),
+                     n_groups=w.n_groups, topk_groups=w.topk_groups, group_rule=w.group_rule)
+    cap = oracle.capacity(w.capacity_factor, w.T, w.top_k, w.E)
+    keep = oracle.first_within_capacity(r["ids"], w.E, cap)
+    offsets, r2a, _ = oracle.permutation(r["ids"], keep, w.E)
+    t_route = time.perf_counter() - t0
+    with_rows = [e for e in range(w.E) if offsets[e + 1] > offsets[e]]
+    per_expert = 3.0 * w.D * w.H * 8
+    if per_expert * len(with_rows) <= CPU_F64_CAP:
+        _log(f"[cpu] upcasting {len(with_rows)} experts to float64")
+        for k in ("w_gate", "w_up", "w_down"):
+            oi[k].prefetch(with_rows)
+        runs = []
+        while sum(runs) < target_s and len(runs) < 20:
+            t0 = time.perf_counter()
+            oracle.forward(oi, capacity_factor=w.capacity_factor, **kw)
+            runs.append(time.perf_counter() - t0)
+        dt = sum(runs) / len(runs)
+        _log(f"[cpu] oracle: whole layer in {dt:.2f}s (mean of {len(runs)})")
+        return {"value": w.T / dt, "unit": "tokens/s", **cores, "kind": "oracle",
+                "sample": f"the whole layer ({w.T} tokens, {len(with_rows)} experts with "
+                          f"rows), oracle.forward in float64, mean of {len(runs)} run(s) of "
+                          f"{dt:.2f} s; inputs upcast to float64 beforehand"}
+    # bounded sample of the experts, every kept row of each
+    n_s = max(1, min(len(with_rows), int(CPU_F64_CAP // per_expert), 32))
+    pick = [with_rows[i] for i in np.linspace(0, len(with_rows) - 1, n_s).round().astype(int)]
+    pick = sorted(set(pick))
+    _log(f"[cpu] upcasting a sample of {len(pick)} of {len(with_rows)} experts to float64")
+    for k in ("w_gate", "w_up", "w_down"):
+        oi[k].prefetch(pick)
+    t0 = time.perf_counter()
+    for e in pick:
+        a = r2a[offsets[e]:offsets[e + 1]]
+        t, sl = a // w.top_k, a % w.top_k
+        y = oracle.swiglu_ffn(oi["x"][t], oi["w_gate"][e], oi["w_up"][e], oi["w_down"][e])
+        y = r["weights"][t, sl][:, None] * y
+    t_exp = time.perf_counter() - t0
+    n_tok = min(w.T, 1024)
+    toks = np.linspace(0, w.T - 1, n_tok).round().astype(np.int64)
+    t0 = time.perf_counter()
+    sh = oracle.shared_expert(oi["x"][toks], oi)
+    Y = np.zeros((n_tok, w.top_k, w.D))
+    oracle.combine(Y, sh)
+    t_tok = time.perf_counter() - t0
+    dt = t_route + t_exp * len(with_rows) / len(pick) + t_tok * w.T / n_tok
+    _log(f"[cpu] oracle: routing {t_route:.2f}s, {len(pick)} experts {t_exp:.2f}s, "
+         f"{n_tok} tokens of shared expert + combine {t_tok:.2f}s -> layer {dt:.2f}s")
+    return {"value": w.T / dt, "unit": "tokens/s", **cores, "kind": "oracle",
+            "sample": f"routing, capacity and permutation of all {w.T} tokens "
+                      f"({t_route:.2f} s); the expert FFNs of {len(pick)} evenly spaced of the "
+                      f"{len(with_rows)} experts with rows, on all their kept rows "
+                      f"({t_exp:.2f} s, scaled by {len(with_rows)}/{len(pick)}); shared expert "
+                      f"and combine on {n_tok} evenly spaced tokens ({t_tok:.2f} s, scaled by "
+                      f"{w.T}/{n_tok}); float64, inputs upcast beforehand; layer estimate "
+                      f"{dt:.2f} s"}
 
-    def run(n):
-        toks = np.linspace(0, w.T - 1, n).astype(np.int64)
-        t0 = time.perf_counter()
-        oracle.forward(oi, top_k=w.top_k, score=w.score, renormalize=w.renormalize,
-                       route_scale=w.route_scale, n_groups=w.n_groups,
-                       topk_groups=w.topk_groups, group_rule=w.group_rule,
-                       capacity_factor=w.capacity_factor, tokens=toks)
-        return time.perf_counter() - t0
 
-    n = min(16, w.T)
-    dt = run(n)
-    _log(f"[cpu] calibration: {n} tokens in {dt:.2f}s")
-    while dt < target_s / 3 and n < w.T:
-        n = int(min(w.T, max(2 * n, n * target_s / max(dt, 1e-3))))
-        dt = run(n)
-        _log(f"[cpu] calibration: {n} tokens in {dt:.2f}s")
-    reps, total = 1, dt
-    while total < target_s and reps < 20:   # whole workload is quick: repeat it
-        total += run(n)
-        reps += 1
-    dt = total / reps
-    _log(f"[cpu] oracle: {n} tokens in {dt:.2f}s (mean of {reps})")
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} of {w.T} tokens (evenly spaced); routing of all {w.T} tokens "
-                      f"included; float64 NumPy; mean of {reps} run(s), {dt:.2f} s each"}
+ORDER = ["tiny_dropless_fp32", "switch_top1_capacity", "mixtral_8x_top2",
+         "deepseek_v3_256x_top8_grouped", "decode_128x_top8"]
+HEADLINE = "mixtral_8x_top2"     # the workload the metric is quoted on
 
 
-def main():
-    args = _parse()
-    if args.pmc_summary:
-        print(_pmc_summary(*args.pmc_summary, args.workload))
-        return
-    if args.mfma_summary:
-        print(_mfma_summary(args.mfma_summary, args.workload))
-        return
-    if args.trace_summary:
-        print(_trace_summary(args.trace_summary, args.workload, args.steps, args.warmup))
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer runs on a single MI355X; it shards by expert across GPUs).",
-              file=sys.stderr)
-        sys.exit(2)
-
+def _bench_workload(w, args, moe, dev):
+    """Time W warm-up and K timed steps of workload w; returns its result."""
     import numpy as np
     import torch
 
-    import mixture_experts_layer_21_amd as moe
     import workloads as W
 
-    w = W.WORKLOADS[args.workload]
-    assert torch.cuda.is_available(), "bench.py needs a visible MI355X"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     _log(f"[bench] {w.name}: drawing inputs")
     gen_dev = "cpu" if w.act_dtype == "f32" else "cuda"
     inp = {k: v.to(dev) for k, v in W.make_inputs(w, gen_dev, seed=args.seed).items()}
@@ -511,12 +622,12 @@ def main():
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
               for _ in range(args.steps)]
-    _log(f"[bench] warmup {args.warmup}")
+    _log(f"[bench] {w.name}: warmup {args.warmup}")
     for i in range(args.warmup):
         step(events[i % args.steps])
         forward()
     torch.cuda.synchronize()
-    _log(f"[bench] timing {args.steps} steps")
+    _log(f"[bench] {w.name}: timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
@@ -528,7 +639,7 @@ def main():
                          for ev in events]).mean(axis=0)
     # each timed step on the device clock (HIP events around the step)
     step_dev = np.array([ev[0].elapsed_time(ev[4]) for ev in events])
-    _log(f"[bench] {ms_per_step:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
+    _log(f"[bench] {w.name}: {ms_per_step:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
     _log("[bench] stages ms: route %.4f permute %.4f grouped_swiglu %.4f combine %.4f"
          % tuple(stage_ms))
     t0 = time.perf_counter()
@@ -536,7 +647,7 @@ def main():
         forward()
     torch.cuda.synchronize()
     fwd_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    _log(f"[bench] moe_forward: {fwd_ms:.3f} ms/step")
+    _log(f"[bench] {w.name}: moe_forward {fwd_ms:.3f} ms/step")
 
     # A step beside the layer, timed on its own (not part of the step above):
     # the RMSNorm pre-norm of the residual stream.  Algorithmic bytes: x read
@@ -551,20 +662,24 @@ def main():
     rev[1].record(stream)
     torch.cuda.synchronize()
     rms_ms = rev[0].elapsed_time(rev[1]) / args.steps
-    esz_x = 2 if w.act_dtype == "bf16" else 4
-    rms_bytes = 2.0 * w.T * w.D * esz_x + 4.0 * w.D
+    bf16 = w.act_dtype == "bf16"
+    esz = 2 if bf16 else 4
+    rms_bytes = 2.0 * w.T * w.D * esz + 4.0 * w.D
 
     # Algorithmic work of the grouped SwiGLU step: 2*D*H FLOP for each of the
     # gate, up and down products per kept row (plus the shared expert on T
     # rows); algorithmic bytes: the three weight matrices of every expert that
-    # keeps at least one row, the gathered input rows and the output rows.
-    bf16 = w.act_dtype == "bf16"
-    esz = 2 if bf16 else 4
+    # keeps at least one row (and of the shared expert), x read once and the
+    # output written once.  The rows the implementation gathers, its hidden
+    # rows and its weighted expert rows are reported beside them.
     kept = np.diff(perm["expert_offsets"].cpu().numpy())
     touched = int((kept > 0).sum())
     flops = 6.0 * w.D * w.H * n_kept + 6.0 * w.D * w.H_shared * w.T
-    nbytes = (3.0 * w.D * w.H * touched * esz + 2.0 * n_kept * w.D * esz
-              + (3.0 * w.D * w.H_shared + 2.0 * w.T * w.D) * esz * (w.H_shared > 0))
+    weight_bytes = 3.0 * w.D * (w.H * touched + w.H_shared) * esz
+    nbytes = weight_bytes + 2.0 * w.T * w.D * esz
+    inter = {"gathered_rows": n_kept * w.D * esz,
+             "hidden_rows_written_and_read": 2.0 * (n_kept * w.H + w.T * w.H_shared) * esz,
+             "expert_rows_written_and_read": 2.0 * (n_kept + w.T * (w.H_shared > 0)) * w.D * esz}
     sec = stage_ms[2] * 1e-3
     peak_f = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     traffic = _traffic(w.name, 1)
@@ -576,13 +691,29 @@ def main():
     roofline = {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 2),
                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": traffic,
-                "kernel": "grouped_swiglu step (gate/up GEMM + down GEMM)",
+                "kernel": "grouped_swiglu step (gate/up GEMM + down GEMM"
+                          + (", routed and shared expert)" if w.H_shared else ")"),
                 "algorithmic_flop_per_launch": flops,
                 "algorithmic_bytes_per_launch": nbytes,
+                "intermediate_bytes_per_launch": inter,
                 "experts_with_rows": touched,
                 "tflops": round(flops / sec / 1e12, 2),
+                "frac_of_mfma_peak": round(flops / sec / 1e12 / peak_f, 4),
                 "hbm_gbs": round(nbytes / sec / 1e9, 1),
+                "frac_of_hbm_peak": round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 4),
                 "launch_ms": round(float(stage_ms[2]), 4)}
+    # The whole layer (route, permute, grouped SwiGLU, combine): the router
+    # GEMM joins the FLOP, its weights the bytes.
+    rsz = 4 if w.router_dtype == "f32" else 2
+    l_flops = flops + 2.0 * w.T * w.D * w.E
+    l_bytes = nbytes + 1.0 * w.E * w.D * rsz
+    l_sec = float(np.median(step_dev)) * 1e-3
+    layer = {"ms_device_median": round(l_sec * 1e3, 4),
+             "algorithmic_flop": l_flops, "algorithmic_bytes": l_bytes,
+             "tflops": round(l_flops / l_sec / 1e12, 2),
+             "frac_of_mfma_peak": round(l_flops / l_sec / 1e12 / peak_f, 4),
+             "hbm_gbs": round(l_bytes / l_sec / 1e9, 1),
+             "frac_of_hbm_peak": round(l_bytes / l_sec / 1e9 / PEAK_HBM_GBS, 4)}
 
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s",
@@ -600,14 +731,76 @@ def main():
         "stages_ms": {k: round(float(v), 4) for k, v in
                       zip(("route", "permute", "grouped_swiglu", "combine"), stage_ms)},
         "roofline": roofline,
+        "layer": layer,
         "beside_the_step": {"rmsnorm_ms": round(rms_ms, 4),
                             "rmsnorm_gbs": round(rms_bytes / (rms_ms * 1e-3) / 1e9, 1)},
     }
     if args.backward:
         result["backward"] = _time_backward(moe, w, cfg, inp, r, n_kept, args.steps, stream)
+    del ws, y, shared_y, xn
+    torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(w, inp, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    del inp
+    torch.cuda.empty_cache()
+    return result
+
+
+def _entry(res):
+    """The per-workload summary carried in the headline line."""
+    e = {k: res[k] for k in ("value", "unit", "ms_per_step", "dtype", "stages_ms", "layer")}
+    e["tokens_per_s"] = e.pop("value")
+    rf = res["roofline"]
+    e["grouped_swiglu"] = {k: rf[k] for k in ("bound", "achieved", "unit", "frac", "tflops",
+                                              "frac_of_mfma_peak", "hbm_gbs",
+                                              "frac_of_hbm_peak", "launch_ms", "traffic",
+                                              "experts_with_rows")}
+    e["kept_rows"] = res["config"]["kept_rows"]
+    if "cpu_baseline" in res:
+        e["cpu_baseline"] = res["cpu_baseline"]
+    return e
+
+
+def main():
+    args = _parse()
+    if args.pmc_summary:
+        print(_pmc_summary(*args.pmc_summary, args.workload))
+        return
+    if args.mfma_summary:
+        print(_counter_table(args.mfma_summary, args.workload, "mfma"))
+        return
+    if args.stall_summary:
+        print(_counter_table(args.stall_summary, args.workload, "stall"))
+        return
+    if args.trace_summary:
+        print(_trace_summary(args.trace_summary, args.workload, args.steps, args.warmup))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer runs on a single MI355X; it shards by expert across GPUs).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_layer_21_amd as moe
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a visible MI355X"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload != "all":
+        print(json.dumps(_bench_workload(W.WORKLOADS[args.workload], args, moe, dev)),
+              flush=True)
+        return
+    # Every workload in one process; the headline fields are the Mixtral-shaped
+    # layer's, the metric's own configuration.
+    results = {}
+    for name in ORDER:
+        results[name] = _bench_workload(W.WORKLOADS[name], args, moe, dev)
+    head = dict(results[HEADLINE])
+    head["configs"] = {name: _entry(res) for name, res in results.items()}
+    print(json.dumps(head), flush=True)
 
 
 if __name__ == "__main__":

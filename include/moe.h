@@ -290,9 +290,11 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg);
  * expert receives g_t dout_t and the gate's logit g_t (1 - g_t) <dout_t, S_t>,
  * formed from the shared down dgrad and the saved SwiGLU output without
  * recomputing S; it reaches w_sg (fixed-order column sums) and dx.
- * With the pre-norm ("Transformer Architecture": the block normalises its
- * input before the sublayer, RMSNorm), the rows are renormalised with the
- * forward's kernel and the gradient passes back through the norm:
+ * With the pre-norm ("Lab: build a tiny MoE in PyTorch", "Put the MoE into a
+ * decoder block": the MoE branch takes the RMS-normalised stream;
+ * st-moe-pytorch "rms-norm": RMSNorm ahead of the MoE in SparseMoEBlock), the
+ * rows are renormalised with the forward's kernel and the gradient passes
+ * back through the norm:
  * with s = sqrt(mean(x^2) + eps) and g = norm_weight * dL/dy,
  *   dx = g / s - x * sum(g x) / (D s^3),   dL/dw_d = sum_t dL/dy_td x_td / s_t,
  * dL/dy kept fp32, dx rounded once.

@@ -211,6 +211,20 @@ def pin_near_tie_flag(o):
     assert r["near_tie"].tolist() == [True, False]
 
 
+def pin_group_near_tie_flag(o):
+    """Hand-worked group-limited tokens: a gap below 1e-5 between the last
+    kept group and the first dropped one is flagged even when the chosen
+    experts are well separated; the same gap at 1e-3, or a near tie between
+    two dropped groups, is not; a near tie between the kept groups is."""
+    g = _golden("group_near_tie_hand_built.json")
+    s = np.array(g["sel"])
+    h = np.log(s / (1.0 - s))  # sigmoid(h) = s
+    r = _route_logits(o, h, g["k"], score="sigmoid", n_groups=g["n_groups"],
+                      topk_groups=g["topk_groups"])
+    assert r["ids"].tolist() == g["expected_ids"], r["ids"]
+    assert r["near_tie"].tolist() == g["expected_near_tie"], r["margin"]
+
+
 # ------------------------------------------------------------- aux ---------
 
 def pin_balance_uniform_is_one(o):

@@ -176,3 +176,22 @@ def test_struct_layout_matches_header(moe, tmp_path):
     assert vals[0] == ctypes.sizeof(moe.MoeConfig)
     for name, off in zip(fields, vals[1:]):
         assert getattr(moe.MoeConfig, name).offset == off, name
+
+
+def test_band_workloads_take_the_medium_tile_rows(moe):
+    """The reduced workloads named *_band have 64 to 191 rows per expert on
+    average (moe_max_rows over E), the range in which the bf16 grouped GEMMs
+    use 128-row tiles, as the full Switch-shaped layer does."""
+    import workloads as W
+    for name in ("switch_band", "mixtral_band"):
+        w = W.SMALL[name]
+        cfg = moe.make_config(w.T, w.D, w.H, w.E, w.top_k, router_dtype=w.router_dtype,
+                              renormalize=w.renormalize, capacity_factor=w.capacity_factor)
+        rows = moe.max_rows(cfg)
+        assert 64 * w.E <= rows < 192 * w.E, (name, rows)
+    full = W.WORKLOADS["switch_top1_capacity"]
+    cfg = moe.make_config(full.T, full.D, full.H, full.E, full.top_k,
+                          router_dtype=full.router_dtype, renormalize=full.renormalize,
+                          capacity_factor=full.capacity_factor)
+    assert 64 * full.E <= moe.max_rows(cfg) < 192 * full.E
+

@@ -366,7 +366,8 @@ def test_backward_beyond_32bit_offsets(moe):
     _sampled_weight_rows(g, r, keep, oi, do, w, rng, "beyond 2 GB", n_experts=2)
 
 
-FULL = ["mixtral_8x_top2", "switch_top1_capacity", "decode_128x_top8"]
+FULL = ["mixtral_8x_top2", "switch_top1_capacity", "decode_128x_top8",
+        "deepseek_v3_256x_top8_grouped"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -393,10 +394,17 @@ def test_full_size_backward(moe, name):
     g = moe.moe_backward(cfg, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
                          inp["w_down"], torch.from_numpy(r["ids"].astype(np.int32)).cuda(),
                          torch.from_numpy(r["weights"].astype(np.float32)).cuda(), dout,
-                         logit_bias=inp.get("logit_bias"), balance_coef=aux[0], z_coef=aux[1],
-                         d_gate_w=True)
+                         logit_bias=inp.get("logit_bias"), ws_gate=inp.get("ws_gate"),
+                         ws_up=inp.get("ws_up"), ws_down=inp.get("ws_down"),
+                         balance_coef=aux[0], z_coef=aux[1], d_gate_w=True)
     torch.cuda.synchronize()
     x, do = oi["x"], dout.to(torch.float64).cpu().numpy()
+    experts = {}  # float64 weights of each expert the samples reach, converted once
+
+    def expert(e):
+        if e not in experts:
+            experts[e] = (oi["w_gate"][e], oi["w_up"][e], oi["w_down"][e])
+        return experts[e]
     # sampled tokens: experts' input gradients, dL/dw, and the router's share
     rng = np.random.default_rng(3)
     toks = np.unique(np.concatenate([rng.choice(w.T, 16, replace=False), [0, w.T - 1],
@@ -409,11 +417,14 @@ def test_full_size_backward(moe, name):
             if not keep[t, s_]:
                 continue
             e = r["ids"][t, s_]
-            dz, _, _, _, F = P.oracle.swiglu_ffn_backward(
-                x[t:t + 1], oi["w_gate"][e], oi["w_up"][e], oi["w_down"][e],
-                r["weights"][t, s_] * do[t:t + 1])
+            dz, _, _, _, F = P.oracle.swiglu_ffn_backward(x[t:t + 1], *expert(e),
+                                                          r["weights"][t, s_] * do[t:t + 1])
             dx[i] += dz[0]
             dgw[t, s_] = float(np.sum(do[t] * F[0]))
+    if w.H_shared:  # the ungated shared expert sees every token with weight 1
+        dz, _, _, _, _ = P.oracle.swiglu_ffn_backward(x[toks], oi["ws_gate"], oi["ws_up"],
+                                                      oi["ws_down"], do[toks])
+        dx += dz
     dh = P.oracle.router_backward(r, dgw, top_k=w.top_k, score=w.score,
                                   renormalize=w.renormalize, route_scale=w.route_scale,
                                   aux_coef=aux, tokens=toks)
@@ -441,4 +452,12 @@ def test_full_size_backward(moe, name):
         if not kept_rows[e][0].size:  # an expert without rows gets exactly zero
             assert not g["dw_gate"][e].any() and not g["dw_down"][e].any()
             break
+    if w.H_shared:  # whole weight-gradient rows of sampled shared-expert units
+        for h in rng.choice(w.H_shared, size=2, replace=False):
+            _, dwg, dwu, dwd, _ = P.oracle.swiglu_ffn_backward(
+                x, oi["ws_gate"][h:h + 1], oi["ws_up"][h:h + 1], oi["ws_down"][:, h:h + 1], do)
+            what = f"{name} shared expert unit {h}"
+            P.compare_rows(g["dws_gate"][h], dwg[0], "bf16", what + " dW_gate row")
+            P.compare_rows(g["dws_up"][h], dwu[0], "bf16", what + " dW_up row")
+            P.compare_rows(g["dws_down"][:, h], dwd[:, 0], "bf16", what + " dW_down column")
     _say(f"[full backward] {name}: {len(with_rows)} experts with rows; checked {list(pick)}")

@@ -188,6 +188,15 @@ MUTANTS = [
     ("shared_gate_bwd_no_dx_term",
      "dx += dlogit[:, None] * np.asarray(wsg, dtype=np.float64)[None, :]",
      "dx += 0.0"),
+    ("group_margin_over_all_groups",
+     "group_margin = _min_adjacent_gap(gsorted, min(topk_groups + 1, n_groups))",
+     "group_margin = _min_adjacent_gap(gsorted, n_groups)"),
+    ("group_margin_kept_groups_only",
+     "group_margin = _min_adjacent_gap(gsorted, min(topk_groups + 1, n_groups))",
+     "group_margin = _min_adjacent_gap(gsorted, topk_groups)"),
+    ("group_margin_dropped",
+     "margin = np.minimum(_min_adjacent_gap(sel_sorted, min(top_k + 1, E)), group_margin)",
+     "margin = _min_adjacent_gap(sel_sorted, min(top_k + 1, E))"),
     ("router_bias_ignored",
      "h = h + np.asarray(logit_bias, dtype=np.float64)[None, :]",
      "h = h + 0.0"),

@@ -93,6 +93,11 @@ SMALL = {
                                      H_shared=256),
     "decode_small": DECODE.with_(name="decode_small", batch=1, seq=37, D=512, H=384,
                                  E=32, top_k=8),
+    # 64-191 rows per expert on average, the band of the full Switch-shaped
+    # layer (8192 rows over 64 experts): a capacity-limited Zipf-skewed layer
+    # (C = 125) and a dropless top-2 one (about 150 rows per expert).
+    "switch_band": SWITCH.with_(name="switch_band", batch=1, seq=1600, D=256, H=320, E=16),
+    "mixtral_band": MIXTRAL.with_(name="mixtral_band", batch=1, seq=601, D=256, H=320, E=8),
 }
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
