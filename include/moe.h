@@ -249,6 +249,36 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
                        float* gate_w, int32_t* counts, float* aux, void* saved,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Scratch bytes that moe_forward_noalloc holds on each GPU it runs on. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory around the call: code under HIP graph capture, tight serving
+ * (decode) loops, harnesses that forbid hipMalloc.  Arguments, results and
+ * errors are those of moe_forward; the call itself allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).  Its scratch is a static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one copy per
+ * GPU, held until the process ends; a configuration whose forward needs more
+ * (moe_workspace_bytes counts a larger split-K area, so it is an upper bound
+ * only) returns MOE_ERR_UNSUPPORTED before anything is enqueued.  Decode-sized
+ * layers fit: e.g. T = 64 tokens, D = 4096, H = 1536, E = 128, top_k = 8.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or different host threads without stream
+ * order) race and give undefined results; stream-ordered calls are safe.
+ * Nothing in the array needs to start at zero (each call writes what it
+ * reads).  Outputs agree with moe_forward to rounding: decode-sized grouped
+ * GEMMs split their last round along K exactly as moe_forward does, larger
+ * tiles run it unsplit. */
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const float* norm_weight,
+                               const void* w_router, const float* logit_bias,
+                               const float* select_bias, const uint8_t* token_mask,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               const void* w_shared_gate, const void* w_shared_up,
+                               const void* w_shared_down, const void* shared_expert_gate,
+                               const void* residual, void* out, int32_t* expert_ids,
+                               float* gate_w, int32_t* counts, float* aux, void* saved,
+                               hipStream_t stream);
+
 /* Bytes of the forward's saved SwiGLU state (0 if the configuration is
  * invalid or not bf16): act, d act/d g and d act/d u of moe_max_rows(cfg)
  * routed rows x H, then of T rows x H_shared. */

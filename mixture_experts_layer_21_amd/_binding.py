@@ -96,6 +96,8 @@ _sigs = {
     "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_forward_noalloc": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_saved_bytes": (ctypes.c_size_t, [_CFG]),
     "moe_rmsnorm": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
     "moe_backward_workspace_bytes": (_SZ, [_CFG]),
@@ -320,14 +322,12 @@ def moe_combine(cfg, y_rows, assign_to_row, shared_rows=None, out=None, validate
     return out
 
 
-def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, select_bias=None,
-                ws_gate=None, ws_up=None, ws_down=None, out=None, expert_ids=None, gate_w=None,
-                counts=None, aux=None, workspace=None, token_mask=None,
-                shared_expert_gate=None, residual=None, norm_weight=None, saved=None):
-    """The whole layer forward (see ``moe_forward``); with ``cfg.pre_norm``
-    the layer takes RMSNorm(x) (``norm_weight`` [D] f32 or None).  ``saved``
-    (uint8 device tensor of ``saved_bytes(cfg)``, see ``new_saved``) receives
-    the SwiGLU state that ``moe_backward(saved=...)`` then reuses."""
+def _forward_args(cfg, x, w_router, w_gate, w_up, w_down, logit_bias, select_bias, ws_gate,
+                  ws_up, ws_down, out, expert_ids, gate_w, counts, aux, token_mask,
+                  shared_expert_gate, residual, norm_weight, saved):
+    """Checked pointer arguments of moe_forward / moe_forward_noalloc up to
+    ``saved`` (the output is allocated here when ``out`` is None), with the
+    output and the token mask actually passed."""
     check_config(cfg)
     T, D, H, E, k, Hs = cfg.T, cfg.D, cfg.H, cfg.E, cfg.top_k, cfg.H_shared
     dt = cfg.act_torch_dtype
@@ -352,14 +352,44 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, sele
     _expect(gate_w, "gate_w", (T, k), torch.float32, required=False)
     _expect(counts, "counts", (E,), torch.int32, required=False)
     _expect(aux, "aux", (2,), torch.float32, required=False)
+    # token_mask may be a converted copy: it rides along in the tuple so that
+    # it stays alive until the call has been enqueued
+    return out, token_mask, (ctypes.byref(cfg), _ptr(x), _ptr(norm_weight), _ptr(w_router),
+                 _ptr(logit_bias), _ptr(select_bias), _ptr(token_mask), _ptr(w_gate),
+                 _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
+                 _ptr(shared_expert_gate), _ptr(residual), _ptr(out), _ptr(expert_ids),
+                 _ptr(gate_w), _ptr(counts), _ptr(aux), _ptr(saved))
+
+
+def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, *, logit_bias=None, select_bias=None,
+                ws_gate=None, ws_up=None, ws_down=None, out=None, expert_ids=None, gate_w=None,
+                counts=None, aux=None, workspace=None, token_mask=None,
+                shared_expert_gate=None, residual=None, norm_weight=None, saved=None):
+    """The whole layer forward (see ``moe_forward``); with ``cfg.pre_norm``
+    the layer takes RMSNorm(x) (``norm_weight`` [D] f32 or None).  ``saved``
+    (uint8 device tensor of ``saved_bytes(cfg)``, see ``new_saved``) receives
+    the SwiGLU state that ``moe_backward(saved=...)`` then reuses."""
+    out, _keep, args = _forward_args(cfg, x, w_router, w_gate, w_up, w_down, logit_bias,
+                                     select_bias, ws_gate, ws_up, ws_down, out, expert_ids,
+                                     gate_w, counts, aux, token_mask, shared_expert_gate,
+                                     residual, norm_weight, saved)
     ws = new_workspace(cfg, x.device) if workspace is None else workspace
-    _check(_lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(norm_weight), _ptr(w_router),
-                            _ptr(logit_bias),
-                            _ptr(select_bias), _ptr(token_mask), _ptr(w_gate), _ptr(w_up),
-                            _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
-                            _ptr(shared_expert_gate), _ptr(residual), _ptr(out),
-                            _ptr(expert_ids), _ptr(gate_w), _ptr(counts), _ptr(aux),
-                            _ptr(saved), _ptr(ws), ws.numel(), _stream()), "moe_forward")
+    _check(_lib.moe_forward(*args, _ptr(ws), ws.numel(), _stream()), "moe_forward")
+    return out
+
+
+def moe_forward_noalloc(cfg, x, w_router, w_gate, w_up, w_down, *, out, logit_bias=None,
+                        select_bias=None, ws_gate=None, ws_up=None, ws_down=None,
+                        expert_ids=None, gate_w=None, counts=None, aux=None, token_mask=None,
+                        shared_expert_gate=None, residual=None, norm_weight=None, saved=None):
+    """``moe_forward`` on the library's static scratch (see
+    ``moe_forward_noalloc``): no workspace, and the caller passes ``out`` so
+    that the call allocates nothing."""
+    out, _keep, args = _forward_args(cfg, x, w_router, w_gate, w_up, w_down, logit_bias,
+                                     select_bias, ws_gate, ws_up, ws_down, out, expert_ids,
+                                     gate_w, counts, aux, token_mask, shared_expert_gate,
+                                     residual, norm_weight, saved)
+    _check(_lib.moe_forward_noalloc(*args, _stream()), "moe_forward_noalloc")
     return out
 
 

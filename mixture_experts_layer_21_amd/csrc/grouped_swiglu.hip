@@ -380,7 +380,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int t
   if (piece >= 0) {
     // A piece of a split tail tile: the raw fp32 sums, row-major over the
     // tile's BM rows and NB*BN columns (gate columns, then up columns).
-    float* part = p.tail_part + (size_t)tail_slot * (kTailSlotBytes / 4);
+    float* part = p.tail_part + (size_t)tail_slot * p.tail_slot_floats;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmPar
   const int m0 = d[1], m_end = d[2], n0 = d[3] * BN;
   const int N = GATEUP ? p.hidden : p.D;
   const int rows = min(BM, m_end - m0);
-  const float* part0 = p.tail_part + (size_t)(xcd * kTailSlots + j * ns) * (kTailSlotBytes / 4);
+  const float* part0 = p.tail_part + (size_t)(xcd * kTailSlots + j * ns) * p.tail_slot_floats;
   for (int idx = threadIdx.x; idx < rows * BN; idx += NTHREADS) {
     const int rl = idx / BN, cl = idx % BN, col = n0 + cl;
     if (col >= N) continue;
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmPar
 #pragma unroll
     for (int pc = 0; pc < 16; ++pc) {
       if (pc < ns) {
-        const float* part = part0 + (size_t)pc * (kTailSlotBytes / 4);
+        const float* part = part0 + (size_t)pc * p.tail_slot_floats;
         v0[pc] = part[rl * W + cl];
         if constexpr (GATEUP) v1[pc] = part[rl * W + BN + cl];
       }
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmParams p) {
   using C = DmaCfg<BM, BNB, BK, S, WGM, NWV, GATEUP>;
   constexpr int VPT = C::MI * C::NI * 4;  // f32x4 vectors of one GEMM thread per NB part
   constexpr int PER_TILE = VPT * C::NT;
-  constexpr size_t SLOT = kTailSlotBytes / 4;
+  const size_t SLOT = p.tail_slot_floats;
   const int xcd = blockIdx.x % kXcds, bx = blockIdx.x / kXcds, nbx = gridDim.x / kXcds;
   const int r = p.tail_meta[2 * xcd], ns = p.tail_meta[2 * xcd + 1];
   const int N = GATEUP ? p.hidden : p.D;
@@ -766,7 +766,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
     dma_mainloop<C, GATEUP, true>(ld, ke - kb, mi_n, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3,
                                   sB0, sB1, sB2, sB3);
   if (piece >= 0) {
-    dma_store_partial<C, GATEUP>(p.tail_part + (size_t)tail_slot * (kTailSlotBytes / 4), tid,
+    dma_store_partial<C, GATEUP>(p.tail_part + (size_t)tail_slot * p.tail_slot_floats, tid,
                                  acc);
     return;
   }
@@ -904,7 +904,9 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   const int mt = mtiles_bound(p, BM);
   const long long tiles = (long long)mt * ((N + BN - 1) / BN);
   if (tiles <= 0) return hipSuccess;
-  const int slots = p.tail_part ? slots_per_xcd(kern, NTHREADS) : 0;
+  constexpr size_t part_floats = (size_t)BM * (GATEUP ? 2 : 1) * BN;
+  const int slots =
+      p.tail_part && part_floats <= p.tail_slot_floats ? slots_per_xcd(kern, NTHREADS) : 0;
   // Every XCD gets at most ceil(tiles/8) tiles plus at most `slots` extra
   // blocks for the pieces of its split tail.
   const long long nblocks = kXcds * ((tiles + kXcds - 1) / kXcds + slots);
@@ -924,7 +926,9 @@ hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
   const int mt = mtiles_bound(p, BM);
   const long long tiles = (long long)mt * ((N + C::BN - 1) / C::BN);
   if (tiles <= 0) return hipSuccess;
-  const int slots = p.tail_part ? slots_per_xcd(kern, C::NT) : 0;
+  constexpr size_t part_floats = (size_t)partial_vectors<C>() * C::NT * 4;
+  const int slots =
+      p.tail_part && part_floats <= p.tail_slot_floats ? slots_per_xcd(kern, C::NT) : 0;
   // Every XCD gets at most ceil(tiles/8) tiles plus at most `slots` extra
   // blocks for the pieces of its split tail.
   const long long nblocks = kXcds * ((tiles + kXcds - 1) / kXcds + slots);

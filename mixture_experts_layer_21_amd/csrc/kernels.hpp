@@ -87,14 +87,20 @@ struct GemmParams {
   float* tail_part;
   int32_t* tail_meta;        // [kXcds * 2]
   int32_t* tail_desc;        // [kXcds * kTailSlots * 4]
+  // Floats per partial-tile slot of tail_part.  A kernel whose fp32 partial
+  // tile is larger than a slot runs its last round unsplit.
+  size_t tail_slot_floats;
 };
 
 // Split-K tail bookkeeping of the large-tile grouped GEMM.
 constexpr int kXcds = 8;
 constexpr int kTailSlots = 64;                       // partial tiles per XCD
 constexpr size_t kTailSlotBytes = (size_t)256 * 256 * 4;  // one fp32 256x256 tile
-inline size_t tail_workspace_bytes() {
-  return (size_t)kXcds * kTailSlots * kTailSlotBytes + 256 + (size_t)kXcds * kTailSlots * 16;
+// Slots of kTailSlotBytes hold the partial tiles of every kernel; slots of
+// 32 KB those of the 32-row (decode-sized) kernels only.
+constexpr size_t kSmallTailSlotBytes = (size_t)32 * 256 * 4;
+inline size_t tail_workspace_bytes(size_t slot_bytes = kTailSlotBytes) {
+  return (size_t)kXcds * kTailSlots * slot_bytes + 256 + (size_t)kXcds * kTailSlots * 16;
 }
 
 struct CombineParams {

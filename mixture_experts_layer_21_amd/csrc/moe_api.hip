@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
@@ -116,7 +117,8 @@ struct Layout {
       offsets, n_kept, r2a, a2r, hbuf, y, shared_y, tail, x_norm, total;
 };
 
-Layout layout_of(const moe_config* c) {
+// tail_slot_bytes: slot size of the grouped GEMMs' split-K partial tiles.
+Layout layout_of(const moe_config* c, size_t tail_slot_bytes = moe::kTailSlotBytes) {
   Layout L{};
   const size_t T = c->T, k = c->top_k, E = c->E, D = c->D;
   const size_t nblk = moe::route_blocks(c->T);
@@ -148,7 +150,7 @@ Layout layout_of(const moe_config* c) {
   L.hbuf = take(std::max(rows * (size_t)c->H, T * (size_t)c->H_shared) * es);
   L.y = take(rows * D * es);
   L.shared_y = take(c->H_shared ? T * D * es : 0);
-  L.tail = take(c->act_dtype == MOE_BF16 ? moe::tail_workspace_bytes() : 0);
+  L.tail = take(c->act_dtype == MOE_BF16 ? moe::tail_workspace_bytes(tail_slot_bytes) : 0);
   L.x_norm = take(c->pre_norm ? T * D * es : 0);
   L.total = off;
   return L;
@@ -268,6 +270,34 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Scratch of moe_forward_noalloc: a static device array, one copy on every
+// GPU the library runs on, held until the process ends.  Host code never
+// uses the array's own name as a device address (on the host it names a
+// stand-in); the address of the current device's copy comes from
+// hipGetSymbolAddress on that device's first call and is kept per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_HIP, "moe_forward_noalloc: no usable current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "moe_forward_noalloc: hipGetSymbolAddress of the scratch "
+                  "array failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 moe::RouteParams route_params(const moe_config* c, const void* x, const void* w_router,
                               const float* lb, const float* sb, const uint8_t* mask,
                               int32_t* ids, float* gw, void* ws, const Layout& L) {
@@ -303,14 +333,16 @@ moe::RouteParams route_params(const moe_config* c, const void* x, const void* w_
 moe::GemmParams gemm_params(const moe_config* c, int n_groups, int hidden, const void* x,
                             const int32_t* r2a, const int32_t* offsets, int max_rows,
                             const float* gw, const void* wg, const void* wu, const void* wd,
-                            void* hbuf, void* y, void* tail) {
+                            void* hbuf, void* y, void* tail,
+                            size_t tail_slot_bytes = moe::kTailSlotBytes) {
   moe::GemmParams p{};
   if (tail) {
     char* t = static_cast<char*>(tail);
-    const size_t parts = (size_t)moe::kXcds * moe::kTailSlots * moe::kTailSlotBytes;
+    const size_t parts = (size_t)moe::kXcds * moe::kTailSlots * tail_slot_bytes;
     p.tail_part = reinterpret_cast<float*>(t);
     p.tail_meta = reinterpret_cast<int32_t*>(t + parts);
     p.tail_desc = reinterpret_cast<int32_t*>(t + parts + 256);
+    p.tail_slot_floats = tail_slot_bytes / 4;
   }
   p.T = c->T;
   p.D = c->D;
@@ -573,27 +605,27 @@ moe_status moe_rmsnorm(const moe_config* cfg, const void* x, const float* norm_w
   return ok();
 }
 
-moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_weight,
-                       const void* w_router,
-                       const float* logit_bias, const float* select_bias,
-                       const uint8_t* token_mask, const void* w_gate, const void* w_up,
-                       const void* w_down, const void* w_shared_gate, const void* w_shared_up,
-                       const void* w_shared_down, const void* shared_expert_gate,
-                       const void* residual, void* out, int32_t* expert_ids, float* gate_w,
-                       int32_t* counts, float* aux, void* saved,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  MOE_TRY(check_config(cfg));
+// Argument checks of the forward entry points (all but the workspace); `who`
+// names the entry point in error messages.
+static moe_status forward_checks(const char* who, const moe_config* cfg, const void* x,
+                                 const float* norm_weight, const void* w_router,
+                                 const float* logit_bias, const float* select_bias,
+                                 const uint8_t* token_mask, const void* w_gate, const void* w_up,
+                                 const void* w_down, const void* w_shared_gate,
+                                 const void* w_shared_up, const void* w_shared_down,
+                                 const void* shared_expert_gate, const void* residual, void* out,
+                                 int32_t* expert_ids, float* gate_w, int32_t* counts, float* aux,
+                                 void* saved) {
   if (saved && cfg->act_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_forward: saved needs bf16 activations");
+    return fail(MOE_ERR_UNSUPPORTED, "%s: saved needs bf16 activations", who);
   if (!x || !w_router || !w_gate || !w_up || !w_down || !out)
-    return fail(MOE_ERR_NULL_PTR, "moe_forward: x, w_router, expert weights and out required");
+    return fail(MOE_ERR_NULL_PTR, "%s: x, w_router, expert weights and out required", who);
   if (cfg->H_shared > 0 && (!w_shared_gate || !w_shared_up || !w_shared_down))
-    return fail(MOE_ERR_NULL_PTR, "moe_forward: H_shared > 0 needs the shared-expert weights");
+    return fail(MOE_ERR_NULL_PTR, "%s: H_shared > 0 needs the shared-expert weights", who);
   if (shared_expert_gate && cfg->H_shared == 0)
-    return fail(MOE_ERR_INVALID_ARG, "moe_forward: shared_expert_gate needs a shared expert");
+    return fail(MOE_ERR_INVALID_ARG, "%s: shared_expert_gate needs a shared expert", who);
   if (norm_weight && !cfg->pre_norm)
-    return fail(MOE_ERR_INVALID_ARG, "moe_forward: norm_weight needs cfg->pre_norm = 1");
-  MOE_TRY(check_ws(cfg, workspace, workspace_bytes));
+    return fail(MOE_ERR_INVALID_ARG, "%s: norm_weight needs cfg->pre_norm = 1", who);
   MOE_TRY(check_dev(x, "x", true));
   MOE_TRY(check_dev(norm_weight, "norm_weight", false));
   MOE_TRY(check_dev(w_router, "w_router", true));
@@ -615,7 +647,6 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
   MOE_TRY(check_dev(gate_w, "gate_w", false));
   MOE_TRY(check_dev(counts, "counts", false));
   MOE_TRY(check_dev(aux, "aux", false));
-  MOE_TRY(check_dev(workspace, "workspace", true));
   MOE_TRY(check_dev(saved, "saved", false));
   if (reinterpret_cast<uintptr_t>(saved) % kAlign)
     return fail(MOE_ERR_INVALID_ARG, "saved must be %zu-byte aligned", kAlign);
@@ -623,8 +654,21 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
     MOE_TRY(check_align16(x, "x"));
     MOE_TRY(check_align16(norm_weight, "norm_weight"));
   }
+  return MOE_OK;
+}
 
-  const Layout L = layout_of(cfg);
+// The stream-ordered launches of the forward on a checked workspace laid out
+// as L (split-K tail slots of tail_slot_bytes).
+static moe_status forward_launch(const moe_config* cfg, const void* x, const float* norm_weight,
+                                 const void* w_router, const float* logit_bias,
+                                 const float* select_bias, const uint8_t* token_mask,
+                                 const void* w_gate, const void* w_up, const void* w_down,
+                                 const void* w_shared_gate, const void* w_shared_up,
+                                 const void* w_shared_down, const void* shared_expert_gate,
+                                 const void* residual, void* out, int32_t* expert_ids,
+                                 float* gate_w, int32_t* counts, float* aux, void* saved,
+                                 void* workspace, const Layout& L, size_t tail_slot_bytes,
+                                 hipStream_t stream) {
   int32_t* ids = expert_ids ? expert_ids : at<int32_t>(workspace, L.ids);
   float* gw = gate_w ? gate_w : at<float>(workspace, L.gate_w);
   int32_t* cnt = counts ? counts : at<int32_t>(workspace, L.counts);
@@ -677,7 +721,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
   const SavedLayout SV = saved_layout_of(cfg);
   auto sv = [&](size_t off) { return reinterpret_cast<uint16_t*>(static_cast<char*>(saved) + off); };
   moe::GemmParams gp = gemm_params(cfg, cfg->E, cfg->H, x, r2a, offsets, rows, gw, w_gate, w_up,
-                                   w_down, saved ? sv(SV.act) : hbuf, y, tail);
+                                   w_down, saved ? sv(SV.act) : hbuf, y, tail, tail_slot_bytes);
   if (saved) {
     gp.save_p1 = sv(SV.p1);
     gp.save_p2 = sv(SV.p2);
@@ -688,7 +732,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
     sy = at<void>(workspace, L.shared_y);
     moe::GemmParams sp2 =
         gemm_params(cfg, 1, cfg->H_shared, x, nullptr, nullptr, cfg->T, nullptr, w_shared_gate,
-                    w_shared_up, w_shared_down, saved ? sv(SV.sact) : hbuf, sy, tail);
+                    w_shared_up, w_shared_down, saved ? sv(SV.sact) : hbuf, sy, tail,
+                    tail_slot_bytes);
     if (saved) {
       sp2.save_p1 = sv(SV.sp1);
       sp2.save_p2 = sv(SV.sp2);
@@ -699,6 +744,61 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_w
                         sy,     x,      shared_expert_gate,      residual, out};
   MOE_TRY(hip_ok(moe::launch_combine(cp, bf16, stream), "combine kernel"));
   return ok();
+}
+
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const float* norm_weight,
+                       const void* w_router,
+                       const float* logit_bias, const float* select_bias,
+                       const uint8_t* token_mask, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* w_shared_gate, const void* w_shared_up,
+                       const void* w_shared_down, const void* shared_expert_gate,
+                       const void* residual, void* out, int32_t* expert_ids, float* gate_w,
+                       int32_t* counts, float* aux, void* saved,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  MOE_TRY(forward_checks("moe_forward", cfg, x, norm_weight, w_router, logit_bias, select_bias,
+                        token_mask, w_gate, w_up, w_down, w_shared_gate, w_shared_up,
+                        w_shared_down, shared_expert_gate, residual, out, expert_ids, gate_w,
+                        counts, aux, saved));
+  MOE_TRY(check_ws(cfg, workspace, workspace_bytes));
+  MOE_TRY(check_dev(workspace, "workspace", true));
+  return forward_launch(cfg, x, norm_weight, w_router, logit_bias, select_bias,
+                        token_mask, w_gate, w_up, w_down, w_shared_gate, w_shared_up,
+                        w_shared_down, shared_expert_gate, residual, out, expert_ids, gate_w,
+                        counts, aux, saved, workspace,
+                        layout_of(cfg), moe::kTailSlotBytes, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const float* norm_weight,
+                               const void* w_router, const float* logit_bias,
+                               const float* select_bias, const uint8_t* token_mask,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               const void* w_shared_gate, const void* w_shared_up,
+                               const void* w_shared_down, const void* shared_expert_gate,
+                               const void* residual, void* out, int32_t* expert_ids,
+                               float* gate_w, int32_t* counts, float* aux, void* saved,
+                               hipStream_t stream) {
+  MOE_TRY(check_config(cfg));
+  // Compact split-K tail slots: the decode-sized 32-row GEMMs split their
+  // last round as in moe_forward; larger tiles run it unsplit.
+  const Layout L = layout_of(cfg, moe::kSmallTailSlotBytes);
+  if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_forward_noalloc: this configuration needs %zu bytes of scratch, more than "
+                "the library's static %zu bytes; use moe_forward with a workspace",
+                L.total, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  MOE_TRY(forward_checks("moe_forward_noalloc", cfg, x, norm_weight, w_router, logit_bias, select_bias,
+                        token_mask, w_gate, w_up, w_down, w_shared_gate, w_shared_up,
+                        w_shared_down, shared_expert_gate, residual, out, expert_ids, gate_w,
+                        counts, aux, saved));
+  void* ws = nullptr;
+  MOE_TRY(noalloc_scratch(&ws));
+  return forward_launch(cfg, x, norm_weight, w_router, logit_bias, select_bias,
+                        token_mask, w_gate, w_up, w_down, w_shared_gate, w_shared_up,
+                        w_shared_down, shared_expert_gate, residual, out, expert_ids, gate_w,
+                        counts, aux, saved, ws, L,
+                        moe::kSmallTailSlotBytes, stream);
 }
 
 size_t moe_backward_workspace_bytes(const moe_config* cfg) {
