@@ -27,8 +27,7 @@ struct Vec16<float> {
 };
 
 template <typename T>
-__device__ __forceinline__ void load16(const T* p, float (&v)[Vec16<T>::N]) {
-  const uint4 q = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void unpack16(const uint4 q, float (&v)[Vec16<T>::N]) {
   if constexpr (Vec16<T>::N == 8) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -42,6 +41,11 @@ __device__ __forceinline__ void load16(const T* p, float (&v)[Vec16<T>::N]) {
     v[2] = __uint_as_float(q.z);
     v[3] = __uint_as_float(q.w);
   }
+}
+
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, float (&v)[Vec16<T>::N]) {
+  unpack16<T>(*reinterpret_cast<const uint4*>(p), v);
 }
 
 template <typename T>
@@ -139,11 +143,74 @@ __global__ __launch_bounds__(NTHREADS) void combine_kernel(CombineParams p, int 
   }
 }
 
+// Without the shared-expert gate every 16-byte chunk of an output row is
+// independent: one thread per (token, chunk), consecutive threads on
+// consecutive chunks of a row.  A thread issues the loads of up to eight
+// slots' rows (and the shared and residual rows) before it adds them in
+// slot order, so the loads of a token overlap instead of following one
+// another; the sum order is that of combine_kernel, so the bits agree.
+template <typename T>
+__global__ __launch_bounds__(NTHREADS) void combine_rows_kernel(CombineParams p) {
+  constexpr int N = Vec16<T>::N;
+  constexpr int G = 8;  // slots loaded together
+  const int nchunk = p.D / N;
+  const long long gid = (long long)blockIdx.x * NTHREADS + threadIdx.x;
+  if (gid >= (long long)p.T * nchunk) return;
+  const int t = (int)(gid / nchunk), c = (int)(gid % nchunk);
+  const T* y = static_cast<const T*>(p.y_rows) + (size_t)c * N;
+  const int32_t* a2r = p.assign_to_row + (size_t)t * p.k;
+  const size_t at = (size_t)t * p.D + (size_t)c * N;
+  uint4 qs = make_uint4(0u, 0u, 0u, 0u), qr = qs;
+  if (p.shared_rows) qs = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.shared_rows) + at);
+  if (p.residual) qr = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.residual) + at);
+  float acc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < p.k; s0 += G) {
+    int row[G];
+    uint4 q[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) row[u] = s0 + u < p.k ? a2r[s0 + u] : -1;
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (row[u] >= 0) q[u] = *reinterpret_cast<const uint4*>(y + (size_t)row[u] * p.D);
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if (row[u] < 0) continue;
+      float v[N];
+      unpack16<T>(q[u], v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += v[i];
+    }
+  }
+  float v[N];
+  if (p.shared_rows) {
+    unpack16<T>(qs, v);
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] += v[i];
+  }
+  if (p.residual) {  // the residual stream joins last, before the one rounding
+    unpack16<T>(qr, v);
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] += v[i];
+  }
+  store16<T>(static_cast<T*>(p.out) + at, acc);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s) {
   const int n = bf16 ? 8 : 4;
   const int nchunk = p.D / n;
+  if (!(p.shared_rows && p.shared_gate)) {
+    const long long threads = (long long)p.T * nchunk;
+    const dim3 grid((unsigned)((threads + NTHREADS - 1) / NTHREADS)), block(NTHREADS);
+    if (bf16)
+      hipLaunchKernelGGL(combine_rows_kernel<uint16_t>, grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL(combine_rows_kernel<float>, grid, block, 0, s, p);
+    return hipGetLastError();
+  }
   int tpb = 1;  // tokens per block: keep at least ~nchunk threads per token
   while (tpb < 64 && NTHREADS / (tpb * 2) >= nchunk) tpb *= 2;
   const dim3 grid((p.T + tpb - 1) / tpb), block(NTHREADS);

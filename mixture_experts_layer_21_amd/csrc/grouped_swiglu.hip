@@ -425,52 +425,60 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int t
   }
 }
 
-// Reduce of the split tail tiles of gemm_bf16_kernel: one block per (XCD,
-// tail tile) adds the row-major partials in piece order and runs the epilogue.
+// Reduce of the split tail tiles of gemm_bf16_kernel.  Each XCD's blocks
+// (block b runs on XCD b % 8, whose L2 holds the partials) stride over that
+// XCD's tail tiles x 4-column vectors of their rows: a thread loads the
+// vector of every piece (gate and up halves for gate/up) before it adds them
+// in piece order, then runs the epilogue on the four columns.
 template <int BM, int BN, bool GATEUP>
 __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmParams p) {
-  constexpr int NB = GATEUP ? 2 : 1, W = NB * BN;
-  static_assert((size_t)BM * W * 4 <= kTailSlotBytes, "tail slot size");
-  // Block b runs on XCD b % 8, the XCD whose L2 holds the partials.
-  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  constexpr int NB = GATEUP ? 2 : 1, W = NB * BN, V = BN / 4;
+  static_assert(BN % 4 == 0, "4-column vectors");
+  const int xcd = blockIdx.x % kXcds, bx = blockIdx.x / kXcds, nbx = gridDim.x / kXcds;
   const int r = p.tail_meta[2 * xcd], ns = p.tail_meta[2 * xcd + 1];
-  if (j >= r) return;
-  const int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + j) * 4;
-  const int m0 = d[1], m_end = d[2], n0 = d[3] * BN;
   const int N = GATEUP ? p.hidden : p.D;
-  const int rows = min(BM, m_end - m0);
-  const float* part0 = p.tail_part + (size_t)(xcd * kTailSlots + j * ns) * p.tail_slot_floats;
-  for (int idx = threadIdx.x; idx < rows * BN; idx += NTHREADS) {
-    const int rl = idx / BN, cl = idx % BN, col = n0 + cl;
-    if (col >= N) continue;
-    // All pieces' values are loaded before the fixed-order sum (ns <= 16).
-    float v0[16], v1[16];
+  const size_t SLOT = p.tail_slot_floats;
+  for (int idx = bx * NTHREADS + threadIdx.x; idx < r * BM * V; idx += nbx * NTHREADS) {
+    const int j = idx / (BM * V), w = idx % (BM * V);
+    const int rl = w / V, cl = 4 * (w % V);
+    const int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + j) * 4;
+    const int m0 = d[1], m_end = d[2], col = d[3] * BN + cl;
+    const int row = m0 + rl;
+    if (row >= m_end || col >= N) continue;  // N is a multiple of 64: all 4 columns valid
+    const float* part0 = p.tail_part + (size_t)(xcd * kTailSlots + j * ns) * SLOT + rl * W + cl;
+    f32x4 v[NB][16];
 #pragma unroll
-    for (int pc = 0; pc < 16; ++pc) {
+    for (int pc = 0; pc < 16; ++pc)
       if (pc < ns) {
-        const float* part = part0 + (size_t)pc * p.tail_slot_floats;
-        v0[pc] = part[rl * W + cl];
-        if constexpr (GATEUP) v1[pc] = part[rl * W + BN + cl];
-      }
-    }
-    float a0 = v0[0], a1 = GATEUP ? v1[0] : 0.f;
 #pragma unroll
-    for (int pc = 1; pc < 16; ++pc) {
-      if (pc < ns) {
-        a0 += v0[pc];
-        if constexpr (GATEUP) a1 += v1[pc];
+        for (int nb = 0; nb < NB; ++nb)
+          v[nb][pc] = *reinterpret_cast<const f32x4*>(part0 + (size_t)pc * SLOT + nb * BN);
       }
+    f32x4 a[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      a[nb] = v[nb][0];
+#pragma unroll
+      for (int pc = 1; pc < 16; ++pc)
+        if (pc < ns) a[nb] += v[nb][pc];
     }
-    const int grow = m0 + rl;
+    const size_t o = (size_t)row * N + col;
+    uint16_t q[4];
     if constexpr (GATEUP) {
-      static_cast<uint16_t*>(p.hbuf)[(size_t)grow * N + col] =
-          f32_to_bf16_bits(swiglu_act(a0, a1, p.swiglu_limit));
-      if (p.save_p1) save_factors(p, (size_t)grow * N + col, a0, a1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        q[u] = f32_to_bf16_bits(swiglu_act(a[0][u], a[NB - 1][u], p.swiglu_limit));
+        if (p.save_p1) save_factors(p, o + u, a[0][u], a[NB - 1][u]);
+      }
     } else {
       float gw = 1.f;
-      if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[grow]];
-      static_cast<uint16_t*>(p.y)[(size_t)grow * N + col] = f32_to_bf16_bits(gw * a0);
+      if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[row]];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = f32_to_bf16_bits(gw * a[0][u]);
     }
+    uint16_t* out = static_cast<uint16_t*>(GATEUP ? p.hbuf : p.y) + o;
+    *reinterpret_cast<uint2*>(out) = make_uint2((uint32_t)q[0] | ((uint32_t)q[1] << 16),
+                                                (uint32_t)q[2] | ((uint32_t)q[3] << 16));
   }
 }
 
@@ -913,7 +921,7 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(NTHREADS), 0, s, p, slots);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || slots == 0) return err;
-  hipLaunchKernelGGL((gemm_tail_reduce_flat_kernel<BM, BN, GATEUP>), dim3(kXcds * kTailSlots),
+  hipLaunchKernelGGL((gemm_tail_reduce_flat_kernel<BM, BN, GATEUP>), dim3(kXcds * 64),
                      dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }

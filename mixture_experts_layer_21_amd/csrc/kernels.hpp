@@ -8,8 +8,11 @@
 namespace moe {
 
 // Tokens per routing block; also the granularity of the per-block expert
-// histograms that the permutation scans.
+// histograms that the permutation scans (route_tile below: small batches use
+// 8-token blocks, one token per wave of the selection kernel).
 constexpr int kRouteTile = 32;
+constexpr int kSmallRouteTile = 8;
+constexpr int kSmallRouteMaxT = 1024;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxGroups = 64;
@@ -24,6 +27,7 @@ struct RouteParams {
   const float* logit_bias;
   const float* select_bias;
   const uint8_t* token_mask;  // [T] or null: 0 = padding token (not routed)
+  int tile;           // tokens per selection block: route_tile(T)
   int32_t* ids;       // [T*k]
   float* gate_w;      // [T*k]
   float* logits_part; // [ksplit*T*E] split-K partial logits
@@ -54,6 +58,7 @@ struct FinalizeParams {
 
 struct ScatterParams {
   int T, E, k, capacity;
+  int tile;                  // tokens per block: route_tile(T)
   const int32_t* ids;
   const int32_t* block_base;
   const int32_t* expert_offsets;
@@ -254,6 +259,10 @@ hipError_t launch_dx(const DxParams& p, bool bf16, hipStream_t s);
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
 hipError_t launch_hist(int T, int E, int k, const int32_t* ids, int32_t* hist, hipStream_t s);
+// Finalize and scatter in one single-workgroup kernel, for small batches
+// (permute_fits_one_block); sp.ids == nullptr: finalize only.
+bool permute_fits_one_block(int T, int E, int k);
+hipError_t launch_permute_small(const FinalizeParams& fp, const ScatterParams& sp, hipStream_t s);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
 hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s);
@@ -269,7 +278,12 @@ hipError_t launch_rmsnorm_bwd(int T, int D, bool bf16, const void* x, const floa
                               const float* dy, void* dx, float* inv_s, float* dw_part,
                               float* dw, hipStream_t s);
 
-inline int route_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
+__host__ __device__ inline int route_tile(int T) {
+  return T <= kSmallRouteMaxT ? kSmallRouteTile : kRouteTile;
+}
+inline int route_blocks(int T) { return (T + route_tile(T) - 1) / route_tile(T); }
+// Token tiles of the per-wave router GEMM (32 tokens: two 16-row MFMA tiles).
+inline int logits_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
 
 // The LDS-tiled router GEMM (64 tokens x 256 experts per block) serves bf16
 // routers with many experts and tokens; the others use the per-wave kernel.
@@ -290,7 +304,7 @@ inline int route_ksplit(int T, int D, int E, bool bf16_mfma) {
   }
   const int NT = (E + 15) / 16;
   const int NTB = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
-  const long long blocks = (long long)route_blocks(T) * ((NT + NTB - 1) / NTB);
+  const long long blocks = (long long)logits_blocks(T) * ((NT + NTB - 1) / NTB);
   int ks = 1;
   while (blocks * ks < 1024 && ks * 2 * 4 <= nsteps && ks < 16) ks *= 2;
   return ks;

@@ -323,11 +323,24 @@ moe::RouteParams route_params(const moe_config* c, const void* x, const void* w_
   p.gate_w = gw;
   p.logits_part = at<float>(ws, L.logits);
   p.ksplit = moe::route_ksplit(c->T, c->D, c->E, p.act_bf16 && p.router_bf16);
+  p.tile = moe::route_tile(c->T);
   p.hist = at<int32_t>(ws, L.hist);
   p.pe_part = at<float>(ws, L.pe_part);
   p.z_part = at<float>(ws, L.z_part);
   p.valid_part = at<int32_t>(ws, L.valid_part);
   return p;
+}
+
+// Finalize (counts, P_e, aux, expert offsets) and, when sp.ids is set, the
+// scatter, from the per-tile histograms in place: one workgroup for small
+// batches, else the per-expert scans and the per-tile scatter.
+moe_status launch_permutation(const moe::FinalizeParams& fp, const moe::ScatterParams& sp,
+                              hipStream_t stream) {
+  if (moe::permute_fits_one_block(fp.T, fp.E, fp.k))
+    return hip_ok(moe::launch_permute_small(fp, sp, stream), "permute kernel");
+  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
+  if (sp.ids) MOE_TRY(hip_ok(moe::launch_scatter(sp, stream), "scatter kernel"));
+  return MOE_OK;
 }
 
 moe::GemmParams gemm_params(const moe_config* c, int n_groups, int hidden, const void* x,
@@ -471,7 +484,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   fp.counts = counts;
   fp.aux = aux;
   fp.mean_prob = mean_prob;
-  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
+  MOE_TRY(launch_permutation(fp, moe::ScatterParams{}, stream));
   return ok();
 }
 
@@ -506,10 +519,9 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* expert_ids, int32_t
   fp.block_base = base;
   fp.expert_offsets = expert_offsets;
   fp.n_kept = n_kept;
-  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
-  moe::ScatterParams sp{cfg->T, cfg->E, cfg->top_k, fp.capacity, expert_ids, base,
-                        expert_offsets, row_to_assign, assign_to_row};
-  MOE_TRY(hip_ok(moe::launch_scatter(sp, stream), "scatter kernel"));
+  moe::ScatterParams sp{cfg->T, cfg->E, cfg->top_k, fp.capacity, moe::route_tile(cfg->T),
+                        expert_ids, base, expert_offsets, row_to_assign, assign_to_row};
+  MOE_TRY(launch_permutation(fp, sp, stream));
   return ok();
 }
 
@@ -707,10 +719,9 @@ static moe_status forward_launch(const moe_config* cfg, const void* x, const flo
   fp.block_base = at<int32_t>(workspace, L.block_base);
   fp.expert_offsets = offsets;
   fp.n_kept = at<int32_t>(workspace, L.n_kept);
-  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
-  moe::ScatterParams sp{cfg->T, cfg->E, cfg->top_k, fp.capacity, ids, fp.block_base, offsets,
-                        r2a, a2r};
-  MOE_TRY(hip_ok(moe::launch_scatter(sp, stream), "scatter kernel"));
+  moe::ScatterParams sp{cfg->T, cfg->E, cfg->top_k, fp.capacity, moe::route_tile(cfg->T), ids,
+                        fp.block_base, offsets, r2a, a2r};
+  MOE_TRY(launch_permutation(fp, sp, stream));
 
   void* hbuf = at<void>(workspace, L.hbuf);
   void* y = at<void>(workspace, L.y);
@@ -909,9 +920,9 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const float* norm_
   fp.block_base = at<int32_t>(workspace, L.block_base);
   fp.expert_offsets = offsets;
   fp.n_kept = at<int32_t>(workspace, L.n_kept);
-  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
-  moe::ScatterParams sp{T, E, k, fp.capacity, expert_ids, fp.block_base, offsets, r2a, a2r};
-  MOE_TRY(hip_ok(moe::launch_scatter(sp, stream), "scatter kernel"));
+  moe::ScatterParams sp{T, E, k, fp.capacity, moe::route_tile(T), expert_ids, fp.block_base,
+                        offsets, r2a, a2r};
+  MOE_TRY(launch_permutation(fp, sp, stream));
   MOE_TRY(hip_ok(moe::launch_pad_offsets(E, offsets, padoff, stream), "pad offsets kernel"));
 
   // 2. the logits (the routing kernels rerun; their own routes are not used)

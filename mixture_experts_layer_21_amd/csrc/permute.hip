@@ -27,8 +27,9 @@ __global__ __launch_bounds__(256) void hist_kernel(int T, int E, int k, const in
   for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
   __syncthreads();
   const int b = blockIdx.x;
-  const int a0 = b * kRouteTile * k;
-  const int a1 = min(T, (b + 1) * kRouteTile) * k;
+  const int tile = route_tile(T);
+  const int a0 = b * tile * k;
+  const int a1 = min(T, (b + 1) * tile) * k;
   for (int a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
     const int e = ids[a];
     if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);  // out-of-range IDs are ignored
@@ -157,8 +158,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(ScatterParams p) {
   __syncthreads();
   int nbits = 1;
   while ((1 << nbits) < p.E) ++nbits;
-  const int a0 = b * kRouteTile * p.k;
-  const int a1 = min(p.T, (b + 1) * kRouteTile) * p.k;
+  const int a0 = b * p.tile * p.k;
+  const int a1 = min(p.T, (b + 1) * p.tile) * p.k;
   const uint64_t below = lanemask_lt();
   for (int c = a0; c < a1; c += 64) {
     const int a = c + (int)threadIdx.x;
@@ -185,6 +186,141 @@ __global__ __launch_bounds__(64) void scatter_kernel(ScatterParams p) {
         p.row_to_assign[row] = a;
       } else {
         p.assign_to_row[a] = -1;
+      }
+    }
+  }
+}
+
+// Small batches: column_scan_kernel, expert_scan_kernel and scatter_kernel
+// in one workgroup of 16 waves (one launch instead of three).  Each expert's
+// tile bases are kept in LDS; the sums of P_e, z and the valid tokens run
+// sequentially in tile order and the balance sum in expert order, so the
+// results are deterministic (they may differ from the multi-block kernels'
+// tree order in the last bits of the float aux values only; counts,
+// offsets and the permutation are identical).
+constexpr int kSmallThreads = 1024, kSmallWaves = kSmallThreads / 64;
+constexpr int kSmallBaseInts = 8192;  // nblk * E entries of the tile bases
+
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(FinalizeParams p,
+                                                                      ScatterParams sp) {
+  __shared__ int base[kSmallBaseInts];
+  __shared__ int offs[kMaxExperts + 1];
+  __shared__ int cnt_lds[kMaxExperts];
+  __shared__ float pe_lds[kMaxExperts];
+  __shared__ int run[kSmallWaves][kMaxExperts];
+  __shared__ float s_nv;
+  const int tid = threadIdx.x, E = p.E, nblk = p.nblk;
+  // 1. per expert: tile bases, count, sum of the P_e partials (tile order)
+  if (tid < E) {
+    const int32_t* h = p.hist + (size_t)tid * nblk;
+    int cnt = 0;
+    for (int b = 0; b < nblk; ++b) {
+      base[tid * nblk + b] = cnt;
+      cnt += h[b];
+    }
+    float ps = 0.f;
+    if (p.pe_part)
+      for (int b = 0; b < nblk; ++b) ps += p.pe_part[(size_t)tid * nblk + b];
+    cnt_lds[tid] = cnt;
+    pe_lds[tid] = ps;
+  }
+  if (tid == 0) {
+    int nv = p.T;
+    if (p.valid_part) {
+      nv = 0;
+      for (int b = 0; b < nblk; ++b) nv += p.valid_part[b];
+    }
+    s_nv = (float)nv;
+  }
+  __syncthreads();
+  const float nv = s_nv;
+  if (tid < E) {
+    const int cnt = cnt_lds[tid];
+    p.counts_ws[tid] = cnt;
+    if (p.counts) p.counts[tid] = cnt;
+    if (p.pe_part) {
+      const float pe = nv > 0.f ? pe_lds[tid] / nv : 0.f;
+      pe_lds[tid] = pe;
+      p.pe_ws[tid] = pe;
+      if (p.mean_prob) p.mean_prob[tid] = pe;
+    }
+  }
+  // 2. wave 0: capacity clip and the exclusive scan of the kept counts
+  // (lane l holds experts 4l .. 4l+3), expert offsets, n_kept, aux losses
+  if (tid < 64) {
+    int v[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * tid + j;
+      const int c = e < E ? cnt_lds[e] : 0;
+      v[j] = p.capacity > 0 ? min(c, p.capacity) : c;
+      sum += v[j];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (tid >= d) incl += o;
+    }
+    int at = incl - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * tid + j;
+      if (e < E) offs[e] = at;
+      at += v[j];
+    }
+    if (tid == 63) offs[E] = incl;
+  }
+  __syncthreads();
+  if (p.expert_offsets && tid <= E) p.expert_offsets[tid] = offs[tid];
+  if (p.n_kept && tid == 0) *p.n_kept = offs[E];
+  if (p.aux && tid == 0) {
+    const float inv = nv > 0.f ? 1.0f / (nv * (float)p.k) : 0.f;
+    float bal = 0.f, z = 0.f;
+    for (int e = 0; e < E; ++e) bal += ((float)cnt_lds[e] * inv) * pe_lds[e];
+    for (int b = 0; b < nblk; ++b) z += p.z_part[b];
+    p.aux[0] = (float)E * bal;
+    p.aux[1] = nv > 0.f ? z / nv : 0.f;
+  }
+  if (!sp.ids) return;
+  // 3. scatter: wave w ranks the assignments of tiles w, w + 16, ... in
+  // order (as scatter_kernel does, its running counts in LDS row w)
+  const int wave = tid >> 6, lane = tid & 63;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t below = lanemask_lt();
+  int* r = run[wave];
+  for (int b = wave; b < nblk; b += kSmallWaves) {
+    for (int e = lane; e < E; e += 64) r[e] = base[e * nblk + b];
+    __builtin_amdgcn_wave_barrier();
+    const int a0 = b * sp.tile * sp.k;
+    const int a1 = min(sp.T, (b + 1) * sp.tile) * sp.k;
+    for (int c = a0; c < a1; c += 64) {
+      const int a = c + lane;
+      const int e_in = a < a1 ? sp.ids[a] : -1;
+      const bool in_range = (unsigned)e_in < (unsigned)E;
+      const bool valid = a < a1 && in_range;
+      const int e = valid ? e_in : 0;
+      if (a < a1 && !in_range) sp.assign_to_row[a] = -1;  // out-of-range IDs are dropped
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (e >> bit) & 1;
+        const uint64_t bb = __ballot(set);
+        peers &= set ? bb : ~bb;
+      }
+      const int rank = valid ? r[e] + __popcll(peers & below) : 0;
+      __builtin_amdgcn_wave_barrier();  // all of the wave's reads of r[] precede the writes
+      if (valid && (peers & below) == 0) r[e] += __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        const bool keep = p.capacity <= 0 || rank < p.capacity;
+        if (keep) {
+          const int row = offs[e] + rank;
+          sp.assign_to_row[a] = row;
+          sp.row_to_assign[row] = a;
+        } else {
+          sp.assign_to_row[a] = -1;
+        }
       }
     }
   }
@@ -230,6 +366,16 @@ hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+bool permute_fits_one_block(int T, int E, int k) {
+  return (long long)route_blocks(T) * E <= kSmallBaseInts && (long long)T * k <= 8192;
+}
+
+hipError_t launch_permute_small(const FinalizeParams& fp, const ScatterParams& sp,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), 0, s, fp, sp);
   return hipGetLastError();
 }
 

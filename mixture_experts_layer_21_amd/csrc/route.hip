@@ -355,10 +355,10 @@ __device__ __forceinline__ float sqrt_softplus(float h) {
 // weights; per-block P_e and z partials and the expert histogram.
 __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p) {
   __shared__ SelectSmem sm;
-  const int blk = blockIdx.x, t0 = blk * RT;
+  const int blk = blockIdx.x, t0 = blk * p.tile;
   const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
   const int E = p.E, k = p.k;
-  const int nt = min(RT, p.T - t0);
+  const int nt = min(p.tile, p.T - t0);
   for (int e = threadIdx.x; e < E; e += SEL_THREADS) sm.hist[e] = 0;
   {
     const int ks = p.ksplit;
@@ -609,7 +609,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
 hipError_t launch_route(const RouteParams& p, hipStream_t s) {
   const int NT = (p.E + 15) / 16;
   const int NTB = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
-  const dim3 grid(route_blocks(p.T), (NT + NTB - 1) / NTB, p.ksplit), block(NTHREADS);
+  const dim3 grid(logits_blocks(p.T), (NT + NTB - 1) / NTB, p.ksplit), block(NTHREADS);
   if (route_tiled(p.T, p.E, p.act_bf16 && p.router_bf16)) {
     const dim3 tgrid((p.T + kRouteTiledM - 1) / kRouteTiledM,
                      (p.E + kRouteTiledN - 1) / kRouteTiledN, p.ksplit);
