@@ -114,6 +114,13 @@ __device__ bool find_tile(const GemmParams& p, int max_mtiles, Tile& t, int* s_s
   return true;
 }
 
+// Most pieces a split tail tile is cut into (at most 16: the reduce kernels
+// hold one vector per piece).
+#ifndef MOE_TAIL_MAX_PIECES
+#define MOE_TAIL_MAX_PIECES 16
+#endif
+static_assert(MOE_TAIL_MAX_PIECES >= 1 && MOE_TAIL_MAX_PIECES <= 16, "tail pieces");
+
 // Column tiles per rasterisation band of the large-tile kernel.
 #ifndef MOE_BAND
 #define MOE_BAND 4
@@ -166,7 +173,7 @@ __device__ bool decode_job(const GemmParams& p, int tail_slots, int* s_scan, Til
     if (tail_slots > 0) {
       nfull = ax / tail_slots * tail_slots;
       r = ax - nfull;
-      nsplit = r > 0 ? min(min(tail_slots / r, 16), nk) : 1;
+      nsplit = r > 0 ? min(min(tail_slots / r, MOE_TAIL_MAX_PIECES), nk) : 1;
       if (nsplit < 2) {
         nfull = ax;
         r = 0;
@@ -974,12 +981,26 @@ hipError_t launch_f32(const GemmParams& p, hipStream_t s) {
 #ifndef MOE_LARGE_MIN_ROWS
 #define MOE_LARGE_MIN_ROWS 192
 #endif
-// Smaller groups of 64 or more rows on average: 128-row tiles.
+// Smaller groups of 64 or more rows on average: 128-row tiles, three stages
+// (on the capacity-limited Switch-shaped layer, whose short k-loops wait on
+// HBM, 15% ahead of two; 256-column down tiles 9% ahead of 512).
 #ifndef MOE_GU_CFG_M
-#define MOE_GU_CFG_M 128, 512, 32, 2, 2, 8
+#define MOE_GU_CFG_M 128, 512, 32, 3, 2, 8
 #endif
 #ifndef MOE_DN_CFG_M
-#define MOE_DN_CFG_M 128, 512, 32, 2, 2, 8
+#define MOE_DN_CFG_M 128, 256, 64, 3, 2, 8
+#endif
+
+// Groups under this many rows on average use the 32-row register-staged
+// tiles (gate/up: MOE_SMALL_GU_BN output columns, down: MOE_SMALL_DN_BN).
+#ifndef MOE_SMALL_MAX_ROWS
+#define MOE_SMALL_MAX_ROWS 64
+#endif
+#ifndef MOE_SMALL_GU_BN
+#define MOE_SMALL_GU_BN 128
+#endif
+#ifndef MOE_SMALL_DN_BN
+#define MOE_SMALL_DN_BN 256
 #endif
 
 // Offsets inside the buffer resources of the large-tile kernel are 32-bit, and
@@ -1004,9 +1025,9 @@ hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s) 
   // tiles so that MFMA work is not spent on padding.
   const int rows = p.expert_offsets ? p.max_rows : p.T;
   const int groups = p.expert_offsets ? p.n_groups : 1;
-  if ((long long)rows < 64LL * groups) {
-    if ((err = launch_bf16<32, 128, 1, true>(p, s)) != hipSuccess) return err;
-    return launch_bf16<32, 256, 1, false>(p, s);
+  if ((long long)rows < (long long)MOE_SMALL_MAX_ROWS * groups) {
+    if ((err = launch_bf16<32, MOE_SMALL_GU_BN, 1, true>(p, s)) != hipSuccess) return err;
+    return launch_bf16<32, MOE_SMALL_DN_BN, 1, false>(p, s);
   }
   using GU = DmaCfg<MOE_GU_CFG, true>;
   using DN = DmaCfg<MOE_DN_CFG, false>;

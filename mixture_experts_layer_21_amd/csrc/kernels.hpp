@@ -8,11 +8,15 @@
 namespace moe {
 
 // Tokens per routing block; also the granularity of the per-block expert
-// histograms that the permutation scans (route_tile below: small batches use
-// 8-token blocks, one token per wave of the selection kernel).
+// histograms that the permutation scans (route_tile below: batches of up to
+// kSmallRouteMaxT tokens use 8-token blocks, one token per wave of the
+// selection kernel, so that more tokens are in flight per CU).
 constexpr int kRouteTile = 32;
 constexpr int kSmallRouteTile = 8;
-constexpr int kSmallRouteMaxT = 1024;
+#ifndef MOE_SMALL_ROUTE_MAX_T
+#define MOE_SMALL_ROUTE_MAX_T 1024
+#endif
+constexpr int kSmallRouteMaxT = MOE_SMALL_ROUTE_MAX_T;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxGroups = 64;

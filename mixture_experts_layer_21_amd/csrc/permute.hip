@@ -208,29 +208,57 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(FinalizePa
   __shared__ int cnt_lds[kMaxExperts];
   __shared__ float pe_lds[kMaxExperts];
   __shared__ int run[kSmallWaves][kMaxExperts];
-  __shared__ float s_nv;
+  __shared__ float s_nv, s_z;
   const int tid = threadIdx.x, E = p.E, nblk = p.nblk;
-  // 1. per expert: tile bases, count, sum of the P_e partials (tile order)
+  const int wave = tid >> 6, lane = tid & 63;
+  // 1. thread e: expert e's tile bases, count and P_e sum, in tile order;
+  // the last thread: valid tokens and the z sum.  Loads go 16 at a time so
+  // that their latencies overlap.
+  constexpr int U = 16;
   if (tid < E) {
-    const int32_t* h = p.hist + (size_t)tid * nblk;
-    int cnt = 0;
-    for (int b = 0; b < nblk; ++b) {
-      base[tid * nblk + b] = cnt;
-      cnt += h[b];
-    }
+    int total = 0;
     float ps = 0.f;
-    if (p.pe_part)
-      for (int b = 0; b < nblk; ++b) ps += p.pe_part[(size_t)tid * nblk + b];
-    cnt_lds[tid] = cnt;
+    for (int b0 = 0; b0 < nblk; b0 += U) {
+      int v[U];
+      float q[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool in = b0 + u < nblk;
+        v[u] = in ? p.hist[(size_t)tid * nblk + b0 + u] : 0;
+        q[u] = (in && p.pe_part) ? p.pe_part[(size_t)tid * nblk + b0 + u] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b0 + u >= nblk) break;
+        base[tid * nblk + b0 + u] = total;
+        total += v[u];
+        ps += q[u];
+      }
+    }
+    cnt_lds[tid] = total;
     pe_lds[tid] = ps;
   }
-  if (tid == 0) {
-    int nv = p.T;
-    if (p.valid_part) {
-      nv = 0;
-      for (int b = 0; b < nblk; ++b) nv += p.valid_part[b];
+  if (tid == kSmallThreads - 1) {
+    int nv = 0;
+    float z = 0.f;
+    for (int b0 = 0; b0 < nblk; b0 += U) {
+      int v[U];
+      float q[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool in = b0 + u < nblk;
+        v[u] = (in && p.valid_part) ? p.valid_part[b0 + u] : 0;
+        q[u] = (in && p.z_part) ? p.z_part[b0 + u] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b0 + u >= nblk) break;
+        nv += v[u];
+        z += q[u];
+      }
     }
-    s_nv = (float)nv;
+    s_nv = (float)(p.valid_part ? nv : p.T);
+    s_z = z;
   }
   __syncthreads();
   const float nv = s_nv;
@@ -276,16 +304,14 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(FinalizePa
   if (p.n_kept && tid == 0) *p.n_kept = offs[E];
   if (p.aux && tid == 0) {
     const float inv = nv > 0.f ? 1.0f / (nv * (float)p.k) : 0.f;
-    float bal = 0.f, z = 0.f;
+    float bal = 0.f;
     for (int e = 0; e < E; ++e) bal += ((float)cnt_lds[e] * inv) * pe_lds[e];
-    for (int b = 0; b < nblk; ++b) z += p.z_part[b];
     p.aux[0] = (float)E * bal;
-    p.aux[1] = nv > 0.f ? z / nv : 0.f;
+    p.aux[1] = nv > 0.f ? s_z / nv : 0.f;
   }
   if (!sp.ids) return;
   // 3. scatter: wave w ranks the assignments of tiles w, w + 16, ... in
   // order (as scatter_kernel does, its running counts in LDS row w)
-  const int wave = tid >> 6, lane = tid & 63;
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t below = lanemask_lt();
@@ -370,7 +396,7 @@ hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s) {
 }
 
 bool permute_fits_one_block(int T, int E, int k) {
-  return (long long)route_blocks(T) * E <= kSmallBaseInts && (long long)T * k <= 8192;
+  return (long long)route_blocks(T) * E <= kSmallBaseInts && (long long)T * k <= 4096;
 }
 
 hipError_t launch_permute_small(const FinalizeParams& fp, const ScatterParams& sp,

@@ -11,10 +11,11 @@
 //  * route_logits_kernel: the [T x E] logits as split-K partial sums.  A
 //    256-thread block covers 32 tokens x up to 64 experts x one K range; each
 //    wave runs 16x16 MFMA tiles (bf16 x bf16: 16x16x32 bf16, products exact;
-//    any fp32 operand: 16x16x4 fp32).  Waves sharing an expert tile split the
+//    bf16 x with fp32 W: the same MFMAs on an exact three-term bf16 split of
+//    W; fp32 x: 16x16x4 fp32).  Waves sharing an expert tile split the
 //    k-steps and are summed through LDS in a fixed order.
 //  * route_select_kernel: the block first adds the K-split partials of its
-//    32 tokens in split order into LDS; then one wave per token does the
+//    tokens (route_tile: 8 or 32) in split order into LDS; then one wave per token does the
 //    scores, group limit, k arg-max rounds (ties to the lower expert index)
 //    and weights.  Lane l holds experts l, l+64, l+128, l+192.  Every
 //    reduction has a fixed order, so results are bit-reproducible.
@@ -46,9 +47,31 @@ __device__ __forceinline__ f32x4 load4(const uint16_t* p) {
 // k = 8*(l/16) .. +7; 16x16x4 fp32 (four per 16-wide step): lane l holds row
 // l%16 and k = 4*(l/16) + j in the j-th MFMA.  Output element i of lane l is
 // row 4*(l/16) + i, column l%16.
-template <typename XT, typename WT, bool BF16>
+// Exact split of eight fp32 values into three bf16 terms, w = hi + mid + lo:
+// hi is w rounded to bf16, mid the rounded remainder, lo the remainder of
+// that, which has at most eight significant bits and is therefore exact in
+// bf16 (for |w| far above the bf16 underflow threshold, as router weights
+// are).  A bf16 x times each term is exact in fp32.
+__device__ __forceinline__ void split3_bf16(const f32x4 a, const f32x4 b, bf16x8& hi, bf16x8& mid,
+                                            bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float w = i < 4 ? a[i] : b[i - 4];
+    const __bf16 h = static_cast<__bf16>(w);
+    const float r = w - static_cast<float>(h);
+    const __bf16 m = static_cast<__bf16>(r);
+    hi[i] = h;
+    mid[i] = m;
+    lo[i] = static_cast<__bf16>(r - static_cast<float>(m));
+  }
+}
+
+// SPLIT3 (bf16 x, fp32 W): each fp32 weight is split into three bf16 terms
+// and the products go through 16x16x32 bf16 MFMAs (exact products, fp32
+// sums), a sixteenth of the matrix-core time of 16x16x4 fp32 MFMAs each.
+template <typename XT, typename WT, bool BF16, bool SPLIT3 = false>
 __global__ __launch_bounds__(NTHREADS) void route_logits_kernel(RouteParams p) {
-  constexpr int KSTEP = BF16 ? 32 : 16;
+  constexpr int KSTEP = (BF16 || SPLIT3) ? 32 : 16;
   const XT* x = static_cast<const XT*>(p.x);
   const WT* w = static_cast<const WT*>(p.w_router);
   const int NT = (p.E + 15) / 16;
@@ -95,6 +118,49 @@ __global__ __launch_bounds__(NTHREADS) void route_logits_kernel(RouteParams p) {
         const bf16x8 B = *reinterpret_cast<const bf16x8*>(pw + k0);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc1, 0, 0, 0);
+      }
+    } else if constexpr (SPLIT3) {
+      const uint16_t* pa = reinterpret_cast<const uint16_t*>(x) + (size_t)ta * p.D + kq * 8;
+      const uint16_t* pb = reinterpret_cast<const uint16_t*>(x) + (size_t)tb * p.D + kq * 8;
+      const float* pw = reinterpret_cast<const float*>(w) + (size_t)e * p.D + kq * 8;
+      int s = s0 + phase;
+      // Two k-steps in flight per iteration.
+      for (; s + WPN < s1; s += 2 * WPN) {
+        bf16x8 A0[2], A1[2];
+        f32x4 W0[2], W1[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int k0 = (s + u * WPN) * 32;
+          A0[u] = *reinterpret_cast<const bf16x8*>(pa + k0);
+          A1[u] = *reinterpret_cast<const bf16x8*>(pb + k0);
+          W0[u] = *reinterpret_cast<const f32x4*>(pw + k0);
+          W1[u] = *reinterpret_cast<const f32x4*>(pw + k0 + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8 h, m, l;
+          split3_bf16(W0[u], W1[u], h, m, l);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[u], h, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[u], h, acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[u], m, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[u], m, acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[u], l, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[u], l, acc1, 0, 0, 0);
+        }
+      }
+      for (; s < s1; s += WPN) {
+        const int k0 = s * 32;
+        const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(pa + k0);
+        const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(pb + k0);
+        bf16x8 h, m, l;
+        split3_bf16(*reinterpret_cast<const f32x4*>(pw + k0),
+                    *reinterpret_cast<const f32x4*>(pw + k0 + 4), h, m, l);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, h, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, h, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, m, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, m, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, l, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, l, acc1, 0, 0, 0);
       }
     } else {
       const XT* pa = x + (size_t)ta * p.D + kq * 4;
@@ -336,8 +402,9 @@ __device__ __forceinline__ V pick4(const V (&a)[4], int j) {
   return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
 }
 
+template <int TILE>
 struct SelectSmem {
-  float lg[RT * kMaxExperts];      // summed logits of the block's tokens, row stride E
+  float lg[TILE * kMaxExperts];    // summed logits of the block's tokens, row stride E
   float pe[SEL_WAVES][kMaxExperts];
   float zw[SEL_WAVES];
   int nv[SEL_WAVES];
@@ -353,8 +420,9 @@ __device__ __forceinline__ float sqrt_softplus(float h) {
 // order, into LDS (all threads, 16-byte loads, up to 16 loads in flight).
 // Phase 2: one wave per token: scores, group limit, k arg-max rounds,
 // weights; per-block P_e and z partials and the expert histogram.
+template <int TILE>
 __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p) {
-  __shared__ SelectSmem sm;
+  __shared__ SelectSmem<TILE> sm;
   const int blk = blockIdx.x, t0 = blk * p.tile;
   const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
   const int E = p.E, k = p.k;
@@ -617,7 +685,7 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s) {
   } else if (p.act_bf16 && p.router_bf16) {
     hipLaunchKernelGGL((route_logits_kernel<uint16_t, uint16_t, true>), grid, block, 0, s, p);
   } else if (p.act_bf16) {
-    hipLaunchKernelGGL((route_logits_kernel<uint16_t, float, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((route_logits_kernel<uint16_t, float, false, true>), grid, block, 0, s, p);
   } else if (p.router_bf16) {
     hipLaunchKernelGGL((route_logits_kernel<float, uint16_t, false>), grid, block, 0, s, p);
   } else {
@@ -625,7 +693,12 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_select_kernel, dim3(route_blocks(p.T)), dim3(SEL_THREADS), 0, s, p);
+  if (p.tile == kSmallRouteTile)
+    hipLaunchKernelGGL(route_select_kernel<kSmallRouteTile>, dim3(route_blocks(p.T)),
+                       dim3(SEL_THREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL(route_select_kernel<kRouteTile>, dim3(route_blocks(p.T)),
+                       dim3(SEL_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
