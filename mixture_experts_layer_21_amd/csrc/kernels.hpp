@@ -104,7 +104,11 @@ struct GemmParams {
 // Split-K tail bookkeeping of the large-tile grouped GEMM.
 constexpr int kXcds = 8;
 constexpr int kTailSlots = 64;                       // partial tiles per XCD
-constexpr size_t kTailSlotBytes = (size_t)256 * 256 * 4;  // one fp32 256x256 tile
+#ifndef MOE_TAIL_SLOT_ROWS
+#define MOE_TAIL_SLOT_ROWS 256
+#endif
+// one fp32 tile of the largest grouped-GEMM tile (MOE_TAIL_SLOT_ROWS x 256)
+constexpr size_t kTailSlotBytes = (size_t)MOE_TAIL_SLOT_ROWS * 256 * 4;
 // Slots of kTailSlotBytes hold the partial tiles of every kernel; slots of
 // 32 KB those of the 32-row (decode-sized) kernels only.
 constexpr size_t kSmallTailSlotBytes = (size_t)32 * 256 * 4;
@@ -294,6 +298,9 @@ inline int logits_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
 inline bool route_tiled(int T, int E, bool bf16_mfma) { return bf16_mfma && E >= 128 && T >= 1024; }
 constexpr int kRouteTiledM = 64, kRouteTiledN = 256;
 
+#ifndef MOE_ROUTE_KSPLIT_MAX
+#define MOE_ROUTE_KSPLIT_MAX 16
+#endif
 // K-split of the router GEMM: enough blocks to fill the GPU while every split
 // keeps at least four k-steps (32 elements each for bf16, 16 for fp32); the
 // tiled kernel keeps at least eight.
@@ -310,7 +317,7 @@ inline int route_ksplit(int T, int D, int E, bool bf16_mfma) {
   const int NTB = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
   const long long blocks = (long long)logits_blocks(T) * ((NT + NTB - 1) / NTB);
   int ks = 1;
-  while (blocks * ks < 1024 && ks * 2 * 4 <= nsteps && ks < 16) ks *= 2;
+  while (blocks * ks < 1024 && ks * 2 * 4 <= nsteps && ks < MOE_ROUTE_KSPLIT_MAX) ks *= 2;
   return ks;
 }
 
