@@ -296,11 +296,29 @@ inline int logits_blocks(int T) { return (T + kRouteTile - 1) / kRouteTile; }
 // The LDS-tiled router GEMM (64 tokens x 256 experts per block) serves bf16
 // routers with many experts and tokens; the others use the per-wave kernel.
 inline bool route_tiled(int T, int E, bool bf16_mfma) { return bf16_mfma && E >= 128 && T >= 1024; }
+
+// Routers of at most kFusedMaxE experts and MOE_ROUTE_FUSED_MAX_BYTES of
+// weights run as one fused kernel (logits over all of K and selection in one
+// block per token tile); larger ones as the split-K logits kernel and the
+// selection kernel.  Each fused block reads the whole router, so the bound
+// keeps that read short next to the block's x rows.
+constexpr int kFusedMaxE = 64;
+#ifndef MOE_ROUTE_FUSED_MAX_BYTES
+#define MOE_ROUTE_FUSED_MAX_BYTES (512 << 10)
+#endif
+inline bool route_fused(int D, int E, bool router_bf16) {
+  return E <= kFusedMaxE &&
+         (long long)E * D * (router_bf16 ? 2 : 4) <= (long long)MOE_ROUTE_FUSED_MAX_BYTES;
+}
 constexpr int kRouteTiledM = 64, kRouteTiledN = 256;
 
 #ifndef MOE_ROUTE_KSPLIT_MAX
 #define MOE_ROUTE_KSPLIT_MAX 16
 #endif
+// The selection kernel adds the splits with a compile-time count: 1 to 16.
+static_assert(MOE_ROUTE_KSPLIT_MAX >= 1 && MOE_ROUTE_KSPLIT_MAX <= 16 &&
+                  (MOE_ROUTE_KSPLIT_MAX & (MOE_ROUTE_KSPLIT_MAX - 1)) == 0,
+              "MOE_ROUTE_KSPLIT_MAX must be a power of two of at most 16");
 // K-split of the router GEMM: enough blocks to fill the GPU while every split
 // keeps at least four k-steps (32 elements each for bf16, 16 for fp32); the
 // tiled kernel keeps at least eight.

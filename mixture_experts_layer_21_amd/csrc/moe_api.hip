@@ -135,7 +135,9 @@ Layout layout_of(const moe_config* c, size_t tail_slot_bytes = moe::kTailSlotByt
   L.counts = take(E * 4);
   L.aux = take(2 * 4);
   const bool mfma16 = c->act_dtype == MOE_BF16 && c->router_dtype == MOE_BF16;
-  L.logits = take((size_t)moe::route_ksplit(c->T, c->D, c->E, mfma16) * T * E * 4);
+  L.logits = take(moe::route_fused(c->D, c->E, c->router_dtype == MOE_BF16)
+                      ? 0
+                      : (size_t)moe::route_ksplit(c->T, c->D, c->E, mfma16) * T * E * 4);
   L.hist = take(nblk * E * 4);
   L.pe_part = take(nblk * E * 4);
   L.z_part = take(nblk * 4);

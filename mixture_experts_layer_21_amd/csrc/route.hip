@@ -7,7 +7,9 @@
 // selection-only per-expert bias), with the NeMo Gate switches score_func,
 // n_groups / topk_groups and route_scale.
 //
-// Two kernels:
+// Routers of at most 64 experts whose weights fit route_fused run as one
+// kernel, route_fused_kernel (below): each block computes its tokens' logits
+// over all of K and selects from them.  Larger routers take two kernels:
 //  * route_logits_kernel: the [T x E] logits as split-K partial sums.  A
 //    256-thread block covers 32 tokens x up to 64 experts x one K range; each
 //    wave runs 16x16 MFMA tiles (bf16 x bf16: 16x16x32 bf16, products exact;
@@ -374,11 +376,12 @@ __device__ __forceinline__ void top2_step(float& a1, float& a2) {
 // One arg-max round over the wave: among the keys of this lane's four slots
 // (slot j is expert lane + 64 j), the largest key wins; equal keys go to the
 // lower expert index.  Returns the winner's lane and slot (wave-uniform).
-__device__ __forceinline__ void wave_argmax_key(const uint32_t (&key)[4], int& wl, int& wj) {
+template <int NS>
+__device__ __forceinline__ void wave_argmax_key(const uint32_t (&key)[NS], int& wl, int& wj) {
   uint32_t lk = key[0];
   int lj = 0;
 #pragma unroll
-  for (int j = 1; j < 4; ++j)
+  for (int j = 1; j < NS; ++j)
     if (key[j] > lk) {
       lk = key[j];
       lj = j;
@@ -387,7 +390,7 @@ __device__ __forceinline__ void wave_argmax_key(const uint32_t (&key)[4], int& w
   wl = 0;
   wj = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NS; ++j) {
     const uint64_t m = __ballot(lk == M && lj == j);
     if (m) {
       wl = __ffsll((unsigned long long)m) - 1;
@@ -397,9 +400,18 @@ __device__ __forceinline__ void wave_argmax_key(const uint32_t (&key)[4], int& w
   }
 }
 
-template <typename V>
-__device__ __forceinline__ V pick4(const V (&a)[4], int j) {
-  return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
+// Slot j of lane l of a (j and l wave-uniform): every slot is read from lane
+// l and the choice is made on the scalar side, so that no register array is
+// indexed at run time.
+template <int NS>
+__device__ __forceinline__ float readlane_slot(const float (&a)[NS], int j, int l) {
+  float v = readlane_f(a[0], l);
+#pragma unroll
+  for (int i = 1; i < NS; ++i) {
+    const float u = readlane_f(a[i], l);
+    if (j == i) v = u;
+  }
+  return v;
 }
 
 template <int TILE>
@@ -416,69 +428,31 @@ __device__ __forceinline__ float sqrt_softplus(float h) {
   return sqrtf(fmaxf(h, 0.f) + log1pf(expf(-fabsf(h))));
 }
 
-// Phase 1: the block's [RT x E] logits, the K-split partials added in split
-// order, into LDS (all threads, 16-byte loads, up to 16 loads in flight).
-// Phase 2: one wave per token: scores, group limit, k arg-max rounds,
-// weights; per-block P_e and z partials and the expert histogram.
-template <int TILE>
-__global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p) {
-  __shared__ SelectSmem<TILE> sm;
-  const int blk = blockIdx.x, t0 = blk * p.tile;
+// The biases of the experts this lane holds in the selection (lane + 64 j),
+// loaded at the start of a kernel so that the loads overlap its first phase.
+__device__ __forceinline__ void load_biases(const RouteParams p, float (&lb)[4], float (&sb)[4]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    lb[j] = (e < p.E && p.logit_bias) ? p.logit_bias[e] : 0.f;
+    sb[j] = (e < p.E && p.select_bias) ? p.select_bias[e] : 0.f;
+  }
+}
+
+// Selection of a block's nt tokens (t0 ..) from their logits in sm.lg (row
+// stride E), published with sm.hist zeroed by a barrier before the call: one
+// wave per token computes the scores, group limit, k arg-max rounds (ties to
+// the lower expert index) and weights; then the block's P_e and z partial
+// sums and expert histogram go to column blk of the per-block arrays.  Lane
+// l holds experts l, l+64, l+128, l+192.  Every reduction has a fixed order,
+// so results are bit-reproducible.
+template <int TILE, int NS>
+__device__ __forceinline__ void select_tokens(const RouteParams p, SelectSmem<TILE>& sm, int blk,
+                                              int t0, int nt, const float (&lb)[4],
+                                              const float (&sb)[4]) {
   const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
   const int E = p.E, k = p.k;
-  const int nt = min(p.tile, p.T - t0);
-  for (int e = threadIdx.x; e < E; e += SEL_THREADS) sm.hist[e] = 0;
-  {
-    const int ks = p.ksplit;
-    const int L = nt * E;
-    const size_t stride = (size_t)p.T * E;
-    const float* base = p.logits_part + (size_t)t0 * E;
-    if ((E & 3) == 0) {
-      const int L4 = L >> 2;
-      const f32x4* b4 = reinterpret_cast<const f32x4*>(base);
-      const size_t s4 = stride >> 2;
-      for (int i0 = threadIdx.x; i0 < L4; i0 += 2 * SEL_THREADS) {
-        const int i1 = i0 + SEL_THREADS;
-        const bool has1 = i1 < L4;
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-        for (int k0 = 0; k0 < ks; k0 += 8) {
-          f32x4 a[8], b[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            if (k0 + u < ks) {
-              a[u] = b4[(k0 + u) * s4 + i0];
-              if (has1) b[u] = b4[(k0 + u) * s4 + i1];
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            if (k0 + u < ks) {
-              s0 = (k0 + u == 0) ? a[u] : s0 + a[u];
-              if (has1) s1 = (k0 + u == 0) ? b[u] : s1 + b[u];
-            }
-          }
-        }
-        *reinterpret_cast<f32x4*>(&sm.lg[4 * i0]) = s0;
-        if (has1) *reinterpret_cast<f32x4*>(&sm.lg[4 * i1]) = s1;
-      }
-    } else {
-      for (int i = threadIdx.x; i < L; i += SEL_THREADS) {
-        float s = 0.f;
-        for (int k0 = 0; k0 < ks; k0 += 8) {
-          float a[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (k0 + u < ks) a[u] = base[(k0 + u) * stride + i];
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (k0 + u < ks) s = (k0 + u == 0) ? a[u] : s + a[u];
-        }
-        sm.lg[i] = s;
-      }
-    }
-  }
-  __syncthreads();
-
   // softmax scores are a distribution over the experts; sigmoid and
   // sqrt-softplus scores are per expert and normalised where a sum is needed.
   const bool per_expert = p.score_func != 0;
@@ -487,16 +461,13 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
   // Group limit with a segmented reduction: groups are aligned runs of gsz
   // lanes in one slot when gsz is a power of two below 64.
   const bool seg_groups = p.n_groups > 1 && gsz < 64 && (gsz & (gsz - 1)) == 0;
-  float lb[4], sb[4];
-  bool ok[4];
+  bool ok[NS];
+  float pacc[NS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    ok[j] = e < E;
-    lb[j] = (ok[j] && p.logit_bias) ? p.logit_bias[e] : 0.f;
-    sb[j] = (ok[j] && p.select_bias) ? p.select_bias[e] : 0.f;
+  for (int j = 0; j < NS; ++j) {
+    ok[j] = lane + 64 * j < E;
+    pacc[j] = 0.f;
   }
-  float pacc[4] = {0.f, 0.f, 0.f, 0.f};
   float zacc = 0.f;
   int nvalid = 0;
 
@@ -510,18 +481,18 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
       continue;
     }
     ++nvalid;
-    float h[4], sc[4], sel[4];
+    float h[NS], sc[NS], sel[NS];
     float mloc = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NS; ++j) {
       h[j] = ok[j] ? sm.lg[tl * E + lane + 64 * j] + lb[j] : -INFINITY;
       mloc = fmaxf(mloc, h[j]);
       if (p.logits_out && ok[j]) p.logits_out[(size_t)t * E + lane + 64 * j] = h[j];
     }
     const float m = wave_max_dpp(mloc);
-    float ex[4], sloc = 0.f;
+    float ex[NS], sloc = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NS; ++j) {
       ex[j] = ok[j] ? expf(h[j] - m) : 0.f;
       sloc += ex[j];
     }
@@ -530,14 +501,14 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
     zacc += lse * lse;
     if (!per_expert) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NS; ++j) {
         sc[j] = ex[j] / S;
         pacc[j] += sc[j];
       }
     } else {
       float ssl = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NS; ++j) {
         if (!ok[j])
           sc[j] = 0.f;
         else
@@ -546,23 +517,25 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
       }
       const float ss = wave_sum_dpp(ssl);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pacc[j] += sc[j] / ss;
+      for (int j = 0; j < NS; ++j) pacc[j] += sc[j] / ss;
     }
     // NaN scores rank as -inf so that every round still picks a valid expert.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NS; ++j) {
       const float v = by_score ? sc[j] + sb[j] : h[j];
       sel[j] = (!ok[j] || v != v) ? -INFINITY : v;
     }
 
-    bool allowed[4] = {ok[0], ok[1], ok[2], ok[3]};
+    bool allowed[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) allowed[j] = ok[j];
     if (p.n_groups > 1) {
       // Group score of every group, then group g's key in lane g.
       uint32_t gkey = 0;
       if (seg_groups) {
-        float a1[4], a2[4];
+        float a1[NS], a2[NS];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NS; ++j) {
           a1[j] = sel[j];
           a2[j] = -INFINITY;
           if (gsz >= 2) top2_step<DPP_XOR1>(a1[j], a2[j]);
@@ -576,10 +549,10 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
         // Group g lives in slot g / (64/gsz), lanes of segment g % (64/gsz).
         const int per_slot = MOE_WAVE / gsz;
         const int g = lane;
-        const int gj = min(g / per_slot, 3), src = (g % per_slot) * gsz;
+        const int gj = min(g / per_slot, NS - 1), src = (g % per_slot) * gsz;
         float gs = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NS; ++j) {
           const float s1 = __shfl(a1[j], src, MOE_WAVE), s2 = __shfl(a2[j], src, MOE_WAVE);
           if (gj == j) gs = p.group_rule == 0 ? s1 + s2 : s1;
         }
@@ -588,7 +561,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
         for (int g = 0; g < p.n_groups; ++g) {
           float a1 = -INFINITY, a2 = -INFINITY;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < NS; ++j) {
             if (ok[j] && (lane + 64 * j) / gsz == g) top2_merge(a1, a2, sel[j], -INFINITY);
           }
 #pragma unroll
@@ -599,7 +572,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
         }
       }
       uint64_t gmask = 0;
-      uint32_t gk[4] = {gkey, 0u, 0u, 0u};
+      uint32_t gk[1] = {gkey};
       for (int r = 0; r < p.topk_groups; ++r) {
         int wl, wj;
         wave_argmax_key(gk, wl, wj);
@@ -607,26 +580,26 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
         if (lane == wl) gk[0] = 0u;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NS; ++j)
         allowed[j] = ok[j] && ((gmask >> ((lane + 64 * j) / gsz)) & 1ull);
     }
 
-    uint32_t key[4];
+    uint32_t key[NS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) key[j] = allowed[j] ? okey(sel[j]) : 0u;
+    for (int j = 0; j < NS; ++j) key[j] = allowed[j] ? okey(sel[j]) : 0u;
     int my_id = 0;
     float my_sc = 0.f;
     for (int r = 0; r < k; ++r) {
       int wl, wj;
       wave_argmax_key(key, wl, wj);
-      const float wsc = readlane_f(pick4(sc, wj), wl);
+      const float wsc = readlane_slot(sc, wj, wl);
       if (lane == r) {
         my_id = wl + 64 * wj;
         my_sc = wsc;
       }
       if (lane == wl) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NS; ++j)
           if (j == wj) key[j] = 0u;
       }
     }
@@ -642,7 +615,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
 
   // Per-block partials, reduced across waves in a fixed order.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NS; ++j) {
     const int e = lane + 64 * j;
     if (e < E) sm.pe[wave][e] = pacc[j];
   }
@@ -672,9 +645,287 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
   }
 }
 
+// select_tokens with as many 64-expert slots per lane as E needs.
+template <int TILE>
+__device__ __forceinline__ void select_slots(const RouteParams p, SelectSmem<TILE>& sm, int blk,
+                                             int t0, int nt, const float (&lb)[4],
+                                             const float (&sb)[4]) {
+  if (p.E <= 64)
+    select_tokens<TILE, 1>(p, sm, blk, t0, nt, lb, sb);
+  else if (p.E <= 128)
+    select_tokens<TILE, 2>(p, sm, blk, t0, nt, lb, sb);
+  else
+    select_tokens<TILE, 4>(p, sm, blk, t0, nt, lb, sb);
+}
+
+// Adds the KS split-K partials of n 16-byte groups of logits (group i of
+// split s at b4[s * s4 + i]) in split order into lg4[i]; each thread takes
+// EPT groups per pass with all their KS * EPT loads in flight (a thread past
+// the end reloads the last group and stores nothing).
+template <int KS, int EPT>
+__device__ __forceinline__ void sum_partials(const f32x4* __restrict__ b4, size_t s4, int n,
+                                             f32x4* lg4) {
+  for (int i0 = threadIdx.x; i0 < n; i0 += EPT * SEL_THREADS) {
+    f32x4 a[EPT][KS];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int i = min(i0 + u * SEL_THREADS, n - 1);
+#pragma unroll
+      for (int sp = 0; sp < KS; ++sp) a[u][sp] = b4[sp * s4 + i];
+    }
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      f32x4 v = a[u][0];
+#pragma unroll
+      for (int sp = 1; sp < KS; ++sp) v += a[u][sp];
+      if (i0 + u * SEL_THREADS < n) lg4[i0 + u * SEL_THREADS] = v;
+    }
+  }
+}
+
+// The block's [tile x E] logits: the K-split partials (a power of two, at
+// most 16) added in split order into LDS, all of a group's loads in flight;
+// then the selection above.
+template <int TILE>
+__global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p) {
+  __shared__ SelectSmem<TILE> sm;
+  const int blk = blockIdx.x, t0 = blk * TILE;
+  const int E = p.E;
+  const int nt = min(TILE, p.T - t0);
+  float lb[4], sb[4];
+  load_biases(p, lb, sb);
+  for (int e = threadIdx.x; e < E; e += SEL_THREADS) sm.hist[e] = 0;
+  {
+    const int ks = p.ksplit;
+    const int L = nt * E;
+    const size_t stride = (size_t)p.T * E;
+    const float* base = p.logits_part + (size_t)t0 * E;
+    if ((E & 3) == 0) {
+      const f32x4* b4 = reinterpret_cast<const f32x4*>(base);
+      f32x4* lg4 = reinterpret_cast<f32x4*>(sm.lg);
+      const size_t s4 = stride >> 2;
+      const int L4 = L >> 2;
+      switch (ks) {
+        case 1: sum_partials<1, 4>(b4, s4, L4, lg4); break;
+        case 2: sum_partials<2, 4>(b4, s4, L4, lg4); break;
+        case 4: sum_partials<4, 4>(b4, s4, L4, lg4); break;
+        case 8: sum_partials<8, 2>(b4, s4, L4, lg4); break;
+        default: sum_partials<16, 1>(b4, s4, L4, lg4); break;
+      }
+    } else {
+      for (int i = threadIdx.x; i < L; i += SEL_THREADS) {
+        float s = 0.f;
+        for (int k0 = 0; k0 < ks; k0 += 8) {
+          float a[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (k0 + u < ks) a[u] = base[(k0 + u) * stride + i];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (k0 + u < ks) s = (k0 + u == 0) ? a[u] : s + a[u];
+        }
+        sm.lg[i] = s;
+      }
+    }
+  }
+  __syncthreads();
+  select_slots<TILE>(p, sm, blk, t0, nt, lb, sb);
+}
+
+// ---------------------------------------------------------------------------
+// Fused routing for routers small enough to stream through one block (at most
+// kFusedMaxE experts, route_fused below): a block owns its tile of tokens,
+// computes their logits against every expert over the whole of K, and selects
+// from them, in one launch and with no split-K partials in HBM.  The waves
+// split the k-steps evenly; each holds the block's whole [tile x E] output as
+// 16x16 MFMA tiles (token tile ts, expert tile et).  The waves' partial tiles
+// go through LDS and are added in wave (= K) order.
+// MODE 0: bf16 x and W, 16x16x32 bf16; 1: bf16 x and fp32 W on the exact
+// three-term bf16 split of W (three MFMAs per tile and k-step, products
+// exact, fp32 sums); 2: an fp32 operand, 16x16x4 fp32.
+template <typename XT, typename WT, int MODE, int TILE>
+__global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p) {
+  constexpr int TS = (TILE + 15) / 16;
+  constexpr int ETM = kFusedMaxE / 16;
+  constexpr int KSTEP = MODE == 2 ? 16 : 32;
+  constexpr int KLANE = MODE == 2 ? 4 : 8;  // k elements per lane per k-step
+  __shared__ SelectSmem<TILE> sm;
+  __shared__ f32x4 red[SEL_WAVES][TS * ETM][MOE_WAVE];
+  const int blk = blockIdx.x, t0 = blk * TILE;
+  const int E = p.E, ET = (E + 15) / 16;
+  const int nt = min(TILE, p.T - t0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+  float lb[4], sb[4];
+  load_biases(p, lb, sb);
+  for (int e = threadIdx.x; e < E; e += SEL_THREADS) sm.hist[e] = 0;
+
+  const XT* x = static_cast<const XT*>(p.x);
+  const WT* w = static_cast<const WT*>(p.w_router);
+  const int nsteps = p.D / KSTEP;
+  const int per = (nsteps + SEL_WAVES - 1) / SEL_WAVES;
+  const int s0 = min(nsteps, wave * per), s1 = min(nsteps, s0 + per);
+  const int r = lane & 15, kq = lane >> 4;
+  // This lane's row of token tile ts and of expert tile et (clamped), at its
+  // k offset inside a k-step.
+  auto xr = [&](int ts) { return x + (size_t)min(t0 + ts * 16 + r, p.T - 1) * p.D + kq * KLANE; };
+  auto wr = [&](int et) { return w + (size_t)min(et * 16 + r, E - 1) * p.D + kq * KLANE; };
+  f32x4 acc[TS][ETM];
+#pragma unroll
+  for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+    for (int et = 0; et < ETM; ++et) acc[ts][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (MODE == 0) {
+    constexpr int U = 4;  // k-steps in flight
+    int s = s0;
+    for (; s + U <= s1; s += U) {
+      bf16x8 A[U][TS], B[U][ETM];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts)
+          A[u][ts] = *reinterpret_cast<const bf16x8*>(xr(ts) + (s + u) * KSTEP);
+#pragma unroll
+        for (int et = 0; et < ETM; ++et)
+          if (et < ET) B[u][et] = *reinterpret_cast<const bf16x8*>(wr(et) + (s + u) * KSTEP);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int et = 0; et < ETM; ++et)
+          if (et < ET)
+#pragma unroll
+            for (int ts = 0; ts < TS; ++ts)
+              acc[ts][et] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u][ts], B[u][et], acc[ts][et], 0, 0, 0);
+    }
+    for (; s < s1; ++s) {
+      bf16x8 A[TS];
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) A[ts] = *reinterpret_cast<const bf16x8*>(xr(ts) + s * KSTEP);
+#pragma unroll
+      for (int et = 0; et < ETM; ++et)
+        if (et < ET) {
+          const bf16x8 B = *reinterpret_cast<const bf16x8*>(wr(et) + s * KSTEP);
+#pragma unroll
+          for (int ts = 0; ts < TS; ++ts)
+            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ts], B, acc[ts][et], 0, 0, 0);
+        }
+    }
+  } else if constexpr (MODE == 1) {
+    constexpr int U = 2;
+    int s = s0;
+    for (; s + U <= s1; s += U) {
+      bf16x8 A[U][TS];
+      f32x4 W0[U][ETM], W1[U][ETM];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts)
+          A[u][ts] = *reinterpret_cast<const bf16x8*>(xr(ts) + (s + u) * KSTEP);
+#pragma unroll
+        for (int et = 0; et < ETM; ++et)
+          if (et < ET) {
+            W0[u][et] = *reinterpret_cast<const f32x4*>(wr(et) + (s + u) * KSTEP);
+            W1[u][et] = *reinterpret_cast<const f32x4*>(wr(et) + (s + u) * KSTEP + 4);
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int et = 0; et < ETM; ++et)
+          if (et < ET) {
+            bf16x8 h, m, l;
+            split3_bf16(W0[u][et], W1[u][et], h, m, l);
+#pragma unroll
+            for (int ts = 0; ts < TS; ++ts) {
+              acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u][ts], h, acc[ts][et], 0, 0, 0);
+              acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u][ts], m, acc[ts][et], 0, 0, 0);
+              acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u][ts], l, acc[ts][et], 0, 0, 0);
+            }
+          }
+    }
+    for (; s < s1; ++s) {
+      bf16x8 A[TS];
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) A[ts] = *reinterpret_cast<const bf16x8*>(xr(ts) + s * KSTEP);
+#pragma unroll
+      for (int et = 0; et < ETM; ++et)
+        if (et < ET) {
+          bf16x8 h, m, l;
+          split3_bf16(*reinterpret_cast<const f32x4*>(wr(et) + s * KSTEP),
+                      *reinterpret_cast<const f32x4*>(wr(et) + s * KSTEP + 4), h, m, l);
+#pragma unroll
+          for (int ts = 0; ts < TS; ++ts) {
+            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ts], h, acc[ts][et], 0, 0, 0);
+            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ts], m, acc[ts][et], 0, 0, 0);
+            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ts], l, acc[ts][et], 0, 0, 0);
+          }
+        }
+    }
+  } else {
+    for (int s = s0; s < s1; ++s) {
+      f32x4 a[TS];
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) a[ts] = load4(xr(ts) + s * KSTEP);
+#pragma unroll
+      for (int et = 0; et < ETM; ++et)
+        if (et < ET) {
+          const f32x4 b = load4(wr(et) + s * KSTEP);
+#pragma unroll
+          for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ts][j], b[j], acc[ts][et], 0, 0, 0);
+        }
+    }
+  }
+#pragma unroll
+  for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+    for (int et = 0; et < ETM; ++et)
+      if (et < ET) red[wave][ts * ETM + et][lane] = acc[ts][et];
+  __syncthreads();
+  // Element i of lane l of tile (ts, et) is token ts*16 + 4*(l/16) + i,
+  // expert et*16 + l%16.
+  for (int idx = threadIdx.x; idx < nt * E; idx += SEL_THREADS) {
+    const int tl = idx / E, e = idx - tl * E;
+    const int tile = (tl >> 4) * ETM + (e >> 4);
+    const int ln = ((tl & 15) >> 2) * 16 + (e & 15), i = tl & 3;
+    const float* rv = reinterpret_cast<const float*>(&red[0][tile][ln]) + i;
+    constexpr int WSTRIDE = TS * ETM * MOE_WAVE * 4;  // floats between two waves' tiles
+    float v = rv[0];
+#pragma unroll
+    for (int wv = 1; wv < SEL_WAVES; ++wv) v += rv[wv * WSTRIDE];
+    sm.lg[idx] = v;
+  }
+  __syncthreads();
+  select_tokens<TILE, 1>(p, sm, blk, t0, nt, lb, sb);  // E <= 64: one slot
+}
+
+template <int TILE>
+void launch_fused(const RouteParams& p, hipStream_t s) {
+  const dim3 grid(route_blocks(p.T)), block(SEL_THREADS);
+  if (p.act_bf16 && p.router_bf16)
+    hipLaunchKernelGGL((route_fused_kernel<uint16_t, uint16_t, 0, TILE>), grid, block, 0, s, p);
+  else if (p.act_bf16)
+    hipLaunchKernelGGL((route_fused_kernel<uint16_t, float, 1, TILE>), grid, block, 0, s, p);
+  else if (p.router_bf16)
+    hipLaunchKernelGGL((route_fused_kernel<float, uint16_t, 2, TILE>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((route_fused_kernel<float, float, 2, TILE>), grid, block, 0, s, p);
+}
+
 }  // namespace
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s) {
+  if (route_fused(p.D, p.E, p.router_bf16)) {
+    if (p.tile == kSmallRouteTile)
+      launch_fused<kSmallRouteTile>(p, s);
+    else
+      launch_fused<kRouteTile>(p, s);
+    return hipGetLastError();
+  }
   const int NT = (p.E + 15) / 16;
   const int NTB = NT >= 4 ? 4 : (NT >= 2 ? 2 : 1);
   const dim3 grid(logits_blocks(p.T), (NT + NTB - 1) / NTB, p.ksplit), block(NTHREADS);

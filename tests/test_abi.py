@@ -210,3 +210,15 @@ def test_noalloc_forward_rejects_large_layers_on_the_host(moe):
     assert "scratch" in _binding._lib.moe_last_error().decode()
     small = moe.make_config(64, 4096, 1536, 128, 8)  # decode-sized: fits, so the
     assert f(ctypes.byref(small), *([None] * 21)) == 2  # NULL x is what it reports
+
+
+def test_route_path_cases_are_valid_configs(moe):
+    """Every case of the GPU routing-path tests passes the host's config
+    checks, so that those tests reach the kernels."""
+    import workloads as W
+    from tests import parity as P
+    from tests.test_gpu_route_paths import CASES
+    for name, T, D, E, k, act, router, score in CASES:
+        w = W.Workload(name, batch=1, seq=T, D=D, H=64, E=E, top_k=k, act_dtype=act,
+                       router_dtype=router, score=score)
+        moe.check_config(P.config_of(w))
