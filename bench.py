@@ -9,6 +9,11 @@ workload (T=4096, d_model=4096, 8 SwiGLU experts of d_hidden=14336, top-2
 softmax, dropless, bf16), the configuration the metric is quoted on, and
 ``configs`` carries every workload's tokens/s, stages, rooflines and CPU
 baseline.  Inputs are resident in HBM when timing starts.
+  * ``value``: tokens/s of the whole hot path, one ``moe_forward`` call per
+    step, K steps between two synchronisations.  The same path as its four
+    stage calls (route, permute, grouped SwiGLU, combine) gives ``stages_ms``
+    from HIP events; ``moe_forward_graph_ms_per_step`` is the forward
+    captured once into a HIP graph and replayed;
   * ``roofline``: the grouped SwiGLU step (gate/up GEMM + down GEMM, the
     dominant work) timed with HIP events on its stream.  Its bound is the
     one its algorithmic intensity selects: FLOP (6*D*H per kept row) per
@@ -66,6 +71,8 @@ def _parse():
                          "headline fields from the Mixtral-shaped layer")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of moe_forward")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -194,7 +201,7 @@ def _pmc_summary(fetch_db, write_db, workload):
              "cd /tmp && export TMPDIR=/tmp",
              *(f"rocprofv3 --kernel-include-regex 'moe::|neg_kernel' --pmc {c} -d /tmp/t_{c} "
                f"-o {workload} -- python3 /root/repo/bench.py --workload {workload} "
-               f"--steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline "
+               f"--steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline --no-graph "
                f"--copy-calibration"
                for c in ("FETCH_SIZE", "WRITE_SIZE")),
              f"python3 /root/repo/bench.py --pmc-summary /tmp/t_FETCH_SIZE/{workload}_results.db "
@@ -226,11 +233,11 @@ def _pmc_summary(fetch_db, write_db, workload):
 
 def _trace_summary(csv_path, workload, steps, warmup):
     """Per-kernel durations from a rocprofv3 kernel trace of
-    `bench.py --workload W --steps K --warmup W0 --no-cpu-baseline`.  Each
-    warm-up round runs one staged step and one moe_forward, then the K timed
-    staged steps run, then K moe_forward calls; a kernel with p launches per
-    step therefore has 2*(W0+K)*p dispatches, and the timed steps' ones are
-    dispatches [2*W0*p, (2*W0+K)*p) in start order."""
+    `bench.py --workload W --steps K --warmup W0 --no-cpu-baseline --no-graph`.
+    Each warm-up round runs one staged step and one moe_forward, then the K
+    timed moe_forward steps run, then K staged steps; a kernel with p launches
+    per step therefore has 2*(W0+K)*p dispatches, and the timed steps' ones
+    are dispatches [2*W0*p, (2*W0+K)*p) in start order."""
     import collections
     import csv
     import statistics
@@ -245,15 +252,15 @@ def _trace_summary(csv_path, workload, steps, warmup):
     cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --kernel-include-regex "
            f"'moe::' --output-format csv -d /tmp/kt_{workload} -o run -- python3 "
            f"/root/repo/bench.py --workload {workload} --steps {steps} --warmup {warmup} "
-           f"--no-cpu-baseline")
+           f"--no-cpu-baseline --no-graph")
     lines = [f"# Kernel trace of the MoE forward: {workload}", "",
              "Per-dispatch durations from a rocprofv3 kernel trace (the library's kernels",
              f"only) of bench.py on one MI355X: {warmup} warm-up rounds (a staged step and a",
-             f"`moe_forward` each), {steps} timed staged steps, then {steps} `moe_forward`",
-             "calls, plus the route/permute calls of the set-up.  \"timed steps\" is the mean",
-             "per step over the dispatches of the timed staged steps (the region bench.py",
-             "times with HIP events), for kernels whose dispatch count is a whole number",
-             "of launches per step; \"all\" is the mean over every dispatch, warm-up included.",
+             f"`moe_forward` each), {steps} timed `moe_forward` steps, then {steps} staged",
+             "steps, plus the route/permute calls of the set-up.  \"timed steps\" is the mean",
+             "per step over the dispatches of the timed `moe_forward` steps (the region",
+             "bench.py times), for kernels whose dispatch count is a whole number of",
+             "launches per step; \"all\" is the mean over every dispatch, warm-up included.",
              "", "Commands:", "", "```", cmd,
              f"python3 /root/repo/bench.py --trace-summary "
              f"$(find /tmp/kt_{workload} -name run_kernel_trace.csv) "
@@ -388,7 +395,7 @@ def _counter_table(db, workload, kind):
     disp = _pmc_dispatches(db, grbm_max=True)
     cmd = (f"rocprofv3 --kernel-include-regex 'moe::' --pmc {counters} -d /tmp/t_{kind} "
            f"-o {workload} -- python3 /root/repo/bench.py --workload {workload} "
-           f"--steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline")
+           f"--steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline --no-graph")
     title = {"mfma": "Clock and MFMA utilisation", "stall": "Wait and LDS-conflict cycles"}[kind]
     lines = [f"# {title} of the MoE kernels: {workload}", "",
              f"source_sha256_16: {_source_hash()}", "",
@@ -586,11 +593,15 @@ def _bench_workload(w, args, moe, dev):
 
     if args.copy_calibration:
         _copy_calibration(dev)
-    # One step = one pass of the whole hot path through the C-ABI entry points
-    # (route, permute, grouped SwiGLU (+ shared expert), combine), with HIP
-    # events recorded between the stages on the launch stream.  The kernels and
-    # their order are those of moe_forward; the fused entry is timed after it
-    # as a cross-check.
+    # One step = one pass of the whole hot path: moe_forward (routing with its
+    # auxiliary sums, permutation, grouped SwiGLU (+ shared expert), combine)
+    # on inputs resident in HBM; W warm-up steps, then K timed steps between
+    # two synchronisations.  The same path is then run as its four C-ABI stage
+    # calls (route, permute, grouped SwiGLU, combine) with HIP events recorded
+    # between them on the launch stream, for the per-stage times and the
+    # roofline of the grouped SwiGLU stage; those calls do a little more than
+    # moe_forward (the route call finishes its own counts and losses, the
+    # permute call builds its own histogram from the expert IDs).
     stream = torch.cuda.current_stream()
     cap = moe.capacity(cfg) if w.capacity_factor is not None else 0
     r = moe.moe_route(cfg, inp["x"], inp["w_router"], inp.get("logit_bias"),
@@ -629,25 +640,27 @@ def _bench_workload(w, args, moe, dev):
     torch.cuda.synchronize()
     _log(f"[bench] {w.name}: timing {args.steps} steps")
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        forward()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = w.T / (elapsed / args.steps)
+    _log(f"[bench] {w.name}: moe_forward {ms_per_step:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    staged_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     stage_ms = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
                          for ev in events]).mean(axis=0)
-    # each timed step on the device clock (HIP events around the step)
+    # each staged step on the device clock (HIP events around the step)
     step_dev = np.array([ev[0].elapsed_time(ev[4]) for ev in events])
-    _log(f"[bench] {w.name}: {ms_per_step:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
-    _log("[bench] stages ms: route %.4f permute %.4f grouped_swiglu %.4f combine %.4f"
-         % tuple(stage_ms))
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        forward()
-    torch.cuda.synchronize()
-    fwd_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    _log(f"[bench] {w.name}: moe_forward {fwd_ms:.3f} ms/step")
+    _log(f"[bench] {w.name}: staged {staged_ms:.3f} ms/step; stages ms: route %.4f permute %.4f "
+         "grouped_swiglu %.4f combine %.4f" % tuple(stage_ms))
+    graph_ms = _graph_ms(forward, args) if not args.no_graph else None
+    if graph_ms is not None:
+        _log(f"[bench] {w.name}: moe_forward as a replayed HIP graph {graph_ms:.3f} ms/step")
 
     # A step beside the layer, timed on its own (not part of the step above):
     # the RMSNorm pre-norm of the residual stream.  Algorithmic bytes: x read
@@ -707,8 +720,8 @@ def _bench_workload(w, args, moe, dev):
     rsz = 4 if w.router_dtype == "f32" else 2
     l_flops = flops + 2.0 * w.T * w.D * w.E
     l_bytes = nbytes + 1.0 * w.E * w.D * rsz
-    l_sec = float(np.median(step_dev)) * 1e-3
-    layer = {"ms_device_median": round(l_sec * 1e3, 4),
+    l_sec = ms_per_step * 1e-3
+    layer = {"ms_per_step": round(l_sec * 1e3, 4),
              "algorithmic_flop": l_flops, "algorithmic_bytes": l_bytes,
              "tflops": round(l_flops / l_sec / 1e12, 2),
              "frac_of_mfma_peak": round(l_flops / l_sec / 1e12 / peak_f, 4),
@@ -724,8 +737,9 @@ def _bench_workload(w, args, moe, dev):
                    "experts": w.E, "top_k": w.top_k, "shared_d_hidden": w.H_shared,
                    "capacity_factor": w.capacity_factor, "kept_rows": n_kept,
                    "parallelism": "none (1 GPU)"},
-        "moe_forward_ms_per_step": round(fwd_ms, 4),
-        "step_ms_device": {"median": round(float(np.median(step_dev)), 4),
+        "staged_ms_per_step": round(staged_ms, 4),
+        "moe_forward_graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "staged_step_ms_device": {"median": round(float(np.median(step_dev)), 4),
                            "min": round(float(step_dev.min()), 4),
                            "p90": round(float(np.percentile(step_dev, 90)), 4)},
         "stages_ms": {k: round(float(v), 4) for k, v in
@@ -746,9 +760,42 @@ def _bench_workload(w, args, moe, dev):
     return result
 
 
+def _graph_ms(forward, args):
+    """ms per step of moe_forward captured once into a HIP graph and replayed
+    (the serving form: the same kernels, without the per-launch host work).
+    W warm-up replays, then K timed replays between two synchronisations.
+    None if the capture fails (the eager figures stand alone then)."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            forward()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            forward()
+        for _ in range(max(args.warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        del g
+        return ms
+    except Exception as e:  # noqa: BLE001 - report and go on with the eager figures
+        _log(f"[bench] HIP graph capture of moe_forward failed: {e}")
+        torch.cuda.synchronize()
+        return None
+
+
 def _entry(res):
     """The per-workload summary carried in the headline line."""
-    e = {k: res[k] for k in ("value", "unit", "ms_per_step", "dtype", "stages_ms", "layer")}
+    e = {k: res[k] for k in ("value", "unit", "ms_per_step", "staged_ms_per_step",
+                             "moe_forward_graph_ms_per_step", "dtype", "stages_ms", "layer")}
     e["tokens_per_s"] = e.pop("value")
     rf = res["roofline"]
     e["grouped_swiglu"] = {k: rf[k] for k in ("bound", "achieved", "unit", "frac", "tflops",
