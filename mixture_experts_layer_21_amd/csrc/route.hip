@@ -743,10 +743,14 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
 // MODE 0: bf16 x and W, 16x16x32 bf16; 1: bf16 x and fp32 W on the exact
 // three-term bf16 split of W (three MFMAs per tile and k-step, products
 // exact, fp32 sums); 2: an fp32 operand, 16x16x4 fp32.
-template <typename XT, typename WT, int MODE, int TILE>
+// ETM: expert tiles held per wave (E <= 16 * ETM).  U k-steps of operands
+// are loaded at once: as many as about 128 (bf16 W) or 160 (fp32 W) VGPRs
+// of operands allow, at most 8.
+constexpr int pow2_floor(int v) { return v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
+
+template <typename XT, typename WT, int MODE, int TILE, int ETM>
 __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p) {
   constexpr int TS = (TILE + 15) / 16;
-  constexpr int ETM = kFusedMaxE / 16;
   constexpr int KSTEP = MODE == 2 ? 16 : 32;
   constexpr int KLANE = MODE == 2 ? 4 : 8;  // k elements per lane per k-step
   __shared__ SelectSmem<TILE> sm;
@@ -776,7 +780,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
     for (int et = 0; et < ETM; ++et) acc[ts][et] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (MODE == 0) {
-    constexpr int U = 4;  // k-steps in flight
+    constexpr int U = pow2_floor(128 / (4 * (TS + ETM)));  // k-steps in flight
     int s = s0;
     for (; s + U <= s1; s += U) {
       bf16x8 A[U][TS], B[U][ETM];
@@ -813,7 +817,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
         }
     }
   } else if constexpr (MODE == 1) {
-    constexpr int U = 2;
+    constexpr int U = pow2_floor(160 / (4 * TS + 8 * ETM));
     int s = s0;
     for (; s + U <= s1; s += U) {
       bf16x8 A[U][TS];
@@ -903,17 +907,29 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
   select_tokens<TILE, 1>(p, sm, blk, t0, nt, lb, sb);  // E <= 64: one slot
 }
 
-template <int TILE>
-void launch_fused(const RouteParams& p, hipStream_t s) {
+template <int TILE, int ETM>
+void launch_fused_etm(const RouteParams& p, hipStream_t s) {
   const dim3 grid(route_blocks(p.T)), block(SEL_THREADS);
   if (p.act_bf16 && p.router_bf16)
-    hipLaunchKernelGGL((route_fused_kernel<uint16_t, uint16_t, 0, TILE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((route_fused_kernel<uint16_t, uint16_t, 0, TILE, ETM>), grid, block, 0, s,
+                       p);
   else if (p.act_bf16)
-    hipLaunchKernelGGL((route_fused_kernel<uint16_t, float, 1, TILE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((route_fused_kernel<uint16_t, float, 1, TILE, ETM>), grid, block, 0, s, p);
   else if (p.router_bf16)
-    hipLaunchKernelGGL((route_fused_kernel<float, uint16_t, 2, TILE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((route_fused_kernel<float, uint16_t, 2, TILE, ETM>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((route_fused_kernel<float, float, 2, TILE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((route_fused_kernel<float, float, 2, TILE, ETM>), grid, block, 0, s, p);
+}
+
+template <int TILE>
+void launch_fused(const RouteParams& p, hipStream_t s) {
+  static_assert(kFusedMaxE == 64, "expert tiles per wave: 1, 2 or 4");
+  if (p.E <= 16)
+    launch_fused_etm<TILE, 1>(p, s);
+  else if (p.E <= 32)
+    launch_fused_etm<TILE, 2>(p, s);
+  else
+    launch_fused_etm<TILE, 4>(p, s);
 }
 
 }  // namespace
