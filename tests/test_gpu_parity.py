@@ -169,6 +169,30 @@ def test_permute_small(moe, name):
     _check_permute(moe, w, cfg, r["ids"], tight)
 
 
+# Shapes past the one-workgroup permutation (more than 4096 assignments):
+# the per-expert scans and the per-tile scatter, with one to 256 experts, E
+# not a power of two, k up to 8, and capacity limits.
+LARGE_PERMUTE_CASES = [
+    # T, E, k, capacity (0: dropless)
+    (3001, 8, 3, 0), (8192, 64, 1, 160), (4100, 5, 2, 0), (2048, 256, 8, 0),
+    (5000, 3, 3, 2000), (1500, 130, 4, 10), (16384, 1, 1, 0), (3000, 2, 2, 0),
+]
+
+
+@pytest.mark.parametrize("T,E,k,cap", LARGE_PERMUTE_CASES)
+def test_permute_large_shapes(moe, T, E, k, cap):
+    w = W.Workload("perm_large", 1, T, D=64, H=64, E=E, top_k=k)
+    _say(f"[permute-large] T={T} E={E} k={k} cap={cap}")
+    cfg = P.config_of(w)
+    rng = np.random.default_rng(T * 131 + E)
+    # skewed, distinct experts per token (as a top-k gives)
+    pref = rng.permutation(E)
+    ids = np.stack([pref[np.sort(rng.choice(E, size=k, replace=False,
+                                            p=np.linspace(2.0, 1.0, E) / np.linspace(2.0, 1.0, E).sum()))]
+                    for _ in range(T)])
+    _check_permute(moe, w, cfg, ids, cap)
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_grouped_swiglu_small(moe, name):
     w = W.SMALL[name]
