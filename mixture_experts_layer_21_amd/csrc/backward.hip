@@ -39,7 +39,7 @@ constexpr int BCH = BBM * BKCH / BT;     // chunks per thread and operand (4)
 // conflict-free 32-row fragment reads).
 __device__ __forceinline__ int bswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-__device__ __forceinline__ float sigm(float v) { return 1.0f / (1.0f + __expf(-v)); }
+__device__ __forceinline__ float sigm(float v) { return sigmoid_f32(v); }
 
 // Tile of the block: group, first row (MROWS: global row), row end, column
 // tile, and the k range.  Returns false when the block has no tile.

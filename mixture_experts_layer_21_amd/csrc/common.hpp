@@ -57,7 +57,15 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU in fp32: g * 1/(1 + e^-g) with the hardware reciprocal (1 ulp) in
+// place of a correctly rounded division (about ten instructions), since the
+// result is rounded to the activation dtype or feeds an fp32 product whose
+// own rounding is larger; e^-g = inf for large negative g gives -0 as the
+// division would.
+__device__ __forceinline__ float sigmoid_f32(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+__device__ __forceinline__ float silu_f32(float g) { return g * sigmoid_f32(g); }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
 

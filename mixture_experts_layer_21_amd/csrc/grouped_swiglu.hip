@@ -57,7 +57,7 @@ __device__ __forceinline__ void save_factors(const GemmParams& p, size_t o, floa
     mg = fabsf(g) < p.swiglu_limit ? 1.f : 0.f;
     mu = fabsf(u) < p.swiglu_limit ? 1.f : 0.f;
   }
-  const float s = 1.0f / (1.0f + __expf(-gc));
+  const float s = sigmoid_f32(gc);
   p.save_p1[o] = f32_to_bf16_bits(mg * uc * (s + gc * s * (1.f - s)));
   p.save_p2[o] = f32_to_bf16_bits(mu * gc * s);
 }
