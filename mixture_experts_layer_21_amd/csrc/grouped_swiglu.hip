@@ -540,6 +540,59 @@ constexpr int partial_vectors() { return C::NB * C::MI * C::NI * 4; }
 // so the two rows one write touches use different banks), then every thread
 // stores whole 16-byte row chunks, full 128-byte lines per row.  The caller
 // has passed the k-loop; the first barrier makes the stage buffers free.
+//
+// The LDS address of accumulator element (mi, i, ni) splits into a per-lane
+// part, computed once, and a compile-time part that goes into the write's
+// immediate offset: a 32-row block (mi) starts at a multiple of 16 rows, so
+// the row's swizzle term 4*((r/4)%4) is 4*((2*(i/4) + lane/32) % 4), which
+// depends on the lane and on the parity of i/4 only.  The clamp of the
+// SwiGLU (swiglu_limit) is decided once per tile, not per element.
+template <class C, bool GATEUP, bool CLAMP>
+__device__ __forceinline__ void staged_write(const GemmParams& p, int wm, int wn, int lr, int lk,
+                                             const f32x16 (&acc)[C::NB][C::MI][C::NI],
+                                             const float* row_gw, uint16_t* s0, uint16_t* s1,
+                                             uint16_t* s2, uint16_t* s3) {
+  constexpr int BN = C::BN;
+  constexpr int ROWS_PER = 16384 / BN;  // rows of one 32 KB buffer
+  static_assert(ROWS_PER % 32 == 0, "a 32-row block lies in one buffer");
+  // per-lane element offsets (uint16 units) inside a buffer, by i/4 parity
+  int off[C::NI][2];
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) {
+    const int col = wn * C::WN + ni * 32 + lr;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      off[ni][g] = 4 * lk * BN + (((col >> 3) ^ (4 * ((2 * g + lk) & 3))) << 3) + (col & 7);
+  }
+  const float lim = p.swiglu_limit;
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) {
+    const int rb = wm * C::WM + mi * 32;  // first row of the block (wave-uniform)
+    const int b = rb / ROWS_PER;
+    uint16_t* base = (b == 0 ? s0 : b == 1 ? s1 : b == 2 ? s2 : s3) + (rb % ROWS_PER) * BN;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rc = 8 * (i >> 2) + (i & 3);  // row inside the block, less 4*lk
+      const float gw = GATEUP ? 1.f : row_gw[rb + rc + 4 * lk];
+#pragma unroll
+      for (int ni = 0; ni < C::NI; ++ni) {
+        float v;
+        if constexpr (GATEUP) {
+          float g = acc[0][mi][ni][i], u = acc[C::NB - 1][mi][ni][i];
+          if constexpr (CLAMP) {
+            g = fminf(fmaxf(g, -lim), lim);
+            u = fminf(fmaxf(u, -lim), lim);
+          }
+          v = silu_f32(g) * u;
+        } else {
+          v = gw * acc[0][mi][ni][i];
+        }
+        base[off[ni][(i >> 2) & 1] + rc * BN] = f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
 template <class C, bool GATEUP>
 __device__ __forceinline__ void dma_epilogue_staged(
     const GemmParams& p, int m0, int m_end, int n0, int wm, int wn, int lr, int lk,
@@ -556,21 +609,10 @@ __device__ __forceinline__ void dma_epilogue_staged(
   };
   const int N = GATEUP ? p.hidden : p.D;
   __syncthreads();
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = wm * C::WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
-      const float gw = GATEUP ? 1.f : row_gw[r];
-#pragma unroll
-      for (int ni = 0; ni < C::NI; ++ni) {
-        const int col = wn * C::WN + ni * 32 + lr;
-        const float v = GATEUP
-            ? swiglu_act(acc[0][mi][ni][i], acc[C::NB - 1][mi][ni][i], p.swiglu_limit)
-            : gw * acc[0][mi][ni][i];
-        at(r, col >> 3)[col & 7] = f32_to_bf16_bits(v);
-      }
-    }
+  if (GATEUP && p.swiglu_limit > 0.f)
+    staged_write<C, GATEUP, true>(p, wm, wn, lr, lk, acc, row_gw, s0, s1, s2, s3);
+  else
+    staged_write<C, GATEUP, false>(p, wm, wn, lr, lk, acc, row_gw, s0, s1, s2, s3);
   __syncthreads();
   uint16_t* out = static_cast<uint16_t*>(GATEUP ? p.hbuf : p.y);
   for (int q = threadIdx.x; q < BM * CPR; q += C::NT) {
@@ -785,10 +827,18 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
                                  acc);
     return;
   }
-  if constexpr (BM == 256 && BNB == 256 && BK == 64 && S == 2) {
-    if (!(GATEUP && p.save_p1)) {  // (saving the SwiGLU factors stores per element)
+  // The bf16 results go out through the free stage buffers when those hold
+  // them (saving the SwiGLU factors stores per element instead).
+  if (!(GATEUP && p.save_p1)) {
+    constexpr int OUT_BYTES = BM * C::BN * 2;
+    if constexpr (BM == 256 && BNB == 256 && BK == 64 && S == 2) {
       dma_epilogue_staged<C, GATEUP>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc, s_gw, sA0,
                                      sA1, sB0, sB1);
+      return;
+    } else if constexpr (BNB * BK * 2 == 32768 && OUT_BYTES <= 2 * 32768) {
+      // 32 KB B stage buffers (the 128-row tiles): two of them hold the tile
+      dma_epilogue_staged<C, GATEUP>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc, s_gw, sB0,
+                                     sB1, sB0, sB1);
       return;
     }
   }
