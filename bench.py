@@ -15,7 +15,8 @@ baseline.  Inputs are resident in HBM when timing starts.
     from HIP events; ``moe_forward_graph_ms_per_step`` is the forward
     captured once into a HIP graph and replayed;
   * ``roofline``: the grouped SwiGLU step (gate/up GEMM + down GEMM, the
-    dominant work) timed with HIP events on its stream.  Its bound is the
+    dominant work), K calls back to back between two HIP events on its
+    stream (so the device never waits on the host).  Its bound is the
     one its algorithmic intensity selects: FLOP (6*D*H per kept row) per
     algorithmic byte (the weights of every expert that keeps a row, x read
     once, the output written once) against the ridge of the bf16 MFMA peak
@@ -137,9 +138,19 @@ def _copy_calibration(dev):
 
 
 # Steps of the counter runs: each warm-up round and each timed round runs one
-# staged step and one moe_forward, so a grouped GEMM kernel with p launches
-# per step has 2 * (PMC_WARMUP + PMC_STEPS) * p dispatches.
+# staged step and one moe_forward, and the grouped SwiGLU stage then runs
+# K + 1 more times on its own (the back-to-back timing), so a grouped GEMM
+# kernel with p launches per step has gemm_rounds(W, K) * p dispatches and
+# any other kernel of the step 2 * (W + K) * p.
 PMC_STEPS, PMC_WARMUP = 2, 1
+
+
+def gemm_rounds(warmup, steps):
+    return 2 * (warmup + steps) + steps + 1
+
+
+def _rounds_of(name, warmup, steps):
+    return gemm_rounds(warmup, steps) if "gemm" in name else 2 * (warmup + steps)
 
 
 def _pmc_dispatches(db, grbm_max=False):
@@ -185,7 +196,7 @@ def _pmc_summary(fetch_db, write_db, workload):
     cal_us = _mean([d for _, d in fetch[calib[0]]]) / 1e3
     f_scale = CALIB_BYTES / f_cal
     w_scale = CALIB_BYTES / w_cal
-    rounds = 2 * (PMC_WARMUP + PMC_STEPS)
+    rounds = gemm_rounds(PMC_WARMUP, PMC_STEPS)
     lines = [f"# HBM traffic of the MoE kernels: {workload}", "",
              f"source_sha256_16: {_source_hash()}", "",
              "FETCH_SIZE and WRITE_SIZE (rocprofv3, one pass each) per dispatch, scaled by",
@@ -236,8 +247,9 @@ def _trace_summary(csv_path, workload, steps, warmup):
     `bench.py --workload W --steps K --warmup W0 --no-cpu-baseline --no-graph`.
     Each warm-up round runs one staged step and one moe_forward, then the K
     timed moe_forward steps run, then K staged steps; a kernel with p launches
-    per step therefore has 2*(W0+K)*p dispatches, and the timed steps' ones
-    are dispatches [2*W0*p, (2*W0+K)*p) in start order."""
+    per step therefore has 2*(W0+K)*p dispatches (gemm kernels K+1 more
+    rounds: the back-to-back stage timing), and the timed steps' ones are
+    dispatches [2*W0*p, (2*W0+K)*p) in start order."""
     import collections
     import csv
     import statistics
@@ -257,7 +269,8 @@ def _trace_summary(csv_path, workload, steps, warmup):
              "Per-dispatch durations from a rocprofv3 kernel trace (the library's kernels",
              f"only) of bench.py on one MI355X: {warmup} warm-up rounds (a staged step and a",
              f"`moe_forward` each), {steps} timed `moe_forward` steps, then {steps} staged",
-             "steps, plus the route/permute calls of the set-up.  \"timed steps\" is the mean",
+             f"steps and {steps + 1} more calls of the grouped SwiGLU stage alone, plus the",
+             "route/permute calls of the set-up.  \"timed steps\" is the mean",
              "per step over the dispatches of the timed `moe_forward` steps (the region",
              "bench.py times), for kernels whose dispatch count is a whole number of",
              "launches per step; \"all\" is the mean over every dispatch, warm-up included.",
@@ -268,11 +281,11 @@ def _trace_summary(csv_path, workload, steps, warmup):
              "| kernel | dispatches | launches per step | timed steps, per step (us) | "
              "all: mean (us) | median (us) | min (us) | max (us) |",
              "|---|---:|---:|---:|---:|---:|---:|---:|"]
-    rounds = 2 * (warmup + steps)
     step_sum = 0.0
     for name in sorted(per):
         d = sorted(per[name])
         us = [x[1] / 1e3 for x in d]
+        rounds = _rounds_of(name, warmup, steps)
         p = len(d) // rounds if len(d) % rounds == 0 else 0
         if p:
             timed = sum(us[2 * warmup * p:(2 * warmup + steps) * p]) / steps
@@ -372,7 +385,7 @@ SIMDS = 256 * 4  # MI355X: 256 compute units of four SIMDs
 def _launch_rows(disp):
     """Dispatch lists of each kernel split per launch of a step (see
     _pmc_summary): [(kernel, launch label, dispatches)]."""
-    rounds = 2 * (PMC_WARMUP + PMC_STEPS)
+    rounds = gemm_rounds(PMC_WARMUP, PMC_STEPS)
     out = []
     for name in sorted(n for n in disp if "moe::" in n):
         d = disp[name]

@@ -34,9 +34,11 @@ def _row(md, kernel):
 
 def test_trace_summary_takes_the_timed_steps(tmp_path):
     """A gemm kernel launched twice per step: 2 * (W + K) rounds of two
-    dispatches; the timed moe_forward steps are dispatches [2W*2, (2W+K)*2)."""
+    dispatches, then K + 1 back-to-back rounds of the stage alone; the timed
+    moe_forward steps are dispatches [2W*2, (2W+K)*2)."""
     W_, K = 1, 2
-    rounds = 2 * (W_ + K)
+    rounds = 2 * (W_ + K) + K + 1
+    assert rounds == bench.gemm_rounds(W_, K)
     path = tmp_path / "run_kernel_trace.csv"
     t = 0
     durs = []
@@ -74,7 +76,8 @@ def test_pmc_summary_splits_launches_and_calibrates(tmp_path):
     """Counter units become bytes through the calibration kernel's reading of
     its known 1 GiB; a gemm kernel with two launches per step gets one row
     per launch and both count in the step's bytes."""
-    rounds = 2 * (bench.PMC_WARMUP + bench.PMC_STEPS)
+    rounds = bench.gemm_rounds(bench.PMC_WARMUP, bench.PMC_STEPS)
+    assert rounds == 2 * (bench.PMC_WARMUP + bench.PMC_STEPS) + bench.PMC_STEPS + 1
     gemm = "void moe::gemm_dma_kernel<256, 256, 64, 2, 2, 8, false>(moe::GemmParams, int)"
     calib = "void at::native::neg_kernel"
     f_units, w_units = 524288.0, 1048576.0  # units per GiB: 2048 B and 1024 B per unit
