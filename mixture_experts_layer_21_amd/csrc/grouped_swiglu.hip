@@ -114,6 +114,11 @@ __device__ bool find_tile(const GemmParams& p, int max_mtiles, Tile& t, int* s_s
   return true;
 }
 
+// Blocks per XCD of the split-K tail reduce of the large and 128-row tiles.
+#ifndef MOE_REDUCE_BLOCKS
+#define MOE_REDUCE_BLOCKS 128
+#endif
+
 // Most pieces a split tail tile is cut into (at most 16: the reduce kernels
 // hold one vector per piece).
 #ifndef MOE_TAIL_MAX_PIECES
@@ -452,6 +457,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmPar
     const int m0 = d[1], m_end = d[2], col = d[3] * BN + cl;
     const int row = m0 + rl;
     if (row >= m_end || col >= N) continue;  // N is a multiple of 64: all 4 columns valid
+    // (the row's assignment index goes out ahead of the partials)
+    const int ra = (!GATEUP && p.gate_w && p.row_to_assign) ? p.row_to_assign[row] : -1;
     const float* part0 = p.tail_part + (size_t)(xcd * kTailSlots + j * ns) * SLOT + rl * W + cl;
     f32x4 v[NB][16];
 #pragma unroll
@@ -478,8 +485,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_reduce_flat_kernel(GemmPar
         if (p.save_p1) save_factors(p, o + u, a[0][u], a[NB - 1][u]);
       }
     } else {
-      float gw = 1.f;
-      if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[row]];
+      const float gw = ra >= 0 ? p.gate_w[ra] : 1.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) q[u] = f32_to_bf16_bits(gw * a[0][u]);
     }
@@ -669,6 +675,15 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmParams p) {
     const int row0 = m0 + wm * C::WM + mi * 32 + 8 * q + 4 * (lane >> 5);
     const int col = nt * C::BN + wn * C::WN + ni * 32 + (lane & 31);
     if (row0 >= m_end || col >= N) continue;
+    // The down GEMM's gate weights of the four rows: their index loads go
+    // out ahead of the partials so that the two dependent lookups overlap
+    // the partial loads instead of following them.
+    int ra[4];
+    const bool gated = !GATEUP && p.gate_w && p.row_to_assign;
+    if (gated) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ra[u] = row0 + u < m_end ? p.row_to_assign[row0 + u] : -1;
+    }
     const float* base = p.tail_part + (size_t)(xcd * kTailSlots + j * ns) * SLOT;
     f32x4 x[C::NB][16];
 #pragma unroll
@@ -678,6 +693,12 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmParams p) {
       for (int pc = 0; pc < 16; ++pc)
         if (pc < ns)
           x[nb][pc] = reinterpret_cast<const f32x4*>(base + pc * SLOT)[v * C::NT + tid];
+    }
+    float gw[4] = {1.f, 1.f, 1.f, 1.f};
+    if (gated) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ra[u] >= 0) gw[u] = p.gate_w[ra[u]];
     }
     f32x4 sum[C::NB];
 #pragma unroll
@@ -697,9 +718,7 @@ __global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(GemmParams p) {
         static_cast<uint16_t*>(p.hbuf)[o] = f32_to_bf16_bits(swiglu_act(g, up, p.swiglu_limit));
         if (p.save_p1) save_factors(p, o, g, up);
       } else {
-        float gw = 1.f;
-        if (p.gate_w && p.row_to_assign) gw = p.gate_w[p.row_to_assign[row]];
-        static_cast<uint16_t*>(p.y)[o] = f32_to_bf16_bits(gw * sum[0][u]);
+        static_cast<uint16_t*>(p.y)[o] = f32_to_bf16_bits(gw[u] * sum[0][u]);
       }
     }
   }
@@ -978,7 +997,7 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(NTHREADS), 0, s, p, slots);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || slots == 0) return err;
-  hipLaunchKernelGGL((gemm_tail_reduce_flat_kernel<BM, BN, GATEUP>), dim3(kXcds * 64),
+  hipLaunchKernelGGL((gemm_tail_reduce_flat_kernel<BM, BN, GATEUP>), dim3(kXcds * MOE_REDUCE_BLOCKS),
                      dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
@@ -1001,7 +1020,7 @@ hipError_t launch_dma(const GemmParams& p, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || slots == 0) return err;
   hipLaunchKernelGGL((gemm_tail_reduce_kernel<BM, BNB, BK, S, WGM, NWV, GATEUP>),
-                     dim3(kXcds * 64), dim3(256), 0, s, p);
+                     dim3(kXcds * MOE_REDUCE_BLOCKS), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
