@@ -86,6 +86,13 @@ struct DmaLoads {
   uint32_t a_kbytes;
 };
 
+// Cache policy of the B-tile (weight) loads: 0, or 2 for non-temporal
+// (streaming) loads.  A translation unit may set it before including this
+// header.
+#ifndef MOE_DMA_B_CPOL
+#define MOE_DMA_B_CPOL 0
+#endif
+
 // One wave load (1 KB) of the B tile of k-step kt into stage buffer sb.
 // K-contiguous B (BTR false): 16-byte chunks along k of BNB rows, GATEUP
 // taking the second half of the rows from rU.  k-major B (BTR true, "B
@@ -101,12 +108,13 @@ struct DmaLoads {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(                                             \
           hi_ ? (ld).rU : (ld).rG, (lds_void_t*)((sb) + blk_ * 512), 16,                    \
           (ld).b_off[i] + (uint32_t)(hi_ ? k_ - (ld).k_split : k_) * (ld).b_kbytes, 0, 0,    \
-          0);                                                                               \
+          MOE_DMA_B_CPOL);                                                                  \
     } else {                                                                                \
       const bool up_ = (GATEUP) && blk_ * 64 >= C::BN * C::KCH;                             \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(up_ ? (ld).rU : (ld).rG,                     \
                                                (lds_void_t*)((sb) + blk_ * 512), 16,        \
-                                               (ld).b_off[i], (kt) * C::BK * 2, 0, 0);      \
+                                               (ld).b_off[i], (kt) * C::BK * 2, 0,          \
+                                               MOE_DMA_B_CPOL);                             \
     }                                                                                       \
   } while (0)
 

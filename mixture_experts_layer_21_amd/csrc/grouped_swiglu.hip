@@ -119,6 +119,11 @@ __device__ bool find_tile(const GemmParams& p, int max_mtiles, Tile& t, int* s_s
 #define MOE_REDUCE_BLOCKS 128
 #endif
 
+// Streaming (non-temporal) weight loads in the 32-row tiles.
+#ifndef MOE_SMALL_NT
+#define MOE_SMALL_NT 1
+#endif
+
 // Most pieces a split tail tile is cut into (at most 16: the reduce kernels
 // hold one vector per piece).
 #ifndef MOE_TAIL_MAX_PIECES
@@ -333,13 +338,21 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int t
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[nb][mi][ni][i] = 0.f;
 
+  // The weights: each byte of a tile's B slice is read by this block only
+  // (with MOE_SMALL_NT, as streaming loads that bypass L2 retention).
+  auto load_b = [](const uint16_t* q) -> u32x4 {
+#if MOE_SMALL_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
+#else
+    return *reinterpret_cast<const u32x4*>(q);
+#endif
+  };
   u32x4 ra[AC], rb[BC];
 #define MOE_GLOAD(k0)                                                                     \
   do {                                                                                    \
     _Pragma("unroll") for (int i = 0; i < AC; ++i) ra[i] =                                \
         *reinterpret_cast<const u32x4*>(a_src[i] + (k0));                                 \
-    _Pragma("unroll") for (int i = 0; i < BC; ++i) rb[i] =                                \
-        *reinterpret_cast<const u32x4*>(b_src[i] + (k0));                                 \
+    _Pragma("unroll") for (int i = 0; i < BC; ++i) rb[i] = load_b(b_src[i] + (k0));        \
   } while (0)
 #define MOE_SSTORE(buf)                                                                   \
   do {                                                                                    \
