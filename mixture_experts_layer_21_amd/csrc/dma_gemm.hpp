@@ -86,14 +86,9 @@ struct DmaLoads {
   uint32_t a_kbytes;
 };
 
-// Cache policy of the B-tile (weight) loads: 0, or 2 for non-temporal
-// (streaming) loads.  A translation unit may set it before including this
-// header.
-#ifndef MOE_DMA_B_CPOL
-#define MOE_DMA_B_CPOL 0
-#endif
-
-// One wave load (1 KB) of the B tile of k-step kt into stage buffer sb.
+// One wave load (1 KB) of the B tile of k-step kt into stage buffer sb, with
+// cache policy BCPOL (a template parameter of the caller): 0, or 2 for
+// non-temporal (streaming) loads of a B slice that no other block reads.
 // K-contiguous B (BTR false): 16-byte chunks along k of BNB rows, GATEUP
 // taking the second half of the rows from rU.  k-major B (BTR true, "B
 // transposed": row k holds the N columns): BK rows of BNB columns, the rows
@@ -108,13 +103,12 @@ struct DmaLoads {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(                                             \
           hi_ ? (ld).rU : (ld).rG, (lds_void_t*)((sb) + blk_ * 512), 16,                    \
           (ld).b_off[i] + (uint32_t)(hi_ ? k_ - (ld).k_split : k_) * (ld).b_kbytes, 0, 0,    \
-          MOE_DMA_B_CPOL);                                                                  \
+          BCPOL);                                                                           \
     } else {                                                                                \
       const bool up_ = (GATEUP) && blk_ * 64 >= C::BN * C::KCH;                             \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(up_ ? (ld).rU : (ld).rG,                     \
                                                (lds_void_t*)((sb) + blk_ * 512), 16,        \
-                                               (ld).b_off[i], (kt) * C::BK * 2, 0,          \
-                                               MOE_DMA_B_CPOL);                             \
+                                               (ld).b_off[i], (kt) * C::BK * 2, 0, BCPOL);  \
     }                                                                                       \
   } while (0)
 
@@ -195,7 +189,7 @@ __device__ __forceinline__ bf16x8 tr_fragment(const uint16_t* tile, int kk, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <class C, bool GATEUP, bool PARTIAL, bool BTR, bool ATR = false>
+template <class C, bool GATEUP, bool PARTIAL, bool BTR, bool ATR = false, int BCPOL = 0>
 __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* sb, int wm,
                                             int wn, int lr, int lk,
                                             f32x16 (&acc)[C::NB][C::MI][C::NI],
@@ -280,7 +274,8 @@ __device__ __forceinline__ void dma_compute(const uint16_t* sa, const uint16_t* 
 // scoped no-alias information, so the compiler's own wait before a fragment
 // read covers only the load into that same buffer (issued S-1 stages earlier)
 // instead of every load in flight.
-template <class C, bool GATEUP, bool PARTIAL, bool BTR = false, bool ATR = false>
+template <class C, bool GATEUP, bool PARTIAL, bool BTR = false, bool ATR = false,
+          int BCPOL = 0>
 __device__ __forceinline__ void dma_mainloop(
     const DmaLoads<C, GATEUP>& ld, int nk, int mi_n, int wm, int wn, int lr, int lk,
     f32x16 (&acc)[C::NB][C::MI][C::NI], uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
@@ -314,7 +309,7 @@ __device__ __forceinline__ void dma_mainloop(
     wait_vmcnt<(S - 2) * C::LPS>();                                                         \
     stage_barrier();                                                                        \
     if (kt < nk)                                                                            \
-      dma_compute<C, GATEUP, PARTIAL, BTR, ATR>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc, \
+      dma_compute<C, GATEUP, PARTIAL, BTR, ATR, BCPOL>(MOE_SA(SI), MOE_SB(SI), wm, wn, lr, lk, acc, \
                                                 ld,                                         \
                                       MOE_SA((SI + S - 1) % S), MOE_SB((SI + S - 1) % S),   \
                                       min(kt + S - 1, nk - 1), mi_n, af, bfr);              \

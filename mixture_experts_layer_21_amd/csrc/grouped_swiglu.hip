@@ -64,6 +64,7 @@ __device__ __forceinline__ void save_factors(const GemmParams& p, size_t o, floa
 
 struct Tile {
   int e, m0, m_end, nt;
+  int rt;  // row tiles of the expert (decode_job only)
 };
 
 // Map blockIdx.x to (expert, first row, row end, column tile).  Returns false
@@ -119,9 +120,12 @@ __device__ bool find_tile(const GemmParams& p, int max_mtiles, Tile& t, int* s_s
 #define MOE_REDUCE_BLOCKS 128
 #endif
 
-// Streaming (non-temporal) weight loads in the 32-row tiles.
-#ifndef MOE_SMALL_NT
-#define MOE_SMALL_NT 1
+// The weights of a layer stream through with non-temporal loads when all
+// its experts' weights together exceed this many bytes (MI355X: a 256 MB
+// Infinity Cache; a smaller set stays there from one call to the next, and
+// streaming loads would give that up).
+#ifndef MOE_STREAM_MIN_BYTES
+#define MOE_STREAM_MIN_BYTES (256ll << 20)
 #endif
 
 // Most pieces a split tail tile is cut into (at most 16: the reduce kernels
@@ -227,6 +231,7 @@ __device__ bool decode_job(const GemmParams& p, int tail_slots, int* s_scan, Til
       tile.e = 0;
       tile.m0 = ml * BM;
       tile.m_end = p.T;
+      tile.rt = total;
     } else {
       if (tid < p.n_groups) {
         const int hi = s_scan[tid], lo = hi - cnt;
@@ -234,12 +239,14 @@ __device__ bool decode_job(const GemmParams& p, int tail_slots, int* s_scan, Til
           s_scan[NTHREADS] = tid;
           s_scan[NTHREADS + 1] = p.expert_offsets[tid] + (ml - lo) * BM;
           s_scan[NTHREADS + 2] = p.expert_offsets[tid + 1];
+          s_scan[NTHREADS + 3] = cnt;
         }
       }
       __syncthreads();
       tile.e = s_scan[NTHREADS];
       tile.m0 = s_scan[NTHREADS + 1];
       tile.m_end = s_scan[NTHREADS + 2];
+      tile.rt = s_scan[NTHREADS + 3];
     }
     if (piece == 0 && tid == 0) {
       int32_t* d = p.tail_desc + (size_t)(xcd * kTailSlots + tail_tile) * 4;
@@ -258,7 +265,7 @@ __device__ bool decode_job(const GemmParams& p, int tail_slots, int* s_scan, Til
 // rows, land on distinct chunk positions.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int BM, int BN, int WGM, bool GATEUP>
+template <int BM, int BN, int WGM, bool GATEUP, bool NT>
 __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int tail_slots) {
   constexpr int BK = 64;
   constexpr int WGN = 4 / WGM;
@@ -338,14 +345,13 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int t
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[nb][mi][ni][i] = 0.f;
 
-  // The weights: each byte of a tile's B slice is read by this block only
-  // (with MOE_SMALL_NT, as streaming loads that bypass L2 retention).
+  // The weights: each byte of a tile's B slice is read by this block only;
+  // with NT they stream through as non-temporal loads.
   auto load_b = [](const uint16_t* q) -> u32x4 {
-#if MOE_SMALL_NT
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
-#else
-    return *reinterpret_cast<const u32x4*>(q);
-#endif
+    if constexpr (NT)
+      return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
+    else
+      return *reinterpret_cast<const u32x4*>(q);
   };
   u32x4 ra[AC], rb[BC];
 #define MOE_GLOAD(k0)                                                                     \
@@ -612,7 +618,9 @@ __device__ __forceinline__ void staged_write(const GemmParams& p, int wm, int wn
   }
 }
 
-template <class C, bool GATEUP>
+// NTS: the rows leave as non-temporal stores (the large tiles' hidden and
+// expert rows, hundreds of MB, would only displace cached operands).
+template <class C, bool GATEUP, bool NTS>
 __device__ __forceinline__ void dma_epilogue_staged(
     const GemmParams& p, int m0, int m_end, int n0, int wm, int wn, int lr, int lk,
     const f32x16 (&acc)[C::NB][C::MI][C::NI], const float* row_gw, uint16_t* s0, uint16_t* s1,
@@ -638,8 +646,11 @@ __device__ __forceinline__ void dma_epilogue_staged(
     const int r = q / CPR, c = q % CPR;
     const int row = m0 + r, col = n0 + c * 8;
     if (row >= m_end || col >= N) continue;
-    *reinterpret_cast<u32x4*>(out + (size_t)row * N + col) =
-        *reinterpret_cast<const u32x4*>(at(r, c));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(at(r, c));
+    if constexpr (NTS)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (size_t)row * N + col));
+    else
+      *reinterpret_cast<u32x4*>(out + (size_t)row * N + col) = v;
   }
 }
 
@@ -848,12 +859,24 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
   // tiles with four row blocks per wave take the second path: with fewer the
   // saving is small and the extra code makes the kernel spill.
   const int mi_n = min(C::MI, max(0, (tile.m_end - tile.m0 - wm * C::WM + 31) / 32));
-  if (C::MI < 4 || mi_n == C::MI)
-    dma_mainloop<C, GATEUP, false>(ld, ke - kb, C::MI, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3,
-                                   sB0, sB1, sB2, sB3);
-  else if constexpr (C::MI >= 4)
-    dma_mainloop<C, GATEUP, true>(ld, ke - kb, mi_n, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3,
-                                  sB0, sB1, sB2, sB3);
+  // The only row tile of its expert is the only block that reads this B
+  // slice: its weights stream through with non-temporal loads (several row
+  // tiles of one expert share the slice through L2 and keep the default).
+  if (!(p.stream_weights && tile.rt == 1)) {
+    if (C::MI < 4 || mi_n == C::MI)
+      dma_mainloop<C, GATEUP, false>(ld, ke - kb, C::MI, wm, wn, lr, lk, acc, sA0, sA1, sA2,
+                                     sA3, sB0, sB1, sB2, sB3);
+    else if constexpr (C::MI >= 4)
+      dma_mainloop<C, GATEUP, true>(ld, ke - kb, mi_n, wm, wn, lr, lk, acc, sA0, sA1, sA2, sA3,
+                                    sB0, sB1, sB2, sB3);
+  } else {
+    if (C::MI < 4 || mi_n == C::MI)
+      dma_mainloop<C, GATEUP, false, false, false, 2>(ld, ke - kb, C::MI, wm, wn, lr, lk, acc,
+                                                      sA0, sA1, sA2, sA3, sB0, sB1, sB2, sB3);
+    else if constexpr (C::MI >= 4)
+      dma_mainloop<C, GATEUP, true, false, false, 2>(ld, ke - kb, mi_n, wm, wn, lr, lk, acc,
+                                                     sA0, sA1, sA2, sA3, sB0, sB1, sB2, sB3);
+  }
   if (piece >= 0) {
     dma_store_partial<C, GATEUP>(p.tail_part + (size_t)tail_slot * p.tail_slot_floats, tid,
                                  acc);
@@ -864,13 +887,13 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
   if (!(GATEUP && p.save_p1)) {
     constexpr int OUT_BYTES = BM * C::BN * 2;
     if constexpr (BM == 256 && BNB == 256 && BK == 64 && S == 2) {
-      dma_epilogue_staged<C, GATEUP>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc, s_gw, sA0,
-                                     sA1, sB0, sB1);
+      dma_epilogue_staged<C, GATEUP, true>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc,
+                                           s_gw, sA0, sA1, sB0, sB1);
       return;
     } else if constexpr (BNB * BK * 2 == 32768 && OUT_BYTES <= 2 * 32768) {
       // 32 KB B stage buffers (the 128-row tiles): two of them hold the tile
-      dma_epilogue_staged<C, GATEUP>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc, s_gw, sB0,
-                                     sB1, sB0, sB1);
+      dma_epilogue_staged<C, GATEUP, false>(p, tile.m0, tile.m_end, n0, wm, wn, lr, lk, acc,
+                                            s_gw, sB0, sB1, sB0, sB1);
       return;
     }
   }
@@ -994,9 +1017,9 @@ int slots_per_xcd(Kern kern, int threads) {
   return cache[dev];
 }
 
-template <int BM, int BN, int WGM, bool GATEUP>
-hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
-  const auto kern = gemm_bf16_kernel<BM, BN, WGM, GATEUP>;
+template <int BM, int BN, int WGM, bool GATEUP, bool NT>
+hipError_t launch_bf16_nt(const GemmParams& p, hipStream_t s) {
+  const auto kern = gemm_bf16_kernel<BM, BN, WGM, GATEUP, NT>;
   const int N = GATEUP ? p.hidden : p.D;
   const int mt = mtiles_bound(p, BM);
   const long long tiles = (long long)mt * ((N + BN - 1) / BN);
@@ -1013,6 +1036,12 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   hipLaunchKernelGGL((gemm_tail_reduce_flat_kernel<BM, BN, GATEUP>), dim3(kXcds * MOE_REDUCE_BLOCKS),
                      dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, bool GATEUP>
+hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
+  return p.stream_weights ? launch_bf16_nt<BM, BN, WGM, GATEUP, true>(p, s)
+                          : launch_bf16_nt<BM, BN, WGM, GATEUP, false>(p, s);
 }
 
 template <int BM, int BNB, int BK, int S, int WGM, int NWV, bool GATEUP>
@@ -1097,8 +1126,11 @@ bool dma_fits(const GemmParams& p) {
   return x_bytes < lim && w_bytes < lim && hb_tile < lim;
 }
 
-hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s) {
+hipError_t launch_grouped_swiglu(const GemmParams& p_in, bool bf16, hipStream_t s) {
   hipError_t err;
+  GemmParams p = p_in;
+  p.stream_weights = (double)p.n_groups * 3.0 * p.D * p.hidden * 2.0 >
+                     (double)MOE_STREAM_MIN_BYTES;
   if (!bf16) {
     if ((err = launch_f32<true>(p, s)) != hipSuccess) return err;
     return launch_f32<false>(p, s);
@@ -1119,6 +1151,11 @@ hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s) 
     if ((err = launch_dma<MOE_GU_CFG, true>(p, s)) != hipSuccess) return err;
     return launch_dma<MOE_DN_CFG, false>(p, s);
   }
+  // Groups of 64-191 rows on average: a capacity limit with a skewed router
+  // can leave rows in a few experts only, whose weights then stay in the
+  // Infinity Cache from one call to the next; their loads keep the default
+  // policy (streaming loads measured 26% slower on the Switch-shaped layer).
+  p.stream_weights = 0;
   if (dma_fits<GUM, DNM>(p)) {
     if ((err = launch_dma<MOE_GU_CFG_M, true>(p, s)) != hipSuccess) return err;
     return launch_dma<MOE_DN_CFG_M, false>(p, s);

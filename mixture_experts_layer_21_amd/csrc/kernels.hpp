@@ -99,6 +99,10 @@ struct GemmParams {
   // Floats per partial-tile slot of tail_part.  A kernel whose fp32 partial
   // tile is larger than a slot runs its last round unsplit.
   size_t tail_slot_floats;
+  // Nonzero: weight slices that one block reads alone stream through with
+  // non-temporal loads (set by the launcher when the experts' weights are
+  // larger than the last-level cache, so nothing is kept across calls).
+  int stream_weights;
 };
 
 // Split-K tail bookkeeping of the large-tile grouped GEMM.
