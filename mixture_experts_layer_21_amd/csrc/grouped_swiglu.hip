@@ -410,8 +410,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int t
   // 8*(i/4) + 4*(l/32) + (i%4), column l%32.
   if (piece >= 0) {
     // A piece of a split tail tile: the raw fp32 sums, row-major over the
-    // tile's BM rows and NB*BN columns (gate columns, then up columns).
+    // tile's BM rows and NB*BN columns (gate columns, then up columns); rows
+    // past the tile's end are not stored (the reduce reads none of them).
     float* part = p.tail_part + (size_t)tail_slot * p.tail_slot_floats;
+    const int vrows = tile.m_end - tile.m0;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmParams p, int t
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int rl = wm * WM + mi * 32 + 8 * (i >> 2) + 4 * lk + (i & 3);
-            part[rl * BROWS + nb * BN + wn * WN + ni * 32 + lr] = acc[nb][mi][ni][i];
+            if (rl < vrows) part[rl * BROWS + nb * BN + wn * WN + ni * 32 + lr] = acc[nb][mi][ni][i];
           }
     return;
   }
@@ -654,8 +656,10 @@ __device__ __forceinline__ void dma_epilogue_staged(
   }
 }
 
+// Only the 32-row blocks that hold rows of the tile are stored (wave_rows:
+// the tile's rows from this wave's first row on); the reduce reads no others.
 template <class C, bool GATEUP>
-__device__ __forceinline__ void dma_store_partial(float* slot, int tid,
+__device__ __forceinline__ void dma_store_partial(float* slot, int tid, int wave_rows,
                                                   const f32x16 (&acc)[C::NB][C::MI][C::NI]) {
   static_assert((size_t)partial_vectors<C>() * C::NT * 16 <= kTailSlotBytes, "tail slot size");
   f32x4* dst = reinterpret_cast<f32x4*>(slot);
@@ -663,6 +667,7 @@ __device__ __forceinline__ void dma_store_partial(float* slot, int tid,
   for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
+      if (mi * 32 < wave_rows)
 #pragma unroll
       for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
@@ -879,7 +884,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_dma_kernel(GemmParams p, int ta
   }
   if (piece >= 0) {
     dma_store_partial<C, GATEUP>(p.tail_part + (size_t)tail_slot * p.tail_slot_floats, tid,
-                                 acc);
+                                 tile.m_end - tile.m0 - wm * C::WM, acc);
     return;
   }
   // The bf16 results go out through the free stage buffers when those hold

@@ -458,7 +458,8 @@ def _sample_tokens(T, n, seed):
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_forward(moe, name):
     """Full-size workload exactly as the benchmark draws and launches it:
-    routing on every token, permutation bit-exact, outputs on sampled tokens."""
+    routing on every token, permutation bit-exact, outputs on sampled tokens
+    (with a capacity limit: on every token that keeps a slot)."""
     w = W.WORKLOADS[name]
     _say(f"[full] {name}: drawing inputs")
     dev = "cpu" if w.act_dtype == "f32" else "cuda"
@@ -483,12 +484,17 @@ def test_full_size_forward(moe, name):
     nflag, ndiff = P.compare_route(w, r, g)
     _say(f"  near ties flagged {nflag}, differing {ndiff}")
     _check_permute(moe, w, cfg, r["ids"], _cap_int(w))
-    toks = _sample_tokens(w.T, 24 if w.T > 1024 else w.T, seed=11)
-    if w.capacity_factor is not None:  # include dropped and kept tokens
+    # Sampled tokens; the Mixtral-shaped layer (8 experts, each upcast once)
+    # takes 256 of them.
+    nsample = 256 if w.E <= 8 else 24
+    toks = _sample_tokens(w.T, nsample if w.T > 1024 else w.T, seed=11)
+    if w.capacity_factor is not None:
+        # Every token that keeps a slot (the capacity-limited layer keeps few
+        # rows, so each of them is compared), and 64 dropped ones.
         keep = oracle.first_within_capacity(r["ids"], w.E,
                                             oracle.capacity(w.capacity_factor, w.T, w.top_k, w.E))
-        toks = np.unique(np.concatenate([toks, np.nonzero(keep.any(1))[0][:8],
-                                         np.nonzero(~keep.any(1))[0][:8]]))
+        toks = np.unique(np.concatenate([toks, np.nonzero(keep.any(1))[0],
+                                         np.nonzero(~keep.any(1))[0][:64]]))
     _say(f"[full] {name}: oracle outputs on {toks.size} tokens")
     f = P.oracle_forward(w, oi, tokens=toks)
     same = P.comparable_tokens(w, r["ids"], ids)[toks]
