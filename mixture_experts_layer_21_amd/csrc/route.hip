@@ -753,8 +753,13 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
   constexpr int TS = (TILE + 15) / 16;
   constexpr int KSTEP = MODE == 2 ? 16 : 32;
   constexpr int KLANE = MODE == 2 ? 4 : 8;  // k elements per lane per k-step
+  // Per-wave LDS region (in 1 KB units): the bf16 operand tiles of one
+  // k-step on their way into the MFMA layout (MODE 0 and 1; an fp32 W tile
+  // takes 2 KB), later the wave's partial output tiles.
+  constexpr int STG = MODE == 2 ? 0 : TS + (MODE == 1 ? 2 : 1) * ETM;
+  constexpr int WT_ = STG > TS * ETM ? STG : TS * ETM;
   __shared__ SelectSmem<TILE> sm;
-  __shared__ f32x4 red[SEL_WAVES][TS * ETM][MOE_WAVE];
+  __shared__ f32x4 red[SEL_WAVES][WT_][MOE_WAVE];
   const int blk = blockIdx.x, t0 = blk * TILE;
   const int E = p.E, ET = (E + 15) / 16;
   const int nt = min(TILE, p.T - t0);
@@ -769,10 +774,31 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
   const int per = (nsteps + SEL_WAVES - 1) / SEL_WAVES;
   const int s0 = min(nsteps, wave * per), s1 = min(nsteps, s0 + per);
   const int r = lane & 15, kq = lane >> 4;
-  // This lane's row of token tile ts and of expert tile et (clamped), at its
-  // k offset inside a k-step.
+  // MODE 2: this lane's row of token tile ts and of expert tile et
+  // (clamped), at its k offset inside a k-step.
   auto xr = [&](int ts) { return x + (size_t)min(t0 + ts * 16 + r, p.T - 1) * p.D + kq * KLANE; };
   auto wr = [&](int et) { return w + (size_t)min(et * 16 + r, E - 1) * p.D + kq * KLANE; };
+  // MODE 0 and 1 load coalesced: four consecutive lanes read one row's 64
+  // contiguous bytes of a k-step (row lane/4, 16-byte chunk lane%4), and
+  // the tile goes through the wave's LDS region into the MFMA layout (lane
+  // l: row l%16, k chunk l/16).  The 16-byte slots are XOR-swizzled so
+  // that the fragment reads are free of bank conflicts.
+  const int lr = lane >> 2, lc = lane & 3;
+  auto xc = [&](int ts) { return x + (size_t)min(t0 + ts * 16 + lr, p.T - 1) * p.D + lc * 8; };
+  auto wc = [&](int et) {
+    return w + (size_t)min(et * 16 + lr, E - 1) * p.D + lc * (MODE == 1 ? 4 : 8);
+  };
+  // bf16 tiles: chunk c of row q in slot 4q + (c ^ (q/4 % 4)); fp32 W
+  // tiles (eight 4-float chunks a row): chunk m of row q in slot
+  // 8q + (m ^ (q/2 % 8)).
+  const int wslot = lr * 4 + (lc ^ ((lr >> 2) & 3));
+  const int rslot = r * 4 + (kq ^ ((r >> 2) & 3));
+  const int wslot_f0 = lr * 8 + (lc ^ ((lr >> 1) & 7));
+  const int wslot_f1 = lr * 8 + ((4 + lc) ^ ((lr >> 1) & 7));
+  const int rslot_f0 = r * 8 + ((2 * kq) ^ ((r >> 1) & 7));
+  const int rslot_f1 = r * 8 + ((2 * kq + 1) ^ ((r >> 1) & 7));
+  bf16x8* stb = reinterpret_cast<bf16x8*>(&red[wave][0][0]);
+  f32x4* stf = reinterpret_cast<f32x4*>(&red[wave][0][0]) + TS * 64;
   f32x4 acc[TS][ETM];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts)
@@ -781,6 +807,25 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
 
   if constexpr (MODE == 0) {
     constexpr int U = pow2_floor(128 / (4 * (TS + ETM)));  // k-steps in flight
+    // One k-step from registers (coalesced layout) through LDS into MFMAs.
+    auto step = [&](const bf16x8 (&A)[TS], const bf16x8 (&B)[ETM]) {
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) stb[ts * 64 + wslot] = A[ts];
+#pragma unroll
+      for (int et = 0; et < ETM; ++et)
+        if (et < ET) stb[(TS + et) * 64 + wslot] = B[et];
+      bf16x8 a[TS];
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) a[ts] = stb[ts * 64 + rslot];
+#pragma unroll
+      for (int et = 0; et < ETM; ++et)
+        if (et < ET) {
+          const bf16x8 b = stb[(TS + et) * 64 + rslot];
+#pragma unroll
+          for (int ts = 0; ts < TS; ++ts)
+            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ts], b, acc[ts][et], 0, 0, 0);
+        }
+    };
     int s = s0;
     for (; s + U <= s1; s += U) {
       bf16x8 A[U][TS], B[U][ETM];
@@ -788,36 +833,50 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
       for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int ts = 0; ts < TS; ++ts)
-          A[u][ts] = *reinterpret_cast<const bf16x8*>(xr(ts) + (s + u) * KSTEP);
+          A[u][ts] = *reinterpret_cast<const bf16x8*>(xc(ts) + (s + u) * KSTEP);
 #pragma unroll
         for (int et = 0; et < ETM; ++et)
-          if (et < ET) B[u][et] = *reinterpret_cast<const bf16x8*>(wr(et) + (s + u) * KSTEP);
+          if (et < ET) B[u][et] = *reinterpret_cast<const bf16x8*>(wc(et) + (s + u) * KSTEP);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int et = 0; et < ETM; ++et)
-          if (et < ET)
-#pragma unroll
-            for (int ts = 0; ts < TS; ++ts)
-              acc[ts][et] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u][ts], B[u][et], acc[ts][et], 0, 0, 0);
+      for (int u = 0; u < U; ++u) step(A[u], B[u]);
     }
     for (; s < s1; ++s) {
-      bf16x8 A[TS];
+      bf16x8 A[TS], B[ETM];
 #pragma unroll
-      for (int ts = 0; ts < TS; ++ts) A[ts] = *reinterpret_cast<const bf16x8*>(xr(ts) + s * KSTEP);
+      for (int ts = 0; ts < TS; ++ts) A[ts] = *reinterpret_cast<const bf16x8*>(xc(ts) + s * KSTEP);
 #pragma unroll
       for (int et = 0; et < ETM; ++et)
-        if (et < ET) {
-          const bf16x8 B = *reinterpret_cast<const bf16x8*>(wr(et) + s * KSTEP);
-#pragma unroll
-          for (int ts = 0; ts < TS; ++ts)
-            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ts], B, acc[ts][et], 0, 0, 0);
-        }
+        if (et < ET) B[et] = *reinterpret_cast<const bf16x8*>(wc(et) + s * KSTEP);
+      step(A, B);
     }
   } else if constexpr (MODE == 1) {
     constexpr int U = pow2_floor(160 / (4 * TS + 8 * ETM));
+    auto step = [&](const bf16x8 (&A)[TS], const f32x4 (&W0)[ETM], const f32x4 (&W1)[ETM]) {
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) stb[ts * 64 + wslot] = A[ts];
+#pragma unroll
+      for (int et = 0; et < ETM; ++et)
+        if (et < ET) {
+          stf[et * 128 + wslot_f0] = W0[et];
+          stf[et * 128 + wslot_f1] = W1[et];
+        }
+      bf16x8 a[TS];
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) a[ts] = stb[ts * 64 + rslot];
+#pragma unroll
+      for (int et = 0; et < ETM; ++et)
+        if (et < ET) {
+          bf16x8 h, m, l;
+          split3_bf16(stf[et * 128 + rslot_f0], stf[et * 128 + rslot_f1], h, m, l);
+#pragma unroll
+          for (int ts = 0; ts < TS; ++ts) {
+            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ts], h, acc[ts][et], 0, 0, 0);
+            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ts], m, acc[ts][et], 0, 0, 0);
+            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ts], l, acc[ts][et], 0, 0, 0);
+          }
+        }
+    };
     int s = s0;
     for (; s + U <= s1; s += U) {
       bf16x8 A[U][TS];
@@ -826,46 +885,29 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
       for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int ts = 0; ts < TS; ++ts)
-          A[u][ts] = *reinterpret_cast<const bf16x8*>(xr(ts) + (s + u) * KSTEP);
+          A[u][ts] = *reinterpret_cast<const bf16x8*>(xc(ts) + (s + u) * KSTEP);
 #pragma unroll
         for (int et = 0; et < ETM; ++et)
           if (et < ET) {
-            W0[u][et] = *reinterpret_cast<const f32x4*>(wr(et) + (s + u) * KSTEP);
-            W1[u][et] = *reinterpret_cast<const f32x4*>(wr(et) + (s + u) * KSTEP + 4);
+            W0[u][et] = *reinterpret_cast<const f32x4*>(wc(et) + (s + u) * KSTEP);
+            W1[u][et] = *reinterpret_cast<const f32x4*>(wc(et) + (s + u) * KSTEP + 16);
           }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int et = 0; et < ETM; ++et)
-          if (et < ET) {
-            bf16x8 h, m, l;
-            split3_bf16(W0[u][et], W1[u][et], h, m, l);
-#pragma unroll
-            for (int ts = 0; ts < TS; ++ts) {
-              acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u][ts], h, acc[ts][et], 0, 0, 0);
-              acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u][ts], m, acc[ts][et], 0, 0, 0);
-              acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u][ts], l, acc[ts][et], 0, 0, 0);
-            }
-          }
+      for (int u = 0; u < U; ++u) step(A[u], W0[u], W1[u]);
     }
     for (; s < s1; ++s) {
       bf16x8 A[TS];
+      f32x4 W0[ETM], W1[ETM];
 #pragma unroll
-      for (int ts = 0; ts < TS; ++ts) A[ts] = *reinterpret_cast<const bf16x8*>(xr(ts) + s * KSTEP);
+      for (int ts = 0; ts < TS; ++ts) A[ts] = *reinterpret_cast<const bf16x8*>(xc(ts) + s * KSTEP);
 #pragma unroll
       for (int et = 0; et < ETM; ++et)
         if (et < ET) {
-          bf16x8 h, m, l;
-          split3_bf16(*reinterpret_cast<const f32x4*>(wr(et) + s * KSTEP),
-                      *reinterpret_cast<const f32x4*>(wr(et) + s * KSTEP + 4), h, m, l);
-#pragma unroll
-          for (int ts = 0; ts < TS; ++ts) {
-            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ts], h, acc[ts][et], 0, 0, 0);
-            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ts], m, acc[ts][et], 0, 0, 0);
-            acc[ts][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ts], l, acc[ts][et], 0, 0, 0);
-          }
+          W0[et] = *reinterpret_cast<const f32x4*>(wc(et) + s * KSTEP);
+          W1[et] = *reinterpret_cast<const f32x4*>(wc(et) + s * KSTEP + 16);
         }
+      step(A, W0, W1);
     }
   } else {
     for (int s = s0; s < s1; ++s) {
@@ -897,7 +939,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
     const int tile = (tl >> 4) * ETM + (e >> 4);
     const int ln = ((tl & 15) >> 2) * 16 + (e & 15), i = tl & 3;
     const float* rv = reinterpret_cast<const float*>(&red[0][tile][ln]) + i;
-    constexpr int WSTRIDE = TS * ETM * MOE_WAVE * 4;  // floats between two waves' tiles
+    constexpr int WSTRIDE = WT_ * MOE_WAVE * 4;  // floats between two waves' regions
     float v = rv[0];
 #pragma unroll
     for (int wv = 1; wv < SEL_WAVES; ++wv) v += rv[wv * WSTRIDE];
