@@ -276,7 +276,10 @@ hipError_t launch_hist(int T, int E, int k, const int32_t* ids, int32_t* hist, h
 bool permute_fits_one_block(int T, int E, int k);
 hipError_t launch_permute_small(const FinalizeParams& fp, const ScatterParams& sp, hipStream_t s);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t s);
-hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
+// launch_finalize and the scatter of the assignments into expert-major rows,
+// in two launches (the scatter blocks compute the expert offsets themselves).
+hipError_t launch_finalize_scatter(const FinalizeParams& fp, const ScatterParams& sp,
+                                   hipStream_t s);
 hipError_t launch_grouped_swiglu(const GemmParams& p, bool bf16, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
 hipError_t launch_update_bias(int E, const int32_t* counts, float gamma, float* bias,

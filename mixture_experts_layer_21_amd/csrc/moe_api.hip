@@ -340,9 +340,8 @@ moe_status launch_permutation(const moe::FinalizeParams& fp, const moe::ScatterP
                               hipStream_t stream) {
   if (moe::permute_fits_one_block(fp.T, fp.E, fp.k))
     return hip_ok(moe::launch_permute_small(fp, sp, stream), "permute kernel");
-  MOE_TRY(hip_ok(moe::launch_finalize(fp, stream), "finalize kernel"));
-  if (sp.ids) MOE_TRY(hip_ok(moe::launch_scatter(sp, stream), "scatter kernel"));
-  return MOE_OK;
+  if (sp.ids) return hip_ok(moe::launch_finalize_scatter(fp, sp, stream), "permute kernels");
+  return hip_ok(moe::launch_finalize(fp, stream), "finalize kernel");
 }
 
 moe::GemmParams gemm_params(const moe_config* c, int n_groups, int hidden, const void* x,

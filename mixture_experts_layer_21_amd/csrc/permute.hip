@@ -12,9 +12,10 @@
 // when the caller supplies the IDs).  column_scan_kernel (one block per
 // expert) turns each column into per-tile running bases, the expert's count
 // and its P_e sum; expert_scan_kernel clips the counts to the capacity, scans
-// them into expert offsets and finishes the aux losses.  scatter_kernel ranks
-// each tile's assignments in order with wave ballots and writes both
-// directions of the permutation.
+// them into expert offsets and finishes the aux losses.  When the
+// permutation is wanted, scatter_offsets_kernel does that scan in every block
+// and then ranks each tile's assignments in order with wave ballots and
+// writes both directions of the permutation.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -112,10 +113,10 @@ __global__ __launch_bounds__(256) void column_scan_kernel(FinalizeParams p) {
   }
 }
 
-// One block: capacity clip, expert offsets, n_kept and the aux losses.
-__global__ __launch_bounds__(256) void expert_scan_kernel(FinalizeParams p) {
-  __shared__ int s_i[4];
-  __shared__ float s_f[4];
+// Capacity clip, expert offsets, n_kept and the aux losses, by one block of
+// 256 threads (expert_scan_kernel, and the first block of
+// scatter_offsets_kernel).
+__device__ __forceinline__ void expert_scan_block(const FinalizeParams& p, int* s_i, float* s_f) {
   int base = 0;
   float bal = 0.f;
   const int nv = p.aux ? valid_tokens(p, s_i) : p.T;
@@ -147,22 +148,57 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(FinalizeParams p) {
   }
 }
 
-// One wave per token tile.  Assignments are taken 64 at a time in index
-// order; lanes holding the same expert find each other with one ballot per
-// bit of the expert ID, so a lane's rank is the number of lower lanes with
-// its expert plus the running count of that expert in LDS.
-__global__ __launch_bounds__(64) void scatter_kernel(ScatterParams p) {
-  __shared__ int run[kMaxExperts];
-  const int b = blockIdx.x;
-  for (int e = threadIdx.x; e < p.E; e += 64) run[e] = p.block_base[(size_t)e * gridDim.x + b];
-  __syncthreads();
+// One block: capacity clip, expert offsets, n_kept and the aux losses.
+__global__ __launch_bounds__(256) void expert_scan_kernel(FinalizeParams p) {
+  __shared__ int s_i[4];
+  __shared__ float s_f[4];
+  expert_scan_block(p, s_i, s_f);
+}
+
+// The expert scan and the scatter in one launch.  Every block scans the
+// clipped per-expert counts into LDS itself (the same scan as
+// expert_scan_block, so the offsets are the same) and the first block also
+// writes the finalize outputs.  Then each of the four waves takes one token
+// tile: its assignments are ranked 64 at a time in index order; lanes
+// holding the same expert find each other with one ballot per bit of the
+// expert ID, so a lane's rank is the number of lower lanes with its expert
+// plus the running count of that expert in the wave's own LDS array (a
+// wave's LDS accesses execute in order, so no barrier is needed between its
+// reads of run[] and its leaders' updates).
+constexpr int kScatterTiles = 4;
+__global__ __launch_bounds__(256) void scatter_offsets_kernel(FinalizeParams fp, ScatterParams p) {
+  __shared__ int s_i[4];
+  __shared__ float s_f[4];
+  __shared__ int off[kMaxExperts];
+  __shared__ int run_all[kScatterTiles][kMaxExperts];
+  if (blockIdx.x == 0) expert_scan_block(fp, s_i, s_f);
+  {
+    int base = 0;
+    for (int e0 = 0; e0 < p.E; e0 += 256) {
+      const int e = e0 + threadIdx.x;
+      const int c = e < p.E ? fp.counts_ws[e] : 0;
+      const int kept = p.capacity > 0 ? min(c, p.capacity) : c;
+      int tot;
+      const int incl = block_scan_incl(kept, s_i, tot);
+      if (e < p.E) off[e] = base + incl - kept;
+      base += tot;
+    }
+  }
+  __syncthreads();  // off[] complete; no block barrier follows
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  const int nblk = (p.T + p.tile - 1) / p.tile;
+  const int b = blockIdx.x * kScatterTiles + wv;
+  if (b >= nblk) return;
+  int* run = run_all[wv];
+  for (int e = lane; e < p.E; e += 64) run[e] = p.block_base[(size_t)e * nblk + b];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   int nbits = 1;
   while ((1 << nbits) < p.E) ++nbits;
   const int a0 = b * p.tile * p.k;
   const int a1 = min(p.T, (b + 1) * p.tile) * p.k;
   const uint64_t below = lanemask_lt();
   for (int c = a0; c < a1; c += 64) {
-    const int a = c + (int)threadIdx.x;
+    const int a = c + lane;
     const int e_in = a < a1 ? p.ids[a] : -1;
     const bool in_range = (unsigned)e_in < (unsigned)p.E;
     const bool valid = a < a1 && in_range;
@@ -175,13 +211,13 @@ __global__ __launch_bounds__(64) void scatter_kernel(ScatterParams p) {
       peers &= set ? bb : ~bb;
     }
     const int rank = valid ? run[e] + __popcll(peers & below) : 0;
-    __syncthreads();  // every lane has read run[] before the leaders advance it
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (valid && (peers & below) == 0) run[e] += __popcll(peers);
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (valid) {
       const bool keep = p.capacity <= 0 || rank < p.capacity;
       if (keep) {
-        const int row = p.expert_offsets[e] + rank;
+        const int row = off[e] + rank;
         p.assign_to_row[a] = row;
         p.row_to_assign[row] = a;
       } else {
@@ -191,8 +227,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(ScatterParams p) {
   }
 }
 
-// Small batches: column_scan_kernel, expert_scan_kernel and scatter_kernel
-// in one workgroup of 16 waves (one launch instead of three).  Each expert's
+// Small batches: column_scan_kernel and scatter_offsets_kernel in one
+// workgroup of 16 waves (one launch instead of two).  Each expert's
 // tile bases are kept in LDS; the sums of P_e, z and the valid tokens run
 // sequentially in tile order and the balance sum in expert order, so the
 // results are deterministic (they may differ from the multi-block kernels'
@@ -311,7 +347,7 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(FinalizePa
   }
   if (!sp.ids) return;
   // 3. scatter: wave w ranks the assignments of tiles w, w + 16, ... in
-  // order (as scatter_kernel does, its running counts in LDS row w)
+  // order (as scatter_offsets_kernel does, its running counts in LDS row w)
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t below = lanemask_lt();
@@ -405,8 +441,14 @@ hipError_t launch_permute_small(const FinalizeParams& fp, const ScatterParams& s
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const ScatterParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(scatter_kernel, dim3(route_blocks(p.T)), dim3(64), 0, s, p);
+hipError_t launch_finalize_scatter(const FinalizeParams& fp, const ScatterParams& sp,
+                                   hipStream_t s) {
+  hipLaunchKernelGGL(column_scan_kernel, dim3(fp.E), dim3(256), 0, s, fp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int nblk = route_blocks(sp.T);
+  hipLaunchKernelGGL(scatter_offsets_kernel, dim3((nblk + kScatterTiles - 1) / kScatterTiles),
+                     dim3(256), 0, s, fp, sp);
   return hipGetLastError();
 }
 

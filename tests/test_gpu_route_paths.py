@@ -30,7 +30,7 @@ CASES = [
     ("fused_split3_tile8", 777, 1024, 64, 1, "bf16", "f32", "softmax"),
     ("fused_split3_at_bound", 1200, 2048, 64, 1, "bf16", "f32", "softmax"),
     ("fused_split3_tile32_E40", 1100, 768, 40, 2, "bf16", "f32", "softmax"),
-    ("fused_bf16_idle_waves_E24", 600, 160, 24, 3, "bf16", "bf16", "sigmoid"),
+    ("fused_bf16_idle_waves_E24", 600, 192, 24, 3, "bf16", "bf16", "sigmoid"),
     ("fused_f32_idle_waves", 1100, 96, 12, 3, "f32", "f32", "softmax"),
     ("fused_f32x_bf16w", 333, 256, 24, 2, "f32", "bf16", "sigmoid"),
     ("split_split3_over_bound", 1500, 4096, 64, 1, "bf16", "f32", "softmax"),
