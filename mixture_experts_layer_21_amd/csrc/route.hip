@@ -743,10 +743,10 @@ __global__ __launch_bounds__(SEL_THREADS) void route_select_kernel(RouteParams p
 // MODE 0: bf16 x and W, 16x16x32 bf16; 1: bf16 x and fp32 W on the exact
 // three-term bf16 split of W (three MFMAs per tile and k-step, products
 // exact, fp32 sums); 2: an fp32 operand, 16x16x4 fp32.
-// ETM: expert tiles held per wave (E <= 16 * ETM).  U k-steps of operands
-// are loaded at once: as many as about 128 (bf16 W) or 160 (fp32 W) VGPRs
-// of operands allow, at most 8.
-constexpr int pow2_floor(int v) { return v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
+// ETM: expert tiles held per wave (E <= 16 * ETM).  U = 2 k-steps of
+// operands are loaded at once: with every wave of every block loading at
+// the same time, more in flight measured slower (Mixtral-shaped router: 18.5
+// us at two k-steps, 19.5 at four, 21.4 at eight; one: 21.9).
 
 template <typename XT, typename WT, int MODE, int TILE, int ETM>
 __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p) {
@@ -806,7 +806,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
     for (int et = 0; et < ETM; ++et) acc[ts][et] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (MODE == 0) {
-    constexpr int U = pow2_floor(128 / (4 * (TS + ETM)));  // k-steps in flight
+    constexpr int U = 2;  // k-steps of operands in flight per wave (see below)
     // One k-step from registers (coalesced layout) through LDS into MFMAs.
     auto step = [&](const bf16x8 (&A)[TS], const bf16x8 (&B)[ETM]) {
 #pragma unroll
@@ -851,7 +851,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
       step(A, B);
     }
   } else if constexpr (MODE == 1) {
-    constexpr int U = pow2_floor(160 / (4 * TS + 8 * ETM));
+    constexpr int U = 2;
     auto step = [&](const bf16x8 (&A)[TS], const f32x4 (&W0)[ETM], const f32x4 (&W1)[ETM]) {
 #pragma unroll
       for (int ts = 0; ts < TS; ++ts) stb[ts * 64 + wslot] = A[ts];
