@@ -171,11 +171,14 @@ def test_permute_small(moe, name):
 
 # Shapes past the one-workgroup permutation (more than 4096 assignments):
 # the per-expert scans and the per-tile scatter, with one to 256 experts, E
-# not a power of two, k up to 8, and capacity limits.
+# not a power of two, k up to 8, and capacity limits; the last two keep
+# 8-token routing tiles (T <= 1024) and leave the scatter's last block with
+# a single tile.
 LARGE_PERMUTE_CASES = [
     # T, E, k, capacity (0: dropless)
     (3001, 8, 3, 0), (8192, 64, 1, 160), (4100, 5, 2, 0), (2048, 256, 8, 0),
     (5000, 3, 3, 2000), (1500, 130, 4, 10), (16384, 1, 1, 0), (3000, 2, 2, 0),
+    (1000, 256, 8, 0), (777, 97, 6, 20),
 ]
 
 
