@@ -317,7 +317,20 @@ inline bool route_fused(int D, int E, bool router_bf16) {
   return E <= kFusedMaxE &&
          (long long)E * D * (router_bf16 ? 2 : 4) <= (long long)MOE_ROUTE_FUSED_MAX_BYTES;
 }
-constexpr int kRouteTiledM = 64, kRouteTiledN = 256;
+// Tokens per block of the LDS-tiled router GEMM (64 or 128: 4 threads a
+// token), experts per block.  On the DeepSeek-shaped router (8192 tokens,
+// 256 experts, K = 7168) 128 tokens and 64-deep k-steps take 50 us, 64
+// tokens and 32-deep k-steps 66 us.
+#ifndef MOE_ROUTE_TILED_M
+#define MOE_ROUTE_TILED_M 128
+#endif
+// k-step depth (32 or 64).
+#ifndef MOE_ROUTE_TILED_K
+#define MOE_ROUTE_TILED_K 64
+#endif
+constexpr int kRouteTiledM = MOE_ROUTE_TILED_M, kRouteTiledN = 256, kRouteTiledK = MOE_ROUTE_TILED_K;
+static_assert(kRouteTiledM == 64 || kRouteTiledM == 128, "tiled router rows");
+static_assert(kRouteTiledK == 32 || kRouteTiledK == 64, "tiled router k-step");
 
 #ifndef MOE_ROUTE_KSPLIT_MAX
 #define MOE_ROUTE_KSPLIT_MAX 16
@@ -335,7 +348,8 @@ inline int route_ksplit(int T, int D, int E, bool bf16_mfma) {
     const long long blocks =
         (long long)((T + kRouteTiledM - 1) / kRouteTiledM) * ((E + kRouteTiledN - 1) / kRouteTiledN);
     int ks = 1;
-    while (blocks * ks < 512 && ks * 2 * 8 <= nsteps && ks < 16) ks *= 2;
+    // about 512 x 64 tokens' worth of blocks in flight
+    while (blocks * ks * kRouteTiledM < 512 * 64 && ks * 2 * 8 <= nsteps && ks < 16) ks *= 2;
     return ks;
   }
   const int NT = (E + 15) / 16;

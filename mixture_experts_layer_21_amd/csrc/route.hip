@@ -203,16 +203,25 @@ __global__ __launch_bounds__(NTHREADS) void route_logits_kernel(RouteParams p) {
   }
 }
 
-// LDS-tiled router GEMM for bf16 x and W: a block computes 64 tokens x 256
-// experts over its K range (32-deep k-steps staged through LDS in two
-// buffers); four waves in a 2 x 2 grid each hold 32 tokens x 128 experts as
-// four 32x32x16 MFMA tiles.  x is read once per K range instead of once per
-// expert tile.  Rows are 64 bytes in LDS; the 16-byte chunk c of row r sits
-// at c ^ ((r >> 2) & 3), which keeps the fragment reads conflict-free.
-__device__ __forceinline__ int rswz(int r) { return (r >> 2) & 3; }
+// LDS-tiled router GEMM for bf16 x and W: a block computes BM tokens x 256
+// experts over its K range (BK-deep k-steps staged through LDS in two
+// buffers, the next k-step's operands in registers meanwhile; a second
+// register set for the k-step after that measured no faster); its BM/16
+// waves in a (BM/32) x 2 grid each hold 32 tokens x 128 experts as four
+// 32x32x16 MFMA tiles.  x is read once per K range instead of once per
+// expert tile, the router once per BM tokens.  The 16-byte chunk c of row r
+// sits at c ^ rswz(r) in LDS, which keeps the fragment reads conflict-free
+// (64-byte rows: (r >> 2) & 3; 128-byte rows: the grouped GEMM's pattern).
+template <int KCH>
+__device__ __forceinline__ int rswz(int r) {
+  if constexpr (KCH == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return (r >> 2) & 3;
+}
 
-__global__ __launch_bounds__(NTHREADS) void route_logits_tiled_kernel(RouteParams p) {
-  constexpr int BM = kRouteTiledM, BN = kRouteTiledN, BK = 32;
+template <int BM, int BK>
+__global__ __launch_bounds__(BM * 4) void route_logits_tiled_kernel(RouteParams p) {
+  constexpr int BN = kRouteTiledN, NT = BM * 4, KCH = BK / 8;
+  constexpr int AC = BM * KCH / NT, BC = BN * KCH / NT;  // chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
   const uint16_t* x = static_cast<const uint16_t*>(p.x);
@@ -226,17 +235,22 @@ __global__ __launch_bounds__(NTHREADS) void route_logits_tiled_kernel(RouteParam
   const int per = (nsteps + p.ksplit - 1) / p.ksplit;
   const int s0 = blockIdx.z * per, s1 = min(nsteps, s0 + per);
 
-  // This thread's 16-byte chunks: one of A (row tid/4), four of B.
-  const int ar = tid >> 2, ac = tid & 3;
-  const uint16_t* asrc = x + (size_t)min(t0 + ar, p.T - 1) * p.D + ac * 8;
-  const int adst = ar * BK + (ac ^ rswz(ar)) * 8;
-  const uint16_t* bsrc[4];
-  int bdst[4];
+  // This thread's 16-byte chunks: AC of A, BC of B (chunk c: row c / KCH).
+  const uint16_t* asrc[AC];
+  int adst[AC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + NTHREADS * i, r = c >> 2, cc = c & 3;
+  for (int i = 0; i < AC; ++i) {
+    const int c = tid + NT * i, r = c / KCH, cc = c % KCH;
+    asrc[i] = x + (size_t)min(t0 + r, p.T - 1) * p.D + cc * 8;
+    adst[i] = r * BK + (cc ^ rswz<KCH>(r)) * 8;
+  }
+  const uint16_t* bsrc[BC];
+  int bdst[BC];
+#pragma unroll
+  for (int i = 0; i < BC; ++i) {
+    const int c = tid + NT * i, r = c / KCH, cc = c % KCH;
     bsrc[i] = w + (size_t)min(e0 + r, p.E - 1) * p.D + cc * 8;
-    bdst[i] = r * BK + (cc ^ rswz(r)) * 8;
+    bdst[i] = r * BK + (cc ^ rswz<KCH>(r)) * 8;
   }
   f32x16 acc[4];
 #pragma unroll
@@ -245,18 +259,20 @@ __global__ __launch_bounds__(NTHREADS) void route_logits_tiled_kernel(RouteParam
     for (int i = 0; i < 16; ++i) acc[ni][i] = 0.f;
 
   if (s0 < s1) {
-    u32x4 ra, rb[4];
+    u32x4 ra[AC], rb[BC];
 #define MOE_RLOAD(s)                                                                        \
   do {                                                                                      \
     const int k0_ = (s) * BK;                                                               \
-    ra = *reinterpret_cast<const u32x4*>(asrc + k0_);                                       \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) rb[i] =                                   \
+    _Pragma("unroll") for (int i = 0; i < AC; ++i) ra[i] =                                  \
+        *reinterpret_cast<const u32x4*>(asrc[i] + k0_);                                     \
+    _Pragma("unroll") for (int i = 0; i < BC; ++i) rb[i] =                                  \
         *reinterpret_cast<const u32x4*>(bsrc[i] + k0_);                                     \
   } while (0)
 #define MOE_RSTORE(buf)                                                                     \
   do {                                                                                      \
-    *reinterpret_cast<u32x4*>(&As[buf][adst]) = ra;                                         \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+    _Pragma("unroll") for (int i = 0; i < AC; ++i)                                          \
+        *reinterpret_cast<u32x4*>(&As[buf][adst[i]]) = ra[i];                               \
+    _Pragma("unroll") for (int i = 0; i < BC; ++i)                                          \
         *reinterpret_cast<u32x4*>(&Bs[buf][bdst[i]]) = rb[i];                               \
   } while (0)
     MOE_RLOAD(s0);
@@ -269,12 +285,13 @@ __global__ __launch_bounds__(NTHREADS) void route_logits_tiled_kernel(RouteParam
       for (int kk = 0; kk < BK / 16; ++kk) {
         const int ch = kk * 2 + lk;
         const int r = wm * 32 + lr;
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[cur][r * BK + (ch ^ rswz(r)) * 8]);
+        const bf16x8 af =
+            *reinterpret_cast<const bf16x8*>(&As[cur][r * BK + (ch ^ rswz<KCH>(r)) * 8]);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           const int rb_ = wn * 128 + ni * 32 + lr;
           const bf16x8 bfr =
-              *reinterpret_cast<const bf16x8*>(&Bs[cur][rb_ * BK + (ch ^ rswz(rb_)) * 8]);
+              *reinterpret_cast<const bf16x8*>(&Bs[cur][rb_ * BK + (ch ^ rswz<KCH>(rb_)) * 8]);
           acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[ni], 0, 0, 0);
         }
       }
@@ -990,7 +1007,8 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s) {
   if (route_tiled(p.T, p.E, p.act_bf16 && p.router_bf16)) {
     const dim3 tgrid((p.T + kRouteTiledM - 1) / kRouteTiledM,
                      (p.E + kRouteTiledN - 1) / kRouteTiledN, p.ksplit);
-    hipLaunchKernelGGL(route_logits_tiled_kernel, tgrid, block, 0, s, p);
+    hipLaunchKernelGGL((route_logits_tiled_kernel<kRouteTiledM, kRouteTiledK>), tgrid,
+                       dim3(kRouteTiledM * 4), 0, s, p);
   } else if (p.act_bf16 && p.router_bf16) {
     hipLaunchKernelGGL((route_logits_kernel<uint16_t, uint16_t, true>), grid, block, 0, s, p);
   } else if (p.act_bf16) {
