@@ -144,57 +144,77 @@ __global__ __launch_bounds__(NTHREADS) void combine_kernel(CombineParams p, int 
 }
 
 // Without the shared-expert gate every 16-byte chunk of an output row is
-// independent: one thread per (token, chunk), consecutive threads on
-// consecutive chunks of a row.  A thread issues the loads of up to eight
-// slots' rows (and the shared and residual rows) before it adds them in
-// slot order, so the loads of a token overlap instead of following one
-// another; the sum order is that of combine_kernel, so the bits agree.
-template <typename T>
+// independent.  A row's chunks are cut into CPT segments; thread i of a row
+// takes chunk i of every segment (consecutive threads on consecutive chunks,
+// so each load instruction covers contiguous bytes).  A thread issues the
+// loads of up to eight slots' rows (and the shared and residual rows) for
+// all its chunks before it adds them in slot order, so the loads of a token
+// overlap instead of following one another; the sum order is that of
+// combine_kernel, so the bits agree.
+template <typename T, int CPT>
 __global__ __launch_bounds__(NTHREADS) void combine_rows_kernel(CombineParams p) {
   constexpr int N = Vec16<T>::N;
-  constexpr int G = 8;  // slots loaded together
-  const int nchunk = p.D / N;
+  constexpr int G = 8 / CPT;  // slots loaded together
+  const int nseg = p.D / N / CPT;
   const long long gid = (long long)blockIdx.x * NTHREADS + threadIdx.x;
-  if (gid >= (long long)p.T * nchunk) return;
-  const int t = (int)(gid / nchunk), c = (int)(gid % nchunk);
+  if (gid >= (long long)p.T * nseg) return;
+  const int t = (int)(gid / nseg), c = (int)(gid % nseg);
   const T* y = static_cast<const T*>(p.y_rows) + (size_t)c * N;
   const int32_t* a2r = p.assign_to_row + (size_t)t * p.k;
   const size_t at = (size_t)t * p.D + (size_t)c * N;
-  uint4 qs = make_uint4(0u, 0u, 0u, 0u), qr = qs;
-  if (p.shared_rows) qs = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.shared_rows) + at);
-  if (p.residual) qr = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.residual) + at);
-  float acc[N];
+  const size_t seg = (size_t)nseg * N;  // elements between a thread's chunks
+  uint4 qs[CPT], qr[CPT];
 #pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = 0.f;
+  for (int h = 0; h < CPT; ++h) {
+    qs[h] = qr[h] = make_uint4(0u, 0u, 0u, 0u);
+    if (p.shared_rows)
+      qs[h] = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.shared_rows) + at + h * seg);
+    if (p.residual)
+      qr[h] = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.residual) + at + h * seg);
+  }
+  float acc[CPT][N];
+#pragma unroll
+  for (int h = 0; h < CPT; ++h)
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[h][i] = 0.f;
   for (int s0 = 0; s0 < p.k; s0 += G) {
     int row[G];
-    uint4 q[G];
+    uint4 q[G][CPT];
 #pragma unroll
     for (int u = 0; u < G; ++u) row[u] = s0 + u < p.k ? a2r[s0 + u] : -1;
 #pragma unroll
     for (int u = 0; u < G; ++u)
-      if (row[u] >= 0) q[u] = *reinterpret_cast<const uint4*>(y + (size_t)row[u] * p.D);
+      if (row[u] >= 0)
+#pragma unroll
+        for (int h = 0; h < CPT; ++h)
+          q[u][h] = *reinterpret_cast<const uint4*>(y + (size_t)row[u] * p.D + h * seg);
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       if (row[u] < 0) continue;
-      float v[N];
-      unpack16<T>(q[u], v);
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += v[i];
+      for (int h = 0; h < CPT; ++h) {
+        float v[N];
+        unpack16<T>(q[u][h], v);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[h][i] += v[i];
+      }
     }
   }
-  float v[N];
-  if (p.shared_rows) {
-    unpack16<T>(qs, v);
 #pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] += v[i];
-  }
-  if (p.residual) {  // the residual stream joins last, before the one rounding
-    unpack16<T>(qr, v);
+  for (int h = 0; h < CPT; ++h) {
+    float v[N];
+    if (p.shared_rows) {
+      unpack16<T>(qs[h], v);
 #pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] += v[i];
+      for (int i = 0; i < N; ++i) acc[h][i] += v[i];
+    }
+    if (p.residual) {  // the residual stream joins last, before the one rounding
+      unpack16<T>(qr[h], v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[h][i] += v[i];
+    }
+    store16<T>(static_cast<T*>(p.out) + at + h * seg, acc[h]);
   }
-  store16<T>(static_cast<T*>(p.out) + at, acc);
 }
 
 }  // namespace
@@ -203,12 +223,28 @@ hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s) {
   const int n = bf16 ? 8 : 4;
   const int nchunk = p.D / n;
   if (!(p.shared_rows && p.shared_gate)) {
-    const long long threads = (long long)p.T * nchunk;
+    // Chunks per thread: four once there are at least 256K chunks (the
+    // capacity-limited Switch-shaped combine 6.95 -> 5.77 us, Mixtral-shaped
+    // 20.2 -> 18.5 us), one for small batches, which need the threads (the
+    // decode-shaped combine 4.3 us with one, 6.2 with four).
+    int cpt = (long long)p.T * nchunk >= (1 << 18) ? 4 : 1;
+    while (cpt > 1 && nchunk % cpt) cpt >>= 1;
+    const long long threads = (long long)p.T * (nchunk / cpt);
     const dim3 grid((unsigned)((threads + NTHREADS - 1) / NTHREADS)), block(NTHREADS);
-    if (bf16)
-      hipLaunchKernelGGL(combine_rows_kernel<uint16_t>, grid, block, 0, s, p);
+#define MOE_COMBINE_LAUNCH(C)                                                              \
+  do {                                                                                     \
+    if (bf16)                                                                              \
+      hipLaunchKernelGGL((combine_rows_kernel<uint16_t, C>), grid, block, 0, s, p);        \
+    else                                                                                   \
+      hipLaunchKernelGGL((combine_rows_kernel<float, C>), grid, block, 0, s, p);           \
+  } while (0)
+    if (cpt >= 4)
+      MOE_COMBINE_LAUNCH(4);
+    else if (cpt == 2)
+      MOE_COMBINE_LAUNCH(2);
     else
-      hipLaunchKernelGGL(combine_rows_kernel<float>, grid, block, 0, s, p);
+      MOE_COMBINE_LAUNCH(1);
+#undef MOE_COMBINE_LAUNCH
     return hipGetLastError();
   }
   int tpb = 1;  // tokens per block: keep at least ~nchunk threads per token

@@ -257,6 +257,42 @@ def test_combine_small(moe, name):
     assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-30)
 
 
+@pytest.mark.parametrize("shared,residual", [(False, False), (True, True)])
+def test_combine_wide(moe, shared, residual):
+    """The combine at a batch of 256K row chunks, where each thread sums four
+    chunks of its token (capacity drops, a shared row and the residual)."""
+    w = W.Workload("combine_wide", 1, 2048, D=1024, H=64, E=8, top_k=3)
+    _say(f"[combine-wide] shared={shared} residual={residual}")
+    cfg = P.config_of(w)
+    rng = np.random.default_rng(17)
+    ids = np.stack([rng.choice(w.E, size=w.top_k, replace=False) for _ in range(w.T)])
+    perm, keep = _check_permute(moe, w, cfg, ids, 600)
+    n = int(perm["n_kept"].item())
+    gen = torch.Generator().manual_seed(9)
+    rows = torch.randn(max(n, 1), w.D, generator=gen).to(torch.bfloat16)
+    sh = torch.randn(w.T, w.D, generator=gen).to(torch.bfloat16) if shared else None
+    res = torch.randn(w.T, w.D, generator=gen).to(torch.bfloat16) if residual else None
+    out = moe.moe_combine(cfg, rows.cuda(), perm["assign_to_row"],
+                          None if sh is None else sh.cuda(),
+                          residual=None if res is None else res.cuda())
+    a2r = perm["assign_to_row"].cpu().numpy().reshape(w.T, w.top_k)
+    R = rows.to(torch.float64).numpy()
+    Y = np.zeros((w.T, w.top_k, w.D))
+    for s_ in range(w.top_k):
+        m = a2r[:, s_] >= 0
+        Y[m, s_] = R[a2r[m, s_]]
+    ref = oracle.combine(Y, None if sh is None else sh.to(torch.float64).numpy(),
+                         residual=None if res is None else res.to(torch.float64).numpy())
+    got = out.cpu().to(torch.float64).numpy()
+    # fp32 sum of at most k+2 terms (error at most (k+1) 2^-24 of the sum of
+    # their magnitudes), then one rounding to bf16 (2^-9 of the value)
+    mag = np.abs(Y).sum(1)
+    mag += 0.0 if sh is None else np.abs(sh.to(torch.float64).numpy())
+    mag += 0.0 if res is None else np.abs(res.to(torch.float64).numpy())
+    fp32_err = (w.top_k + 1) * 2.0 ** -24 * mag
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * (np.abs(ref) + fp32_err) + fp32_err)
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_forward_small(moe, name):
     w = W.SMALL[name]
