@@ -823,7 +823,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_fused_kernel(RouteParams p)
     for (int et = 0; et < ETM; ++et) acc[ts][et] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (MODE == 0) {
-    constexpr int U = 2;  // k-steps of operands in flight per wave (see below)
+    constexpr int U = 2;  // k-steps of operands in flight per wave (see above)
     // One k-step from registers (coalesced layout) through LDS into MFMAs.
     auto step = [&](const bf16x8 (&A)[TS], const bf16x8 (&B)[ETM]) {
 #pragma unroll
