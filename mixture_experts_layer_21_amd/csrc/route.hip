@@ -547,13 +547,23 @@ __device__ __forceinline__ void select_tokens(const RouteParams p, SelectSmem<TI
 #pragma unroll
     for (int j = 0; j < NS; ++j) allowed[j] = ok[j];
     if (p.n_groups > 1) {
+      // Group scores are taken over the selection scores themselves: for
+      // softmax the probabilities, not the logits the expert rounds may rank
+      // by (a sum of two probabilities is not ordered like the sum of their
+      // logits).
+      float gin[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const float v = by_score ? sel[j] : sc[j];
+        gin[j] = (!ok[j] || v != v) ? -INFINITY : v;
+      }
       // Group score of every group, then group g's key in lane g.
       uint32_t gkey = 0;
       if (seg_groups) {
         float a1[NS], a2[NS];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          a1[j] = sel[j];
+          a1[j] = gin[j];
           a2[j] = -INFINITY;
           if (gsz >= 2) top2_step<DPP_XOR1>(a1[j], a2[j]);
           if (gsz >= 4) top2_step<DPP_XOR2>(a1[j], a2[j]);
@@ -579,7 +589,7 @@ __device__ __forceinline__ void select_tokens(const RouteParams p, SelectSmem<TI
           float a1 = -INFINITY, a2 = -INFINITY;
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
-            if (ok[j] && (lane + 64 * j) / gsz == g) top2_merge(a1, a2, sel[j], -INFINITY);
+            if (ok[j] && (lane + 64 * j) / gsz == g) top2_merge(a1, a2, gin[j], -INFINITY);
           }
 #pragma unroll
           for (int msk = 32; msk >= 1; msk >>= 1)

@@ -94,23 +94,29 @@ def test_route_small(moe, name):
 
 # Group-limit shapes: group sizes 2..32 (segmented in-wave reduction), 64 and
 # 12 (the general path), both group rules, and softmax as well as sigmoid.
+# With softmax the top-2 group sum is over probabilities, which the sum of
+# two logits does not order alike once the logits spread out (x_std 4 and no
+# selection bias: the last two cases, one per group path).
 GROUP_CASES = [
-    # E, n_groups, topk_groups, k, rule, score
-    (64, 32, 8, 6, "top2sum", "sigmoid"),
-    (64, 16, 4, 8, "top2sum", "sigmoid"),
-    (128, 8, 3, 8, "top2sum", "softmax"),
-    (256, 8, 4, 8, "max", "sigmoid"),
-    (256, 4, 2, 8, "top2sum", "sigmoid"),
-    (48, 4, 2, 6, "top2sum", "sigmoid"),
-    (96, 3, 1, 4, "max", "softmax"),
+    # E, n_groups, topk_groups, k, rule, score, x_std, selection-bias sigma
+    (64, 32, 8, 6, "top2sum", "sigmoid", 1.0, 0.01),
+    (64, 16, 4, 8, "top2sum", "sigmoid", 1.0, 0.01),
+    (128, 8, 3, 8, "top2sum", "softmax", 1.0, 0.01),
+    (256, 8, 4, 8, "max", "sigmoid", 1.0, 0.01),
+    (256, 4, 2, 8, "top2sum", "sigmoid", 1.0, 0.01),
+    (48, 4, 2, 6, "top2sum", "sigmoid", 1.0, 0.01),
+    (96, 3, 1, 4, "max", "softmax", 1.0, 0.01),
+    (64, 8, 5, 8, "top2sum", "softmax", 4.0, 0.0),
+    (96, 8, 3, 6, "top2sum", "softmax", 4.0, 0.0),
 ]
 
 
-@pytest.mark.parametrize("E,ng,tg,k,rule,score", GROUP_CASES)
-def test_route_group_limits(moe, E, ng, tg, k, rule, score):
+@pytest.mark.parametrize("E,ng,tg,k,rule,score,x_std,sel", GROUP_CASES)
+def test_route_group_limits(moe, E, ng, tg, k, rule, score, x_std, sel):
     w = W.SMALL["deepseek_small"].with_(
         seq=173, E=E, top_k=k, n_groups=ng, topk_groups=tg, group_rule=rule, score=score,
-        route_scale=2.5 if score == "sigmoid" else 1.0, H_shared=0)
+        route_scale=2.5 if score == "sigmoid" else 1.0, H_shared=0, x_std=x_std,
+        select_bias_sigma=sel)
     _say(f"[route-groups] E={E} groups={ng} keep={tg} k={k} {rule} {score}")
     inp = W.make_inputs(w, "cpu", seed=3)
     cfg = P.config_of(w)
