@@ -23,11 +23,11 @@ import workloads as W
 from tests import parity as P
 
 
-def _configs(n=24, seed=1204):
+def _configs(n=48, seed=1204):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        E = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 40, 64, 96, 128, 200, 256]))
+        E = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 40, 64, 96, 128, 160, 200, 256]))
         k = int(rng.integers(1, min(E, 8) + 1))
         D = int(rng.choice([64, 128, 192, 256, 512]))
         H = int(rng.choice([64, 128, 192, 320, 512]))
@@ -101,3 +101,19 @@ def test_random_config(i):
                                   w.act_dtype, f"{w.name} forward")
     print(f"  near ties {nflag} (differing {ndiff}), max|err| {err:.3g} max|ref| {scale:.3g}",
           file=sys.stderr, flush=True)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(0, len(CONFIGS), 2))
+def test_random_config_backward(i):
+    """Every gradient of every other configuration above (the device on the
+    oracle's routes), every element, at the layer's bf16 tolerance ("Lab:
+    build a tiny MoE in PyTorch", "Smoke test and backward pass")."""
+    import mixture_experts_layer_21_amd as moe
+    from tests.test_gpu_backward import GRADS, SHARED, _compare, _run
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    w = CONFIGS[i]
+    print(f"[random-backward] {w.name}: {_describe(w)}", file=sys.stderr, flush=True)
+    g, ref = _run(moe, w, seed=200 + i)
+    names = GRADS + (SHARED if w.H_shared else ())
+    _compare(g, ref, names + ("d_gate_w",), w.name)
