@@ -117,3 +117,74 @@ def test_random_config_backward(i):
     g, ref = _run(moe, w, seed=200 + i)
     names = GRADS + (SHARED if w.H_shared else ())
     _compare(g, ref, names + ("d_gate_w",), w.name)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(1, len(CONFIGS), 2))
+def test_random_config_variants(i):
+    """The other half of the configurations with a seeded choice of the
+    forward's variants: a token (padding) mask, the SwiGLU clamp, the
+    residual add, the RMSNorm pre-norm and the gated shared expert ([NEMO]
+    ``token_mask``, ``swiglu_limit``, ``shared_expert_gate``; "Lab: build a
+    tiny MoE in PyTorch", "Put the MoE into a decoder block")."""
+    import mixture_experts_layer_21_amd as moe
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    w = CONFIGS[i]
+    rng = np.random.default_rng(500 + i)
+    use_mask = bool(rng.random() < 0.5)
+    limit = float(rng.choice([0.0, 0.05, 0.5]))
+    use_res = bool(rng.random() < 0.5)
+    use_pre = bool(rng.random() < 0.4)
+    use_gate = bool(w.H_shared > 0 and rng.random() < 0.6)
+    print(f"[random-variants] {w.name}: {_describe(w)} mask={use_mask} limit={limit} "
+          f"residual={use_res} pre_norm={use_pre} shared_gate={use_gate}",
+          file=sys.stderr, flush=True)
+    inp = W.make_inputs(w, "cpu", seed=300 + i)
+    if use_gate:
+        gen = torch.Generator().manual_seed(300 + i)
+        inp["ws_sgate"] = (torch.randn(w.D, generator=gen) / w.D ** 0.5).to(torch.bfloat16)
+    d = {kk: v.to("cuda") for kk, v in inp.items()}
+    cfg = P.config_of(w, swiglu_limit=limit)
+    mask = None
+    kw = {}
+    if use_mask:
+        mask = rng.random(w.T) >= 0.3
+        kw["token_mask"] = torch.from_numpy(mask).cuda()
+    if use_res:
+        kw["residual"] = d["x"]
+    nw = None
+    if use_pre:
+        cfg.pre_norm, cfg.norm_eps = 1, 1e-5
+        nw = torch.rand(w.D, generator=torch.Generator().manual_seed(400 + i)) + 0.5
+        kw["norm_weight"] = nw.cuda()
+    if use_gate:
+        kw["shared_expert_gate"] = d["ws_sgate"]
+    ids = torch.empty(w.T, w.top_k, dtype=torch.int32, device="cuda")
+    gw = torch.empty(w.T, w.top_k, dtype=torch.float32, device="cuda")
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    aux = torch.empty(2, dtype=torch.float32, device="cuda")
+    out = moe.moe_forward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                          logit_bias=d.get("logit_bias"), select_bias=d.get("select_bias"),
+                          ws_gate=d.get("ws_gate"), ws_up=d.get("ws_up"),
+                          ws_down=d.get("ws_down"), expert_ids=ids, gate_w=gw, counts=counts,
+                          aux=aux, **kw)
+    x_dev = moe.moe_rmsnorm(cfg, d["x"], nw.cuda()) if use_pre else d["x"]
+    g = moe.moe_route(cfg, x_dev, d["w_router"], d.get("logit_bias"), d.get("select_bias"),
+                      token_mask=kw.get("token_mask"))
+    torch.cuda.synchronize()
+    assert torch.equal(g["expert_ids"], ids) and torch.equal(g["gate_w"], gw)
+    oi = P.oracle_inputs(inp)
+    pre = None
+    x_route = oi["x"]
+    if use_pre:
+        pre = (nw.to(torch.float64).numpy(), float(np.float32(1e-5)), w.act_dtype)
+        x_route = P.oracle.rms_norm(oi["x"], *pre)
+    r = P.oracle_route(w, dict(oi, x=x_route), token_mask=mask)
+    nflag, ndiff = P.compare_route(w, r, {"expert_ids": ids, "gate_w": gw, "counts": counts,
+                                          "aux": aux, "mean_prob": g["mean_prob"]})
+    f = P.oracle_forward(w, oi, token_mask=mask, swiglu_limit=limit,
+                         residual=oi["x"] if use_res else None, pre_norm=pre)
+    err, scale = P.compare_tokens(out, f["out"], P.comparable_tokens(w, r["ids"], ids),
+                                  w.act_dtype, f"{w.name} forward variants")
+    print(f"  near ties {nflag} (differing {ndiff}), max|err| {err:.3g} max|ref| {scale:.3g}",
+          file=sys.stderr, flush=True)
