@@ -23,14 +23,18 @@ import workloads as W
 from tests import parity as P
 
 
-def _configs(n=48, seed=1204):
+def _configs(n=48, seed=1204, act="bf16"):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         E = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 40, 64, 96, 128, 160, 200, 256]))
         k = int(rng.integers(1, min(E, 8) + 1))
-        D = int(rng.choice([64, 128, 192, 256, 512]))
-        H = int(rng.choice([64, 128, 192, 320, 512]))
+        if act == "bf16":  # the bf16 path takes widths in multiples of 64
+            D = int(rng.choice([64, 128, 192, 256, 512]))
+            H = int(rng.choice([64, 128, 192, 320, 512]))
+        else:
+            D = int(rng.choice([48, 80, 96, 144, 256]))
+            H = int(rng.choice([32, 48, 112, 128, 200]))
         rows_per_expert = int(rng.choice([8, 40, 100, 160, 300]))
         T = int(np.clip(rows_per_expert * E // k + rng.integers(-7, 8), 1, 3000))
         while T > 1 and T * k * D * H > 3e8:  # keeps the float64 oracle to about a second
@@ -45,7 +49,8 @@ def _configs(n=48, seed=1204):
         cf = None if rng.random() < 0.5 else float(rng.choice([0.5, 1.0, 1.25, 2.0]))
         Hs = 0 if rng.random() < 0.7 else int(rng.choice([64, 128]))
         out.append(W.Workload(
-            f"random{i}", batch=1, seq=T, D=D, H=H, E=E, top_k=k,
+            f"random{i}" if act == "bf16" else f"random_f32_{i}", batch=1, seq=T, D=D, H=H,
+            E=E, top_k=k, act_dtype=act,
             router_dtype="f32" if rng.random() < 0.25 else "bf16", score=score,
             renormalize=renorm, route_scale=1.0 if score == "softmax" else 2.5,
             n_groups=n_groups, topk_groups=topk_groups,
@@ -55,7 +60,10 @@ def _configs(n=48, seed=1204):
     return out
 
 
-CONFIGS = _configs()
+# bf16 layers first (the forward, backward and variant tests index these),
+# then fp32 layers (forward only: the backward is bf16).
+CONFIGS = _configs() + _configs(12, seed=1205, act="f32")
+N_BF16 = 48
 
 
 def _describe(w):
@@ -104,7 +112,7 @@ def test_random_config(i):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("i", range(0, len(CONFIGS), 2))
+@pytest.mark.parametrize("i", range(0, N_BF16, 2))
 def test_random_config_backward(i):
     """Every gradient of every other configuration above (the device on the
     oracle's routes), every element, at the layer's bf16 tolerance ("Lab:
@@ -120,7 +128,7 @@ def test_random_config_backward(i):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("i", range(1, len(CONFIGS), 2))
+@pytest.mark.parametrize("i", range(1, N_BF16, 2))
 def test_random_config_variants(i):
     """The other half of the configurations with a seeded choice of the
     forward's variants: a token (padding) mask, the SwiGLU clamp, the
@@ -142,7 +150,8 @@ def test_random_config_variants(i):
     inp = W.make_inputs(w, "cpu", seed=300 + i)
     if use_gate:
         gen = torch.Generator().manual_seed(300 + i)
-        inp["ws_sgate"] = (torch.randn(w.D, generator=gen) / w.D ** 0.5).to(torch.bfloat16)
+        inp["ws_sgate"] = (torch.randn(w.D, generator=gen) / w.D ** 0.5).to(
+            W.torch_dtype(w.act_dtype))
     d = {kk: v.to("cuda") for kk, v in inp.items()}
     cfg = P.config_of(w, swiglu_limit=limit)
     mask = None
