@@ -87,3 +87,15 @@ def test_noalloc_rejects_a_layer_beyond_its_scratch(moe):
     with pytest.raises(moe.MoeError, match="UNSUPPORTED.*scratch"):
         moe.moe_forward_noalloc(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"],
                                 d["w_down"], out=out)
+
+
+@pytest.mark.parametrize("i", range(0, 60, 3))
+def test_noalloc_random_configs(moe, i):
+    """Every third seeded random configuration (bf16 and fp32 layers of 1 to
+    256 experts), one after another on the same static scratch."""
+    from tests.test_gpu_random_configs import CONFIGS
+    w = CONFIGS[i]
+    _say(f"[noalloc-random] {w.name}: T={w.T} D={w.D} H={w.H} E={w.E} k={w.top_k}")
+    d = {k: v.to("cuda") for k, v in W.make_inputs(w, "cpu", seed=600 + i).items()}
+    wa, ra = _both(moe, w, d, w.T)
+    _agree(wa, ra, f"{w.name} T={w.T}")
