@@ -16,7 +16,11 @@ from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["decode_small", "switch_small", "deepseek_small", "tiny"]
+# 32-row GEMM tiles (decode_small, switch_small, deepseek_small), the 128-row
+# band with its split-K tail (switch_band, mixtral_band), the 256-row tiles
+# (mixtral_small) and the fp32 path (tiny).
+NAMES = ["decode_small", "switch_small", "deepseek_small", "tiny", "switch_band",
+         "mixtral_band", "mixtral_small"]
 
 
 @pytest.fixture(scope="module")
