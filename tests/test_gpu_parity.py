@@ -546,3 +546,45 @@ def test_full_size_forward(moe, name):
     err, scale = P.compare_tokens(out[torch.from_numpy(toks).cuda()], f["out"], same,
                                   w.act_dtype, f"{name} sampled outputs")
     _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
+
+
+@pytest.mark.parametrize("name,n_pick", [("deepseek_v3_256x_top8_grouped", 4),
+                                         ("mixtral_8x_top2", 2)])
+def test_full_size_expert_rows(moe, name, n_pick):
+    """Every row of a few whole experts of the full-size grouped SwiGLU stage
+    (all their row tiles, partial ones and split-K tail pieces included), on
+    the oracle's routes, weights and permutation: the experts with the most
+    and the fewest rows and evenly spaced ones between."""
+    w = W.WORKLOADS[name]
+    _say(f"[full-rows] {name}: drawing inputs")
+    inp = {k: v.to("cuda") for k, v in W.make_inputs(w, "cuda", seed=0).items()}
+    cfg = P.config_of(w)
+    oi = P.oracle_inputs(inp)
+    r = P.oracle_route(w, oi)
+    cap = _cap_int(w)
+    keep = oracle.first_within_capacity(r["ids"], w.E, cap if cap > 0 else None)
+    off, r2a, _ = oracle.permutation(r["ids"], keep, w.E)
+    ids = torch.from_numpy(r["ids"].astype(np.int32)).cuda()
+    gw = torch.from_numpy(r["weights"].astype(np.float32)).cuda()
+    perm = moe.moe_permute(cfg, ids, cap)
+    assert np.array_equal(perm["expert_offsets"].cpu().numpy(), off)
+    rows = moe.max_rows(cfg)
+    y = torch.empty(max(rows, 1), w.D, dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_swiglu(cfg, inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                           row_to_assign=perm["row_to_assign"],
+                           expert_offsets=perm["expert_offsets"], max_rows_bound=rows,
+                           gate_w=gw, y_rows=y)
+    torch.cuda.synchronize()
+    n = np.diff(off)
+    with_rows = np.nonzero(n)[0]
+    by_size = with_rows[np.argsort(n[with_rows], kind="stable")]
+    picks = sorted(set(int(by_size[j]) for j in
+                       np.linspace(0, by_size.size - 1, n_pick).round().astype(int)))
+    for e in picks:
+        a = np.asarray(r2a[off[e]:off[e + 1]])
+        t, s = a // w.top_k, a % w.top_k
+        ref = r["weights"][t, s][:, None] * oracle.swiglu_ffn(
+            oi["x"][t], oi["w_gate"][e], oi["w_up"][e], oi["w_down"][e])
+        err, scale = P.compare_rows(y[off[e]:off[e + 1]], ref, w.act_dtype,
+                                    f"{name} expert {e} ({a.size} rows)")
+        _say(f"  expert {e}: {a.size} rows, max|err| {err:.3g} max|ref| {scale:.3g}")
