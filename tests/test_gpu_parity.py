@@ -548,13 +548,14 @@ def test_full_size_forward(moe, name):
     _say(f"  max|err| {err:.3g} max|ref| {scale:.3g}")
 
 
-@pytest.mark.parametrize("name,n_pick", [("deepseek_v3_256x_top8_grouped", 4),
-                                         ("mixtral_8x_top2", 2)])
+@pytest.mark.parametrize("name,n_pick", [("deepseek_v3_256x_top8_grouped", 16),
+                                         ("mixtral_8x_top2", 8)])
 def test_full_size_expert_rows(moe, name, n_pick):
-    """Every row of a few whole experts of the full-size grouped SwiGLU stage
-    (all their row tiles, partial ones and split-K tail pieces included), on
-    the oracle's routes, weights and permutation: the experts with the most
-    and the fewest rows and evenly spaced ones between."""
+    """Every row of whole experts of the full-size grouped SwiGLU stage (all
+    their row tiles, partial ones and split-K tail pieces included), on the
+    oracle's routes, weights and permutation: every expert of the
+    Mixtral-shaped layer (the whole stage), and 16 of the DeepSeek-shaped
+    layer's, from the fewest rows to the most."""
     w = W.WORKLOADS[name]
     _say(f"[full-rows] {name}: drawing inputs")
     inp = {k: v.to("cuda") for k, v in W.make_inputs(w, "cuda", seed=0).items()}
