@@ -624,7 +624,8 @@ __global__ __launch_bounds__(256) void pad_offsets_kernel(int G, const int32_t* 
   if (tid == 0)
     for (int g = 1; g <= G; ++g) s[g] += s[g - 1];
   __syncthreads();
-  if (tid <= G) padoff[tid] = s[tid];
+  // G + 1 values: with G = 256 groups the end offset is the 257th
+  for (int i = tid; i <= G; i += blockDim.x) padoff[i] = s[i];
 }
 
 // dL/dh for one token per wave (experts lane + 64j, j < 4).

@@ -33,7 +33,7 @@ def _say(*a):
 
 
 def _run(moe, w, seed, aux=(0.3, 0.2), token_mask=None, swiglu_limit=0.0, pre_norm=None,
-         mutate=None):
+         mutate=None, workspace=None):
     """``pre_norm`` = (norm weight [D] f32 CPU tensor or None, eps): the layer
     takes RMSNorm(x) and x is the input before the norm.  ``mutate`` edits the
     drawn inputs in place before either side sees them."""
@@ -75,7 +75,7 @@ def _run(moe, w, seed, aux=(0.3, 0.2), token_mask=None, swiglu_limit=0.0, pre_no
                          ws_gate=d.get("ws_gate"), ws_up=d.get("ws_up"),
                          ws_down=d.get("ws_down"), balance_coef=aux[0], z_coef=aux[1],
                          d_gate_w=True, norm_weight=nw_dev,
-                         shared_expert_gate=d.get("ws_sgate"))
+                         shared_expert_gate=d.get("ws_sgate"), workspace=workspace)
     torch.cuda.synchronize()
     return g, ref
 
@@ -96,6 +96,18 @@ def test_backward_matches_oracle(moe, name):
     g2, _ = _run(moe, w, seed=30)
     for n in names:  # deterministic: a second call gives the same bits
         assert torch.equal(g[n], g2[n]), n
+
+
+def test_backward_256_experts(moe):
+    """256 experts, the most the library takes: the padded offsets of the
+    ragged-K weight-gradient GEMMs have 257 entries, one more than the
+    threads of the kernel that writes them.  On a zero-filled workspace a
+    missing last entry would leave the last expert without gradient."""
+    w = W.Workload("bwd_256", 1, 600, D=192, H=128, E=256, top_k=4)
+    cfg = P.config_of(w)
+    ws = torch.zeros(moe.backward_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    g, ref = _run(moe, w, seed=33, workspace=ws)
+    _compare(g, ref, GRADS + ("d_gate_w",), "256 experts")
 
 
 def test_backward_without_aux_terms(moe):
